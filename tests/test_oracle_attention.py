@@ -1,0 +1,104 @@
+"""Pins for the attention oracle (CPU only): the K-mean against an exact rational mean, softmax
+against a direct fp64 definition and its shift invariance (the property K-smoothing relies on),
+a hand-checkable all-equal-logit case, and decode/prefill consistency."""
+import math
+from fractions import Fraction
+
+import numpy as np
+
+from oracle.attention import (attn_decode_ref, attn_prefill_ref, code_v, kmean_ref, softmax_rows,
+                              softmax_scale)
+from oracle.mx import mx_dequantize
+from quantized_gemm_algorithm_amd.synth import attention_qkv, bf16_bits_to_f32, f32_to_bf16_bits
+
+
+def test_kmean_is_rounded_exact_mean():
+    rng = np.random.default_rng(31)
+    k = f32_to_bf16_bits((rng.standard_normal((300, 2, 32)) * 7 + 3).astype(np.float32))
+    mu = kmean_ref(k, "bf16")
+    kf = bf16_bits_to_f32(k).astype(np.float64)
+    for h in range(2):
+        for c in range(0, 32, 5):
+            exact = sum(Fraction(float(v)) for v in kf[:, h, c]) / 300
+            got = Fraction(float(mu[h, c]))
+            ulp = Fraction(float(np.spacing(np.float32(float(exact)))))
+            assert abs(got - exact) <= ulp / 2 * (1 + Fraction(1, 2**20))
+
+
+def test_kmean_constant_column():
+    k = f32_to_bf16_bits(np.full((77, 1, 32), 1.5, np.float32))
+    assert np.all(kmean_ref(k, "bf16") == 1.5)
+
+
+def test_softmax_against_fp64_definition_and_shift_invariance():
+    rng = np.random.default_rng(32)
+    s = (rng.standard_normal((5, 64)) * 30).astype(np.float32)
+    n_valid = np.array([64, 10, 1, 33, 64])
+    p, l, m = softmax_rows(s, n_valid, 128)
+    scale = float(softmax_scale(128))
+    for r in range(5):
+        z = s[r, : n_valid[r]].astype(np.float64) * scale
+        want = np.exp(z - z.max()) / np.exp(z - z.max()).sum()
+        assert np.allclose(p[r, : n_valid[r]] / l[r], want, rtol=1e-5, atol=1e-7)
+        assert np.all(p[r, n_valid[r]:] == 0)
+        assert p[r, : n_valid[r]].max() == 1.0
+    # a constant shift of every logit in a row leaves the normalised softmax unchanged
+    p2, l2, _ = softmax_rows((s + np.float32(256.0)).astype(np.float32), n_valid, 128)
+    for r in range(5):
+        assert np.allclose(p2[r] / l2[r], p[r] / l[r], rtol=1e-4, atol=1e-6)
+
+
+def test_smoothing_leaves_unquantised_attention_unchanged():
+    # gamma(K) = K - mean(K) shifts every logit of a query row by q.mu: softmax is unchanged.
+    g = attention_qkv(T=64, Hq=2, Hkv=1, d=128, seed_cfg=4)
+    q = bf16_bits_to_f32(g["q"]).astype(np.float64)
+    k = bf16_bits_to_f32(g["k"]).astype(np.float64)
+    mu = k.mean(axis=0, keepdims=True)
+    for h in range(2):
+        a = q[:, h] @ k[:, 0].T / math.sqrt(128)
+        b = q[:, h] @ (k[:, 0] - mu[:, 0]).T / math.sqrt(128)
+        sa = np.exp(a - a.max(1, keepdims=True)); sa /= sa.sum(1, keepdims=True)
+        sb = np.exp(b - b.max(1, keepdims=True)); sb /= sb.sum(1, keepdims=True)
+        assert np.allclose(sa, sb, rtol=1e-9, atol=1e-12)
+
+
+def test_equal_logits_give_causal_mean_of_v():
+    # q = 0 -> every logit 0 -> p = 1 on unmasked keys, P-hat = 1 exactly, l = i + 1,
+    # so O[i] is the mean of the coded V over tokens 0..i.
+    T, d = 64, 32
+    rng = np.random.default_rng(33)
+    q = np.zeros((T, 1, d), np.uint16)
+    k = f32_to_bf16_bits(rng.standard_normal((T, 1, d)).astype(np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((T, 1, d)).astype(np.float32))
+    r = attn_prefill_ref(q, k, v, "bf16", causal=True)
+    vc, vs = code_v(v, "bf16")
+    vd = mx_dequantize(vc[0], vs[0], "fp4")  # [d, T]
+    for i in (0, 1, 31, 32, 63):
+        assert np.all(r["p"][0, i, : i + 1] == 1.0) and np.all(r["p"][0, i, i + 1:] == 0.0)
+        assert r["l"][0, i] == i + 1
+        want = vd[:, : i + 1].sum(axis=1) / (i + 1)
+        assert np.allclose(r["o"][0, i], want, rtol=0, atol=1e-12)
+
+
+def test_decode_matches_prefill_last_row():
+    T, Hq, Hkv, d = 96, 4, 2, 64
+    g = attention_qkv(T=T, Hq=Hq, Hkv=Hkv, d=d, seed_cfg=4)
+    pre = attn_prefill_ref(g["q"], g["k"], g["v"], "bf16", causal=True, rows=np.array([T - 1]))
+    dec = attn_decode_ref(g["q"][T - 1][None], g["k"][None], g["v"][None], pre["mu"][None], np.array([T]))
+    for h in range(Hq):
+        assert np.array_equal(dec["p_codes"][0][h], pre["p_codes"][h, 0])
+        assert np.array_equal(dec["o_bf16"][0][h], pre["o_bf16"][h, 0])
+
+
+def test_decode_partial_block_zero_padded():
+    T, Hq, Hkv, d = 70, 2, 1, 32
+    g = attention_qkv(T=T, Hq=Hq, Hkv=Hkv, d=d, seed_cfg=4)
+    mu = kmean_ref(g["k"][:64], "bf16")
+    dec = attn_decode_ref(g["q"][T - 1][None], g["k"][None], g["v"][None], mu[None], np.array([T]))
+    assert len(dec["p"][0][0]) == 96
+    assert np.all(dec["p"][0][0][T:] == 0)
+    vpad = np.zeros((96, 1, d), np.uint16)
+    vpad[:T] = g["v"]
+    vc1, vs1 = code_v(g["v"], "bf16")
+    vc2, vs2 = code_v(vpad, "bf16")
+    assert np.array_equal(vc1, vc2) and np.array_equal(vs1, vs2)
