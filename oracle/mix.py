@@ -56,6 +56,19 @@ def _check(fmt, x):
         raise ValueError("MiX blocks run along the last axis, whose length must be a multiple of 32")
 
 
+def _exact_abs_diff(x, v):
+    """|x - v| as an unevaluated pair (hi, lo) with hi = fl(|x - v|), exactly (TwoSum).
+
+    Pairs compare exactly in lexicographic order; v = +inf gives (inf, nan), which never wins.
+    """
+    with np.errstate(invalid="ignore"):
+        s = x - v
+        bb = s - x
+        e = (x - (s - bb)) + (-v - bb)
+        sign = np.where(s < 0, -1.0, 1.0)
+        return np.abs(s), sign * e
+
+
 def mix_quantize(x, fmt, dtype="f32"):
     """Quantize rows of ``x`` to MiX codes, following Algorithm 1 step by step.
 
@@ -102,8 +115,16 @@ def mix_quantize(x, fmt, dtype="f32"):
     cands_de = [np.clip(de_naive + 1, 0, 6), np.clip(de_naive, 0, 6), np.clip(de_naive - 1, 0, 6)]
     values = [np.zeros_like(xb), np.where(pos, M * np.ldexp(1.0, E - 7), np.inf)]
     values += [sgn * M * np.ldexp(1.0, E - d) for d in cands_de]
-    err = np.stack([np.abs(xb - v) for v in values], axis=0)
-    pick = np.argmin(err, axis=0)  # first minimum = smallest magnitude on a tie
+    # Reconstruction error |x - v| compared exactly: fp64 subtraction alone can round two
+    # different distances to one value when |x| is far above the block's range (saturation).
+    pick = np.zeros(xb.shape, np.int64)  # first minimum = smallest magnitude on a tie
+    best_hi, best_lo = _exact_abs_diff(xb, values[0])
+    for c in range(1, len(values)):
+        hi, lo = _exact_abs_diff(xb, values[c])
+        better = (hi < best_hi) | ((hi == best_hi) & (lo < best_lo))
+        pick = np.where(better, c, pick)
+        best_hi = np.where(better, hi, best_hi)
+        best_lo = np.where(better, lo, best_lo)
 
     de_pick = np.choose(np.clip(pick - 2, 0, 2), cands_de)
     nib = np.where(xb < 0.0, 8, 0) | de_pick

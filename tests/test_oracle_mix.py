@@ -6,6 +6,7 @@ search over all 16 nibbles, and the reconstruction of the block maximum.
 """
 import math
 import struct
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -33,11 +34,13 @@ def _code_value(nib, emax, m):
 
 
 def _nearest_code(x, emax, m):
-    """Brute force over all 16 nibbles: nearest value, ties to the smaller magnitude."""
+    """Brute force over all 16 nibbles: nearest value (exact rational distances), ties to the
+    smaller magnitude."""
     best = None
+    xf = Fraction(x)
     for nib in range(16):
         v = _code_value(nib, emax, m)
-        key = (abs(x - v), abs(v))
+        key = (abs(xf - Fraction(v)), abs(v))
         if best is None or key < best[0]:
             best = (key, nib)
     return best[1]
@@ -177,7 +180,7 @@ def test_exhaustive_bf16_sweep(emax, m):
     # vectorised brute force over the 16 codes (values via IEEE fields)
     table = np.array([_code_value(c, emax, m) for c in range(16)], np.float64)
     xx = x.astype(np.float64)[:, :, None]
-    err = np.abs(xx - table[None, None, :])
+    err = np.abs(xx - table[None, None, :])  # exact here: |x| <= top keeps every difference in 30 bits
     best = np.argmin(err, axis=2)
     # resolve exact ties toward the smaller magnitude
     minerr = np.take_along_axis(err, best[:, :, None], axis=2)
@@ -280,3 +283,19 @@ def test_rejects_bad_shapes_and_nonfinite():
         mix_quantize(np.full((1, 32), np.inf, np.float32), "4.5b")
     with pytest.raises(ValueError):
         mix_quantize(np.ones((1, 32), np.float32), "5b")
+
+
+@pytest.mark.parametrize("fmt", ["4.25b", "4.5b"])
+def test_far_above_range_saturates_to_nearest(fmt):
+    # A block whose maximum is far above 2^9 clamps Emax to 8; its elements take the nearest of the
+    # representable values, which for huge magnitudes is the largest one, never zero.
+    x = np.zeros((1, 32), np.float32)
+    x[0, :8] = [1e30, -3e38, 5e20, 1e10, 700.0, -1e6, 3.0, -2.0**-20]
+    x[0, 8:16] = [2.0e36, 1e-30, -1e-10, 0.5, 96.0, -65536.0, 1e3, 3e38]
+    codes, shared = mix_quantize(x, fmt)
+    emax, ms = _fields(shared[:, 0], fmt, 0)
+    assert emax == 8
+    nibs = _nibbles(codes[0])
+    for i in range(32):
+        assert nibs[i] == _nearest_code(float(x[0, i]), emax, ms[i // 8]), i
+    assert nibs[0] == 0x0 and nibs[1] == 0x8
