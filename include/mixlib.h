@@ -1,0 +1,219 @@
+/*
+ * mixlib -- MiX (Micro-Inverted-Scaling) quantizers, the A-MiX x W-MX matrix product and
+ * K-smoothed attention on AMD Instinct MI355X (gfx950).
+ *
+ * Sources. "P1" is the pchao.org digest of the paper, titled
+ * "MiX：面向端到端低比特视觉语言模型加速的微反缩放"; each declaration below names the section,
+ * figure or equation of P1 that defines the operation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Memory: every buffer argument is DEVICE memory owned by the caller, except where a comment
+ *   says "host". The library never allocates, frees or synchronises; it enqueues kernels on
+ *   `stream` (a hipStream_t; NULL is the null stream) and returns.
+ * - Validation happens on the host before any HIP call; on failure nothing is enqueued, a status
+ *   code is returned and mix_last_error() (per thread) describes the problem.
+ * - Shapes: `rows`/`cols`/M/N/K are element counts. Every block axis (MiX and MX blocks hold 32
+ *   elements) must be a multiple of 32. A zero extent is a valid empty call (MIX_OK, nothing is
+ *   read or written, pointers may be NULL). Negative extents are MIX_E_SHAPE.
+ * - Alignment: element pointers and row pitches of fp32/bf16 inputs must be 16-byte aligned
+ *   (MIX_E_ALIGN); code/scale buffers must be 16-byte aligned.
+ * - Inputs must be finite. A non-finite input gives unspecified codes (no error is raised).
+ * - Device faults surface at the caller's next synchronisation as HIP errors.
+ *
+ * Data formats (P1, 方法概览 / method overview, format bullets; Fig. 4 in 逐图理解论文)
+ * -----------------------------------------------------------------------------------
+ * MiX codes: one nibble per element, element 2j in the low nibble of byte j; nibble =
+ *   (sign << 3) | dE, value (-1)^s (1 + m/8) 2^(Emax - dE); nibble 0x7 is zero and nibble 0xF is
+ *   +(1 + m/8) 2^(Emax - 7) (the reclaimed negative zero).
+ * MiX shared field per 32-element block: MIX_4P25 -> uint8, bits 3:0 = Emax + 7, bits 6:4 = m.
+ *   MIX_4P5 -> uint16, bits 3:0 = Emax + 7, then m0..m3 (one per 8-element sub-block) in bits
+ *   6:4, 9:7, 12:10, 15:13.
+ * MX codes: same nibble order; MX_FP4 nibbles are OCP E2M1, MX_INT4 nibbles are two's-complement
+ *   q with value q 2^(X - 2). MX scale per block: uint8 E8M0 = X + 127 (0 for an all-zero block).
+ */
+#ifndef MIXLIB_H
+#define MIXLIB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MIX_ABI_VERSION 1
+
+typedef enum {
+  MIX_OK = 0,
+  MIX_E_NULL = 1,        /* a required pointer is NULL */
+  MIX_E_SHAPE = 2,       /* negative extent, block axis not a multiple of 32, pitch < row length, ... */
+  MIX_E_ALIGN = 3,       /* pointer or pitch not 16-byte aligned */
+  MIX_E_ENUM = 4,        /* unknown format / dtype value */
+  MIX_E_UNSUPPORTED = 5, /* a valid but unimplemented combination */
+  MIX_E_HIP = 6,         /* a HIP call failed (launch error); see mix_last_error() */
+  MIX_E_WORKSPACE = 7    /* workspace smaller than the size the matching *_workspace_bytes returned */
+} mix_status_t;
+
+typedef enum { MIX_4P25 = 0, MIX_4P5 = 1 } mix_fmt_t; /* MiX-4.25b, MiX-4.5b */
+typedef enum { MX_INT4 = 0, MX_FP4 = 1 } mx_fmt_t;    /* MXINT4 (floor exponent), MXFP4 (ceil exponent) */
+typedef enum { MIX_F32 = 0, MIX_BF16 = 1 } mix_dtype_t;
+
+/* ABI version compiled into the library (MIX_ABI_VERSION). */
+int mix_abi_version(void);
+/* Static text for a status code. */
+const char* mix_status_str(mix_status_t status);
+/* Description of the last error on the calling thread ("" if none). The pointer stays valid until
+ * the next library call on this thread. */
+const char* mix_last_error(void);
+
+/*
+ * MiX activation quantizer -- P1, method overview, the Algorithm 1 bullet.
+ * Per 32-element block along each row: Emax = clamp(floor(log2 max|x|), -7, 8); the shared
+ * mantissa m = the top three fraction bits of the largest element's significand (of the block for
+ * MIX_4P25, of each 8-element sub-block for MIX_4P5); each element takes the nearest
+ * representable value (the naive dE = Emax - floor(log2|x|) refined by +-1), ties to the smaller
+ * magnitude. An all-zero block has shared field 0 and nibbles 0x7.
+ *   x       [rows, cols] fp32 or bf16 (dtype), row pitch ldx elements (ldx >= cols)
+ *   codes   [rows, cols/2] uint8, dense
+ *   shared  [rows, cols/32] uint8 (MIX_4P25) or uint16 (MIX_4P5), dense
+ */
+mix_status_t mix_quantize(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
+                          uint8_t* codes, void* shared, void* stream);
+
+/*
+ * MX weight quantizer -- P1, figure walk (Fig. 4: shared 8-bit exponent, 4-bit element) and key
+ * results (the MXFP4 bullet: the shared exponent uses ceil instead of OCP's floor).
+ * MX_FP4: X = ceil(log2 max|x|) - 2 (>= -127); elements x 2^-X rounded to nearest-even on the
+ *   E2M1 grid, sign of zero kept. MX_INT4: X = clamp(floor(log2 max|x|), -125, 127);
+ *   q = clamp(RNE(x 2^(2-X)), -7, 7).
+ * If mu != NULL the operand is fp32(x - mu[col]) (K-smoothing, P1 method overview last bullet).
+ *   x       [rows, cols] fp32 or bf16, row pitch ldx
+ *   mu      NULL or [cols] fp32
+ *   codes   [rows, cols/2] uint8; scales [rows, cols/32] uint8 (E8M0)
+ */
+mix_status_t mx_quantize(mx_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
+                         const float* mu, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * MXFP4 with blocks running down the columns (the V operand along tokens): block j of column c
+ * covers rows [32 j, 32 j + 32); rows at or beyond `rows` count as zero.
+ *   x       [rows, cols] fp32 or bf16, row pitch ldx
+ *   codes   [cols, prows/2], scales [cols, prows/32] where prows = rows rounded up to 32
+ */
+mix_status_t mx_quantize_cols(const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
+                              uint8_t* codes, uint8_t* scales, void* stream);
+
+/* Decoders (closed forms above) to fp32 [rows, cols]; for tests and inspection. */
+mix_status_t mix_dequantize(mix_fmt_t fmt, const uint8_t* codes, const void* shared, int64_t rows, int64_t cols,
+                            float* out, void* stream);
+mix_status_t mx_dequantize(mx_fmt_t fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                           float* out, void* stream);
+
+/*
+ * A-MiX x W-MX product -- P1, method overview, the dual-format bullet and Eq. (6).
+ * C = deq(A) . deq(B)^T with fp32 accumulation; fp32 output is the accumulator, bf16 output its
+ * round-to-nearest-even. Runs on the gfx950 block-scaled MFMA (E4M3 A x E2M1/E4M3 B with per-32
+ * power-of-two scales; every product is exact).
+ *   A: a_codes [M, K/2], a_shared [M, K/32] (uint8 or uint16 by a_fmt)
+ *   B: b_codes [N, K/2], b_scales [N, K/32]   (B holds W^T: one row per output column)
+ *   c  [M, N] fp32 or bf16 (c_dtype), row pitch ldc elements (ldc >= N)
+ */
+mix_status_t mix_mx_gemm(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, mx_fmt_t b_fmt,
+                         const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
+                         mix_dtype_t c_dtype, int64_t ldc, void* stream);
+
+/*
+ * The same product computed as P1's Eq. (6) on the vector ALUs: integer sub-block sums of the MX
+ * mantissas scaled by 2^(7 - dE), times (8 + m_k), one power-of-two scale per block, fp32
+ * accumulation across blocks. Same arguments and results (to fp32 rounding) as mix_mx_gemm.
+ */
+mix_status_t mix_mx_gemm_eq6(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, mx_fmt_t b_fmt,
+                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
+                             void* c, mix_dtype_t c_dtype, int64_t ldc, void* stream);
+
+/*
+ * Per-channel mean of the keys -- P1, method overview, last bullet (K-smoothing with the prefill
+ * mean frozen for decode). mu[c] = fp32(exact_sum_t k[t, c] / T), the division in fp64.
+ *   k  [T, C] fp32 or bf16 (C = kv_heads * head_dim), row pitch ldk
+ *   mu [C] fp32
+ */
+mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, int64_t ldk, float* mu, void* stream);
+
+/* Optional dumps of the attention stages (any pointer may be NULL). Shapes: prefill [Hq, T, Tp]
+ * for s/p, [Hq, T, Tp/2] p_codes, [Hq, T, Tp/32] p_shared, [Hq, T] l; decode [B, Hq, Lp] etc.
+ * (Tp, Lp = lengths rounded up to 32). Entries above the causal diagonal or past the sequence are
+ * not written for s. */
+typedef struct {
+  float* s;
+  float* p;
+  uint8_t* p_codes;
+  uint16_t* p_shared;
+  float* l;
+} mix_attn_debug_t;
+
+/*
+ * K-smoothed prefill attention -- P1, method overview (last bullet), innovations (third bullet:
+ * the attention products are coded too). Operand formats: Q and P as MiX-4.5b (blocks along the
+ * head dimension and along keys), smoothed K and V as MXFP4 (blocks along the head dimension and
+ * along tokens).
+ *   1. mu = K-mean over the T tokens (written to `mu`, [Hkv, d], for decode)
+ *   2. K^ = MXFP4(fp32(K - mu)), Q^ = MiX-4.5b(Q), V^ = MXFP4 along tokens
+ *   3. S = Q^ K^T per query head (head h reads KV head h / (Hq / Hkv)), causal if `causal`
+ *   4. z = fp32(S) * fp32(1/sqrt(d)); m = row max over unmasked keys; p = exp(z - m);
+ *      l = sum of p; P^ = MiX-4.5b(p) along keys
+ *   5. O = bf16((P^ V^) / l)
+ *   q [T, Hq, d], k/v [T, Hkv, d] bf16, dense;  o [T, Hq, d] bf16;  mu [Hkv, d] fp32 (output)
+ *   ws: workspace of at least mix_attn_prefill_workspace_bytes(T, Hq, Hkv, d) bytes, 256-B aligned
+ * Requires d % 32 == 0 and Hq % Hkv == 0; T may be ragged.
+ */
+size_t mix_attn_prefill_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t d);
+mix_status_t mix_attn_prefill(const void* q, const void* k, const void* v, int64_t T, int64_t Hq, int64_t Hkv,
+                              int64_t d, int causal, float* mu, void* o, void* ws, size_t ws_bytes,
+                              const mix_attn_debug_t* dbg, void* stream);
+
+/*
+ * MX-coded KV cache for decode (caller-owned device buffers; all dense, head-major):
+ *   k_codes  [B, Hkv, Lmax, d/2]   MXFP4 of fp32(k - mu_b) along d
+ *   k_scales [B, Hkv, Lmax, d/32]
+ *   v_codes  [B, Hkv, d, Lmax/2]   MXFP4 along tokens: block j covers tokens [32 j, 32 j + 32)
+ *   v_scales [B, Hkv, d, Lmax/32]
+ *   v_stage  [B, 32, Hkv, d] bf16  the tokens of each row's current (possibly partial) V block
+ * Lmax % 32 == 0, d % 32 == 0. The block that holds the newest token is always coded from the
+ * staged tokens present, the others zero (P1 leaves partial blocks open; see the design notes).
+ */
+typedef struct {
+  uint8_t* k_codes;
+  uint8_t* k_scales;
+  uint8_t* v_codes;
+  uint8_t* v_scales;
+  void* v_stage;
+  int64_t B, Lmax, Hkv, d;
+} mix_kv_cache_t;
+
+/*
+ * Fill row b of the cache from a prefill of T tokens (k/v [T, Hkv, d] bf16 dense) with the frozen
+ * mean mu [Hkv, d] fp32 (P1 method overview last bullet: the prefill mean is reused, so cached
+ * keys are never re-coded). 0 < T <= Lmax.
+ */
+mix_status_t mix_kv_cache_prefill(const mix_kv_cache_t* cache, int64_t b, const void* k, const void* v, int64_t T,
+                                  const float* mu, void* stream);
+
+/*
+ * One decode step for B sequences: append k_new/v_new [B, Hkv, d] bf16 at position pos[b]
+ * (device int32 [B]), then attend q [B, Hq, d] bf16 over keys [0, pos[b]] with no causal mask,
+ * using the frozen mean mu [B, Hkv, d] fp32; o [B, Hq, d] bf16. Same operand formats and softmax
+ * as prefill. `max_pos` (host) bounds every pos[b] (0 <= pos[b] <= max_pos < Lmax); rows whose pos
+ * is outside [0, max_pos] write zeros to o and leave the cache untouched.
+ *   ws: at least mix_attn_decode_workspace_bytes(B, Hq, Hkv, d, max_pos) bytes, 256-B aligned
+ */
+size_t mix_attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos);
+mix_status_t mix_attn_decode(const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* cache,
+                             const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
+                             size_t ws_bytes, const mix_attn_debug_t* dbg, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIXLIB_H */

@@ -1,1 +1,247 @@
-"""MiX (Micro-Inverted-Scaling) hot path on MI355X: Python binding over the HIP C-ABI library."""
+"""MiX (Micro-Inverted-Scaling) hot path on MI355X -- Python binding over the HIP C-ABI (libmix.so).
+
+Every function here only marshals arguments: it allocates outputs with torch on the input's
+device, passes raw device pointers and torch's current stream to the C entry point of the same
+name, and raises ``MixError`` on a non-zero status. All arithmetic runs in the HIP kernels. There
+is no CPU fallback: without a built ``libmix.so`` every call raises.
+
+Format names: MiX ``"4.25b"`` / ``"4.5b"``; MX ``"int4"`` / ``"fp4"``. bf16 inputs are
+``torch.bfloat16`` tensors; MiX-4.5b shared fields come back as ``torch.int16`` holding the uint16
+bit patterns.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import MixError, check
+
+MIX_FMT = {"4.25b": 0, "4.5b": 1}
+MX_FMT = {"int4": 0, "fp4": 1}
+DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+
+__all__ = [
+    "MixError", "mix_quantize", "mx_quantize", "mx_quantize_cols", "mix_dequantize", "mx_dequantize",
+    "mix_mx_gemm", "mix_mx_gemm_eq6", "mix_kmean", "mix_attn_prefill", "KVCache", "mix_kv_cache_prefill",
+    "mix_attn_decode", "abi_version",
+]
+
+
+def _lib_():
+    return _lib.load()
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise MixError("libmix works on device tensors only (got a CPU tensor)")
+
+
+def _matrix(x, name):
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise MixError(f"{name} must be a 2-D tensor with unit column stride")
+    if x.dtype not in DTYPE:
+        raise MixError(f"{name} must be float32 or bfloat16")
+    return x.shape[0], x.shape[1], x.stride(0)
+
+
+def abi_version():
+    return _lib_().mix_abi_version()
+
+
+def mix_quantize(x, fmt="4.5b"):
+    """MiX-quantize rows of x [rows, cols]. Returns (codes uint8 [rows, cols/2], shared [rows, cols/32])."""
+    _need_cuda(x)
+    rows, cols, ld = _matrix(x, "x")
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    shared = torch.empty((rows, cols // 32), dtype=torch.uint8 if fmt == "4.25b" else torch.int16, device=x.device)
+    check(_lib_().mix_quantize(MIX_FMT[fmt], _p(x), DTYPE[x.dtype], rows, cols, ld, _p(codes), _p(shared), _stream()),
+          "mix_quantize")
+    return codes, shared
+
+
+def mx_quantize(x, fmt="fp4", mu=None):
+    """MX-quantize rows of x [rows, cols] (optionally fp32(x - mu)). Returns (codes, scales uint8)."""
+    _need_cuda(x, mu)
+    rows, cols, ld = _matrix(x, "x")
+    if mu is not None and (mu.dtype != torch.float32 or mu.numel() != cols or not mu.is_contiguous()):
+        raise MixError("mu must be a contiguous float32 tensor with one value per column")
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    check(_lib_().mx_quantize(MX_FMT[fmt], _p(x), DTYPE[x.dtype], rows, cols, ld, _p(mu), _p(codes), _p(scales),
+                              _stream()), "mx_quantize")
+    return codes, scales
+
+
+def mx_quantize_cols(x):
+    """MXFP4 with 32-row blocks down each column of x [rows, cols]. Returns codes [cols, prows/2], scales."""
+    _need_cuda(x)
+    rows, cols, ld = _matrix(x, "x")
+    prows = (rows + 31) // 32 * 32
+    codes = torch.empty((cols, prows // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((cols, prows // 32), dtype=torch.uint8, device=x.device)
+    check(_lib_().mx_quantize_cols(_p(x), DTYPE[x.dtype], rows, cols, ld, _p(codes), _p(scales), _stream()),
+          "mx_quantize_cols")
+    return codes, scales
+
+
+def mix_dequantize(codes, shared, fmt="4.5b"):
+    _need_cuda(codes, shared)
+    rows, cols = codes.shape[0], codes.shape[1] * 2
+    out = torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
+    check(_lib_().mix_dequantize(MIX_FMT[fmt], _p(codes), _p(shared), rows, cols, _p(out), _stream()), "mix_dequantize")
+    return out
+
+
+def mx_dequantize(codes, scales, fmt="fp4"):
+    _need_cuda(codes, scales)
+    rows, cols = codes.shape[0], codes.shape[1] * 2
+    out = torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
+    check(_lib_().mx_dequantize(MX_FMT[fmt], _p(codes), _p(scales), rows, cols, _p(out), _stream()), "mx_dequantize")
+    return out
+
+
+def _gemm(name, a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype, out):
+    _need_cuda(a_codes, a_shared, b_codes, b_scales, out)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = b_codes.shape[0]
+    if b_codes.shape[1] * 2 != K:
+        raise MixError("A and B disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    check(getattr(_lib_(), name)(MIX_FMT[a_fmt], _p(a_codes), _p(a_shared), MX_FMT[b_fmt], _p(b_codes), _p(b_scales),
+                                 M, N, K, _p(out), DTYPE[out.dtype], out.stride(0), _stream()), name)
+    return out
+
+
+def mix_mx_gemm(a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype=torch.float32, out=None):
+    """C = deq(A) . deq(B)^T on the block-scaled MFMA. A: MiX [M, K]; B: MX [N, K] (W^T)."""
+    return _gemm("mix_mx_gemm", a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype, out)
+
+
+def mix_mx_gemm_eq6(a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype=torch.float32, out=None):
+    """The same product by Eq. (6) integer shift-add on the vector ALUs."""
+    return _gemm("mix_mx_gemm_eq6", a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype, out)
+
+
+def mix_kmean(k):
+    """Per-column mean of k [T, C] (exact sum, fp64 division, fp32 result)."""
+    _need_cuda(k)
+    T, C, ld = _matrix(k, "k")
+    mu = torch.empty((C,), dtype=torch.float32, device=k.device)
+    check(_lib_().mix_kmean(_p(k), DTYPE[k.dtype], T, C, ld, _p(mu), _stream()), "mix_kmean")
+    return mu
+
+
+# ---------------------------------------------------------------- attention
+
+
+class _Debug(ctypes.Structure):
+    _fields_ = [("s", ctypes.c_void_p), ("p", ctypes.c_void_p), ("p_codes", ctypes.c_void_p),
+                ("p_shared", ctypes.c_void_p), ("l", ctypes.c_void_p)]
+
+
+def _debug_struct(d):
+    if d is None:
+        return None, None
+    st = _Debug(*(None if d.get(k) is None else d[k].data_ptr() for k in ("s", "p", "p_codes", "p_shared", "l")))
+    return st, ctypes.byref(st)
+
+
+def mix_attn_prefill(q, k, v, causal=True, debug=False, workspace=None):
+    """K-smoothed MiX/MX attention prefill. q [T, Hq, d], k/v [T, Hkv, d] bf16.
+
+    Returns (o bf16 [T, Hq, d], mu fp32 [Hkv, d], dbg dict or None). With ``debug`` the dict holds
+    s / p (fp32 [Hq, T, Tp]), p_codes, p_shared and l from inside the call.
+    """
+    _need_cuda(q, k, v)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise MixError("q, k, v must be contiguous bfloat16")
+    lib = _lib_()
+    wsb = lib.mix_attn_prefill_workspace_bytes(T, Hq, Hkv, d)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=q.device)
+    o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=q.device)
+    mu = torch.empty((Hkv, d), dtype=torch.float32, device=q.device)
+    dbg = None
+    if debug:
+        Tp = (T + 31) // 32 * 32
+        dev = q.device
+        dbg = {"s": torch.zeros((Hq, T, Tp), dtype=torch.float32, device=dev),
+               "p": torch.zeros((Hq, T, Tp), dtype=torch.float32, device=dev),
+               "p_codes": torch.empty((Hq, T, Tp // 2), dtype=torch.uint8, device=dev),
+               "p_shared": torch.empty((Hq, T, Tp // 32), dtype=torch.int16, device=dev),
+               "l": torch.empty((Hq, T), dtype=torch.float32, device=dev)}
+    st, ref = _debug_struct(dbg)
+    check(lib.mix_attn_prefill(_p(q), _p(k), _p(v), T, Hq, Hkv, d, int(bool(causal)), _p(mu), _p(o), _p(workspace),
+                               workspace.numel(), ref, _stream()), "mix_attn_prefill")
+    return o, mu, dbg
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("v_scales", ctypes.c_void_p), ("v_stage", ctypes.c_void_p), ("B", ctypes.c_int64),
+                ("Lmax", ctypes.c_int64), ("Hkv", ctypes.c_int64), ("d", ctypes.c_int64)]
+
+
+class KVCache:
+    """Device buffers of an MX-coded KV cache (layouts as in mixlib.h), allocated with torch."""
+
+    def __init__(self, B, Lmax, Hkv, d, device="cuda"):
+        if Lmax % 32 or d % 32:
+            raise MixError("Lmax and d must be multiples of 32")
+        self.B, self.Lmax, self.Hkv, self.d = B, Lmax, Hkv, d
+        self.k_codes = torch.zeros((B, Hkv, Lmax, d // 2), dtype=torch.uint8, device=device)
+        self.k_scales = torch.zeros((B, Hkv, Lmax, d // 32), dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros((B, Hkv, d, Lmax // 2), dtype=torch.uint8, device=device)
+        self.v_scales = torch.zeros((B, Hkv, d, Lmax // 32), dtype=torch.uint8, device=device)
+        self.v_stage = torch.zeros((B, 32, Hkv, d), dtype=torch.bfloat16, device=device)
+        self._st = _Cache(self.k_codes.data_ptr(), self.k_scales.data_ptr(), self.v_codes.data_ptr(),
+                          self.v_scales.data_ptr(), self.v_stage.data_ptr(), B, Lmax, Hkv, d)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._st)
+
+
+def mix_kv_cache_prefill(cache, b, k, v, mu):
+    """Write a prefill of T tokens (k/v [T, Hkv, d] bf16) into row b of the cache with frozen mean mu."""
+    _need_cuda(k, v, mu)
+    T = k.shape[0]
+    check(_lib_().mix_kv_cache_prefill(cache.ref, b, _p(k), _p(v), T, _p(mu), _stream()), "mix_kv_cache_prefill")
+
+
+def mix_attn_decode(q, k_new, v_new, cache, pos, max_pos, mu, debug=False, workspace=None):
+    """One decode step. q [B, Hq, d], k_new/v_new [B, Hkv, d] bf16; pos int32 [B] (device);
+    mu fp32 [B, Hkv, d]. Returns (o bf16 [B, Hq, d], dbg dict or None)."""
+    _need_cuda(q, k_new, v_new, pos, mu)
+    B, Hq, d = q.shape
+    lib = _lib_()
+    wsb = lib.mix_attn_decode_workspace_bytes(B, Hq, cache.Hkv, d, max_pos)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=q.device)
+    o = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
+    dbg = None
+    if debug:
+        Lp = (max_pos + 1 + 31) // 32 * 32
+        dev = q.device
+        dbg = {"s": torch.zeros((B, Hq, Lp), dtype=torch.float32, device=dev),
+               "p": torch.zeros((B, Hq, Lp), dtype=torch.float32, device=dev),
+               "p_codes": torch.empty((B, Hq, Lp // 2), dtype=torch.uint8, device=dev),
+               "p_shared": torch.empty((B, Hq, Lp // 32), dtype=torch.int16, device=dev),
+               "l": torch.empty((B, Hq), dtype=torch.float32, device=dev)}
+    st, ref = _debug_struct(dbg)
+    check(lib.mix_attn_decode(_p(q), _p(k_new), _p(v_new), cache.ref, _p(pos), max_pos, Hq, _p(mu), _p(o),
+                              _p(workspace), workspace.numel(), ref, _stream()), "mix_attn_decode")
+    return o, dbg

@@ -1,0 +1,217 @@
+// C-ABI of the MiX library: argument validation on the host, then kernel dispatch on the caller's
+// stream. Nothing here allocates, frees or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/mixlib.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+mix_status_t fail(mix_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+mix_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MIX_OK;
+  return fail(MIX_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline int dtype_size(int dt) { return dt == MIX_BF16 ? 2 : 4; }
+
+mix_status_t check_dtype(int dt) {
+  if (dt != MIX_F32 && dt != MIX_BF16) return fail(MIX_E_ENUM, "unknown dtype %d", dt);
+  return MIX_OK;
+}
+
+// Common checks for a [rows, cols] input with blocks along cols. Sets *empty for zero extents.
+mix_status_t check_matrix_in(const char* fn, const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx,
+                             bool* empty) {
+  *empty = false;
+  if (rows < 0 || cols < 0) return fail(MIX_E_SHAPE, "%s: negative extent (rows=%lld cols=%lld)", fn, (long long)rows, (long long)cols);
+  if (cols % 32) return fail(MIX_E_SHAPE, "%s: cols=%lld is not a multiple of 32", fn, (long long)cols);
+  if (rows == 0 || cols == 0) { *empty = true; return MIX_OK; }
+  if (ldx < cols) return fail(MIX_E_SHAPE, "%s: ldx=%lld < cols=%lld", fn, (long long)ldx, (long long)cols);
+  if (!x) return fail(MIX_E_NULL, "%s: x is NULL", fn);
+  if (!aligned16(x) || (ldx * dtype_size(dt)) % 16) return fail(MIX_E_ALIGN, "%s: x or its row pitch is not 16-byte aligned", fn);
+  return MIX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mix_abi_version(void) { return MIX_ABI_VERSION; }
+
+const char* mix_status_str(mix_status_t s) {
+  switch (s) {
+    case MIX_OK: return "ok";
+    case MIX_E_NULL: return "null pointer";
+    case MIX_E_SHAPE: return "bad shape";
+    case MIX_E_ALIGN: return "misaligned pointer or pitch";
+    case MIX_E_ENUM: return "unknown enum value";
+    case MIX_E_UNSUPPORTED: return "unsupported combination";
+    case MIX_E_HIP: return "HIP error";
+    case MIX_E_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+const char* mix_last_error(void) { return g_err.c_str(); }
+
+mix_status_t mix_quantize(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
+                          uint8_t* codes, void* shared, void* stream) {
+  g_err.clear();
+  if (fmt != MIX_4P25 && fmt != MIX_4P5) return fail(MIX_E_ENUM, "mix_quantize: unknown MiX format %d", (int)fmt);
+  if (mix_status_t st = check_dtype(dtype)) return st;
+  bool empty;
+  if (mix_status_t st = check_matrix_in("mix_quantize", x, dtype, rows, cols, ldx, &empty)) return st;
+  if (empty) return MIX_OK;
+  if (!codes || !shared) return fail(MIX_E_NULL, "mix_quantize: codes or shared is NULL");
+  if (!aligned16(codes) || ((uintptr_t)shared & 1u)) return fail(MIX_E_ALIGN, "mix_quantize: codes not 16-byte aligned or shared not 2-byte aligned");
+  return hip_status(mix::launch_mix_quantize((int)fmt, x, (int)dtype, rows, cols, ldx, codes, shared, (hipStream_t)stream),
+                    "mix_quantize launch");
+}
+
+mix_status_t mx_quantize(mx_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
+                         const float* mu, uint8_t* codes, uint8_t* scales, void* stream) {
+  g_err.clear();
+  if (fmt != MX_INT4 && fmt != MX_FP4) return fail(MIX_E_ENUM, "mx_quantize: unknown MX format %d", (int)fmt);
+  if (mix_status_t st = check_dtype(dtype)) return st;
+  bool empty;
+  if (mix_status_t st = check_matrix_in("mx_quantize", x, dtype, rows, cols, ldx, &empty)) return st;
+  if (empty) return MIX_OK;
+  if (!codes || !scales) return fail(MIX_E_NULL, "mx_quantize: codes or scales is NULL");
+  if (!aligned16(codes) || (mu && !aligned16(mu))) return fail(MIX_E_ALIGN, "mx_quantize: codes or mu not 16-byte aligned");
+  return hip_status(mix::launch_mx_quantize(fmt == MX_FP4, x, (int)dtype, rows, cols, ldx, mu, codes, scales,
+                                            (hipStream_t)stream),
+                    "mx_quantize launch");
+}
+
+mix_status_t mx_quantize_cols(const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
+                              uint8_t* codes, uint8_t* scales, void* stream) {
+  g_err.clear();
+  if (mix_status_t st = check_dtype(dtype)) return st;
+  if (rows < 0 || cols < 0) return fail(MIX_E_SHAPE, "mx_quantize_cols: negative extent");
+  if (rows == 0 || cols == 0) return MIX_OK;
+  if (ldx < cols) return fail(MIX_E_SHAPE, "mx_quantize_cols: ldx < cols");
+  if (!x || !codes || !scales) return fail(MIX_E_NULL, "mx_quantize_cols: NULL pointer");
+  if (!aligned16(codes)) return fail(MIX_E_ALIGN, "mx_quantize_cols: codes not 16-byte aligned");
+  if ((uintptr_t)x % dtype_size(dtype)) return fail(MIX_E_ALIGN, "mx_quantize_cols: x misaligned");
+  int64_t prows = (rows + 31) / 32 * 32;
+  if (prows / 32 > 65535) return fail(MIX_E_SHAPE, "mx_quantize_cols: rows too large");
+  return hip_status(mix::launch_mx_quantize_cols(x, (int)dtype, rows, prows, cols, ldx, codes, scales, (hipStream_t)stream),
+                    "mx_quantize_cols launch");
+}
+
+mix_status_t mix_dequantize(mix_fmt_t fmt, const uint8_t* codes, const void* shared, int64_t rows, int64_t cols,
+                            float* out, void* stream) {
+  g_err.clear();
+  if (fmt != MIX_4P25 && fmt != MIX_4P5) return fail(MIX_E_ENUM, "mix_dequantize: unknown MiX format %d", (int)fmt);
+  if (rows < 0 || cols < 0 || cols % 32) return fail(MIX_E_SHAPE, "mix_dequantize: bad shape");
+  if (rows == 0 || cols == 0) return MIX_OK;
+  if (!codes || !shared || !out) return fail(MIX_E_NULL, "mix_dequantize: NULL pointer");
+  if (fmt == MIX_4P5 && ((uintptr_t)shared & 1u)) return fail(MIX_E_ALIGN, "mix_dequantize: shared misaligned");
+  return hip_status(mix::launch_mix_dequantize((int)fmt, codes, shared, rows, cols, out, (hipStream_t)stream),
+                    "mix_dequantize launch");
+}
+
+mix_status_t mx_dequantize(mx_fmt_t fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                           float* out, void* stream) {
+  g_err.clear();
+  if (fmt != MX_INT4 && fmt != MX_FP4) return fail(MIX_E_ENUM, "mx_dequantize: unknown MX format %d", (int)fmt);
+  if (rows < 0 || cols < 0 || cols % 32) return fail(MIX_E_SHAPE, "mx_dequantize: bad shape");
+  if (rows == 0 || cols == 0) return MIX_OK;
+  if (!codes || !scales || !out) return fail(MIX_E_NULL, "mx_dequantize: NULL pointer");
+  return hip_status(mix::launch_mx_dequantize(fmt == MX_FP4, codes, scales, rows, cols, out, (hipStream_t)stream),
+                    "mx_dequantize launch");
+}
+
+static mix_status_t gemm_common(const char* fn, bool eq6, mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared,
+                                mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
+                                int64_t K, void* c, mix_dtype_t c_dtype, int64_t ldc, void* stream) {
+  g_err.clear();
+  if (a_fmt != MIX_4P25 && a_fmt != MIX_4P5) return fail(MIX_E_ENUM, "%s: unknown MiX format %d", fn, (int)a_fmt);
+  if (b_fmt != MX_INT4 && b_fmt != MX_FP4) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (mix_status_t st = check_dtype(c_dtype)) return st;
+  if (M < 0 || N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
+  if (K % 32) return fail(MIX_E_SHAPE, "%s: K=%lld is not a multiple of 32", fn, (long long)K);
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(MIX_E_SHAPE, "%s: extent above 2^31-1", fn);
+  if (M == 0 || N == 0) return MIX_OK;
+  if (ldc < N) return fail(MIX_E_SHAPE, "%s: ldc=%lld < N=%lld", fn, (long long)ldc, (long long)N);
+  if (!c) return fail(MIX_E_NULL, "%s: c is NULL", fn);
+  if (K > 0 && (!a_codes || !a_shared || !b_codes || !b_scales)) return fail(MIX_E_NULL, "%s: operand pointer is NULL", fn);
+  if (K > 0 && (!aligned16(a_codes) || !aligned16(b_codes))) return fail(MIX_E_ALIGN, "%s: code buffers must be 16-byte aligned", fn);
+  if (K > 0 && a_fmt == MIX_4P5 && ((uintptr_t)a_shared & 1u)) return fail(MIX_E_ALIGN, "%s: a_shared misaligned", fn);
+  if ((uintptr_t)c % dtype_size(c_dtype)) return fail(MIX_E_ALIGN, "%s: c misaligned", fn);
+  int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  if (tiles > INT32_MAX) return fail(MIX_E_SHAPE, "%s: too many tiles", fn);
+  mix::GemmArgs g{};
+  g.a_codes = a_codes; g.a_shared = a_shared; g.a_pitch = K / 2; g.a_sh_pitch = K / 32;
+  g.b_codes = b_codes; g.b_scales = b_scales; g.b_pitch = K / 2; g.b_sc_pitch = K / 32; g.b_group = 1;
+  g.c = c; g.ldc = ldc; g.row_div = nullptr;
+  g.M = (int)M; g.N = (int)N; g.K = (int)K; g.batch = 1; g.causal = 0;
+  hipError_t e = eq6 ? mix::launch_gemm_eq6(a_fmt == MIX_4P5, b_fmt == MX_FP4, c_dtype == MIX_BF16, g, (hipStream_t)stream)
+                     : mix::launch_gemm_mfma(a_fmt == MIX_4P5, b_fmt == MX_FP4, c_dtype == MIX_BF16, g, (hipStream_t)stream);
+  return hip_status(e, eq6 ? "mix_mx_gemm_eq6 launch" : "mix_mx_gemm launch");
+}
+
+mix_status_t mix_mx_gemm(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, mx_fmt_t b_fmt,
+                         const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
+                         mix_dtype_t c_dtype, int64_t ldc, void* stream) {
+  return gemm_common("mix_mx_gemm", false, a_fmt, a_codes, a_shared, b_fmt, b_codes, b_scales, M, N, K, c, c_dtype, ldc,
+                     stream);
+}
+
+mix_status_t mix_mx_gemm_eq6(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, mx_fmt_t b_fmt,
+                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
+                             void* c, mix_dtype_t c_dtype, int64_t ldc, void* stream) {
+  return gemm_common("mix_mx_gemm_eq6", true, a_fmt, a_codes, a_shared, b_fmt, b_codes, b_scales, M, N, K, c, c_dtype,
+                     ldc, stream);
+}
+
+mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, int64_t ldk, float* mu, void* stream) {
+  g_err.clear();
+  if (mix_status_t st = check_dtype(dtype)) return st;
+  if (T < 0 || C < 0) return fail(MIX_E_SHAPE, "mix_kmean: negative extent");
+  if (C == 0) return MIX_OK;
+  if (T == 0) return fail(MIX_E_SHAPE, "mix_kmean: the mean of zero tokens is undefined");
+  if (ldk < C) return fail(MIX_E_SHAPE, "mix_kmean: ldk < C");
+  if (!k || !mu) return fail(MIX_E_NULL, "mix_kmean: NULL pointer");
+  if ((uintptr_t)k % dtype_size(dtype)) return fail(MIX_E_ALIGN, "mix_kmean: k misaligned");
+  return hip_status(mix::launch_kmean(k, (int)dtype, T, C, ldk, mu, (hipStream_t)stream), "mix_kmean launch");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- attention (stubs until implemented)
+extern "C" {
+size_t mix_attn_prefill_workspace_bytes(int64_t, int64_t, int64_t, int64_t) { return 0; }
+mix_status_t mix_attn_prefill(const void*, const void*, const void*, int64_t, int64_t, int64_t, int64_t, int, float*,
+                              void*, void*, size_t, const mix_attn_debug_t*, void*) {
+  g_err = "mix_attn_prefill: not implemented";
+  return MIX_E_UNSUPPORTED;
+}
+mix_status_t mix_kv_cache_prefill(const mix_kv_cache_t*, int64_t, const void*, const void*, int64_t, const float*,
+                                  void*) {
+  g_err = "mix_kv_cache_prefill: not implemented";
+  return MIX_E_UNSUPPORTED;
+}
+size_t mix_attn_decode_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int64_t) { return 0; }
+mix_status_t mix_attn_decode(const void*, const void*, const void*, const mix_kv_cache_t*, const int32_t*, int64_t,
+                             int64_t, const float*, void*, void*, size_t, const mix_attn_debug_t*, void*) {
+  g_err = "mix_attn_decode: not implemented";
+  return MIX_E_UNSUPPORTED;
+}
+}

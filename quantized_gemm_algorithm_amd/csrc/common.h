@@ -1,0 +1,75 @@
+// Device helpers shared by the MiX HIP kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mix {
+
+// ------------------------------------------------------------------ bit helpers
+
+__device__ __forceinline__ uint32_t f32_bits(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float bits_f32(uint32_t u) { return __uint_as_float(u); }
+
+// bf16 pattern -> exact fp32 bits
+__device__ __forceinline__ uint32_t bf16_to_f32_bits(uint32_t b16) { return b16 << 16; }
+
+// fp32 -> bf16 round-to-nearest-even (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Exact fp32 bit pattern of k * 2^e for 1 <= k < 2^24 (normal or subnormal result; e >= -149 - bits).
+__device__ __forceinline__ uint32_t exact_f32_bits(uint32_t k, int e) {
+  int nb = 31 - __builtin_clz(k);  // index of the leading one
+  int ex = e + nb;                  // unbiased exponent of the value
+  if (ex >= -126) {
+    uint32_t mant = (nb <= 23) ? ((k << (23 - nb)) & 0x7FFFFFu) : ((k >> (nb - 23)) & 0x7FFFFFu);
+    return ((uint32_t)(ex + 127) << 23) | mant;
+  }
+  int sh = e + 149;  // subnormal: value = k * 2^e = (k << sh) * 2^-149
+  return sh >= 0 ? (k << sh) : (k >> (-sh));
+}
+
+// Top three fraction bits of the significand of a non-negative float given by its bits
+// (subnormals are normalised first; zero gives 0).
+__device__ __forceinline__ uint32_t mant3_of(uint32_t a) {
+  if (a == 0) return 0;
+  uint32_t e = a >> 23;
+  uint32_t m = a & 0x7FFFFFu;
+  if (e == 0) {
+    int sh = __builtin_clz(m) - 8;  // move the leading one to bit 23
+    m = (m << sh) & 0x7FFFFFu;
+  }
+  return m >> 20;
+}
+
+// ------------------------------------------------------------------ cross-lane reductions (DPP)
+
+// max over the 4 lanes of a quad (lanes 4q..4q+3), unsigned
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  v = v > t ? v : t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  return v > t ? v : t;
+}
+
+// bitwise OR over the 4 lanes of a quad
+__device__ __forceinline__ uint32_t quad_or_u32(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+  return v;
+}
+
+// full-wave reductions through ds_swizzle / bpermute (64 lanes)
+__device__ __forceinline__ float wave_max_f32(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace mix

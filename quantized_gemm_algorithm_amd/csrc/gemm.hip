@@ -1,0 +1,408 @@
+// A-MiX x W-MX matrix product for gfx950.
+//
+// The method (P1, 方法概览 / method overview, the dual-format bullet and Eq. (6)): activations are
+// MiX-coded and weights MX-coded; in each 32-element block dot product the shared MiX mantissa
+// and the exponents factor out, leaving per-element shifts of the MX mantissa.
+//
+// Two kernels compute the same product:
+//
+// * k_gemm_mfma -- the MI355X path. Each MiX element (1.m)_2 2^(Emax-dE) is written, exactly, as
+//   the E4M3 byte (1.m)_2 2^(1-dE) times a per-block power of two 2^(Emax-1); 4 significant bits
+//   over 8 binades fit E4M3 without rounding. MXFP4 elements are already E2M1; MXINT4 elements q
+//   become the E4M3 byte of q/4. The per-32 powers of two (2^(Emax-1) for A, the E8M0 exponent for
+//   B) are exactly the block scales of the gfx950 block-scaled MFMA
+//   (v_mfma_scale_f32_16x16x128_f8f6f4), so every product is exact and the MFMA accumulates in
+//   fp32. Codes are decoded into LDS once per workgroup tile.
+// * k_gemm_eq6 -- Eq. (6) on the vector ALUs: per 8-element sub-block an integer sum
+//   T_k = sum s_i Wint_i 2^(7-dE_i), then blk = sum_k (8+m_k) T_k and one exact power-of-two
+//   scale 2^(Emax+X-10-c_w) per block, accumulated in fp32. (The power-of-two factor is applied
+//   with an integer multiply-add, the vector-ALU form of the shifter.)
+//
+// Operand layout of v_mfma_scale_f32_16x16x128_f8f6f4 (established on the device): lane
+// l = r + 16 g (r < 16, g < 4) supplies row/column r; an FP4 operand holds K elements
+// [32 g, 32 g + 32) of that row in 16 bytes, low nibble first; an FP8 operand holds elements
+// [16 g, 16 g + 16) in bytes 0..15 and [64 + 16 g, 64 + 16 g + 16) in bytes 16..31; the scale
+// operand of lane l is the E8M0 scale of row/column r for K block g. Result register i of lane l
+// is C[4 (l >> 4) + i][l & 15].
+#include "common.h"
+#include "kernels.h"
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+namespace mix {
+
+// ------------------------------------------------------------------ code -> E4M3 decoders
+
+// 8 MiX nibbles (element e at bits 4e) with shared mantissa m -> 8 E4M3 bytes in element order.
+// byte = s<<7 | (8-dE)<<3 | m; nibble 0x7 (zero) -> 0x00; nibble 0xF -> (1<<3) | m.
+__device__ __forceinline__ void mix8_to_e4m3(uint32_t w, uint32_t m, uint32_t& out0, uint32_t& out1) {
+  const uint32_t m4 = m * 0x01010101u;
+  uint32_t r[2];
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    uint32_t x = (w >> (4 * h)) & 0x0F0F0F0Fu;  // h=0: elements 0,2,4,6; h=1: 1,3,5,7
+    uint32_t d = x & 0x07070707u;
+    uint32_t s = x & 0x08080808u;
+    uint32_t v = (0x40404040u - (d << 3)) | (s << 4) | m4;
+    uint32_t d7 = (d + 0x01010101u) & 0x08080808u;  // 0x08 in bytes with dE == 7
+    v &= ~(d7 << 4);                                // reclaimed pattern: positive
+    uint32_t z = d7 & ~s;                           // dE == 7 with sign 0: zero
+    v &= ~((z >> 3) * 0xFFu);
+    r[h] = v;
+  }
+  out0 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);
+  out1 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);
+}
+
+// 8 MXINT4 nibbles -> 8 E4M3 bytes of q/4 (q two's complement in [-8, 7]).
+__device__ __forceinline__ void int4x8_to_e4m3(uint32_t w, uint32_t& out0, uint32_t& out1) {
+  const uint32_t lo0 = 0x34302800u, lo1 = 0x3E3C3A38u;  // q = 0..7
+  const uint32_t hi0 = 0xBABCBEC0u, hi1 = 0xA8B0B4B8u;  // q = -8..-1
+  uint32_t r[2];
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    uint32_t x = (w >> (4 * h)) & 0x0F0F0F0Fu;
+    uint32_t sel = x & 0x07070707u;
+    uint32_t a = __builtin_amdgcn_perm(lo1, lo0, sel);
+    uint32_t b = __builtin_amdgcn_perm(hi1, hi0, sel);
+    uint32_t msk = ((x & 0x08080808u) >> 3) * 0xFFu;
+    r[h] = (a & ~msk) | (b & msk);
+  }
+  out0 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);
+  out1 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);
+}
+
+// ------------------------------------------------------------------ MFMA kernel
+
+constexpr int BM = 128, BN = 128, BK = 128;
+
+template <int A_FMT, int B_FP4>
+struct TileRegs {
+  uint4 a[2];      // 32 MiX code bytes (2 blocks) of this thread's A row
+  uint32_t a_sh[2];
+  uint4 b[2];      // 32 MX code bytes of this thread's B row
+  uint32_t b_sc[2];
+};
+
+// Thread t loads row t >> 1, blocks 2 (t & 1) and 2 (t & 1) + 1 of the K step, for A and B.
+template <int A_FMT, int B_FP4>
+__device__ __forceinline__ void load_tile(const GemmArgs& g, const uint8_t* ab, const void* ash, const uint8_t* bb,
+                                          const uint8_t* bsc, int m0, int n0, int k0, TileRegs<A_FMT, B_FP4>& R) {
+  const int t = threadIdx.x;
+  const int row = t >> 1, hb = t & 1;
+  const int nkb = g.K >> 5;
+  const int gm = m0 + row, gn = n0 + row;
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    int gb = (k0 >> 5) + 2 * hb + q;
+    bool ka = gm < g.M && gb < nkb;
+    bool kb = gn < g.N && gb < nkb;
+    R.a[q] = ka ? *(const uint4*)(ab + (int64_t)gm * g.a_pitch + (int64_t)gb * 16) : make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
+    if (A_FMT == 1) R.a_sh[q] = ka ? ((const uint16_t*)ash)[(int64_t)gm * g.a_sh_pitch + gb] : 0u;
+    else R.a_sh[q] = ka ? ((const uint8_t*)ash)[(int64_t)gm * g.a_sh_pitch + gb] : 0u;
+    R.b[q] = kb ? *(const uint4*)(bb + (int64_t)gn * g.b_pitch + (int64_t)gb * 16) : make_uint4(0, 0, 0, 0);
+    R.b_sc[q] = kb ? bsc[(int64_t)gn * g.b_sc_pitch + gb] : 127u;
+  }
+}
+
+// LDS tile: A as E4M3 [128 rows][128 B] with 16-byte chunk c of row r stored at chunk c ^ (r & 7);
+// B as raw FP4 [128][64 B] (chunk c at c ^ (r & 3)) or E4M3 [128][128 B] for MXINT4; scales as
+// [g][half][r][i] bytes so that one lane reads the scales of its four 16-row sub-tiles at once.
+template <int B_FP4>
+struct Smem {
+  uint8_t a[BM * BK];
+  uint8_t b[B_FP4 ? BN * BK / 2 : BN * BK];
+  uint8_t as[4 * 2 * 16 * 4];
+  uint8_t bs[4 * 2 * 16 * 4];
+};
+
+__device__ __forceinline__ int scale_slot(int row, int g) {
+  // row = 64 half + 16 i + r
+  int half = row >> 6, i = (row >> 4) & 3, r = row & 15;
+  return ((g * 2 + half) * 16 + r) * 4 + i;
+}
+
+template <int A_FMT, int B_FP4>
+__device__ __forceinline__ void store_tile(Smem<B_FP4>& S, const TileRegs<A_FMT, B_FP4>& R) {
+  const int t = threadIdx.x;
+  const int row = t >> 1, hb = t & 1;
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const int kb = 2 * hb + q;  // block within the K step
+    uint32_t sh = R.a_sh[q];
+    uint32_t words[4] = {R.a[q].x, R.a[q].y, R.a[q].z, R.a[q].w};
+    uint32_t e[8];
+#pragma unroll
+    for (int sb = 0; sb < 4; sb++) {
+      uint32_t m = A_FMT == 1 ? (sh >> (4 + 3 * sb)) & 7u : (sh >> 4) & 7u;
+      mix8_to_e4m3(words[sb], m, e[2 * sb], e[2 * sb + 1]);
+    }
+    // block kb covers bytes [32 kb, 32 kb + 32) = chunks 2 kb, 2 kb + 1
+#pragma unroll
+    for (int hc = 0; hc < 2; hc++) {
+      int ch = (2 * kb + hc) ^ (row & 7);
+      *(uint4*)(S.a + row * BK + ch * 16) = make_uint4(e[4 * hc], e[4 * hc + 1], e[4 * hc + 2], e[4 * hc + 3]);
+    }
+    S.as[scale_slot(row, kb)] = (uint8_t)((sh & 15u) + 119u);  // E8M0 of 2^(Emax - 1)
+    if (B_FP4) {
+      int ch = kb ^ (row & 3);
+      *(uint4*)(S.b + row * (BK / 2) + ch * 16) = R.b[q];
+    } else {
+      uint32_t bw[4] = {R.b[q].x, R.b[q].y, R.b[q].z, R.b[q].w};
+      uint32_t f[8];
+#pragma unroll
+      for (int sb = 0; sb < 4; sb++) int4x8_to_e4m3(bw[sb], f[2 * sb], f[2 * sb + 1]);
+#pragma unroll
+      for (int hc = 0; hc < 2; hc++) {
+        int ch = (2 * kb + hc) ^ (row & 7);
+        *(uint4*)(S.b + row * BK + ch * 16) = make_uint4(f[4 * hc], f[4 * hc + 1], f[4 * hc + 2], f[4 * hc + 3]);
+      }
+    }
+    S.bs[scale_slot(row, kb)] = (uint8_t)R.b_sc[q];
+  }
+}
+
+template <int A_FMT, int B_FP4, int C_BF16>
+__global__ void __launch_bounds__(256, 2) k_gemm_mfma(GemmArgs g) {
+  __shared__ Smem<B_FP4> S;
+  const int tiles_n = (g.N + BN - 1) / BN;
+  const int tile = blockIdx.x;
+  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int batch = blockIdx.z;
+  if (g.causal == 1 && n0 > m0 + BM - 1) return;
+  int kend = g.K;
+  if (g.causal == 2) kend = min(g.K, m0 + BM);
+
+  const uint8_t* ab = g.a_codes + (int64_t)batch * g.a_bstride;
+  const void* ash = A_FMT == 1 ? (const void*)((const uint16_t*)g.a_shared + (int64_t)batch * g.a_sh_bstride)
+                               : (const void*)((const uint8_t*)g.a_shared + (int64_t)batch * g.a_sh_bstride);
+  const int bbatch = batch / g.b_group;
+  const uint8_t* bb = g.b_codes + (int64_t)bbatch * g.b_bstride;
+  const uint8_t* bsc = g.b_scales + (int64_t)bbatch * g.b_sc_bstride;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 15, gq = lane >> 4;
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  TileRegs<A_FMT, B_FP4> R;
+  load_tile<A_FMT, B_FP4>(g, ab, ash, bb, bsc, m0, n0, 0, R);
+  for (int k0 = 0; k0 < kend; k0 += BK) {
+    __syncthreads();
+    store_tile<A_FMT, B_FP4>(S, R);
+    __syncthreads();
+    if (k0 + BK < kend) load_tile<A_FMT, B_FP4>(g, ab, ash, bb, bsc, m0, n0, k0 + BK, R);
+
+    v8i af[4], bf[4];
+    int sa[4], sb[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      int row = 64 * wm + 16 * i + r;
+      uint4 lo = *(const uint4*)(S.a + row * BK + ((gq) ^ (row & 7)) * 16);
+      uint4 hi = *(const uint4*)(S.a + row * BK + ((4 + gq) ^ (row & 7)) * 16);
+      af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      sa[i] = S.as[scale_slot(row, gq)];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      int row = 64 * wn + 16 * j + r;
+      if (B_FP4) {
+        uint4 v = *(const uint4*)(S.b + row * (BK / 2) + ((gq) ^ (row & 3)) * 16);
+        bf[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      } else {
+        uint4 lo = *(const uint4*)(S.b + row * BK + ((gq) ^ (row & 7)) * 16);
+        uint4 hi = *(const uint4*)(S.b + row * BK + ((4 + gq) ^ (row & 7)) * 16);
+        bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      sb[j] = S.bs[scale_slot(row, gq)];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], 0, B_FP4 ? 4 : 0, 0,
+                                                                      sa[i], 0, sb[j]);
+  }
+
+  // epilogue
+  const float* rdiv = g.row_div ? g.row_div + (int64_t)batch * g.row_div_bstride : nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      int m = m0 + 64 * wm + 16 * i + 4 * gq + e;
+      if (m >= g.M) continue;
+      float dv = rdiv ? rdiv[m] : 1.0f;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        int n = n0 + 64 * wn + 16 * j + r;
+        if (n >= g.N) continue;
+        float v = acc[i][j][e];
+        if (rdiv) v = __fdiv_rn(v, dv);
+        int64_t idx = (int64_t)batch * g.c_bstride + (int64_t)m * g.ldc + n;
+        if (C_BF16) ((uint16_t*)g.c)[idx] = f32_to_bf16_rne(v);
+        else ((float*)g.c)[idx] = v;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ Eq. (6) vector-ALU kernel
+
+constexpr int EM = 64, EN = 64;
+
+template <int A_FMT, int B_FP4, int C_BF16>
+__global__ void __launch_bounds__(256) k_gemm_eq6(GemmArgs g) {
+  // per K block: A as s*2^(7-dE) (int16) [32][64], B as Wint (int16) [32][64], k-major
+  __shared__ int16_t sa[32][EM];
+  __shared__ int16_t sb[32][EN];
+  __shared__ int sam[EM][4];  // 8 + m_k
+  __shared__ int sae[EM];     // Emax
+  __shared__ int sbe[EN];     // X
+  const int tiles_n = (g.N + EN - 1) / EN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int m0 = tm * EM, n0 = tn * EN;
+  const int batch = blockIdx.z;
+  if (g.causal == 1 && n0 > m0 + EM - 1) return;
+  int kend = g.K;
+  if (g.causal == 2) kend = min(g.K, m0 + EM);
+  const uint8_t* ab = g.a_codes + (int64_t)batch * g.a_bstride;
+  const int bbatch = batch / g.b_group;
+  const uint8_t* bb = g.b_codes + (int64_t)bbatch * g.b_bstride;
+  const uint8_t* bsc = g.b_scales + (int64_t)bbatch * g.b_sc_bstride;
+  const int cw = B_FP4 ? 1 : 2;
+
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;  // thread owns rows 4 ty .. +3, cols 4 tx .. +3
+  float acc[4][4] = {};
+  const int nkb = g.K >> 5;
+  for (int k0 = 0; k0 < kend; k0 += 32) {
+    const int gb = k0 >> 5;
+    __syncthreads();
+    {  // 64 rows x 16 bytes of A and of B: thread -> (row = tid >> 2, 4-byte word tid & 3)
+      int row = tid >> 2, wd = tid & 3;
+      int gm = m0 + row, gn = n0 + row;
+      uint32_t aw = 0x77777777u, bw = 0;
+      uint32_t sh = 0;
+      if (gm < g.M && gb < nkb) {
+        aw = *(const uint32_t*)(ab + (int64_t)gm * g.a_pitch + gb * 16 + wd * 4);
+        sh = A_FMT == 1 ? ((const uint16_t*)g.a_shared)[(int64_t)batch * g.a_sh_bstride + (int64_t)gm * g.a_sh_pitch + gb]
+                        : ((const uint8_t*)g.a_shared)[(int64_t)batch * g.a_sh_bstride + (int64_t)gm * g.a_sh_pitch + gb];
+      }
+      int X = 0;
+      if (gn < g.N && gb < nkb) {
+        bw = *(const uint32_t*)(bb + (int64_t)gn * g.b_pitch + gb * 16 + wd * 4);
+        X = (int)bsc[(int64_t)gn * g.b_sc_pitch + gb] - 127;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        uint32_t na = (aw >> (4 * e)) & 15u, nb = (bw >> (4 * e)) & 15u;
+        int av;
+        if (na == 0x7) av = 0;
+        else if (na == 0xF) av = 1;
+        else av = (na & 8) ? -(1 << (7 - (int)(na & 7))) : (1 << (7 - (int)(na & 7)));
+        int wv;
+        if (B_FP4) {
+          const int tab[8] = {0, 1, 2, 3, 4, 6, 8, 12};
+          wv = (nb & 8) ? -tab[nb & 7] : tab[nb & 7];
+        } else {
+          wv = nb >= 8 ? (int)nb - 16 : (int)nb;
+        }
+        sa[wd * 8 + e][row] = (int16_t)av;
+        sb[wd * 8 + e][row] = (int16_t)wv;
+      }
+      if (wd == 0) {
+        sae[row] = (int)(sh & 15u) - 7;
+        sbe[row] = X;
+#pragma unroll
+        for (int k = 0; k < 4; k++) sam[row][k] = 8 + (int)(A_FMT == 1 ? (sh >> (4 + 3 * k)) & 7u : (sh >> 4) & 7u);
+      }
+    }
+    __syncthreads();
+    int blk[4][4] = {};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      int T[4][4] = {};
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        int a[4], w[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) a[i] = sa[k * 8 + e][4 * ty + i];
+#pragma unroll
+        for (int j = 0; j < 4; j++) w[j] = sb[k * 8 + e][4 * tx + j];
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) T[i][j] += a[i] * w[j];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        int mk = sam[4 * ty + i][k];
+#pragma unroll
+        for (int j = 0; j < 4; j++) blk[i][j] += mk * T[i][j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        acc[i][j] += ldexpf((float)blk[i][j], sae[4 * ty + i] + sbe[4 * tx + j] - 10 - cw);
+  }
+  const float* rdiv = g.row_div ? g.row_div + (int64_t)batch * g.row_div_bstride : nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    int m = m0 + 4 * ty + i;
+    if (m >= g.M) continue;
+    float dv = rdiv ? rdiv[m] : 1.0f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      int n = n0 + 4 * tx + j;
+      if (n >= g.N) continue;
+      float v = acc[i][j];
+      if (rdiv) v = __fdiv_rn(v, dv);
+      int64_t idx = (int64_t)batch * g.c_bstride + (int64_t)m * g.ldc + n;
+      if (C_BF16) ((uint16_t*)g.c)[idx] = f32_to_bf16_rne(v);
+      else ((float*)g.c)[idx] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+#define DISPATCH3(KERN, GRID, BLOCK, ...)                                                        \
+  do {                                                                                           \
+    if (a_fmt) {                                                                                 \
+      if (b_fp4) { if (c_bf16) hipLaunchKernelGGL((KERN<1, 1, 1>), GRID, BLOCK, 0, s, __VA_ARGS__); \
+                   else hipLaunchKernelGGL((KERN<1, 1, 0>), GRID, BLOCK, 0, s, __VA_ARGS__); }       \
+      else { if (c_bf16) hipLaunchKernelGGL((KERN<1, 0, 1>), GRID, BLOCK, 0, s, __VA_ARGS__);        \
+             else hipLaunchKernelGGL((KERN<1, 0, 0>), GRID, BLOCK, 0, s, __VA_ARGS__); }             \
+    } else {                                                                                     \
+      if (b_fp4) { if (c_bf16) hipLaunchKernelGGL((KERN<0, 1, 1>), GRID, BLOCK, 0, s, __VA_ARGS__); \
+                   else hipLaunchKernelGGL((KERN<0, 1, 0>), GRID, BLOCK, 0, s, __VA_ARGS__); }       \
+      else { if (c_bf16) hipLaunchKernelGGL((KERN<0, 0, 1>), GRID, BLOCK, 0, s, __VA_ARGS__);        \
+             else hipLaunchKernelGGL((KERN<0, 0, 0>), GRID, BLOCK, 0, s, __VA_ARGS__); }             \
+    }                                                                                            \
+  } while (0)
+
+hipError_t launch_gemm_mfma(int a_fmt, int b_fp4, int c_bf16, const GemmArgs& g, hipStream_t s) {
+  int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  dim3 grid(tiles, 1, g.batch), block(256);
+  DISPATCH3(k_gemm_mfma, grid, block, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_eq6(int a_fmt, int b_fp4, int c_bf16, const GemmArgs& g, hipStream_t s) {
+  int tiles = ((g.M + EM - 1) / EM) * ((g.N + EN - 1) / EN);
+  dim3 grid(tiles, 1, g.batch), block(256);
+  DISPATCH3(k_gemm_eq6, grid, block, g);
+  return hipGetLastError();
+}
+
+}  // namespace mix

@@ -1,0 +1,45 @@
+// Host-side launchers of the MiX HIP kernels (internal to the library; the public C-ABI is
+// include/mixlib.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mix {
+
+hipError_t launch_mix_quantize(int fmt, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                               uint8_t* codes, void* shared, hipStream_t s);
+hipError_t launch_mx_quantize(int fp4, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                              const float* mu, uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_mx_quantize_cols(const void* x, int dtype, int64_t rows, int64_t prows, int64_t cols, int64_t ldx,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_mix_dequantize(int fmt, const uint8_t* codes, const void* shared, int64_t rows, int64_t cols,
+                                 float* out, hipStream_t s);
+hipError_t launch_mx_dequantize(int fp4, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                                float* out, hipStream_t s);
+hipError_t launch_kmean(const void* x, int dtype, int64_t T, int64_t C, int64_t ldx, float* mu, hipStream_t s);
+
+// Operands of the block-scaled product C = deq(A) . deq(B)^T, optionally batched.
+struct GemmArgs {
+  const uint8_t* a_codes;   // MiX codes, rows of K/2 bytes
+  const void* a_shared;     // MiX shared fields (u8 for 4.25b, u16 for 4.5b), rows of K/32
+  int64_t a_pitch;          // bytes between consecutive rows of A codes
+  int64_t a_sh_pitch;       // elements between consecutive rows of A shared fields
+  int64_t a_bstride;        // bytes between batches of A codes
+  int64_t a_sh_bstride;     // elements between batches of A shared fields
+  const uint8_t* b_codes;   // MX codes, rows of K/2 bytes
+  const uint8_t* b_scales;  // E8M0 scales, rows of K/32 bytes
+  int64_t b_pitch, b_sc_pitch, b_bstride, b_sc_bstride;
+  int b_group;              // batch b uses B batch b / b_group (grouped-query attention)
+  void* c;                  // output, fp32 or bf16
+  int64_t ldc;              // elements between rows of C
+  int64_t c_bstride;        // elements between batches of C
+  const float* row_div;     // optional: row m of C is divided by row_div[m] before rounding
+  int64_t row_div_bstride;
+  int M, N, K, batch;
+  int causal;               // 0 none; 1 skip tiles strictly above the diagonal; 2 stop K at the tile's last row
+};
+
+hipError_t launch_gemm_mfma(int a_fmt, int b_fp4, int c_bf16, const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_eq6(int a_fmt, int b_fp4, int c_bf16, const GemmArgs& g, hipStream_t s);
+
+}  // namespace mix

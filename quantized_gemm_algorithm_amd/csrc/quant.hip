@@ -1,0 +1,344 @@
+// MiX and MX quantizers, their decoders and the K-mean, for gfx950.
+//
+// MiX (P1 = the pchao.org digest "MiX：面向端到端低比特视觉语言模型加速的微反缩放", section
+// 方法概览 / method overview, format bullets and the Algorithm 1 bullet; Fig. 4 in the figure
+// walk): a 32-element block stores a 4-bit Emax and a 3-bit shared mantissa (one per block for
+// MiX-4.25b, one per 8-element sub-block for MiX-4.5b); each element stores a sign and a 3-bit
+// relative exponent dE; value = (-1)^s (1.m)_2 2^(Emax - dE); dE = 7 is zero and the negative
+// zero pattern is one more positive step. Algorithm 1 takes Emax and the mantissa from the
+// block's (sub-block's) largest element and picks dE among the naive exponent and its two
+// neighbours by reconstruction error.
+//
+// Layout of one lane's work: a lane owns one 8-element sub-block (16 B of bf16 or 32 B of fp32),
+// a quad of lanes owns one 32-element block. The block max is a quad reduction over DPP. Codes
+// leave as one 32-bit word per lane (8 nibbles), so a wave stores 256 contiguous bytes.
+//
+// Element decision. With M = 1 + m/8 the nonzero magnitudes are c_d = M 2^(Emax-d). The nearest
+// one (ties to the smaller magnitude) is c_d* with d* = #{d : a <= mid_d}, mid_d the midpoint of
+// c_d and c_(d+1). For d <= 5 the midpoints are 1.5 M 2^(Emax-1-d), a geometric sequence, so the
+// count is an exponent difference plus one mantissa comparison -- the naive dE plus its +-1
+// refinement. Only the last step differs by sign: positives have c_7 (the reclaimed pattern) and
+// then zero; negatives go from c_6 to zero. All thresholds are exact fp32 values and every
+// comparison is an unsigned comparison of fp32 bit patterns, so the decision is exact.
+#include "common.h"
+#include "kernels.h"
+#include "quant_dev.h"
+
+namespace mix {
+
+// ------------------------------------------------------------------ loading 8 elements
+
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, int64_t row, int64_t ld, int64_t col, uint32_t (&x)[8]) {
+  if (DT == 1) {  // bf16
+    const uint16_t* p = (const uint16_t*)base + row * ld + col;
+    uint4 v = *(const uint4*)p;
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      x[2 * i] = (w[i] & 0xFFFFu) << 16;
+      x[2 * i + 1] = w[i] & 0xFFFF0000u;
+    }
+  } else {  // fp32
+    const float* p = (const float*)base + row * ld + col;
+    uint4 v0 = *(const uint4*)p;
+    uint4 v1 = *(const uint4*)(p + 4);
+    x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+    x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+  }
+}
+
+// ------------------------------------------------------------------ MiX quantizer (K1)
+
+template <int DT, int FMT>  // FMT 0 = MiX-4.25b, 1 = MiX-4.5b
+__global__ void __launch_bounds__(256) k_mix_quantize(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                                                       uint8_t* __restrict__ codes, void* __restrict__ shared) {
+  const int64_t sub_per_row = cols >> 3;
+  const int64_t total = rows * sub_per_row;  // multiple of 4
+  const int lane = threadIdx.x & 63;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g - lane < total;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    // whole quads are active or inactive together (total is a multiple of 4)
+    if (g >= total) continue;
+    int64_t row = g / sub_per_row;
+    int64_t sc = g - row * sub_per_row;  // sub-block index in the row
+    uint32_t xb[8];
+    load8<DT>(x, row, ldx, sc * 8, xb);
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      uint32_t a = xb[i] & 0x7FFFFFFFu;
+      lmax = a > lmax ? a : lmax;
+    }
+    uint32_t bmax = quad_max_u32(lmax);
+    int emax;
+    if (bmax == 0) emax = -7;
+    else {
+      int e = (int)(bmax >> 23) - 127;
+      emax = e < -7 ? -7 : (e > 8 ? 8 : e);
+    }
+    uint32_t m = mant3_of(FMT == 1 ? lmax : bmax);
+    MixThresholds t = mix_thresholds(emax, m);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) word |= mix_code(xb[i], t) << (4 * i);
+    *(uint32_t*)(codes + row * (cols >> 1) + sc * 4) = word;
+    int q = (int)(sc & 3);
+    int64_t blk = sc >> 2;
+    if (FMT == 1) {
+      uint32_t f = (q == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * q));
+      f = quad_or_u32(f);
+      if (q == 0) ((uint16_t*)shared)[row * (cols >> 5) + blk] = (uint16_t)f;
+    } else {
+      if (q == 0) ((uint8_t*)shared)[row * (cols >> 5) + blk] = (uint8_t)((uint32_t)(emax + 7) | (m << 4));
+    }
+  }
+}
+
+// ------------------------------------------------------------------ MX quantizer (K2), blocks along rows
+
+template <int DT, int FP4, int MU>
+__global__ void __launch_bounds__(256) k_mx_quantize(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                                                      const float* __restrict__ mu, uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales) {
+  const int64_t sub_per_row = cols >> 3;
+  const int64_t total = rows * sub_per_row;
+  const int lane = threadIdx.x & 63;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g - lane < total;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    if (g >= total) continue;
+    int64_t row = g / sub_per_row;
+    int64_t sc = g - row * sub_per_row;
+    uint32_t xb[8];
+    load8<DT>(x, row, ldx, sc * 8, xb);
+    if (MU) {
+      const float4* mp = (const float4*)(mu + sc * 8);
+      float4 m0 = mp[0], m1 = mp[1];
+      float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+      for (int i = 0; i < 8; i++) xb[i] = f32_bits(__fsub_rn(bits_f32(xb[i]), mv[i]));
+    }
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      uint32_t a = xb[i] & 0x7FFFFFFFu;
+      lmax = a > lmax ? a : lmax;
+    }
+    uint32_t bmax = quad_max_u32(lmax);
+    uint32_t word = 0;
+    int X = mx_exponent(bmax, FP4);
+    if (bmax != 0) {
+      if (FP4) {
+        Fp4Thr r = fp4_thresholds(X);
+#pragma unroll
+        for (int i = 0; i < 8; i++) word |= fp4_code(xb[i], r) << (4 * i);
+      } else {
+        Int4Thr r = int4_thresholds(X);
+#pragma unroll
+        for (int i = 0; i < 8; i++) word |= int4_code(xb[i], r) << (4 * i);
+      }
+    }
+    *(uint32_t*)(codes + row * (cols >> 1) + sc * 4) = word;
+    if ((sc & 3) == 0) scales[row * (cols >> 5) + (sc >> 2)] = bmax ? (uint8_t)(X + 127) : (uint8_t)0;
+  }
+}
+
+// ------------------------------------------------------------------ MX quantizer, blocks along columns
+// x [rows, cols] (row pitch ldx); a block is 32 consecutive rows of one column. Output codes
+// [cols, rows/2] and scales [cols, rows/32] (the transposed layout used for V along tokens).
+// Rows beyond `rows` up to the padded count `prows` are zero.
+template <int DT>
+__global__ void __launch_bounds__(256) k_mx_quantize_cols(const void* __restrict__ x, int64_t rows, int64_t prows,
+                                                           int64_t cols, int64_t ldx, uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales) {
+  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t rb = blockIdx.y;  // 32-row block
+  if (c >= cols) return;
+  uint32_t xb[32];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 32; i++) {
+    int64_t r = rb * 32 + i;
+    uint32_t v = 0;
+    if (r < rows) {
+      if (DT == 1) v = (uint32_t)((const uint16_t*)x)[r * ldx + c] << 16;
+      else v = ((const uint32_t*)x)[r * ldx + c];
+    }
+    xb[i] = v;
+    uint32_t a = v & 0x7FFFFFFFu;
+    amax = a > amax ? a : amax;
+  }
+  uint32_t w[4] = {0, 0, 0, 0};
+  int X = mx_exponent(amax, 1);
+  if (amax != 0) {
+    Fp4Thr r = fp4_thresholds(X);
+#pragma unroll
+    for (int i = 0; i < 32; i++) w[i >> 3] |= fp4_code(xb[i], r) << (4 * (i & 7));
+  }
+  uint4 o = {w[0], w[1], w[2], w[3]};
+  *(uint4*)(codes + c * (prows >> 1) + rb * 16) = o;
+  scales[c * (prows >> 5) + rb] = amax ? (uint8_t)(X + 127) : (uint8_t)0;
+}
+
+// ------------------------------------------------------------------ decoders (debug / tests)
+
+__global__ void k_mix_dequantize(int fmt, const uint8_t* __restrict__ codes, const void* __restrict__ shared, int64_t rows,
+                                 int64_t cols, float* __restrict__ out) {
+  int64_t n = rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t r = i / cols, c = i - r * cols;
+    uint32_t nib = (codes[r * (cols >> 1) + (c >> 1)] >> ((c & 1) * 4)) & 0xF;
+    uint32_t f = fmt ? ((const uint16_t*)shared)[r * (cols >> 5) + (c >> 5)]
+                     : ((const uint8_t*)shared)[r * (cols >> 5) + (c >> 5)];
+    int emax = (int)(f & 15) - 7;
+    uint32_t m = fmt ? (f >> (4 + 3 * ((c & 31) >> 3))) & 7 : (f >> 4) & 7;
+    float v;
+    if (nib == 0x7) v = 0.f;
+    else {
+      int de = nib == 0xF ? 7 : (int)(nib & 7);
+      v = ldexpf(1.0f + (float)m * 0.125f, emax - de);
+      if (nib != 0xF && (nib & 8)) v = -v;
+    }
+    out[i] = v;
+  }
+}
+
+__global__ void k_mx_dequantize(int fp4, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                int64_t rows, int64_t cols, float* __restrict__ out) {
+  const float e2m1[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+  int64_t n = rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t r = i / cols, c = i - r * cols;
+    uint32_t nib = (codes[r * (cols >> 1) + (c >> 1)] >> ((c & 1) * 4)) & 0xF;
+    int X = (int)scales[r * (cols >> 5) + (c >> 5)] - 127;
+    float v;
+    if (fp4) {
+      v = ldexpf(e2m1[nib & 7], X);
+      if (nib & 8) v = -v;
+    } else {
+      int q = nib >= 8 ? (int)nib - 16 : (int)nib;
+      v = ldexpf((float)q, X - 2);
+    }
+    out[i] = v;
+  }
+}
+
+// ------------------------------------------------------------------ K-mean (exact sum)
+// mu[c] = fp32( sum_t x[t, c] / T ) with the sum carried exactly as an unevaluated pair of
+// doubles (TwoSum): exact for the bf16 inputs here, whose binade spread is far below 100.
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+struct DD { double hi, lo; };
+__device__ __forceinline__ DD dd_add(DD x, double y) {
+  double s, e;
+  two_sum(x.hi, y, s, e);
+  e += x.lo;
+  double h, l;
+  two_sum(s, e, h, l);
+  return DD{h, l};
+}
+__device__ __forceinline__ DD dd_add(DD x, DD y) {
+  double s, e;
+  two_sum(x.hi, y.hi, s, e);
+  e += x.lo + y.lo;
+  double h, l;
+  two_sum(s, e, h, l);
+  return DD{h, l};
+}
+
+template <int DT>
+__global__ void __launch_bounds__(256) k_kmean(const void* __restrict__ x, int64_t T, int64_t C, int64_t ldx,
+                                                float* __restrict__ mu) {
+  // block: 32 columns x 8 row lanes
+  __shared__ double shi[8][32];
+  __shared__ double slo[8][32];
+  int cl = threadIdx.x & 31, rl = threadIdx.x >> 5;
+  int64_t c = (int64_t)blockIdx.x * 32 + cl;
+  DD acc{0.0, 0.0};
+  if (c < C) {
+    for (int64_t t = rl; t < T; t += 8) {
+      float v = DT == 1 ? __uint_as_float((uint32_t)((const uint16_t*)x)[t * ldx + c] << 16)
+                        : ((const float*)x)[t * ldx + c];
+      acc = dd_add(acc, (double)v);
+    }
+  }
+  shi[rl][cl] = acc.hi;
+  slo[rl][cl] = acc.lo;
+  __syncthreads();
+  if (rl == 0 && c < C) {
+    DD s{shi[0][cl], slo[0][cl]};
+    for (int i = 1; i < 8; i++) s = dd_add(s, DD{shi[i][cl], slo[i][cl]});
+    double sum = s.hi + s.lo;  // correctly rounded: the pair is normalised
+    mu[c] = (float)(sum / (double)T);
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+static inline int grid_for(int64_t threads_needed) {
+  int64_t b = (threads_needed + 255) / 256;
+  if (b > 65535 * 4) b = 65535 * 4;
+  return (int)(b < 1 ? 1 : b);
+}
+
+hipError_t launch_mix_quantize(int fmt, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                               uint8_t* codes, void* shared, hipStream_t s) {
+  int64_t total = rows * (cols >> 3);
+  dim3 g(grid_for(total)), b(256);
+  if (dtype == 1) {
+    if (fmt == 1) hipLaunchKernelGGL((k_mix_quantize<1, 1>), g, b, 0, s, x, rows, cols, ldx, codes, shared);
+    else hipLaunchKernelGGL((k_mix_quantize<1, 0>), g, b, 0, s, x, rows, cols, ldx, codes, shared);
+  } else {
+    if (fmt == 1) hipLaunchKernelGGL((k_mix_quantize<0, 1>), g, b, 0, s, x, rows, cols, ldx, codes, shared);
+    else hipLaunchKernelGGL((k_mix_quantize<0, 0>), g, b, 0, s, x, rows, cols, ldx, codes, shared);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize(int fp4, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                              const float* mu, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  int64_t total = rows * (cols >> 3);
+  dim3 g(grid_for(total)), b(256);
+#define MXQ(DT, F, M) hipLaunchKernelGGL((k_mx_quantize<DT, F, M>), g, b, 0, s, x, rows, cols, ldx, mu, codes, scales)
+  if (dtype == 1) {
+    if (fp4) { if (mu) MXQ(1, 1, 1); else MXQ(1, 1, 0); }
+    else { if (mu) MXQ(1, 0, 1); else MXQ(1, 0, 0); }
+  } else {
+    if (fp4) { if (mu) MXQ(0, 1, 1); else MXQ(0, 1, 0); }
+    else { if (mu) MXQ(0, 0, 1); else MXQ(0, 0, 0); }
+  }
+#undef MXQ
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize_cols(const void* x, int dtype, int64_t rows, int64_t prows, int64_t cols, int64_t ldx,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  dim3 g((unsigned)((cols + 255) / 256), (unsigned)(prows / 32)), b(256);
+  if (dtype == 1) hipLaunchKernelGGL((k_mx_quantize_cols<1>), g, b, 0, s, x, rows, prows, cols, ldx, codes, scales);
+  else hipLaunchKernelGGL((k_mx_quantize_cols<0>), g, b, 0, s, x, rows, prows, cols, ldx, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mix_dequantize(int fmt, const uint8_t* codes, const void* shared, int64_t rows, int64_t cols,
+                                 float* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_mix_dequantize, dim3(grid_for(rows * cols)), dim3(256), 0, s, fmt, codes, shared, rows, cols, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_dequantize(int fp4, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                                float* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_mx_dequantize, dim3(grid_for(rows * cols)), dim3(256), 0, s, fp4, codes, scales, rows, cols, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_kmean(const void* x, int dtype, int64_t T, int64_t C, int64_t ldx, float* mu, hipStream_t s) {
+  dim3 g((unsigned)((C + 31) / 32)), b(256);
+  if (dtype == 1) hipLaunchKernelGGL((k_kmean<1>), g, b, 0, s, x, T, C, ldx, mu);
+  else hipLaunchKernelGGL((k_kmean<0>), g, b, 0, s, x, T, C, ldx, mu);
+  return hipGetLastError();
+}
+
+}  // namespace mix

@@ -1,0 +1,99 @@
+// Device-side element coders shared by the quantizer kernels and the attention kernels.
+//
+// MiX element decision. With M = 1 + m/8 the nonzero magnitudes of a block are c_d = M 2^(Emax-d).
+// The nearest one (ties to the smaller magnitude) is c_d* with d* = #{d : a <= mid_d}, mid_d the
+// midpoint of c_d and c_(d+1). For d <= 5 the midpoints are 1.5 M 2^(Emax-1-d), a geometric
+// sequence, so the count is an exponent difference plus one mantissa comparison (the naive dE
+// with its +-1 refinement). Only the last step depends on the sign: positives have c_7 (the
+// reclaimed pattern) and then zero; negatives go from c_6 to zero. All thresholds are exact fp32
+// values and all comparisons are unsigned comparisons of fp32 bit patterns.
+#pragma once
+#include "common.h"
+
+namespace mix {
+
+// Returns the 4-bit code of one element given the block's thresholds.
+struct MixThresholds {
+  uint32_t e_mu0;   // biased exponent of mid_0 = 1.5 M 2^(Emax-1)
+  uint32_t m_mu0;   // its mantissa bits
+  uint32_t pos_bottom;  // midpoint of c_7 and 0 for positives: M 2^(Emax-8)
+  uint32_t neg_bottom;  // midpoint of c_6 and 0 for negatives: M 2^(Emax-7)
+};
+
+__device__ __forceinline__ MixThresholds mix_thresholds(int emax, uint32_t m) {
+  MixThresholds t;
+  uint32_t t3 = 3u * (8u + m);  // 1.5 M = t3 / 16
+  uint32_t mu0 = exact_f32_bits(t3, emax - 5);
+  t.e_mu0 = mu0 >> 23;
+  t.m_mu0 = mu0 & 0x7FFFFFu;
+  t.pos_bottom = exact_f32_bits(8u + m, emax - 11);
+  t.neg_bottom = exact_f32_bits(8u + m, emax - 10);
+  return t;
+}
+
+__device__ __forceinline__ uint32_t mix_code(uint32_t xbits, const MixThresholds& t) {
+  uint32_t a = xbits & 0x7FFFFFFFu;
+  int ea = (int)(a >> 23);
+  uint32_t ma = a & 0x7FFFFFu;
+  int cnt = (int)t.e_mu0 - ea - (t.m_mu0 < ma ? 1 : 0) + 1;  // #{d in 0..6 : mid_d >= a}
+  cnt = cnt < 0 ? 0 : (cnt > 7 ? 7 : cnt);
+  bool neg = (xbits >> 31) && a != 0;
+  uint32_t code;
+  if (!neg) {
+    code = (cnt < 7) ? (uint32_t)cnt : (a <= t.pos_bottom ? 0x7u : 0xFu);
+  } else {
+    code = (cnt < 6) ? (0x8u | (uint32_t)cnt) : (a <= t.neg_bottom ? 0x7u : 0xEu);
+  }
+  return code;
+}
+
+// MXFP4 code of one element, thresholds at the E2M1 midpoints times 2^X, ties to the even code.
+struct Fp4Thr { uint32_t t[7]; };
+__device__ __forceinline__ Fp4Thr fp4_thresholds(int X) {
+  Fp4Thr r;
+  // midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 = k 2^s
+  r.t[0] = exact_f32_bits(1, X - 2);
+  r.t[1] = exact_f32_bits(3, X - 2);
+  r.t[2] = exact_f32_bits(5, X - 2);
+  r.t[3] = exact_f32_bits(7, X - 2);
+  r.t[4] = exact_f32_bits(5, X - 1);
+  r.t[5] = exact_f32_bits(7, X - 1);
+  r.t[6] = exact_f32_bits(5, X);
+  return r;
+}
+__device__ __forceinline__ uint32_t fp4_code(uint32_t xbits, const Fp4Thr& r) {
+  uint32_t a = xbits & 0x7FFFFFFFu;
+  uint32_t idx = (a > r.t[0]) + (a >= r.t[1]) + (a > r.t[2]) + (a >= r.t[3]) + (a > r.t[4]) + (a >= r.t[5]) +
+                 (a > r.t[6]);
+  return ((xbits >> 31) << 3) | idx;
+}
+// MXINT4: |q| = RNE(a 2^(2-X)) clamped to 7; thresholds (2k+1) 2^(X-3), ties to even.
+struct Int4Thr { uint32_t t[7]; };
+__device__ __forceinline__ Int4Thr int4_thresholds(int X) {
+  Int4Thr r;
+#pragma unroll
+  for (int k = 0; k < 7; k++) r.t[k] = exact_f32_bits(2 * k + 1, X - 3);
+  return r;
+}
+__device__ __forceinline__ uint32_t int4_code(uint32_t xbits, const Int4Thr& r) {
+  uint32_t a = xbits & 0x7FFFFFFFu;
+  uint32_t q = 0;
+#pragma unroll
+  for (int k = 0; k < 7; k++) q += (k & 1) ? (a >= r.t[k]) : (a > r.t[k]);
+  return (xbits >> 31) ? ((0u - q) & 0xFu) : q;
+}
+
+__device__ __forceinline__ int mx_exponent(uint32_t bmax, int fp4) {
+  int E = (int)(bmax >> 23);
+  if (fp4) {  // ceil(log2 a) - 2, at least -127
+    if (E == 0) return -127;
+    int X = E - 127 + ((bmax & 0x7FFFFFu) != 0) - 2;
+    return X < -127 ? -127 : X;
+  }
+  if (E == 0) return -125;  // floor(log2 a) - for a subnormal maximum - is below the clamp
+  int X = E - 127;
+  return X < -125 ? -125 : X;
+}
+
+
+}  // namespace mix

@@ -1,0 +1,96 @@
+"""The C-ABI library loads, exports every entry point declared in include/mixlib.h, and rejects bad
+arguments on the host before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mixlib.h")
+LIB = os.path.join(ROOT, "quantized_gemm_algorithm_amd", "libmix.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmix.so not built")
+
+MIX_OK, MIX_E_NULL, MIX_E_SHAPE, MIX_E_ALIGN, MIX_E_ENUM, MIX_E_UNSUPPORTED, MIX_E_HIP, MIX_E_WORKSPACE = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:const\s+)?\w+\s*\*?\s+(mix\w+|mx\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from quantized_gemm_algorithm_amd import _lib
+    return _lib.load(LIB)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 15, names
+    for n in names:
+        assert hasattr(lib, n), n
+    from quantized_gemm_algorithm_amd._lib import SIGNATURES
+    assert set(names) == set(SIGNATURES), set(names) ^ set(SIGNATURES)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mix_abi_version() == 1
+    for s in range(8):
+        assert lib.mix_status_str(s)
+    assert lib.mix_status_str(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)        # never dereferenced: validation fails or the call is empty first
+MISALIGNED = P(0x10001)
+
+
+def test_quantize_validation(lib):
+    # unknown format / dtype
+    assert lib.mix_quantize(7, FAKE, 0, 1, 32, 32, FAKE, FAKE, None) == MIX_E_ENUM
+    assert lib.mix_quantize(1, FAKE, 5, 1, 32, 32, FAKE, FAKE, None) == MIX_E_ENUM
+    assert b"dtype" in lib.mix_last_error()
+    # shapes
+    assert lib.mix_quantize(1, FAKE, 0, 1, 33, 33, FAKE, FAKE, None) == MIX_E_SHAPE
+    assert lib.mix_quantize(1, FAKE, 0, -1, 32, 32, FAKE, FAKE, None) == MIX_E_SHAPE
+    assert lib.mix_quantize(1, FAKE, 0, 2, 64, 32, FAKE, FAKE, None) == MIX_E_SHAPE
+    # null pointers
+    assert lib.mix_quantize(1, None, 0, 1, 32, 32, FAKE, FAKE, None) == MIX_E_NULL
+    assert lib.mix_quantize(1, FAKE, 0, 1, 32, 32, None, FAKE, None) == MIX_E_NULL
+    # alignment: pointer and pitch
+    assert lib.mix_quantize(1, MISALIGNED, 0, 1, 32, 32, FAKE, FAKE, None) == MIX_E_ALIGN
+    assert lib.mix_quantize(1, FAKE, 1, 2, 32, 36, FAKE, FAKE, None) == MIX_E_ALIGN
+    # empty calls succeed without touching memory
+    assert lib.mix_quantize(1, None, 0, 0, 32, 32, None, None, None) == MIX_OK
+    assert lib.mix_quantize(1, None, 0, 5, 0, 0, None, None, None) == MIX_OK
+    assert lib.mx_quantize(2, FAKE, 0, 1, 32, 32, None, FAKE, FAKE, None) == MIX_E_ENUM
+    assert lib.mx_quantize(1, FAKE, 0, 1, 32, 32, MISALIGNED, FAKE, FAKE, None) == MIX_E_ALIGN
+    assert lib.mx_quantize(1, None, 0, 0, 64, 64, None, None, None, None) == MIX_OK
+    assert lib.mx_quantize_cols(FAKE, 1, 10, 4, 2, FAKE, FAKE, None) == MIX_E_SHAPE
+
+
+def test_gemm_validation(lib):
+    args_ok = dict(a=FAKE, s=FAKE, b=FAKE, bs=FAKE)
+    for fn in (lib.mix_mx_gemm, lib.mix_mx_gemm_eq6):
+        assert fn(3, FAKE, FAKE, 1, FAKE, FAKE, 4, 4, 32, FAKE, 0, 4, None) == MIX_E_ENUM
+        assert fn(1, FAKE, FAKE, 9, FAKE, FAKE, 4, 4, 32, FAKE, 0, 4, None) == MIX_E_ENUM
+        assert fn(1, FAKE, FAKE, 1, FAKE, FAKE, 4, 4, 40, FAKE, 0, 4, None) == MIX_E_SHAPE
+        assert fn(1, FAKE, FAKE, 1, FAKE, FAKE, 4, 4, 32, FAKE, 0, 3, None) == MIX_E_SHAPE
+        assert fn(1, FAKE, FAKE, 1, FAKE, FAKE, -4, 4, 32, FAKE, 0, 4, None) == MIX_E_SHAPE
+        assert fn(1, None, FAKE, 1, FAKE, FAKE, 4, 4, 32, FAKE, 0, 4, None) == MIX_E_NULL
+        assert fn(1, FAKE, FAKE, 1, FAKE, FAKE, 4, 4, 32, None, 0, 4, None) == MIX_E_NULL
+        assert fn(1, MISALIGNED, FAKE, 1, FAKE, FAKE, 4, 4, 32, FAKE, 0, 4, None) == MIX_E_ALIGN
+        assert fn(1, None, None, 1, None, None, 0, 4, 32, None, 0, 4, None) == MIX_OK
+        assert fn(1, None, None, 1, None, None, 4, 0, 32, None, 0, 0, None) == MIX_OK
+        assert fn(1, FAKE, FAKE, 1, FAKE, FAKE, 2**31, 4, 32, FAKE, 0, 4, None) == MIX_E_SHAPE
+    del args_ok
+
+
+def test_kmean_validation(lib):
+    assert lib.mix_kmean(FAKE, 1, 0, 32, 32, FAKE, None) == MIX_E_SHAPE
+    assert lib.mix_kmean(None, 1, 4, 32, 32, FAKE, None) == MIX_E_NULL
+    assert lib.mix_kmean(FAKE, 1, 4, 32, 16, FAKE, None) == MIX_E_SHAPE
+    assert lib.mix_kmean(None, 1, 4, 0, 0, None, None) == MIX_OK

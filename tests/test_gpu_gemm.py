@@ -1,0 +1,138 @@
+"""GPU parity of the A-MiX x W-MX product (MFMA path and the Eq. (6) vector-ALU path) against the
+oracle's exact dyadic dot products, within the fp32-accumulation tolerance (1e-5 of sum|a b| per
+element and normwise). Inputs are coded by the oracle, so the product is checked on its own."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import assert_bf16_matches, assert_codes_equal, assert_gemm_close, dev_bf16, dev_f32, dev_u8, dev_u16, host
+from oracle.gemm import gemm_abs_bound, gemm_exact, gemm_ref, gemm_ref_entries
+from oracle.mix import mix_dequantize as o_mix_deq, mix_quantize as o_mix_q
+from oracle.mx import mx_dequantize as o_mx_deq, mx_quantize as o_mx_q
+from quantized_gemm_algorithm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [(a, b) for a in ("4.25b", "4.5b") for b in ("int4", "fp4")]
+
+
+def _lib():
+    import quantized_gemm_algorithm_amd as q
+    return q
+
+
+def _code(x, w_t, a_fmt, b_fmt, dtype="f32"):
+    ac, as_ = o_mix_q(x, a_fmt, dtype)
+    bc, bs = o_mx_q(w_t, b_fmt, dtype)
+    return ac, as_, bc, bs
+
+
+def _to_dev(ac, as_, bc, bs, a_fmt):
+    return dev_u8(ac), (dev_u16(as_) if a_fmt == "4.5b" else dev_u8(as_)), dev_u8(bc), dev_u8(bs)
+
+
+def _run(fn_name, ac, as_, bc, bs, a_fmt, b_fmt, out_dtype):
+    q = _lib()
+    A, S, B, Bs = _to_dev(ac, as_, bc, bs, a_fmt)
+    out = getattr(q, fn_name)(A, S, a_fmt, B, Bs, b_fmt, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", PAIRS)
+@pytest.mark.parametrize("fn", ["mix_mx_gemm", "mix_mx_gemm_eq6"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (64, 256, 512), (200, 136, 352), (130, 300, 96), (16, 18, 4096)])
+def test_gemm_random_shapes(a_fmt, b_fmt, fn, M, N, K):
+    rng = np.random.default_rng(M * 131 + N * 7 + K)
+    x = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-6, 6, (M, K)))).astype(np.float32)
+    w = (0.05 * rng.standard_normal((N, K))).astype(np.float32)
+    ac, as_, bc, bs = _code(x, w, a_fmt, b_fmt)
+    ad, bd = o_mix_deq(ac, as_, a_fmt), o_mx_deq(bc, bs, b_fmt)
+    ref = gemm_ref(ad, bd)
+    bound = gemm_abs_bound(ad, bd)
+    got = _run(fn, ac, as_, bc, bs, a_fmt, b_fmt, torch.float32)
+    assert_gemm_close(got, ref, bound, f"{fn} {a_fmt}x{b_fmt} fp32 {M}x{N}x{K}")
+    gotb = _run(fn, ac, as_, bc, bs, a_fmt, b_fmt, torch.bfloat16)
+    assert_bf16_matches(gotb, ref, bound, f"{fn} {a_fmt}x{b_fmt} bf16 {M}x{N}x{K}")
+
+
+def test_gemm_workload1_against_exact_integer_product():
+    g = synth.tiny()
+    ac, as_, bc, bs = _code(g["x"], g["w_t"], "4.5b", "int4")
+    exact, _ = gemm_exact(ac, as_, "4.5b", bc, bs, "int4")
+    ad, bd = o_mix_deq(ac, as_, "4.5b"), o_mx_deq(bc, bs, "int4")
+    bound = gemm_abs_bound(ad, bd)
+    for fn in ("mix_mx_gemm", "mix_mx_gemm_eq6"):
+        got = _run(fn, ac, as_, bc, bs, "4.5b", "int4", torch.float32)
+        assert_gemm_close(got, exact, bound, fn)
+
+
+def test_gemm_zero_and_empty():
+    q = _lib()
+    # K = 0 gives zeros; M = 0 is an empty call
+    A = torch.zeros((4, 0), dtype=torch.uint8, device="cuda")
+    S = torch.zeros((4, 0), dtype=torch.int16, device="cuda")
+    B = torch.zeros((3, 0), dtype=torch.uint8, device="cuda")
+    Bs = torch.zeros((3, 0), dtype=torch.uint8, device="cuda")
+    out = torch.full((4, 3), 7.0, device="cuda")
+    q.mix_mx_gemm(A, S, "4.5b", B, Bs, "fp4", out=out)
+    assert torch.all(out == 0)
+    A = torch.zeros((0, 16), dtype=torch.uint8, device="cuda")
+    S = torch.zeros((0, 1), dtype=torch.int16, device="cuda")
+    B = torch.zeros((3, 16), dtype=torch.uint8, device="cuda")
+    Bs = torch.zeros((3, 1), dtype=torch.uint8, device="cuda")
+    out = q.mix_mx_gemm(A, S, "4.5b", B, Bs, "fp4")
+    assert out.shape == (0, 3)
+
+
+def _sampled_check(out_bits, ac, as_, a_fmt, bc, bs, b_fmt, nsamp, seed, what):
+    rng = np.random.default_rng(seed)
+    M, N = ac.shape[0], bc.shape[0]
+    rows = rng.integers(0, M, nsamp)
+    cols = rng.integers(0, N, nsamp)
+    ur = np.unique(rows)
+    uc = np.unique(cols)
+    ad = o_mix_deq(ac[ur], as_[ur], a_fmt)
+    bd = o_mx_deq(bc[uc], bs[uc], b_fmt)
+    ri = np.searchsorted(ur, rows)
+    ci = np.searchsorted(uc, cols)
+    ref = gemm_ref_entries(ad, bd, ri, ci)
+    bound = np.einsum("tk,tk->t", np.abs(ad[ri]), np.abs(bd[ci]))
+    got = out_bits[rows, cols]
+    assert_bf16_matches(got, ref, bound, what)
+
+
+def test_gemm_workload2_full_size_sampled():
+    # Qwen2-VL-7B-shaped prefill linear: 4096 x 18944 x 3584, MiX-4.5b x MXFP4, bf16 out
+    q = _lib()
+    g = synth.prefill_linear()
+    xd, wd = dev_bf16(g["x"]), dev_bf16(g["w_t"])
+    ac, as_ = q.mix_quantize(xd, "4.5b")
+    bc, bs = q.mx_quantize(wd, "fp4")
+    out = q.mix_mx_gemm(ac, as_, "4.5b", bc, bs, "fp4", out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    # the GPU's codes equal the oracle's (checked in test_gpu_quant); take them as the operands
+    _sampled_check(host(out), host(ac), host(as_), "4.5b", host(bc), host(bs), "fp4", 4096, 2, "workload 2")
+
+
+def test_gemm_workload3_full_size_sampled():
+    q = _lib()
+    g = synth.vision_linear()
+    ac, as_ = q.mix_quantize(dev_bf16(g["x"]), "4.25b")
+    bc, bs = q.mx_quantize(dev_bf16(g["w_t"]), "int4")
+    out = q.mix_mx_gemm(ac, as_, "4.25b", bc, bs, "int4", out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    _sampled_check(host(out), host(ac), host(as_), "4.25b", host(bc), host(bs), "int4", 4096, 3, "workload 3")
+    # spot-check the codes against the oracle on a slice
+    want = o_mix_q(g["x"][:512], "4.25b", "bf16")
+    assert_codes_equal(host(ac)[:512], want[0], "x codes slice")
+
+
+def test_gemm_eq6_workload3_sampled():
+    q = _lib()
+    g = synth.vision_linear()
+    ac, as_ = q.mix_quantize(dev_bf16(g["x"]), "4.25b")
+    bc, bs = q.mx_quantize(dev_bf16(g["w_t"]), "int4")
+    out = q.mix_mx_gemm_eq6(ac, as_, "4.25b", bc, bs, "int4", out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    _sampled_check(host(out), host(ac), host(as_), "4.25b", host(bc), host(bs), "int4", 2048, 4, "workload 3 eq6")

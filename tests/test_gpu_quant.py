@@ -1,0 +1,214 @@
+"""GPU parity of the MiX and MX quantizers against the CPU oracle: codes and shared fields must be
+bit-exact, on the workload shapes (full size) and on edge cases."""
+import numpy as np
+import pytest
+
+from helpers import assert_codes_equal, dev_bf16, dev_f32, host
+from oracle.mix import mix_dequantize as o_mix_deq, mix_quantize as o_mix_q
+from oracle.mx import mx_dequantize as o_mx_deq, mx_quantize as o_mx_q
+from quantized_gemm_algorithm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import quantized_gemm_algorithm_amd as q
+    return q
+
+
+def _wide(rng, rows, cols, spread=14):
+    return (rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-spread, spread, (rows, cols)))).astype(np.float32)
+
+
+def _bf16(x):
+    return synth.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("fmt", ["4.25b", "4.5b"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (37, 96), (64, 512), (257, 1024)])
+def test_mix_quantize_random(fmt, dtype, rows, cols):
+    q = _lib()
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = _wide(rng, rows, cols)
+    x[0, :32] = 0.0  # an all-zero block
+    if rows > 2:
+        x[2, 32:64] = np.float32(1e-41)  # a subnormal block
+    if dtype == "bf16":
+        xb = _bf16(x)
+        codes, shared = q.mix_quantize(dev_bf16(xb), fmt)
+        want = o_mix_q(xb, fmt, "bf16")
+    else:
+        codes, shared = q.mix_quantize(dev_f32(x), fmt)
+        want = o_mix_q(x, fmt, "f32")
+    assert_codes_equal(host(codes), want[0], "codes")
+    assert_codes_equal(host(shared), want[1], "shared")
+
+
+@pytest.mark.parametrize("fmt", ["4.25b", "4.5b"])
+def test_mix_quantize_exhaustive_bf16(fmt):
+    # every finite bf16 pattern, in blocks whose maxima sweep many (Emax, m) pairs
+    q = _lib()
+    pats = np.arange(65536, dtype=np.uint32)
+    vals = (pats << 16).view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    rng = np.random.default_rng(5)
+    rng.shuffle(vals)
+    n = len(vals) // 32 * 32
+    x = vals[:n].reshape(-1, 32)
+    xb = _bf16(x)
+    codes, shared = q.mix_quantize(dev_bf16(xb), fmt)
+    want = o_mix_q(xb, fmt, "bf16")
+    assert_codes_equal(host(codes), want[0], "codes")
+    assert_codes_equal(host(shared), want[1], "shared")
+
+
+def test_mix_quantize_ties_and_special_values():
+    q = _lib()
+    rows = []
+    for m in range(8):
+        M = 1 + m / 8
+        for emax in (-7, -2, 0, 3, 8):
+            blk = np.zeros(32, np.float32)
+            blk[0] = M * 2.0**emax
+            ds = np.arange(8)
+            blk[1:9] = 1.5 * M * 2.0 ** (emax - 1 - ds)      # every midpoint between neighbours
+            blk[9:17] = -1.5 * M * 2.0 ** (emax - 1 - ds)
+            blk[17] = M * 2.0 ** (emax - 8)                  # zero / reclaimed-step midpoint
+            blk[18] = -M * 2.0 ** (emax - 7)                 # negative zero midpoint
+            blk[19] = np.nextafter(np.float32(M * 2.0 ** (emax - 8)), np.float32(1))
+            blk[20] = -0.0
+            blk[21] = 1000.0 if emax == 8 else 0.0           # saturation
+            rows.append(blk)
+    x = np.stack(rows).astype(np.float32)
+    for fmt in ("4.25b", "4.5b"):
+        codes, shared = q.mix_quantize(dev_f32(x), fmt)
+        want = o_mix_q(x, fmt, "f32")
+        assert_codes_equal(host(codes), want[0], f"codes {fmt}")
+        assert_codes_equal(host(shared), want[1], f"shared {fmt}")
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp4"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("with_mu", [False, True])
+def test_mx_quantize_random(fmt, dtype, with_mu):
+    q = _lib()
+    rng = np.random.default_rng(17)
+    x = _wide(rng, 129, 256)
+    x[1, :32] = 0.0
+    x[3, 64:96] = np.float32(3e-40)
+    x[4, 5] = -0.0
+    mu = (rng.standard_normal(256) * 4).astype(np.float32) if with_mu else None
+    if dtype == "bf16":
+        xb = _bf16(x)
+        codes, scales = q.mx_quantize(dev_bf16(xb), fmt, mu=None if mu is None else dev_f32(mu))
+        want = o_mx_q(xb, fmt, "bf16", mu=mu)
+    else:
+        codes, scales = q.mx_quantize(dev_f32(x), fmt, mu=None if mu is None else dev_f32(mu))
+        want = o_mx_q(x, fmt, "f32", mu=mu)
+    assert_codes_equal(host(codes), want[0], "codes")
+    assert_codes_equal(host(scales), want[1], "scales")
+
+
+def test_mx_quantize_exhaustive_bf16():
+    q = _lib()
+    pats = np.arange(65536, dtype=np.uint32)
+    vals = (pats << 16).view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    rng = np.random.default_rng(6)
+    rng.shuffle(vals)
+    n = len(vals) // 32 * 32
+    xb = _bf16(vals[:n].reshape(-1, 32))
+    for fmt in ("int4", "fp4"):
+        codes, scales = q.mx_quantize(dev_bf16(xb), fmt)
+        want = o_mx_q(xb, fmt, "bf16")
+        assert_codes_equal(host(codes), want[0], f"codes {fmt}")
+        assert_codes_equal(host(scales), want[1], f"scales {fmt}")
+
+
+def test_mx_quantize_cols_matches_transposed_rows():
+    q = _lib()
+    rng = np.random.default_rng(8)
+    for T in (32, 100, 256):
+        v = _bf16((rng.standard_normal((T, 96)) * 3).astype(np.float32))
+        codes, scales = q.mx_quantize_cols(dev_bf16(v))
+        Tp = (T + 31) // 32 * 32
+        vp = np.zeros((Tp, 96), np.uint16)
+        vp[:T] = v
+        want = o_mx_q(np.ascontiguousarray(vp.T), "fp4", "bf16")
+        assert_codes_equal(host(codes), want[0], "codes")
+        assert_codes_equal(host(scales), want[1], "scales")
+
+
+def test_dequantizers_match_oracle():
+    q = _lib()
+    rng = np.random.default_rng(9)
+    x = _wide(rng, 16, 128)
+    for fmt in ("4.25b", "4.5b"):
+        c, s = q.mix_quantize(dev_f32(x), fmt)
+        d = host(q.mix_dequantize(c, s, fmt))
+        assert np.array_equal(d.astype(np.float64), o_mix_deq(host(c), host(s), fmt))
+    for fmt in ("int4", "fp4"):
+        c, s = q.mx_quantize(dev_f32(x), fmt)
+        d = host(q.mx_dequantize(c, s, fmt))
+        assert np.array_equal(d.astype(np.float64), o_mx_deq(host(c), host(s), fmt))
+
+
+# ---------------------------------------------------------------- workload shapes, full size
+
+def test_workload1_tiny():
+    q = _lib()
+    g = synth.tiny()
+    c, s = q.mix_quantize(dev_f32(g["x"]), "4.5b")
+    want = o_mix_q(g["x"], "4.5b", "f32")
+    assert_codes_equal(host(c), want[0], "x codes")
+    assert_codes_equal(host(s), want[1], "x shared")
+    c, s = q.mx_quantize(dev_f32(g["w_t"]), "int4")
+    want = o_mx_q(g["w_t"], "int4", "f32")
+    assert_codes_equal(host(c), want[0], "w codes")
+    assert_codes_equal(host(s), want[1], "w scales")
+
+
+def test_workload2_prefill_activations_full():
+    q = _lib()
+    g = synth.prefill_linear(with_weights=False)
+    c, s = q.mix_quantize(dev_bf16(g["x"]), "4.5b")
+    want = o_mix_q(g["x"], "4.5b", "bf16")
+    assert_codes_equal(host(c), want[0], "codes")
+    assert_codes_equal(host(s), want[1], "shared")
+
+
+def test_workload2_weights_sampled_rows():
+    q = _lib()
+    g = synth.prefill_linear()
+    w = g["w_t"]
+    c, s = q.mx_quantize(dev_bf16(w), "fp4")
+    rows = np.random.default_rng(2).choice(w.shape[0], 512, replace=False)
+    want = o_mx_q(w[rows], "fp4", "bf16")
+    assert_codes_equal(host(c)[rows], want[0], "codes")
+    assert_codes_equal(host(s)[rows], want[1], "scales")
+
+
+def test_workload3_vision_full():
+    q = _lib()
+    g = synth.vision_linear()
+    c, s = q.mix_quantize(dev_bf16(g["x"]), "4.25b")
+    want = o_mix_q(g["x"], "4.25b", "bf16")
+    assert_codes_equal(host(c), want[0], "x codes")
+    assert_codes_equal(host(s), want[1], "x shared")
+    c, s = q.mx_quantize(dev_bf16(g["w_t"]), "int4")
+    want = o_mx_q(g["w_t"], "int4", "bf16")
+    assert_codes_equal(host(c), want[0], "w codes")
+    assert_codes_equal(host(s), want[1], "w scales")
+
+
+def test_kmean_matches_oracle():
+    import torch
+    from oracle.attention import kmean_ref
+    q = _lib()
+    g = synth.attention_qkv(T=1000, Hq=4, Hkv=2, d=128)
+    k = g["k"]
+    mu = q.mix_kmean(dev_bf16(k.reshape(1000, -1)))
+    want = kmean_ref(k, "bf16")
+    assert_codes_equal(host(mu).view(np.uint32), want.reshape(-1).view(np.uint32), "mu bits")
+    assert torch.isfinite(mu).all()
