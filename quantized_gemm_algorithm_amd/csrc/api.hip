@@ -111,7 +111,8 @@ mix_status_t mx_quantize_cols(const void* x, mix_dtype_t dtype, int64_t rows, in
   if ((uintptr_t)x % dtype_size(dtype)) return fail(MIX_E_ALIGN, "mx_quantize_cols: x misaligned");
   int64_t prows = (rows + 31) / 32 * 32;
   if (prows / 32 > 65535) return fail(MIX_E_SHAPE, "mx_quantize_cols: rows too large");
-  return hip_status(mix::launch_mx_quantize_cols(x, (int)dtype, rows, prows, cols, ldx, codes, scales, (hipStream_t)stream),
+  return hip_status(mix::launch_mx_quantize_cols(x, (int)dtype, rows, prows, cols, ldx, codes, scales, prows / 2,
+                                                 prows / 32, (hipStream_t)stream),
                     "mx_quantize_cols launch");
 }
 
@@ -195,23 +196,79 @@ mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, i
 
 }  // extern "C"
 
-// ---------------------------------------------------------------- attention (stubs until implemented)
+// ---------------------------------------------------------------- attention
 extern "C" {
-size_t mix_attn_prefill_workspace_bytes(int64_t, int64_t, int64_t, int64_t) { return 0; }
-mix_status_t mix_attn_prefill(const void*, const void*, const void*, int64_t, int64_t, int64_t, int64_t, int, float*,
-                              void*, void*, size_t, const mix_attn_debug_t*, void*) {
-  g_err = "mix_attn_prefill: not implemented";
-  return MIX_E_UNSUPPORTED;
+
+size_t mix_attn_prefill_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t d) {
+  if (T <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return 0;
+  return mix::attn_prefill_ws_bytes(T, Hq, Hkv, d);
 }
-mix_status_t mix_kv_cache_prefill(const mix_kv_cache_t*, int64_t, const void*, const void*, int64_t, const float*,
-                                  void*) {
-  g_err = "mix_kv_cache_prefill: not implemented";
-  return MIX_E_UNSUPPORTED;
+
+mix_status_t mix_attn_prefill(const void* q, const void* k, const void* v, int64_t T, int64_t Hq, int64_t Hkv,
+                              int64_t d, int causal, float* mu, void* o, void* ws, size_t ws_bytes,
+                              const mix_attn_debug_t* dbg, void* stream) {
+  g_err.clear();
+  if (T < 0 || Hq < 0 || Hkv < 0 || d < 0) return fail(MIX_E_SHAPE, "mix_attn_prefill: negative extent");
+  if (T == 0 || Hq == 0 || d == 0) return MIX_OK;
+  if (Hkv == 0 || Hq % Hkv) return fail(MIX_E_SHAPE, "mix_attn_prefill: Hq=%lld is not a multiple of Hkv=%lld", (long long)Hq, (long long)Hkv);
+  if (d % 32) return fail(MIX_E_SHAPE, "mix_attn_prefill: head dim %lld is not a multiple of 32", (long long)d);
+  if (T > (1 << 24) || Hq * d > (1 << 20)) return fail(MIX_E_SHAPE, "mix_attn_prefill: extent too large");
+  if (!q || !k || !v || !mu || !o || !ws) return fail(MIX_E_NULL, "mix_attn_prefill: NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(mu) || ((uintptr_t)ws & 255u) || ((uintptr_t)o & 1u))
+    return fail(MIX_E_ALIGN, "mix_attn_prefill: q/k/v/mu must be 16-byte aligned and ws 256-byte aligned");
+  if (dbg && (!aligned16(dbg->p) || ((uintptr_t)dbg->p_shared & 1u)))
+    return fail(MIX_E_ALIGN, "mix_attn_prefill: debug p must be 16-byte aligned");
+  size_t need = mix::attn_prefill_ws_bytes(T, Hq, Hkv, d);
+  if (ws_bytes < need) return fail(MIX_E_WORKSPACE, "mix_attn_prefill: workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(mix::attn_prefill_run(q, k, v, T, Hq, Hkv, d, causal, mu, o, ws, dbg, (hipStream_t)stream),
+                    "mix_attn_prefill");
 }
-size_t mix_attn_decode_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int64_t) { return 0; }
-mix_status_t mix_attn_decode(const void*, const void*, const void*, const mix_kv_cache_t*, const int32_t*, int64_t,
-                             int64_t, const float*, void*, void*, size_t, const mix_attn_debug_t*, void*) {
-  g_err = "mix_attn_decode: not implemented";
-  return MIX_E_UNSUPPORTED;
+
+static mix_status_t check_cache(const char* fn, const mix_kv_cache_t* c) {
+  if (!c) return fail(MIX_E_NULL, "%s: cache is NULL", fn);
+  if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales || !c->v_stage)
+    return fail(MIX_E_NULL, "%s: a cache buffer is NULL", fn);
+  if (c->B <= 0 || c->Hkv <= 0 || c->Lmax <= 0 || c->Lmax % 32 || c->d <= 0 || c->d % 32)
+    return fail(MIX_E_SHAPE, "%s: bad cache extents (Lmax and d must be positive multiples of 32)", fn);
+  if (!aligned16(c->k_codes) || !aligned16(c->v_codes) || !aligned16(c->v_stage))
+    return fail(MIX_E_ALIGN, "%s: cache code buffers must be 16-byte aligned", fn);
+  return MIX_OK;
 }
+
+mix_status_t mix_kv_cache_prefill(const mix_kv_cache_t* cache, int64_t b, const void* k, const void* v, int64_t T,
+                                  const float* mu, void* stream) {
+  g_err.clear();
+  if (mix_status_t st = check_cache("mix_kv_cache_prefill", cache)) return st;
+  if (b < 0 || b >= cache->B) return fail(MIX_E_SHAPE, "mix_kv_cache_prefill: row %lld outside [0, %lld)", (long long)b, (long long)cache->B);
+  if (T <= 0 || T > cache->Lmax) return fail(MIX_E_SHAPE, "mix_kv_cache_prefill: T=%lld outside (0, Lmax]", (long long)T);
+  if (!k || !v || !mu) return fail(MIX_E_NULL, "mix_kv_cache_prefill: NULL pointer");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(mu)) return fail(MIX_E_ALIGN, "mix_kv_cache_prefill: k/v/mu must be 16-byte aligned");
+  return hip_status(mix::kv_cache_prefill_run(cache, b, k, v, T, mu, (hipStream_t)stream), "mix_kv_cache_prefill");
 }
+
+size_t mix_attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos) {
+  (void)Hkv;
+  if (B <= 0 || Hq <= 0 || d <= 0 || max_pos < 0) return 0;
+  return mix::attn_decode_ws_bytes(B, Hq, d, max_pos);
+}
+
+mix_status_t mix_attn_decode(const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* cache,
+                             const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
+                             size_t ws_bytes, const mix_attn_debug_t* dbg, void* stream) {
+  g_err.clear();
+  if (mix_status_t st = check_cache("mix_attn_decode", cache)) return st;
+  if (Hq <= 0 || Hq % cache->Hkv) return fail(MIX_E_SHAPE, "mix_attn_decode: Hq must be a positive multiple of Hkv");
+  if (cache->d != 128) return fail(MIX_E_UNSUPPORTED, "mix_attn_decode: head dim %lld (only 128 is implemented)", (long long)cache->d);
+  if (Hq / cache->Hkv > 16) return fail(MIX_E_UNSUPPORTED, "mix_attn_decode: more than 16 query heads per KV head");
+  if (max_pos < 0 || max_pos >= cache->Lmax) return fail(MIX_E_SHAPE, "mix_attn_decode: max_pos=%lld outside [0, Lmax)", (long long)max_pos);
+  if (!q || !k_new || !v_new || !pos || !mu || !o || !ws) return fail(MIX_E_NULL, "mix_attn_decode: NULL pointer");
+  if (((uintptr_t)ws & 255u) || !aligned16(q) || ((uintptr_t)o & 1u) || ((uintptr_t)pos & 3u) || ((uintptr_t)mu & 3u))
+    return fail(MIX_E_ALIGN, "mix_attn_decode: misaligned argument (ws must be 256-byte aligned, q 16-byte)");
+  if (dbg && !aligned16(dbg->p)) return fail(MIX_E_ALIGN, "mix_attn_decode: debug p must be 16-byte aligned");
+  size_t need = mix::attn_decode_ws_bytes(cache->B, Hq, cache->d, max_pos);
+  if (ws_bytes < need) return fail(MIX_E_WORKSPACE, "mix_attn_decode: workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(mix::attn_decode_run(q, k_new, v_new, cache, pos, max_pos, Hq, mu, o, ws, dbg, (hipStream_t)stream),
+                    "mix_attn_decode");
+}
+
+}  // extern "C"

@@ -1,0 +1,627 @@
+// K-smoothed attention over MiX/MX-coded operands, prefill and decode, for gfx950.
+//
+// What it computes (P1, 方法概览 / method overview, last bullet; 核心创新 / innovations, third
+// bullet; 关键结果 / key results, first bullet): keys are smoothed by subtracting their per-channel
+// mean over the prefill tokens (softmax is unchanged by a constant shift per query row), the mean is
+// kept frozen for decode so cached keys are never re-coded, and both attention products run on
+// low-bit operands. Operand formats: Q and P as MiX-4.5b (activations, blocks along the head
+// dimension and along keys); smoothed K and V as MXFP4 (cached operands, blocks along the head
+// dimension and along tokens).
+//
+// Prefill is unfused: quantizers, then S = Q^ K^T on the block-scaled MFMA GEMM, then one wave
+// per query row computes z = fp32(S) * fp32(1/sqrt(d)), the exact row max, p = exp(z - m),
+// l = sum p and P^ = MiX-4.5b(p) along keys, then O = (P^ V^)/l on the same GEMM.
+//
+// Decode keeps the exact global row max with two passes over the keys: pass 1 (scores) computes S
+// for 256-key chunks on the MFMA and per-chunk maxima; pass 2 (pv) takes the global max, forms p
+// and P^ for its chunk and multiplies by V^ on the MFMA; a final kernel sums the chunk partials.
+#include "../../include/mixlib.h"
+#include "common.h"
+#include "kernels.h"
+#include "quant_dev.h"
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+namespace mix {
+
+// ------------------------------------------------------------------ one MiX-4.5b sub-block of p
+
+// Codes the 8 values of this lane (one 8-element sub-block; a quad of lanes is one 32-element
+// block) as MiX-4.5b. Returns the code word; *shared receives the block's field on the quad's
+// first lane; *m_out this sub-block's mantissa.
+__device__ __forceinline__ uint32_t mix45_code8(const float (&p)[8], int quad_pos, uint32_t* shared,
+                                                uint32_t* m_out) {
+  uint32_t xb[8];
+  uint32_t lmax = 0;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    xb[e] = f32_bits(p[e]);
+    uint32_t a = xb[e] & 0x7FFFFFFFu;
+    lmax = a > lmax ? a : lmax;
+  }
+  uint32_t bmax = quad_max_u32(lmax);
+  int emax;
+  if (bmax == 0) emax = -7;
+  else {
+    int e = (int)(bmax >> 23) - 127;
+    emax = e < -7 ? -7 : (e > 8 ? 8 : e);
+  }
+  uint32_t m = mant3_of(lmax);
+  MixThresholds t = mix_thresholds(emax, m);
+  uint32_t word = 0;
+#pragma unroll
+  for (int e = 0; e < 8; e++) word |= mix_code(xb[e], t) << (4 * e);
+  uint32_t f = (quad_pos == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * quad_pos));
+  *shared = quad_or_u32(f);
+  *m_out = m;
+  return word;
+}
+
+// ------------------------------------------------------------------ prefill softmax + P coding
+
+constexpr int SM_NREG = 8;  // row chunks of 512 logits kept in registers (rows up to 4096 keys)
+
+__device__ __forceinline__ void load8f(const float* p, float (&v)[8]) {
+  float4 a = *(const float4*)p;
+  float4 b = *(const float4*)(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void softmax_chunk(const float (&s)[8], int j0, int n_valid, float scale, float m,
+                                              int64_t row, int Tp, float& lsum, uint8_t* pc, uint16_t* ps,
+                                              float* dbg_p, int lane) {
+  float p[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    float v = 0.f;
+    if (j0 + e < n_valid) v = expf(__fsub_rn(__fmul_rn(s[e], scale), m));
+    p[e] = v;
+    lsum += v;
+  }
+  uint32_t sh, msub;
+  uint32_t word = mix45_code8(p, lane & 3, &sh, &msub);
+  *(uint32_t*)(pc + row * (int64_t)(Tp >> 1) + (j0 >> 1)) = word;
+  if ((lane & 3) == 0) ps[row * (int64_t)(Tp >> 5) + (j0 >> 5)] = (uint16_t)sh;
+  if (dbg_p) {
+    float* d = dbg_p + row * (int64_t)Tp + j0;
+    *(float4*)d = make_float4(p[0], p[1], p[2], p[3]);
+    *(float4*)(d + 4) = make_float4(p[4], p[5], p[6], p[7]);
+  }
+}
+
+// One wave per query row (h, i) of S [Hq, T, Tp]. Writes P^ codes [Hq, T, Tp/2] and shared
+// [Hq, T, Tp/32] for keys [0, n_write), l [Hq, T]; masked keys are zero.
+__global__ void __launch_bounds__(256) k_softmax_pquant(const float* __restrict__ S, int T, int Tp, int64_t nrows,
+                                                         int causal, float scale, uint8_t* __restrict__ pc,
+                                                         uint16_t* __restrict__ ps, float* __restrict__ l,
+                                                         float* __restrict__ dbg_p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  const int i = (int)(row % T);
+  const int n_valid = causal ? i + 1 : T;
+  const int n_write = causal ? min(Tp, ((i + 1 + 255) / 256) * 256) : Tp;
+  const float* srow = S + row * (int64_t)Tp;
+  const int nit_valid = (n_valid + 511) / 512;
+  const int nit_write = (n_write + 511) / 512;
+
+  float cache[SM_NREG][8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int it = 0; it < SM_NREG; it++) {
+    if (it < nit_valid) {
+      int j0 = it * 512 + lane * 8;
+      if (j0 < n_valid) {
+        load8f(srow + j0, cache[it]);
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          if (j0 + e < n_valid) mx = fmaxf(mx, cache[it][e]);
+      }
+    }
+  }
+  for (int it = SM_NREG; it < nit_valid; it++) {
+    int j0 = it * 512 + lane * 8;
+    if (j0 < n_valid) {
+      float v[8];
+      load8f(srow + j0, v);
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+        if (j0 + e < n_valid) mx = fmaxf(mx, v[e]);
+    }
+  }
+  mx = wave_max_f32(mx);
+  const float m = __fmul_rn(mx, scale);  // rounding is monotone: max of z = fp32(max S * scale)
+
+  float lsum = 0.f;
+#pragma unroll
+  for (int it = 0; it < SM_NREG; it++) {
+    if (it < nit_write) {
+      int j0 = it * 512 + lane * 8;
+      if (j0 < n_write) {  // n_write is a multiple of 32: quads stay whole
+        float v[8];
+        if (it < nit_valid && j0 < n_valid) {
+#pragma unroll
+          for (int e = 0; e < 8; e++) v[e] = cache[it][e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; e++) v[e] = 0.f;
+        }
+        softmax_chunk(v, j0, n_valid, scale, m, row, Tp, lsum, pc, ps, dbg_p, lane);
+      }
+    }
+  }
+  for (int it = SM_NREG; it < nit_write; it++) {
+    int j0 = it * 512 + lane * 8;
+    if (j0 < n_write) {
+      float v[8];
+      if (j0 < n_valid) load8f(srow + j0, v);
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) v[e] = 0.f;
+      }
+      softmax_chunk(v, j0, n_valid, scale, m, row, Tp, lsum, pc, ps, dbg_p, lane);
+    }
+  }
+  lsum = wave_sum_f32(lsum);
+  if (lane == 0) l[row] = lsum;
+}
+
+// ------------------------------------------------------------------ decode: append
+
+// grid (Hkv, B), block d threads (one channel each). Codes the new key (smoothed with the frozen
+// mean) into slot pos, stages the new value and re-codes the value block that holds it from the
+// staged tokens present (zero for the rest).
+__global__ void k_kv_append(const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                            const float* __restrict__ mu, const int32_t* __restrict__ pos, int64_t max_pos, int Hkv,
+                            int d, int64_t Lmax, uint8_t* __restrict__ kc, uint8_t* __restrict__ ks,
+                            uint8_t* __restrict__ vc, uint8_t* __restrict__ vs, uint16_t* __restrict__ stage) {
+  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int p = pos[b];
+  if (p < 0 || p > max_pos) return;
+  const int64_t bh = (int64_t)b * Hkv + h;
+  // ---- key: MXFP4 of fp32(k - mu) along the head dimension (32-channel blocks = half waves)
+  float kx = __fsub_rn(__uint_as_float((uint32_t)k_new[bh * d + c] << 16), mu[bh * d + c]);
+  uint32_t kb = f32_bits(kx);
+  uint32_t amax = kb & 0x7FFFFFFFu;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)amax, off, 32);
+    amax = o > amax ? o : amax;
+  }
+  int X = mx_exponent(amax, 1);
+  uint32_t nib = amax ? fp4_code(kb, fp4_thresholds(X)) : 0u;
+  uint32_t nxt = (uint32_t)__shfl_down((int)nib, 1, 32);
+  const int64_t krow = bh * Lmax + p;
+  if ((c & 1) == 0) kc[krow * (d >> 1) + (c >> 1)] = (uint8_t)(nib | (nxt << 4));
+  if ((c & 31) == 0) ks[krow * (d >> 5) + (c >> 5)] = amax ? (uint8_t)(X + 127) : (uint8_t)0;
+  // ---- value: stage, then code the block along tokens
+  const int slot = p & 31;
+  const uint16_t vnew = v_new[bh * d + c];
+  stage[(((int64_t)b * 32 + slot) * Hkv + h) * d + c] = vnew;
+  uint32_t vb[32];
+  uint32_t vmax = 0;
+#pragma unroll
+  for (int s = 0; s < 32; s++) {
+    uint32_t u = 0;
+    if (s < slot) u = (uint32_t)stage[(((int64_t)b * 32 + s) * Hkv + h) * d + c] << 16;
+    else if (s == slot) u = (uint32_t)vnew << 16;
+    vb[s] = u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    vmax = a > vmax ? a : vmax;
+  }
+  int XV = mx_exponent(vmax, 1);
+  uint32_t w[4] = {0, 0, 0, 0};
+  if (vmax) {
+    Fp4Thr r = fp4_thresholds(XV);
+#pragma unroll
+    for (int s = 0; s < 32; s++) w[s >> 3] |= fp4_code(vb[s], r) << (4 * (s & 7));
+  }
+  const int64_t vrow = bh * d + c;
+  *(uint4*)(vc + vrow * (Lmax >> 1) + (p >> 5) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  vs[vrow * (Lmax >> 5) + (p >> 5)] = vmax ? (uint8_t)(XV + 127) : (uint8_t)0;
+}
+
+// ------------------------------------------------------------------ decode: scores (pass 1)
+
+constexpr int DCH = 256;  // keys per chunk
+
+// grid (nchunk, Hkv, B), block 256 (4 waves x 64 keys). Requires d == 128 and G = Hq/Hkv <= 16.
+// S [B, Hq, Lp] fp32 for keys <= pos; pmax [B, Hq, nchunk].
+__global__ void __launch_bounds__(256) k_decode_scores(const uint8_t* __restrict__ qc, const uint16_t* __restrict__ qs,
+                                                        const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks,
+                                                        const int32_t* __restrict__ pos, int64_t max_pos, int Hq,
+                                                        int Hkv, int64_t Lmax, int64_t Lp, int nchunk,
+                                                        float* __restrict__ S, float* __restrict__ pmax) {
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int p = pos[b];
+  if (p < 0 || p > max_pos || chunk * DCH > p) return;
+  const int G = Hq / Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  __shared__ float smax[4][16];
+
+  // A operand: the G query rows of this KV head as E4M3, per-block scales 2^(Emax-1)
+  v8i af = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  int sa = 127;
+  if (r < G) {
+    const int64_t qrow = (int64_t)b * Hq + (int64_t)h * G + r;
+    const uint8_t* qrc = qc + qrow * 64;
+    const uint16_t* qrs = qs + qrow * 4;
+    // bytes for K elements [16 g, 16 g + 16): block g/2, sub-blocks 2 (g&1), 2 (g&1) + 1
+    uint32_t o[8];
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+      int blk = (g >> 1) + 2 * half;
+      uint32_t sh = qrs[blk];
+      uint2 wv = *(const uint2*)(qrc + blk * 16 + (g & 1) * 8);
+      mix8_to_e4m3(wv.x, (sh >> (4 + 3 * (2 * (g & 1)))) & 7u, o[4 * half + 0], o[4 * half + 1]);
+      mix8_to_e4m3(wv.y, (sh >> (4 + 3 * (2 * (g & 1) + 1))) & 7u, o[4 * half + 2], o[4 * half + 3]);
+    }
+    af = v8i{(int)o[0], (int)o[1], (int)o[2], (int)o[3], (int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+    sa = (int)(qrs[g] & 15u) + 119;
+  }
+  float rmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  const int64_t bh = (int64_t)b * Hkv + h;
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const int j0 = chunk * DCH + wave * 64 + t * 16;
+    if (j0 > p) break;
+    const int j = j0 + r;
+    v8i bf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    int sb = 127;
+    if (j <= p) {
+      uint4 v = *(const uint4*)(kc + (bh * Lmax + j) * 64 + g * 16);
+      bf = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      sb = ks[(bh * Lmax + j) * 4 + g];
+    }
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc, 0, 4, 0, sa, 0, sb);
+    // result register i: query row 4 g + i, key j0 + r
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      int qr = 4 * g + i;
+      if (qr < G && j <= p) {
+        S[((int64_t)b * Hq + (int64_t)h * G + qr) * Lp + j] = acc[i];
+        rmax[i] = fmaxf(rmax[i], acc[i]);
+      }
+    }
+  }
+  // max over the 16 lanes that share a query row (lane bits 0..3)
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) rmax[i] = fmaxf(rmax[i], __shfl_xor(rmax[i], off, 64));
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) smax[wave][4 * g + i] = rmax[i];
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float v = fmaxf(fmaxf(smax[0][threadIdx.x], smax[1][threadIdx.x]), fmaxf(smax[2][threadIdx.x], smax[3][threadIdx.x]));
+    pmax[((int64_t)b * Hq + (int64_t)h * G + threadIdx.x) * nchunk + chunk] = v;
+  }
+}
+
+// ------------------------------------------------------------------ decode: p, P^ and P^ V^ (pass 2)
+
+// grid (nchunk, Hkv, B), block 256. P^ codes [B, Hq, Lp/2], shared [B, Hq, Lp/32];
+// lpart [B, Hq, nchunk]; opart [B, Hq, nchunk, 128].
+__global__ void __launch_bounds__(256) k_decode_pv(const float* __restrict__ S, const float* __restrict__ pmax,
+                                                    const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
+                                                    const int32_t* __restrict__ pos, int64_t max_pos, int Hq, int Hkv,
+                                                    int64_t Lmax, int64_t Lp, int nchunk, float scale,
+                                                    uint8_t* __restrict__ pc, uint16_t* __restrict__ ps,
+                                                    float* __restrict__ lpart, float* __restrict__ opart,
+                                                    float* __restrict__ dbg_p) {
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int p = pos[b];
+  if (p < 0 || p > max_pos || chunk * DCH > p) return;
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float sm[16];
+  __shared__ uint8_t sP[16][DCH];  // P^ as E4M3, row-major; rows >= G stay zero
+  __shared__ uint8_t sPs[16][DCH / 32];
+
+  // global row max over the chunks that hold keys <= pos
+  const int last = p / DCH;
+  if (tid < 16) {
+    float v = -INFINITY;
+    if (tid < G) {
+      const float* pm = pmax + ((int64_t)b * Hq + (int64_t)h * G + tid) * nchunk;
+      for (int c = 0; c <= last; c++) v = fmaxf(v, pm[c]);
+    }
+    sm[tid] = __fmul_rn(v, scale);
+  }
+  for (int i = tid; i < 16 * DCH / 4; i += 256) ((uint32_t*)sP)[i] = 0u;
+  for (int i = tid; i < 16 * DCH / 32; i += 256) ((uint8_t*)sPs)[i] = 127;
+  __syncthreads();
+
+  // p and P^: thread -> (row = tid / 32, sub-block = tid % 32); 8 rows per pass
+  for (int r0 = 0; r0 < G; r0 += 8) {
+    const int row = r0 + (tid >> 5), sb = tid & 31;
+    if (row < G) {  // 32 threads per row: whole quads
+      const int64_t qrow = (int64_t)b * Hq + (int64_t)h * G + row;
+      const int jb = chunk * DCH + sb * 8;
+      const float m = sm[row];
+      float pv[8];
+      float lsum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        int j = jb + e;
+        float v = 0.f;
+        if (j <= p) v = expf(__fsub_rn(__fmul_rn(S[qrow * Lp + j], scale), m));
+        pv[e] = v;
+        lsum += v;
+      }
+      uint32_t shf, msub;
+      uint32_t word = mix45_code8(pv, sb & 3, &shf, &msub);
+      *(uint32_t*)(pc + qrow * (Lp >> 1) + (jb >> 1)) = word;
+      if ((sb & 3) == 0) {
+        ps[qrow * (Lp >> 5) + (jb >> 5)] = (uint16_t)shf;
+        sPs[row][sb >> 2] = (uint8_t)((shf & 15u) + 119u);
+      }
+      uint32_t e0, e1;
+      mix8_to_e4m3(word, msub, e0, e1);
+      *(uint2*)(&sP[row][sb * 8]) = make_uint2(e0, e1);
+      if (dbg_p) {
+        float* d = dbg_p + qrow * Lp + jb;
+        *(float4*)d = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        *(float4*)(d + 4) = make_float4(pv[4], pv[5], pv[6], pv[7]);
+      }
+      // l partial: sum over the 32 threads of this row (half a wave)
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off, 32);
+      if (sb == 0) lpart[qrow * nchunk + chunk] = lsum;
+    }
+  }
+  __syncthreads();
+
+  // O partial = P^ V^ over this chunk: wave w handles channel tiles 2w, 2w+1 (16 channels each)
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t bh = (int64_t)b * Hkv + h;
+  v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ks = 0; ks < DCH / 128; ks++) {
+    const int kbase = chunk * DCH + ks * 128;  // first key of this K step
+    if (kbase > p) break;
+    uint4 lo = *(const uint4*)(&sP[r][ks * 128 + 16 * g]);
+    uint4 hi = *(const uint4*)(&sP[r][ks * 128 + 64 + 16 * g]);
+    v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    int sa = sPs[r][ks * 4 + g];
+    const bool blk_live = kbase + 32 * g <= p;  // V blocks past the newest token are not read
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const int ch = (2 * wave + t) * 16 + r;
+      v8i bf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      int sb = 127;
+      if (blk_live) {
+        uint4 v = *(const uint4*)(vc + (bh * 128 + ch) * (Lmax >> 1) + ((kbase + 32 * g) >> 1));
+        bf = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        sb = vs[(bh * 128 + ch) * (Lmax >> 5) + ((kbase + 32 * g) >> 5)];
+      }
+      acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc[t], 0, 4, 0, sa, 0, sb);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const int ch = (2 * wave + t) * 16 + r;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      int row = 4 * g + i;
+      if (row < G) opart[(((int64_t)b * Hq + (int64_t)h * G + row) * nchunk + chunk) * 128 + ch] = acc[t][i];
+    }
+  }
+}
+
+// grid (B * Hq), block d: O = sum_chunks O_part / sum_chunks l_part, rounded to bf16.
+__global__ void k_decode_combine(const float* __restrict__ lpart, const float* __restrict__ opart,
+                                 const int32_t* __restrict__ pos, int64_t max_pos, int Hq, int nchunk, int d,
+                                 uint16_t* __restrict__ o, float* __restrict__ dbg_l) {
+  const int64_t qrow = blockIdx.x;
+  const int b = (int)(qrow / Hq), c = threadIdx.x;
+  const int p = pos[b];
+  if (p < 0 || p > max_pos) {
+    o[qrow * d + c] = 0;
+    return;
+  }
+  const int last = p / DCH;
+  float l = 0.f, acc = 0.f;
+  for (int k = 0; k <= last; k++) {
+    l += lpart[qrow * nchunk + k];
+    acc += opart[(qrow * nchunk + k) * d + c];
+  }
+  o[qrow * d + c] = f32_to_bf16_rne(__fdiv_rn(acc, l));
+  if (dbg_l && c == 0) dbg_l[qrow] = l;
+}
+
+// ------------------------------------------------------------------ host orchestration
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct PrefillWs {
+  size_t qc, qs, kc, ks, vc, vs, s, pc, ps, l, total;
+};
+
+static PrefillWs prefill_layout(int64_t T, int64_t Hq, int64_t Hkv, int64_t d) {
+  const int64_t Tp = (T + 31) / 32 * 32;
+  PrefillWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  w.qc = take((size_t)T * Hq * d / 2);
+  w.qs = take((size_t)T * Hq * (d / 32) * 2);
+  w.kc = take((size_t)T * Hkv * d / 2);
+  w.ks = take((size_t)T * Hkv * (d / 32));
+  w.vc = take((size_t)Hkv * d * Tp / 2);
+  w.vs = take((size_t)Hkv * d * (Tp / 32));
+  w.s = take((size_t)Hq * T * Tp * 4);
+  w.pc = take((size_t)Hq * T * Tp / 2);
+  w.ps = take((size_t)Hq * T * (Tp / 32) * 2);
+  w.l = take((size_t)Hq * T * 4);
+  w.total = off;
+  return w;
+}
+
+size_t attn_prefill_ws_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t d) {
+  return prefill_layout(T, Hq, Hkv, d).total;
+}
+
+#define HIPCHK(x)                      \
+  do {                                 \
+    hipError_t e_ = (x);               \
+    if (e_ != hipSuccess) return e_;   \
+  } while (0)
+
+hipError_t attn_prefill_run(const void* q, const void* k, const void* v, int64_t T, int64_t Hq, int64_t Hkv,
+                            int64_t d, int causal, float* mu, void* o, void* ws, const mix_attn_debug_t* dbg,
+                            hipStream_t s) {
+  const int64_t Tp = (T + 31) / 32 * 32;
+  const int64_t G = Hq / Hkv;
+  PrefillWs w = prefill_layout(T, Hq, Hkv, d);
+  uint8_t* base = (uint8_t*)ws;
+  uint8_t* qc = base + w.qc;
+  uint16_t* qs = (uint16_t*)(base + w.qs);
+  uint8_t* kc = base + w.kc;
+  uint8_t* ks = base + w.ks;
+  uint8_t* vc = base + w.vc;
+  uint8_t* vs = base + w.vs;
+  float* S = (float*)(base + w.s);
+  uint8_t* pc = base + w.pc;
+  uint16_t* ps = (uint16_t*)(base + w.ps);
+  float* l = (float*)(base + w.l);
+
+  // 1. K-mean; 2. coded operands
+  HIPCHK(launch_kmean(k, 1, T, Hkv * d, Hkv * d, mu, s));
+  HIPCHK(launch_mx_quantize(1, k, 1, T, Hkv * d, Hkv * d, mu, kc, ks, s));
+  HIPCHK(launch_mix_quantize(1, q, 1, T, Hq * d, Hq * d, qc, qs, s));
+  HIPCHK(launch_mx_quantize_cols(v, 1, T, Tp, Hkv * d, Hkv * d, vc, vs, Tp / 2, Tp / 32, s));
+
+  // 3. S = Q^ K^T per query head
+  GemmArgs g1{};
+  g1.a_codes = qc; g1.a_shared = qs; g1.a_pitch = Hq * d / 2; g1.a_sh_pitch = Hq * d / 32;
+  g1.a_bstride = d / 2; g1.a_sh_bstride = d / 32;
+  g1.b_codes = kc; g1.b_scales = ks; g1.b_pitch = Hkv * d / 2; g1.b_sc_pitch = Hkv * d / 32;
+  g1.b_bstride = d / 2; g1.b_sc_bstride = d / 32; g1.b_group = (int)G;
+  g1.c = S; g1.ldc = Tp; g1.c_bstride = T * Tp; g1.row_div = nullptr;
+  g1.M = (int)T; g1.N = (int)T; g1.K = (int)d; g1.batch = (int)Hq; g1.causal = causal ? 1 : 0;
+  HIPCHK(launch_gemm_mfma(1, 1, 0, g1, s));
+
+  // 4. softmax and P^
+  const float scale = (float)(1.0 / sqrt((double)d));
+  const int64_t nrows = Hq * T;
+  hipLaunchKernelGGL(k_softmax_pquant, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, S, (int)T, (int)Tp, nrows,
+                     causal, scale, pc, ps, l, dbg ? dbg->p : nullptr);
+  HIPCHK(hipGetLastError());
+
+  // 5. O = (P^ V^) / l
+  GemmArgs g2{};
+  g2.a_codes = pc; g2.a_shared = ps; g2.a_pitch = Tp / 2; g2.a_sh_pitch = Tp / 32;
+  g2.a_bstride = T * Tp / 2; g2.a_sh_bstride = T * (Tp / 32);
+  g2.b_codes = vc; g2.b_scales = vs; g2.b_pitch = Tp / 2; g2.b_sc_pitch = Tp / 32;
+  g2.b_bstride = d * Tp / 2; g2.b_sc_bstride = d * (Tp / 32); g2.b_group = (int)G;
+  g2.c = o; g2.ldc = Hq * d; g2.c_bstride = d; g2.row_div = l; g2.row_div_bstride = T;
+  g2.M = (int)T; g2.N = (int)d; g2.K = (int)Tp; g2.batch = (int)Hq; g2.causal = causal ? 2 : 0;
+  HIPCHK(launch_gemm_mfma(1, 1, 1, g2, s));
+
+  if (dbg) {
+    if (dbg->s) HIPCHK(hipMemcpyAsync(dbg->s, S, (size_t)Hq * T * Tp * 4, hipMemcpyDeviceToDevice, s));
+    if (dbg->p_codes) HIPCHK(hipMemcpyAsync(dbg->p_codes, pc, (size_t)Hq * T * Tp / 2, hipMemcpyDeviceToDevice, s));
+    if (dbg->p_shared)
+      HIPCHK(hipMemcpyAsync(dbg->p_shared, ps, (size_t)Hq * T * (Tp / 32) * 2, hipMemcpyDeviceToDevice, s));
+    if (dbg->l) HIPCHK(hipMemcpyAsync(dbg->l, l, (size_t)Hq * T * 4, hipMemcpyDeviceToDevice, s));
+  }
+  return hipSuccess;
+}
+
+hipError_t kv_cache_prefill_run(const mix_kv_cache_t* c, int64_t b, const void* k, const void* v, int64_t T,
+                                const float* mu, hipStream_t s) {
+  const int64_t Hkv = c->Hkv, d = c->d, Lmax = c->Lmax;
+  const int64_t Tp = (T + 31) / 32 * 32;
+  for (int64_t h = 0; h < Hkv; h++) {
+    const int64_t bh = b * Hkv + h;
+    HIPCHK(launch_mx_quantize(1, (const uint16_t*)k + h * d, 1, T, d, Hkv * d, mu + h * d,
+                              c->k_codes + bh * Lmax * (d / 2), c->k_scales + bh * Lmax * (d / 32), s));
+    HIPCHK(launch_mx_quantize_cols((const uint16_t*)v + h * d, 1, T, Tp, d, Hkv * d, c->v_codes + bh * d * (Lmax / 2),
+                                   c->v_scales + bh * d * (Lmax / 32), Lmax / 2, Lmax / 32, s));
+  }
+  const int64_t rem = T % 32;
+  if (rem) {
+    HIPCHK(hipMemcpyAsync((uint16_t*)c->v_stage + b * 32 * Hkv * d, (const uint16_t*)v + (T - rem) * Hkv * d,
+                          (size_t)rem * Hkv * d * 2, hipMemcpyDeviceToDevice, s));
+  }
+  return hipSuccess;
+}
+
+struct DecodeWs {
+  size_t qc, qs, s, pmax, pc, ps, lpart, opart, total;
+};
+
+static DecodeWs decode_layout(int64_t B, int64_t Hq, int64_t d, int64_t max_pos, int64_t* Lp_out, int* nchunk_out) {
+  const int nchunk = (int)((max_pos + 1 + DCH - 1) / DCH);
+  const int64_t Lp = (int64_t)nchunk * DCH;
+  DecodeWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  w.qc = take((size_t)B * Hq * d / 2);
+  w.qs = take((size_t)B * Hq * (d / 32) * 2);
+  w.s = take((size_t)B * Hq * Lp * 4);
+  w.pmax = take((size_t)B * Hq * nchunk * 4);
+  w.pc = take((size_t)B * Hq * Lp / 2);
+  w.ps = take((size_t)B * Hq * (Lp / 32) * 2);
+  w.lpart = take((size_t)B * Hq * nchunk * 4);
+  w.opart = take((size_t)B * Hq * nchunk * d * 4);
+  w.total = off;
+  if (Lp_out) *Lp_out = Lp;
+  if (nchunk_out) *nchunk_out = nchunk;
+  return w;
+}
+
+size_t attn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t d, int64_t max_pos) {
+  return decode_layout(B, Hq, d, max_pos, nullptr, nullptr).total;
+}
+
+hipError_t attn_decode_run(const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* c,
+                           const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
+                           const mix_attn_debug_t* dbg, hipStream_t s) {
+  const int64_t B = c->B, Hkv = c->Hkv, d = c->d, Lmax = c->Lmax;
+  int64_t Lp;
+  int nchunk;
+  DecodeWs w = decode_layout(B, Hq, d, max_pos, &Lp, &nchunk);
+  uint8_t* base = (uint8_t*)ws;
+  uint8_t* qc = base + w.qc;
+  uint16_t* qs = (uint16_t*)(base + w.qs);
+  float* S = (float*)(base + w.s);
+  float* pmax = (float*)(base + w.pmax);
+  uint8_t* pc = base + w.pc;
+  uint16_t* ps = (uint16_t*)(base + w.ps);
+  float* lpart = (float*)(base + w.lpart);
+  float* opart = (float*)(base + w.opart);
+
+  hipLaunchKernelGGL(k_kv_append, dim3((unsigned)Hkv, (unsigned)B), dim3((unsigned)d), 0, s, (const uint16_t*)k_new,
+                     (const uint16_t*)v_new, mu, pos, max_pos, (int)Hkv, (int)d, Lmax, c->k_codes, c->k_scales,
+                     c->v_codes, c->v_scales, (uint16_t*)c->v_stage);
+  HIPCHK(hipGetLastError());
+  HIPCHK(launch_mix_quantize(1, q, 1, B * Hq, d, d, qc, qs, s));
+  dim3 grid((unsigned)nchunk, (unsigned)Hkv, (unsigned)B);
+  hipLaunchKernelGGL(k_decode_scores, grid, dim3(256), 0, s, qc, qs, c->k_codes, c->k_scales, pos, max_pos, (int)Hq,
+                     (int)Hkv, Lmax, Lp, nchunk, S, pmax);
+  HIPCHK(hipGetLastError());
+  const float scale = (float)(1.0 / sqrt((double)d));
+  hipLaunchKernelGGL(k_decode_pv, grid, dim3(256), 0, s, S, pmax, c->v_codes, c->v_scales, pos, max_pos, (int)Hq,
+                     (int)Hkv, Lmax, Lp, nchunk, scale, pc, ps, lpart, opart, dbg ? dbg->p : nullptr);
+  HIPCHK(hipGetLastError());
+  hipLaunchKernelGGL(k_decode_combine, dim3((unsigned)(B * Hq)), dim3((unsigned)d), 0, s, lpart, opart, pos, max_pos,
+                     (int)Hq, nchunk, (int)d, (uint16_t*)o, dbg ? dbg->l : nullptr);
+  HIPCHK(hipGetLastError());
+  if (dbg) {
+    if (dbg->s) HIPCHK(hipMemcpyAsync(dbg->s, S, (size_t)B * Hq * Lp * 4, hipMemcpyDeviceToDevice, s));
+    if (dbg->p_codes) HIPCHK(hipMemcpyAsync(dbg->p_codes, pc, (size_t)B * Hq * Lp / 2, hipMemcpyDeviceToDevice, s));
+    if (dbg->p_shared)
+      HIPCHK(hipMemcpyAsync(dbg->p_shared, ps, (size_t)B * Hq * (Lp / 32) * 2, hipMemcpyDeviceToDevice, s));
+  }
+  return hipSuccess;
+}
+
+}  // namespace mix

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/mixlib.h"
+
 namespace mix {
 
 hipError_t launch_mix_quantize(int fmt, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
@@ -11,7 +13,7 @@ hipError_t launch_mix_quantize(int fmt, const void* x, int dtype, int64_t rows, 
 hipError_t launch_mx_quantize(int fp4, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                               const float* mu, uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_mx_quantize_cols(const void* x, int dtype, int64_t rows, int64_t prows, int64_t cols, int64_t ldx,
-                                   uint8_t* codes, uint8_t* scales, hipStream_t s);
+                                   uint8_t* codes, uint8_t* scales, int64_t cpitch, int64_t spitch, hipStream_t s);
 hipError_t launch_mix_dequantize(int fmt, const uint8_t* codes, const void* shared, int64_t rows, int64_t cols,
                                  float* out, hipStream_t s);
 hipError_t launch_mx_dequantize(int fp4, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
@@ -41,5 +43,17 @@ struct GemmArgs {
 
 hipError_t launch_gemm_mfma(int a_fmt, int b_fp4, int c_bf16, const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_eq6(int a_fmt, int b_fp4, int c_bf16, const GemmArgs& g, hipStream_t s);
+
+// attention (arguments validated by the C-ABI layer)
+size_t attn_prefill_ws_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t d);
+hipError_t attn_prefill_run(const void* q, const void* k, const void* v, int64_t T, int64_t Hq, int64_t Hkv,
+                            int64_t d, int causal, float* mu, void* o, void* ws, const mix_attn_debug_t* dbg,
+                            hipStream_t s);
+hipError_t kv_cache_prefill_run(const mix_kv_cache_t* c, int64_t b, const void* k, const void* v, int64_t T,
+                                const float* mu, hipStream_t s);
+size_t attn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t d, int64_t max_pos);
+hipError_t attn_decode_run(const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* c,
+                           const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
+                           const mix_attn_debug_t* dbg, hipStream_t s);
 
 }  // namespace mix

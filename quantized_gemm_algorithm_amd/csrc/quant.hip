@@ -12,14 +12,7 @@
 // Layout of one lane's work: a lane owns one 8-element sub-block (16 B of bf16 or 32 B of fp32),
 // a quad of lanes owns one 32-element block. The block max is a quad reduction over DPP. Codes
 // leave as one 32-bit word per lane (8 nibbles), so a wave stores 256 contiguous bytes.
-//
-// Element decision. With M = 1 + m/8 the nonzero magnitudes are c_d = M 2^(Emax-d). The nearest
-// one (ties to the smaller magnitude) is c_d* with d* = #{d : a <= mid_d}, mid_d the midpoint of
-// c_d and c_(d+1). For d <= 5 the midpoints are 1.5 M 2^(Emax-1-d), a geometric sequence, so the
-// count is an exponent difference plus one mantissa comparison -- the naive dE plus its +-1
-// refinement. Only the last step differs by sign: positives have c_7 (the reclaimed pattern) and
-// then zero; negatives go from c_6 to zero. All thresholds are exact fp32 values and every
-// comparison is an unsigned comparison of fp32 bit patterns, so the decision is exact.
+
 #include "common.h"
 #include "kernels.h"
 #include "quant_dev.h"
@@ -145,12 +138,14 @@ __global__ void __launch_bounds__(256) k_mx_quantize(const void* __restrict__ x,
 
 // ------------------------------------------------------------------ MX quantizer, blocks along columns
 // x [rows, cols] (row pitch ldx); a block is 32 consecutive rows of one column. Output codes
-// [cols, rows/2] and scales [cols, rows/32] (the transposed layout used for V along tokens).
-// Rows beyond `rows` up to the padded count `prows` are zero.
+// [cols, >= prows/2] and scales [cols, >= prows/32] with row pitches cpitch / spitch bytes (the
+// transposed layout used for V along tokens). Rows beyond `rows` up to the padded count `prows`
+// are zero.
 template <int DT>
 __global__ void __launch_bounds__(256) k_mx_quantize_cols(const void* __restrict__ x, int64_t rows, int64_t prows,
                                                            int64_t cols, int64_t ldx, uint8_t* __restrict__ codes,
-                                                           uint8_t* __restrict__ scales) {
+                                                           uint8_t* __restrict__ scales, int64_t cpitch,
+                                                           int64_t spitch) {
   int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t rb = blockIdx.y;  // 32-row block
   if (c >= cols) return;
@@ -176,8 +171,8 @@ __global__ void __launch_bounds__(256) k_mx_quantize_cols(const void* __restrict
     for (int i = 0; i < 32; i++) w[i >> 3] |= fp4_code(xb[i], r) << (4 * (i & 7));
   }
   uint4 o = {w[0], w[1], w[2], w[3]};
-  *(uint4*)(codes + c * (prows >> 1) + rb * 16) = o;
-  scales[c * (prows >> 5) + rb] = amax ? (uint8_t)(X + 127) : (uint8_t)0;
+  *(uint4*)(codes + c * cpitch + rb * 16) = o;
+  scales[c * spitch + rb] = amax ? (uint8_t)(X + 127) : (uint8_t)0;
 }
 
 // ------------------------------------------------------------------ decoders (debug / tests)
@@ -315,10 +310,12 @@ hipError_t launch_mx_quantize(int fp4, const void* x, int dtype, int64_t rows, i
 }
 
 hipError_t launch_mx_quantize_cols(const void* x, int dtype, int64_t rows, int64_t prows, int64_t cols, int64_t ldx,
-                                   uint8_t* codes, uint8_t* scales, hipStream_t s) {
+                                   uint8_t* codes, uint8_t* scales, int64_t cpitch, int64_t spitch, hipStream_t s) {
   dim3 g((unsigned)((cols + 255) / 256), (unsigned)(prows / 32)), b(256);
-  if (dtype == 1) hipLaunchKernelGGL((k_mx_quantize_cols<1>), g, b, 0, s, x, rows, prows, cols, ldx, codes, scales);
-  else hipLaunchKernelGGL((k_mx_quantize_cols<0>), g, b, 0, s, x, rows, prows, cols, ldx, codes, scales);
+  if (dtype == 1)
+    hipLaunchKernelGGL((k_mx_quantize_cols<1>), g, b, 0, s, x, rows, prows, cols, ldx, codes, scales, cpitch, spitch);
+  else
+    hipLaunchKernelGGL((k_mx_quantize_cols<0>), g, b, 0, s, x, rows, prows, cols, ldx, codes, scales, cpitch, spitch);
   return hipGetLastError();
 }
 

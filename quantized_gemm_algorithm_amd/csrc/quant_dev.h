@@ -96,4 +96,45 @@ __device__ __forceinline__ int mx_exponent(uint32_t bmax, int fp4) {
 }
 
 
+// ------------------------------------------------------------------ code -> E4M3 decoders
+
+// 8 MiX nibbles (element e at bits 4e) with shared mantissa m -> 8 E4M3 bytes in element order.
+// byte = s<<7 | (8-dE)<<3 | m; nibble 0x7 (zero) -> 0x00; nibble 0xF -> (1<<3) | m.
+__device__ __forceinline__ void mix8_to_e4m3(uint32_t w, uint32_t m, uint32_t& out0, uint32_t& out1) {
+  const uint32_t m4 = m * 0x01010101u;
+  uint32_t r[2];
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    uint32_t x = (w >> (4 * h)) & 0x0F0F0F0Fu;  // h=0: elements 0,2,4,6; h=1: 1,3,5,7
+    uint32_t d = x & 0x07070707u;
+    uint32_t s = x & 0x08080808u;
+    uint32_t v = (0x40404040u - (d << 3)) | (s << 4) | m4;
+    uint32_t d7 = (d + 0x01010101u) & 0x08080808u;  // 0x08 in bytes with dE == 7
+    v &= ~(d7 << 4);                                // reclaimed pattern: positive
+    uint32_t z = d7 & ~s;                           // dE == 7 with sign 0: zero
+    v &= ~((z >> 3) * 0xFFu);
+    r[h] = v;
+  }
+  out0 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);
+  out1 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);
+}
+
+// 8 MXINT4 nibbles -> 8 E4M3 bytes of q/4 (q two's complement in [-8, 7]).
+__device__ __forceinline__ void int4x8_to_e4m3(uint32_t w, uint32_t& out0, uint32_t& out1) {
+  const uint32_t lo0 = 0x34302800u, lo1 = 0x3E3C3A38u;  // q = 0..7
+  const uint32_t hi0 = 0xBABCBEC0u, hi1 = 0xA8B0B4B8u;  // q = -8..-1
+  uint32_t r[2];
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    uint32_t x = (w >> (4 * h)) & 0x0F0F0F0Fu;
+    uint32_t sel = x & 0x07070707u;
+    uint32_t a = __builtin_amdgcn_perm(lo1, lo0, sel);
+    uint32_t b = __builtin_amdgcn_perm(hi1, hi0, sel);
+    uint32_t msk = ((x & 0x08080808u) >> 3) * 0xFFu;
+    r[h] = (a & ~msk) | (b & msk);
+  }
+  out0 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);
+  out1 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);
+}
+
 }  // namespace mix
