@@ -109,7 +109,7 @@ def code_p(p):
 
 
 def attn_prefill_ref(q, k, v, dtype="bf16", causal=True, rows=None, heads=None):
-    """Oracle prefill for Q [T, Hq, d], K/V [T, Hkv, d] (T % 32 == 0).
+    """Oracle prefill for Q [T, Hq, d], K/V [T, Hkv, d]; a ragged T is zero-padded to a multiple of 32.
 
     ``rows``/``heads`` restrict which query rows and heads are computed (all by
     default); everything they depend on (all keys, the K-mean) is still exact.
@@ -134,8 +134,10 @@ def attn_prefill_ref(q, k, v, dtype="bf16", causal=True, rows=None, heads=None):
         qd = mix_dequantize(qc[:, h], qs[:, h], "4.5b")  # [R, d]
         kd = mx_dequantize(kc[:, hk], ks[:, hk], "fp4")  # [T, d]
         vd = mx_dequantize(vc[hk], vs[hk], "fp4")  # [d, T]
-        S = qd @ kd.T  # exact products, fp64 sum
-        S = np.where(np.arange(T)[None, :] < n_valid[:, None], S, 0.0)
+        Tp = vd.shape[1]  # T rounded up to 32: keys past T are masked and code as zero (D17)
+        S = np.zeros((len(rows), Tp))
+        S[:, :T] = qd @ kd.T  # exact products, fp64 sum
+        S = np.where(np.arange(Tp)[None, :] < n_valid[:, None], S, 0.0)
         p, l, _ = softmax_rows(S.astype(np.float32), n_valid, d)
         pc, ps = code_p(p)
         pd = mix_dequantize(pc, ps, "4.5b")

@@ -102,3 +102,13 @@ def test_decode_partial_block_zero_padded():
     vc1, vs1 = code_v(g["v"], "bf16")
     vc2, vs2 = code_v(vpad, "bf16")
     assert np.array_equal(vc1, vc2) and np.array_equal(vs1, vs2)
+
+
+def test_ragged_prefill_pads_keys_with_zero():
+    # T = 40: the P^ and V^ blocks past T are zero, so O equals the O of the same inputs padded to 64
+    # tokens whose extra keys are masked (causal rows < 40 never see them).
+    g = attention_qkv(T=40, Hq=2, Hkv=1, d=32, seed_cfg=4)
+    r = attn_prefill_ref(g["q"], g["k"], g["v"], "bf16", causal=True)
+    assert r["p"].shape == (2, 40, 64)
+    assert np.all(r["p"][:, :, 40:] == 0)
+    assert np.all(r["p_codes"][:, :, 20:] == 0x77)
