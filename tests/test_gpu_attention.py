@@ -1,0 +1,284 @@
+"""GPU parity of the K-smoothed MiX/MX attention (prefill and decode) against the CPU oracle.
+
+Staged parity: every stage is checked against the oracle applied to the GPU's own input to that
+stage, so each comparison is exact or bounded:
+  1. the K-mean is bit-exact;
+  2. S is within the fp32 accumulation bound of the exact Q^ K^T;
+  3. the oracle's softmax of the GPU's S is within 4 ulp of the GPU's p (libm vs device exp);
+  4. the oracle's MiX-4.5b coding of the GPU's p reproduces the GPU's P^ bit for bit;
+  5. O is the bf16 rounding of (P^ V^)/l within the accumulation bound, given the GPU's P^ and l.
+End to end against a fully independent oracle run the P codes may flip at midpoints (exp differs by
+an ulp); that comparison only reports the flip rate and bounds it loosely (parity unpinned).
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import assert_bf16_matches, assert_codes_equal, dev_bf16, host
+from oracle.attention import (attn_decode_ref, attn_prefill_ref, code_k, code_q, code_v, kmean_ref, softmax_rows)
+from oracle.mix import mix_dequantize as o_mix_deq, mix_quantize as o_mix_q
+from oracle.mx import mx_dequantize as o_mx_deq
+from quantized_gemm_algorithm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL = 1e-5
+
+
+def _lib():
+    import quantized_gemm_algorithm_amd as q
+    return q
+
+
+def _ulp_dist(a, b):
+    a = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(a - b)
+
+
+def _prefill_stages(g, T, Hq, Hkv, d, causal, rows, heads):
+    """Run the GPU prefill with debug dumps and check every stage on the selected (head, row) pairs."""
+    q = _lib()
+    G = Hq // Hkv
+    Tp = (T + 31) // 32 * 32
+    o, mu, dbg = q.mix_attn_prefill(dev_bf16(g["q"]), dev_bf16(g["k"]), dev_bf16(g["v"]), causal=causal, debug=True)
+    torch.cuda.synchronize()
+    # 1. K-mean
+    mu_ref = kmean_ref(g["k"], "bf16")
+    assert_codes_equal(host(mu).view(np.uint32), mu_ref.view(np.uint32), "mu")
+    # oracle-coded operands
+    qc, qs = code_q(g["q"], "bf16")
+    kc, ks = code_k(g["k"], mu_ref, "bf16")
+    vc, vs = code_v(g["v"], "bf16")
+    hidx = torch.as_tensor(heads, device="cuda")
+    ridx = torch.as_tensor(rows, device="cuda")
+    S = host(dbg["s"][hidx][:, ridx])
+    P = host(dbg["p"][hidx][:, ridx])
+    PC = host(dbg["p_codes"][hidx][:, ridx])
+    PS = host(dbg["p_shared"][hidx][:, ridx])
+    L = host(dbg["l"][hidx][:, ridx])
+    O = host(o[ridx][:, hidx])  # [rows, heads, d]
+    flips = 0
+    total = 0
+    for a, h in enumerate(heads):
+        hk = h // G
+        qd = o_mix_deq(qc[rows, h], qs[rows, h], "4.5b")
+        kd = o_mx_deq(kc[:, hk], ks[:, hk], "fp4")
+        vd = o_mx_deq(vc[hk], vs[hk], "fp4")  # [d, Tp]
+        n_valid = (np.asarray(rows) + 1) if causal else np.full(len(rows), T)
+        # 2. S
+        s_ref = qd @ kd.T
+        bound = np.abs(qd) @ np.abs(kd).T
+        for t, i in enumerate(rows):
+            nv = n_valid[t]
+            err = np.abs(S[a, t, :nv] - s_ref[t, :nv])
+            assert np.all(err <= REL * bound[t, :nv] + 1e-30), (h, i, err.max())
+        # 3. p from the GPU's S
+        s_gpu = np.zeros((len(rows), Tp), np.float32)
+        for t in range(len(rows)):
+            s_gpu[t, : n_valid[t]] = S[a, t, : n_valid[t]]
+        p_ref, l_ref, _ = softmax_rows(s_gpu, n_valid, d)
+        for t in range(len(rows)):
+            nv = n_valid[t]
+            assert np.all(_ulp_dist(P[a, t, :nv], p_ref[t, :nv]) <= 4), (h, rows[t])
+            nw = min(Tp, ((rows[t] + 1 + 255) // 256) * 256) if causal else Tp
+            assert np.all(P[a, t, nv:nw] == 0)
+            # l: fp32 sum of the GPU's p in another order
+            lt = float(np.sum(P[a, t, :nv].astype(np.float64)))
+            assert abs(float(L[a, t]) - lt) <= nv * 2.0**-23 * lt
+        # 4. P^ = oracle coding of the GPU's p
+        pg = np.zeros((len(rows), Tp), np.float32)
+        for t in range(len(rows)):
+            pg[t, : n_valid[t]] = P[a, t, : n_valid[t]]
+        pc_ref, ps_ref = o_mix_q(pg, "4.5b", "f32")
+        for t in range(len(rows)):
+            nw = min(Tp, ((rows[t] + 1 + 255) // 256) * 256) if causal else Tp
+            assert_codes_equal(PC[a, t, : nw // 2], pc_ref[t, : nw // 2], f"P codes h{h} i{rows[t]}")
+            assert_codes_equal(PS[a, t, : nw // 32], ps_ref[t, : nw // 32], f"P shared h{h} i{rows[t]}")
+        # 5. O from the GPU's P^ and l
+        pd = o_mix_deq(pc_ref, ps_ref, "4.5b")
+        num = pd @ vd.T
+        absb = np.abs(pd) @ np.abs(vd).T
+        lg = L[a].astype(np.float64)[:, None]
+        assert_bf16_matches(O[:, a, :], num / lg, absb / lg + 2.0**-23 * np.abs(num / lg), f"O head {h}")
+        # end to end (unpinned): an independent oracle run
+        full = attn_prefill_ref(g["q"], g["k"], g["v"], "bf16", causal=causal, rows=np.asarray(rows), heads=np.array([h]))
+        flips += int(np.sum(full["p_codes"][0] != pc_ref))
+        total += pc_ref.size
+        o_ind = (full["o_bf16"][0].astype(np.uint32) << 16).view(np.float32)
+        o_gpu = (O[:, a, :].astype(np.uint32) << 16).view(np.float32)
+        scale = np.abs(o_ind).max() + 1e-30
+        assert np.abs(o_gpu - o_ind).max() <= 0.05 * scale
+    assert flips <= 0.01 * total, (flips, total)
+    return flips, total
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,d,causal", [(256, 4, 2, 128, True), (200, 2, 1, 64, True), (96, 3, 3, 32, False),
+                                                (640, 7, 1, 128, True)])
+def test_prefill_small(T, Hq, Hkv, d, causal):
+    g = synth.attention_qkv(T=T, Hq=Hq, Hkv=Hkv, d=d, seed_cfg=4)
+    rows = sorted(set([0, 1, 31, 32, T // 2, T - 1] + list(range(0, T, max(1, T // 16)))))
+    _prefill_stages(g, T, Hq, Hkv, d, causal, rows, list(range(Hq)))
+
+
+def test_prefill_workload4_full_size_sampled():
+    # 28 query heads / 4 KV heads, d = 128, T = 4096, causal
+    g = synth.attention_qkv()
+    rows = [0, 15, 16, 31, 255, 256, 1000, 2047, 2048, 3333, 4095]
+    _prefill_stages(g, 4096, 28, 4, 128, True, rows, [0, 6, 7, 13, 20, 27])
+
+
+def _decode_case(B, Hq, Hkv, L_each, seed=5):
+    q = _lib()
+    d = 128
+    rng = np.random.default_rng(seed)
+    Lmax = ((max(L_each) + 1 + 31) // 32) * 32 + 32
+    kh = np.zeros((B, Lmax, Hkv, d), np.uint16)
+    vh = np.zeros((B, Lmax, Hkv, d), np.uint16)
+    for b in range(B):
+        g = synth.attention_qkv(T=Lmax, Hq=1, Hkv=Hkv, d=d, rng=rng)
+        kh[b], vh[b] = g["k"], g["v"]
+    qd = synth.f32_to_bf16_bits(rng.standard_normal((B, Hq, d)).astype(np.float32) * 3)
+    pos = np.array(L_each, np.int32)  # the new token's position; tokens [0, pos) are the prefill
+    cache = q.KVCache(B, Lmax, Hkv, d)
+    mus = []
+    for b in range(B):
+        T0 = int(pos[b])
+        kd = dev_bf16(kh[b, :T0])
+        mu = q.mix_kmean(kd.reshape(T0, Hkv * d)).reshape(Hkv, d)
+        mus.append(mu)
+        q.mix_kv_cache_prefill(cache, b, kd, dev_bf16(vh[b, :T0]), mu)
+    mu_all = torch.stack(mus)
+    knew = dev_bf16(np.stack([kh[b, pos[b]] for b in range(B)]))
+    vnew = dev_bf16(np.stack([vh[b, pos[b]] for b in range(B)]))
+    max_pos = int(pos.max())
+    o, dbg = q.mix_attn_decode(dev_bf16(qd), knew, vnew, cache, torch.as_tensor(pos, device="cuda"), max_pos, mu_all,
+                               debug=True)
+    torch.cuda.synchronize()
+    return dict(qd=qd, kh=kh, vh=vh, pos=pos, mu=host(mu_all), o=host(o), dbg={k: host(v) for k, v in dbg.items()},
+                cache=cache, Lmax=Lmax, d=d)
+
+
+def _check_decode(r, Hq, Hkv, batch_rows=None):
+    d = r["d"]
+    G = Hq // Hkv
+    pos, mu = r["pos"], r["mu"]
+    B = len(pos)
+    cache = r["cache"]
+    for b in (range(B) if batch_rows is None else batch_rows):
+        L = int(pos[b]) + 1
+        Lp = r["dbg"]["s"].shape[2]
+        assert_codes_equal(mu[b].view(np.uint32), kmean_ref(r["kh"][b, : L - 1], "bf16").view(np.uint32), f"mu b{b}")
+        kc, ks = code_k(r["kh"][b, :L], mu[b], "bf16")
+        vc, vs = code_v(r["vh"][b, :L], "bf16")
+        # the cache holds exactly the oracle's codes
+        for h in range(Hkv):
+            assert_codes_equal(host(cache.k_codes[b, h, :L]), kc[:, h], f"K cache b{b} h{h}")
+            assert_codes_equal(host(cache.k_scales[b, h, :L]), ks[:, h], f"K scales b{b} h{h}")
+            nb = vc.shape[2]
+            assert_codes_equal(host(cache.v_codes[b, h, :, :nb]), vc[h], f"V cache b{b} h{h}")
+            assert_codes_equal(host(cache.v_scales[b, h, :, : vs.shape[2]]), vs[h], f"V scales b{b} h{h}")
+        qc, qs = code_q(r["qd"][b][None], "bf16")
+        for h in range(Hq):
+            hk = h // G
+            qdq = o_mix_deq(qc[:, h], qs[:, h], "4.5b")[0]
+            kd = o_mx_deq(kc[:, hk], ks[:, hk], "fp4")
+            vd = o_mx_deq(vc[hk], vs[hk], "fp4")
+            s_ref = kd @ qdq
+            bound = np.abs(kd) @ np.abs(qdq)
+            S = r["dbg"]["s"][b, h]
+            assert np.all(np.abs(S[:L] - s_ref) <= REL * bound + 1e-30), (b, h)
+            s_gpu = np.zeros((1, Lp), np.float32)
+            s_gpu[0, :L] = S[:L]
+            p_ref, _, _ = softmax_rows(s_gpu, np.array([L]), d)
+            P = r["dbg"]["p"][b, h]
+            nw = ((L - 1) // 256 + 1) * 256  # the chunks this row's P^ is written for
+            assert np.all(_ulp_dist(P[:L], p_ref[0, :L]) <= 4), (b, h)
+            assert np.all(P[L:nw] == 0)
+            pc_ref, ps_ref = o_mix_q(P[None, :nw].astype(np.float32), "4.5b", "f32")
+            assert_codes_equal(r["dbg"]["p_codes"][b, h][None, : nw // 2], pc_ref, f"P codes b{b} h{h}")
+            assert_codes_equal(r["dbg"]["p_shared"][b, h][None, : nw // 32], ps_ref, f"P shared b{b} h{h}")
+            lg = float(r["dbg"]["l"][b, h])
+            lt = float(np.sum(P[:L].astype(np.float64)))
+            assert abs(lg - lt) <= L * 2.0**-23 * lt
+            pd = o_mix_deq(pc_ref, ps_ref, "4.5b")[0][: vd.shape[1]]
+            num = vd @ pd
+            absb = np.abs(vd) @ np.abs(pd)
+            assert_bf16_matches(r["o"][b, h], num / lg, absb / lg + 2.0**-23 * np.abs(num / lg), f"O b{b} h{h}")
+        # end to end (unpinned): the independent oracle
+        full = attn_decode_ref(r["qd"][b][None], r["kh"][b][None, :L], r["vh"][b][None, :L], mu[b][None],
+                               np.array([L]))
+        o_ind = (np.stack(full["o_bf16"][0]).astype(np.uint32) << 16).view(np.float32)
+        o_gpu = (r["o"][b].astype(np.uint32) << 16).view(np.float32)
+        assert np.abs(o_gpu - o_ind).max() <= 0.05 * (np.abs(o_ind).max() + 1e-30)
+
+
+def test_decode_small_partial_blocks():
+    # positions inside a block, on a block edge, and past one chunk of 256 keys
+    r = _decode_case(B=4, Hq=8, Hkv=2, L_each=[40, 63, 255, 300])
+    _check_decode(r, 8, 2)
+
+
+def test_decode_rejects_unsupported_and_skips_bad_rows():
+    q = _lib()
+    cache = q.KVCache(2, 64, 1, 64)
+    qd = torch.zeros((2, 2, 64), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((2, 1, 64), dtype=torch.bfloat16, device="cuda")
+    mu = torch.zeros((2, 1, 64), dtype=torch.float32, device="cuda")
+    pos = torch.tensor([3, 5], dtype=torch.int32, device="cuda")
+    with pytest.raises(q.MixError):
+        q.mix_attn_decode(qd, kv, kv, cache, pos, 5, mu)  # head dim 64 is not implemented for decode
+    cache = q.KVCache(2, 64, 1, 128)
+    qd = torch.ones((2, 2, 128), dtype=torch.bfloat16, device="cuda")
+    kv = torch.ones((2, 1, 128), dtype=torch.bfloat16, device="cuda")
+    mu = torch.zeros((2, 1, 128), dtype=torch.float32, device="cuda")
+    pos = torch.tensor([70, 3], dtype=torch.int32, device="cuda")  # row 0 beyond max_pos: zeros
+    o, _ = q.mix_attn_decode(qd, kv, kv, cache, pos, 10, mu)
+    torch.cuda.synchronize()
+    assert torch.all(o[0].float() == 0)
+    # keys 0..2 are empty slots (zero codes): their p is tiny and codes to zero in P^, so O is v_new
+    assert torch.all(o[1].float() == 1.0)
+
+
+def test_decode_workload5_full_size_sampled():
+    # batch 16, 28 query / 4 KV heads, d = 128, 8191 prefill tokens per row, the new token at 8191
+    q = _lib()
+    g = synth.decode_step(with_weights=False)
+    B, L = 16, 8192
+    Hq, Hkv, d = 28, 4, 128
+    cache = q.KVCache(B, L, Hkv, d)
+    mus = []
+    for b in range(B):
+        kd = dev_bf16(g["k_hist"][b, : L - 1])
+        mu = q.mix_kmean(kd.reshape(L - 1, Hkv * d)).reshape(Hkv, d)
+        mus.append(mu)
+        q.mix_kv_cache_prefill(cache, b, kd, dev_bf16(g["v_hist"][b, : L - 1]), mu)
+    mu_all = torch.stack(mus)
+    pos = torch.full((B,), L - 1, dtype=torch.int32, device="cuda")
+    o, dbg = q.mix_attn_decode(dev_bf16(g["q"]), dev_bf16(g["k_hist"][:, L - 1]), dev_bf16(g["v_hist"][:, L - 1]),
+                               cache, pos, L - 1, mu_all, debug=True)
+    torch.cuda.synchronize()
+    r = dict(qd=g["q"], kh=g["k_hist"], vh=g["v_hist"], pos=np.full(B, L - 1, np.int32), mu=host(mu_all), o=host(o),
+             dbg={k: host(v) for k, v in dbg.items()}, cache=cache, Lmax=L, d=d)
+    _check_decode(r, Hq, Hkv, batch_rows=[0, 15])
+
+
+def test_decode_linear_workload5_sampled():
+    # the decode GEMV: x [16, 3584] MiX-4.5b x W^T [18944, 3584] MXFP4 -> bf16
+    q = _lib()
+    g = synth.decode_step(with_history=False)
+    ac, as_ = q.mix_quantize(dev_bf16(g["x"]), "4.5b")
+    bc, bs = q.mx_quantize(dev_bf16(g["w_t"]), "fp4")
+    out = q.mix_mx_gemm(ac, as_, "4.5b", bc, bs, "fp4", out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    want = o_mix_q(g["x"], "4.5b", "bf16")
+    assert_codes_equal(host(ac), want[0], "x codes")
+    cols = np.random.default_rng(1).choice(18944, 1024, replace=False)
+    from oracle.gemm import gemm_ref
+    from oracle.mx import mx_quantize as o_mx_q
+    bcr, bsr = o_mx_q(g["w_t"][cols], "fp4", "bf16")
+    ad = o_mix_deq(want[0], want[1], "4.5b")
+    bd = o_mx_deq(bcr, bsr, "fp4")
+    ref = gemm_ref(ad, bd)
+    bound = np.abs(ad) @ np.abs(bd).T
+    assert_bf16_matches(host(out)[:, cols], ref, bound, "decode linear")
