@@ -96,7 +96,7 @@ def softmax_rows(s_rows, n_valid, d):
     z = (s * softmax_scale(d)).astype(np.float32)
     mask = np.arange(L)[None, :] < np.asarray(n_valid)[:, None]
     m = np.where(mask, z, -np.inf).max(axis=1).astype(np.float32)
-    diff = (z - m[:, None]).astype(np.float32)
+    diff = np.where(mask, z - m[:, None], np.float32(-np.inf)).astype(np.float32)
     p = np.exp(diff.astype(np.float64)).astype(np.float32)
     p = np.where(mask, p, np.float32(0.0)).astype(np.float32)
     l = np.array([math.fsum(row) for row in p.astype(np.float64)]).astype(np.float32)

@@ -30,6 +30,9 @@ def common_flags():
         "-O3",
         "-std=c++17",
         "-fPIC",
+        # fp32 steps (softmax scale, z - m, sums) keep IEEE single-rounding semantics: no silent
+        # fusion of a multiply into the following add
+        "-ffp-contract=off",
         # no packed-fp32 instructions in any kernel
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(ROOT, "include"),

@@ -214,6 +214,202 @@ __global__ void __launch_bounds__(256, 2) k_gemm_mfma(GemmArgs g) {
   }
 }
 
+// ------------------------------------------------------------------ MFMA kernel, 256 x 256 tiles
+//
+// Each of the 4 waves owns a 128 x 128 sub-tile (8 x 8 MFMAs, 256 fp32 accumulators per lane).
+// LDS holds two K steps (double buffer): while the MFMAs consume one, the codes of the next step
+// are already in registers and are decoded into the other buffer; one barrier per K step.
+// Thread t loads and decodes row t of A and row t of B for each K step.
+
+constexpr int GM = 256, GN = 256;
+
+template <int A_FMT, int B_FP4>
+struct BigRegs {
+  uint4 a[4];
+  uint32_t a_sh[4];
+  uint4 b[4];
+  uint32_t b_sc[4];
+};
+
+template <int B_FP4>
+struct BigSmem {
+  uint8_t a[2][GM * BK];
+  uint8_t b[2][B_FP4 ? GN * BK / 2 : GN * BK];
+  uint8_t as[2][GM * 4];
+  uint8_t bs[2][GN * 4];
+};
+
+// scale byte of (row, K block g) at [g][wave half][r][i] so a lane reads its 8 sub-tiles' scales at once
+__device__ __forceinline__ int big_scale_slot(int row, int g) {
+  int half = row >> 7, i = (row >> 4) & 7, r = row & 15;
+  return ((g * 2 + half) * 16 + r) * 8 + i;
+}
+
+template <int A_FMT, int B_FP4>
+__device__ __forceinline__ void big_load(const GemmArgs& g, const uint8_t* ab, const void* ash, const uint8_t* bb,
+                                         const uint8_t* bsc, int m0, int n0, int k0, BigRegs<A_FMT, B_FP4>& R) {
+  const int row = threadIdx.x;
+  const int nkb = g.K >> 5;
+  const int gm = m0 + row, gn = n0 + row;
+  const int kb0 = k0 >> 5;
+  const bool am = gm < g.M, bn = gn < g.N;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int gb = kb0 + q;
+    const bool ka = am && gb < nkb, kb = bn && gb < nkb;
+    R.a[q] = ka ? *(const uint4*)(ab + (int64_t)gm * g.a_pitch + (int64_t)gb * 16)
+                : make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
+    if (A_FMT == 1) R.a_sh[q] = ka ? ((const uint16_t*)ash)[(int64_t)gm * g.a_sh_pitch + gb] : 0u;
+    else R.a_sh[q] = ka ? ((const uint8_t*)ash)[(int64_t)gm * g.a_sh_pitch + gb] : 0u;
+    R.b[q] = kb ? *(const uint4*)(bb + (int64_t)gn * g.b_pitch + (int64_t)gb * 16) : make_uint4(0, 0, 0, 0);
+    R.b_sc[q] = kb ? bsc[(int64_t)gn * g.b_sc_pitch + gb] : 127u;
+  }
+}
+
+template <int A_FMT, int B_FP4>
+__device__ __forceinline__ void big_store(BigSmem<B_FP4>& S, int buf, const BigRegs<A_FMT, B_FP4>& R) {
+  const int row = threadIdx.x;
+  uint8_t* sa = S.a[buf] + row * BK;
+  uint8_t* sbm = S.b[buf];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    uint32_t sh = R.a_sh[q];
+    uint32_t w[4] = {R.a[q].x, R.a[q].y, R.a[q].z, R.a[q].w};
+    uint32_t e[8];
+#pragma unroll
+    for (int sb = 0; sb < 4; sb++) {
+      uint32_t m = A_FMT == 1 ? (sh >> (4 + 3 * sb)) & 7u : (sh >> 4) & 7u;
+      mix8_to_e4m3(w[sb], m, e[2 * sb], e[2 * sb + 1]);
+    }
+#pragma unroll
+    for (int hc = 0; hc < 2; hc++) {
+      int ch = (2 * q + hc) ^ (row & 7);
+      *(uint4*)(sa + ch * 16) = make_uint4(e[4 * hc], e[4 * hc + 1], e[4 * hc + 2], e[4 * hc + 3]);
+    }
+    S.as[buf][big_scale_slot(row, q)] = (uint8_t)((sh & 15u) + 119u);
+    if (B_FP4) {
+      int ch = q ^ ((row >> 1) & 3);
+      *(uint4*)(sbm + row * (BK / 2) + ch * 16) = R.b[q];
+    } else {
+      uint32_t bw[4] = {R.b[q].x, R.b[q].y, R.b[q].z, R.b[q].w};
+      uint32_t f[8];
+#pragma unroll
+      for (int sb = 0; sb < 4; sb++) int4x8_to_e4m3(bw[sb], f[2 * sb], f[2 * sb + 1]);
+#pragma unroll
+      for (int hc = 0; hc < 2; hc++) {
+        int ch = (2 * q + hc) ^ (row & 7);
+        *(uint4*)(sbm + row * BK + ch * 16) = make_uint4(f[4 * hc], f[4 * hc + 1], f[4 * hc + 2], f[4 * hc + 3]);
+      }
+    }
+    S.bs[buf][big_scale_slot(row, q)] = (uint8_t)R.b_sc[q];
+  }
+}
+
+// Tile order: workgroups are dispatched round-robin over the 8 XCDs (workgroup b on XCD b % 8);
+// give each XCD a contiguous range of tiles and walk M fastest, so the workgroups resident on one
+// XCD share B columns in its L2.
+__device__ __forceinline__ int xcd_tile(int bid, int nt) {
+  const int x = bid & 7, idx = bid >> 3;
+  const int base = nt >> 3, rem = nt & 7;
+  return x * base + min(x, rem) + idx;
+}
+
+template <int A_FMT, int B_FP4, int C_BF16>
+__global__ void __launch_bounds__(256, 1) k_gemm_mfma_big(GemmArgs g) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  BigSmem<B_FP4>& S = *reinterpret_cast<BigSmem<B_FP4>*>(smem_raw);
+  const int tiles_m = (g.M + GM - 1) / GM, tiles_n = (g.N + GN - 1) / GN;
+  const int t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+  const int tn = t / tiles_m, tm = t - tn * tiles_m;
+  const int m0 = tm * GM, n0 = tn * GN;
+  const int batch = blockIdx.z;
+  if (g.causal == 1 && n0 > m0 + GM - 1) return;
+  int kend = g.K;
+  if (g.causal == 2) kend = min(g.K, m0 + GM);
+
+  const uint8_t* ab = g.a_codes + (int64_t)batch * g.a_bstride;
+  const void* ash = A_FMT == 1 ? (const void*)((const uint16_t*)g.a_shared + (int64_t)batch * g.a_sh_bstride)
+                               : (const void*)((const uint8_t*)g.a_shared + (int64_t)batch * g.a_sh_bstride);
+  const int bbatch = batch / g.b_group;
+  const uint8_t* bb = g.b_codes + (int64_t)bbatch * g.b_bstride;
+  const uint8_t* bsc = g.b_scales + (int64_t)bbatch * g.b_sc_bstride;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 15, gq = lane >> 4;
+
+  v4f acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int j = 0; j < 8; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (kend + BK - 1) / BK;
+  BigRegs<A_FMT, B_FP4> R;
+  big_load<A_FMT, B_FP4>(g, ab, ash, bb, bsc, m0, n0, 0, R);
+  big_store<A_FMT, B_FP4>(S, 0, R);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt++) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) big_load<A_FMT, B_FP4>(g, ab, ash, bb, bsc, m0, n0, (kt + 1) * BK, R);
+    const uint8_t* sa = S.a[cur];
+    const uint8_t* sbm = S.b[cur];
+    // B fragments and scales of this wave's 8 column sub-tiles
+    v8i bf[8];
+    const uint2 bsw = *(const uint2*)(S.bs[cur] + ((gq * 2 + wn) * 16 + r) * 8);
+    const uint2 asw = *(const uint2*)(S.as[cur] + ((gq * 2 + wm) * 16 + r) * 8);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int row = 128 * wn + 16 * j + r;
+      if (B_FP4) {
+        uint4 v = *(const uint4*)(sbm + row * (BK / 2) + (gq ^ ((row >> 1) & 3)) * 16);
+        bf[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      } else {
+        uint4 lo = *(const uint4*)(sbm + row * BK + (gq ^ (row & 7)) * 16);
+        uint4 hi = *(const uint4*)(sbm + row * BK + ((4 + gq) ^ (row & 7)) * 16);
+        bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int row = 128 * wm + 16 * i + r;
+      uint4 lo = *(const uint4*)(sa + row * BK + (gq ^ (row & 7)) * 16);
+      uint4 hi = *(const uint4*)(sa + row * BK + ((4 + gq) ^ (row & 7)) * 16);
+      v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const int sa_i = (int)(((i < 4 ? asw.x : asw.y) >> (8 * (i & 3))) & 0xFFu);
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int sb_j = (int)(((j < 4 ? bsw.x : bsw.y) >> (8 * (j & 3))) & 0xFFu);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, B_FP4 ? 4 : 0, 0, sa_i,
+                                                                      0, sb_j);
+      }
+    }
+    if (kt + 1 < nk) big_store<A_FMT, B_FP4>(S, cur ^ 1, R);
+    __syncthreads();
+  }
+
+  const float* rdiv = g.row_div ? g.row_div + (int64_t)batch * g.row_div_bstride : nullptr;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int m = m0 + 128 * wm + 16 * i + 4 * gq + e;
+      if (m >= g.M) continue;
+      const float dv = rdiv ? rdiv[m] : 1.0f;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int n = n0 + 128 * wn + 16 * j + r;
+        if (n >= g.N) continue;
+        float v = acc[i][j][e];
+        if (rdiv) v = __fdiv_rn(v, dv);
+        const int64_t idx = (int64_t)batch * g.c_bstride + (int64_t)m * g.ldc + n;
+        if (C_BF16) ((uint16_t*)g.c)[idx] = f32_to_bf16_rne(v);
+        else ((float*)g.c)[idx] = v;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ Eq. (6) vector-ALU kernel
 
 constexpr int EM = 64, EN = 64;
@@ -351,7 +547,30 @@ __global__ void __launch_bounds__(256) k_gemm_eq6(GemmArgs g) {
     }                                                                                            \
   } while (0)
 
+template <int A_FMT, int B_FP4, int C_BF16>
+static hipError_t launch_big(const GemmArgs& g, hipStream_t s) {
+  const size_t lds = sizeof(BigSmem<B_FP4>);
+  static bool attr_set = false;  // raise the dynamic LDS limit once per instantiation
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma_big<A_FMT, B_FP4, C_BF16>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int tiles = ((g.M + GM - 1) / GM) * ((g.N + GN - 1) / GN);
+  hipLaunchKernelGGL((k_gemm_mfma_big<A_FMT, B_FP4, C_BF16>), dim3(tiles, 1, g.batch), dim3(256), lds, s, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_mfma(int a_fmt, int b_fp4, int c_bf16, const GemmArgs& g, hipStream_t s) {
+  if (g.M >= GM && g.N >= GN) {
+    if (a_fmt) {
+      if (b_fp4) return c_bf16 ? launch_big<1, 1, 1>(g, s) : launch_big<1, 1, 0>(g, s);
+      return c_bf16 ? launch_big<1, 0, 1>(g, s) : launch_big<1, 0, 0>(g, s);
+    }
+    if (b_fp4) return c_bf16 ? launch_big<0, 1, 1>(g, s) : launch_big<0, 1, 0>(g, s);
+    return c_bf16 ? launch_big<0, 0, 1>(g, s) : launch_big<0, 0, 0>(g, s);
+  }
   int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   dim3 grid(tiles, 1, g.batch), block(256);
   DISPATCH3(k_gemm_mfma, grid, block, g);
