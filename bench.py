@@ -119,6 +119,8 @@ def bench_linear(torch, q, args, which):
     bc, bs = q.mx_quantize(w, b_fmt)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     codes = [q.mix_quantize(x, a_fmt) for x in xs[:2]]
+    wsb = q.mix_mx_gemm_workspace_bytes(a_fmt, b_fmt, M, N, K)
+    ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev) if wsb else None
 
     def step(i, marks=None):
         x = xs[i % nrot]
@@ -126,7 +128,7 @@ def bench_linear(torch, q, args, which):
         e0 = marks.mark() if marks else None
         q.mix_quantize(x, a_fmt, codes=ac, shared=as_)
         e1 = marks.mark() if marks else None
-        q.mix_mx_gemm(ac, as_, a_fmt, bc, bs, b_fmt, out=out)
+        q.mix_mx_gemm(ac, as_, a_fmt, bc, bs, b_fmt, out=out, workspace=ws)
         e2 = marks.mark() if marks else None
         return e0, e1, e2
 

@@ -118,10 +118,20 @@ mix_status_t mx_dequantize(mx_fmt_t fmt, const uint8_t* codes, const uint8_t* sc
  *   A: a_codes [M, K/2], a_shared [M, K/32] (uint8 or uint16 by a_fmt)
  *   B: b_codes [N, K/2], b_scales [N, K/32]   (B holds W^T: one row per output column)
  *   c  [M, N] fp32 or bf16 (c_dtype), row pitch ldc elements (ldc >= N)
+ *   ws, ws_bytes: optional workspace (see mix_mx_gemm_workspace_bytes); NULL is allowed
  */
 mix_status_t mix_mx_gemm(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, mx_fmt_t b_fmt,
                          const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
-                         mix_dtype_t c_dtype, int64_t ldc, void* stream);
+                         mix_dtype_t c_dtype, int64_t ldc, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Workspace for mix_mx_gemm's fast path: the MiX codes of A decoded once into E4M3 bytes plus E8M0
+ * scales (and MXINT4 weights into E4M3 bytes), so the MFMA loop streams operands without decoding.
+ * Returns 0 when the shape does not take the fast path (K % 128 != 0, M < 64 or N < 256). With
+ * ws == NULL or ws_bytes below this size mix_mx_gemm decodes inside the GEMM instead (same results).
+ * ws must be 256-byte aligned; its contents are scratch (overwritten by each call).
+ */
+size_t mix_mx_gemm_workspace_bytes(mix_fmt_t a_fmt, mx_fmt_t b_fmt, int64_t M, int64_t N, int64_t K);
 
 /*
  * The same product computed as P1's Eq. (6) on the vector ALUs: integer sub-block sums of the MX

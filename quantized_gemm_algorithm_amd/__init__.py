@@ -117,27 +117,53 @@ def mx_dequantize(codes, scales, fmt="fp4"):
     return out
 
 
-def _gemm(name, a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype, out):
-    _need_cuda(a_codes, a_shared, b_codes, b_scales, out)
+def _gemm_shapes(a_codes, b_codes):
     M, K = a_codes.shape[0], a_codes.shape[1] * 2
     N = b_codes.shape[0]
     if b_codes.shape[1] * 2 != K:
         raise MixError("A and B disagree on K")
+    return M, N, K
+
+
+def mix_mx_gemm_workspace_bytes(a_fmt, b_fmt, M, N, K):
+    return _lib_().mix_mx_gemm_workspace_bytes(MIX_FMT[a_fmt], MX_FMT[b_fmt], M, N, K)
+
+
+def mix_mx_gemm(a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype=torch.float32, out=None,
+                workspace="auto"):
+    """C = deq(A) . deq(B)^T on the block-scaled MFMA. A: MiX [M, K]; B: MX [N, K] (W^T).
+
+    ``workspace``: "auto" allocates the fast path's scratch with torch; a uint8 tensor is used as
+    given; None selects the in-GEMM decode (same results).
+    """
+    _need_cuda(a_codes, a_shared, b_codes, b_scales, out)
+    M, N, K = _gemm_shapes(a_codes, b_codes)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
-    check(getattr(_lib_(), name)(MIX_FMT[a_fmt], _p(a_codes), _p(a_shared), MX_FMT[b_fmt], _p(b_codes), _p(b_scales),
-                                 M, N, K, _p(out), DTYPE[out.dtype], out.stride(0), _stream()), name)
+    ws = None
+    if isinstance(workspace, str):
+        nb = mix_mx_gemm_workspace_bytes(a_fmt, b_fmt, M, N, K)
+        if nb:
+            ws = torch.empty((nb,), dtype=torch.uint8, device=a_codes.device)
+    elif workspace is not None:
+        _need_cuda(workspace)
+        ws = workspace
+    check(_lib_().mix_mx_gemm(MIX_FMT[a_fmt], _p(a_codes), _p(a_shared), MX_FMT[b_fmt], _p(b_codes), _p(b_scales),
+                              M, N, K, _p(out), DTYPE[out.dtype], out.stride(0), _p(ws),
+                              0 if ws is None else ws.numel(), _stream()), "mix_mx_gemm")
     return out
-
-
-def mix_mx_gemm(a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype=torch.float32, out=None):
-    """C = deq(A) . deq(B)^T on the block-scaled MFMA. A: MiX [M, K]; B: MX [N, K] (W^T)."""
-    return _gemm("mix_mx_gemm", a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype, out)
 
 
 def mix_mx_gemm_eq6(a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype=torch.float32, out=None):
     """The same product by Eq. (6) integer shift-add on the vector ALUs."""
-    return _gemm("mix_mx_gemm_eq6", a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype, out)
+    _need_cuda(a_codes, a_shared, b_codes, b_scales, out)
+    M, N, K = _gemm_shapes(a_codes, b_codes)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    check(_lib_().mix_mx_gemm_eq6(MIX_FMT[a_fmt], _p(a_codes), _p(a_shared), MX_FMT[b_fmt], _p(b_codes),
+                                  _p(b_scales), M, N, K, _p(out), DTYPE[out.dtype], out.stride(0), _stream()),
+          "mix_mx_gemm_eq6")
+    return out
 
 
 def mix_kmean(k):

@@ -27,7 +27,9 @@ SIGNATURES = {
     "mx_quantize_cols": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr, c_ptr, c_ptr]),
     "mix_dequantize": (c_int, [c_int, c_ptr, c_ptr, c_i64, c_i64, c_ptr, c_ptr]),
     "mx_dequantize": (c_int, [c_int, c_ptr, c_ptr, c_i64, c_i64, c_ptr, c_ptr]),
-    "mix_mx_gemm": (c_int, [c_int, c_ptr, c_ptr, c_int, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_int, c_i64, c_ptr]),
+    "mix_mx_gemm": (c_int, [c_int, c_ptr, c_ptr, c_int, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_int, c_i64, c_ptr,
+                            ctypes.c_size_t, c_ptr]),
+    "mix_mx_gemm_workspace_bytes": (ctypes.c_size_t, [c_int, c_int, c_i64, c_i64, c_i64]),
     "mix_mx_gemm_eq6": (c_int, [c_int, c_ptr, c_ptr, c_int, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_int, c_i64,
                                 c_ptr]),
     "mix_kmean": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr, c_ptr]),

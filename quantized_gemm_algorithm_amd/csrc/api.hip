@@ -141,7 +141,8 @@ mix_status_t mx_dequantize(mx_fmt_t fmt, const uint8_t* codes, const uint8_t* sc
 
 static mix_status_t gemm_common(const char* fn, bool eq6, mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared,
                                 mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
-                                int64_t K, void* c, mix_dtype_t c_dtype, int64_t ldc, void* stream) {
+                                int64_t K, void* c, mix_dtype_t c_dtype, int64_t ldc, void* ws, size_t ws_bytes,
+                                void* stream) {
   g_err.clear();
   if (a_fmt != MIX_4P25 && a_fmt != MIX_4P5) return fail(MIX_E_ENUM, "%s: unknown MiX format %d", fn, (int)a_fmt);
   if (b_fmt != MX_INT4 && b_fmt != MX_FP4) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
@@ -158,6 +159,14 @@ static mix_status_t gemm_common(const char* fn, bool eq6, mix_fmt_t a_fmt, const
   if ((uintptr_t)c % dtype_size(c_dtype)) return fail(MIX_E_ALIGN, "%s: c misaligned", fn);
   int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   if (tiles > INT32_MAX) return fail(MIX_E_SHAPE, "%s: too many tiles", fn);
+  if (!eq6 && ws && mix::gemm_f8_eligible(M, N, K) && ws_bytes >= mix::gemm_f8_ws_bytes(b_fmt == MX_FP4, M, N, K)) {
+    if ((uintptr_t)ws & 255u) return fail(MIX_E_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+    if (a_fmt == MIX_4P5 && ((uintptr_t)a_shared & 1u)) return fail(MIX_E_ALIGN, "%s: a_shared misaligned", fn);
+    if (((uintptr_t)b_scales & 3u)) return fail(MIX_E_ALIGN, "%s: b_scales must be 4-byte aligned", fn);
+    return hip_status(mix::launch_gemm_f8(a_fmt == MIX_4P5, b_fmt == MX_FP4, c_dtype == MIX_BF16, a_codes, a_shared,
+                                          b_codes, b_scales, M, N, K, c, ldc, nullptr, ws, (hipStream_t)stream),
+                      "mix_mx_gemm launch");
+  }
   mix::GemmArgs g{};
   g.a_codes = a_codes; g.a_shared = a_shared; g.a_pitch = K / 2; g.a_sh_pitch = K / 32;
   g.b_codes = b_codes; g.b_scales = b_scales; g.b_pitch = K / 2; g.b_sc_pitch = K / 32; g.b_group = 1;
@@ -168,18 +177,25 @@ static mix_status_t gemm_common(const char* fn, bool eq6, mix_fmt_t a_fmt, const
   return hip_status(e, eq6 ? "mix_mx_gemm_eq6 launch" : "mix_mx_gemm launch");
 }
 
+size_t mix_mx_gemm_workspace_bytes(mix_fmt_t a_fmt, mx_fmt_t b_fmt, int64_t M, int64_t N, int64_t K) {
+  (void)a_fmt;
+  if (M <= 0 || N <= 0 || K <= 0 || (b_fmt != MX_INT4 && b_fmt != MX_FP4)) return 0;
+  if (!mix::gemm_f8_eligible(M, N, K)) return 0;
+  return mix::gemm_f8_ws_bytes(b_fmt == MX_FP4, M, N, K);
+}
+
 mix_status_t mix_mx_gemm(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, mx_fmt_t b_fmt,
                          const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
-                         mix_dtype_t c_dtype, int64_t ldc, void* stream) {
+                         mix_dtype_t c_dtype, int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
   return gemm_common("mix_mx_gemm", false, a_fmt, a_codes, a_shared, b_fmt, b_codes, b_scales, M, N, K, c, c_dtype, ldc,
-                     stream);
+                     ws, ws_bytes, stream);
 }
 
 mix_status_t mix_mx_gemm_eq6(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, mx_fmt_t b_fmt,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
                              void* c, mix_dtype_t c_dtype, int64_t ldc, void* stream) {
   return gemm_common("mix_mx_gemm_eq6", true, a_fmt, a_codes, a_shared, b_fmt, b_codes, b_scales, M, N, K, c, c_dtype,
-                     ldc, stream);
+                     ldc, nullptr, 0, stream);
 }
 
 mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, int64_t ldk, float* mu, void* stream) {

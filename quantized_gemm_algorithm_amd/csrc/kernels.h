@@ -44,6 +44,13 @@ struct GemmArgs {
 hipError_t launch_gemm_mfma(int a_fmt, int b_fp4, int c_bf16, const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_eq6(int a_fmt, int b_fp4, int c_bf16, const GemmArgs& g, hipStream_t s);
 
+// fast path: decode pass into a workspace, then the MXFP8 x MX GEMM
+bool gemm_f8_eligible(int64_t M, int64_t N, int64_t K);
+size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_f8(int a_fmt, int b_fp4, int c_bf16, const uint8_t* a_codes, const void* a_shared,
+                          const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
+                          int64_t ldc, const float* row_div, void* ws, hipStream_t s);
+
 // attention (arguments validated by the C-ABI layer)
 size_t attn_prefill_ws_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t d);
 hipError_t attn_prefill_run(const void* q, const void* k, const void* v, int64_t T, int64_t Hq, int64_t Hkv,

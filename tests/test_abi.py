@@ -73,8 +73,10 @@ def test_quantize_validation(lib):
 
 
 def test_gemm_validation(lib):
-    args_ok = dict(a=FAKE, s=FAKE, b=FAKE, bs=FAKE)
-    for fn in (lib.mix_mx_gemm, lib.mix_mx_gemm_eq6):
+    def gemm(*a):
+        return lib.mix_mx_gemm(*a[:-1], None, 0, a[-1])
+
+    for fn in (gemm, lib.mix_mx_gemm_eq6):
         assert fn(3, FAKE, FAKE, 1, FAKE, FAKE, 4, 4, 32, FAKE, 0, 4, None) == MIX_E_ENUM
         assert fn(1, FAKE, FAKE, 9, FAKE, FAKE, 4, 4, 32, FAKE, 0, 4, None) == MIX_E_ENUM
         assert fn(1, FAKE, FAKE, 1, FAKE, FAKE, 4, 4, 40, FAKE, 0, 4, None) == MIX_E_SHAPE
@@ -86,7 +88,14 @@ def test_gemm_validation(lib):
         assert fn(1, None, None, 1, None, None, 0, 4, 32, None, 0, 4, None) == MIX_OK
         assert fn(1, None, None, 1, None, None, 4, 0, 32, None, 0, 0, None) == MIX_OK
         assert fn(1, FAKE, FAKE, 1, FAKE, FAKE, 2**31, 4, 32, FAKE, 0, 4, None) == MIX_E_SHAPE
-    del args_ok
+    # fast-path workspace size: zero when the shape does not take it
+    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 4096, 18944, 3584) == 4096 * 3584 + 4096 * 112
+    assert lib.mix_mx_gemm_workspace_bytes(1, 0, 256, 256, 128) == 256 * 128 + 1024 + 256 * 128
+    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 256, 256, 96) == 0
+    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 16, 18944, 3584) == 0
+    # a misaligned workspace is rejected when the fast path is taken
+    assert lib.mix_mx_gemm(1, FAKE, FAKE, 1, FAKE, FAKE, 256, 256, 128, FAKE, 0, 256, MISALIGNED, 1 << 20,
+                           None) == MIX_E_ALIGN
 
 
 def test_kmean_validation(lib):

@@ -31,12 +31,36 @@ def _to_dev(ac, as_, bc, bs, a_fmt):
     return dev_u8(ac), (dev_u16(as_) if a_fmt == "4.5b" else dev_u8(as_)), dev_u8(bc), dev_u8(bs)
 
 
-def _run(fn_name, ac, as_, bc, bs, a_fmt, b_fmt, out_dtype):
+def _run(fn_name, ac, as_, bc, bs, a_fmt, b_fmt, out_dtype, workspace="auto"):
     q = _lib()
     A, S, B, Bs = _to_dev(ac, as_, bc, bs, a_fmt)
-    out = getattr(q, fn_name)(A, S, a_fmt, B, Bs, b_fmt, out_dtype=out_dtype)
+    if fn_name == "mix_mx_gemm":
+        out = q.mix_mx_gemm(A, S, a_fmt, B, Bs, b_fmt, out_dtype=out_dtype, workspace=workspace)
+    else:
+        out = getattr(q, fn_name)(A, S, a_fmt, B, Bs, b_fmt, out_dtype=out_dtype)
     torch.cuda.synchronize()
     return host(out)
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", PAIRS)
+@pytest.mark.parametrize("workspace", ["auto", None])
+@pytest.mark.parametrize("M,N,K", [(64, 256, 128), (300, 520, 1024), (257, 300, 384), (512, 768, 3584)])
+def test_gemm_fast_path_shapes(a_fmt, b_fmt, workspace, M, N, K):
+    # shapes the decode-once path takes (K % 128 == 0, M >= 64, N >= 256), with ragged M/N tails;
+    # workspace=None runs the same shapes through the decode-in-GEMM kernels
+    q = _lib()
+    assert q.mix_mx_gemm_workspace_bytes(a_fmt, b_fmt, M, N, K) > 0
+    rng = np.random.default_rng(M + 3 * N + 7 * K)
+    x = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-8, 8, (M, K)))).astype(np.float32)
+    w = (0.05 * rng.standard_normal((N, K)) * np.exp2(rng.integers(-3, 3, (N, K)))).astype(np.float32)
+    ac, as_, bc, bs = _code(x, w, a_fmt, b_fmt)
+    ad, bd = o_mix_deq(ac, as_, a_fmt), o_mx_deq(bc, bs, b_fmt)
+    ref = gemm_ref(ad, bd)
+    bound = gemm_abs_bound(ad, bd)
+    got = _run("mix_mx_gemm", ac, as_, bc, bs, a_fmt, b_fmt, torch.float32, workspace)
+    assert_gemm_close(got, ref, bound, f"{a_fmt}x{b_fmt} fp32 {M}x{N}x{K} ws={workspace}")
+    gotb = _run("mix_mx_gemm", ac, as_, bc, bs, a_fmt, b_fmt, torch.bfloat16, workspace)
+    assert_bf16_matches(gotb, ref, bound, f"{a_fmt}x{b_fmt} bf16 {M}x{N}x{K} ws={workspace}")
 
 
 @pytest.mark.parametrize("a_fmt,b_fmt", PAIRS)
