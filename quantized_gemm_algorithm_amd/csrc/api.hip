@@ -162,9 +162,8 @@ static mix_status_t gemm_common(const char* fn, bool eq6, mix_fmt_t a_fmt, const
   if (!eq6 && ws && mix::gemm_f8_eligible(M, N, K) && ws_bytes >= mix::gemm_f8_ws_bytes(b_fmt == MX_FP4, M, N, K)) {
     if ((uintptr_t)ws & 255u) return fail(MIX_E_ALIGN, "%s: workspace must be 256-byte aligned", fn);
     if (a_fmt == MIX_4P5 && ((uintptr_t)a_shared & 1u)) return fail(MIX_E_ALIGN, "%s: a_shared misaligned", fn);
-    if (((uintptr_t)b_scales & 3u)) return fail(MIX_E_ALIGN, "%s: b_scales must be 4-byte aligned", fn);
     return hip_status(mix::launch_gemm_f8(a_fmt == MIX_4P5, b_fmt == MX_FP4, c_dtype == MIX_BF16, a_codes, a_shared,
-                                          b_codes, b_scales, M, N, K, c, ldc, nullptr, ws, (hipStream_t)stream),
+                                          b_codes, b_scales, M, N, K, c, ldc, ws, (hipStream_t)stream),
                       "mix_mx_gemm launch");
   }
   mix::GemmArgs g{};

@@ -12,9 +12,15 @@
 // MXINT4 weights become E4M3 bytes of q/4 (k_expand_b_int4), which keeps their E8M0 scales
 // unchanged. MXFP4 weights are used as stored: the E2M1 nibbles are the FP4 MFMA operand.
 //
-// The GEMM streams both operands global->LDS with global_load_lds_dwordx4 (no registers, no VALU).
-// It uses 256 x 256 tiles, 4 waves of 128 x 128 (4 x 4 MFMAs of 32 x 32 per 64-wide K half, 256
-// fp32 accumulators per lane), and an NS-stage LDS ring with one barrier per 128-wide K step.
+// The GEMM streams both operands global->LDS with global_load_lds_dwordx4 (no registers, no
+// VALU). Each workgroup computes one 256 x 256 tile with 8 waves (two per SIMD, so one wave's
+// LDS reads and barrier wait overlap the other's MFMAs), each wave 64 x 128 outputs (2 x 4 MFMAs
+// of 32 x 32 per 64-wide K half, 128 fp32 accumulators per lane). A two-stage LDS ring carries
+// one barrier per 128-wide K step. Tiles are ordered in bands of 8 tile rows and split into
+// XCD-contiguous chunks, so the tiles an XCD runs at once share A and B panels in its L2. Block
+// scales are laid out per (K step, tile) in the order the lanes read them: one 8-byte LDS read
+// gives a lane all its scales for a K step, and the MFMA's scale op_sel picks the byte. The
+// epilogue goes through LDS so that every global store writes whole output rows.
 //
 // v_mfma_scale_f32_32x32x64_f8f6f4 operand layout (established on the device): lane
 // l = r + 32 g (r < 32, g < 2) supplies row/column r. An FP8 operand holds K elements
@@ -35,12 +41,23 @@ namespace mix {
 
 // ------------------------------------------------------------------ decode passes
 
+constexpr int FT = 256;   // tile M = tile N
+constexpr int FK = 128;   // K per stage
+
+// Byte position of the scale of (tile row rin, block b4 within the K step) inside the 1 KB a
+// (K step, tile) pair owns: [half-tile w][lane group gq][r][K half h][sub-tile i].
+__device__ __forceinline__ int f8_scale_pos(int rin, int b4) {
+  const int w = rin >> 7, i = (rin >> 5) & 3, r = rin & 31;
+  const int h = b4 >> 1, gq = b4 & 1;
+  return ((w * 2 + gq) * 32 + r) * 8 + h * 4 + i;
+}
+
 // One lane per 8-element sub-block: 4 code bytes -> 8 E4M3 bytes. Quad lane 0 writes the block's
-// E8M0 scale 2^(Emax-1) into the per-K-step layout [K/128][M][4].
+// E8M0 scale 2^(Emax-1) into the permuted scale layout [K/128][tiles_m][1024].
 template <int A_FMT>
 __global__ void __launch_bounds__(256) k_expand_a(const uint8_t* __restrict__ codes, const void* __restrict__ shared,
-                                                   int64_t M, int64_t K, uint8_t* __restrict__ a8,
-                                                   uint8_t* __restrict__ as_t) {
+                                                   int64_t M, int64_t K, int tiles_m, uint8_t* __restrict__ a8,
+                                                   uint8_t* __restrict__ as_p) {
   const int64_t sub_per_row = K >> 3;
   const int64_t total = M * sub_per_row;
   for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total; g += (int64_t)gridDim.x * blockDim.x) {
@@ -54,7 +71,22 @@ __global__ void __launch_bounds__(256) k_expand_a(const uint8_t* __restrict__ co
     uint32_t e0, e1;
     mix8_to_e4m3(w, m, e0, e1);
     *(uint2*)(a8 + row * K + sb * 8) = make_uint2(e0, e1);
-    if ((sb & 3) == 0) as_t[((blk >> 2) * M + row) * 4 + (blk & 3)] = (uint8_t)((sh & 15u) + 119u);
+    if ((sb & 3) == 0) {
+      const int64_t st = blk >> 2, tile = row / FT;
+      as_p[(st * tiles_m + tile) * 1024 + f8_scale_pos((int)(row % FT), (int)(blk & 3))] = (uint8_t)((sh & 15u) + 119u);
+    }
+  }
+}
+
+// MX scales [N, K/32] -> the permuted layout [K/128][tiles_n][1024].
+__global__ void __launch_bounds__(256) k_permute_b_scales(const uint8_t* __restrict__ bs, int64_t N, int64_t K,
+                                                           int tiles_n, uint8_t* __restrict__ bs_p) {
+  const int64_t nb = K >> 5;
+  const int64_t total = N * nb;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total; g += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = g / nb, blk = g - row * nb;
+    const int64_t st = blk >> 2, tile = row / FT;
+    bs_p[(st * tiles_n + tile) * 1024 + f8_scale_pos((int)(row % FT), (int)(blk & 3))] = bs[g];
   }
 }
 
@@ -73,26 +105,22 @@ __global__ void __launch_bounds__(256) k_expand_b_int4(const uint8_t* __restrict
 
 // ------------------------------------------------------------------ GEMM
 
-constexpr int FT = 256;   // tile M = tile N
-constexpr int FK = 128;   // K per stage
-
 template <int B_FP4>
 struct F8Stage {
   static constexpr int A_BYTES = FT * FK;                          // E4M3 A, 128 B per row
   static constexpr int B_BYTES = B_FP4 ? FT * FK / 2 : FT * FK;    // FP4 (64 B/row) or E4M3 B
   static constexpr int AS_OFF = A_BYTES + B_BYTES;
-  static constexpr int BS_OFF = AS_OFF + FT * 4;
-  static constexpr int BYTES = BS_OFF + FT * 4;
+  static constexpr int BS_OFF = AS_OFF + 1024;
+  static constexpr int BYTES = BS_OFF + 1024;
 };
 
 struct F8Args {
   const uint8_t* a8;      // [M, K] E4M3
-  const uint8_t* as_t;    // [K/128][M][4] E8M0
+  const uint8_t* as_p;    // [K/128][tiles_m][1024] E8M0, permuted
   const uint8_t* b;       // [N, K/2] FP4 codes or [N, K] E4M3
-  const uint8_t* bs;      // [N, K/32] E8M0
+  const uint8_t* bs_p;    // [K/128][tiles_n][1024] E8M0, permuted
   void* c;
   int64_t ldc;
-  const float* row_div;
   int M, N, K;
 };
 
@@ -112,62 +140,58 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
 }
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
-}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
 
-// Issue the global->LDS copies of one K step into stage buffer `st`. Every wave issues the same
-// number of copy instructions (f8_loads_per_stage), so per-wave vmcnt arithmetic is a constant.
+constexpr int F8_THREADS = 512;   // 8 waves: 4 along M x 2 along N, 64 x 128 outputs each
+
+// Copies of one K step of tile (tm, tn) into stage buffer `st`; each wave copies whole
+// 1 KB runs (64 lanes x 16 bytes) of the stage image.
 template <int B_FP4>
-__device__ __forceinline__ void f8_issue(const F8Args& g, uint8_t* st, int m0, int n0, int k0) {
+__device__ __forceinline__ void f8_issue(const F8Args& g, uint8_t* st, int tm, int tn, int tiles_m, int tiles_n,
+                                         int ks) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = tm * FT, n0 = tn * FT, k0 = ks * FK;
   // A: 2048 16-byte chunks; chunk q lands at LDS byte 16 q; q -> (row q/8, slot q%8) holding
-  // logical chunk slot ^ (row & 7) of that row.
+  // logical chunk slot ^ (row & 7) of that row (rows past M repeat row M-1; never stored).
 #pragma unroll
-  for (int p = 0; p < 8; p++) {
-    const int q = p * 256 + wave * 64 + lane;
+  for (int p = 0; p < 4; p++) {
+    const int q = p * F8_THREADS + wave * 64 + lane;
     const int row = q >> 3, slot = q & 7;
     const int c = slot ^ (row & 7);
     const int grow = min(m0 + row, g.M - 1);
-    const uint8_t* src = g.a8 + (int64_t)grow * g.K + k0 + 16 * c;
-    dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(st + (p * 256 + wave * 64) * 16)));
+    dma16(g.a8 + (int64_t)grow * g.K + k0 + 16 * c,
+          __builtin_amdgcn_readfirstlane(lds_addr(st + (p * F8_THREADS + wave * 64) * 16)));
   }
   if (B_FP4) {
-    // B: 1024 chunks of 16 B; (row q/4, slot q%4) holds logical chunk slot ^ ((row >> 1) & 3)
+    // B: 1024 chunks; (row q/4, slot q%4) holds logical chunk slot ^ ((row >> 1) & 3)
 #pragma unroll
-    for (int p = 0; p < 4; p++) {
-      const int q = p * 256 + wave * 64 + lane;
+    for (int p = 0; p < 2; p++) {
+      const int q = p * F8_THREADS + wave * 64 + lane;
       const int row = q >> 2, slot = q & 3;
       const int c = slot ^ ((row >> 1) & 3);
       const int grow = min(n0 + row, g.N - 1);
-      const uint8_t* src = g.b + (int64_t)grow * (g.K >> 1) + (k0 >> 1) + 16 * c;
-      dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::A_BYTES + (p * 256 + wave * 64) * 16)));
+      dma16(g.b + (int64_t)grow * (g.K >> 1) + (k0 >> 1) + 16 * c,
+            __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::A_BYTES + (p * F8_THREADS + wave * 64) * 16)));
     }
   } else {
 #pragma unroll
-    for (int p = 0; p < 8; p++) {
-      const int q = p * 256 + wave * 64 + lane;
+    for (int p = 0; p < 4; p++) {
+      const int q = p * F8_THREADS + wave * 64 + lane;
       const int row = q >> 3, slot = q & 7;
       const int c = slot ^ (row & 7);
       const int grow = min(n0 + row, g.N - 1);
-      const uint8_t* src = g.b + (int64_t)grow * g.K + k0 + 16 * c;
-      dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::A_BYTES + (p * 256 + wave * 64) * 16)));
+      dma16(g.b + (int64_t)grow * g.K + k0 + 16 * c,
+            __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::A_BYTES + (p * F8_THREADS + wave * 64) * 16)));
     }
   }
-  // scales: 4 bytes per row; wave w copies rows 64 w .. 64 w + 63
-  {
-    const int row = wave * 64 + lane;
-    const int ga = min(m0 + row, g.M - 1);
-    const uint8_t* sa = g.as_t + ((int64_t)(k0 >> 7) * g.M + ga) * 4;
-    dma4(sa, __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::AS_OFF + wave * 256)));
-    const int gb = min(n0 + row, g.N - 1);
-    const uint8_t* sb = g.bs + (int64_t)gb * (g.K >> 5) + (k0 >> 5);
-    dma4(sb, __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::BS_OFF + wave * 256)));
-  }
+  // scales: the (K step, tile) 1 KB blocks are contiguous; waves 0-3 copy A's, waves 4-7 B's
+  if (wave < 4)
+    dma4(g.as_p + ((int64_t)ks * tiles_m + tm) * 1024 + wave * 256 + lane * 4,
+         __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::AS_OFF + wave * 256)));
+  else
+    dma4(g.bs_p + ((int64_t)ks * tiles_n + tn) * 1024 + (wave - 4) * 256 + lane * 4,
+         __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::BS_OFF + (wave - 4) * 256)));
 }
-
-template <int B_FP4>
-constexpr int f8_loads_per_stage() { return 8 + (B_FP4 ? 4 : 8) + 2; }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
 template <int N>
@@ -176,152 +200,147 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-// One 128-wide K step from stage buffer `st`. The MFMA computes C^T tiles: its A operand is the
-// weight tile (rows n), its B operand the activation tile (rows m), so result register k of lane
-// l holds C[m = l & 31][n = 8 (k >> 2) + 4 (l >> 5) + (k & 3)] -- four consecutive n per lane,
-// which the epilogue writes as 8-byte runs.
-template <int B_FP4>
-__device__ __forceinline__ void f8_compute(const uint8_t* st, v16f (&acc)[4][4], int wm, int wn, int r, int gq) {
-  const uint8_t* sa = st;
-  const uint8_t* sbm = st + F8Stage<B_FP4>::A_BYTES;
-  const uint8_t* sas = st + F8Stage<B_FP4>::AS_OFF;
-  const uint8_t* sbs = st + F8Stage<B_FP4>::BS_OFF;
-#pragma unroll
-  for (int h = 0; h < 2; h++) {  // 64-wide K halves
-    v8i xf[4];  // activation fragments (m sub-tiles)
-    int xs[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int row = 128 * wm + 32 * i + r;
-      const int c0 = 4 * h + gq, c1 = 4 * h + 2 + gq;
-      uint4 lo = *(const uint4*)(sa + row * 128 + ((c0 ^ (row & 7)) * 16));
-      uint4 hi = *(const uint4*)(sa + row * 128 + ((c1 ^ (row & 7)) * 16));
-      xf[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      xs[i] = sas[row * 4 + 2 * h + gq];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int row = 128 * wn + 32 * j + r;
-      v8i wf;
-      if (B_FP4) {
-        const int c = 2 * h + gq;
-        uint4 v = *(const uint4*)(sbm + row * 64 + ((c ^ ((row >> 1) & 3)) * 16));
-        wf = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      } else {
-        const int c0 = 4 * h + gq, c1 = 4 * h + 2 + gq;
-        uint4 lo = *(const uint4*)(sbm + row * 128 + ((c0 ^ (row & 7)) * 16));
-        uint4 hi = *(const uint4*)(sbm + row * 128 + ((c1 ^ (row & 7)) * 16));
-        wf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-      const int ws = sbs[row * 4 + 2 * h + gq];
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, xf[i], acc[i][j], B_FP4 ? 4 : 0, 0, 0, ws, 0,
-                                                                     xs[i]);
-    }
-  }
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Tile order: XCD-contiguous chunks of a banded order (bands of GM tile rows, column by column
+// inside a band), so the ~32 tiles an XCD runs at once share a few A and B panels in its L2.
+__device__ __forceinline__ void f8_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const int t = f8_xcd_tile(bid, tiles_m * tiles_n);
+  const int band_sz = GM * tiles_n;
+  const int band = t / band_sz;
+  const int rem = t - band * band_sz;
+  const int gm = min(GM, tiles_m - band * GM);
+  tn = rem / gm;
+  tm = band * GM + (rem - tn * gm);
 }
 
-template <int B_FP4, int C_BF16, int NS>
-__global__ void __launch_bounds__(256, 1) k_gemm_f8(F8Args g) {
+// One 256 x 256 output tile per workgroup; a two-stage LDS ring with one barrier per 128-wide K
+// step (the next step's copies are issued right after the barrier and land while this step's
+// MFMAs run). The MFMA computes C^T tiles: its A operand is the weight fragment (rows n), its B
+// operand the activation fragment (rows m), so result register k of lane l holds
+// C[m = l & 31][n = 8 (k >> 2) + 4 (l >> 5) + (k & 3)].
+template <int B_FP4, int C_BF16>
+__global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int SB = F8Stage<B_FP4>::BYTES;
-  constexpr int LPS = f8_loads_per_stage<B_FP4>();
+  constexpr int NS = 2;
   const int tiles_m = (g.M + FT - 1) / FT, tiles_n = (g.N + FT - 1) / FT;
-  const int t = f8_xcd_tile(blockIdx.x, tiles_m * tiles_n);
-  const int tn = t / tiles_m, tm = t - tn * tiles_m;
-  const int m0 = tm * FT, n0 = tn * FT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, gq = lane >> 5;
   const int nk = g.K / FK;
+  // this lane's 8 scale bytes [h][sub-tile] in the permuted 1 KB block (see f8_scale_pos)
+  const int sc_a = (((wm >> 1) * 2 + gq) * 32 + r) * 8;
+  const int sc_b = ((wn * 2 + gq) * 32 + r) * 8;
+  const int sub_a = 16 * (wm & 1);   // bit offset of this wave's two A sub-tiles in a 4-byte word
 
-  v16f acc[4][4];
+  int tm, tn;
+  f8_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  f8_issue<B_FP4>(g, smem, tm, tn, tiles_m, tiles_n, 0);
+
+  v16f acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < 2; i++)
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = v16f{};
 
-  // prologue: steps 0 .. NS-2 in flight
-#pragma unroll
-  for (int s = 0; s < NS - 1; s++)
-    if (s < nk) f8_issue<B_FP4>(g, smem + s * SB, m0, n0, s * FK);
-
   for (int kt = 0; kt < nk; kt++) {
-    // this wave's copies for step kt are complete once only the later steps' copies are pending
-    if (NS == 3 && kt + 1 < nk) wait_vmcnt<LPS>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // every wave's copies of step kt are in LDS; step kt-1 is consumed
-    if (kt + NS - 1 < nk) f8_issue<B_FP4>(g, smem + ((kt + NS - 1) % NS) * SB, m0, n0, (kt + NS - 1) * FK);
-    f8_compute<B_FP4>(smem + (kt % NS) * SB, acc, wm, wn, r, gq);
-  }
-
-  // Epilogue. Each wave stages its 128 x 128 tile in LDS row-major (row pitch padded by 16 bytes)
-  // and writes whole rows with 16-byte stores: 64 lanes cover 4 rows (bf16) or 2 rows (fp32) per
-  // instruction. fp32 output goes in two 64-row passes to fit.
-  __builtin_amdgcn_s_barrier();  // the last step's operands are consumed before LDS is reused
-  constexpr int ES = C_BF16 ? 2 : 4;           // bytes per output element
-  constexpr int PASS_ROWS = C_BF16 ? 128 : 64;
-  constexpr int PITCH = 128 * ES + 16;
-  uint8_t* ep = smem + wave * (PASS_ROWS * PITCH);
-  const int mw = m0 + 128 * wm, nw = n0 + 128 * wn;
-  const bool vec_ok = (g.ldc % (16 / ES)) == 0 && (((uintptr_t)g.c) & 15) == 0;
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();   // step kt is in LDS; every wave is done with step kt-1's slot
+    if (kt + 1 < nk) f8_issue<B_FP4>(g, smem + ((kt + 1) % NS) * SB, tm, tn, tiles_m, tiles_n, kt + 1);
+    const uint8_t* st = smem + (kt % NS) * SB;
+    const uint8_t* sa = st;
+    const uint8_t* sbm = st + F8Stage<B_FP4>::A_BYTES;
+    const uint2 xs8 = *(const uint2*)(st + F8Stage<B_FP4>::AS_OFF + sc_a);
+    const uint2 ws8 = *(const uint2*)(st + F8Stage<B_FP4>::BS_OFF + sc_b);
 #pragma unroll
-  for (int pass = 0; pass < 128 / PASS_ROWS; pass++) {
-    // registers -> LDS: lane holds C[m = 32 i + r][n = 32 j + 8 (k>>2) + 4 gq + (0..3)]
+    for (int h = 0; h < 2; h++) {
+      const int xsw = (int)((h ? xs8.y : xs8.x) >> sub_a);
+      const int wsw = (int)(h ? ws8.y : ws8.x);
+      v8i xf[2];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      if ((32 * i) / PASS_ROWS != pass) continue;
-      const int lr = 32 * i + r - pass * PASS_ROWS;
-      const int gm = mw + 32 * i + r;
-      const float dv = (g.row_div && gm < g.M) ? g.row_div[gm] : 1.0f;
+      for (int i = 0; i < 2; i++) {
+        const int row = 64 * wm + 32 * i + r;
+        const int c0 = 4 * h + gq, c1 = 4 * h + 2 + gq;
+        const uint4 lo = *(const uint4*)(sa + row * 128 + ((c0 ^ (row & 7)) * 16));
+        const uint4 hi = *(const uint4*)(sa + row * 128 + ((c1 ^ (row & 7)) * 16));
+        xf[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            v[e] = acc[i][j][4 * q + e];
-            if (g.row_div) v[e] = __fdiv_rn(v[e], dv);
-          }
-          const int col = 32 * j + 8 * q + 4 * gq;
-          if (C_BF16) {
-            uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-            uint32_t hi = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-            *(uint2*)(ep + lr * PITCH + col * 2) = make_uint2(lo, hi);
-          } else {
-            *(float4*)(ep + lr * PITCH + col * 4) = make_float4(v[0], v[1], v[2], v[3]);
-          }
+        const int row = 128 * wn + 32 * j + r;
+        v8i wf;
+        if (B_FP4) {
+          // FP4 operands read only the low 4 registers of the 8-register tuple
+          const int c = 2 * h + gq;
+          const v4i w = *(const v4i*)(sbm + row * 64 + ((c ^ ((row >> 1) & 3)) * 16));
+          wf = __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
+        } else {
+          const int c0 = 4 * h + gq, c1 = 4 * h + 2 + gq;
+          const v4i lo = *(const v4i*)(sbm + row * 128 + ((c0 ^ (row & 7)) * 16));
+          const v4i hi = *(const v4i*)(sbm + row * 128 + ((c1 ^ (row & 7)) * 16));
+          wf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
+        // the scale operands' op_sel picks byte j of the weight word and byte i of the
+        // activation word
+#define F8_MFMA(I, J)                                                                                      \
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, xf[I], acc[I][J], B_FP4 ? 4 : 0, 0, J, wsw, \
+                                                              I, xsw)
+        if (j == 0) { F8_MFMA(0, 0); F8_MFMA(1, 0); }
+        if (j == 1) { F8_MFMA(0, 1); F8_MFMA(1, 1); }
+        if (j == 2) { F8_MFMA(0, 2); F8_MFMA(1, 2); }
+        if (j == 3) { F8_MFMA(0, 3); F8_MFMA(1, 3); }
+#undef F8_MFMA
       }
     }
-    __builtin_amdgcn_wave_barrier();
-    // LDS -> global: 16-byte chunks, whole rows
-    constexpr int CHUNKS = 128 * ES / 16;           // per row
-    constexpr int ROWS_PER_INSTR = 64 / CHUNKS;
-#pragma unroll 4
-    for (int it = 0; it < PASS_ROWS / ROWS_PER_INSTR; it++) {
-      const int lr = it * ROWS_PER_INSTR + lane / CHUNKS;
-      const int ch = lane % CHUNKS;
-      const int gm = mw + pass * PASS_ROWS + lr;
-      const int gn = nw + ch * (16 / ES);
+  }
+
+  // Epilogue, staged through LDS so that global stores write whole rows: for each 32-row half
+  // of its sub-tile a wave writes its results into a private LDS region, then reads rows back,
+  // 16 bytes per lane, and stores them. Every wave must be done with the stage buffers first.
+  constexpr int ES = C_BF16 ? 2 : 4;                 // output element size
+  constexpr int PITCH = 128 * ES + 8 * ES;           // padded row pitch of the region
+  constexpr int EPL = 16 / ES;                       // outputs per 16-byte chunk
+  constexpr int CPR = 128 / EPL;                     // chunks per row (16 or 32)
+  constexpr int RPI = 64 / CPR;                      // rows per read-back instruction (4 or 2)
+  __builtin_amdgcn_s_barrier();
+  uint8_t* reg = smem + wave * (32 * PITCH);
+  const int mw = tm * FT + 64 * wm, nw = tn * FT + 128 * wn;
+  const bool vec_ok = (g.ldc % EPL) == 0 && (((uintptr_t)g.c) & 15) == 0;
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        uint8_t* dst = reg + r * PITCH + (32 * j + 8 * q + 4 * gq) * ES;
+        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+        if (C_BF16)
+          *(uint2*)dst = make_uint2((uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16),
+                                    (uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16));
+        else
+          *(float4*)dst = make_float4(v0, v1, v2, v3);
+      }
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; it++) {
+      const int row = it * RPI + lane / CPR, ch = lane % CPR;
+      const uint4 v = *(const uint4*)(reg + row * PITCH + ch * 16);
+      const int gm = mw + 32 * i + row, gn = nw + ch * EPL;
       if (gm >= g.M) continue;
-      const uint4 v = *(const uint4*)(ep + lr * PITCH + ch * 16);
-      uint8_t* dst = (uint8_t*)g.c + ((int64_t)gm * g.ldc + gn) * ES;
-      if (vec_ok && gn + 16 / ES <= g.N) {
-        *(uint4*)dst = v;
+      uint8_t* out = (uint8_t*)g.c + ((int64_t)gm * g.ldc + gn) * ES;
+      if (vec_ok && gn + EPL <= g.N) {
+        *(uint4*)out = v;
       } else {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < 16 / ES; e++) {
+        for (int e = 0; e < EPL; e++) {
           if (gn + e >= g.N) break;
-          if (C_BF16) ((uint16_t*)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-          else ((uint32_t*)dst)[e] = w[e];
+          if (C_BF16) ((uint16_t*)out)[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+          else ((uint32_t*)out)[e] = w4[e];
         }
       }
     }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -331,65 +350,78 @@ static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool gemm_f8_eligible(int64_t M, int64_t N, int64_t K) { return K > 0 && K % FK == 0 && M >= 64 && N >= FT; }
 
-size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K) {
-  size_t s = al256((size_t)M * K) + al256((size_t)M * (K / 32));
-  if (!b_fp4) s += al256((size_t)N * K);
-  return s;
+struct F8Ws {
+  size_t a8, as_p, bs_p, b8, total;
+};
+static F8Ws f8_ws_layout(int b_fp4, int64_t M, int64_t N, int64_t K) {
+  const int64_t tm = (M + FT - 1) / FT, tn = (N + FT - 1) / FT;
+  F8Ws w{};
+  size_t off = 0;
+  w.a8 = off; off += al256((size_t)M * K);
+  w.as_p = off; off += al256((size_t)(K / FK) * tm * 1024);
+  w.bs_p = off; off += al256((size_t)(K / FK) * tn * 1024);
+  w.b8 = off; if (!b_fp4) off += al256((size_t)N * K);
+  w.total = off;
+  return w;
 }
 
-// LDS the kernel needs: the stage ring, or the epilogue's per-wave staging if that is larger
-template <int B_FP4, int C_BF16, int NS>
+size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K) { return f8_ws_layout(b_fp4, M, N, K).total; }
+
+template <int B_FP4, int C_BF16>
 constexpr size_t f8_lds_bytes() {
-  constexpr size_t ring = (size_t)NS * F8Stage<B_FP4>::BYTES;
-  constexpr size_t epi = 4 * (C_BF16 ? 128 * (128 * 2 + 16) : 64 * (128 * 4 + 16));
+  const size_t ring = (size_t)2 * F8Stage<B_FP4>::BYTES;
+  const size_t epi = (size_t)(F8_THREADS / 64) * 32 * (C_BF16 ? 272 : 544);
   return ring > epi ? ring : epi;
 }
 
-template <int B_FP4, int C_BF16, int NS>
+template <int B_FP4, int C_BF16>
 static hipError_t launch_f8(const F8Args& a, hipStream_t s) {
-  const size_t lds = f8_lds_bytes<B_FP4, C_BF16, NS>();
-  static_assert(f8_lds_bytes<B_FP4, C_BF16, NS>() <= 160 * 1024, "LDS budget");
+  constexpr size_t lds = f8_lds_bytes<B_FP4, C_BF16>();
+  static_assert(lds <= 160 * 1024, "LDS budget");
   static bool attr = false;  // raise the dynamic LDS limit once per instantiation
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_f8<B_FP4, C_BF16, NS>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_f8<B_FP4, C_BF16>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int tiles = ((a.M + FT - 1) / FT) * ((a.N + FT - 1) / FT);
-  hipLaunchKernelGGL((k_gemm_f8<B_FP4, C_BF16, NS>), dim3(tiles), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((k_gemm_f8<B_FP4, C_BF16>), dim3(tiles), dim3(F8_THREADS), lds, s, a);
   return hipGetLastError();
+}
+
+static inline unsigned grid1d(int64_t n) {
+  int64_t b = (n + 255) / 256;
+  if (b > 65535 * 4) b = 65535 * 4;
+  return (unsigned)(b < 1 ? 1 : b);
 }
 
 hipError_t launch_gemm_f8(int a_fmt, int b_fp4, int c_bf16, const uint8_t* a_codes, const void* a_shared,
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
-                          int64_t ldc, const float* row_div, void* ws, hipStream_t s) {
+                          int64_t ldc, void* ws, hipStream_t s) {
+  const F8Ws L = f8_ws_layout(b_fp4, M, N, K);
   uint8_t* base = (uint8_t*)ws;
-  uint8_t* a8 = base;
-  uint8_t* as_t = base + al256((size_t)M * K);
-  uint8_t* b8 = as_t + al256((size_t)M * (K / 32));
-  {
-    const int64_t total = M * (K >> 3);
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65535 * 4) blocks = 65535 * 4;
-    if (a_fmt) hipLaunchKernelGGL(k_expand_a<1>, dim3((unsigned)blocks), dim3(256), 0, s, a_codes, a_shared, M, K, a8, as_t);
-    else hipLaunchKernelGGL(k_expand_a<0>, dim3((unsigned)blocks), dim3(256), 0, s, a_codes, a_shared, M, K, a8, as_t);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const int tiles_m = (int)((M + FT - 1) / FT), tiles_n = (int)((N + FT - 1) / FT);
+  if (a_fmt)
+    hipLaunchKernelGGL(k_expand_a<1>, dim3(grid1d(M * (K >> 3))), dim3(256), 0, s, a_codes, a_shared, M, K, tiles_m,
+                       base + L.a8, base + L.as_p);
+  else
+    hipLaunchKernelGGL(k_expand_a<0>, dim3(grid1d(M * (K >> 3))), dim3(256), 0, s, a_codes, a_shared, M, K, tiles_m,
+                       base + L.a8, base + L.as_p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_permute_b_scales, dim3(grid1d(N * (K >> 5))), dim3(256), 0, s, b_scales, N, K, tiles_n,
+                     base + L.bs_p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (!b_fp4) {
-    const int64_t total = N * (K >> 3);
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65535 * 4) blocks = 65535 * 4;
-    hipLaunchKernelGGL(k_expand_b_int4, dim3((unsigned)blocks), dim3(256), 0, s, b_codes, N, K, b8);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_expand_b_int4, dim3(grid1d(N * (K >> 3))), dim3(256), 0, s, b_codes, N, K, base + L.b8);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   F8Args a{};
-  a.a8 = a8; a.as_t = as_t; a.b = b_fp4 ? b_codes : b8; a.bs = b_scales;
-  a.c = c; a.ldc = ldc; a.row_div = row_div; a.M = (int)M; a.N = (int)N; a.K = (int)K;
-  if (b_fp4) return c_bf16 ? launch_f8<1, 1, 3>(a, s) : launch_f8<1, 0, 3>(a, s);
-  return c_bf16 ? launch_f8<0, 1, 2>(a, s) : launch_f8<0, 0, 2>(a, s);
+  a.a8 = base + L.a8; a.as_p = base + L.as_p; a.b = b_fp4 ? b_codes : base + L.b8; a.bs_p = base + L.bs_p;
+  a.c = c; a.ldc = ldc; a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  if (b_fp4) return c_bf16 ? launch_f8<1, 1>(a, s) : launch_f8<1, 0>(a, s);
+  return c_bf16 ? launch_f8<0, 1>(a, s) : launch_f8<0, 0>(a, s);
 }
 
 }  // namespace mix

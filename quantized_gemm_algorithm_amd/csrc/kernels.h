@@ -49,7 +49,7 @@ bool gemm_f8_eligible(int64_t M, int64_t N, int64_t K);
 size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_f8(int a_fmt, int b_fp4, int c_bf16, const uint8_t* a_codes, const void* a_shared,
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
-                          int64_t ldc, const float* row_div, void* ws, hipStream_t s);
+                          int64_t ldc, void* ws, hipStream_t s);
 
 // attention (arguments validated by the C-ABI layer)
 size_t attn_prefill_ws_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t d);

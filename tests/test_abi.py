@@ -89,8 +89,9 @@ def test_gemm_validation(lib):
         assert fn(1, None, None, 1, None, None, 4, 0, 32, None, 0, 0, None) == MIX_OK
         assert fn(1, FAKE, FAKE, 1, FAKE, FAKE, 2**31, 4, 32, FAKE, 0, 4, None) == MIX_E_SHAPE
     # fast-path workspace size: zero when the shape does not take it
-    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 4096, 18944, 3584) == 4096 * 3584 + 4096 * 112
-    assert lib.mix_mx_gemm_workspace_bytes(1, 0, 256, 256, 128) == 256 * 128 + 1024 + 256 * 128
+    # E4M3 A + per-(K step, 256-row tile) 1 KB scale blocks for A and B (+ E4M3 B for MXINT4)
+    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 4096, 18944, 3584) == 4096 * 3584 + 28 * 16 * 1024 + 28 * 74 * 1024
+    assert lib.mix_mx_gemm_workspace_bytes(1, 0, 256, 256, 128) == 256 * 128 + 1024 + 1024 + 256 * 128
     assert lib.mix_mx_gemm_workspace_bytes(1, 1, 256, 256, 96) == 0
     assert lib.mix_mx_gemm_workspace_bytes(1, 1, 16, 18944, 3584) == 0
     # a misaligned workspace is rejected when the fast path is taken
