@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the MiX hot path on one MI355X.
 
-One step = MiX-4.5b quantization of the activations X [4096 x 3584] (bf16) followed by the
-A-MiX x W-MXFP4 product with W^T [18944 x 3584] (bf16 output) -- the Qwen2-VL-7B-shaped prefill
-linear layer. The weights are MX-coded once before timing (offline in deployment); their
-quantizer is timed separately and reported beside the step.
+One step = MiX-4.5b quantization of the activations X [4096 x 3584] (bf16; one kernel writes the
+MiX codes and the GEMM's decoded A image) followed by the A-MiX x W-MXFP4 product with
+W^T [18944 x 3584] (bf16 output) -- the Qwen2-VL-7B-shaped prefill linear layer. The weights are
+MX-coded and imaged once before timing (offline in deployment); their quantizer is timed
+separately and reported beside the step.
 
 Prints ONE JSON line. ``value`` is the step's throughput in TFLOP/s (2 M N K per step over the
 timed wall time, inputs resident in HBM). ``roofline`` reports the dominant kernel (the GEMM)
@@ -90,8 +91,8 @@ def cpu_baseline_linear(x_bits, w_t_bits, a_fmt, b_fmt, rows, cols, label):
     flops = 2.0 * rows * cols * K
     assert np.isfinite(c).all()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{label}: rows 0..{rows - 1} of X x columns 0..{cols - 1} of W (MiX quantize + fp64 product), "
-                      f"{dt:.1f} s"}
+            "sample": f"{label}: rows 0..{rows - 1} of X x columns 0..{cols - 1} of W (MiX quantize, decode, fp64 "
+                      f"product; the weights' MX codes made before timing), {dt:.1f} s"}
 
 
 # ---------------------------------------------------------------- workloads
@@ -115,20 +116,20 @@ def bench_linear(torch, q, args, which):
     w = to_bf16(g["w_t"])
     nrot = rotating(x0.numel() * 2)
     xs = [x0] + [x0.clone() for _ in range(nrot - 1)]
-    # weights: coded once (timed separately below)
+    # weights: MX-coded and imaged once (offline in deployment; the quantizer is timed separately)
     bc, bs = q.mx_quantize(w, b_fmt)
+    bimg = q.mx_gemm_b_image(bc, bs, b_fmt)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    codes = [q.mix_quantize(x, a_fmt) for x in xs[:2]]
-    wsb = q.mix_mx_gemm_workspace_bytes(a_fmt, b_fmt, M, N, K)
-    ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev) if wsb else None
+    # per step: MiX codes + the GEMM's A image in one pass, then the GEMM from the images
+    bufs = [q.mix_quantize_gemm(x, a_fmt) for x in xs[:2]]
 
     def step(i, marks=None):
         x = xs[i % nrot]
-        ac, as_ = codes[i % 2]
+        ac, as_, aimg = bufs[i % 2]
         e0 = marks.mark() if marks else None
-        q.mix_quantize(x, a_fmt, codes=ac, shared=as_)
+        q.mix_quantize_gemm(x, a_fmt, codes=ac, shared=as_, image=aimg)
         e1 = marks.mark() if marks else None
-        q.mix_mx_gemm(ac, as_, a_fmt, bc, bs, b_fmt, out=out, workspace=ws)
+        q.mix_mx_gemm_images(aimg, bimg, out=out)
         e2 = marks.mark() if marks else None
         return e0, e1, e2
 
@@ -161,9 +162,13 @@ def bench_linear(torch, q, args, which):
 
     flops = 2.0 * M * N * K
     sh_bytes = 2 if a_fmt == "4.5b" else 1
-    q_bytes = M * K * 2 + M * K // 2 + M * (K // 32) * sh_bytes  # bf16 in, codes + shared out
+    tiles_m, tiles_n = -(-M // 256), -(-N // 256)
+    a_img_bytes = M * K + (K // 128) * tiles_m * 1024
+    # quantizer: bf16 in; codes + shared fields + the A image out
+    q_bytes = M * K * 2 + M * K // 2 + M * (K // 32) * sh_bytes + a_img_bytes
     wq_bytes = N * K * 2 + N * K // 2 + N * (K // 32)
-    gemm_bytes = M * K // 2 + M * (K // 32) * sh_bytes + N * K // 2 + N * (K // 32) + M * N * 2
+    b_bytes = (N * K // 2 if b_fmt == "fp4" else N * K) + (K // 128) * tiles_n * 1024
+    gemm_bytes = a_img_bytes + b_bytes + M * N * 2  # each operand once + C
     gemm_tflops = flops / (g_ms * 1e-3) / 1e12
     res = {
         "metric": "A-MiX4.5b x W-MXFP4 GEMM TFLOP/s + quantizer GB/s (% of MI355X peak)" if which == "prefill_linear"
@@ -177,16 +182,17 @@ def bench_linear(torch, q, args, which):
         "config": {"workload": wl, "M": M, "K": K, "N": N, "a_format": "MiX-" + a_fmt,
                    "b_format": "MX" + b_fmt.upper(), "out": "bf16"},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gemm_tflops / FP8_MFMA_PEAK_TFLOPS, "traffic": None, "kernel": "k_gemm_mfma",
-                     "kernel_ms": g_ms, "algorithmic_bytes": gemm_bytes},
-        "quantizer": {"kernel": "k_mix_quantize", "ms": q_ms, "GB/s": q_bytes / (q_ms * 1e-3) / 1e9,
+                     "frac": gemm_tflops / FP8_MFMA_PEAK_TFLOPS, "traffic": None, "kernel": "k_gemm_f8",
+                     "kernel_ms": g_ms, "algorithmic_flops": flops, "operand_bytes": gemm_bytes},
+        "quantizer": {"kernel": "k_mix_quantize (codes + A image)", "ms": q_ms,
+                      "GB/s": q_bytes / (q_ms * 1e-3) / 1e9,
                       "frac_hbm": q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": q_bytes,
                       "rotating_buffers": nrot},
         "weight_quantizer": {"kernel": "k_mx_quantize", "ms": wq_ms, "GB/s": wq_bytes / (wq_ms * 1e-3) / 1e9,
                              "frac_hbm": wq_bytes / (wq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": wq_bytes},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_linear(g["x"], g["w_t"], a_fmt, b_fmt, 128, 4096, wl)
+        res["cpu_baseline"] = cpu_baseline_linear(g["x"], g["w_t"], a_fmt, b_fmt, M, N, wl)
     return res
 
 

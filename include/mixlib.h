@@ -134,6 +134,46 @@ mix_status_t mix_mx_gemm(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_
 size_t mix_mx_gemm_workspace_bytes(mix_fmt_t a_fmt, mx_fmt_t b_fmt, int64_t M, int64_t N, int64_t K);
 
 /*
+ * GEMM operand images: the decode-once form mix_mx_gemm's fast path streams, exposed so that a
+ * weight's image is built once and an activation's image comes straight out of the quantizer.
+ * The values are exactly those of the codes (same product as mix_mx_gemm, P1 method overview,
+ * dual-format bullet and Eq. (6)): a MiX element (1.m)_2 2^(Emax - dE) is stored as the E4M3
+ * byte of (1.m)_2 2^(1 - dE) under the E8M0 block scale 2^(Emax - 1); an MXINT4 element
+ * q 2^(X - 2) as the E4M3 byte of q/4 under its unchanged scale 2^X; MXFP4 codes are the E2M1
+ * operand as stored.
+ * Images are opaque byte buffers of the sizes below (0 = no image for that shape: K must be a
+ * positive multiple of 128), 256-byte aligned, owned by the caller. An image depends only on the
+ * operand's codes and shape (not on the other operand).
+ */
+size_t mix_gemm_a_image_bytes(int64_t M, int64_t K);
+size_t mx_gemm_b_image_bytes(mx_fmt_t b_fmt, int64_t N, int64_t K);
+
+/* A image from MiX codes ([M, K/2] codes, [M, K/32] shared fields as for mix_mx_gemm). */
+mix_status_t mix_gemm_a_image(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, int64_t M, int64_t K,
+                              void* img, size_t img_bytes, void* stream);
+
+/*
+ * mix_quantize that also writes the A image of the quantized rows in the same pass (rows = M,
+ * cols = K). codes and shared may both be NULL: then only the image is written. The image equals
+ * mix_gemm_a_image of the codes mix_quantize produces.
+ */
+mix_status_t mix_quantize_gemm(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols,
+                               int64_t ldx, uint8_t* codes, void* shared, void* img, size_t img_bytes, void* stream);
+
+/* B image from MX codes ([N, K/2] codes, [N, K/32] E8M0 scales). */
+mix_status_t mx_gemm_b_image(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8_t* b_scales, int64_t N, int64_t K,
+                             void* img, size_t img_bytes, void* stream);
+
+/*
+ * C = A . B^T from the two images (same results as mix_mx_gemm on the codes). For MX_FP4 the
+ * E2M1 nibbles are read from b_codes ([N, K/2], 16-byte aligned) -- the B image holds only the
+ * scales; for MX_INT4 b_codes is ignored and may be NULL. c and ldc as for mix_mx_gemm.
+ */
+mix_status_t mix_mx_gemm_images(mx_fmt_t b_fmt, const void* a_img, const void* b_img, const uint8_t* b_codes,
+                                int64_t M, int64_t N, int64_t K, void* c, mix_dtype_t c_dtype, int64_t ldc,
+                                void* stream);
+
+/*
  * The same product computed as P1's Eq. (6) on the vector ALUs: integer sub-block sums of the MX
  * mantissas scaled by 2^(7 - dE), times (8 + m_k), one power-of-two scale per block, fp32
  * accumulation across blocks. Same arguments and results (to fp32 rounding) as mix_mx_gemm.

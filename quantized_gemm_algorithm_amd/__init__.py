@@ -22,7 +22,8 @@ DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 
 __all__ = [
     "MixError", "mix_quantize", "mx_quantize", "mx_quantize_cols", "mix_dequantize", "mx_dequantize",
-    "mix_mx_gemm", "mix_mx_gemm_eq6", "mix_kmean", "mix_attn_prefill", "KVCache", "mix_kv_cache_prefill",
+    "mix_mx_gemm", "mix_mx_gemm_eq6", "AImage", "BImage", "mix_gemm_a_image", "mix_quantize_gemm",
+    "mx_gemm_b_image", "mix_mx_gemm_images", "mix_kmean", "mix_attn_prefill", "KVCache", "mix_kv_cache_prefill",
     "mix_attn_decode", "abi_version",
 ]
 
@@ -151,6 +152,97 @@ def mix_mx_gemm(a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype=to
     check(_lib_().mix_mx_gemm(MIX_FMT[a_fmt], _p(a_codes), _p(a_shared), MX_FMT[b_fmt], _p(b_codes), _p(b_scales),
                               M, N, K, _p(out), DTYPE[out.dtype], out.stride(0), _p(ws),
                               0 if ws is None else ws.numel(), _stream()), "mix_mx_gemm")
+    return out
+
+
+class AImage:
+    """Decode-once GEMM operand of an [M, K] MiX matrix: opaque device bytes (``buf``)."""
+
+    def __init__(self, buf, M, K):
+        self.buf, self.M, self.K = buf, M, K
+
+
+class BImage:
+    """Decode-once GEMM operand of an [N, K] MX matrix; MXFP4 images keep a reference to the codes."""
+
+    def __init__(self, buf, fmt, N, K, codes):
+        self.buf, self.fmt, self.N, self.K, self.codes = buf, fmt, N, K, codes
+
+
+def mix_gemm_a_image_bytes(M, K):
+    return _lib_().mix_gemm_a_image_bytes(M, K)
+
+
+def mx_gemm_b_image_bytes(b_fmt, N, K):
+    return _lib_().mx_gemm_b_image_bytes(MX_FMT[b_fmt], N, K)
+
+
+def _image_buf(nbytes, device, buf, what):
+    if nbytes == 0:
+        raise MixError(f"{what}: no image for this shape (K must be a positive multiple of 128)")
+    if buf is None:
+        return torch.empty((nbytes,), dtype=torch.uint8, device=device)
+    _need_cuda(buf)
+    if buf.dtype != torch.uint8 or not buf.is_contiguous() or buf.numel() < nbytes:
+        raise MixError(f"{what}: image buffer must be a contiguous uint8 tensor of at least {nbytes} bytes")
+    return buf
+
+
+def mix_gemm_a_image(codes, shared, fmt="4.5b", out=None):
+    """A image of MiX codes [M, K/2] + shared fields [M, K/32]."""
+    _need_cuda(codes, shared)
+    M, K = codes.shape[0], codes.shape[1] * 2
+    buf = _image_buf(mix_gemm_a_image_bytes(M, K), codes.device, out, "mix_gemm_a_image")
+    check(_lib_().mix_gemm_a_image(MIX_FMT[fmt], _p(codes), _p(shared), M, K, _p(buf), buf.numel(), _stream()),
+          "mix_gemm_a_image")
+    return AImage(buf, M, K)
+
+
+def mix_quantize_gemm(x, fmt="4.5b", codes=None, shared=None, image=None, write_codes=True):
+    """mix_quantize that also writes the A image in the same pass. Returns (codes, shared, AImage);
+    with ``write_codes=False`` only the image is written and codes/shared are None."""
+    if isinstance(image, AImage):
+        image = image.buf
+    _need_cuda(x, codes, shared, image)
+    rows, cols, ld = _matrix(x, "x")
+    if write_codes:
+        if codes is None:
+            codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+        if shared is None:
+            shared = torch.empty((rows, cols // 32), dtype=torch.uint8 if fmt == "4.25b" else torch.int16,
+                                 device=x.device)
+        if codes.numel() != rows * (cols // 2) or shared.numel() != rows * (cols // 32) or not codes.is_contiguous() \
+                or not shared.is_contiguous() or shared.element_size() != (1 if fmt == "4.25b" else 2):
+            raise MixError("codes/shared do not match the input's shape or the format")
+    else:
+        codes = shared = None
+    buf = _image_buf(mix_gemm_a_image_bytes(rows, cols), x.device, image, "mix_quantize_gemm")
+    check(_lib_().mix_quantize_gemm(MIX_FMT[fmt], _p(x), DTYPE[x.dtype], rows, cols, ld, _p(codes), _p(shared),
+                                    _p(buf), buf.numel(), _stream()), "mix_quantize_gemm")
+    return codes, shared, AImage(buf, rows, cols)
+
+
+def mx_gemm_b_image(codes, scales, fmt="fp4", out=None):
+    """B image of MX codes [N, K/2] + E8M0 scales [N, K/32] (built once per weight)."""
+    _need_cuda(codes, scales)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    buf = _image_buf(mx_gemm_b_image_bytes(fmt, N, K), codes.device, out, "mx_gemm_b_image")
+    check(_lib_().mx_gemm_b_image(MX_FMT[fmt], _p(codes), _p(scales), N, K, _p(buf), buf.numel(), _stream()),
+          "mx_gemm_b_image")
+    return BImage(buf, fmt, N, K, codes)
+
+
+def mix_mx_gemm_images(a_img, b_img, out_dtype=torch.float32, out=None):
+    """C [M, N] = A . B^T from an AImage and a BImage (same results as mix_mx_gemm on the codes)."""
+    if a_img.K != b_img.K:
+        raise MixError("A and B images disagree on K")
+    M, N, K = a_img.M, b_img.N, a_img.K
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_img.buf.device)
+    _need_cuda(out)
+    check(_lib_().mix_mx_gemm_images(MX_FMT[b_img.fmt], _p(a_img.buf), _p(b_img.buf),
+                                     _p(b_img.codes) if b_img.fmt == "fp4" else None, M, N, K, _p(out),
+                                     DTYPE[out.dtype], out.stride(0), _stream()), "mix_mx_gemm_images")
     return out
 
 

@@ -32,6 +32,13 @@ SIGNATURES = {
     "mix_mx_gemm_workspace_bytes": (ctypes.c_size_t, [c_int, c_int, c_i64, c_i64, c_i64]),
     "mix_mx_gemm_eq6": (c_int, [c_int, c_ptr, c_ptr, c_int, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_int, c_i64,
                                 c_ptr]),
+    "mix_gemm_a_image_bytes": (ctypes.c_size_t, [c_i64, c_i64]),
+    "mx_gemm_b_image_bytes": (ctypes.c_size_t, [c_int, c_i64, c_i64]),
+    "mix_gemm_a_image": (c_int, [c_int, c_ptr, c_ptr, c_i64, c_i64, c_ptr, ctypes.c_size_t, c_ptr]),
+    "mix_quantize_gemm": (c_int, [c_int, c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr, c_ptr, c_ptr, ctypes.c_size_t,
+                                  c_ptr]),
+    "mx_gemm_b_image": (c_int, [c_int, c_ptr, c_ptr, c_i64, c_i64, c_ptr, ctypes.c_size_t, c_ptr]),
+    "mix_mx_gemm_images": (c_int, [c_int, c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_int, c_i64, c_ptr]),
     "mix_kmean": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr, c_ptr]),
     "mix_attn_prefill_workspace_bytes": (ctypes.c_size_t, [c_i64, c_i64, c_i64, c_i64]),
     "mix_attn_prefill": (c_int, [c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_i64, c_int, c_ptr, c_ptr, c_ptr,

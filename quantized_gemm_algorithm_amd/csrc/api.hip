@@ -6,6 +6,7 @@
 #include <string>
 
 #include "../../include/mixlib.h"
+#include "f8_image.h"
 #include "kernels.h"
 
 namespace {
@@ -195,6 +196,98 @@ mix_status_t mix_mx_gemm_eq6(mix_fmt_t a_fmt, const uint8_t* a_codes, const void
                              void* c, mix_dtype_t c_dtype, int64_t ldc, void* stream) {
   return gemm_common("mix_mx_gemm_eq6", true, a_fmt, a_codes, a_shared, b_fmt, b_codes, b_scales, M, N, K, c, c_dtype,
                      ldc, nullptr, 0, stream);
+}
+
+// ---------------------------------------------------------------- GEMM operand images
+
+static bool image_k_ok(int64_t K) { return K > 0 && K % mix::FK == 0 && K <= INT32_MAX; }
+
+size_t mix_gemm_a_image_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || M > INT32_MAX || !image_k_ok(K)) return 0;
+  return mix::f8_a_image_layout(M, K).total;
+}
+
+size_t mx_gemm_b_image_bytes(mx_fmt_t b_fmt, int64_t N, int64_t K) {
+  if ((b_fmt != MX_INT4 && b_fmt != MX_FP4) || N <= 0 || N > INT32_MAX || !image_k_ok(K)) return 0;
+  return mix::f8_b_image_layout(b_fmt == MX_FP4, N, K).total;
+}
+
+static mix_status_t check_image(const char* fn, const void* img, size_t img_bytes, size_t need) {
+  if (!img) return fail(MIX_E_NULL, "%s: image is NULL", fn);
+  if ((uintptr_t)img & 255u) return fail(MIX_E_ALIGN, "%s: image must be 256-byte aligned", fn);
+  if (img_bytes < need) return fail(MIX_E_WORKSPACE, "%s: image buffer %zu < %zu bytes", fn, img_bytes, need);
+  return MIX_OK;
+}
+
+mix_status_t mix_gemm_a_image(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, int64_t M, int64_t K,
+                              void* img, size_t img_bytes, void* stream) {
+  g_err.clear();
+  const char* fn = "mix_gemm_a_image";
+  if (a_fmt != MIX_4P25 && a_fmt != MIX_4P5) return fail(MIX_E_ENUM, "%s: unknown MiX format %d", fn, (int)a_fmt);
+  if (M < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
+  if (M == 0) return MIX_OK;
+  if (M > INT32_MAX || !image_k_ok(K)) return fail(MIX_E_SHAPE, "%s: K=%lld is not a positive multiple of 128", fn, (long long)K);
+  if (!a_codes || !a_shared) return fail(MIX_E_NULL, "%s: codes or shared is NULL", fn);
+  if (!aligned16(a_codes) || (a_fmt == MIX_4P5 && ((uintptr_t)a_shared & 1u)))
+    return fail(MIX_E_ALIGN, "%s: codes not 16-byte aligned or shared misaligned", fn);
+  if (mix_status_t st = check_image(fn, img, img_bytes, mix::f8_a_image_layout(M, K).total)) return st;
+  return hip_status(mix::launch_gemm_a_image(a_fmt == MIX_4P5, a_codes, a_shared, M, K, img, (hipStream_t)stream), fn);
+}
+
+mix_status_t mix_quantize_gemm(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols,
+                               int64_t ldx, uint8_t* codes, void* shared, void* img, size_t img_bytes, void* stream) {
+  g_err.clear();
+  const char* fn = "mix_quantize_gemm";
+  if (fmt != MIX_4P25 && fmt != MIX_4P5) return fail(MIX_E_ENUM, "%s: unknown MiX format %d", fn, (int)fmt);
+  if (mix_status_t st = check_dtype(dtype)) return st;
+  bool empty;
+  if (mix_status_t st = check_matrix_in(fn, x, dtype, rows, cols, ldx, &empty)) return st;
+  if (rows == 0) return MIX_OK;
+  if (rows > INT32_MAX || !image_k_ok(cols))
+    return fail(MIX_E_SHAPE, "%s: cols=%lld is not a positive multiple of 128", fn, (long long)cols);
+  if (!codes != !shared) return fail(MIX_E_NULL, "%s: codes and shared must both be given or both be NULL", fn);
+  if (codes && (!aligned16(codes) || ((uintptr_t)shared & 1u)))
+    return fail(MIX_E_ALIGN, "%s: codes not 16-byte aligned or shared not 2-byte aligned", fn);
+  if (mix_status_t st = check_image(fn, img, img_bytes, mix::f8_a_image_layout(rows, cols).total)) return st;
+  return hip_status(mix::launch_mix_quantize_img((int)fmt, x, (int)dtype, rows, cols, ldx, codes, shared, img,
+                                                 (hipStream_t)stream),
+                    fn);
+}
+
+mix_status_t mx_gemm_b_image(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8_t* b_scales, int64_t N, int64_t K,
+                             void* img, size_t img_bytes, void* stream) {
+  g_err.clear();
+  const char* fn = "mx_gemm_b_image";
+  if (b_fmt != MX_INT4 && b_fmt != MX_FP4) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
+  if (N == 0) return MIX_OK;
+  if (N > INT32_MAX || !image_k_ok(K)) return fail(MIX_E_SHAPE, "%s: K=%lld is not a positive multiple of 128", fn, (long long)K);
+  if (!b_scales || (b_fmt == MX_INT4 && !b_codes)) return fail(MIX_E_NULL, "%s: codes or scales is NULL", fn);
+  if (b_fmt == MX_INT4 && !aligned16(b_codes)) return fail(MIX_E_ALIGN, "%s: codes not 16-byte aligned", fn);
+  if (mix_status_t st = check_image(fn, img, img_bytes, mix::f8_b_image_layout(b_fmt == MX_FP4, N, K).total)) return st;
+  return hip_status(mix::launch_gemm_b_image(b_fmt == MX_FP4, b_codes, b_scales, N, K, img, (hipStream_t)stream), fn);
+}
+
+mix_status_t mix_mx_gemm_images(mx_fmt_t b_fmt, const void* a_img, const void* b_img, const uint8_t* b_codes,
+                                int64_t M, int64_t N, int64_t K, void* c, mix_dtype_t c_dtype, int64_t ldc,
+                                void* stream) {
+  g_err.clear();
+  const char* fn = "mix_mx_gemm_images";
+  if (b_fmt != MX_INT4 && b_fmt != MX_FP4) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (mix_status_t st = check_dtype(c_dtype)) return st;
+  if (M < 0 || N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
+  if (M == 0 || N == 0) return MIX_OK;
+  if (M > INT32_MAX || N > INT32_MAX || !image_k_ok(K))
+    return fail(MIX_E_SHAPE, "%s: K=%lld is not a positive multiple of 128 (or an extent is above 2^31-1)", fn, (long long)K);
+  if (ldc < N) return fail(MIX_E_SHAPE, "%s: ldc=%lld < N=%lld", fn, (long long)ldc, (long long)N);
+  if (!c || !a_img || !b_img) return fail(MIX_E_NULL, "%s: c or an image is NULL", fn);
+  if (b_fmt == MX_FP4 && !b_codes) return fail(MIX_E_NULL, "%s: MXFP4 codes are NULL", fn);
+  if (((uintptr_t)a_img & 255u) || ((uintptr_t)b_img & 255u)) return fail(MIX_E_ALIGN, "%s: images must be 256-byte aligned", fn);
+  if (b_fmt == MX_FP4 && !aligned16(b_codes)) return fail(MIX_E_ALIGN, "%s: codes not 16-byte aligned", fn);
+  if ((uintptr_t)c % dtype_size(c_dtype)) return fail(MIX_E_ALIGN, "%s: c misaligned", fn);
+  return hip_status(mix::launch_gemm_images(b_fmt == MX_FP4, c_dtype == MIX_BF16, a_img, b_img, b_codes, M, N, K, c,
+                                            ldc, (hipStream_t)stream),
+                    fn);
 }
 
 mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, int64_t ldk, float* mu, void* stream) {

@@ -7,10 +7,12 @@
 // the product is exact and the MFMA accumulates in fp32.
 //
 // Decoding codes into MFMA operands inside the GEMM would repeat the work once per tile column
-// (74 times for a 4096 x 18944 x 3584 product). So the codes are decoded once by k_expand_a into
-// a workspace: E4M3 bytes [M, K] plus E8M0 scales laid out per 128-wide K step, [K/128][M][4].
-// MXINT4 weights become E4M3 bytes of q/4 (k_expand_b_int4), which keeps their E8M0 scales
-// unchanged. MXFP4 weights are used as stored: the E2M1 nibbles are the FP4 MFMA operand.
+// (74 times for a 4096 x 18944 x 3584 product). So each operand is decoded once into an image
+// (layout in f8_image.h): k_expand_a (or the quantizer itself) turns MiX codes into E4M3 bytes
+// plus permuted E8M0 scales; a weight's image (k_permute_b_scales, and k_expand_b_int4 for MXINT4
+// weights, whose q/4 is exact in E4M3 under the unchanged E8M0 scale) depends on the weight only
+// and can be built once. MXFP4 weights are used as stored: the E2M1 nibbles are the FP4 MFMA
+// operand.
 //
 // The GEMM streams both operands global->LDS with global_load_lds_dwordx4 (no registers, no
 // VALU). Each workgroup computes one 256 x 256 tile with 8 waves (two per SIMD, so one wave's
@@ -29,6 +31,7 @@
 // scale of row/column r for K block g. Result register k of lane l is
 // C[8 (k >> 2) + 4 (l >> 5) + (k & 3)][l & 31].
 #include "common.h"
+#include "f8_image.h"
 #include "kernels.h"
 #include "quant_dev.h"
 
@@ -40,17 +43,6 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 namespace mix {
 
 // ------------------------------------------------------------------ decode passes
-
-constexpr int FT = 256;   // tile M = tile N
-constexpr int FK = 128;   // K per stage
-
-// Byte position of the scale of (tile row rin, block b4 within the K step) inside the 1 KB a
-// (K step, tile) pair owns: [half-tile w][lane group gq][r][K half h][sub-tile i].
-__device__ __forceinline__ int f8_scale_pos(int rin, int b4) {
-  const int w = rin >> 7, i = (rin >> 5) & 3, r = rin & 31;
-  const int h = b4 >> 1, gq = b4 & 1;
-  return ((w * 2 + gq) * 32 + r) * 8 + h * 4 + i;
-}
 
 // One lane per 8-element sub-block: 4 code bytes -> 8 E4M3 bytes. Quad lane 0 writes the block's
 // E8M0 scale 2^(Emax-1) into the permuted scale layout [K/128][tiles_m][1024].
@@ -346,26 +338,11 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
 
 // ------------------------------------------------------------------ host side
 
-static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 bool gemm_f8_eligible(int64_t M, int64_t N, int64_t K) { return K > 0 && K % FK == 0 && M >= 64 && N >= FT; }
 
-struct F8Ws {
-  size_t a8, as_p, bs_p, b8, total;
-};
-static F8Ws f8_ws_layout(int b_fp4, int64_t M, int64_t N, int64_t K) {
-  const int64_t tm = (M + FT - 1) / FT, tn = (N + FT - 1) / FT;
-  F8Ws w{};
-  size_t off = 0;
-  w.a8 = off; off += al256((size_t)M * K);
-  w.as_p = off; off += al256((size_t)(K / FK) * tm * 1024);
-  w.bs_p = off; off += al256((size_t)(K / FK) * tn * 1024);
-  w.b8 = off; if (!b_fp4) off += al256((size_t)N * K);
-  w.total = off;
-  return w;
+size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K) {
+  return f8_a_image_layout(M, K).total + f8_b_image_layout(b_fp4, N, K).total;
 }
-
-size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K) { return f8_ws_layout(b_fp4, M, N, K).total; }
 
 template <int B_FP4, int C_BF16>
 constexpr size_t f8_lds_bytes() {
@@ -396,32 +373,56 @@ static inline unsigned grid1d(int64_t n) {
   return (unsigned)(b < 1 ? 1 : b);
 }
 
-hipError_t launch_gemm_f8(int a_fmt, int b_fp4, int c_bf16, const uint8_t* a_codes, const void* a_shared,
-                          const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
-                          int64_t ldc, void* ws, hipStream_t s) {
-  const F8Ws L = f8_ws_layout(b_fp4, M, N, K);
-  uint8_t* base = (uint8_t*)ws;
-  const int tiles_m = (int)((M + FT - 1) / FT), tiles_n = (int)((N + FT - 1) / FT);
+hipError_t launch_gemm_a_image(int a_fmt, const uint8_t* a_codes, const void* a_shared, int64_t M, int64_t K,
+                               void* img, hipStream_t s) {
+  const F8AImage L = f8_a_image_layout(M, K);
+  uint8_t* base = (uint8_t*)img;
+  const int tiles_m = (int)((M + FT - 1) / FT);
   if (a_fmt)
     hipLaunchKernelGGL(k_expand_a<1>, dim3(grid1d(M * (K >> 3))), dim3(256), 0, s, a_codes, a_shared, M, K, tiles_m,
                        base + L.a8, base + L.as_p);
   else
     hipLaunchKernelGGL(k_expand_a<0>, dim3(grid1d(M * (K >> 3))), dim3(256), 0, s, a_codes, a_shared, M, K, tiles_m,
                        base + L.a8, base + L.as_p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_b_image(int b_fp4, const uint8_t* b_codes, const uint8_t* b_scales, int64_t N, int64_t K,
+                               void* img, hipStream_t s) {
+  const F8BImage L = f8_b_image_layout(b_fp4, N, K);
+  uint8_t* base = (uint8_t*)img;
+  const int tiles_n = (int)((N + FT - 1) / FT);
   hipLaunchKernelGGL(k_permute_b_scales, dim3(grid1d(N * (K >> 5))), dim3(256), 0, s, b_scales, N, K, tiles_n,
                      base + L.bs_p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (!b_fp4) {
-    hipLaunchKernelGGL(k_expand_b_int4, dim3(grid1d(N * (K >> 3))), dim3(256), 0, s, b_codes, N, K, base + L.b8);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || b_fp4) return e;
+  hipLaunchKernelGGL(k_expand_b_int4, dim3(grid1d(N * (K >> 3))), dim3(256), 0, s, b_codes, N, K, base + L.b8);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const void* b_img, const uint8_t* b_codes,
+                              int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, hipStream_t s) {
+  const F8AImage LA = f8_a_image_layout(M, K);
+  const F8BImage LB = f8_b_image_layout(b_fp4, N, K);
   F8Args a{};
-  a.a8 = base + L.a8; a.as_p = base + L.as_p; a.b = b_fp4 ? b_codes : base + L.b8; a.bs_p = base + L.bs_p;
+  a.a8 = (const uint8_t*)a_img + LA.a8;
+  a.as_p = (const uint8_t*)a_img + LA.as_p;
+  a.b = b_fp4 ? b_codes : (const uint8_t*)b_img + LB.b8;
+  a.bs_p = (const uint8_t*)b_img + LB.bs_p;
   a.c = c; a.ldc = ldc; a.M = (int)M; a.N = (int)N; a.K = (int)K;
   if (b_fp4) return c_bf16 ? launch_f8<1, 1>(a, s) : launch_f8<1, 0>(a, s);
   return c_bf16 ? launch_f8<0, 1>(a, s) : launch_f8<0, 0>(a, s);
+}
+
+hipError_t launch_gemm_f8(int a_fmt, int b_fp4, int c_bf16, const uint8_t* a_codes, const void* a_shared,
+                          const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
+                          int64_t ldc, void* ws, hipStream_t s) {
+  uint8_t* a_img = (uint8_t*)ws;
+  uint8_t* b_img = a_img + f8_a_image_layout(M, K).total;
+  hipError_t e = launch_gemm_a_image(a_fmt, a_codes, a_shared, M, K, a_img, s);
+  if (e != hipSuccess) return e;
+  if ((e = launch_gemm_b_image(b_fp4, b_codes, b_scales, N, K, b_img, s)) != hipSuccess) return e;
+  return launch_gemm_images(b_fp4, c_bf16, a_img, b_img, b_codes, M, N, K, c, ldc, s);
 }
 
 }  // namespace mix

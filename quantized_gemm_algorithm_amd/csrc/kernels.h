@@ -50,6 +50,14 @@ size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_f8(int a_fmt, int b_fp4, int c_bf16, const uint8_t* a_codes, const void* a_shared,
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
                           int64_t ldc, void* ws, hipStream_t s);
+hipError_t launch_gemm_a_image(int a_fmt, const uint8_t* a_codes, const void* a_shared, int64_t M, int64_t K,
+                               void* img, hipStream_t s);
+hipError_t launch_gemm_b_image(int b_fp4, const uint8_t* b_codes, const uint8_t* b_scales, int64_t N, int64_t K,
+                               void* img, hipStream_t s);
+hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const void* b_img, const uint8_t* b_codes,
+                              int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, hipStream_t s);
+hipError_t launch_mix_quantize_img(int fmt, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                   uint8_t* codes, void* shared, void* img, hipStream_t s);
 
 // attention (arguments validated by the C-ABI layer)
 size_t attn_prefill_ws_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t d);

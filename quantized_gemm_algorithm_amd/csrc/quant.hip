@@ -14,6 +14,7 @@
 // leave as one 32-bit word per lane (8 nibbles), so a wave stores 256 contiguous bytes.
 
 #include "common.h"
+#include "f8_image.h"
 #include "kernels.h"
 #include "quant_dev.h"
 
@@ -43,9 +44,13 @@ __device__ __forceinline__ void load8(const void* base, int64_t row, int64_t ld,
 
 // ------------------------------------------------------------------ MiX quantizer (K1)
 
-template <int DT, int FMT>  // FMT 0 = MiX-4.25b, 1 = MiX-4.5b
+// With IMG the lane also writes the GEMM A image of its sub-block (f8_image.h): 8 E4M3 bytes, and
+// on quad lane 0 the block's E8M0 scale 2^(Emax-1). codes/shared may then be NULL (not written).
+template <int DT, int FMT, int IMG>  // FMT 0 = MiX-4.25b, 1 = MiX-4.5b
 __global__ void __launch_bounds__(256) k_mix_quantize(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
-                                                       uint8_t* __restrict__ codes, void* __restrict__ shared) {
+                                                       uint8_t* __restrict__ codes, void* __restrict__ shared,
+                                                       uint8_t* __restrict__ a8, uint8_t* __restrict__ as_p,
+                                                       int tiles_m) {
   const int64_t sub_per_row = cols >> 3;
   const int64_t total = rows * sub_per_row;  // multiple of 4
   const int lane = threadIdx.x & 63;
@@ -75,15 +80,25 @@ __global__ void __launch_bounds__(256) k_mix_quantize(const void* __restrict__ x
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; i++) word |= mix_code(xb[i], t) << (4 * i);
-    *(uint32_t*)(codes + row * (cols >> 1) + sc * 4) = word;
     int q = (int)(sc & 3);
     int64_t blk = sc >> 2;
-    if (FMT == 1) {
-      uint32_t f = (q == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * q));
-      f = quad_or_u32(f);
-      if (q == 0) ((uint16_t*)shared)[row * (cols >> 5) + blk] = (uint16_t)f;
-    } else {
-      if (q == 0) ((uint8_t*)shared)[row * (cols >> 5) + blk] = (uint8_t)((uint32_t)(emax + 7) | (m << 4));
+    if (!IMG || codes) {
+      *(uint32_t*)(codes + row * (cols >> 1) + sc * 4) = word;
+      if (FMT == 1) {
+        uint32_t f = (q == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * q));
+        f = quad_or_u32(f);
+        if (q == 0) ((uint16_t*)shared)[row * (cols >> 5) + blk] = (uint16_t)f;
+      } else {
+        if (q == 0) ((uint8_t*)shared)[row * (cols >> 5) + blk] = (uint8_t)((uint32_t)(emax + 7) | (m << 4));
+      }
+    }
+    if (IMG) {
+      uint32_t e0, e1;
+      mix8_to_e4m3(word, m, e0, e1);
+      *(uint2*)(a8 + row * cols + sc * 8) = make_uint2(e0, e1);
+      if (q == 0)
+        as_p[((blk >> 2) * tiles_m + row / FT) * 1024 + f8_scale_pos((int)(row % FT), (int)(blk & 3))] =
+            (uint8_t)(emax + 126);
     }
   }
 }
@@ -283,13 +298,27 @@ hipError_t launch_mix_quantize(int fmt, const void* x, int dtype, int64_t rows, 
                                uint8_t* codes, void* shared, hipStream_t s) {
   int64_t total = rows * (cols >> 3);
   dim3 g(grid_for(total)), b(256);
-  if (dtype == 1) {
-    if (fmt == 1) hipLaunchKernelGGL((k_mix_quantize<1, 1>), g, b, 0, s, x, rows, cols, ldx, codes, shared);
-    else hipLaunchKernelGGL((k_mix_quantize<1, 0>), g, b, 0, s, x, rows, cols, ldx, codes, shared);
-  } else {
-    if (fmt == 1) hipLaunchKernelGGL((k_mix_quantize<0, 1>), g, b, 0, s, x, rows, cols, ldx, codes, shared);
-    else hipLaunchKernelGGL((k_mix_quantize<0, 0>), g, b, 0, s, x, rows, cols, ldx, codes, shared);
-  }
+#define MQ(DT, F) hipLaunchKernelGGL((k_mix_quantize<DT, F, 0>), g, b, 0, s, x, rows, cols, ldx, codes, shared, \
+                                     nullptr, nullptr, 0)
+  if (dtype == 1) { if (fmt == 1) MQ(1, 1); else MQ(1, 0); }
+  else { if (fmt == 1) MQ(0, 1); else MQ(0, 0); }
+#undef MQ
+  return hipGetLastError();
+}
+
+hipError_t launch_mix_quantize_img(int fmt, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                   uint8_t* codes, void* shared, void* img, hipStream_t s) {
+  int64_t total = rows * (cols >> 3);
+  dim3 g(grid_for(total)), b(256);
+  const F8AImage L = f8_a_image_layout(rows, cols);
+  uint8_t* a8 = (uint8_t*)img + L.a8;
+  uint8_t* as_p = (uint8_t*)img + L.as_p;
+  const int tiles_m = (int)((rows + FT - 1) / FT);
+#define MQ(DT, F) hipLaunchKernelGGL((k_mix_quantize<DT, F, 1>), g, b, 0, s, x, rows, cols, ldx, codes, shared, a8, \
+                                     as_p, tiles_m)
+  if (dtype == 1) { if (fmt == 1) MQ(1, 1); else MQ(1, 0); }
+  else { if (fmt == 1) MQ(0, 1); else MQ(0, 0); }
+#undef MQ
   return hipGetLastError();
 }
 

@@ -104,3 +104,40 @@ def test_kmean_validation(lib):
     assert lib.mix_kmean(None, 1, 4, 32, 32, FAKE, None) == MIX_E_NULL
     assert lib.mix_kmean(FAKE, 1, 4, 32, 16, FAKE, None) == MIX_E_SHAPE
     assert lib.mix_kmean(None, 1, 4, 0, 0, None, None) == MIX_OK
+
+
+def test_image_sizes(lib):
+    # A image: E4M3 [M, K] (256-byte rounded) + one 1 KB scale block per (128-wide K step, 256-row tile)
+    assert lib.mix_gemm_a_image_bytes(4096, 3584) == 4096 * 3584 + 28 * 16 * 1024
+    assert lib.mix_gemm_a_image_bytes(1, 128) == 256 + 1024
+    assert lib.mix_gemm_a_image_bytes(4, 96) == 0
+    assert lib.mix_gemm_a_image_bytes(0, 128) == 0
+    # B image: permuted scales (+ E4M3 bytes of q/4 for MXINT4)
+    assert lib.mx_gemm_b_image_bytes(1, 18944, 3584) == 28 * 74 * 1024
+    assert lib.mx_gemm_b_image_bytes(0, 300, 256) == 2 * 2 * 1024 + 300 * 256
+    assert lib.mx_gemm_b_image_bytes(2, 300, 256) == 0
+    assert lib.mx_gemm_b_image_bytes(1, 300, 0) == 0
+
+
+def test_image_validation(lib):
+    A16 = P(0x10010)  # 16-byte but not 256-byte aligned
+    assert lib.mix_gemm_a_image(3, FAKE, FAKE, 4, 128, FAKE, 1 << 20, None) == MIX_E_ENUM
+    assert lib.mix_gemm_a_image(1, FAKE, FAKE, 4, 96, FAKE, 1 << 20, None) == MIX_E_SHAPE
+    assert lib.mix_gemm_a_image(1, None, FAKE, 4, 128, FAKE, 1 << 20, None) == MIX_E_NULL
+    assert lib.mix_gemm_a_image(1, FAKE, FAKE, 4, 128, A16, 1 << 20, None) == MIX_E_ALIGN
+    assert lib.mix_gemm_a_image(1, FAKE, FAKE, 4, 128, FAKE, 100, None) == MIX_E_WORKSPACE
+    assert lib.mix_gemm_a_image(1, None, None, 0, 128, None, 0, None) == MIX_OK
+    # codes and shared go together; cols must be a multiple of 128
+    assert lib.mix_quantize_gemm(1, FAKE, 1, 4, 128, 128, FAKE, None, FAKE, 1 << 20, None) == MIX_E_NULL
+    assert lib.mix_quantize_gemm(1, FAKE, 1, 4, 96, 96, None, None, FAKE, 1 << 20, None) == MIX_E_SHAPE
+    assert lib.mix_quantize_gemm(1, FAKE, 1, 4, 128, 128, None, None, FAKE, 10, None) == MIX_E_WORKSPACE
+    assert lib.mix_quantize_gemm(1, None, 1, 0, 128, 128, None, None, None, 0, None) == MIX_OK
+    assert lib.mx_gemm_b_image(1, FAKE, None, 4, 128, FAKE, 1 << 20, None) == MIX_E_NULL
+    assert lib.mx_gemm_b_image(0, None, FAKE, 4, 128, FAKE, 1 << 20, None) == MIX_E_NULL
+    assert lib.mx_gemm_b_image(0, FAKE, FAKE, 4, 128, A16, 1 << 20, None) == MIX_E_ALIGN
+    # GEMM from images: MXFP4 needs the codes; K a multiple of 128; images 256-byte aligned
+    assert lib.mix_mx_gemm_images(1, FAKE, FAKE, None, 4, 4, 128, FAKE, 0, 4, None) == MIX_E_NULL
+    assert lib.mix_mx_gemm_images(0, FAKE, FAKE, None, 4, 4, 100, FAKE, 0, 4, None) == MIX_E_SHAPE
+    assert lib.mix_mx_gemm_images(0, A16, FAKE, None, 4, 4, 128, FAKE, 0, 4, None) == MIX_E_ALIGN
+    assert lib.mix_mx_gemm_images(0, FAKE, FAKE, None, 4, 4, 128, FAKE, 0, 3, None) == MIX_E_SHAPE
+    assert lib.mix_mx_gemm_images(0, None, None, None, 0, 4, 128, None, 0, 4, None) == MIX_OK

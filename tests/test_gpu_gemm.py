@@ -64,6 +64,47 @@ def test_gemm_fast_path_shapes(a_fmt, b_fmt, workspace, M, N, K):
 
 
 @pytest.mark.parametrize("a_fmt,b_fmt", PAIRS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (300, 520, 1024), (257, 300, 384), (64, 256, 3584)])
+def test_gemm_images(a_fmt, b_fmt, M, N, K):
+    # the image path: operand images built from the codes (and straight from x by the fused
+    # quantizer), then the GEMM from images, against the oracle
+    q = _lib()
+    rng = np.random.default_rng(11 * M + 5 * N + K)
+    x = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-8, 8, (M, K)))).astype(np.float32)
+    w = (0.05 * rng.standard_normal((N, K)) * np.exp2(rng.integers(-3, 3, (N, K)))).astype(np.float32)
+    ac, as_, bc, bs = _code(x, w, a_fmt, b_fmt)
+    ad, bd = o_mix_deq(ac, as_, a_fmt), o_mx_deq(bc, bs, b_fmt)
+    ref, bound = gemm_ref(ad, bd), gemm_abs_bound(ad, bd)
+    A, S, B, Bs = _to_dev(ac, as_, bc, bs, a_fmt)
+    na = q.mix_gemm_a_image_bytes(M, K)
+    ai = q.mix_gemm_a_image(A, S, a_fmt, out=torch.zeros(na, dtype=torch.uint8, device="cuda"))
+    bi = q.mx_gemm_b_image(B, Bs, b_fmt)
+    got = q.mix_mx_gemm_images(ai, bi, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_gemm_close(host(got), ref, bound, f"images {a_fmt}x{b_fmt} fp32 {M}x{N}x{K}")
+    gotb = q.mix_mx_gemm_images(ai, bi, out_dtype=torch.bfloat16)
+    assert_bf16_matches(host(gotb), ref, bound, f"images {a_fmt}x{b_fmt} bf16 {M}x{N}x{K}")
+    # the fused quantizer writes the oracle's codes and the same image bytes
+    xd = dev_f32(x)
+    c2, s2, ai2 = q.mix_quantize_gemm(xd, a_fmt, image=torch.zeros(na, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert_codes_equal(host(c2), ac, "fused codes")
+    assert_codes_equal(host(s2), as_, "fused shared")
+    assert torch.equal(ai2.buf, ai.buf), "fused image differs from mix_gemm_a_image"
+    _, _, ai3 = q.mix_quantize_gemm(xd, a_fmt, write_codes=False,
+                                    image=torch.zeros(na, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(ai3.buf, ai.buf), "image-only quantize differs"
+    _, _, ai4 = q.mix_quantize_gemm(xd, a_fmt, codes=c2, shared=s2, image=ai3)  # an AImage is reused in place
+    torch.cuda.synchronize()
+    assert ai4.buf.data_ptr() == ai3.buf.data_ptr() and torch.equal(ai4.buf, ai.buf)
+    # same kernel as mix_mx_gemm's fast path: identical bits where that path is taken
+    if q.mix_mx_gemm_workspace_bytes(a_fmt, b_fmt, M, N, K):
+        ws = q.mix_mx_gemm(A, S, a_fmt, B, Bs, b_fmt, out_dtype=torch.float32, workspace="auto")
+        assert torch.equal(ws, got)
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", PAIRS)
 @pytest.mark.parametrize("fn", ["mix_mx_gemm", "mix_mx_gemm_eq6"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (64, 256, 512), (200, 136, 352), (130, 300, 96), (16, 18, 4096)])
 def test_gemm_random_shapes(a_fmt, b_fmt, fn, M, N, K):
