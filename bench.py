@@ -160,6 +160,16 @@ def bench_linear(torch, q, args, which):
         wq_ms.append(a.elapsed_time(b))
     wq_ms = float(np.median(wq_ms))
 
+    # the Eq. (6) shift-and-add path on the vector ALUs (the comparison), same operands
+    ac0, as0, _ = bufs[0]
+    eq6_ms = []
+    for _ in range(3):
+        a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+        a.record(); q.mix_mx_gemm_eq6(ac0, as0, a_fmt, bc, bs, b_fmt, out=out); b.record()
+        torch.cuda.synchronize()
+        eq6_ms.append(a.elapsed_time(b))
+    eq6_ms = float(np.median(eq6_ms))
+
     flops = 2.0 * M * N * K
     sh_bytes = 2 if a_fmt == "4.5b" else 1
     tiles_m, tiles_n = -(-M // 256), -(-N // 256)
@@ -190,9 +200,185 @@ def bench_linear(torch, q, args, which):
                       "rotating_buffers": nrot},
         "weight_quantizer": {"kernel": "k_mx_quantize", "ms": wq_ms, "GB/s": wq_bytes / (wq_ms * 1e-3) / 1e9,
                              "frac_hbm": wq_bytes / (wq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": wq_bytes},
+        "eq6_valu_gemm": {"kernel": "k_gemm_eq6", "ms": eq6_ms, "TFLOP/s": flops / (eq6_ms * 1e-3) / 1e12},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_linear(g["x"], g["w_t"], a_fmt, b_fmt, M, N, wl)
+    return res
+
+
+def bench_decode(torch, q, args):
+    """Decode step (batch 16): x [16, 3584] -> MiX-4.5b (+ A image) -> product with the MXFP4
+    weights [18944, 3584]; attention of q [16, 28, 128] over 8192 MX-coded cached tokens per row
+    (the new token at position 8191 smoothed with the frozen prefill mean and appended)."""
+    from quantized_gemm_algorithm_amd import synth
+    g = synth.decode_step()
+    B, L, Hkv, d = g["k_hist"].shape
+    Hq = g["q"].shape[1]
+    N, K = g["w_t"].shape
+    dev = torch.device("cuda")
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x = bf16(g["x"])
+    qd = bf16(g["q"])
+    w = bf16(g["w_t"])
+    bc, bs = q.mx_quantize(w, "fp4")
+    del w
+    # one set = weights (codes + image) and a KV cache; sets rotate to defeat the 256 MB MALL
+    w_bytes = N * K // 2 + N * (K // 32)
+    kv_bytes = 2 * B * Hkv * L * (d // 2 + d // 32)
+    nset = rotating(w_bytes + kv_bytes, min_total=600 << 20)
+    pos = torch.full((B,), L - 1, dtype=torch.int32, device=dev)
+    k_new = bf16(g["k_hist"][:, L - 1])
+    v_new = bf16(g["v_hist"][:, L - 1])
+    sets = []
+    mus = []
+    for b in range(B):
+        kd = bf16(g["k_hist"][b, :L - 1])
+        mus.append(q.mix_kmean(kd.reshape(L - 1, Hkv * d)).reshape(Hkv, d))
+    mu = torch.stack(mus)
+    for si in range(nset):
+        bci, bsi = (bc, bs) if si == 0 else (bc.clone(), bs.clone())
+        cache = q.KVCache(B, L, Hkv, d)
+        for b in range(B):
+            q.mix_kv_cache_prefill(cache, b, bf16(g["k_hist"][b, :L - 1]), bf16(g["v_hist"][b, :L - 1]), mu[b])
+        sets.append((q.mx_gemm_b_image(bci, bsi, "fp4"), cache))
+    torch.cuda.synchronize()
+    y = torch.empty((B, N), dtype=torch.bfloat16, device=dev)
+    _, _, aimg = q.mix_quantize_gemm(x, "4.5b")
+    ac, as_ = q.mix_quantize(x, "4.5b")
+    wsb = q._lib_().mix_attn_decode_workspace_bytes(B, Hq, Hkv, d, L - 1)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+
+    def step(i, marks=None):
+        bimg, cache = sets[i % nset]
+        e0 = marks.mark() if marks else None
+        q.mix_quantize_gemm(x, "4.5b", codes=ac, shared=as_, image=aimg)
+        e1 = marks.mark() if marks else None
+        q.mix_mx_gemm_images(aimg, bimg, out=y)
+        e2 = marks.mark() if marks else None
+        q.mix_attn_decode(qd, k_new, v_new, cache, pos, L - 1, mu, workspace=ws)
+        e3 = marks.mark() if marks else None
+        return e0, e1, e2, e3
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timer = KernelTimer(torch)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    evs = []
+    t0.record()
+    for i in range(args.steps):
+        evs.append(step(i, timer))
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    q_ms = float(np.mean([a.elapsed_time(b) for a, b, _, _ in evs]))
+    gv_ms = float(np.mean([b.elapsed_time(c) for _, b, c, _ in evs]))
+    at_ms = float(np.mean([c.elapsed_time(e) for _, _, c, e in evs]))
+
+    a_img_bytes = B * K + (K // 128) * 1024
+    gv_bytes = N * K // 2 + (K // 128) * (-(-N // 256)) * 1024 + a_img_bytes + B * N * 2
+    q_bytes = B * K * 2 + B * K // 2 + B * (K // 32) * 2 + a_img_bytes
+    # attention: the cached K and V codes + scales of 8192 tokens, q, the new token in and out, o
+    at_bytes = kv_bytes + B * Hq * d * 2 * 2 + 2 * B * Hkv * d * 2 + B * Hkv * d * 4
+    step_bytes = q_bytes + gv_bytes + at_bytes
+    gbs = gv_bytes / (gv_ms * 1e-3) / 1e9
+    res = {
+        "metric": "decode GB/s (% of MI355X HBM peak)",
+        "value": step_bytes / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3xe2m1->f32", "data": "synthetic",
+        "config": {"workload": "decode_step_b16_l8192", "B": B, "K": K, "N": N, "L": L, "Hq": Hq, "Hkv": Hkv,
+                   "d": d, "frac_hbm": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "bytes_per_step": step_bytes, "rotating_sets": nset},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "k_gemv_f8", "kernel_ms": gv_ms,
+                     "algorithmic_bytes": gv_bytes},
+        "parts": {"quantize_x_ms": q_ms, "gemv_ms": gv_ms,
+                  "attention_ms": at_ms, "attention_GB/s": at_bytes / (at_ms * 1e-3) / 1e9,
+                  "attention_bytes": at_bytes},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(g, w_bytes, kv_bytes // B)
+    return res
+
+
+def cpu_baseline_decode(g, w_bytes, kv_bytes_row, rows=2):
+    import oracle.attention as oa
+    import oracle.gemm as og
+    import oracle.mix as om
+    import oracle.mx as ox
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    bc, bs = ox.mx_quantize(g["w_t"], "fp4", "bf16")  # weights offline, as on the GPU
+    L = g["k_hist"].shape[1]
+    mu = np.stack([oa.kmean_ref(g["k_hist"][b, :L - 1], "bf16") for b in range(rows)])  # prefill's, frozen
+    t0 = time.perf_counter()
+    ac, as_ = om.mix_quantize(g["x"], "4.5b", "bf16")
+    og.gemm_ref(om.mix_dequantize(ac, as_, "4.5b"), ox.mx_dequantize(bc, bs, "fp4"))
+    oa.attn_decode_ref(g["q"][:rows], g["k_hist"][:rows], g["v_hist"][:rows], mu, np.full(rows, L))
+    dt = time.perf_counter() - t0
+    byts = w_bytes + rows * kv_bytes_row
+    return {"value": byts / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"decode step: the full x x W product (weights MX-coded before timing) and attention of batch "
+                      f"rows 0..{rows - 1} over {L} tokens (the oracle codes their K/V history itself), {dt:.1f} s; "
+                      f"credited bytes = weights + those rows' cached K/V"}
+
+
+def bench_attention(torch, q, args):
+    """Prefill attention: q [4096, 28, 128], k/v [4096, 4, 128] bf16, causal, K-smoothed."""
+    from quantized_gemm_algorithm_amd import synth
+    g = synth.attention_qkv()
+    T, Hq, d = g["q"].shape
+    Hkv = g["k"].shape[1]
+    dev = torch.device("cuda")
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    qd, kd, vd = bf16(g["q"]), bf16(g["k"]), bf16(g["v"])
+    wsb = q._lib_().mix_attn_prefill_workspace_bytes(T, Hq, Hkv, d)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+
+    def step():
+        q.mix_attn_prefill(qd, kd, vd, causal=True, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    # causal-exact work: row i attends to i + 1 keys; QK^T and PV each 2 d flops per (row, key)
+    pairs = Hq * T * (T + 1) // 2
+    flops = 2 * 2.0 * d * pairs
+    tf = flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "prefill attention TFLOP/s (causal-exact flops)",
+        "value": tf, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3xe2m1->f32", "data": "synthetic",
+        "config": {"workload": "prefill_attention_t4096_h28_kv4_d128", "T": T, "Hq": Hq, "Hkv": Hkv, "d": d,
+                   "causal": True, "workspace_bytes": wsb},
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / FP8_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "mix_attn_prefill (all kernels of the call)", "kernel_ms": ms_step},
+    }
     return res
 
 
@@ -225,9 +411,10 @@ def main():
     q._lib_()  # fail loudly if the HIP library is missing
     if args.workload in ("prefill_linear", "vision_linear"):
         res = bench_linear(torch, q, args, args.workload)
+    elif args.workload == "decode":
+        res = bench_decode(torch, q, args)
     else:
-        print(f"workload {args.workload} is not wired into bench.py yet", file=sys.stderr)
-        sys.exit(2)
+        res = bench_attention(torch, q, args)
     print(json.dumps(res))
 
 

@@ -336,9 +336,149 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   }
 }
 
+// ------------------------------------------------------------------ small-M product (decode)
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// M <= 16: the product is a stream over the weights. A workgroup owns 16 G weight rows
+// (G <= 8). Its slice of B, one K chunk at a time, is copied into LDS in one burst
+// (global_load_lds, rows padded by 16 bytes so that the 16 rows an MFMA reads sit in distinct
+// banks), while each wave loads its A fragments from the image. The 4 waves split the chunk's
+// 128-wide K steps; partial sums are added through LDS at the end. MFMA:
+// v_mfma_scale_f32_16x16x128_f8f6f4 with the weight rows as its A operand (lane l = r + 16 g holds
+// row r: FP4 K elements [32 g, 32 g + 32) in 16 bytes; E4M3 [16 g, 16 g + 16) and
+// [64 + 16 g, 64 + 16 g + 16)), the 16 activation rows as its B operand (E4M3, same split), and
+// the scale of lane l = the E8M0 scale of its row for K block g. Result register i of lane l is
+// C^T[4 (l >> 4) + i][l & 15]: four consecutive n for one m.
+constexpr int GV_MAXG = 8;
+constexpr int GV_MAXSPW = 8;   // K steps per wave per chunk (chunk <= 32 steps = 4096)
+
+struct GvArgs {
+  F8Args g;
+  int G;        // 16-row weight groups per workgroup
+  int kc;       // K chunk (multiple of 128, <= 4096)
+  int tiles_n;  // 256-row tiles of the B image's scale layout
+};
+
+template <int B_FP4, int C_BF16>
+__global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const F8Args& g = ga.g;
+  const int G = ga.G;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, gq = lane >> 4;
+  const int R = 16 * G;
+  const int n0 = blockIdx.x * R;
+  const int rowA = min(r, g.M - 1);
+  const int64_t browg = B_FP4 ? (g.K >> 1) : g.K;   // bytes per B row in global memory
+  constexpr int CPS = B_FP4 ? 4 : 8;                // 16-byte chunks of a B row per 128-wide K step
+  v4f acc[GV_MAXG];
+#pragma unroll
+  for (int j = 0; j < GV_MAXG; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int kc0 = 0; kc0 < g.K; kc0 += ga.kc) {
+    const int nks = min(ga.kc, g.K - kc0) / FK;      // K steps in this chunk
+    const int c16 = nks * CPS;                       // chunks per row in LDS (+1 pad)
+    const int spw = (nks + 3) >> 2;
+    const int s0 = wave * spw;
+    // this wave's A fragments and scales (A image: E4M3 [M, K], scales [K/128][1][1024])
+    v8i af[GV_MAXSPW];
+    int asc[GV_MAXSPW];
+#pragma unroll
+    for (int i = 0; i < GV_MAXSPW; i++) {
+      if (i < spw && s0 + i < nks) {
+        const int ks = kc0 / FK + s0 + i;
+        const uint8_t* ap = g.a8 + (int64_t)rowA * g.K + (int64_t)ks * FK + 16 * gq;
+        const uint4 lo = *(const uint4*)ap;
+        const uint4 hi = *(const uint4*)(ap + 64);
+        af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        asc[i] = g.as_p[(int64_t)ks * 1024 + f8_scale_pos(rowA, gq)];
+      }
+    }
+    // B slice: R rows x c16 chunks -> LDS rows of c16 + 1 chunks; each copy instruction fills
+    // 64 consecutive LDS chunks; a pad chunk gets a copy of its row's last chunk (never read)
+    const int total = R * (c16 + 1);
+    for (int base = wave * 64; base < total; base += 256) {
+      const int idx = min(base + lane, total - 1);
+      const int row = idx / (c16 + 1);
+      const int slot = min(idx - row * (c16 + 1), c16 - 1);
+      const int grow = min(n0 + row, g.N - 1);
+      dma16(g.b + (int64_t)grow * browg + (int64_t)kc0 * (B_FP4 ? 1 : 2) / 2 + 16 * slot,
+            __builtin_amdgcn_readfirstlane(lds_addr(smem + base * 16)));
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int i = 0; i < GV_MAXSPW; i++) {
+      if (i < spw && s0 + i < nks) {
+        const int s = s0 + i;
+        const int ks = kc0 / FK + s;
+#pragma unroll
+        for (int j = 0; j < GV_MAXG; j++) {
+          if (j < G) {
+            const int row = 16 * j + r;
+            const uint8_t* wp = smem + (row * (c16 + 1) + s * CPS) * 16;
+            v8i wf;
+            if (B_FP4) {
+              const v4i w = *(const v4i*)(wp + 16 * gq);
+              wf = __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
+            } else {
+              const v4i lo = *(const v4i*)(wp + 16 * gq);
+              const v4i hi = *(const v4i*)(wp + 64 + 16 * gq);
+              wf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            const int n = min(n0 + row, g.N - 1);
+            const int ws = g.bs_p[((int64_t)ks * ga.tiles_n + n / FT) * 1024 + f8_scale_pos(n % FT, gq)];
+            acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, af[i], acc[j], B_FP4 ? 4 : 0, 0, 0, ws, 0,
+                                                                      asc[i]);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_barrier();   // the slice is consumed before the next chunk overwrites it
+  }
+
+  // add the 4 waves' partial sums: wave w stores its G x 64 x 4 floats, then wave w sums result
+  // groups w, w + 4, ...
+  float* red = (float*)smem;
+#pragma unroll
+  for (int j = 0; j < GV_MAXG; j++)
+    if (j < G) *(v4f*)(red + ((wave * G + j) * 64 + lane) * 4) = acc[j];
+  __builtin_amdgcn_s_barrier();
+  for (int j = wave; j < G; j += 4) {
+    v4f sum = *(const v4f*)(red + (j * 64 + lane) * 4);
+#pragma unroll
+    for (int w = 1; w < 4; w++) {
+      const v4f v = *(const v4f*)(red + ((w * G + j) * 64 + lane) * 4);
+      sum = v4f{sum[0] + v[0], sum[1] + v[1], sum[2] + v[2], sum[3] + v[3]};
+    }
+    const int m = r, n = n0 + 16 * j + 4 * gq;
+    if (m >= g.M || n >= g.N) continue;
+    const float vv[4] = {sum[0], sum[1], sum[2], sum[3]};
+    const bool vec = n + 4 <= g.N && (g.ldc % 4) == 0 && (((uintptr_t)g.c) & 15) == 0;
+    if (C_BF16) {
+      uint16_t* dst = (uint16_t*)g.c + (int64_t)m * g.ldc + n;
+      if (vec) {
+        *(uint2*)dst = make_uint2((uint32_t)f32_to_bf16_rne(vv[0]) | ((uint32_t)f32_to_bf16_rne(vv[1]) << 16),
+                                  (uint32_t)f32_to_bf16_rne(vv[2]) | ((uint32_t)f32_to_bf16_rne(vv[3]) << 16));
+      } else {
+        for (int e = 0; e < 4 && n + e < g.N; e++) dst[e] = f32_to_bf16_rne(vv[e]);
+      }
+    } else {
+      float* dst = (float*)g.c + (int64_t)m * g.ldc + n;
+      if (vec) *(float4*)dst = make_float4(vv[0], vv[1], vv[2], vv[3]);
+      else for (int e = 0; e < 4 && n + e < g.N; e++) dst[e] = vv[e];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
-bool gemm_f8_eligible(int64_t M, int64_t N, int64_t K) { return K > 0 && K % FK == 0 && M >= 64 && N >= FT; }
+// Shapes mix_mx_gemm sends through the images: the tiled GEMM for M >= 64 and N >= 256, the
+// weight stream (k_gemv_f8) for M <= 16; others decode inside k_gemm_mfma.
+bool gemm_f8_eligible(int64_t M, int64_t N, int64_t K) {
+  return K > 0 && K % FK == 0 && ((M >= 64 && N >= FT) || (M >= 1 && M <= 16));
+}
 
 size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K) {
   return f8_a_image_layout(M, K).total + f8_b_image_layout(b_fp4, N, K).total;
@@ -400,6 +540,46 @@ hipError_t launch_gemm_b_image(int b_fp4, const uint8_t* b_codes, const uint8_t*
   return hipGetLastError();
 }
 
+// LDS bytes of k_gemv_f8 for G row groups and a K chunk kc: the padded slice, rounded up to whole
+// 1 KB copy runs, and at least the 4 x G KB of partial sums.
+static size_t gv_lds_bytes(int b_fp4, int G, int kc) {
+  const size_t chunks = (size_t)16 * G * ((size_t)(kc / FK) * (b_fp4 ? 4 : 8) + 1);
+  const size_t slice = (chunks + 63) / 64 * 64 * 16;
+  const size_t red = (size_t)4 * G * 1024;
+  return slice > red ? slice : red;
+}
+
+template <int B_FP4, int C_BF16>
+static hipError_t launch_gv(const GvArgs& a, size_t lds, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemv_f8<B_FP4, C_BF16>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int blocks = (a.g.N + 16 * a.G - 1) / (16 * a.G);
+  hipLaunchKernelGGL((k_gemv_f8<B_FP4, C_BF16>), dim3(blocks), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+static hipError_t launch_gemv_f8(int b_fp4, int c_bf16, const F8Args& f, hipStream_t s) {
+  // enough row groups that about one workgroup lands on each of the 256 CUs, then the largest K
+  // chunk whose slice fits in LDS
+  int G = (int)((f.N + 16 * 256 - 1) / (16 * 256));
+  G = G < 1 ? 1 : (G > GV_MAXG ? GV_MAXG : G);
+  int kc = f.K < 32 * FK ? f.K : 32 * FK;
+  while (gv_lds_bytes(b_fp4, G, kc) > 160 * 1024) {
+    if (kc > FK) kc -= FK;
+    else G--;
+  }
+  GvArgs a{};
+  a.g = f; a.G = G; a.kc = kc; a.tiles_n = (f.N + FT - 1) / FT;
+  const size_t lds = gv_lds_bytes(b_fp4, G, kc);
+  if (b_fp4) return c_bf16 ? launch_gv<1, 1>(a, lds, s) : launch_gv<1, 0>(a, lds, s);
+  return c_bf16 ? launch_gv<0, 1>(a, lds, s) : launch_gv<0, 0>(a, lds, s);
+}
+
 hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const void* b_img, const uint8_t* b_codes,
                               int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, hipStream_t s) {
   const F8AImage LA = f8_a_image_layout(M, K);
@@ -410,6 +590,7 @@ hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const vo
   a.b = b_fp4 ? b_codes : (const uint8_t*)b_img + LB.b8;
   a.bs_p = (const uint8_t*)b_img + LB.bs_p;
   a.c = c; a.ldc = ldc; a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  if (M <= 16) return launch_gemv_f8(b_fp4, c_bf16, a, s);
   if (b_fp4) return c_bf16 ? launch_f8<1, 1>(a, s) : launch_f8<1, 0>(a, s);
   return c_bf16 ? launch_f8<0, 1>(a, s) : launch_f8<0, 0>(a, s);
 }

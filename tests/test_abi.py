@@ -93,7 +93,9 @@ def test_gemm_validation(lib):
     assert lib.mix_mx_gemm_workspace_bytes(1, 1, 4096, 18944, 3584) == 4096 * 3584 + 28 * 16 * 1024 + 28 * 74 * 1024
     assert lib.mix_mx_gemm_workspace_bytes(1, 0, 256, 256, 128) == 256 * 128 + 1024 + 1024 + 256 * 128
     assert lib.mix_mx_gemm_workspace_bytes(1, 1, 256, 256, 96) == 0
-    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 16, 18944, 3584) == 0
+    # M <= 16 streams the weights through the same images
+    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 16, 18944, 3584) == 16 * 3584 + 28 * 1024 + 28 * 74 * 1024
+    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 32, 18944, 3584) == 0
     # a misaligned workspace is rejected when the fast path is taken
     assert lib.mix_mx_gemm(1, FAKE, FAKE, 1, FAKE, FAKE, 256, 256, 128, FAKE, 0, 256, MISALIGNED, 1 << 20,
                            None) == MIX_E_ALIGN

@@ -105,6 +105,28 @@ def test_gemm_images(a_fmt, b_fmt, M, N, K):
 
 
 @pytest.mark.parametrize("a_fmt,b_fmt", PAIRS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (5, 300, 3584), (16, 18, 4096), (16, 5000, 4224), (3, 700, 896),
+                                   (16, 40000, 256), (7, 4099, 1152)])
+def test_gemv_shapes(a_fmt, b_fmt, M, N, K):
+    # M <= 16: the weight-streaming kernel (row groups per workgroup, K chunks, 4-way K split);
+    # ragged N, K above one LDS chunk, and more row groups than fit one workgroup
+    q = _lib()
+    rng = np.random.default_rng(3 * M + 7 * N + K)
+    x = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-8, 8, (M, K)))).astype(np.float32)
+    w = (0.05 * rng.standard_normal((N, K)) * np.exp2(rng.integers(-3, 3, (N, K)))).astype(np.float32)
+    ac, as_, bc, bs = _code(x, w, a_fmt, b_fmt)
+    ad, bd = o_mix_deq(ac, as_, a_fmt), o_mx_deq(bc, bs, b_fmt)
+    ref, bound = gemm_ref(ad, bd), gemm_abs_bound(ad, bd)
+    for dt in (torch.float32, torch.bfloat16):
+        got = _run("mix_mx_gemm", ac, as_, bc, bs, a_fmt, b_fmt, dt)
+        what = f"gemv {a_fmt}x{b_fmt} {dt} {M}x{N}x{K}"
+        if dt == torch.float32:
+            assert_gemm_close(got, ref, bound, what)
+        else:
+            assert_bf16_matches(got, ref, bound, what)
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", PAIRS)
 @pytest.mark.parametrize("fn", ["mix_mx_gemm", "mix_mx_gemm_eq6"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (64, 256, 512), (200, 136, 352), (130, 300, 96), (16, 18, 4096)])
 def test_gemm_random_shapes(a_fmt, b_fmt, fn, M, N, K):
