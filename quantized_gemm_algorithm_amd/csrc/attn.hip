@@ -168,21 +168,59 @@ __global__ void __launch_bounds__(256) k_softmax_pquant(const float* __restrict_
   if (lane == 0) l[row] = lsum;
 }
 
-// ------------------------------------------------------------------ decode: append
+// ------------------------------------------------------------------ decode: append + q operand
 
-// grid (Hkv, B), block d threads (one channel each). Codes the new key (smoothed with the frozen
-// mean) into slot pos, stages the new value and re-codes the value block that holds it from the
-// staged tokens present (zero for the rest).
-__global__ void k_kv_append(const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-                            const float* __restrict__ mu, const int32_t* __restrict__ pos, int64_t max_pos, int Hkv,
-                            int d, int64_t Lmax, uint8_t* __restrict__ kc, uint8_t* __restrict__ ks,
-                            uint8_t* __restrict__ vc, uint8_t* __restrict__ vs, uint16_t* __restrict__ stage) {
+// grid (Hkv, B), block 128 (one thread per channel; requires d == 128 and G = Hq/Hkv <= 16).
+// 1. The MFMA operand of the G query rows of this KV head: MiX-4.5b along the head dimension,
+//    as E4M3 bytes qi8 [B*Hq, 128] with per-block E8M0 scales 2^(Emax-1) qis [B*Hq, 4].
+// 2. The new key, MXFP4 of fp32(k - mu) along the head dimension, into slot pos.
+// 3. The new value into the staging rows, and the value block that holds pos re-coded along tokens
+//    from the staged tokens present (zero for the rest).
+__global__ void __launch_bounds__(128) k_decode_prep(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
+                                                     const uint16_t* __restrict__ v_new, const float* __restrict__ mu,
+                                                     const int32_t* __restrict__ pos, int64_t max_pos, int Hq, int Hkv,
+                                                     int64_t Lmax, uint8_t* __restrict__ kc, uint8_t* __restrict__ ks,
+                                                     uint8_t* __restrict__ vc, uint8_t* __restrict__ vs,
+                                                     uint16_t* __restrict__ stage, uint8_t* __restrict__ qi8,
+                                                     uint8_t* __restrict__ qis) {
+  constexpr int d = 128;
   const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int G = Hq / Hkv;
   const int p = pos[b];
   if (p < 0 || p > max_pos) return;
   const int64_t bh = (int64_t)b * Hkv + h;
-  // ---- key: MXFP4 of fp32(k - mu) along the head dimension (32-channel blocks = half waves)
-  float kx = __fsub_rn(__uint_as_float((uint32_t)k_new[bh * d + c] << 16), mu[bh * d + c]);
+  // loads first: the key and value channel, the 32 staged values of the block, q
+  const uint32_t kraw = k_new[bh * d + c];
+  const float muc = mu[bh * d + c];
+  const int slot = p & 31;
+  const uint16_t vnew = v_new[bh * d + c];
+  uint32_t st[32];
+#pragma unroll
+  for (int s = 0; s < 32; s++) st[s] = stage[(((int64_t)b * 32 + s) * Hkv + h) * d + c];
+  // 1. q operand: thread -> (row r0 + c / 16, 8-element sub-block c % 16); quads are blocks
+  for (int r0 = 0; r0 < G; r0 += 8) {
+    const int row = r0 + (c >> 4), sb = c & 15;
+    if (row < G) {
+      const int64_t qrow = (int64_t)b * Hq + (int64_t)h * G + row;
+      const uint4 v = *(const uint4*)(q + qrow * d + sb * 8);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      uint32_t xb[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        xb[2 * i] = (w4[i] & 0xFFFFu) << 16;
+        xb[2 * i + 1] = w4[i] & 0xFFFF0000u;
+      }
+      int emax;
+      uint32_t m;
+      const uint32_t word = mix_quant_lane<1>(xb, emax, m);
+      uint32_t e0, e1;
+      mix8_to_e4m3(word, m, e0, e1);
+      *(uint2*)(qi8 + qrow * d + sb * 8) = make_uint2(e0, e1);
+      if ((sb & 3) == 0) qis[qrow * 4 + (sb >> 2)] = (uint8_t)(emax + 126);
+    }
+  }
+  // 2. key: MXFP4 of fp32(k - mu) along the head dimension (32-channel blocks = half waves)
+  float kx = __fsub_rn(__uint_as_float(kraw << 16), muc);
   uint32_t kb = f32_bits(kx);
   uint32_t amax = kb & 0x7FFFFFFFu;
 #pragma unroll
@@ -196,19 +234,15 @@ __global__ void k_kv_append(const uint16_t* __restrict__ k_new, const uint16_t* 
   const int64_t krow = bh * Lmax + p;
   if ((c & 1) == 0) kc[krow * (d >> 1) + (c >> 1)] = (uint8_t)(nib | (nxt << 4));
   if ((c & 31) == 0) ks[krow * (d >> 5) + (c >> 5)] = amax ? (uint8_t)(X + 127) : (uint8_t)0;
-  // ---- value: stage, then code the block along tokens
-  const int slot = p & 31;
-  const uint16_t vnew = v_new[bh * d + c];
+  // 3. value: stage, then code the block along tokens
   stage[(((int64_t)b * 32 + slot) * Hkv + h) * d + c] = vnew;
   uint32_t vb[32];
   uint32_t vmax = 0;
 #pragma unroll
   for (int s = 0; s < 32; s++) {
-    uint32_t u = 0;
-    if (s < slot) u = (uint32_t)stage[(((int64_t)b * 32 + s) * Hkv + h) * d + c] << 16;
-    else if (s == slot) u = (uint32_t)vnew << 16;
+    const uint32_t u = s < slot ? st[s] << 16 : (s == slot ? (uint32_t)vnew << 16 : 0u);
     vb[s] = u;
-    uint32_t a = u & 0x7FFFFFFFu;
+    const uint32_t a = u & 0x7FFFFFFFu;
     vmax = a > vmax ? a : vmax;
   }
   int XV = mx_exponent(vmax, 1);
@@ -228,8 +262,9 @@ __global__ void k_kv_append(const uint16_t* __restrict__ k_new, const uint16_t* 
 constexpr int DCH = 256;  // keys per chunk
 
 // grid (nchunk, Hkv, B), block 256 (4 waves x 64 keys). Requires d == 128 and G = Hq/Hkv <= 16.
-// S [B, Hq, Lp] fp32 for keys <= pos; pmax [B, Hq, nchunk].
-__global__ void __launch_bounds__(256) k_decode_scores(const uint8_t* __restrict__ qc, const uint16_t* __restrict__ qs,
+// S [B, Hq, Lp] fp32 for keys <= pos; pmax [B, Hq, nchunk]. Cache rows past pos are never used:
+// their loads are clamped to row pos and their products discarded.
+__global__ void __launch_bounds__(256) k_decode_scores(const uint8_t* __restrict__ qi8, const uint8_t* __restrict__ qis,
                                                         const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks,
                                                         const int32_t* __restrict__ pos, int64_t max_pos, int Hq,
                                                         int Hkv, int64_t Lmax, int64_t Lp, int nchunk,
@@ -241,48 +276,41 @@ __global__ void __launch_bounds__(256) k_decode_scores(const uint8_t* __restrict
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   __shared__ float smax[4][16];
-
-  // A operand: the G query rows of this KV head as E4M3, per-block scales 2^(Emax-1)
-  v8i af = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  int sa = 127;
-  if (r < G) {
-    const int64_t qrow = (int64_t)b * Hq + (int64_t)h * G + r;
-    const uint8_t* qrc = qc + qrow * 64;
-    const uint16_t* qrs = qs + qrow * 4;
-    // bytes for K elements [16 g, 16 g + 16): block g/2, sub-blocks 2 (g&1), 2 (g&1) + 1
-    uint32_t o[8];
-#pragma unroll
-    for (int half = 0; half < 2; half++) {
-      int blk = (g >> 1) + 2 * half;
-      uint32_t sh = qrs[blk];
-      uint2 wv = *(const uint2*)(qrc + blk * 16 + (g & 1) * 8);
-      mix8_to_e4m3(wv.x, (sh >> (4 + 3 * (2 * (g & 1)))) & 7u, o[4 * half + 0], o[4 * half + 1]);
-      mix8_to_e4m3(wv.y, (sh >> (4 + 3 * (2 * (g & 1) + 1))) & 7u, o[4 * half + 2], o[4 * half + 3]);
-    }
-    af = v8i{(int)o[0], (int)o[1], (int)o[2], (int)o[3], (int)o[4], (int)o[5], (int)o[6], (int)o[7]};
-    sa = (int)(qrs[g] & 15u) + 119;
-  }
-  float rmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   const int64_t bh = (int64_t)b * Hkv + h;
+
+  // K fragments of the wave's 4 groups of 16 keys (issued first)
+  uint4 kv[4];
+  int ksc[4];
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const int j = min(chunk * DCH + wave * 64 + t * 16 + r, p);
+    kv[t] = *(const uint4*)(kc + (bh * Lmax + j) * 64 + g * 16);
+    ksc[t] = ks[(bh * Lmax + j) * 4 + g];
+  }
+  // A operand: the G query rows of this KV head (E4M3 split: bytes [16 g, +16) and [64 + 16 g, +16))
+  const int rq = min(r, G - 1);
+  const int64_t qrow = (int64_t)b * Hq + (int64_t)h * G + rq;
+  const uint4 qlo = *(const uint4*)(qi8 + qrow * 128 + 16 * g);
+  const uint4 qhi = *(const uint4*)(qi8 + qrow * 128 + 64 + 16 * g);
+  const v8i af = v8i{(int)qlo.x, (int)qlo.y, (int)qlo.z, (int)qlo.w, (int)qhi.x, (int)qhi.y, (int)qhi.z, (int)qhi.w};
+  const int sa = qis[qrow * 4 + g];
+
+  float rmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int t = 0; t < 4; t++) {
     const int j0 = chunk * DCH + wave * 64 + t * 16;
-    if (j0 > p) break;
     const int j = j0 + r;
-    v8i bf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    int sb = 127;
-    if (j <= p) {
-      uint4 v = *(const uint4*)(kc + (bh * Lmax + j) * 64 + g * 16);
-      bf = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      sb = ks[(bh * Lmax + j) * 4 + g];
-    }
+    const bool live = j <= p;
+    const v8i bf = live ? v8i{(int)kv[t].x, (int)kv[t].y, (int)kv[t].z, (int)kv[t].w, 0, 0, 0, 0}
+                        : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    const int sb = live ? ksc[t] : 127;
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc, 0, 4, 0, sa, 0, sb);
     // result register i: query row 4 g + i, key j0 + r
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       int qr = 4 * g + i;
-      if (qr < G && j <= p) {
+      if (qr < G && live) {
         S[((int64_t)b * Hq + (int64_t)h * G + qr) * Lp + j] = acc[i];
         rmax[i] = fmaxf(rmax[i], acc[i]);
       }
@@ -321,19 +349,38 @@ __global__ void __launch_bounds__(256) k_decode_pv(const float* __restrict__ S, 
   if (p < 0 || p > max_pos || chunk * DCH > p) return;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t bh = (int64_t)b * Hkv + h;
   __shared__ float sm[16];
   __shared__ uint8_t sP[16][DCH];  // P^ as E4M3, row-major; rows >= G stay zero
   __shared__ uint8_t sPs[16][DCH / 32];
 
-  // global row max over the chunks that hold keys <= pos
-  const int last = p / DCH;
-  if (tid < 16) {
-    float v = -INFINITY;
-    if (tid < G) {
-      const float* pm = pmax + ((int64_t)b * Hq + (int64_t)h * G + tid) * nchunk;
-      for (int c = 0; c <= last; c++) v = fmaxf(v, pm[c]);
+  // V fragments of this chunk (issued first): wave w handles channel tiles 2w, 2w+1 (16 channels
+  // each); blocks past the newest token are clamped to its block and their products discarded
+  uint4 vv[DCH / 128][2];
+  int vsc[DCH / 128][2];
+#pragma unroll
+  for (int k2 = 0; k2 < DCH / 128; k2++) {
+    const int kb = min(chunk * DCH + k2 * 128 + 32 * g, p) >> 5;
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const int ch = (2 * wave + t) * 16 + r;
+      vv[k2][t] = *(const uint4*)(vc + (bh * 128 + ch) * (Lmax >> 1) + kb * 16);
+      vsc[k2][t] = vs[(bh * 128 + ch) * (Lmax >> 5) + kb];
     }
-    sm[tid] = __fmul_rn(v, scale);
+  }
+  // global row max over the chunks that hold keys <= pos: 16 threads per row
+  const int last = p / DCH;
+  {
+    const int row = tid >> 4, part = tid & 15;
+    float v = -INFINITY;
+    if (row < G) {
+      const float* pm = pmax + ((int64_t)b * Hq + (int64_t)h * G + row) * nchunk;
+      for (int c = part; c <= last; c += 16) v = fmaxf(v, pm[c]);
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    if (part == 0) sm[row] = __fmul_rn(v, scale);
   }
   for (int i = tid; i < 16 * DCH / 4; i += 256) ((uint32_t*)sP)[i] = 0u;
   for (int i = tid; i < 16 * DCH / 32; i += 256) ((uint8_t*)sPs)[i] = 127;
@@ -345,14 +392,17 @@ __global__ void __launch_bounds__(256) k_decode_pv(const float* __restrict__ S, 
     if (row < G) {  // 32 threads per row: whole quads
       const int64_t qrow = (int64_t)b * Hq + (int64_t)h * G + row;
       const int jb = chunk * DCH + sb * 8;
+      const float4 s0 = *(const float4*)(S + qrow * Lp + jb);
+      const float4 s1 = *(const float4*)(S + qrow * Lp + jb + 4);
+      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
       const float m = sm[row];
       float pv[8];
       float lsum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        int j = jb + e;
+        const int j = jb + e;
         float v = 0.f;
-        if (j <= p) v = expf(__fsub_rn(__fmul_rn(S[qrow * Lp + j], scale), m));
+        if (j <= p) v = expf(__fsub_rn(__fmul_rn(sv[e], scale), m));
         pv[e] = v;
         lsum += v;
       }
@@ -379,29 +429,22 @@ __global__ void __launch_bounds__(256) k_decode_pv(const float* __restrict__ S, 
   }
   __syncthreads();
 
-  // O partial = P^ V^ over this chunk: wave w handles channel tiles 2w, 2w+1 (16 channels each)
-  const int r = lane & 15, g = lane >> 4;
-  const int64_t bh = (int64_t)b * Hkv + h;
+  // O partial = P^ V^ over this chunk
   v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int ks = 0; ks < DCH / 128; ks++) {
-    const int kbase = chunk * DCH + ks * 128;  // first key of this K step
+  for (int k2 = 0; k2 < DCH / 128; k2++) {
+    const int kbase = chunk * DCH + k2 * 128;  // first key of this K step
     if (kbase > p) break;
-    uint4 lo = *(const uint4*)(&sP[r][ks * 128 + 16 * g]);
-    uint4 hi = *(const uint4*)(&sP[r][ks * 128 + 64 + 16 * g]);
+    uint4 lo = *(const uint4*)(&sP[r][k2 * 128 + 16 * g]);
+    uint4 hi = *(const uint4*)(&sP[r][k2 * 128 + 64 + 16 * g]);
     v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    int sa = sPs[r][ks * 4 + g];
-    const bool blk_live = kbase + 32 * g <= p;  // V blocks past the newest token are not read
+    int sa = sPs[r][k2 * 4 + g];
+    const bool blk_live = kbase + 32 * g <= p;
 #pragma unroll
     for (int t = 0; t < 2; t++) {
-      const int ch = (2 * wave + t) * 16 + r;
-      v8i bf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      int sb = 127;
-      if (blk_live) {
-        uint4 v = *(const uint4*)(vc + (bh * 128 + ch) * (Lmax >> 1) + ((kbase + 32 * g) >> 1));
-        bf = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        sb = vs[(bh * 128 + ch) * (Lmax >> 5) + ((kbase + 32 * g) >> 5)];
-      }
+      const v8i bf = blk_live ? v8i{(int)vv[k2][t].x, (int)vv[k2][t].y, (int)vv[k2][t].z, (int)vv[k2][t].w, 0, 0, 0, 0}
+                              : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      const int sb = blk_live ? vsc[k2][t] : 127;
       acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc[t], 0, 4, 0, sa, 0, sb);
     }
   }
@@ -416,7 +459,8 @@ __global__ void __launch_bounds__(256) k_decode_pv(const float* __restrict__ S, 
   }
 }
 
-// grid (B * Hq), block d: O = sum_chunks O_part / sum_chunks l_part, rounded to bf16.
+// grid (B * Hq), block d: O = sum_chunks O_part / sum_chunks l_part, rounded to bf16. Four
+// independent partial sums keep the chunk loads in flight together.
 __global__ void k_decode_combine(const float* __restrict__ lpart, const float* __restrict__ opart,
                                  const int32_t* __restrict__ pos, int64_t max_pos, int Hq, int nchunk, int d,
                                  uint16_t* __restrict__ o, float* __restrict__ dbg_l) {
@@ -427,12 +471,22 @@ __global__ void k_decode_combine(const float* __restrict__ lpart, const float* _
     o[qrow * d + c] = 0;
     return;
   }
-  const int last = p / DCH;
-  float l = 0.f, acc = 0.f;
-  for (int k = 0; k <= last; k++) {
-    l += lpart[qrow * nchunk + k];
-    acc += opart[(qrow * nchunk + k) * d + c];
+  const int n = p / DCH + 1;
+  float l4[4] = {0.f, 0.f, 0.f, 0.f}, a4[4] = {0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 4 <= n; k += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      l4[u] += lpart[qrow * nchunk + k + u];
+      a4[u] += opart[(qrow * nchunk + k + u) * d + c];
+    }
   }
+  for (; k < n; k++) {
+    l4[0] += lpart[qrow * nchunk + k];
+    a4[0] += opart[(qrow * nchunk + k) * d + c];
+  }
+  const float l = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+  const float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
   o[qrow * d + c] = f32_to_bf16_rne(__fdiv_rn(acc, l));
   if (dbg_l && c == 0) dbg_l[qrow] = l;
 }
@@ -555,7 +609,7 @@ hipError_t kv_cache_prefill_run(const mix_kv_cache_t* c, int64_t b, const void* 
 }
 
 struct DecodeWs {
-  size_t qc, qs, s, pmax, pc, ps, lpart, opart, total;
+  size_t qi8, qis, s, pmax, pc, ps, lpart, opart, total;
 };
 
 static DecodeWs decode_layout(int64_t B, int64_t Hq, int64_t d, int64_t max_pos, int64_t* Lp_out, int* nchunk_out) {
@@ -564,8 +618,8 @@ static DecodeWs decode_layout(int64_t B, int64_t Hq, int64_t d, int64_t max_pos,
   DecodeWs w{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  w.qc = take((size_t)B * Hq * d / 2);
-  w.qs = take((size_t)B * Hq * (d / 32) * 2);
+  w.qi8 = take((size_t)B * Hq * d);
+  w.qis = take((size_t)B * Hq * (d / 32));
   w.s = take((size_t)B * Hq * Lp * 4);
   w.pmax = take((size_t)B * Hq * nchunk * 4);
   w.pc = take((size_t)B * Hq * Lp / 2);
@@ -590,8 +644,8 @@ hipError_t attn_decode_run(const void* q, const void* k_new, const void* v_new, 
   int nchunk;
   DecodeWs w = decode_layout(B, Hq, d, max_pos, &Lp, &nchunk);
   uint8_t* base = (uint8_t*)ws;
-  uint8_t* qc = base + w.qc;
-  uint16_t* qs = (uint16_t*)(base + w.qs);
+  uint8_t* qi8 = base + w.qi8;
+  uint8_t* qis = base + w.qis;
   float* S = (float*)(base + w.s);
   float* pmax = (float*)(base + w.pmax);
   uint8_t* pc = base + w.pc;
@@ -599,13 +653,12 @@ hipError_t attn_decode_run(const void* q, const void* k_new, const void* v_new, 
   float* lpart = (float*)(base + w.lpart);
   float* opart = (float*)(base + w.opart);
 
-  hipLaunchKernelGGL(k_kv_append, dim3((unsigned)Hkv, (unsigned)B), dim3((unsigned)d), 0, s, (const uint16_t*)k_new,
-                     (const uint16_t*)v_new, mu, pos, max_pos, (int)Hkv, (int)d, Lmax, c->k_codes, c->k_scales,
-                     c->v_codes, c->v_scales, (uint16_t*)c->v_stage);
+  hipLaunchKernelGGL(k_decode_prep, dim3((unsigned)Hkv, (unsigned)B), dim3(128), 0, s, (const uint16_t*)q,
+                     (const uint16_t*)k_new, (const uint16_t*)v_new, mu, pos, max_pos, (int)Hq, (int)Hkv, Lmax,
+                     c->k_codes, c->k_scales, c->v_codes, c->v_scales, (uint16_t*)c->v_stage, qi8, qis);
   HIPCHK(hipGetLastError());
-  HIPCHK(launch_mix_quantize(1, q, 1, B * Hq, d, d, qc, qs, s));
   dim3 grid((unsigned)nchunk, (unsigned)Hkv, (unsigned)B);
-  hipLaunchKernelGGL(k_decode_scores, grid, dim3(256), 0, s, qc, qs, c->k_codes, c->k_scales, pos, max_pos, (int)Hq,
+  hipLaunchKernelGGL(k_decode_scores, grid, dim3(256), 0, s, qi8, qis, c->k_codes, c->k_scales, pos, max_pos, (int)Hq,
                      (int)Hkv, Lmax, Lp, nchunk, S, pmax);
   HIPCHK(hipGetLastError());
   const float scale = (float)(1.0 / sqrt((double)d));

@@ -350,49 +350,63 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // [64 + 16 g, 64 + 16 g + 16)), the 16 activation rows as its B operand (E4M3, same split), and
 // the scale of lane l = the E8M0 scale of its row for K block g. Result register i of lane l is
 // C^T[4 (l >> 4) + i][l & 15]: four consecutive n for one m.
-constexpr int GV_MAXG = 8;
 constexpr int GV_MAXSPW = 8;   // K steps per wave per chunk (chunk <= 32 steps = 4096)
 
 struct GvArgs {
   F8Args g;
-  int G;        // 16-row weight groups per workgroup
   int kc;       // K chunk (multiple of 128, <= 4096)
   int tiles_n;  // 256-row tiles of the B image's scale layout
 };
 
-template <int B_FP4, int C_BF16>
+template <int B_FP4, int C_BF16, int G>
 __global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
   extern __shared__ __align__(16) uint8_t smem[];
   const F8Args& g = ga.g;
-  const int G = ga.G;
+  constexpr int R = 16 * G;
+  constexpr int CPS = B_FP4 ? 4 : 8;                // 16-byte chunks of a B row per 128-wide K step
+  constexpr int GW = (G + 3) / 4;                   // scale words per step (4 row groups each)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, gq = lane >> 4;
-  const int R = 16 * G;
   const int n0 = blockIdx.x * R;
   const int rowA = min(r, g.M - 1);
   const int64_t browg = B_FP4 ? (g.K >> 1) : g.K;   // bytes per B row in global memory
-  constexpr int CPS = B_FP4 ? 4 : 8;                // 16-byte chunks of a B row per 128-wide K step
-  v4f acc[GV_MAXG];
+  const int nkt = g.K / FK;
+  v4f acc[G];
 #pragma unroll
-  for (int j = 0; j < GV_MAXG; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < G; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   for (int kc0 = 0; kc0 < g.K; kc0 += ga.kc) {
     const int nks = min(ga.kc, g.K - kc0) / FK;      // K steps in this chunk
     const int c16 = nks * CPS;                       // chunks per row in LDS (+1 pad)
     const int spw = (nks + 3) >> 2;
     const int s0 = wave * spw;
-    // this wave's A fragments and scales (A image: E4M3 [M, K], scales [K/128][1][1024])
+    // Operand loads that do not wait on the copies: A fragments and scales (A image: E4M3
+    // [M, K], scales [K/128][1][1024]) and the weight rows' scale bytes, four row groups per
+    // register (the MFMA's scale op_sel picks the byte). Indices are clamped so every load is
+    // issued unconditionally; steps past this wave's share are loaded but not used.
     v8i af[GV_MAXSPW];
     int asc[GV_MAXSPW];
+    uint32_t wsc[GV_MAXSPW][GW];
 #pragma unroll
     for (int i = 0; i < GV_MAXSPW; i++) {
-      if (i < spw && s0 + i < nks) {
-        const int ks = kc0 / FK + s0 + i;
-        const uint8_t* ap = g.a8 + (int64_t)rowA * g.K + (int64_t)ks * FK + 16 * gq;
-        const uint4 lo = *(const uint4*)ap;
-        const uint4 hi = *(const uint4*)(ap + 64);
-        af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        asc[i] = g.as_p[(int64_t)ks * 1024 + f8_scale_pos(rowA, gq)];
+      const int ks = min(kc0 / FK + s0 + i, nkt - 1);
+      const uint8_t* ap = g.a8 + (int64_t)rowA * g.K + (int64_t)ks * FK + 16 * gq;
+      const uint4 lo = *(const uint4*)ap;
+      const uint4 hi = *(const uint4*)(ap + 64);
+      af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      asc[i] = g.as_p[(int64_t)ks * 1024 + f8_scale_pos(rowA, gq)];
+      uint32_t b[G];
+#pragma unroll
+      for (int j = 0; j < G; j++) {
+        const int n = min(n0 + 16 * j + r, g.N - 1);
+        b[j] = g.bs_p[((int64_t)ks * ga.tiles_n + n / FT) * 1024 + f8_scale_pos(n % FT, gq)];
+      }
+#pragma unroll
+      for (int w = 0; w < GW; w++) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int j = 4 * w; j < G && j < 4 * w + 4; j++) v |= b[j] << (8 * (j & 3));
+        wsc[i][w] = v;
       }
     }
     // B slice: R rows x c16 chunks -> LDS rows of c16 + 1 chunks; each copy instruction fills
@@ -412,26 +426,30 @@ __global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
     for (int i = 0; i < GV_MAXSPW; i++) {
       if (i < spw && s0 + i < nks) {
         const int s = s0 + i;
-        const int ks = kc0 / FK + s;
+        v8i wf[G];
 #pragma unroll
-        for (int j = 0; j < GV_MAXG; j++) {
-          if (j < G) {
-            const int row = 16 * j + r;
-            const uint8_t* wp = smem + (row * (c16 + 1) + s * CPS) * 16;
-            v8i wf;
-            if (B_FP4) {
-              const v4i w = *(const v4i*)(wp + 16 * gq);
-              wf = __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
-            } else {
-              const v4i lo = *(const v4i*)(wp + 16 * gq);
-              const v4i hi = *(const v4i*)(wp + 64 + 16 * gq);
-              wf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-            const int n = min(n0 + row, g.N - 1);
-            const int ws = g.bs_p[((int64_t)ks * ga.tiles_n + n / FT) * 1024 + f8_scale_pos(n % FT, gq)];
-            acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, af[i], acc[j], B_FP4 ? 4 : 0, 0, 0, ws, 0,
-                                                                      asc[i]);
+        for (int j = 0; j < G; j++) {
+          const uint8_t* wp = smem + ((16 * j + r) * (c16 + 1) + s * CPS) * 16;
+          if (B_FP4) {
+            const v4i w = *(const v4i*)(wp + 16 * gq);
+            wf[j] = __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
+          } else {
+            const v4i lo = *(const v4i*)(wp + 16 * gq);
+            const v4i hi = *(const v4i*)(wp + 64 + 16 * gq);
+            wf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           }
+        }
+#pragma unroll
+        for (int j = 0; j < G; j++) {
+          const int ws = (int)wsc[i][j >> 2];
+#define GV_MFMA(SEL)                                                                                          \
+  acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], af[i], acc[j], B_FP4 ? 4 : 0, 0, SEL, ws, 0, \
+                                                            asc[i])
+          if ((j & 3) == 0) GV_MFMA(0);
+          if ((j & 3) == 1) GV_MFMA(1);
+          if ((j & 3) == 2) GV_MFMA(2);
+          if ((j & 3) == 3) GV_MFMA(3);
+#undef GV_MFMA
         }
       }
     }
@@ -442,8 +460,7 @@ __global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
   // groups w, w + 4, ...
   float* red = (float*)smem;
 #pragma unroll
-  for (int j = 0; j < GV_MAXG; j++)
-    if (j < G) *(v4f*)(red + ((wave * G + j) * 64 + lane) * 4) = acc[j];
+  for (int j = 0; j < G; j++) *(v4f*)(red + ((wave * G + j) * 64 + lane) * 4) = acc[j];
   __builtin_amdgcn_s_barrier();
   for (int j = wave; j < G; j += 4) {
     v4f sum = *(const v4f*)(red + (j * 64 + lane) * 4);
@@ -549,35 +566,39 @@ static size_t gv_lds_bytes(int b_fp4, int G, int kc) {
   return slice > red ? slice : red;
 }
 
-template <int B_FP4, int C_BF16>
-static hipError_t launch_gv(const GvArgs& a, size_t lds, hipStream_t s) {
+template <int B_FP4, int C_BF16, int G>
+static hipError_t launch_gv(const F8Args& f, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemv_f8<B_FP4, C_BF16>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemv_f8<B_FP4, C_BF16, G>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int blocks = (a.g.N + 16 * a.G - 1) / (16 * a.G);
-  hipLaunchKernelGGL((k_gemv_f8<B_FP4, C_BF16>), dim3(blocks), dim3(256), lds, s, a);
+  // the largest K chunk whose slice fits in LDS
+  int kc = f.K < 32 * FK ? f.K : 32 * FK;
+  while (kc > FK && gv_lds_bytes(B_FP4, G, kc) > 160 * 1024) kc -= FK;
+  GvArgs a{};
+  a.g = f; a.kc = kc; a.tiles_n = (f.N + FT - 1) / FT;
+  const int blocks = (f.N + 16 * G - 1) / (16 * G);
+  hipLaunchKernelGGL((k_gemv_f8<B_FP4, C_BF16, G>), dim3(blocks), dim3(256), gv_lds_bytes(B_FP4, G, kc), s, a);
   return hipGetLastError();
 }
 
+template <int B_FP4, int C_BF16>
+static hipError_t launch_gv_g(const F8Args& f, hipStream_t s) {
+  // enough 16-row groups per workgroup that about one workgroup lands on each of the 256 CUs
+  const int need = (int)((f.N + 16 * 256 - 1) / (16 * 256));
+  if (need <= 1) return launch_gv<B_FP4, C_BF16, 1>(f, s);
+  if (need <= 2) return launch_gv<B_FP4, C_BF16, 2>(f, s);
+  if (need <= 4) return launch_gv<B_FP4, C_BF16, 4>(f, s);
+  if (need <= 5) return launch_gv<B_FP4, C_BF16, 5>(f, s);
+  return launch_gv<B_FP4, C_BF16, 8>(f, s);
+}
+
 static hipError_t launch_gemv_f8(int b_fp4, int c_bf16, const F8Args& f, hipStream_t s) {
-  // enough row groups that about one workgroup lands on each of the 256 CUs, then the largest K
-  // chunk whose slice fits in LDS
-  int G = (int)((f.N + 16 * 256 - 1) / (16 * 256));
-  G = G < 1 ? 1 : (G > GV_MAXG ? GV_MAXG : G);
-  int kc = f.K < 32 * FK ? f.K : 32 * FK;
-  while (gv_lds_bytes(b_fp4, G, kc) > 160 * 1024) {
-    if (kc > FK) kc -= FK;
-    else G--;
-  }
-  GvArgs a{};
-  a.g = f; a.G = G; a.kc = kc; a.tiles_n = (f.N + FT - 1) / FT;
-  const size_t lds = gv_lds_bytes(b_fp4, G, kc);
-  if (b_fp4) return c_bf16 ? launch_gv<1, 1>(a, lds, s) : launch_gv<1, 0>(a, lds, s);
-  return c_bf16 ? launch_gv<0, 1>(a, lds, s) : launch_gv<0, 0>(a, lds, s);
+  if (b_fp4) return c_bf16 ? launch_gv_g<1, 1>(f, s) : launch_gv_g<1, 0>(f, s);
+  return c_bf16 ? launch_gv_g<0, 1>(f, s) : launch_gv_g<0, 0>(f, s);
 }
 
 hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const void* b_img, const uint8_t* b_codes,

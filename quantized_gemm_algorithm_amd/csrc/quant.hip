@@ -62,24 +62,9 @@ __global__ void __launch_bounds__(256) k_mix_quantize(const void* __restrict__ x
     int64_t sc = g - row * sub_per_row;  // sub-block index in the row
     uint32_t xb[8];
     load8<DT>(x, row, ldx, sc * 8, xb);
-    uint32_t lmax = 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      uint32_t a = xb[i] & 0x7FFFFFFFu;
-      lmax = a > lmax ? a : lmax;
-    }
-    uint32_t bmax = quad_max_u32(lmax);
     int emax;
-    if (bmax == 0) emax = -7;
-    else {
-      int e = (int)(bmax >> 23) - 127;
-      emax = e < -7 ? -7 : (e > 8 ? 8 : e);
-    }
-    uint32_t m = mant3_of(FMT == 1 ? lmax : bmax);
-    MixThresholds t = mix_thresholds(emax, m);
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) word |= mix_code(xb[i], t) << (4 * i);
+    uint32_t m;
+    const uint32_t word = mix_quant_lane<FMT>(xb, emax, m);
     int q = (int)(sc & 3);
     int64_t blk = sc >> 2;
     if (!IMG || codes) {

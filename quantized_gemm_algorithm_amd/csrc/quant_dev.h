@@ -47,6 +47,33 @@ __device__ __forceinline__ uint32_t mix_code(uint32_t xbits, const MixThresholds
   return code;
 }
 
+// One lane's share of a MiX block: the lane holds 8 consecutive elements (fp32 bit patterns) and
+// the 4 sub-blocks of a 32-element block sit in the 4 lanes of a quad (sub-block = lane & 3).
+// Returns the 8 nibbles (element e at bits 4e) and sets the block's Emax (clamped to [-7, 8]) and
+// this lane's 3-bit shared mantissa m (its sub-block's for MiX-4.5b, the block's for MiX-4.25b).
+template <int FMT>  // 0 = MiX-4.25b, 1 = MiX-4.5b
+__device__ __forceinline__ uint32_t mix_quant_lane(const uint32_t (&xb)[8], int& emax, uint32_t& m) {
+  uint32_t lmax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint32_t a = xb[i] & 0x7FFFFFFFu;
+    lmax = a > lmax ? a : lmax;
+  }
+  const uint32_t bmax = quad_max_u32(lmax);
+  if (bmax == 0) {
+    emax = -7;
+  } else {
+    const int e = (int)(bmax >> 23) - 127;
+    emax = e < -7 ? -7 : (e > 8 ? 8 : e);
+  }
+  m = mant3_of(FMT == 1 ? lmax : bmax);
+  const MixThresholds t = mix_thresholds(emax, m);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) word |= mix_code(xb[i], t) << (4 * i);
+  return word;
+}
+
 // MXFP4 code of one element, thresholds at the E2M1 midpoints times 2^X, ties to the even code.
 struct Fp4Thr { uint32_t t[7]; };
 __device__ __forceinline__ Fp4Thr fp4_thresholds(int X) {
