@@ -64,6 +64,27 @@ class KernelTimer:
         return a.elapsed_time(b)
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch of the workload's dominant kernel, from the FETCH_SIZE / WRITE_SIZE counter runs
+    recorded in profiles/traffic.json (scaled by a plain copy's counts); None if none was recorded or the
+    kernel's sources changed since."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        rec = json.load(open(os.path.join(root, "profiles", "traffic.json"))).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in rec["source_files"]:
+        try:
+            h.update(open(os.path.join(root, f), "rb").read())
+        except OSError:
+            return None
+    return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
+
+
 def rotating(n_bytes_each, min_total=320 << 20):
     """How many copies of a buffer are needed to exceed the 256 MB last-level cache."""
     return max(1, math.ceil(min_total / max(1, n_bytes_each)))
@@ -192,7 +213,7 @@ def bench_linear(torch, q, args, which):
         "config": {"workload": wl, "M": M, "K": K, "N": N, "a_format": "MiX-" + a_fmt,
                    "b_format": "MX" + b_fmt.upper(), "out": "bf16"},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gemm_tflops / FP8_MFMA_PEAK_TFLOPS, "traffic": None, "kernel": "k_gemm_f8",
+                     "frac": gemm_tflops / FP8_MFMA_PEAK_TFLOPS, "traffic": measured_traffic(which), "kernel": "k_gemm_f8",
                      "kernel_ms": g_ms, "algorithmic_flops": flops, "operand_bytes": gemm_bytes},
         "quantizer": {"kernel": "k_mix_quantize (codes + A image)", "ms": q_ms,
                       "GB/s": q_bytes / (q_ms * 1e-3) / 1e9,
