@@ -204,15 +204,9 @@ __global__ void __launch_bounds__(128) k_decode_prep(const uint16_t* __restrict_
       const int64_t qrow = (int64_t)b * Hq + (int64_t)h * G + row;
       const uint4 v = *(const uint4*)(q + qrow * d + sb * 8);
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-      uint32_t xb[8];
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        xb[2 * i] = (w4[i] & 0xFFFFu) << 16;
-        xb[2 * i + 1] = w4[i] & 0xFFFF0000u;
-      }
       int emax;
       uint32_t m;
-      const uint32_t word = mix_quant_lane<1>(xb, emax, m);
+      const uint32_t word = mix_quant_lane_bf16<1>(w4, emax, m);
       uint32_t e0, e1;
       mix8_to_e4m3(word, m, e0, e1);
       *(uint2*)(qi8 + qrow * d + sb * 8) = make_uint2(e0, e1);

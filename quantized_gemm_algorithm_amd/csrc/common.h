@@ -55,6 +55,29 @@ __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
   return v > t ? v : t;
 }
 
+// Division of a flat index n < 2^31 by a fixed d < 2^31 as a multiply and a shift:
+// q = (n * m) >> sh with sh = 31 + ceil(log2 d), m = ceil(2^sh / d) < 2^33. The error term is below
+// n / 2^sh < 2^-ceil(log2 d) <= 1/d, less than the distance from n/d to the next integer, so q is
+// floor(n / d) exactly. For larger indices (ok == 0) the plain 64-bit division is used.
+struct FastDiv {
+  uint64_t m;
+  int sh;
+  int ok;
+};
+inline FastDiv make_fastdiv(int64_t d, int64_t n_max) {
+  FastDiv f{0, 0, 0};
+  if (d <= 0 || d >= (int64_t(1) << 31) || n_max >= (int64_t(1) << 31)) return f;
+  int l = 0;
+  while ((int64_t(1) << l) < d) l++;
+  f.sh = 31 + l;
+  f.m = (((uint64_t)1 << f.sh) + (uint64_t)d - 1) / (uint64_t)d;
+  f.ok = 1;
+  return f;
+}
+__device__ __forceinline__ int64_t fast_div(int64_t n, int64_t d, const FastDiv& f) {
+  return f.ok ? (int64_t)(((uint64_t)(uint32_t)n * f.m) >> f.sh) : n / d;
+}
+
 // bitwise OR over the 4 lanes of a quad
 __device__ __forceinline__ uint32_t quad_or_u32(uint32_t v) {
   v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);

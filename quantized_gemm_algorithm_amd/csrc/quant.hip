@@ -46,44 +46,73 @@ __device__ __forceinline__ void load8(const void* base, int64_t row, int64_t ld,
 
 // With IMG the lane also writes the GEMM A image of its sub-block (f8_image.h): 8 E4M3 bytes, and
 // on quad lane 0 the block's E8M0 scale 2^(Emax-1). codes/shared may then be NULL (not written).
+//
+// Work layout: grid (column chunks, row pairs); a workgroup codes MQ_R rows of one chunk of
+// blockDim.x sub-blocks (the launcher sizes blocks to the row when it has at most 1024
+// sub-blocks), so every row-dependent offset is a wave-uniform scalar and a lane only adds its
+// sub-block's offset. The MQ_R rows' loads are issued together.
+constexpr int MQ_R = 2;
+
 template <int DT, int FMT, int IMG>  // FMT 0 = MiX-4.25b, 1 = MiX-4.5b
-__global__ void __launch_bounds__(256) k_mix_quantize(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
-                                                       uint8_t* __restrict__ codes, void* __restrict__ shared,
-                                                       uint8_t* __restrict__ a8, uint8_t* __restrict__ as_p,
-                                                       int tiles_m) {
-  const int64_t sub_per_row = cols >> 3;
-  const int64_t total = rows * sub_per_row;  // multiple of 4
-  const int lane = threadIdx.x & 63;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g - lane < total;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    // whole quads are active or inactive together (total is a multiple of 4)
-    if (g >= total) continue;
-    int64_t row = g / sub_per_row;
-    int64_t sc = g - row * sub_per_row;  // sub-block index in the row
-    uint32_t xb[8];
-    load8<DT>(x, row, ldx, sc * 8, xb);
-    int emax;
-    uint32_t m;
-    const uint32_t word = mix_quant_lane<FMT>(xb, emax, m);
-    int q = (int)(sc & 3);
-    int64_t blk = sc >> 2;
-    if (!IMG || codes) {
-      *(uint32_t*)(codes + row * (cols >> 1) + sc * 4) = word;
-      if (FMT == 1) {
-        uint32_t f = (q == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * q));
-        f = quad_or_u32(f);
-        if (q == 0) ((uint16_t*)shared)[row * (cols >> 5) + blk] = (uint16_t)f;
+__global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                                                        uint8_t* __restrict__ codes, void* __restrict__ shared,
+                                                        uint8_t* __restrict__ a8, uint8_t* __restrict__ as_p,
+                                                        int tiles_m) {
+  const int spr = (int)(cols >> 3);                       // sub-blocks per row
+  const int sc = blockIdx.x * blockDim.x + threadIdx.x;   // this lane's sub-block in the row
+  // whole quads are in or out of range together (spr and the chunk size are multiples of 4)
+  const bool col_ok = sc < spr;
+  const int scc = col_ok ? sc : (sc & 3);
+  const int q = scc & 3;
+  const int blk = scc >> 2;
+  // the lane's part of the permuted scale position: [K step][tile][half][gq][r][h][i]
+  const int h = (blk & 3) >> 1, gq = blk & 1;
+  for (int64_t r0 = (int64_t)blockIdx.y * MQ_R; r0 < rows; r0 += (int64_t)gridDim.y * MQ_R) {
+    uint32_t xb[MQ_R][8];  // bf16: the 16 raw bytes in xb[u][0..3]; fp32: the 8 bit patterns
+#pragma unroll
+    for (int u = 0; u < MQ_R; u++) {
+      const int64_t row = r0 + u < rows ? r0 + u : rows - 1;
+      if (DT == 1) {
+        const uint4 v = *(const uint4*)((const uint16_t*)x + row * ldx + (int64_t)scc * 8);
+        xb[u][0] = v.x; xb[u][1] = v.y; xb[u][2] = v.z; xb[u][3] = v.w;
       } else {
-        if (q == 0) ((uint8_t*)shared)[row * (cols >> 5) + blk] = (uint8_t)((uint32_t)(emax + 7) | (m << 4));
+        load8<DT>(x, row, ldx, (int64_t)scc * 8, xb[u]);
       }
     }
-    if (IMG) {
-      uint32_t e0, e1;
-      mix8_to_e4m3(word, m, e0, e1);
-      *(uint2*)(a8 + row * cols + sc * 8) = make_uint2(e0, e1);
-      if (q == 0)
-        as_p[((blk >> 2) * tiles_m + row / FT) * 1024 + f8_scale_pos((int)(row % FT), (int)(blk & 3))] =
-            (uint8_t)(emax + 126);
+#pragma unroll
+    for (int u = 0; u < MQ_R; u++) {
+      const int64_t row = r0 + u;
+      int emax;
+      uint32_t m;
+      uint32_t word;
+      if (DT == 1) {
+        const uint32_t w4[4] = {xb[u][0], xb[u][1], xb[u][2], xb[u][3]};
+        word = mix_quant_lane_bf16<FMT>(w4, emax, m);
+      } else {
+        word = mix_quant_lane<FMT>(xb[u], emax, m);
+      }
+      uint32_t f = 0;
+      if (FMT == 1) f = quad_or_u32((q == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * q)));
+      if (!col_ok || row >= rows) continue;
+      if (!IMG || codes) {
+        *(uint32_t*)(codes + row * (cols >> 1) + scc * 4) = word;
+        if (FMT == 1) {
+          if (q == 0) ((uint16_t*)shared)[row * (cols >> 5) + blk] = (uint16_t)f;
+        } else {
+          if (q == 0) ((uint8_t*)shared)[row * (cols >> 5) + blk] = (uint8_t)((uint32_t)(emax + 7) | (m << 4));
+        }
+      }
+      if (IMG) {
+        uint32_t e0, e1;
+        mix8_to_e4m3(word, m, e0, e1);
+        *(uint2*)(a8 + row * cols + scc * 8) = make_uint2(e0, e1);
+        if (q == 0) {
+          const int rin = (int)(row & (FT - 1));
+          const int64_t tile_base = ((int64_t)(blk >> 2) * tiles_m + (row >> 8)) * 1024;   // FT = 256
+          as_p[tile_base + (((rin >> 7) * 2 + gq) * 32 + (rin & 31)) * 8 + h * 4 + ((rin >> 5) & 3)] =
+              (uint8_t)(emax + 126);
+        }
+      }
     }
   }
 }
@@ -279,10 +308,20 @@ static inline int grid_for(int64_t threads_needed) {
   return (int)(b < 1 ? 1 : b);
 }
 
+static void mq_grid(int64_t rows, int64_t cols, dim3& g, dim3& b) {
+  const int64_t spr = cols >> 3;
+  const int64_t bx = spr <= 1024 ? (spr + 63) / 64 * 64 : 1024;
+  b = dim3((unsigned)bx);
+  const int64_t gx = (spr + bx - 1) / bx;
+  int64_t gy = (rows + MQ_R - 1) / MQ_R;
+  if (gy > 65535) gy = 65535;
+  g = dim3((unsigned)gx, (unsigned)(gy < 1 ? 1 : gy));
+}
+
 hipError_t launch_mix_quantize(int fmt, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                                uint8_t* codes, void* shared, hipStream_t s) {
-  int64_t total = rows * (cols >> 3);
-  dim3 g(grid_for(total)), b(256);
+  dim3 g, b;
+  mq_grid(rows, cols, g, b);
 #define MQ(DT, F) hipLaunchKernelGGL((k_mix_quantize<DT, F, 0>), g, b, 0, s, x, rows, cols, ldx, codes, shared, \
                                      nullptr, nullptr, 0)
   if (dtype == 1) { if (fmt == 1) MQ(1, 1); else MQ(1, 0); }
@@ -293,8 +332,8 @@ hipError_t launch_mix_quantize(int fmt, const void* x, int dtype, int64_t rows, 
 
 hipError_t launch_mix_quantize_img(int fmt, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                                    uint8_t* codes, void* shared, void* img, hipStream_t s) {
-  int64_t total = rows * (cols >> 3);
-  dim3 g(grid_for(total)), b(256);
+  dim3 g, b;
+  mq_grid(rows, cols, g, b);
   const F8AImage L = f8_a_image_layout(rows, cols);
   uint8_t* a8 = (uint8_t*)img + L.a8;
   uint8_t* as_p = (uint8_t*)img + L.as_p;

@@ -74,6 +74,67 @@ __device__ __forceinline__ uint32_t mix_quant_lane(const uint32_t (&xb)[8], int&
   return word;
 }
 
+// The same decision for bf16 inputs, two elements per 32-bit operation. Every threshold has at
+// most 6 significant bits and stays in the normal range, so it is exact in bf16 (its fp32 pattern
+// has 16 low zero bits) and the comparisons run on 16-bit patterns: with d = mu0 - a as a signed
+// 16-bit difference, #{d' : mid_d' >= a} = clamp((d >> 7) + 1, 0, 7) (7 mantissa bits). The sign
+// and zero rules become bit selects. x holds element 2i in its low half and 2i+1 in its high half;
+// the result holds their 4-bit codes in bits 0..3 and 16..19.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t mix_code2_bf16(uint32_t x, uint32_t MU2, uint32_t PB2, uint32_t NB2) {
+  const uint32_t a = x & 0x7FFF7FFFu;
+  i16x2 c = ((__builtin_bit_cast(i16x2, MU2) - __builtin_bit_cast(i16x2, a)) >> (i16x2)7) + (i16x2)1;
+  c = __builtin_elementwise_min(__builtin_elementwise_max(c, (i16x2)0), (i16x2)7);
+  const uint32_t cnt = __builtin_bit_cast(uint32_t, c);
+  // [a > pos_bottom], [a > neg_bottom]: the sign bit of the 16-bit difference
+  const uint32_t gtp =
+      (__builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, PB2) - __builtin_bit_cast(u16x2, a)) >> 15) & 0x00010001u;
+  const uint32_t gtn =
+      (__builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, NB2) - __builtin_bit_cast(u16x2, a)) >> 15) & 0x00010001u;
+  // positives: cnt, except cnt == 7 -> 0xF above pos_bottom, else 0x7
+  const uint32_t eq7 = ((cnt + 0x00010001u) >> 3) & 0x00010001u;
+  const uint32_t pos = cnt | ((gtp & eq7) << 3);
+  // negatives: 8 | cnt for cnt < 6, else 0xE above neg_bottom, else 0x7
+  const uint32_t s6 = ((cnt + 0x00020002u) >> 3) & 0x00010001u;
+  const uint32_t hi = 0x00070007u + (gtn << 3) - gtn;
+  const uint32_t lo = cnt | 0x00080008u;
+  const uint32_t m6 = __builtin_bit_cast(uint32_t, (u16x2)0 - __builtin_bit_cast(u16x2, s6));
+  const uint32_t negc = (hi & m6) | (lo & ~m6);
+  const uint32_t nz = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), (u16x2)1));
+  const uint32_t neg = (x >> 15) & 0x00010001u & nz;
+  const uint32_t mn = __builtin_bit_cast(uint32_t, (u16x2)0 - __builtin_bit_cast(u16x2, neg));
+  return (negc & mn) | (pos & ~mn);
+}
+
+// mix_quant_lane for 8 bf16 elements held two per word (element 2i in the low half of w[i]).
+template <int FMT>
+__device__ __forceinline__ uint32_t mix_quant_lane_bf16(const uint32_t (&w)[4], int& emax, uint32_t& m) {
+  const u16x2 a01 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu),
+                                              __builtin_bit_cast(u16x2, w[1] & 0x7FFF7FFFu));
+  const u16x2 a23 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[2] & 0x7FFF7FFFu),
+                                              __builtin_bit_cast(u16x2, w[3] & 0x7FFF7FFFu));
+  const u16x2 am = __builtin_elementwise_max(a01, a23);
+  const uint32_t lmax = (uint32_t)(am[0] > am[1] ? am[0] : am[1]) << 16;
+  const uint32_t bmax = quad_max_u32(lmax);
+  const int e = (int)(bmax >> 23) - 127;   // an all-zero block gives -127, clamped to -7
+  emax = e < -7 ? -7 : (e > 8 ? 8 : e);
+  m = mant3_of(FMT == 1 ? lmax : bmax);
+  const uint32_t t3 = 24u + 3u * m;          // 1.5 M 2^(Emax-1) = t3 2^(Emax-5)
+  const uint32_t mu = t3 < 32u ? (((uint32_t)(emax + 126) << 7) | ((t3 << 3) & 0x7Fu))
+                               : (((uint32_t)(emax + 127) << 7) | ((t3 << 2) & 0x7Fu));
+  const uint32_t pb = ((uint32_t)(emax + 119) << 7) | (m << 4);   // M 2^(Emax-8)
+  const uint32_t nb = ((uint32_t)(emax + 120) << 7) | (m << 4);   // M 2^(Emax-7)
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t c2 = mix_code2_bf16(w[i], mu * 0x00010001u, pb * 0x00010001u, nb * 0x00010001u);
+    word |= ((c2 & 0xFu) | ((c2 >> 12) & 0xF0u)) << (8 * i);
+  }
+  return word;
+}
+
 // MXFP4 code of one element, thresholds at the E2M1 midpoints times 2^X, ties to the even code.
 struct Fp4Thr { uint32_t t[7]; };
 __device__ __forceinline__ Fp4Thr fp4_thresholds(int X) {
