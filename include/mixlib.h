@@ -185,7 +185,8 @@ mix_status_t mix_mx_gemm_eq6(mix_fmt_t a_fmt, const uint8_t* a_codes, const void
 /*
  * Per-channel mean of the keys -- P1, method overview, last bullet (K-smoothing with the prefill
  * mean frozen for decode). mu[c] = fp32(exact_sum_t k[t, c] / T), the division in fp64.
- *   k  [T, C] fp32 or bf16 (C = kv_heads * head_dim), row pitch ldk
+ *   k  [T, C] fp32 or bf16 (C = kv_heads * head_dim, a multiple of 32), row pitch ldk; k and the
+ *      row pitch in bytes 16-byte aligned
  *   mu [C] fp32
  */
 mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, int64_t ldk, float* mu, void* stream);

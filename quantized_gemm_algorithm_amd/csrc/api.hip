@@ -296,9 +296,11 @@ mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, i
   if (T < 0 || C < 0) return fail(MIX_E_SHAPE, "mix_kmean: negative extent");
   if (C == 0) return MIX_OK;
   if (T == 0) return fail(MIX_E_SHAPE, "mix_kmean: the mean of zero tokens is undefined");
+  if (C % 32) return fail(MIX_E_SHAPE, "mix_kmean: C=%lld is not a multiple of 32", (long long)C);
   if (ldk < C) return fail(MIX_E_SHAPE, "mix_kmean: ldk < C");
   if (!k || !mu) return fail(MIX_E_NULL, "mix_kmean: NULL pointer");
-  if ((uintptr_t)k % dtype_size(dtype)) return fail(MIX_E_ALIGN, "mix_kmean: k misaligned");
+  if (!aligned16(k) || (ldk * dtype_size(dtype)) % 16)
+    return fail(MIX_E_ALIGN, "mix_kmean: k or its row pitch is not 16-byte aligned");
   return hip_status(mix::launch_kmean(k, (int)dtype, T, C, ldk, mu, (hipStream_t)stream), "mix_kmean launch");
 }
 

@@ -380,8 +380,10 @@ __global__ void __launch_bounds__(256, 1) k_gemm_mfma_big(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 8; j++) {
         const int sb_j = (int)(((j < 4 ? bsw.x : bsw.y) >> (8 * (j & 3))) & 0xFFu);
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, B_FP4 ? 4 : 0, 0, sa_i,
-                                                                      0, sb_j);
+        // the B fragment is the MFMA's A operand, so result register e of lane l holds
+        // C[m = l & 15][n = 4 (l >> 4) + e]: four consecutive outputs of one row
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], B_FP4 ? 4 : 0, 0, 0, sb_j,
+                                                                      0, sa_i);
       }
     }
     if (kt + 1 < nk) big_store<A_FMT, B_FP4>(S, cur ^ 1, R);
@@ -389,22 +391,34 @@ __global__ void __launch_bounds__(256, 1) k_gemm_mfma_big(GemmArgs g) {
   }
 
   const float* rdiv = g.row_div ? g.row_div + (int64_t)batch * g.row_div_bstride : nullptr;
+  const bool vec_ok = (g.ldc % 4) == 0 && (g.c_bstride % 4) == 0 && (((uintptr_t)g.c) & 15) == 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
+    const int m = m0 + 128 * wm + 16 * i + r;
+    if (m >= g.M) continue;
+    const float dv = rdiv ? rdiv[m] : 1.0f;
 #pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const int m = m0 + 128 * wm + 16 * i + 4 * gq + e;
-      if (m >= g.M) continue;
-      const float dv = rdiv ? rdiv[m] : 1.0f;
+    for (int j = 0; j < 8; j++) {
+      const int n = n0 + 128 * wn + 16 * j + 4 * gq;
+      if (n >= g.N) continue;
+      float v[4];
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int n = n0 + 128 * wn + 16 * j + r;
-        if (n >= g.N) continue;
-        float v = acc[i][j][e];
-        if (rdiv) v = __fdiv_rn(v, dv);
-        const int64_t idx = (int64_t)batch * g.c_bstride + (int64_t)m * g.ldc + n;
-        if (C_BF16) ((uint16_t*)g.c)[idx] = f32_to_bf16_rne(v);
-        else ((float*)g.c)[idx] = v;
+      for (int e = 0; e < 4; e++) v[e] = rdiv ? __fdiv_rn(acc[i][j][e], dv) : acc[i][j][e];
+      const int64_t idx = (int64_t)batch * g.c_bstride + (int64_t)m * g.ldc + n;
+      if (vec_ok && n + 4 <= g.N) {
+        if (C_BF16)
+          *(uint2*)((uint16_t*)g.c + idx) =
+              make_uint2((uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
+                         (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16));
+        else
+          *(float4*)((float*)g.c + idx) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          if (n + e >= g.N) break;
+          if (C_BF16) ((uint16_t*)g.c)[idx + e] = f32_to_bf16_rne(v[e]);
+          else ((float*)g.c)[idx + e] = v[e];
+        }
       }
     }
   }

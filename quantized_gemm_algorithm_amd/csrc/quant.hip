@@ -273,30 +273,51 @@ __device__ __forceinline__ DD dd_add(DD x, DD y) {
   return DD{h, l};
 }
 
+// One workgroup per group of KM_CW columns (16 bytes of a row): its 1024 threads take rows
+// t, t + 1024, ... and keep one exact pair per column; the pairs are added across the wave by
+// shuffles and across the 16 waves in LDS. The result does not depend on the order whenever the
+// exact sum fits the pair (as above).
+constexpr int KM_THREADS = 1024;
+
 template <int DT>
-__global__ void __launch_bounds__(256) k_kmean(const void* __restrict__ x, int64_t T, int64_t C, int64_t ldx,
-                                                float* __restrict__ mu) {
-  // block: 32 columns x 8 row lanes
-  __shared__ double shi[8][32];
-  __shared__ double slo[8][32];
-  int cl = threadIdx.x & 31, rl = threadIdx.x >> 5;
-  int64_t c = (int64_t)blockIdx.x * 32 + cl;
-  DD acc{0.0, 0.0};
-  if (c < C) {
-    for (int64_t t = rl; t < T; t += 8) {
-      float v = DT == 1 ? __uint_as_float((uint32_t)((const uint16_t*)x)[t * ldx + c] << 16)
-                        : ((const float*)x)[t * ldx + c];
-      acc = dd_add(acc, (double)v);
+__global__ void __launch_bounds__(KM_THREADS) k_kmean(const void* __restrict__ x, int64_t T, int64_t C, int64_t ldx,
+                                                       float* __restrict__ mu) {
+  constexpr int CW = DT == 1 ? 8 : 4;  // columns per thread (one 16-byte load)
+  __shared__ double shi[KM_THREADS / 64][CW];
+  __shared__ double slo[KM_THREADS / 64][CW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * CW;
+  DD acc[CW];
+#pragma unroll
+  for (int j = 0; j < CW; j++) acc[j] = DD{0.0, 0.0};
+  for (int64_t t = threadIdx.x; t < T; t += KM_THREADS) {
+    const uint4 v = DT == 1 ? *(const uint4*)((const uint16_t*)x + t * ldx + c0) : *(const uint4*)((const float*)x + t * ldx + c0);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < CW; j++) {
+      const float f = DT == 1 ? __uint_as_float(j & 1 ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16)) : __uint_as_float(w[j]);
+      acc[j] = dd_add(acc[j], (double)f);
     }
   }
-  shi[rl][cl] = acc.hi;
-  slo[rl][cl] = acc.lo;
+#pragma unroll
+  for (int j = 0; j < CW; j++) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const DD o{__shfl_xor(acc[j].hi, off, 64), __shfl_xor(acc[j].lo, off, 64)};
+      acc[j] = dd_add(acc[j], o);
+    }
+    if (lane == 0) {
+      shi[wave][j] = acc[j].hi;
+      slo[wave][j] = acc[j].lo;
+    }
+  }
   __syncthreads();
-  if (rl == 0 && c < C) {
-    DD s{shi[0][cl], slo[0][cl]};
-    for (int i = 1; i < 8; i++) s = dd_add(s, DD{shi[i][cl], slo[i][cl]});
-    double sum = s.hi + s.lo;  // correctly rounded: the pair is normalised
-    mu[c] = (float)(sum / (double)T);
+  if (threadIdx.x < CW) {
+    const int j = threadIdx.x;
+    DD s2{shi[0][j], slo[0][j]};
+    for (int w2 = 1; w2 < KM_THREADS / 64; w2++) s2 = dd_add(s2, DD{shi[w2][j], slo[w2][j]});
+    const double sum = s2.hi + s2.lo;  // correctly rounded: the pair is normalised
+    mu[c0 + j] = (float)(sum / (double)T);
   }
 }
 
@@ -385,7 +406,7 @@ hipError_t launch_mx_dequantize(int fp4, const uint8_t* codes, const uint8_t* sc
 }
 
 hipError_t launch_kmean(const void* x, int dtype, int64_t T, int64_t C, int64_t ldx, float* mu, hipStream_t s) {
-  dim3 g((unsigned)((C + 31) / 32)), b(256);
+  dim3 g((unsigned)(C / (dtype == 1 ? 8 : 4))), b(KM_THREADS);
   if (dtype == 1) hipLaunchKernelGGL((k_kmean<1>), g, b, 0, s, x, T, C, ldx, mu);
   else hipLaunchKernelGGL((k_kmean<0>), g, b, 0, s, x, T, C, ldx, mu);
   return hipGetLastError();

@@ -106,6 +106,9 @@ def test_kmean_validation(lib):
     assert lib.mix_kmean(None, 1, 4, 32, 32, FAKE, None) == MIX_E_NULL
     assert lib.mix_kmean(FAKE, 1, 4, 32, 16, FAKE, None) == MIX_E_SHAPE
     assert lib.mix_kmean(None, 1, 4, 0, 0, None, None) == MIX_OK
+    assert lib.mix_kmean(FAKE, 1, 4, 40, 40, FAKE, None) == MIX_E_SHAPE
+    assert lib.mix_kmean(MISALIGNED, 1, 4, 32, 32, FAKE, None) == MIX_E_ALIGN
+    assert lib.mix_kmean(FAKE, 1, 4, 32, 36, FAKE, None) == MIX_E_ALIGN
 
 
 def test_image_sizes(lib):

@@ -212,3 +212,29 @@ def test_kmean_matches_oracle():
     want = kmean_ref(k, "bf16")
     assert_codes_equal(host(mu).view(np.uint32), want.reshape(-1).view(np.uint32), "mu bits")
     assert torch.isfinite(mu).all()
+
+
+@pytest.mark.parametrize("T", [1, 1000, 4097])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kmean_shapes_and_pitch(T, dtype):
+    # the mean over T tokens is fp32 of the exact sum / T, whatever the row split: ragged T, fp32
+    # input, a row pitch wider than the columns
+    import torch
+    from oracle.attention import kmean_ref
+    q = _lib()
+    rng = np.random.default_rng(T)
+    kf = (rng.standard_normal((T, 2, 64)) * np.exp2(rng.integers(-6, 6, (T, 2, 64)))).astype(np.float32)
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(kf)
+        want = kmean_ref(bits, "bf16")
+        wide = np.zeros((T, 160), np.uint16)
+        wide[:, :128] = bits.reshape(T, 128)
+        dev = dev_bf16(wide)[:, :128]
+    else:
+        want = kmean_ref(kf, "f32")
+        wide = np.zeros((T, 132), np.float32)
+        wide[:, :128] = kf.reshape(T, 128)
+        dev = torch.from_numpy(wide).cuda()[:, :128]
+    mu = q.mix_kmean(dev)
+    torch.cuda.synchronize()
+    assert_codes_equal(host(mu).view(np.uint32), want.reshape(-1).view(np.uint32), f"mu {dtype} T={T}")
