@@ -167,7 +167,9 @@ mix_status_t mx_gemm_b_image(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8
 /*
  * C = A . B^T from the two images (same results as mix_mx_gemm on the codes). For MX_FP4 the
  * E2M1 nibbles are read from b_codes ([N, K/2], 16-byte aligned) -- the B image holds only the
- * scales; for MX_INT4 b_codes is ignored and may be NULL. c and ldc as for mix_mx_gemm.
+ * scales; for MX_INT4 b_codes is ignored and may be NULL. c and ldc as for mix_mx_gemm. For
+ * M > 16 each operand image must stay below 2^31 bytes (MIX_E_UNSUPPORTED otherwise; mix_mx_gemm
+ * then decodes inside the GEMM instead).
  */
 mix_status_t mix_mx_gemm_images(mx_fmt_t b_fmt, const void* a_img, const void* b_img, const uint8_t* b_codes,
                                 int64_t M, int64_t N, int64_t K, void* c, mix_dtype_t c_dtype, int64_t ldc,

@@ -280,6 +280,9 @@ mix_status_t mix_mx_gemm_images(mx_fmt_t b_fmt, const void* a_img, const void* b
   if (M > INT32_MAX || N > INT32_MAX || !image_k_ok(K))
     return fail(MIX_E_SHAPE, "%s: K=%lld is not a positive multiple of 128 (or an extent is above 2^31-1)", fn, (long long)K);
   if (ldc < N) return fail(MIX_E_SHAPE, "%s: ldc=%lld < N=%lld", fn, (long long)ldc, (long long)N);
+  if (M > 16 && !mix::gemm_f8_offsets_ok(M, N, K))
+    return fail(MIX_E_UNSUPPORTED, "%s: an operand image of %lld x %lld x %lld reaches 2^31 bytes", fn, (long long)M,
+                (long long)N, (long long)K);
   if (!c || !a_img || !b_img) return fail(MIX_E_NULL, "%s: c or an image is NULL", fn);
   if (b_fmt == MX_FP4 && !b_codes) return fail(MIX_E_NULL, "%s: MXFP4 codes are NULL", fn);
   if (((uintptr_t)a_img & 255u) || ((uintptr_t)b_img & 255u)) return fail(MIX_E_ALIGN, "%s: images must be 256-byte aligned", fn);

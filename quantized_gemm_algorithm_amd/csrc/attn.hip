@@ -33,25 +33,11 @@ namespace mix {
 __device__ __forceinline__ uint32_t mix45_code8(const float (&p)[8], int quad_pos, uint32_t* shared,
                                                 uint32_t* m_out) {
   uint32_t xb[8];
-  uint32_t lmax = 0;
 #pragma unroll
-  for (int e = 0; e < 8; e++) {
-    xb[e] = f32_bits(p[e]);
-    uint32_t a = xb[e] & 0x7FFFFFFFu;
-    lmax = a > lmax ? a : lmax;
-  }
-  uint32_t bmax = quad_max_u32(lmax);
+  for (int e = 0; e < 8; e++) xb[e] = f32_bits(p[e]);
   int emax;
-  if (bmax == 0) emax = -7;
-  else {
-    int e = (int)(bmax >> 23) - 127;
-    emax = e < -7 ? -7 : (e > 8 ? 8 : e);
-  }
-  uint32_t m = mant3_of(lmax);
-  MixThresholds t = mix_thresholds(emax, m);
-  uint32_t word = 0;
-#pragma unroll
-  for (int e = 0; e < 8; e++) word |= mix_code(xb[e], t) << (4 * e);
+  uint32_t m;
+  const uint32_t word = mix_quant_lane<1>(xb, emax, m);
   uint32_t f = (quad_pos == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * quad_pos));
   *shared = quad_or_u32(f);
   *m_out = m;

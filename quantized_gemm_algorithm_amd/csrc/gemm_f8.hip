@@ -110,10 +110,11 @@ struct F8Args {
   const uint8_t* a8;      // [M, K] E4M3
   const uint8_t* as_p;    // [K/128][tiles_m][1024] E8M0, permuted
   const uint8_t* b;       // [N, K/2] FP4 codes or [N, K] E4M3
-  const uint8_t* bs_p;    // [K/128][tiles_n][1024] E8M0, permuted
+  const uint8_t* bs_p;    // [K/128][bs_tn][1024] E8M0, permuted
   void* c;
   int64_t ldc;
   int M, N, K;
+  int bs_tn;              // 256-row tiles of the B image (its scale layout)
 };
 
 __device__ __forceinline__ int f8_xcd_tile(int bid, int nt) {
@@ -151,7 +152,7 @@ __device__ __forceinline__ void f8_issue(const F8Args& g, uint8_t* st, int tm, i
     const int row = q >> 3, slot = q & 7;
     const int c = slot ^ (row & 7);
     const int grow = min(m0 + row, g.M - 1);
-    dma16(g.a8 + (int64_t)grow * g.K + k0 + 16 * c,
+    dma16(g.a8 + (uint32_t)(grow * g.K + k0 + 16 * c),
           __builtin_amdgcn_readfirstlane(lds_addr(st + (p * F8_THREADS + wave * 64) * 16)));
   }
   if (B_FP4) {
@@ -162,7 +163,7 @@ __device__ __forceinline__ void f8_issue(const F8Args& g, uint8_t* st, int tm, i
       const int row = q >> 2, slot = q & 3;
       const int c = slot ^ ((row >> 1) & 3);
       const int grow = min(n0 + row, g.N - 1);
-      dma16(g.b + (int64_t)grow * (g.K >> 1) + (k0 >> 1) + 16 * c,
+      dma16(g.b + (uint32_t)(grow * (g.K >> 1) + (k0 >> 1) + 16 * c),
             __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::A_BYTES + (p * F8_THREADS + wave * 64) * 16)));
     }
   } else {
@@ -172,16 +173,16 @@ __device__ __forceinline__ void f8_issue(const F8Args& g, uint8_t* st, int tm, i
       const int row = q >> 3, slot = q & 7;
       const int c = slot ^ (row & 7);
       const int grow = min(n0 + row, g.N - 1);
-      dma16(g.b + (int64_t)grow * g.K + k0 + 16 * c,
+      dma16(g.b + (uint32_t)(grow * g.K + k0 + 16 * c),
             __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::A_BYTES + (p * F8_THREADS + wave * 64) * 16)));
     }
   }
   // scales: the (K step, tile) 1 KB blocks are contiguous; waves 0-3 copy A's, waves 4-7 B's
   if (wave < 4)
-    dma4(g.as_p + ((int64_t)ks * tiles_m + tm) * 1024 + wave * 256 + lane * 4,
+    dma4(g.as_p + (uint32_t)((ks * tiles_m + tm) * 1024 + wave * 256 + lane * 4),
          __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::AS_OFF + wave * 256)));
   else
-    dma4(g.bs_p + ((int64_t)ks * tiles_n + tn) * 1024 + (wave - 4) * 256 + lane * 4,
+    dma4(g.bs_p + (uint32_t)((ks * g.bs_tn + tn) * 1024 + (wave - 4) * 256 + lane * 4),
          __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::BS_OFF + (wave - 4) * 256)));
 }
 
@@ -491,10 +492,19 @@ __global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
 
 // ------------------------------------------------------------------ host side
 
+bool gemm_f8_offsets_ok(int64_t M, int64_t N, int64_t K);
+
 // Shapes mix_mx_gemm sends through the images: the tiled GEMM for M >= 64 and N >= 256, the
 // weight stream (k_gemv_f8) for M <= 16; others decode inside k_gemm_mfma.
 bool gemm_f8_eligible(int64_t M, int64_t N, int64_t K) {
-  return K > 0 && K % FK == 0 && ((M >= 64 && N >= FT) || (M >= 1 && M <= 16));
+  return K > 0 && K % FK == 0 && ((M >= 64 && N >= FT) || (M >= 1 && M <= 16)) && gemm_f8_offsets_ok(M, N, K);
+}
+
+// The tiled kernel addresses its operands with 32-bit byte offsets.
+bool gemm_f8_offsets_ok(int64_t M, int64_t N, int64_t K) {
+  const int64_t lim = (int64_t)1 << 31;
+  return M * K < lim && N * K < lim && (K / FK) * ((M + FT - 1) / FT) * 1024 < lim &&
+         (K / FK) * ((N + FT - 1) / FT) * 1024 < lim;
 }
 
 size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K) {
@@ -579,7 +589,7 @@ static hipError_t launch_gv(const F8Args& f, hipStream_t s) {
   int kc = f.K < 32 * FK ? f.K : 32 * FK;
   while (kc > FK && gv_lds_bytes(B_FP4, G, kc) > 160 * 1024) kc -= FK;
   GvArgs a{};
-  a.g = f; a.kc = kc; a.tiles_n = (f.N + FT - 1) / FT;
+  a.g = f; a.kc = kc; a.tiles_n = f.bs_tn;
   const int blocks = (f.N + 16 * G - 1) / (16 * G);
   hipLaunchKernelGGL((k_gemv_f8<B_FP4, C_BF16, G>), dim3(blocks), dim3(256), gv_lds_bytes(B_FP4, G, kc), s, a);
   return hipGetLastError();
@@ -611,6 +621,7 @@ hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const vo
   a.b = b_fp4 ? b_codes : (const uint8_t*)b_img + LB.b8;
   a.bs_p = (const uint8_t*)b_img + LB.bs_p;
   a.c = c; a.ldc = ldc; a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  a.bs_tn = (int)((N + FT - 1) / FT);
   if (M <= 16) return launch_gemv_f8(b_fp4, c_bf16, a, s);
   if (b_fp4) return c_bf16 ? launch_f8<1, 1>(a, s) : launch_f8<1, 0>(a, s);
   return c_bf16 ? launch_f8<0, 1>(a, s) : launch_f8<0, 0>(a, s);

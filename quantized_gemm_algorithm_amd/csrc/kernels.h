@@ -46,6 +46,7 @@ hipError_t launch_gemm_eq6(int a_fmt, int b_fp4, int c_bf16, const GemmArgs& g, 
 
 // fast path: decode pass into a workspace, then the MXFP8 x MX GEMM
 bool gemm_f8_eligible(int64_t M, int64_t N, int64_t K);
+bool gemm_f8_offsets_ok(int64_t M, int64_t N, int64_t K);
 size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_f8(int a_fmt, int b_fp4, int c_bf16, const uint8_t* a_codes, const void* a_shared,
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,

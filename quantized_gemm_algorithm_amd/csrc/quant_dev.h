@@ -47,33 +47,6 @@ __device__ __forceinline__ uint32_t mix_code(uint32_t xbits, const MixThresholds
   return code;
 }
 
-// One lane's share of a MiX block: the lane holds 8 consecutive elements (fp32 bit patterns) and
-// the 4 sub-blocks of a 32-element block sit in the 4 lanes of a quad (sub-block = lane & 3).
-// Returns the 8 nibbles (element e at bits 4e) and sets the block's Emax (clamped to [-7, 8]) and
-// this lane's 3-bit shared mantissa m (its sub-block's for MiX-4.5b, the block's for MiX-4.25b).
-template <int FMT>  // 0 = MiX-4.25b, 1 = MiX-4.5b
-__device__ __forceinline__ uint32_t mix_quant_lane(const uint32_t (&xb)[8], int& emax, uint32_t& m) {
-  uint32_t lmax = 0;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const uint32_t a = xb[i] & 0x7FFFFFFFu;
-    lmax = a > lmax ? a : lmax;
-  }
-  const uint32_t bmax = quad_max_u32(lmax);
-  if (bmax == 0) {
-    emax = -7;
-  } else {
-    const int e = (int)(bmax >> 23) - 127;
-    emax = e < -7 ? -7 : (e > 8 ? 8 : e);
-  }
-  m = mant3_of(FMT == 1 ? lmax : bmax);
-  const MixThresholds t = mix_thresholds(emax, m);
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 8; i++) word |= mix_code(xb[i], t) << (4 * i);
-  return word;
-}
-
 // The same decision for bf16 inputs, two elements per 32-bit operation. Every threshold has at
 // most 6 significant bits and stays in the normal range, so it is exact in bf16 (its fp32 pattern
 // has 16 low zero bits) and the comparisons run on 16-bit patterns: with d = mu0 - a as a signed
@@ -108,6 +81,25 @@ __device__ __forceinline__ uint32_t mix_code2_bf16(uint32_t x, uint32_t MU2, uin
   return (negc & mn) | (pos & ~mn);
 }
 
+// The 8 nibbles of a sub-block from its 16-bit patterns (two per word, element 2i in the low half
+// of w[i]) and the block's Emax and mantissa m. The thresholds as 16-bit patterns (all normal):
+// mid_0 = 1.5 M 2^(Emax-1) = t3 2^(Emax-5) with t3 = 3 (8 + m), pos_bottom = M 2^(Emax-8),
+// neg_bottom = M 2^(Emax-7).
+__device__ __forceinline__ uint32_t mix_code8_packed(const uint32_t (&w)[4], int emax, uint32_t m) {
+  const uint32_t t3 = 24u + 3u * m;
+  const uint32_t mu = t3 < 32u ? (((uint32_t)(emax + 126) << 7) | ((t3 << 3) & 0x7Fu))
+                               : (((uint32_t)(emax + 127) << 7) | ((t3 << 2) & 0x7Fu));
+  const uint32_t pb = ((uint32_t)(emax + 119) << 7) | (m << 4);
+  const uint32_t nb = ((uint32_t)(emax + 120) << 7) | (m << 4);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t c2 = mix_code2_bf16(w[i], mu * 0x00010001u, pb * 0x00010001u, nb * 0x00010001u);
+    word |= ((c2 & 0xFu) | ((c2 >> 12) & 0xF0u)) << (8 * i);
+  }
+  return word;
+}
+
 // mix_quant_lane for 8 bf16 elements held two per word (element 2i in the low half of w[i]).
 template <int FMT>
 __device__ __forceinline__ uint32_t mix_quant_lane_bf16(const uint32_t (&w)[4], int& emax, uint32_t& m) {
@@ -121,18 +113,38 @@ __device__ __forceinline__ uint32_t mix_quant_lane_bf16(const uint32_t (&w)[4], 
   const int e = (int)(bmax >> 23) - 127;   // an all-zero block gives -127, clamped to -7
   emax = e < -7 ? -7 : (e > 8 ? 8 : e);
   m = mant3_of(FMT == 1 ? lmax : bmax);
-  const uint32_t t3 = 24u + 3u * m;          // 1.5 M 2^(Emax-1) = t3 2^(Emax-5)
-  const uint32_t mu = t3 < 32u ? (((uint32_t)(emax + 126) << 7) | ((t3 << 3) & 0x7Fu))
-                               : (((uint32_t)(emax + 127) << 7) | ((t3 << 2) & 0x7Fu));
-  const uint32_t pb = ((uint32_t)(emax + 119) << 7) | (m << 4);   // M 2^(Emax-8)
-  const uint32_t nb = ((uint32_t)(emax + 120) << 7) | (m << 4);   // M 2^(Emax-7)
-  uint32_t word = 0;
+  return mix_code8_packed(w, emax, m);
+}
+
+// One lane's share of a MiX block: the lane holds 8 consecutive elements (fp32 bit patterns) and
+// the 4 sub-blocks of a 32-element block sit in the 4 lanes of a quad (sub-block = lane & 3).
+// Returns the 8 nibbles (element e at bits 4e) and sets the block's Emax (clamped to [-7, 8]) and
+// this lane's 3-bit shared mantissa m (its sub-block's for MiX-4.5b, the block's for MiX-4.25b).
+// Emax and m come from the exact fp32 maxima. The element decisions compare against thresholds
+// that are 16-bit patterns (see mix_code2_bf16), and for such a threshold t and |x| = a,
+// a > t exactly when ceil(a / 2^16) > t / 2^16; so the elements are coded by the packed coder on
+// their patterns rounded up to 16 bits, with the same result as mix_code on the fp32 patterns.
+template <int FMT>  // 0 = MiX-4.25b, 1 = MiX-4.5b
+__device__ __forceinline__ uint32_t mix_quant_lane(const uint32_t (&xb)[8], int& emax, uint32_t& m) {
+  uint32_t lmax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint32_t a = xb[i] & 0x7FFFFFFFu;
+    lmax = a > lmax ? a : lmax;
+  }
+  const uint32_t bmax = quad_max_u32(lmax);
+  const int e = (int)(bmax >> 23) - 127;   // an all-zero block gives -127, clamped to -7
+  emax = e < -7 ? -7 : (e > 8 ? 8 : e);
+  m = mant3_of(FMT == 1 ? lmax : bmax);
+  uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const uint32_t c2 = mix_code2_bf16(w[i], mu * 0x00010001u, pb * 0x00010001u, nb * 0x00010001u);
-    word |= ((c2 & 0xFu) | ((c2 >> 12) & 0xF0u)) << (8 * i);
+    const uint32_t x0 = xb[2 * i], x1 = xb[2 * i + 1];
+    const uint32_t h0 = ((x0 >> 16) & 0x8000u) | (((x0 & 0x7FFFFFFFu) + 0xFFFFu) >> 16);
+    const uint32_t h1 = ((x1 >> 16) & 0x8000u) | (((x1 & 0x7FFFFFFFu) + 0xFFFFu) >> 16);
+    w[i] = h0 | (h1 << 16);
   }
-  return word;
+  return mix_code8_packed(w, emax, m);
 }
 
 // MXFP4 code of one element, thresholds at the E2M1 midpoints times 2^X, ties to the even code.

@@ -146,3 +146,6 @@ def test_image_validation(lib):
     assert lib.mix_mx_gemm_images(0, A16, FAKE, None, 4, 4, 128, FAKE, 0, 4, None) == MIX_E_ALIGN
     assert lib.mix_mx_gemm_images(0, FAKE, FAKE, None, 4, 4, 128, FAKE, 0, 3, None) == MIX_E_SHAPE
     assert lib.mix_mx_gemm_images(0, None, None, None, 0, 4, 128, None, 0, 4, None) == MIX_OK
+    # 32-bit offsets inside the tiled kernel: a 2^31-byte A image is refused (M > 16)
+    assert lib.mix_mx_gemm_images(1, FAKE, FAKE, FAKE, 1 << 20, 256, 2048, FAKE, 0, 256, None) == MIX_E_UNSUPPORTED
+    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 1 << 20, 256, 2048) == 0
