@@ -93,18 +93,21 @@ __global__ void __launch_bounds__(256) k_softmax_pquant(const float* __restrict_
   const int nit_valid = (n_valid + 511) / 512;
   const int nit_write = (n_write + 511) / 512;
 
+  // all of the row's register chunks are requested before any is used
   float cache[SM_NREG][8];
+#pragma unroll
+  for (int it = 0; it < SM_NREG; it++) {
+    const int j0 = it * 512 + lane * 8;
+    if (it < nit_valid && j0 < n_valid) load8f(srow + j0, cache[it]);
+  }
   float mx = -INFINITY;
 #pragma unroll
   for (int it = 0; it < SM_NREG; it++) {
-    if (it < nit_valid) {
-      int j0 = it * 512 + lane * 8;
-      if (j0 < n_valid) {
-        load8f(srow + j0, cache[it]);
+    const int j0 = it * 512 + lane * 8;
+    if (it < nit_valid && j0 < n_valid) {
 #pragma unroll
-        for (int e = 0; e < 8; e++)
-          if (j0 + e < n_valid) mx = fmaxf(mx, cache[it][e]);
-      }
+      for (int e = 0; e < 8; e++)
+        if (j0 + e < n_valid) mx = fmaxf(mx, cache[it][e]);
     }
   }
   for (int it = SM_NREG; it < nit_valid; it++) {
@@ -152,6 +155,183 @@ __global__ void __launch_bounds__(256) k_softmax_pquant(const float* __restrict_
   }
   lsum = wave_sum_f32(lsum);
   if (lane == 0) l[row] = lsum;
+}
+
+// ------------------------------------------------------------------ prefill: fused S passes
+
+// S = Q^ K^T is never stored. Pass 1 computes each query row's exact maximum over its unmasked
+// keys; pass 2 recomputes S, turns it into p = exp(z - m), sums l and codes P^ (MiX-4.5b along
+// keys). Workgroup: 4 waves, 64 query rows of one head (wave w: rows 16 w .. 16 w + 15), key tiles
+// of 64. MFMA v_mfma_scale_f32_16x16x128_f8f6f4 over the whole head dimension (d = 128): its A
+// operand is 16 keys of K^ (FP4, lane l = r + 16 g holds key r, elements [32 g, 32 g + 32)), its
+// B operand 16 query rows of Q^ decoded to E4M3 (row r, elements [16 g, +16) and [64 + 16 g, +16)),
+// so result register e of lane l is S[query r][key 4 g + e]: each lane holds, per 16-key group j,
+// four consecutive keys of one query.
+constexpr int PQ = 64;   // query rows per workgroup
+constexpr int PK = 64;   // keys per tile
+
+struct PrefillOps {
+  const uint8_t* qc;     // Q^ codes [T, Hq, d/2]
+  const uint16_t* qs;    // Q^ shared fields [T, Hq, d/32]
+  const uint8_t* kc;     // K^ codes [T, Hkv, d/2]
+  const uint8_t* ks;     // K^ scales [T, Hkv, d/32]
+  int T, Tp, Hq, Hkv, causal;
+};
+
+// Q^ operand of query row q (head h) for this lane's K group g, decoded from MiX codes to E4M3
+__device__ __forceinline__ void q_operand(const PrefillOps& P, int q, int h, int g, v8i& qf, int& qsc) {
+  const int64_t qrow = (int64_t)q * P.Hq + h;
+  const uint8_t* qrc = P.qc + qrow * 64;
+  const uint16_t* qrs = P.qs + qrow * 4;
+  uint32_t o[8];
+#pragma unroll
+  for (int half = 0; half < 2; half++) {
+    const int blk = (g >> 1) + 2 * half;   // elements [16 g + 64 half, +16): sub-blocks 2 (g & 1), 2 (g & 1) + 1
+    const uint32_t sh = qrs[blk];
+    const uint2 wv = *(const uint2*)(qrc + blk * 16 + (g & 1) * 8);
+    mix8_to_e4m3(wv.x, (sh >> (4 + 3 * (2 * (g & 1)))) & 7u, o[4 * half + 0], o[4 * half + 1]);
+    mix8_to_e4m3(wv.y, (sh >> (4 + 3 * (2 * (g & 1) + 1))) & 7u, o[4 * half + 2], o[4 * half + 3]);
+  }
+  qf = v8i{(int)o[0], (int)o[1], (int)o[2], (int)o[3], (int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+  qsc = (int)(qrs[g] & 15u) + 119;
+}
+
+// K^ fragments of keys k0 .. k0 + 63 for this lane (keys past T read key T-1; masked later)
+struct KFrag {
+  uint4 kv[4];
+  int ksc[4];
+};
+__device__ __forceinline__ void k_load(const PrefillOps& P, int hk, int k0, int r, int g, KFrag& F) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int key = min(k0 + 16 * j + r, P.T - 1);
+    const int64_t krow = (int64_t)key * P.Hkv + hk;
+    F.kv[j] = *(const uint4*)(P.kc + krow * 64 + g * 16);
+    F.ksc[j] = P.ks[krow * 4 + g];
+  }
+}
+// S for the wave's 16 queries and the 64 keys of F
+__device__ __forceinline__ void s_tile(const KFrag& F, const v8i& qf, int qsc, v4f (&acc)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const v8i kf = v8i{(int)F.kv[j].x, (int)F.kv[j].y, (int)F.kv[j].z, (int)F.kv[j].w, 0, 0, 0, 0};
+    acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf, v4f{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, F.ksc[j], 0, qsc);
+  }
+}
+
+// Key tiles are visited from a start that rotates with the query tile (the workgroups of a head
+// then read different K^ rows at the same time); the next tile's fragments load while the current
+// one is used. Neither the row maximum nor the codes depend on the order.
+__device__ __forceinline__ int tile_rot(int nt) { return nt > 0 ? (int)(blockIdx.x % (unsigned)nt) : 0; }
+
+// grid (ceil(T / 64), Hq), block 256. smax [Hq, T]: max of S over the unmasked keys of each row.
+__global__ void __launch_bounds__(256) k_attn_rowmax(PrefillOps P, float* __restrict__ smax) {
+  const int h = blockIdx.y, hk = h / (P.Hq / P.Hkv);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int q = blockIdx.x * PQ + 16 * wave + r;
+  v8i qf;
+  int qsc;
+  q_operand(P, min(q, P.T - 1), h, g, qf, qsc);
+  const int nvalid = P.causal ? min(q + 1, P.T) : P.T;
+  const int kend = P.causal ? min(blockIdx.x * PQ + PQ, P.T) : P.T;   // keys any row of the tile sees
+  float mx = -INFINITY;
+  const int nt = (kend + PK - 1) / PK, t0 = tile_rot(nt);
+  KFrag F;
+  if (nt > 0) k_load(P, hk, t0 * PK, r, g, F);
+  for (int it = 0; it < nt; it++) {
+    const int k0 = ((t0 + it) % nt) * PK;
+    v4f acc[4];
+    s_tile(F, qf, qsc, acc);
+    if (it + 1 < nt) k_load(P, hk, ((t0 + it + 1) % nt) * PK, r, g, F);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        if (k0 + 16 * j + 4 * g + e < nvalid) mx = fmaxf(mx, acc[j][e]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (g == 0 && q < P.T) smax[(int64_t)h * P.T + q] = mx;
+}
+
+// grid (ceil(T / 64), Hq), block 256. P^ codes [Hq, T, Tp/2] and shared [Hq, T, Tp/32] for keys
+// [0, min(Tp, round_up(i + 1, 256))) of row i (all Tp without the mask; masked keys code as zero),
+// l [Hq, T]; optional S and p dumps [Hq, T, Tp].
+__global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* __restrict__ smax, float scale,
+                                                     uint8_t* __restrict__ pc, uint16_t* __restrict__ ps,
+                                                     float* __restrict__ l, float* __restrict__ dbg_s,
+                                                     float* __restrict__ dbg_p) {
+  constexpr int PP = PK + 4;                     // padded LDS row (floats)
+  __shared__ __align__(16) float sp[4][16][PP];  // each wave's p tile: 16 rows x 64 keys
+  const int h = blockIdx.y, hk = h / (P.Hq / P.Hkv);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int q0w = blockIdx.x * PQ + 16 * wave;   // the wave's first query row
+  const int q = q0w + r;
+  v8i qf;
+  int qsc;
+  q_operand(P, min(q, P.T - 1), h, g, qf, qsc);
+  const int nvalid = P.causal ? min(q + 1, P.T) : P.T;
+  const float mz = q < P.T ? __fmul_rn(smax[(int64_t)h * P.T + min(q, P.T - 1)], scale) : 0.f;
+  const int qlast = min(blockIdx.x * PQ + PQ, P.T) - 1;
+  const int kend = P.causal ? qlast + 1 : P.T;                                 // keys with some unmasked entry
+  const int kwrite = P.causal ? min(P.Tp, (qlast + 1 + 255) / 256 * 256) : P.Tp;  // keys whose codes are written
+  float lsum = 0.f;
+  // read-back role: row rr = lane / 8 (+ 8 per pass), 8 keys kk = 8 (lane % 8); quads are 32-key blocks
+  const int rr0 = lane >> 3, kk = 8 * (lane & 7);
+  const int nt = (kwrite + PK - 1) / PK, ntc = (kend + PK - 1) / PK, t0 = tile_rot(ntc);
+  KFrag F;
+  if (ntc > 0) k_load(P, hk, t0 * PK, r, g, F);
+  for (int it = 0; it < nt; it++) {
+    // the ntc tiles with unmasked keys first (rotated), then the all-zero tiles up to kwrite
+    const int kt = it < ntc ? (t0 + it) % ntc : it;
+    const int k0 = kt * PK;
+    if (it < ntc) {
+      v4f acc[4];
+      s_tile(F, qf, qsc, acc);
+      if (it + 1 < ntc) k_load(P, hk, ((t0 + it + 1) % ntc) * PK, r, g, F);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int key = k0 + 16 * j + 4 * g + e;
+          pv[e] = key < nvalid ? expf(__fsub_rn(__fmul_rn(acc[j][e], scale), mz)) : 0.f;
+          lsum += pv[e];
+        }
+        *(float4*)&sp[wave][r][16 * j + 4 * g] = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        const int key0 = k0 + 16 * j + 4 * g;
+        if (q < P.T && key0 < P.Tp) {
+          const int64_t o = ((int64_t)h * P.T + q) * P.Tp + key0;
+          if (dbg_s) *(float4*)(dbg_s + o) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+          if (dbg_p) *(float4*)(dbg_p + o) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; j++) *(float4*)&sp[wave][r][16 * j + 4 * g] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // code P^ from the wave's own tile (LDS is in order within a wave; no workgroup barrier)
+#pragma unroll
+    for (int pass = 0; pass < 2; pass++) {
+      const int rr = rr0 + 8 * pass;
+      const float4 a = *(const float4*)&sp[wave][rr][kk];
+      const float4 b = *(const float4*)&sp[wave][rr][kk + 4];
+      const float pv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t sh, msub;
+      const uint32_t word = mix45_code8(pv, lane & 3, &sh, &msub);
+      const int qq = q0w + rr, key = k0 + kk;
+      if (qq < P.T && key < P.Tp) {   // Tp is a multiple of 32: quads stay whole
+        const int64_t row = (int64_t)h * P.T + qq;
+        *(uint32_t*)(pc + row * (P.Tp >> 1) + (key >> 1)) = word;
+        if ((lane & 3) == 0) ps[row * (P.Tp >> 5) + (key >> 5)] = (uint16_t)sh;
+      }
+    }
+  }
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (g == 0 && q < P.T) l[(int64_t)h * P.T + q] = lsum;
 }
 
 // ------------------------------------------------------------------ decode: append + q operand
@@ -490,7 +670,8 @@ static PrefillWs prefill_layout(int64_t T, int64_t Hq, int64_t Hkv, int64_t d) {
   w.ks = take((size_t)T * Hkv * (d / 32));
   w.vc = take((size_t)Hkv * d * Tp / 2);
   w.vs = take((size_t)Hkv * d * (Tp / 32));
-  w.s = take((size_t)Hq * T * Tp * 4);
+  // d = 128 takes the fused S passes (row maxima only); other head sizes store S
+  w.s = take(d == 128 ? (size_t)Hq * T * 4 : (size_t)Hq * T * Tp * 4);
   w.pc = take((size_t)Hq * T * Tp / 2);
   w.ps = take((size_t)Hq * T * (Tp / 32) * 2);
   w.l = take((size_t)Hq * T * 4);
@@ -532,6 +713,17 @@ hipError_t attn_prefill_run(const void* q, const void* k, const void* v, int64_t
   HIPCHK(launch_mix_quantize(1, q, 1, T, Hq * d, Hq * d, qc, qs, s));
   HIPCHK(launch_mx_quantize_cols(v, 1, T, Tp, Hkv * d, Hkv * d, vc, vs, Tp / 2, Tp / 32, s));
 
+  const float scale = (float)(1.0 / sqrt((double)d));
+  if (d == 128) {
+    // 3-4. fused: row maxima of S, then S again -> p, l and P^ (S is not stored)
+    PrefillOps P{qc, qs, kc, ks, (int)T, (int)Tp, (int)Hq, (int)Hkv, causal ? 1 : 0};
+    dim3 grid((unsigned)((T + PQ - 1) / PQ), (unsigned)Hq);
+    hipLaunchKernelGGL(k_attn_rowmax, grid, dim3(256), 0, s, P, S);
+    HIPCHK(hipGetLastError());
+    hipLaunchKernelGGL(k_attn_pcode, grid, dim3(256), 0, s, P, (const float*)S, scale, pc, ps, l,
+                       dbg ? dbg->s : nullptr, dbg ? dbg->p : nullptr);
+    HIPCHK(hipGetLastError());
+  } else {
   // 3. S = Q^ K^T per query head
   GemmArgs g1{};
   g1.a_codes = qc; g1.a_shared = qs; g1.a_pitch = Hq * d / 2; g1.a_sh_pitch = Hq * d / 32;
@@ -543,11 +735,12 @@ hipError_t attn_prefill_run(const void* q, const void* k, const void* v, int64_t
   HIPCHK(launch_gemm_mfma(1, 1, 0, g1, s));
 
   // 4. softmax and P^
-  const float scale = (float)(1.0 / sqrt((double)d));
   const int64_t nrows = Hq * T;
   hipLaunchKernelGGL(k_softmax_pquant, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, S, (int)T, (int)Tp, nrows,
                      causal, scale, pc, ps, l, dbg ? dbg->p : nullptr);
   HIPCHK(hipGetLastError());
+  if (dbg && dbg->s) HIPCHK(hipMemcpyAsync(dbg->s, S, (size_t)Hq * T * Tp * 4, hipMemcpyDeviceToDevice, s));
+  }
 
   // 5. O = (P^ V^) / l
   GemmArgs g2{};
@@ -560,7 +753,6 @@ hipError_t attn_prefill_run(const void* q, const void* k, const void* v, int64_t
   HIPCHK(launch_gemm_mfma(1, 1, 1, g2, s));
 
   if (dbg) {
-    if (dbg->s) HIPCHK(hipMemcpyAsync(dbg->s, S, (size_t)Hq * T * Tp * 4, hipMemcpyDeviceToDevice, s));
     if (dbg->p_codes) HIPCHK(hipMemcpyAsync(dbg->p_codes, pc, (size_t)Hq * T * Tp / 2, hipMemcpyDeviceToDevice, s));
     if (dbg->p_shared)
       HIPCHK(hipMemcpyAsync(dbg->p_shared, ps, (size_t)Hq * T * (Tp / 32) * 2, hipMemcpyDeviceToDevice, s));

@@ -114,7 +114,8 @@ def _prefill_stages(g, T, Hq, Hkv, d, causal, rows, heads):
 
 
 @pytest.mark.parametrize("T,Hq,Hkv,d,causal", [(256, 4, 2, 128, True), (200, 2, 1, 64, True), (96, 3, 3, 32, False),
-                                                (640, 7, 1, 128, True)])
+                                                (640, 7, 1, 128, True), (200, 4, 1, 128, True),
+                                                (100, 2, 2, 128, False)])
 def test_prefill_small(T, Hq, Hkv, d, causal):
     g = synth.attention_qkv(T=T, Hq=Hq, Hkv=Hkv, d=d, seed_cfg=4)
     rows = sorted(set([0, 1, 31, 32, T // 2, T - 1] + list(range(0, T, max(1, T // 16)))))
