@@ -196,63 +196,149 @@ __device__ __forceinline__ void q_operand(const PrefillOps& P, int q, int h, int
   qsc = (int)(qrs[g] & 15u) + 119;
 }
 
-// K^ fragments of keys k0 .. k0 + 63 for this lane (keys past T read key T-1; masked later)
-struct KFrag {
-  uint4 kv[4];
-  int ksc[4];
-};
-__device__ __forceinline__ void k_load(const PrefillOps& P, int hk, int k0, int r, int g, KFrag& F) {
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int key = min(k0 + 16 * j + r, P.T - 1);
-    const int64_t krow = (int64_t)key * P.Hkv + hk;
-    F.kv[j] = *(const uint4*)(P.kc + krow * 64 + g * 16);
-    F.ksc[j] = P.ks[krow * 4 + g];
-  }
-}
-// S for the wave's 16 queries and the 64 keys of F
-__device__ __forceinline__ void s_tile(const KFrag& F, const v8i& qf, int qsc, v4f (&acc)[4]) {
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const v8i kf = v8i{(int)F.kv[j].x, (int)F.kv[j].y, (int)F.kv[j].z, (int)F.kv[j].w, 0, 0, 0, 0};
-    acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf, v4f{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, F.ksc[j], 0, qsc);
+// K^ tiles are staged in LDS once per workgroup (its 4 waves use the same 64 keys): a 2-stage ring
+// filled by global_load_lds, the copy of tile t + 1 overlapping the use of tile t. A stage holds
+// 64 keys x 64 code bytes, the 16-byte chunk g of key kl at slot g ^ kswz(kl) so that the 8 or 16
+// lanes an LDS read serves at once hit distinct banks, then the 64 x 4 scale bytes.
+constexpr int KST = PK * 64 + PK * 4;
+__device__ __forceinline__ int kswz(int kl) { return ((kl >> 1) ^ (kl >> 3)) & 3; }
+
+// wave w copies keys 16 w .. 16 w + 15 of the tile at k0 (keys past T repeat key T-1 and are
+// masked later); wave 0 also copies the scales
+__device__ __forceinline__ void k_stage(const PrefillOps& P, int hk, int k0, uint8_t* st) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kl = 16 * wave + (lane >> 2);
+  const int64_t krow = (int64_t)min(k0 + kl, P.T - 1) * P.Hkv + hk;
+  dma16(P.kc + krow * 64 + 16 * ((lane & 3) ^ kswz(kl)), __builtin_amdgcn_readfirstlane(lds_addr(st + wave * 1024)));
+  if (wave == 0) {
+    const int64_t srow = (int64_t)min(k0 + lane, P.T - 1) * P.Hkv + hk;
+    dma4(P.ks + srow * 4, __builtin_amdgcn_readfirstlane(lds_addr(st + PK * 64)));
   }
 }
 
-// Key tiles are visited from a start that rotates with the query tile (the workgroups of a head
-// then read different K^ rows at the same time); the next tile's fragments load while the current
-// one is used. Neither the row maximum nor the codes depend on the order.
-__device__ __forceinline__ int tile_rot(int nt) { return nt > 0 ? (int)(blockIdx.x % (unsigned)nt) : 0; }
+// S for the wave's 16 queries and the 64 keys of stage st
+__device__ __forceinline__ void s_tile(const uint8_t* st, int r, int g, const v8i& qf, int qsc, v4f (&acc)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int kl = 16 * j + r;
+    const uint4 kv = *(const uint4*)(st + kl * 64 + 16 * (g ^ kswz(kl)));
+    const int ksc = st[PK * 64 + kl * 4 + g];
+    const v8i kf = v8i{(int)kv.x, (int)kv.y, (int)kv.z, (int)kv.w, 0, 0, 0, 0};
+    acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf, v4f{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, ksc, 0, qsc);
+  }
+}
 
 // grid (ceil(T / 64), Hq), block 256. smax [Hq, T]: max of S over the unmasked keys of each row.
 __global__ void __launch_bounds__(256) k_attn_rowmax(PrefillOps P, float* __restrict__ smax) {
+  __shared__ __align__(16) uint8_t kst[2][KST];
   const int h = blockIdx.y, hk = h / (P.Hq / P.Hkv);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int q = blockIdx.x * PQ + 16 * wave + r;
+  const int q0w = blockIdx.x * PQ + 16 * wave;
+  const int q = q0w + r;
   v8i qf;
   int qsc;
   q_operand(P, min(q, P.T - 1), h, g, qf, qsc);
   const int nvalid = P.causal ? min(q + 1, P.T) : P.T;
+  const int nfull = P.causal ? min(q0w + 1, P.T) : P.T;               // keys unmasked for all the wave's rows
   const int kend = P.causal ? min(blockIdx.x * PQ + PQ, P.T) : P.T;   // keys any row of the tile sees
+  const int nt = (kend + PK - 1) / PK;
   float mx = -INFINITY;
-  const int nt = (kend + PK - 1) / PK, t0 = tile_rot(nt);
-  KFrag F;
-  if (nt > 0) k_load(P, hk, t0 * PK, r, g, F);
+  if (nt > 0) k_stage(P, hk, 0, kst[0]);
   for (int it = 0; it < nt; it++) {
-    const int k0 = ((t0 + it) % nt) * PK;
+    const int k0 = it * PK;
+    wait_vmcnt<0>();
+    __syncthreads();   // stage it is complete; every wave is done with the other stage
+    if (it + 1 < nt) k_stage(P, hk, k0 + PK, kst[(it + 1) & 1]);
     v4f acc[4];
-    s_tile(F, qf, qsc, acc);
-    if (it + 1 < nt) k_load(P, hk, ((t0 + it + 1) % nt) * PK, r, g, F);
+    s_tile(kst[it & 1], r, g, qf, qsc, acc);
+    if (k0 + PK <= nfull) {
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+      for (int j = 0; j < 4; j++) mx = fmaxf(fmaxf(mx, fmaxf(acc[j][0], acc[j][1])), fmaxf(acc[j][2], acc[j][3]));
+    } else {
 #pragma unroll
-      for (int e = 0; e < 4; e++)
-        if (k0 + 16 * j + 4 * g + e < nvalid) mx = fmaxf(mx, acc[j][e]);
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          if (k0 + 16 * j + 4 * g + e < nvalid) mx = fmaxf(mx, acc[j][e]);
+    }
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   if (g == 0 && q < P.T) smax[(int64_t)h * P.T + q] = mx;
+}
+
+// exp(x) for finite x <= 0: 2^(x log2 e), with x log2 e carried as t + pl (log2 e split into a
+// fp32 head and tail, the product's rounding error recovered exactly with an fma), the integer
+// part of t applied by ldexp and the remaining fraction in [-1/2, 1/2] by the hardware exp2.
+// Within about 2 ulp of the correctly rounded exponential; below exp(-160) the result is 0, as is
+// the fp32 rounding of the exact value.
+__device__ __forceinline__ float exp_nonpos(float x) {
+  constexpr float L_HI = 1.44269502162933349609375f;   // fp32 rounding of log2 e
+  constexpr float L_LO = 1.925963033500011e-08f;       // log2 e - L_HI, rounded
+  x = fmaxf(x, -160.f);
+  const float t = __fmul_rn(x, L_HI);
+  const float pl = __fmaf_rn(x, L_LO, __fmaf_rn(x, L_HI, -t));
+  const float e = __builtin_rintf(t);
+  const float f = __fadd_rn(__fsub_rn(t, e), pl);
+  return __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(f), (int)e);
+}
+
+// MiX-4.5b codes of 8 consecutive softmax weights p = a ++ b (non-negative, this lane's sub-block
+// of a 32-key block whose 4 sub-blocks sit in the 4 lanes of a quad). Emax comes from the block's
+// fp32 maximum and the lane's 3-bit mantissa from its sub-block maximum. Only the rule for
+// non-negative elements applies: on the 16-bit patterns a' of the values rounded up (all
+// thresholds are 16-bit patterns, so the decisions are those on the fp32 values),
+// d* = clamp(((mu0 - a') >> 7) + 1, 0, 7), and d* = 7 codes 0xF above M 2^(Emax-8), else 0x7 (zero).
+// Elements i and i + 4 are coded together as the two halves of a word, whose codes land in
+// nibbles i and i + 4. Returns the code word and sets the block's 16-bit shared field.
+__device__ __forceinline__ uint32_t p_code8(const float4& a, const float4& b, int quad_pos, uint32_t& shared) {
+  const uint32_t x[8] = {f32_bits(a.x), f32_bits(a.y), f32_bits(a.z), f32_bits(a.w),
+                         f32_bits(b.x), f32_bits(b.y), f32_bits(b.z), f32_bits(b.w)};
+  const uint32_t lmax = max(max(max(x[0], x[1]), max(x[2], x[3])), max(max(x[4], x[5]), max(x[6], x[7])));
+  const uint32_t bmax = quad_max_u32(lmax);
+  const int emax = min(max((int)(bmax >> 23) - 127, -7), 8);
+  const uint32_t m = mant3_of(lmax);
+  const uint32_t t3 = 24u + 3u * m;   // mid_0 = 1.5 M 2^(Emax-1) = t3 2^(Emax-5)
+  const uint32_t mu = t3 < 32u ? (((uint32_t)(emax + 126) << 7) | ((t3 << 3) & 0x7Fu))
+                               : (((uint32_t)(emax + 127) << 7) | ((t3 << 2) & 0x7Fu));
+  const uint32_t pb = ((uint32_t)(emax + 119) << 7) | (m << 4);   // M 2^(Emax-8)
+  const i16x2 MU1 = __builtin_bit_cast(i16x2, (mu + 128u) * 0x00010001u);
+  const u16x2 PB2 = __builtin_bit_cast(u16x2, pb * 0x00010001u);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t w = __builtin_amdgcn_perm(x[i + 4] + 0xFFFFu, x[i] + 0xFFFFu, 0x07060302u);
+    i16x2 c = (MU1 - __builtin_bit_cast(i16x2, w)) >> (i16x2)7;
+    c = __builtin_elementwise_min(__builtin_elementwise_max(c, (i16x2)0), (i16x2)7);
+    const u16x2 cu = __builtin_bit_cast(u16x2, c);
+    const u16x2 gt = (PB2 - __builtin_bit_cast(u16x2, w)) >> (u16x2)15;   // a' > pb
+    const u16x2 e7 = (cu + (u16x2)1) >> (u16x2)3;                          // d* == 7
+    const uint32_t c2 = __builtin_bit_cast(uint32_t, cu | ((gt & e7) << (u16x2)3));
+    word |= c2 << (4 * i);
+  }
+  shared = quad_or_u32((quad_pos == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * quad_pos)));
+  return word;
+}
+
+// p = exp(fp32(S scale) - fp32(m scale)) of the lane's 16 scores into the wave's LDS p row, masked
+// keys (key >= nvalid) as 0 unless the whole tile is unmasked (FULL); returns their sum.
+template <bool FULL>
+__device__ __forceinline__ float p_tile(const v4f (&acc)[4], float scale, float mz, int k0, int g, int nvalid,
+                                        float* prow) {
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    float pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      pv[e] = exp_nonpos(__fsub_rn(__fmul_rn(acc[j][e], scale), mz));
+      if (!FULL && k0 + 16 * j + 4 * g + e >= nvalid) pv[e] = 0.f;
+      sum += pv[e];
+    }
+    *(float4*)(prow + 16 * j + 4 * g) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+  }
+  return sum;
 }
 
 // grid (ceil(T / 64), Hq), block 256. P^ codes [Hq, T, Tp/2] and shared [Hq, T, Tp/32] for keys
@@ -264,6 +350,7 @@ __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* _
                                                      float* __restrict__ dbg_p) {
   constexpr int PP = PK + 4;                     // padded LDS row (floats)
   __shared__ __align__(16) float sp[4][16][PP];  // each wave's p tile: 16 rows x 64 keys
+  __shared__ __align__(16) uint8_t kst[2][KST];
   const int h = blockIdx.y, hk = h / (P.Hq / P.Hkv);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -273,44 +360,57 @@ __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* _
   int qsc;
   q_operand(P, min(q, P.T - 1), h, g, qf, qsc);
   const int nvalid = P.causal ? min(q + 1, P.T) : P.T;
+  const int nfull = P.causal ? min(q0w + 1, P.T) : P.T;
   const float mz = q < P.T ? __fmul_rn(smax[(int64_t)h * P.T + min(q, P.T - 1)], scale) : 0.f;
   const int qlast = min(blockIdx.x * PQ + PQ, P.T) - 1;
-  const int kend = P.causal ? qlast + 1 : P.T;                                 // keys with some unmasked entry
+  const int kend = P.causal ? qlast + 1 : P.T;                                    // keys with some unmasked entry
   const int kwrite = P.causal ? min(P.Tp, (qlast + 1 + 255) / 256 * 256) : P.Tp;  // keys whose codes are written
   float lsum = 0.f;
   // read-back role: row rr = lane / 8 (+ 8 per pass), 8 keys kk = 8 (lane % 8); quads are 32-key blocks
   const int rr0 = lane >> 3, kk = 8 * (lane & 7);
-  const int nt = (kwrite + PK - 1) / PK, ntc = (kend + PK - 1) / PK, t0 = tile_rot(ntc);
-  KFrag F;
-  if (ntc > 0) k_load(P, hk, t0 * PK, r, g, F);
-  for (int it = 0; it < nt; it++) {
-    // the ntc tiles with unmasked keys first (rotated), then the all-zero tiles up to kwrite
-    const int kt = it < ntc ? (t0 + it) % ntc : it;
-    const int k0 = kt * PK;
-    if (it < ntc) {
-      v4f acc[4];
-      s_tile(F, qf, qsc, acc);
-      if (it + 1 < ntc) k_load(P, hk, ((t0 + it + 1) % ntc) * PK, r, g, F);
+  const int64_t crow0 = (int64_t)h * P.T + q0w + rr0;   // P^ row of pass 0 (pass 1: + 8)
+  const bool st0 = q0w + rr0 < P.T, st1 = q0w + rr0 + 8 < P.T;
+  // a tile's codes are stored at the start of the next tile (after its barrier) so that the copy
+  // wait before the barrier does not wait for them
+  uint32_t cw[2] = {0, 0}, cs[2] = {0, 0};
+  int kprev = -1;
+  auto store_codes = [&](int key) {   // Tp is a multiple of 32: quads stay whole
+    if (key < P.Tp) {
+#pragma unroll
+      for (int pass = 0; pass < 2; pass++) {
+        if (pass == 0 ? st0 : st1) {
+          const int64_t row = crow0 + 8 * pass;
+          *(uint32_t*)(pc + row * (P.Tp >> 1) + (key >> 1)) = cw[pass];
+          if ((lane & 3) == 0) ps[row * (P.Tp >> 5) + (key >> 5)] = (uint16_t)cs[pass];
+        }
+      }
+    }
+  };
+  const int ntc = (kend + PK - 1) / PK, nt = (kwrite + PK - 1) / PK;
+  if (ntc > 0) k_stage(P, hk, 0, kst[0]);
+  for (int it = 0; it < ntc; it++) {
+    const int k0 = it * PK;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (kprev >= 0) store_codes(kprev);
+    if (it + 1 < ntc) k_stage(P, hk, k0 + PK, kst[(it + 1) & 1]);
+    v4f acc[4];
+    s_tile(kst[it & 1], r, g, qf, qsc, acc);
+    if (k0 + PK <= nfull)
+      lsum += p_tile<true>(acc, scale, mz, k0, g, nvalid, sp[wave][r]);
+    else
+      lsum += p_tile<false>(acc, scale, mz, k0, g, nvalid, sp[wave][r]);
+    if (dbg_s || dbg_p) {
+      const float* prow = sp[wave][r];
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        float pv[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int key = k0 + 16 * j + 4 * g + e;
-          pv[e] = key < nvalid ? expf(__fsub_rn(__fmul_rn(acc[j][e], scale), mz)) : 0.f;
-          lsum += pv[e];
-        }
-        *(float4*)&sp[wave][r][16 * j + 4 * g] = make_float4(pv[0], pv[1], pv[2], pv[3]);
         const int key0 = k0 + 16 * j + 4 * g;
         if (q < P.T && key0 < P.Tp) {
           const int64_t o = ((int64_t)h * P.T + q) * P.Tp + key0;
           if (dbg_s) *(float4*)(dbg_s + o) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
-          if (dbg_p) *(float4*)(dbg_p + o) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+          if (dbg_p) *(float4*)(dbg_p + o) = *(const float4*)(prow + 16 * j + 4 * g);
         }
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; j++) *(float4*)&sp[wave][r][16 * j + 4 * g] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     // code P^ from the wave's own tile (LDS is in order within a wave; no workgroup barrier)
 #pragma unroll
@@ -318,17 +418,15 @@ __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* _
       const int rr = rr0 + 8 * pass;
       const float4 a = *(const float4*)&sp[wave][rr][kk];
       const float4 b = *(const float4*)&sp[wave][rr][kk + 4];
-      const float pv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      uint32_t sh, msub;
-      const uint32_t word = mix45_code8(pv, lane & 3, &sh, &msub);
-      const int qq = q0w + rr, key = k0 + kk;
-      if (qq < P.T && key < P.Tp) {   // Tp is a multiple of 32: quads stay whole
-        const int64_t row = (int64_t)h * P.T + qq;
-        *(uint32_t*)(pc + row * (P.Tp >> 1) + (key >> 1)) = word;
-        if ((lane & 3) == 0) ps[row * (P.Tp >> 5) + (key >> 5)] = (uint16_t)sh;
-      }
+      cw[pass] = p_code8(a, b, lane & 3, cs[pass]);
     }
+    kprev = k0 + kk;
   }
+  if (kprev >= 0) store_codes(kprev);
+  // tiles past every unmasked key of the tile rows: all-zero blocks (codes 0x7, shared field 0)
+  cw[0] = cw[1] = 0x77777777u;
+  cs[0] = cs[1] = 0u;
+  for (int it = ntc; it < nt; it++) store_codes(it * PK + kk);
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
   if (g == 0 && q < P.T) l[(int64_t)h * P.T + q] = lsum;

@@ -55,6 +55,26 @@ __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
   return v > t ? v : t;
 }
 
+// global -> LDS copies (global_load_lds_dword[x4]): lane i's bytes land at LDS byte
+// m0 + size * i. The copy has no destination register; it is written as a statement so that the
+// compiler does not drain every outstanding copy before each LDS read of another stage -- a kernel
+// waits for its copies explicitly (vmcnt) before the barrier that publishes a stage.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
 // Division of a flat index n < 2^31 by a fixed d < 2^31 as a multiply and a shift:
 // q = (n * m) >> sh with sh = 31 + ceil(log2 d), m = ceil(2^sh / d) < 2^33. The error term is below
 // n / 2^sh < 2^-ceil(log2 d) <= 1/d, less than the distance from n/d to the next integer, so q is

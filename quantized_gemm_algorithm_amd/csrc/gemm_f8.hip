@@ -37,7 +37,6 @@
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 namespace mix {
@@ -123,18 +122,6 @@ __device__ __forceinline__ int f8_xcd_tile(int bid, int nt) {
   return x * base + min(x, rem) + idx;
 }
 
-// global -> LDS copies (global_load_lds_dword[x4]): lane i's bytes land at LDS byte
-// m0 + size * i. The copy has no destination register; it is written as a statement so that the
-// compiler does not drain every outstanding copy before each LDS read of another stage -- the
-// kernel waits for its copies explicitly (vmcnt) before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
-
 constexpr int F8_THREADS = 512;   // 8 waves: 4 along M x 2 along N, 64 x 128 outputs each
 
 // Copies of one K step of tile (tm, tn) into stage buffer `st`; each wave copies whole
@@ -184,13 +171,6 @@ __device__ __forceinline__ void f8_issue(const F8Args& g, uint8_t* st, int tm, i
   else
     dma4(g.bs_p + (uint32_t)((ks * g.bs_tn + tn) * 1024 + (wave - 4) * 256 + lane * 4),
          __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::BS_OFF + (wave - 4) * 256)));
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
 typedef int v4i __attribute__((ext_vector_type(4)));
