@@ -228,20 +228,26 @@ __device__ __forceinline__ void s_tile(const uint8_t* st, int r, int g, const v8
   }
 }
 
-// grid (ceil(T / 64), Hq), block 256. smax [Hq, T]: max of S over the unmasked keys of each row.
+// Workgroup -> (query tile, head): heads vary fastest and, with the causal mask, the query tiles
+// run from the last (most keys) to the first, so the longest workgroups start first.
+__device__ __forceinline__ int q_tile(const PrefillOps& P) {
+  return P.causal ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+}
+
+// grid (Hq, ceil(T / 64)), block 256. smax [Hq, T]: max of S over the unmasked keys of each row.
 __global__ void __launch_bounds__(256) k_attn_rowmax(PrefillOps P, float* __restrict__ smax) {
   __shared__ __align__(16) uint8_t kst[2][KST];
-  const int h = blockIdx.y, hk = h / (P.Hq / P.Hkv);
+  const int h = blockIdx.x, hk = h / (P.Hq / P.Hkv), qt = q_tile(P);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int q0w = blockIdx.x * PQ + 16 * wave;
+  const int q0w = qt * PQ + 16 * wave;
   const int q = q0w + r;
   v8i qf;
   int qsc;
   q_operand(P, min(q, P.T - 1), h, g, qf, qsc);
   const int nvalid = P.causal ? min(q + 1, P.T) : P.T;
-  const int nfull = P.causal ? min(q0w + 1, P.T) : P.T;               // keys unmasked for all the wave's rows
-  const int kend = P.causal ? min(blockIdx.x * PQ + PQ, P.T) : P.T;   // keys any row of the tile sees
+  const int nfull = P.causal ? min(q0w + 1, P.T) : P.T;        // keys unmasked for all the wave's rows
+  const int kend = P.causal ? min(qt * PQ + PQ, P.T) : P.T;    // keys any row of the tile sees
   const int nt = (kend + PK - 1) / PK;
   float mx = -INFINITY;
   if (nt > 0) k_stage(P, hk, 0, kst[0]);
@@ -341,7 +347,7 @@ __device__ __forceinline__ float p_tile(const v4f (&acc)[4], float scale, float 
   return sum;
 }
 
-// grid (ceil(T / 64), Hq), block 256. P^ codes [Hq, T, Tp/2] and shared [Hq, T, Tp/32] for keys
+// grid (Hq, ceil(T / 64)), block 256. P^ codes [Hq, T, Tp/2] and shared [Hq, T, Tp/32] for keys
 // [0, min(Tp, round_up(i + 1, 256))) of row i (all Tp without the mask; masked keys code as zero),
 // l [Hq, T]; optional S and p dumps [Hq, T, Tp].
 __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* __restrict__ smax, float scale,
@@ -351,10 +357,10 @@ __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* _
   constexpr int PP = PK + 4;                     // padded LDS row (floats)
   __shared__ __align__(16) float sp[4][16][PP];  // each wave's p tile: 16 rows x 64 keys
   __shared__ __align__(16) uint8_t kst[2][KST];
-  const int h = blockIdx.y, hk = h / (P.Hq / P.Hkv);
+  const int h = blockIdx.x, hk = h / (P.Hq / P.Hkv), qt = q_tile(P);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int q0w = blockIdx.x * PQ + 16 * wave;   // the wave's first query row
+  const int q0w = qt * PQ + 16 * wave;   // the wave's first query row
   const int q = q0w + r;
   v8i qf;
   int qsc;
@@ -362,7 +368,7 @@ __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* _
   const int nvalid = P.causal ? min(q + 1, P.T) : P.T;
   const int nfull = P.causal ? min(q0w + 1, P.T) : P.T;
   const float mz = q < P.T ? __fmul_rn(smax[(int64_t)h * P.T + min(q, P.T - 1)], scale) : 0.f;
-  const int qlast = min(blockIdx.x * PQ + PQ, P.T) - 1;
+  const int qlast = min(qt * PQ + PQ, P.T) - 1;
   const int kend = P.causal ? qlast + 1 : P.T;                                    // keys with some unmasked entry
   const int kwrite = P.causal ? min(P.Tp, (qlast + 1 + 255) / 256 * 256) : P.Tp;  // keys whose codes are written
   float lsum = 0.f;
@@ -815,7 +821,7 @@ hipError_t attn_prefill_run(const void* q, const void* k, const void* v, int64_t
   if (d == 128) {
     // 3-4. fused: row maxima of S, then S again -> p, l and P^ (S is not stored)
     PrefillOps P{qc, qs, kc, ks, (int)T, (int)Tp, (int)Hq, (int)Hkv, causal ? 1 : 0};
-    dim3 grid((unsigned)((T + PQ - 1) / PQ), (unsigned)Hq);
+    dim3 grid((unsigned)Hq, (unsigned)((T + PQ - 1) / PQ));
     hipLaunchKernelGGL(k_attn_rowmax, grid, dim3(256), 0, s, P, S);
     HIPCHK(hipGetLastError());
     hipLaunchKernelGGL(k_attn_pcode, grid, dim3(256), 0, s, P, (const float*)S, scale, pc, ps, l,

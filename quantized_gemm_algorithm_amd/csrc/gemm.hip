@@ -127,10 +127,15 @@ template <int A_FMT, int B_FP4, int C_BF16>
 __global__ void __launch_bounds__(256, 2) k_gemm_mfma(GemmArgs g) {
   __shared__ Smem<B_FP4> S;
   const int tiles_n = (g.N + BN - 1) / BN;
-  const int tile = blockIdx.x;
+  int tile = blockIdx.x, batch = blockIdx.z;
+  if (g.causal == 2) {
+    // K ranges grow with the row tile: the last row tiles of every batch entry run first
+    const int lin = blockIdx.z * gridDim.x + blockIdx.x;
+    batch = lin % g.batch;
+    tile = gridDim.x - 1 - lin / g.batch;
+  }
   const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int batch = blockIdx.z;
   if (g.causal == 1 && n0 > m0 + BM - 1) return;
   int kend = g.K;
   if (g.causal == 2) kend = min(g.K, m0 + BM);
