@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time only hipBLASLt (torch._scaled_mm) on the prefill linear shape, as context")
     return ap.parse_args()
 
 
@@ -415,6 +417,51 @@ def calibrate_copy(torch):
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}))
 
 
+def vendor_gemm(torch, args):
+    """hipBLASLt through torch._scaled_mm on the prefill linear shape (M=4096, N=18944, K=3584, bf16
+    out): tensorwise FP8, block-scaled MXFP8 (E8M0 per 32) and MXFP4 x MXFP4. Context for the
+    block-scaled MFMA GEMM's roofline, not part of the step."""
+    M, K, N = 4096, 3584, 18944
+    dev = "cuda"
+    flop = 2.0 * M * N * K
+    gen = torch.Generator(device=dev).manual_seed(0)
+
+    def timeit(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        return {"us": ms * 1e3, "TFLOP/s": flop / ms / 1e9}
+
+    out = {"workload": "vendor_gemm_4096x18944x3584", "library": "hipBLASLt via torch._scaled_mm"}
+    a = (torch.randn(M, K, device=dev, generator=gen) * 0.5).to(torch.float8_e4m3fn)
+    b = (torch.randn(N, K, device=dev, generator=gen) * 0.5).to(torch.float8_e4m3fn)
+    one = torch.tensor(1.0, device=dev)
+    e8 = torch.float8_e8m0fnu
+    sa = torch.full((M, K // 32), 127, dtype=torch.uint8, device=dev).view(e8)
+    sb = torch.full((N, K // 32), 127, dtype=torch.uint8, device=dev).view(e8)
+    cases = {
+        "fp8_tensorwise": lambda: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16),
+        "mxfp8": lambda: torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16),
+    }
+    a4 = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=dev, generator=gen).view(torch.float4_e2m1fn_x2)
+    b4 = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev, generator=gen).view(torch.float4_e2m1fn_x2)
+    cases["mxfp4"] = lambda: torch._scaled_mm(a4, b4.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+    for name, fn in cases.items():
+        try:
+            out[name] = timeit(fn)
+        except Exception as e:  # a format this torch/hipBLASLt build does not offer
+            out[name] = {"error": repr(e)[:200]}
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -427,6 +474,9 @@ def main():
         sys.exit(1)
     if args.calibrate_copy:
         calibrate_copy(torch)
+        return
+    if args.vendor_gemm:
+        vendor_gemm(torch, args)
         return
     import quantized_gemm_algorithm_amd as q
     q._lib_()  # fail loudly if the HIP library is missing

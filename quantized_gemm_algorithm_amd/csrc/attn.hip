@@ -438,111 +438,129 @@ __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* _
   if (g == 0 && q < P.T) l[(int64_t)h * P.T + q] = lsum;
 }
 
-// ------------------------------------------------------------------ decode: append + q operand
-
-// grid (Hkv, B), block 128 (one thread per channel; requires d == 128 and G = Hq/Hkv <= 16).
-// 1. The MFMA operand of the G query rows of this KV head: MiX-4.5b along the head dimension,
-//    as E4M3 bytes qi8 [B*Hq, 128] with per-block E8M0 scales 2^(Emax-1) qis [B*Hq, 4].
-// 2. The new key, MXFP4 of fp32(k - mu) along the head dimension, into slot pos.
-// 3. The new value into the staging rows, and the value block that holds pos re-coded along tokens
-//    from the staged tokens present (zero for the rest).
-__global__ void __launch_bounds__(128) k_decode_prep(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
-                                                     const uint16_t* __restrict__ v_new, const float* __restrict__ mu,
-                                                     const int32_t* __restrict__ pos, int64_t max_pos, int Hq, int Hkv,
-                                                     int64_t Lmax, uint8_t* __restrict__ kc, uint8_t* __restrict__ ks,
-                                                     uint8_t* __restrict__ vc, uint8_t* __restrict__ vs,
-                                                     uint16_t* __restrict__ stage, uint8_t* __restrict__ qi8,
-                                                     uint8_t* __restrict__ qis) {
-  constexpr int d = 128;
-  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  const int G = Hq / Hkv;
-  const int p = pos[b];
-  if (p < 0 || p > max_pos) return;
-  const int64_t bh = (int64_t)b * Hkv + h;
-  // loads first: the key and value channel, the 32 staged values of the block, q
-  const uint32_t kraw = k_new[bh * d + c];
-  const float muc = mu[bh * d + c];
-  const int slot = p & 31;
-  const uint16_t vnew = v_new[bh * d + c];
-  uint32_t st[32];
-#pragma unroll
-  for (int s = 0; s < 32; s++) st[s] = stage[(((int64_t)b * 32 + s) * Hkv + h) * d + c];
-  // 1. q operand: thread -> (row r0 + c / 16, 8-element sub-block c % 16); quads are blocks
-  for (int r0 = 0; r0 < G; r0 += 8) {
-    const int row = r0 + (c >> 4), sb = c & 15;
-    if (row < G) {
-      const int64_t qrow = (int64_t)b * Hq + (int64_t)h * G + row;
-      const uint4 v = *(const uint4*)(q + qrow * d + sb * 8);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-      int emax;
-      uint32_t m;
-      const uint32_t word = mix_quant_lane_bf16<1>(w4, emax, m);
-      uint32_t e0, e1;
-      mix8_to_e4m3(word, m, e0, e1);
-      *(uint2*)(qi8 + qrow * d + sb * 8) = make_uint2(e0, e1);
-      if ((sb & 3) == 0) qis[qrow * 4 + (sb >> 2)] = (uint8_t)(emax + 126);
-    }
-  }
-  // 2. key: MXFP4 of fp32(k - mu) along the head dimension (32-channel blocks = half waves)
-  float kx = __fsub_rn(__uint_as_float(kraw << 16), muc);
-  uint32_t kb = f32_bits(kx);
-  uint32_t amax = kb & 0x7FFFFFFFu;
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) {
-    uint32_t o = (uint32_t)__shfl_xor((int)amax, off, 32);
-    amax = o > amax ? o : amax;
-  }
-  int X = mx_exponent(amax, 1);
-  uint32_t nib = amax ? fp4_code(kb, fp4_thresholds(X)) : 0u;
-  uint32_t nxt = (uint32_t)__shfl_down((int)nib, 1, 32);
-  const int64_t krow = bh * Lmax + p;
-  if ((c & 1) == 0) kc[krow * (d >> 1) + (c >> 1)] = (uint8_t)(nib | (nxt << 4));
-  if ((c & 31) == 0) ks[krow * (d >> 5) + (c >> 5)] = amax ? (uint8_t)(X + 127) : (uint8_t)0;
-  // 3. value: stage, then code the block along tokens
-  stage[(((int64_t)b * 32 + slot) * Hkv + h) * d + c] = vnew;
-  uint32_t vb[32];
-  uint32_t vmax = 0;
-#pragma unroll
-  for (int s = 0; s < 32; s++) {
-    const uint32_t u = s < slot ? st[s] << 16 : (s == slot ? (uint32_t)vnew << 16 : 0u);
-    vb[s] = u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    vmax = a > vmax ? a : vmax;
-  }
-  int XV = mx_exponent(vmax, 1);
-  uint32_t w[4] = {0, 0, 0, 0};
-  if (vmax) {
-    Fp4Thr r = fp4_thresholds(XV);
-#pragma unroll
-    for (int s = 0; s < 32; s++) w[s >> 3] |= fp4_code(vb[s], r) << (4 * (s & 7));
-  }
-  const int64_t vrow = bh * d + c;
-  *(uint4*)(vc + vrow * (Lmax >> 1) + (p >> 5) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-  vs[vrow * (Lmax >> 5) + (p >> 5)] = vmax ? (uint8_t)(XV + 127) : (uint8_t)0;
-}
-
 // ------------------------------------------------------------------ decode: scores (pass 1)
+//
+// Decode attends the G = Hq/Hkv query rows of each (sequence b, KV head h) over keys [0, pos[b]]
+// in chunks of DCH keys: pass 1 (one workgroup per chunk, one more that appends the new key and
+// value) codes the query rows and writes S and the chunk maxima; pass 2 turns S into p and P^ with the row
+// maximum over all chunks and multiplies P^ by V^ (the chunk partials); a third pass sums the
+// partials into O.
 
 constexpr int DCH = 256;  // keys per chunk
 
-// grid (nchunk, Hkv, B), block 256 (4 waves x 64 keys). Requires d == 128 and G = Hq/Hkv <= 16.
-// S [B, Hq, Lp] fp32 for keys <= pos; pmax [B, Hq, nchunk]. Cache rows past pos are never used:
-// their loads are clamped to row pos and their products discarded.
-__global__ void __launch_bounds__(256) k_decode_scores(const uint8_t* __restrict__ qi8, const uint8_t* __restrict__ qis,
-                                                        const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks,
-                                                        const int32_t* __restrict__ pos, int64_t max_pos, int Hq,
-                                                        int Hkv, int64_t Lmax, int64_t Lp, int nchunk,
-                                                        float* __restrict__ S, float* __restrict__ pmax) {
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+// Decode workgroup -> (chunk, KV head h, sequence b) over a 1-D grid of 8 per ceil(B Hkv / 8)
+// workgroups, per workgroups for each (b, h). Workgroups are spread over the 8 XCDs round-robin, so the chunks of one (b, h) get
+// ids equal modulo 8: they run on one XCD and share its L2 for the per-channel value scales (one
+// 128-byte line serves 16 chunks), the chunk maxima and the S rows pass 2 reads back.
+struct DecWg {
+  int chunk, h, b;
+  bool valid;
+};
+__device__ __forceinline__ DecWg dec_wg(int per, int Hkv, int B) {
+  const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+  const int bh = x + 8 * (i / per);
+  DecWg w;
+  w.chunk = i % per;
+  w.b = bh / Hkv;
+  w.h = bh - w.b * Hkv;
+  w.valid = bh < B * Hkv;
+  return w;
+}
+
+// The new key of a (sequence, KV head): MXFP4 of fp32(k - mu) along the head dimension, thread c
+// of the first two waves holding channel c (a 32-channel block is half a wave). Even threads get
+// the code byte of channels (c, c + 1); threads 0, 32, 64, 96 also the block's E8M0 scale.
+__device__ __forceinline__ void new_key_code(uint32_t kraw, float muc, uint32_t& byte, uint32_t& scale) {
+  const uint32_t kb = f32_bits(__fsub_rn(__uint_as_float(kraw << 16), muc));
+  uint32_t amax = kb & 0x7FFFFFFFu;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off, 32));
+  const int X = mx_exponent(amax, 1);
+  const uint32_t nib = amax ? fp4_code(kb, fp4_thresholds(X)) : 0u;
+  byte = nib | ((uint32_t)__shfl_down((int)nib, 1, 32) << 4);
+  scale = amax ? (uint32_t)(X + 127) : 0u;
+}
+
+// grid 8 (nchunk + 1) ceil(B Hkv / 8) (dec_wg over nchunk + 1 workgroups per (b, h)), block 256.
+// Requires d == 128 and G <= 16. Workgroup `nchunk` of (b, h) appends the new token to the cache:
+// the new key's codes into slot pos; the new value into the staging rows and the value block that
+// holds pos re-coded along tokens from the staged tokens present (zero for the rest). The others,
+// one per chunk of 256 keys (4 waves x 64 keys):
+// 1. code the G query rows of this KV head: MiX-4.5b along the head dimension, decoded to the
+//    MFMA's E4M3 operand (per-block E8M0 scale 2^(Emax-1)) in LDS;
+// 2. the chunk that holds pos codes the new key too and uses it in place of the slot's contents;
+// 3. write S [B, Hq, Lp] fp32 for keys <= pos and the chunk maxima pmax [B, Hq, nchunk]. Cache rows
+//    past pos are never used: their loads are clamped to row pos and their products discarded.
+__global__ void __launch_bounds__(256) k_decode_qk(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
+                                                    const uint16_t* __restrict__ v_new, const float* __restrict__ mu,
+                                                    const int32_t* __restrict__ pos, int64_t max_pos, int Hq, int Hkv,
+                                                    int64_t Lmax, uint8_t* __restrict__ kc, uint8_t* __restrict__ ks,
+                                                    uint8_t* __restrict__ vc, uint8_t* __restrict__ vs,
+                                                    uint16_t* __restrict__ stage, int64_t Lp, int B,
+                                                    int nchunk, float* __restrict__ S, float* __restrict__ pmax) {
+  constexpr int d = 128;
+  const DecWg wg = dec_wg(nchunk + 1, Hkv, B);
+  if (!wg.valid) return;
+  const int h = wg.h, b = wg.b;
   const int p = pos[b];
-  if (p < 0 || p > max_pos || chunk * DCH > p) return;
-  const int G = Hq / Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15, g = lane >> 4;
-  __shared__ float smax[4][16];
+  if (p < 0 || p > max_pos) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t bh = (int64_t)b * Hkv + h;
 
-  // K fragments of the wave's 4 groups of 16 keys (issued first)
+  if (wg.chunk == nchunk) {
+    // append: loads first (key channel, mean, value channel, the 16 staged rows of this thread)
+    const int c = tid >> 1, half = tid & 1, slot = p & 31;
+    const uint32_t kraw = k_new[bh * d + (tid & (d - 1))];
+    const float muc = mu[bh * d + (tid & (d - 1))];
+    const uint16_t vnew = v_new[bh * d + c];
+    uint32_t u[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) u[i] = stage[(((int64_t)b * 32 + 16 * half + i) * Hkv + h) * d + c];
+    if (tid < d) {
+      uint32_t byte, sc;
+      new_key_code(kraw, muc, byte, sc);
+      const int64_t krow = bh * Lmax + p;
+      if ((tid & 1) == 0) kc[krow * (d >> 1) + (tid >> 1)] = (uint8_t)byte;
+      if ((tid & 31) == 0) ks[krow * (d >> 5) + (tid >> 5)] = (uint8_t)sc;
+    }
+    // value: thread -> (channel c, tokens [16 half, +16) of the block)
+    uint32_t vmax = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int s2 = 16 * half + i;
+      u[i] = s2 < slot ? u[i] << 16 : (s2 == slot ? (uint32_t)vnew << 16 : 0u);
+      vmax = max(vmax, u[i] & 0x7FFFFFFFu);
+    }
+    vmax = max(vmax, (uint32_t)__shfl_xor((int)vmax, 1, 64));
+    if (half == (slot >> 4)) stage[(((int64_t)b * 32 + slot) * Hkv + h) * d + c] = vnew;
+    const int XV = mx_exponent(vmax, 1);
+    uint32_t w0 = 0, w1 = 0;
+    if (vmax) {
+      const Fp4Thr thr = fp4_thresholds(XV);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        w0 |= fp4_code(u[i], thr) << (4 * i);
+        w1 |= fp4_code(u[8 + i], thr) << (4 * i);
+      }
+    }
+    const int64_t vrow = bh * d + c;
+    *(uint2*)(vc + vrow * (Lmax >> 1) + (p >> 5) * 16 + 8 * half) = make_uint2(w0, w1);
+    if (half == 0) vs[vrow * (Lmax >> 5) + (p >> 5)] = vmax ? (uint8_t)(XV + 127) : (uint8_t)0;
+    return;
+  }
+
+  const int chunk = wg.chunk;
+  if (chunk * DCH > p) return;
+  const int G = Hq / Hkv;
+  const int r = lane & 15, g = lane >> 4;
+  const bool owner = chunk == p / DCH;
+  __shared__ float smax[4][16];
+  __shared__ __align__(16) uint8_t sq[16][d];   // query rows as E4M3
+  __shared__ uint8_t sqs[16][4];                // their E8M0 block scales
+  __shared__ __align__(16) uint8_t snk[d / 2];  // the new key's codes
+  __shared__ uint8_t snks[d / 32];
+
+  // loads first: K fragments of the wave's 4 groups of 16 keys, the query sub-block, the new key
   uint4 kv[4];
   int ksc[4];
 #pragma unroll
@@ -551,13 +569,37 @@ __global__ void __launch_bounds__(256) k_decode_scores(const uint8_t* __restrict
     kv[t] = *(const uint4*)(kc + (bh * Lmax + j) * 64 + g * 16);
     ksc[t] = ks[(bh * Lmax + j) * 4 + g];
   }
-  // A operand: the G query rows of this KV head (E4M3 split: bytes [16 g, +16) and [64 + 16 g, +16))
+  const int qr = tid >> 4, qsb = tid & 15;   // query row, 8-element sub-block (quads are blocks)
+  const uint4 qv = *(const uint4*)(q + ((int64_t)b * Hq + (int64_t)h * G + min(qr, G - 1)) * d + qsb * 8);
+  const uint32_t kraw = k_new[bh * d + (tid & (d - 1))];
+  const float muc = mu[bh * d + (tid & (d - 1))];
+  // 1. query operand
+  if (qr < G) {
+    const uint32_t w4[4] = {qv.x, qv.y, qv.z, qv.w};
+    int emax;
+    uint32_t m;
+    const uint32_t word = mix_quant_lane_bf16<1>(w4, emax, m);
+    uint32_t e0, e1;
+    mix8_to_e4m3(word, m, e0, e1);
+    *(uint2*)&sq[qr][qsb * 8] = make_uint2(e0, e1);
+    if ((qsb & 3) == 0) sqs[qr][qsb >> 2] = (uint8_t)(emax + 126);
+  }
+  // 2. new key
+  if (owner && tid < d) {
+    uint32_t byte, sc;
+    new_key_code(kraw, muc, byte, sc);
+    if ((tid & 1) == 0) snk[tid >> 1] = (uint8_t)byte;
+    if ((tid & 31) == 0) snks[tid >> 5] = (uint8_t)sc;
+  }
+  __syncthreads();
+
+  // A operand: query row r (rows past G repeat row G-1; their results are discarded), bytes
+  // [16 g, +16) and [64 + 16 g, +16)
   const int rq = min(r, G - 1);
-  const int64_t qrow = (int64_t)b * Hq + (int64_t)h * G + rq;
-  const uint4 qlo = *(const uint4*)(qi8 + qrow * 128 + 16 * g);
-  const uint4 qhi = *(const uint4*)(qi8 + qrow * 128 + 64 + 16 * g);
+  const uint4 qlo = *(const uint4*)&sq[rq][16 * g];
+  const uint4 qhi = *(const uint4*)&sq[rq][64 + 16 * g];
   const v8i af = v8i{(int)qlo.x, (int)qlo.y, (int)qlo.z, (int)qlo.w, (int)qhi.x, (int)qhi.y, (int)qhi.z, (int)qhi.w};
-  const int sa = qis[qrow * 4 + g];
+  const int sa = sqs[rq][g];
 
   float rmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -565,6 +607,10 @@ __global__ void __launch_bounds__(256) k_decode_scores(const uint8_t* __restrict
     const int j0 = chunk * DCH + wave * 64 + t * 16;
     const int j = j0 + r;
     const bool live = j <= p;
+    if (owner && j == p) {
+      kv[t] = *(const uint4*)&snk[16 * g];
+      ksc[t] = snks[g];
+    }
     const v8i bf = live ? v8i{(int)kv[t].x, (int)kv[t].y, (int)kv[t].z, (int)kv[t].w, 0, 0, 0, 0}
                         : v8i{0, 0, 0, 0, 0, 0, 0, 0};
     const int sb = live ? ksc[t] : 127;
@@ -573,9 +619,9 @@ __global__ void __launch_bounds__(256) k_decode_scores(const uint8_t* __restrict
     // result register i: query row 4 g + i, key j0 + r
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      int qr = 4 * g + i;
-      if (qr < G && live) {
-        S[((int64_t)b * Hq + (int64_t)h * G + qr) * Lp + j] = acc[i];
+      const int row = 4 * g + i;
+      if (row < G && live) {
+        S[((int64_t)b * Hq + (int64_t)h * G + row) * Lp + j] = acc[i];
         rmax[i] = fmaxf(rmax[i], acc[i]);
       }
     }
@@ -591,124 +637,152 @@ __global__ void __launch_bounds__(256) k_decode_scores(const uint8_t* __restrict
     for (int i = 0; i < 4; i++) smax[wave][4 * g + i] = rmax[i];
   }
   __syncthreads();
-  if (threadIdx.x < G) {
-    float v = fmaxf(fmaxf(smax[0][threadIdx.x], smax[1][threadIdx.x]), fmaxf(smax[2][threadIdx.x], smax[3][threadIdx.x]));
-    pmax[((int64_t)b * Hq + (int64_t)h * G + threadIdx.x) * nchunk + chunk] = v;
+  if (tid < G) {
+    const float v = fmaxf(fmaxf(smax[0][tid], smax[1][tid]), fmaxf(smax[2][tid], smax[3][tid]));
+    pmax[((int64_t)b * Hq + (int64_t)h * G + tid) * nchunk + chunk] = v;
   }
 }
 
-// ------------------------------------------------------------------ decode: p, P^ and P^ V^ (pass 2)
+// ------------------------------------------------------------------ decode: p, P^, P^ V^, O (pass 2)
 
-// grid (nchunk, Hkv, B), block 256. P^ codes [B, Hq, Lp/2], shared [B, Hq, Lp/32];
-// lpart [B, Hq, nchunk]; opart [B, Hq, nchunk, 128].
-__global__ void __launch_bounds__(256) k_decode_pv(const float* __restrict__ S, const float* __restrict__ pmax,
+// The chunk's value codes in LDS: 128 channel rows of 128 bytes (the chunk's 8 blocks of 32
+// tokens), the 16-byte block j of channel ch at slot j ^ vswz(ch) so that the 8 or 16 lanes an LDS
+// read serves at once hit distinct banks.
+__device__ __forceinline__ int vswz(int ch) { return (ch ^ (ch >> 3)) & 7; }
+
+// LDS bytes of k_decode_pv: the value tile, then P^ as E4M3 [G][DCH] and its scales [G][DCH/32],
+// then the row maxima
+inline size_t decode_pv_lds_bytes(int G) { return 128 * 128 + (size_t)G * DCH + (size_t)G * (DCH / 32) + 16 * 4; }
+
+// grid 8 nchunk ceil(B Hkv / 8) (dec_wg), block 256, LDS decode_pv_lds_bytes(G). P^ codes
+// [B, Hq, Lp/2], shared [B, Hq, Lp/32]; chunk partials lpart [B, Hq, nchunk], opart [B, Hq, nchunk, 128].
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) k_decode_pv(const float* __restrict__ S, const float* __restrict__ pmax,
                                                     const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
                                                     const int32_t* __restrict__ pos, int64_t max_pos, int Hq, int Hkv,
-                                                    int64_t Lmax, int64_t Lp, int nchunk, float scale,
+                                                    int64_t Lmax, int64_t Lp, int B, int nchunk, float scale,
                                                     uint8_t* __restrict__ pc, uint16_t* __restrict__ ps,
                                                     float* __restrict__ lpart, float* __restrict__ opart,
                                                     float* __restrict__ dbg_p) {
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int p = pos[b];
-  if (p < 0 || p > max_pos || chunk * DCH > p) return;
+  constexpr int d = 128;
+  extern __shared__ __align__(16) uint8_t dsm[];
+  const DecWg wg = dec_wg(nchunk, Hkv, B);
+  if (!wg.valid) return;
+  const int chunk = wg.chunk, h = wg.h, b = wg.b;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = pos[b];
+  if (p < 0 || p > max_pos || chunk * DCH > p) return;
   const int r = lane & 15, g = lane >> 4;
   const int64_t bh = (int64_t)b * Hkv + h;
-  __shared__ float sm[16];
-  __shared__ uint8_t sP[16][DCH];  // P^ as E4M3, row-major; rows >= G stay zero
-  __shared__ uint8_t sPs[16][DCH / 32];
+  uint8_t* sV = dsm;                                   // [128][128] value codes
+  uint8_t* sP = dsm + 128 * 128;                       // [G][DCH] P^ as E4M3
+  uint8_t* sPs = sP + G * DCH;                         // [G][DCH/32] its scales
+  float* sm = (float*)(((uintptr_t)(sPs + G * (DCH / 32)) + 3) & ~(uintptr_t)3);   // [16] scaled row maxima
 
-  // V fragments of this chunk (issued first): wave w handles channel tiles 2w, 2w+1 (16 channels
-  // each); blocks past the newest token are clamped to its block and their products discarded
-  uint4 vv[DCH / 128][2];
+  // loads first. Value codes -> LDS: wave w copies channel rows 32 w .. 32 w + 31, 8 per copy
+  // (lane -> row + lane / 8, slot lane % 8); blocks past the newest token are clamped to its block
+  // and their products discarded
+  const int pb = p >> 5;
+#pragma unroll
+  for (int it = 0; it < 4; it++) {
+    const int row0 = 32 * wave + 8 * it, ch = row0 + (lane >> 3), slot = lane & 7;
+    const int kb = min(chunk * (DCH / 32) + (slot ^ vswz(ch)), pb);
+    dma16(vc + (bh * d + ch) * (Lmax >> 1) + kb * 16, __builtin_amdgcn_readfirstlane(lds_addr(sV + row0 * 128)));
+  }
+  // value scales of the wave's channel tiles 2w, 2w+1 (16 channels each), K steps k2, blocks g
   int vsc[DCH / 128][2];
 #pragma unroll
   for (int k2 = 0; k2 < DCH / 128; k2++) {
     const int kb = min(chunk * DCH + k2 * 128 + 32 * g, p) >> 5;
 #pragma unroll
-    for (int t = 0; t < 2; t++) {
-      const int ch = (2 * wave + t) * 16 + r;
-      vv[k2][t] = *(const uint4*)(vc + (bh * 128 + ch) * (Lmax >> 1) + kb * 16);
-      vsc[k2][t] = vs[(bh * 128 + ch) * (Lmax >> 5) + kb];
-    }
+    for (int t = 0; t < 2; t++) vsc[k2][t] = vs[(bh * d + (2 * wave + t) * 16 + r) * (Lmax >> 5) + kb];
   }
-  // global row max over the chunks that hold keys <= pos: 16 threads per row
+  // S of the thread's (row, 8 keys): thread -> (row = tid / 32 + 8 pass, sub-block = tid % 32);
+  // the first pass's values are loaded here, a second pass (G > 8) loads its own
+  const int sbk = tid & 31, jb = chunk * DCH + sbk * 8;
+  auto load_s = [&](int row, float (&v)[8]) {
+    const float* sp = S + ((int64_t)b * Hq + (int64_t)h * G + row) * Lp + jb;
+    const float4 s0 = *(const float4*)sp;
+    const float4 s1 = *(const float4*)(sp + 4);
+    v[0] = s0.x; v[1] = s0.y; v[2] = s0.z; v[3] = s0.w;
+    v[4] = s1.x; v[5] = s1.y; v[6] = s1.z; v[7] = s1.w;
+  };
+  float sv[8];
+  load_s(min(tid >> 5, G - 1), sv);   // rows past G load row G-1 (not used)
+  // chunk maxima: 16 threads per row, the first two loads clamped to the last live chunk (repeats
+  // do not change a maximum)
   const int last = p / DCH;
-  {
-    const int row = tid >> 4, part = tid & 15;
-    float v = -INFINITY;
-    if (row < G) {
-      const float* pm = pmax + ((int64_t)b * Hq + (int64_t)h * G + row) * nchunk;
-      for (int c = part; c <= last; c += 16) v = fmaxf(v, pm[c]);
-    }
+  const int mrow = min(tid >> 4, G - 1), part = tid & 15;
+  const float* pm = pmax + ((int64_t)b * Hq + (int64_t)h * G + mrow) * nchunk;
+  float pmv = fmaxf(pm[min(part, last)], pm[min(part + 16, last)]);
+  for (int c = part + 32; c <= last; c += 16) pmv = fmaxf(pmv, pm[c]);
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    if (part == 0) sm[row] = __fmul_rn(v, scale);
-  }
-  for (int i = tid; i < 16 * DCH / 4; i += 256) ((uint32_t*)sP)[i] = 0u;
-  for (int i = tid; i < 16 * DCH / 32; i += 256) ((uint8_t*)sPs)[i] = 127;
+  for (int off = 1; off < 16; off <<= 1) pmv = fmaxf(pmv, __shfl_xor(pmv, off, 64));
+  if ((tid & 15) == 0 && (tid >> 4) < G) sm[tid >> 4] = __fmul_rn(pmv, scale);
   __syncthreads();
 
-  // p and P^: thread -> (row = tid / 32, sub-block = tid % 32); 8 rows per pass
-  for (int r0 = 0; r0 < G; r0 += 8) {
-    const int row = r0 + (tid >> 5), sb = tid & 31;
+  // p and P^
+#pragma unroll
+  for (int pass = 0; pass < 2; pass++) {
+    const int row = 8 * pass + (tid >> 5);
     if (row < G) {  // 32 threads per row: whole quads
+      if (pass == 1) load_s(row, sv);
       const int64_t qrow = (int64_t)b * Hq + (int64_t)h * G + row;
-      const int jb = chunk * DCH + sb * 8;
-      const float4 s0 = *(const float4*)(S + qrow * Lp + jb);
-      const float4 s1 = *(const float4*)(S + qrow * Lp + jb + 4);
-      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
       const float m = sm[row];
       float pv[8];
       float lsum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        const int j = jb + e;
-        float v = 0.f;
-        if (j <= p) v = expf(__fsub_rn(__fmul_rn(sv[e], scale), m));
-        pv[e] = v;
-        lsum += v;
+        const float v = exp_nonpos(__fsub_rn(__fmul_rn(sv[e], scale), m));
+        pv[e] = jb + e <= p ? v : 0.f;
+        lsum += pv[e];
       }
-      uint32_t shf, msub;
-      uint32_t word = mix45_code8(pv, sb & 3, &shf, &msub);
+      uint32_t shf;
+      const uint32_t word = p_code8(make_float4(pv[0], pv[1], pv[2], pv[3]), make_float4(pv[4], pv[5], pv[6], pv[7]),
+                                    sbk & 3, shf);
       *(uint32_t*)(pc + qrow * (Lp >> 1) + (jb >> 1)) = word;
-      if ((sb & 3) == 0) {
+      if ((sbk & 3) == 0) {
         ps[qrow * (Lp >> 5) + (jb >> 5)] = (uint16_t)shf;
-        sPs[row][sb >> 2] = (uint8_t)((shf & 15u) + 119u);
+        sPs[row * (DCH / 32) + (sbk >> 2)] = (uint8_t)((shf & 15u) + 119u);
       }
       uint32_t e0, e1;
-      mix8_to_e4m3(word, msub, e0, e1);
-      *(uint2*)(&sP[row][sb * 8]) = make_uint2(e0, e1);
+      mix8_to_e4m3(word, (shf >> (4 + 3 * (sbk & 3))) & 7u, e0, e1);
+      *(uint2*)(sP + row * DCH + sbk * 8) = make_uint2(e0, e1);
       if (dbg_p) {
-        float* d = dbg_p + qrow * Lp + jb;
-        *(float4*)d = make_float4(pv[0], pv[1], pv[2], pv[3]);
-        *(float4*)(d + 4) = make_float4(pv[4], pv[5], pv[6], pv[7]);
+        float* dp = dbg_p + qrow * Lp + jb;
+        *(float4*)dp = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        *(float4*)(dp + 4) = make_float4(pv[4], pv[5], pv[6], pv[7]);
       }
       // l partial: sum over the 32 threads of this row (half a wave)
 #pragma unroll
       for (int off = 16; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off, 32);
-      if (sb == 0) lpart[qrow * nchunk + chunk] = lsum;
+      if (sbk == 0) lpart[qrow * nchunk + chunk] = lsum;
     }
   }
+  wait_vmcnt<0>();   // this wave's value copies have landed
   __syncthreads();
 
-  // O partial = P^ V^ over this chunk
+  // O partial = P^ V^ over this chunk (A operand: P^ row r; rows past G repeat row G-1, their
+  // results are discarded)
   v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int k2 = 0; k2 < DCH / 128; k2++) {
     const int kbase = chunk * DCH + k2 * 128;  // first key of this K step
     if (kbase > p) break;
-    uint4 lo = *(const uint4*)(&sP[r][k2 * 128 + 16 * g]);
-    uint4 hi = *(const uint4*)(&sP[r][k2 * 128 + 64 + 16 * g]);
-    v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    int sa = sPs[r][k2 * 4 + g];
+    const int pr = min(r, G - 1);
+    const uint4 lo = *(const uint4*)(sP + pr * DCH + k2 * 128 + 16 * g);
+    const uint4 hi = *(const uint4*)(sP + pr * DCH + k2 * 128 + 64 + 16 * g);
+    const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    const int sa = sPs[pr * (DCH / 32) + k2 * 4 + g];
     const bool blk_live = kbase + 32 * g <= p;
 #pragma unroll
     for (int t = 0; t < 2; t++) {
-      const v8i bf = blk_live ? v8i{(int)vv[k2][t].x, (int)vv[k2][t].y, (int)vv[k2][t].z, (int)vv[k2][t].w, 0, 0, 0, 0}
+      const int ch = (2 * wave + t) * 16 + r, j = k2 * 4 + g;
+      const uint4 vf = *(const uint4*)(sV + ch * 128 + 16 * (j ^ vswz(ch)));
+      const int vscale = vsc[k2][t];
+      const v8i bf = blk_live ? v8i{(int)vf.x, (int)vf.y, (int)vf.z, (int)vf.w, 0, 0, 0, 0}
                               : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      const int sb = blk_live ? vsc[k2][t] : 127;
+      const int sb = blk_live ? vscale : 127;
       acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc[t], 0, 4, 0, sa, 0, sb);
     }
   }
@@ -717,14 +791,15 @@ __global__ void __launch_bounds__(256) k_decode_pv(const float* __restrict__ S, 
     const int ch = (2 * wave + t) * 16 + r;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      int row = 4 * g + i;
-      if (row < G) opart[(((int64_t)b * Hq + (int64_t)h * G + row) * nchunk + chunk) * 128 + ch] = acc[t][i];
+      const int row = 4 * g + i;
+      if (row < G) opart[(((int64_t)b * Hq + (int64_t)h * G + row) * nchunk + chunk) * d + ch] = acc[t][i];
     }
   }
 }
 
-// grid (B * Hq), block d: O = sum_chunks O_part / sum_chunks l_part, rounded to bf16. Four
-// independent partial sums keep the chunk loads in flight together.
+// grid (B * Hq), block d: O = sum_chunks O_part / sum_chunks l_part, rounded to bf16 (rows whose
+// pos is outside [0, max_pos]: zeros). Four independent partial sums keep the chunk loads in
+// flight together.
 __global__ void k_decode_combine(const float* __restrict__ lpart, const float* __restrict__ opart,
                                  const int32_t* __restrict__ pos, int64_t max_pos, int Hq, int nchunk, int d,
                                  uint16_t* __restrict__ o, float* __restrict__ dbg_l) {
@@ -736,18 +811,20 @@ __global__ void k_decode_combine(const float* __restrict__ lpart, const float* _
     return;
   }
   const int n = p / DCH + 1;
+  const float* lp = lpart + qrow * nchunk;
+  const float* op = opart + qrow * nchunk * d + c;
   float l4[4] = {0.f, 0.f, 0.f, 0.f}, a4[4] = {0.f, 0.f, 0.f, 0.f};
   int k = 0;
   for (; k + 4 <= n; k += 4) {
 #pragma unroll
     for (int u = 0; u < 4; u++) {
-      l4[u] += lpart[qrow * nchunk + k + u];
-      a4[u] += opart[(qrow * nchunk + k + u) * d + c];
+      l4[u] += lp[k + u];
+      a4[u] += op[(int64_t)(k + u) * d];
     }
   }
   for (; k < n; k++) {
-    l4[0] += lpart[qrow * nchunk + k];
-    a4[0] += opart[(qrow * nchunk + k) * d + c];
+    l4[0] += lp[k];
+    a4[0] += op[(int64_t)k * d];
   }
   const float l = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   const float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
@@ -885,7 +962,7 @@ hipError_t kv_cache_prefill_run(const mix_kv_cache_t* c, int64_t b, const void* 
 }
 
 struct DecodeWs {
-  size_t qi8, qis, s, pmax, pc, ps, lpart, opart, total;
+  size_t s, pmax, pc, ps, lpart, opart, total;
 };
 
 static DecodeWs decode_layout(int64_t B, int64_t Hq, int64_t d, int64_t max_pos, int64_t* Lp_out, int* nchunk_out) {
@@ -894,8 +971,6 @@ static DecodeWs decode_layout(int64_t B, int64_t Hq, int64_t d, int64_t max_pos,
   DecodeWs w{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  w.qi8 = take((size_t)B * Hq * d);
-  w.qis = take((size_t)B * Hq * (d / 32));
   w.s = take((size_t)B * Hq * Lp * 4);
   w.pmax = take((size_t)B * Hq * nchunk * 4);
   w.pc = take((size_t)B * Hq * Lp / 2);
@@ -920,8 +995,6 @@ hipError_t attn_decode_run(const void* q, const void* k_new, const void* v_new, 
   int nchunk;
   DecodeWs w = decode_layout(B, Hq, d, max_pos, &Lp, &nchunk);
   uint8_t* base = (uint8_t*)ws;
-  uint8_t* qi8 = base + w.qi8;
-  uint8_t* qis = base + w.qis;
   float* S = (float*)(base + w.s);
   float* pmax = (float*)(base + w.pmax);
   uint8_t* pc = base + w.pc;
@@ -929,20 +1002,20 @@ hipError_t attn_decode_run(const void* q, const void* k_new, const void* v_new, 
   float* lpart = (float*)(base + w.lpart);
   float* opart = (float*)(base + w.opart);
 
-  hipLaunchKernelGGL(k_decode_prep, dim3((unsigned)Hkv, (unsigned)B), dim3(128), 0, s, (const uint16_t*)q,
-                     (const uint16_t*)k_new, (const uint16_t*)v_new, mu, pos, max_pos, (int)Hq, (int)Hkv, Lmax,
-                     c->k_codes, c->k_scales, c->v_codes, c->v_scales, (uint16_t*)c->v_stage, qi8, qis);
-  HIPCHK(hipGetLastError());
-  dim3 grid((unsigned)nchunk, (unsigned)Hkv, (unsigned)B);
-  hipLaunchKernelGGL(k_decode_scores, grid, dim3(256), 0, s, qi8, qis, c->k_codes, c->k_scales, pos, max_pos, (int)Hq,
-                     (int)Hkv, Lmax, Lp, nchunk, S, pmax);
+  const unsigned bh8 = (unsigned)((B * Hkv + 7) / 8);
+  const dim3 grid_qk(8u * (unsigned)(nchunk + 1) * bh8), grid((unsigned)(8 * nchunk) * bh8);
+  hipLaunchKernelGGL(k_decode_qk, grid_qk, dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)k_new,
+                     (const uint16_t*)v_new, mu, pos, max_pos, (int)Hq, (int)Hkv, Lmax, c->k_codes, c->k_scales,
+                     c->v_codes, c->v_scales, (uint16_t*)c->v_stage, Lp, (int)B, nchunk, S, pmax);
   HIPCHK(hipGetLastError());
   const float scale = (float)(1.0 / sqrt((double)d));
-  hipLaunchKernelGGL(k_decode_pv, grid, dim3(256), 0, s, S, pmax, c->v_codes, c->v_scales, pos, max_pos, (int)Hq,
-                     (int)Hkv, Lmax, Lp, nchunk, scale, pc, ps, lpart, opart, dbg ? dbg->p : nullptr);
+  hipLaunchKernelGGL(k_decode_pv, grid, dim3(256), decode_pv_lds_bytes((int)(Hq / Hkv)), s, (const float*)S,
+                     (const float*)pmax,
+                     (const uint8_t*)c->v_codes, (const uint8_t*)c->v_scales, pos, max_pos, (int)Hq, (int)Hkv, Lmax, Lp,
+                     (int)B, nchunk, scale, pc, ps, lpart, opart, dbg ? dbg->p : nullptr);
   HIPCHK(hipGetLastError());
-  hipLaunchKernelGGL(k_decode_combine, dim3((unsigned)(B * Hq)), dim3((unsigned)d), 0, s, lpart, opart, pos, max_pos,
-                     (int)Hq, nchunk, (int)d, (uint16_t*)o, dbg ? dbg->l : nullptr);
+  hipLaunchKernelGGL(k_decode_combine, dim3((unsigned)(B * Hq)), dim3((unsigned)d), 0, s, (const float*)lpart,
+                     (const float*)opart, pos, max_pos, (int)Hq, nchunk, (int)d, (uint16_t*)o, dbg ? dbg->l : nullptr);
   HIPCHK(hipGetLastError());
   if (dbg) {
     if (dbg->s) HIPCHK(hipMemcpyAsync(dbg->s, S, (size_t)B * Hq * Lp * 4, hipMemcpyDeviceToDevice, s));
