@@ -577,10 +577,8 @@ __global__ void __launch_bounds__(256) k_decode_qk(const uint16_t* __restrict__ 
   if (qr < G) {
     const uint32_t w4[4] = {qv.x, qv.y, qv.z, qv.w};
     int emax;
-    uint32_t m;
-    const uint32_t word = mix_quant_lane_bf16<1>(w4, emax, m);
-    uint32_t e0, e1;
-    mix8_to_e4m3(word, m, e0, e1);
+    uint32_t m, e0, e1;
+    mix_quant_lane_bf16_img<1, true>(w4, emax, m, e0, e1);
     *(uint2*)&sq[qr][qsb * 8] = make_uint2(e0, e1);
     if ((qsb & 3) == 0) sqs[qr][qsb >> 2] = (uint8_t)(emax + 126);
   }

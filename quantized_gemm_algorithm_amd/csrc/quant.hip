@@ -83,13 +83,13 @@ __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ 
     for (int u = 0; u < MQ_R; u++) {
       const int64_t row = r0 + u;
       int emax;
-      uint32_t m;
+      uint32_t m, e0, e1;   // e0, e1: the sub-block's 8 E4M3 image bytes (IMG)
       uint32_t word;
       if (DT == 1) {
         const uint32_t w4[4] = {xb[u][0], xb[u][1], xb[u][2], xb[u][3]};
-        word = mix_quant_lane_bf16<FMT>(w4, emax, m);
+        word = mix_quant_lane_bf16_img<FMT, IMG != 0>(w4, emax, m, e0, e1);
       } else {
-        word = mix_quant_lane<FMT>(xb[u], emax, m);
+        word = mix_quant_lane_img<FMT, IMG != 0>(xb[u], emax, m, e0, e1);
       }
       uint32_t f = 0;
       if (FMT == 1) f = quad_or_u32((q == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * q)));
@@ -103,8 +103,6 @@ __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ 
         }
       }
       if (IMG) {
-        uint32_t e0, e1;
-        mix8_to_e4m3(word, m, e0, e1);
         *(uint2*)(a8 + row * cols + scc * 8) = make_uint2(e0, e1);
         if (q == 0) {
           const int rin = (int)(row & (FT - 1));

@@ -49,71 +49,106 @@ __device__ __forceinline__ uint32_t mix_code(uint32_t xbits, const MixThresholds
 
 // The same decision for bf16 inputs, two elements per 32-bit operation. Every threshold has at
 // most 6 significant bits and stays in the normal range, so it is exact in bf16 (its fp32 pattern
-// has 16 low zero bits) and the comparisons run on 16-bit patterns: with d = mu0 - a as a signed
-// 16-bit difference, #{d' : mid_d' >= a} = clamp((d >> 7) + 1, 0, 7) (7 mantissa bits). The sign
-// and zero rules become bit selects. x holds element 2i in its low half and 2i+1 in its high half;
-// the result holds their 4-bit codes in bits 0..3 and 16..19.
+// has 16 low zero bits) and the comparisons run on 16-bit patterns a (sign cleared) of the two
+// halves. With mid_0 the pattern of 1.5 M 2^(Emax-1), cnt = #{d : mid_d >= a} =
+// clamp(((mid_0 + 128 - a) >> 7), 0, 7) as a signed 16-bit shift (7 mantissa bits). A negative
+// element has no value below c_6, so its index is v = min(cnt, 7 - s) for the sign s; it is zero
+// (code 0x7) when a <= the midpoint of its last value and 0, M 2^(Emax-8) + s 2^(Emax-8) (one
+// exponent step higher for negatives); otherwise its code is (s << 3) | v, the positive v = 7
+// (the reclaimed step) giving 0xF. The E4M3 byte of a nonzero element is
+// (s << 7) | ((8 - v) << 3) | m = 64 + m + 128 s - 8 v, and 0 for zero.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t mix_code2_bf16(uint32_t x, uint32_t MU2, uint32_t PB2, uint32_t NB2) {
-  const uint32_t a = x & 0x7FFF7FFFu;
-  i16x2 c = ((__builtin_bit_cast(i16x2, MU2) - __builtin_bit_cast(i16x2, a)) >> (i16x2)7) + (i16x2)1;
-  c = __builtin_elementwise_min(__builtin_elementwise_max(c, (i16x2)0), (i16x2)7);
-  const uint32_t cnt = __builtin_bit_cast(uint32_t, c);
-  // [a > pos_bottom], [a > neg_bottom]: the sign bit of the 16-bit difference
-  const uint32_t gtp =
-      (__builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, PB2) - __builtin_bit_cast(u16x2, a)) >> 15) & 0x00010001u;
-  const uint32_t gtn =
-      (__builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, NB2) - __builtin_bit_cast(u16x2, a)) >> 15) & 0x00010001u;
-  // positives: cnt, except cnt == 7 -> 0xF above pos_bottom, else 0x7
-  const uint32_t eq7 = ((cnt + 0x00010001u) >> 3) & 0x00010001u;
-  const uint32_t pos = cnt | ((gtp & eq7) << 3);
-  // negatives: 8 | cnt for cnt < 6, else 0xE above neg_bottom, else 0x7
-  const uint32_t s6 = ((cnt + 0x00020002u) >> 3) & 0x00010001u;
-  const uint32_t hi = 0x00070007u + (gtn << 3) - gtn;
-  const uint32_t lo = cnt | 0x00080008u;
-  const uint32_t m6 = __builtin_bit_cast(uint32_t, (u16x2)0 - __builtin_bit_cast(u16x2, s6));
-  const uint32_t negc = (hi & m6) | (lo & ~m6);
-  const uint32_t nz = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), (u16x2)1));
-  const uint32_t neg = (x >> 15) & 0x00010001u & nz;
-  const uint32_t mn = __builtin_bit_cast(uint32_t, (u16x2)0 - __builtin_bit_cast(u16x2, neg));
-  return (negc & mn) | (pos & ~mn);
+// per-block constants of the pair coder, both halves equal
+struct MixPk {
+  uint32_t mu1;   // mid_0 pattern + 128
+  uint32_t pb;    // pattern of M 2^(Emax-8)
+  uint32_t m64;   // 64 + m (E4M3 byte of a positive element with v = 0)
+};
+__device__ __forceinline__ MixPk mix_pk(int emax, uint32_t m) {
+  const uint32_t t3 = 24u + 3u * m;   // mid_0 = 1.5 M 2^(Emax-1) = t3 2^(Emax-5)
+  const uint32_t mu = t3 < 32u ? (((uint32_t)(emax + 126) << 7) | ((t3 << 3) & 0x7Fu))
+                               : (((uint32_t)(emax + 127) << 7) | ((t3 << 2) & 0x7Fu));
+  MixPk k;
+  k.mu1 = (mu + 128u) * 0x00010001u;
+  k.pb = (((uint32_t)(emax + 119) << 7) | (m << 4)) * 0x00010001u;
+  k.m64 = (64u + m) * 0x00010001u;
+  return k;
+}
+
+// Two elements (bf16 patterns, element 2i in the low half of x) -> their codes in bits 0..3 and
+// 16..19; with IMG also their E4M3 bytes in bits 0..7 and 16..23 of img.
+template <bool IMG>
+__device__ __forceinline__ uint32_t mix_pair(uint32_t x, const MixPk& k, uint32_t& img) {
+  const u16x2 a = __builtin_bit_cast(u16x2, x & 0x7FFF7FFFu);
+  const u16x2 s = __builtin_bit_cast(u16x2, x) >> (u16x2)15;
+  i16x2 c = (__builtin_bit_cast(i16x2, k.mu1) - __builtin_bit_cast(i16x2, a)) >> (i16x2)7;
+  c = __builtin_elementwise_max(c, (i16x2)0);
+  const u16x2 v = __builtin_elementwise_min(__builtin_bit_cast(u16x2, c), (u16x2)7 - s);
+  const u16x2 zthr = s * (u16x2)128 + __builtin_bit_cast(u16x2, k.pb);
+  const u16x2 nz = (zthr - a) >> (u16x2)15;                        // a above the zero threshold
+  const u16x2 w = s * (u16x2)8 + v;
+  const uint32_t cnz = __builtin_bit_cast(uint32_t, w) | (__builtin_bit_cast(uint32_t, w + (u16x2)1) & 0x00080008u);
+  const uint32_t mask = __builtin_bit_cast(uint32_t, nz * (u16x2)0xFF);
+  if (IMG) {
+    const u16x2 byte = v * (u16x2)0xFFF8 + (s * (u16x2)128 + __builtin_bit_cast(u16x2, k.m64));
+    img = __builtin_bit_cast(uint32_t, byte) & mask;
+  }
+  return (cnz & mask) | (0x00070007u & ~mask);
 }
 
 // The 8 nibbles of a sub-block from its 16-bit patterns (two per word, element 2i in the low half
-// of w[i]) and the block's Emax and mantissa m. The thresholds as 16-bit patterns (all normal):
-// mid_0 = 1.5 M 2^(Emax-1) = t3 2^(Emax-5) with t3 = 3 (8 + m), pos_bottom = M 2^(Emax-8),
-// neg_bottom = M 2^(Emax-7).
-__device__ __forceinline__ uint32_t mix_code8_packed(const uint32_t (&w)[4], int emax, uint32_t m) {
-  const uint32_t t3 = 24u + 3u * m;
-  const uint32_t mu = t3 < 32u ? (((uint32_t)(emax + 126) << 7) | ((t3 << 3) & 0x7Fu))
-                               : (((uint32_t)(emax + 127) << 7) | ((t3 << 2) & 0x7Fu));
-  const uint32_t pb = ((uint32_t)(emax + 119) << 7) | (m << 4);
-  const uint32_t nb = ((uint32_t)(emax + 120) << 7) | (m << 4);
-  uint32_t word = 0;
+// of w[i]) and the block's constants; with IMG also the 8 E4M3 bytes in element order.
+template <bool IMG>
+__device__ __forceinline__ uint32_t mix_code8_pk(const uint32_t (&w)[4], const MixPk& k, uint32_t& out0,
+                                                 uint32_t& out1) {
+  uint32_t t[4], im[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const uint32_t c2 = mix_code2_bf16(w[i], mu * 0x00010001u, pb * 0x00010001u, nb * 0x00010001u);
-    word |= ((c2 & 0xFu) | ((c2 >> 12) & 0xF0u)) << (8 * i);
+    const uint32_t c2 = mix_pair<IMG>(w[i], k, im[i]);
+    t[i] = c2 | (c2 >> 12);   // byte 0: element 2i's nibble, then element 2i + 1's
   }
-  return word;
+  if (IMG) {
+    out0 = __builtin_amdgcn_perm(im[1], im[0], 0x06040200u);
+    out1 = __builtin_amdgcn_perm(im[3], im[2], 0x06040200u);
+  }
+  return __builtin_amdgcn_perm(t[1], t[0], 0x0C0C0400u) | __builtin_amdgcn_perm(t[3], t[2], 0x04000C0Cu);
 }
 
-// mix_quant_lane for 8 bf16 elements held two per word (element 2i in the low half of w[i]).
-template <int FMT>
-__device__ __forceinline__ uint32_t mix_quant_lane_bf16(const uint32_t (&w)[4], int& emax, uint32_t& m) {
+__device__ __forceinline__ uint32_t mix_code8_packed(const uint32_t (&w)[4], int emax, uint32_t m) {
+  uint32_t o0, o1;
+  return mix_code8_pk<false>(w, mix_pk(emax, m), o0, o1);
+}
+
+// Block max of a quad of lanes (one 32-element block) through DPP quad permutes
+__device__ __forceinline__ uint32_t quad_max_dpp(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true)); // quad_perm [2,3,0,1]
+}
+
+// mix_quant_lane for 8 bf16 elements held two per word (element 2i in the low half of w[i]); with
+// IMG also the 8 E4M3 image bytes.
+template <int FMT, bool IMG>
+__device__ __forceinline__ uint32_t mix_quant_lane_bf16_img(const uint32_t (&w)[4], int& emax, uint32_t& m,
+                                                            uint32_t& out0, uint32_t& out1) {
   const u16x2 a01 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu),
                                               __builtin_bit_cast(u16x2, w[1] & 0x7FFF7FFFu));
   const u16x2 a23 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[2] & 0x7FFF7FFFu),
                                               __builtin_bit_cast(u16x2, w[3] & 0x7FFF7FFFu));
   const u16x2 am = __builtin_elementwise_max(a01, a23);
   const uint32_t lmax = (uint32_t)(am[0] > am[1] ? am[0] : am[1]) << 16;
-  const uint32_t bmax = quad_max_u32(lmax);
+  const uint32_t bmax = quad_max_dpp(lmax);
   const int e = (int)(bmax >> 23) - 127;   // an all-zero block gives -127, clamped to -7
   emax = e < -7 ? -7 : (e > 8 ? 8 : e);
   m = mant3_of(FMT == 1 ? lmax : bmax);
-  return mix_code8_packed(w, emax, m);
+  return mix_code8_pk<IMG>(w, mix_pk(emax, m), out0, out1);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t mix_quant_lane_bf16(const uint32_t (&w)[4], int& emax, uint32_t& m) {
+  uint32_t o0, o1;
+  return mix_quant_lane_bf16_img<FMT, false>(w, emax, m, o0, o1);
 }
 
 // One lane's share of a MiX block: the lane holds 8 consecutive elements (fp32 bit patterns) and
@@ -121,18 +156,16 @@ __device__ __forceinline__ uint32_t mix_quant_lane_bf16(const uint32_t (&w)[4], 
 // Returns the 8 nibbles (element e at bits 4e) and sets the block's Emax (clamped to [-7, 8]) and
 // this lane's 3-bit shared mantissa m (its sub-block's for MiX-4.5b, the block's for MiX-4.25b).
 // Emax and m come from the exact fp32 maxima. The element decisions compare against thresholds
-// that are 16-bit patterns (see mix_code2_bf16), and for such a threshold t and |x| = a,
+// that are 16-bit patterns (see mix_pair), and for such a threshold t and |x| = a,
 // a > t exactly when ceil(a / 2^16) > t / 2^16; so the elements are coded by the packed coder on
 // their patterns rounded up to 16 bits, with the same result as mix_code on the fp32 patterns.
-template <int FMT>  // 0 = MiX-4.25b, 1 = MiX-4.5b
-__device__ __forceinline__ uint32_t mix_quant_lane(const uint32_t (&xb)[8], int& emax, uint32_t& m) {
+template <int FMT, bool IMG>  // FMT 0 = MiX-4.25b, 1 = MiX-4.5b
+__device__ __forceinline__ uint32_t mix_quant_lane_img(const uint32_t (&xb)[8], int& emax, uint32_t& m,
+                                                       uint32_t& out0, uint32_t& out1) {
   uint32_t lmax = 0;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const uint32_t a = xb[i] & 0x7FFFFFFFu;
-    lmax = a > lmax ? a : lmax;
-  }
-  const uint32_t bmax = quad_max_u32(lmax);
+  for (int i = 0; i < 8; i++) lmax = max(lmax, xb[i] & 0x7FFFFFFFu);
+  const uint32_t bmax = quad_max_dpp(lmax);
   const int e = (int)(bmax >> 23) - 127;   // an all-zero block gives -127, clamped to -7
   emax = e < -7 ? -7 : (e > 8 ? 8 : e);
   m = mant3_of(FMT == 1 ? lmax : bmax);
@@ -144,7 +177,13 @@ __device__ __forceinline__ uint32_t mix_quant_lane(const uint32_t (&xb)[8], int&
     const uint32_t h1 = ((x1 >> 16) & 0x8000u) | (((x1 & 0x7FFFFFFFu) + 0xFFFFu) >> 16);
     w[i] = h0 | (h1 << 16);
   }
-  return mix_code8_packed(w, emax, m);
+  return mix_code8_pk<IMG>(w, mix_pk(emax, m), out0, out1);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t mix_quant_lane(const uint32_t (&xb)[8], int& emax, uint32_t& m) {
+  uint32_t o0, o1;
+  return mix_quant_lane_img<FMT, false>(xb, emax, m, o0, o1);
 }
 
 // MXFP4 code of one element, thresholds at the E2M1 midpoints times 2^X, ties to the even code.
