@@ -58,6 +58,11 @@ __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ 
                                                         uint8_t* __restrict__ codes, void* __restrict__ shared,
                                                         uint8_t* __restrict__ a8, uint8_t* __restrict__ as_p,
                                                         int tiles_m) {
+  __shared__ uint4 pk_tbl[128];   // block constants of the pair coder per (Emax, m)
+  if (DT == 1) {
+    mix_pk_table_fill(pk_tbl);
+    __syncthreads();
+  }
   const int spr = (int)(cols >> 3);                       // sub-blocks per row
   const int sc = blockIdx.x * blockDim.x + threadIdx.x;   // this lane's sub-block in the row
   // whole quads are in or out of range together (spr and the chunk size are multiples of 4)
@@ -87,12 +92,12 @@ __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ 
       uint32_t word;
       if (DT == 1) {
         const uint32_t w4[4] = {xb[u][0], xb[u][1], xb[u][2], xb[u][3]};
-        word = mix_quant_lane_bf16_img<FMT, IMG != 0>(w4, emax, m, e0, e1);
+        word = mix_quant_lane_bf16_tbl<FMT, IMG != 0>(w4, pk_tbl, emax, m, e0, e1);
       } else {
         word = mix_quant_lane_img<FMT, IMG != 0>(xb[u], emax, m, e0, e1);
       }
       uint32_t f = 0;
-      if (FMT == 1) f = quad_or_u32((q == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * q)));
+      if (FMT == 1) f = quad_or_dpp((q == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * q)));
       if (!col_ok || row >= rows) continue;
       if (!IMG || codes) {
         *(uint32_t*)(codes + row * (cols >> 1) + scc * 4) = word;

@@ -78,7 +78,9 @@ __device__ __forceinline__ MixPk mix_pk(int emax, uint32_t m) {
 }
 
 // Two elements (bf16 patterns, element 2i in the low half of x) -> their codes in bits 0..3 and
-// 16..19; with IMG also their E4M3 bytes in bits 0..7 and 16..23 of img.
+// 16..19; with IMG also their E4M3 bytes in bits 0..7 and 16..23 of img. nzm is all ones in a half
+// whose element lies above its zero threshold; a zero element takes w = 7, and bit 3 is added where
+// w + 1 reaches 8 (the positive reclaimed step; negatives have it already).
 template <bool IMG>
 __device__ __forceinline__ uint32_t mix_pair(uint32_t x, const MixPk& k, uint32_t& img) {
   const u16x2 a = __builtin_bit_cast(u16x2, x & 0x7FFF7FFFu);
@@ -86,16 +88,15 @@ __device__ __forceinline__ uint32_t mix_pair(uint32_t x, const MixPk& k, uint32_
   i16x2 c = (__builtin_bit_cast(i16x2, k.mu1) - __builtin_bit_cast(i16x2, a)) >> (i16x2)7;
   c = __builtin_elementwise_max(c, (i16x2)0);
   const u16x2 v = __builtin_elementwise_min(__builtin_bit_cast(u16x2, c), (u16x2)7 - s);
-  const u16x2 zthr = s * (u16x2)128 + __builtin_bit_cast(u16x2, k.pb);
-  const u16x2 nz = (zthr - a) >> (u16x2)15;                        // a above the zero threshold
-  const u16x2 w = s * (u16x2)8 + v;
-  const uint32_t cnz = __builtin_bit_cast(uint32_t, w) | (__builtin_bit_cast(uint32_t, w + (u16x2)1) & 0x00080008u);
-  const uint32_t mask = __builtin_bit_cast(uint32_t, nz * (u16x2)0xFF);
-  if (IMG) {
-    const u16x2 byte = v * (u16x2)0xFFF8 + (s * (u16x2)128 + __builtin_bit_cast(u16x2, k.m64));
-    img = __builtin_bit_cast(uint32_t, byte) & mask;
-  }
-  return (cnz & mask) | (0x00070007u & ~mask);
+  const u16x2 s7 = s << (u16x2)7;
+  const uint32_t nzm = __builtin_bit_cast(
+      uint32_t, (__builtin_bit_cast(i16x2, s7 + __builtin_bit_cast(u16x2, k.pb)) - __builtin_bit_cast(i16x2, a)) >>
+                    (i16x2)15);
+  const uint32_t w = __builtin_bit_cast(uint32_t, (s << (u16x2)3) | v);
+  const uint32_t wz = (w & nzm) | (0x00070007u & ~nzm);
+  if (IMG) img = __builtin_bit_cast(uint32_t, s7 + __builtin_bit_cast(u16x2, k.m64) - (v << (u16x2)3)) & nzm;
+  return wz | (__builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, wz) - __builtin_bit_cast(u16x2, nzm)) &
+               0x00080008u);
 }
 
 // The 8 nibbles of a sub-block from its 16-bit patterns (two per word, element 2i in the low half
@@ -143,6 +144,46 @@ __device__ __forceinline__ uint32_t mix_quant_lane_bf16_img(const uint32_t (&w)[
   emax = e < -7 ? -7 : (e > 8 ? 8 : e);
   m = mant3_of(FMT == 1 ? lmax : bmax);
   return mix_code8_pk<IMG>(w, mix_pk(emax, m), out0, out1);
+}
+
+// The block constants for every (Emax, m): entry (Emax + 7) * 8 + m = {mu1, pb, m64, 0}; a
+// workgroup fills its copy in LDS once.
+__device__ __forceinline__ void mix_pk_table_fill(uint4* tbl) {
+  for (int t = threadIdx.x; t < 128; t += blockDim.x) {
+    const MixPk k = mix_pk((t >> 3) - 7, (uint32_t)t & 7u);
+    tbl[t] = make_uint4(k.mu1, k.pb, k.m64, 0u);
+  }
+}
+__device__ __forceinline__ MixPk mix_pk_lookup(const uint4* tbl, int emax, uint32_t m) {
+  const uint4 e = tbl[(emax + 7) * 8 + (int)m];
+  MixPk k;
+  k.mu1 = e.x;
+  k.pb = e.y;
+  k.m64 = e.z;
+  return k;
+}
+
+// As mix_quant_lane_bf16_img with the block constants looked up in a filled table.
+template <int FMT, bool IMG>
+__device__ __forceinline__ uint32_t mix_quant_lane_bf16_tbl(const uint32_t (&w)[4], const uint4* tbl, int& emax,
+                                                            uint32_t& m, uint32_t& out0, uint32_t& out1) {
+  const u16x2 a01 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu),
+                                              __builtin_bit_cast(u16x2, w[1] & 0x7FFF7FFFu));
+  const u16x2 a23 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[2] & 0x7FFF7FFFu),
+                                              __builtin_bit_cast(u16x2, w[3] & 0x7FFF7FFFu));
+  const u16x2 am = __builtin_elementwise_max(a01, a23);
+  const uint32_t lmax = (uint32_t)(am[0] > am[1] ? am[0] : am[1]) << 16;
+  const uint32_t bmax = quad_max_dpp(lmax);
+  const int e = (int)(bmax >> 23) - 127;
+  emax = e < -7 ? -7 : (e > 8 ? 8 : e);
+  m = mant3_of(FMT == 1 ? lmax : bmax);
+  return mix_code8_pk<IMG>(w, mix_pk_lookup(tbl, emax, m), out0, out1);
+}
+
+// OR over a quad of lanes through DPP quad permutes
+__device__ __forceinline__ uint32_t quad_or_dpp(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);
+  return v | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);
 }
 
 template <int FMT>
