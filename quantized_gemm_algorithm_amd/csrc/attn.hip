@@ -8,13 +8,17 @@
 // dimension and along keys); smoothed K and V as MXFP4 (cached operands, blocks along the head
 // dimension and along tokens).
 //
-// Prefill is unfused: quantizers, then S = Q^ K^T on the block-scaled MFMA GEMM, then one wave
-// per query row computes z = fp32(S) * fp32(1/sqrt(d)), the exact row max, p = exp(z - m),
-// l = sum p and P^ = MiX-4.5b(p) along keys, then O = (P^ V^)/l on the same GEMM.
+// Prefill (d = 128) codes the operands, then makes two passes over S without storing it: pass 1
+// finds each query row's exact maximum (the P^ codes depend on it), pass 2 recomputes S tile by
+// tile, forms z = fp32(S) * fp32(1/sqrt(d)), p = exp(z - m), l = sum p and P^ = MiX-4.5b(p) along
+// keys, and accumulates P^ V^ on the MFMA; O = (P^ V^)/l. Other head sizes take the unfused path:
+// S on the block-scaled MFMA GEMM, one wave per query row for p and P^, O on the same GEMM.
 //
 // Decode keeps the exact global row max with two passes over the keys: pass 1 (scores) computes S
 // for 256-key chunks on the MFMA and per-chunk maxima; pass 2 (pv) takes the global max, forms p
 // and P^ for its chunk and multiplies by V^ on the MFMA; a final kernel sums the chunk partials.
+#include <type_traits>
+
 #include "../../include/mixlib.h"
 #include "common.h"
 #include "kernels.h"
@@ -175,7 +179,9 @@ struct PrefillOps {
   const uint16_t* qs;    // Q^ shared fields [T, Hq, d/32]
   const uint8_t* kc;     // K^ codes [T, Hkv, d/2]
   const uint8_t* ks;     // K^ scales [T, Hkv, d/32]
-  int T, Tp, Hq, Hkv, causal;
+  const uint8_t* vc;     // V^ codes [Hkv, d, Tp/2] (blocks along tokens)
+  const uint8_t* vs;     // V^ scales [Hkv, d, vsp] (vsp = Tp/32 rounded up to a multiple of 4)
+  int T, Tp, Hq, Hkv, causal, vsp;
 };
 
 // Q^ operand of query row q (head h) for this lane's K group g, decoded from MiX codes to E4M3
@@ -327,6 +333,44 @@ __device__ __forceinline__ uint32_t p_code8(const float4& a, const float4& b, in
   return word;
 }
 
+// p_code8 that also returns the 8 E4M3 bytes of the coded values in element order (the MFMA
+// operand of P^ V^): 64 + m - 8 d for a nonzero code d, 0 for zero.
+template <bool CODES>   // CODES: also form the code word and the full shared field (else only Emax)
+__device__ __forceinline__ uint32_t p_code8_img(const float4& a, const float4& b, int quad_pos, uint32_t& shared,
+                                                uint32_t& out0, uint32_t& out1) {
+  const uint32_t x[8] = {f32_bits(a.x), f32_bits(a.y), f32_bits(a.z), f32_bits(a.w),
+                         f32_bits(b.x), f32_bits(b.y), f32_bits(b.z), f32_bits(b.w)};
+  const uint32_t lmax = max(max(max(x[0], x[1]), max(x[2], x[3])), max(max(x[4], x[5]), max(x[6], x[7])));
+  const uint32_t bmax = quad_max_dpp(lmax);
+  const int emax = min(max((int)(bmax >> 23) - 127, -7), 8);
+  const uint32_t m = mant3_of(lmax);
+  const uint32_t t3 = 24u + 3u * m;
+  const uint32_t mu = t3 < 32u ? (((uint32_t)(emax + 126) << 7) | ((t3 << 3) & 0x7Fu))
+                               : (((uint32_t)(emax + 127) << 7) | ((t3 << 2) & 0x7Fu));
+  const uint32_t pb = ((uint32_t)(emax + 119) << 7) | (m << 4);
+  const i16x2 MU1 = __builtin_bit_cast(i16x2, (mu + 128u) * 0x00010001u);
+  const u16x2 PB2 = __builtin_bit_cast(u16x2, pb * 0x00010001u);
+  const u16x2 M64 = __builtin_bit_cast(u16x2, (64u + m) * 0x00010001u);
+  uint32_t word = 0, im[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t w = __builtin_amdgcn_perm(x[i + 4] + 0xFFFFu, x[i] + 0xFFFFu, 0x07060302u);
+    i16x2 c = (MU1 - __builtin_bit_cast(i16x2, w)) >> (i16x2)7;
+    c = __builtin_elementwise_min(__builtin_elementwise_max(c, (i16x2)0), (i16x2)7);
+    const u16x2 cu = __builtin_bit_cast(u16x2, c);
+    const u16x2 gt = (PB2 - __builtin_bit_cast(u16x2, w)) >> (u16x2)15;   // a' > pb
+    const u16x2 e7 = (cu + (u16x2)1) >> (u16x2)3;                          // d* == 7
+    if (CODES) word |= __builtin_bit_cast(uint32_t, cu | ((gt & e7) << (u16x2)3)) << (4 * i);
+    const u16x2 zm = (e7 & ~gt) - (u16x2)1;                                // all ones unless zero
+    im[i] = __builtin_bit_cast(uint32_t, (M64 - (cu << (u16x2)3)) & zm);   // elements i (low), i + 4 (high)
+  }
+  out0 = __builtin_amdgcn_perm(im[1], im[0], 0x0C0C0400u) | __builtin_amdgcn_perm(im[3], im[2], 0x04000C0Cu);
+  out1 = __builtin_amdgcn_perm(im[1], im[0], 0x0C0C0602u) | __builtin_amdgcn_perm(im[3], im[2], 0x06020C0Cu);
+  shared = CODES ? quad_or_dpp((quad_pos == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * quad_pos)))
+                 : (uint32_t)(emax + 7);
+  return word;
+}
+
 // p = exp(fp32(S scale) - fp32(m scale)) of the lane's 16 scores into the wave's LDS p row, masked
 // keys (key >= nvalid) as 0 unless the whole tile is unmasked (FULL); returns their sum.
 template <bool FULL>
@@ -347,16 +391,51 @@ __device__ __forceinline__ float p_tile(const v4f (&acc)[4], float scale, float 
   return sum;
 }
 
-// grid (Hq, ceil(T / 64)), block 256. P^ codes [Hq, T, Tp/2] and shared [Hq, T, Tp/32] for keys
-// [0, min(Tp, round_up(i + 1, 256))) of row i (all Tp without the mask; masked keys code as zero),
-// l [Hq, T]; optional S and p dumps [Hq, T, Tp].
+// The V^ tile of 64 keys in LDS: 128 channel rows of 32 bytes, the 16-byte chunk c of channel ch
+// at slot c ^ vslot(ch) so that the lanes an LDS read serves at once hit distinct banks; then one
+// scale dword per channel (the four 32-token blocks from floor(k0 / 128)).
+constexpr int VST = 128 * 32 + 128 * 4;
+constexpr int FST = KST + VST;   // one ring stage: the K^ tile, then the V^ tile
+__device__ __forceinline__ int vslot(int ch) { return ((ch >> 2) ^ (ch >> 3)) & 1; }
+
+// wave w copies the V^ codes of channels 32 w .. 32 w + 31; waves 0 and 1 the scale dwords.
+// A chunk past Tp (the tile's upper half in the last tile) repeats chunk 0; its keys have p = 0.
+__device__ __forceinline__ void v_stage(const PrefillOps& P, int hk, int k0, uint8_t* st) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ch = 32 * wave + (lane >> 1);
+  int c = (lane & 1) ^ vslot(ch);
+  if (k0 + 32 * c >= P.Tp) c = 0;
+  dma16(P.vc + ((int64_t)hk * 128 + ch) * (P.Tp >> 1) + (k0 >> 1) + 16 * c,
+        __builtin_amdgcn_readfirstlane(lds_addr(st + wave * 1024)));
+  if (wave < 2) {
+    const int ch2 = 64 * wave + lane;
+    dma4(P.vs + ((int64_t)hk * 128 + ch2) * P.vsp + ((k0 >> 5) & ~3),
+         __builtin_amdgcn_readfirstlane(lds_addr(st + 128 * 32 + wave * 256)));
+  }
+}
+
+// The wave's P^ tile (16 query rows x 64 keys, E4M3) in LDS: row r's 16-byte chunk c at slot
+// c ^ pswz(r); the block scales (E8M0 2^(Emax-1)) of its two 32-key blocks after the 16 rows.
+__device__ __forceinline__ int pswz(int r) { return (r ^ (r >> 2)) & 3; }
+
+// grid (Hq, ceil(T / 64)), block 256. For d = 128: recomputes S tile by tile, forms p with the row
+// maxima of k_attn_rowmax, codes P^ (MiX-4.5b along keys) and accumulates O^T += V^ P^ on the MFMA,
+// then writes O = (P^ V^) / l rounded to bf16 [T, Hq, d] and l [Hq, T]. P^ codes [Hq, T, Tp/2] and
+// shared fields [Hq, T, Tp/32] are written only when pc is given (for keys
+// [0, min(Tp, round_up(i + 1, 256))) of row i, all Tp without the mask; masked keys code as zero);
+// optional S and p dumps [Hq, T, Tp].
+// PV: v_mfma_scale_f32_16x16x128_f8f6f4 with V^ (FP4, 16 channels) as A and P^ (E4M3, 16 queries)
+// as B, the tile's 64 keys as K elements [0, 64) and zeros above; result register e of lane
+// r + 16 g is O^T[channel 4 g + e][query r].
+template <bool DBG>   // DBG: the debug dumps (S, p, P^ codes and shared fields) are written
 __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* __restrict__ smax, float scale,
-                                                     uint8_t* __restrict__ pc, uint16_t* __restrict__ ps,
-                                                     float* __restrict__ l, float* __restrict__ dbg_s,
-                                                     float* __restrict__ dbg_p) {
+                                                     uint16_t* __restrict__ o, uint8_t* __restrict__ pc,
+                                                     uint16_t* __restrict__ ps, float* __restrict__ l,
+                                                     float* __restrict__ dbg_s, float* __restrict__ dbg_p) {
   constexpr int PP = PK + 4;                     // padded LDS row (floats)
   __shared__ __align__(16) float sp[4][16][PP];  // each wave's p tile: 16 rows x 64 keys
-  __shared__ __align__(16) uint8_t kst[2][KST];
+  __shared__ __align__(16) uint8_t fst[2][FST];  // K^ and V^ tiles, two stages
+  __shared__ __align__(16) uint8_t spb[4][16 * 64 + 16 * 2];   // each wave's P^ tile and block scales
   const int h = blockIdx.x, hk = h / (P.Hq / P.Hkv), qt = q_tile(P);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -372,12 +451,16 @@ __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* _
   const int kend = P.causal ? qlast + 1 : P.T;                                    // keys with some unmasked entry
   const int kwrite = P.causal ? min(P.Tp, (qlast + 1 + 255) / 256 * 256) : P.Tp;  // keys whose codes are written
   float lsum = 0.f;
+  v4f acc_o[8];
+#pragma unroll
+  for (int t = 0; t < 8; t++) acc_o[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint8_t* pbw = spb[wave];
   // read-back role: row rr = lane / 8 (+ 8 per pass), 8 keys kk = 8 (lane % 8); quads are 32-key blocks
   const int rr0 = lane >> 3, kk = 8 * (lane & 7);
   const int64_t crow0 = (int64_t)h * P.T + q0w + rr0;   // P^ row of pass 0 (pass 1: + 8)
   const bool st0 = q0w + rr0 < P.T, st1 = q0w + rr0 + 8 < P.T;
-  // a tile's codes are stored at the start of the next tile (after its barrier) so that the copy
-  // wait before the barrier does not wait for them
+  // a tile's codes (debug) are stored at the start of the next tile (after its barrier) so that
+  // the copy wait before the barrier does not wait for them
   uint32_t cw[2] = {0, 0}, cs[2] = {0, 0};
   int kprev = -1;
   auto store_codes = [&](int key) {   // Tp is a multiple of 32: quads stay whole
@@ -393,49 +476,101 @@ __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* _
     }
   };
   const int ntc = (kend + PK - 1) / PK, nt = (kwrite + PK - 1) / PK;
-  if (ntc > 0) k_stage(P, hk, 0, kst[0]);
+  if (ntc > 0) {
+    k_stage(P, hk, 0, fst[0]);
+    v_stage(P, hk, 0, fst[0] + KST);
+  }
   for (int it = 0; it < ntc; it++) {
     const int k0 = it * PK;
     wait_vmcnt<0>();
     __syncthreads();
-    if (kprev >= 0) store_codes(kprev);
-    if (it + 1 < ntc) k_stage(P, hk, k0 + PK, kst[(it + 1) & 1]);
+    if (DBG && pc && kprev >= 0) store_codes(kprev);
+    if (it + 1 < ntc) {
+      k_stage(P, hk, k0 + PK, fst[(it + 1) & 1]);
+      v_stage(P, hk, k0 + PK, fst[(it + 1) & 1] + KST);
+    }
+    const uint8_t* st = fst[it & 1];
     v4f acc[4];
-    s_tile(kst[it & 1], r, g, qf, qsc, acc);
+    s_tile(st, r, g, qf, qsc, acc);
     if (k0 + PK <= nfull)
       lsum += p_tile<true>(acc, scale, mz, k0, g, nvalid, sp[wave][r]);
     else
       lsum += p_tile<false>(acc, scale, mz, k0, g, nvalid, sp[wave][r]);
-    if (dbg_s || dbg_p) {
+    if (DBG && (dbg_s || dbg_p)) {
       const float* prow = sp[wave][r];
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const int key0 = k0 + 16 * j + 4 * g;
         if (q < P.T && key0 < P.Tp) {
-          const int64_t o = ((int64_t)h * P.T + q) * P.Tp + key0;
-          if (dbg_s) *(float4*)(dbg_s + o) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
-          if (dbg_p) *(float4*)(dbg_p + o) = *(const float4*)(prow + 16 * j + 4 * g);
+          const int64_t oi = ((int64_t)h * P.T + q) * P.Tp + key0;
+          if (dbg_s) *(float4*)(dbg_s + oi) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+          if (dbg_p) *(float4*)(dbg_p + oi) = *(const float4*)(prow + 16 * j + 4 * g);
         }
       }
     }
-    // code P^ from the wave's own tile (LDS is in order within a wave; no workgroup barrier)
-#pragma unroll
-    for (int pass = 0; pass < 2; pass++) {
+    // code P^ from the wave's own tile (LDS is in order within a wave; no workgroup barrier) into
+    // the wave's E4M3 tile; the code words and shared fields only for the debug dump
+    auto code_pass = [&](auto codes, int pass) {
       const int rr = rr0 + 8 * pass;
       const float4 a = *(const float4*)&sp[wave][rr][kk];
       const float4 b = *(const float4*)&sp[wave][rr][kk + 4];
-      cw[pass] = p_code8(a, b, lane & 3, cs[pass]);
+      uint32_t e0, e1, sh;
+      const uint32_t word = p_code8_img<decltype(codes)::value>(a, b, lane & 3, sh, e0, e1);
+      if (decltype(codes)::value) {
+        cw[pass] = word;
+        cs[pass] = sh;
+      }
+      *(uint2*)(pbw + rr * 64 + 16 * ((kk >> 4) ^ pswz(rr)) + (kk & 8)) = make_uint2(e0, e1);
+      if ((lane & 3) == 0) pbw[16 * 64 + rr * 2 + (kk >> 5)] = (uint8_t)((sh & 15u) + 119u);
+    };
+    if (DBG && pc) {
+      code_pass(std::true_type{}, 0);
+      code_pass(std::true_type{}, 1);
+    } else {
+      code_pass(std::false_type{}, 0);
+      code_pass(std::false_type{}, 1);
     }
     kprev = k0 + kk;
+    // O^T += V^ P^ over the tile's keys
+    const uint4 pb = *(const uint4*)(pbw + r * 64 + 16 * (g ^ pswz(r)));
+    const v8i pf = v8i{(int)pb.x, (int)pb.y, (int)pb.z, (int)pb.w, 0, 0, 0, 0};
+    const int psc = g < 2 ? (int)pbw[16 * 64 + r * 2 + g] : 127;
+    // lanes g = 2, 3 carry K elements [64, 128), where P^ is zero: any finite V^ data will do (FP4
+    // has no inf or NaN), with scale 1
+    const uint8_t* sv = st + KST;
+    const int vblk = ((k0 >> 5) & 3) + (g & 1);              // byte of this lane's block in the dword
+    const bool vlive = g < 2 && k0 + 32 * g < P.Tp;
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      const int ch = 16 * t + r;
+      const uint4 vf = *(const uint4*)(sv + ch * 32 + 16 * ((g & 1) ^ vslot(ch)));
+      const int vsc = vlive ? (int)sv[128 * 32 + ch * 4 + vblk] : 127;
+      const v8i vfa = v8i{(int)vf.x, (int)vf.y, (int)vf.z, (int)vf.w, 0, 0, 0, 0};
+      acc_o[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vfa, pf, acc_o[t], 4, 0, 0, vsc, 0, psc);
+      __builtin_amdgcn_sched_barrier(0);   // one V^ fragment live at a time
+    }
   }
-  if (kprev >= 0) store_codes(kprev);
-  // tiles past every unmasked key of the tile rows: all-zero blocks (codes 0x7, shared field 0)
-  cw[0] = cw[1] = 0x77777777u;
-  cs[0] = cs[1] = 0u;
-  for (int it = ntc; it < nt; it++) store_codes(it * PK + kk);
+  if (DBG && pc) {
+    if (kprev >= 0) store_codes(kprev);
+    // tiles past every unmasked key of the tile rows: all-zero blocks (codes 0x7, shared field 0)
+    cw[0] = cw[1] = 0x77777777u;
+    cs[0] = cs[1] = 0u;
+    for (int it = ntc; it < nt; it++) store_codes(it * PK + kk);
+  }
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
-  if (g == 0 && q < P.T) l[(int64_t)h * P.T + q] = lsum;
+  if (q < P.T) {
+    if (g == 0) l[(int64_t)h * P.T + q] = lsum;
+    uint16_t* orow = o + ((int64_t)q * P.Hq + h) * 128 + 4 * g;
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(__fdiv_rn(acc_o[t][0], lsum)) |
+                          ((uint32_t)f32_to_bf16_rne(__fdiv_rn(acc_o[t][1], lsum)) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(__fdiv_rn(acc_o[t][2], lsum)) |
+                          ((uint32_t)f32_to_bf16_rne(__fdiv_rn(acc_o[t][3], lsum)) << 16);
+      *(uint2*)(orow + 16 * t) = make_uint2(lo, hi);
+    }
+  }
 }
 
 // ------------------------------------------------------------------ decode: scores (pass 1)
@@ -834,6 +969,9 @@ __global__ void k_decode_combine(const float* __restrict__ lpart, const float* _
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// V^ scale rows are padded to a multiple of 4 blocks (the fused pass copies them as dwords)
+static inline int64_t prefill_vsp(int64_t Tp) { return (Tp / 32 + 3) / 4 * 4; }
+
 struct PrefillWs {
   size_t qc, qs, kc, ks, vc, vs, s, pc, ps, l, total;
 };
@@ -848,7 +986,7 @@ static PrefillWs prefill_layout(int64_t T, int64_t Hq, int64_t Hkv, int64_t d) {
   w.kc = take((size_t)T * Hkv * d / 2);
   w.ks = take((size_t)T * Hkv * (d / 32));
   w.vc = take((size_t)Hkv * d * Tp / 2);
-  w.vs = take((size_t)Hkv * d * (Tp / 32));
+  w.vs = take((size_t)Hkv * d * prefill_vsp(Tp));
   // d = 128 takes the fused S passes (row maxima only); other head sizes store S
   w.s = take(d == 128 ? (size_t)Hq * T * 4 : (size_t)Hq * T * Tp * 4);
   w.pc = take((size_t)Hq * T * Tp / 2);
@@ -890,46 +1028,53 @@ hipError_t attn_prefill_run(const void* q, const void* k, const void* v, int64_t
   HIPCHK(launch_kmean(k, 1, T, Hkv * d, Hkv * d, mu, s));
   HIPCHK(launch_mx_quantize(1, k, 1, T, Hkv * d, Hkv * d, mu, kc, ks, s));
   HIPCHK(launch_mix_quantize(1, q, 1, T, Hq * d, Hq * d, qc, qs, s));
-  HIPCHK(launch_mx_quantize_cols(v, 1, T, Tp, Hkv * d, Hkv * d, vc, vs, Tp / 2, Tp / 32, s));
+  const int64_t vsp = prefill_vsp(Tp);
+  HIPCHK(launch_mx_quantize_cols(v, 1, T, Tp, Hkv * d, Hkv * d, vc, vs, Tp / 2, vsp, s));
 
   const float scale = (float)(1.0 / sqrt((double)d));
   if (d == 128) {
-    // 3-4. fused: row maxima of S, then S again -> p, l and P^ (S is not stored)
-    PrefillOps P{qc, qs, kc, ks, (int)T, (int)Tp, (int)Hq, (int)Hkv, causal ? 1 : 0};
+    // 3-5. fused: row maxima of S, then S again -> p, l, P^ and O += P^ V^ (S and P^ stay on chip;
+    // P^ codes are written only for the debug dump)
+    PrefillOps P{qc, qs, kc, ks, vc, vs, (int)T, (int)Tp, (int)Hq, (int)Hkv, causal ? 1 : 0, (int)vsp};
     dim3 grid((unsigned)Hq, (unsigned)((T + PQ - 1) / PQ));
     hipLaunchKernelGGL(k_attn_rowmax, grid, dim3(256), 0, s, P, S);
     HIPCHK(hipGetLastError());
-    hipLaunchKernelGGL(k_attn_pcode, grid, dim3(256), 0, s, P, (const float*)S, scale, pc, ps, l,
-                       dbg ? dbg->s : nullptr, dbg ? dbg->p : nullptr);
+    const bool want_codes = dbg && (dbg->p_codes || dbg->p_shared);
+    if (dbg)
+      hipLaunchKernelGGL(k_attn_pcode<true>, grid, dim3(256), 0, s, P, (const float*)S, scale, (uint16_t*)o,
+                         want_codes ? pc : nullptr, want_codes ? ps : nullptr, l, dbg->s, dbg->p);
+    else
+      hipLaunchKernelGGL(k_attn_pcode<false>, grid, dim3(256), 0, s, P, (const float*)S, scale, (uint16_t*)o,
+                         nullptr, nullptr, l, nullptr, nullptr);
     HIPCHK(hipGetLastError());
   } else {
-  // 3. S = Q^ K^T per query head
-  GemmArgs g1{};
-  g1.a_codes = qc; g1.a_shared = qs; g1.a_pitch = Hq * d / 2; g1.a_sh_pitch = Hq * d / 32;
-  g1.a_bstride = d / 2; g1.a_sh_bstride = d / 32;
-  g1.b_codes = kc; g1.b_scales = ks; g1.b_pitch = Hkv * d / 2; g1.b_sc_pitch = Hkv * d / 32;
-  g1.b_bstride = d / 2; g1.b_sc_bstride = d / 32; g1.b_group = (int)G;
-  g1.c = S; g1.ldc = Tp; g1.c_bstride = T * Tp; g1.row_div = nullptr;
-  g1.M = (int)T; g1.N = (int)T; g1.K = (int)d; g1.batch = (int)Hq; g1.causal = causal ? 1 : 0;
-  HIPCHK(launch_gemm_mfma(1, 1, 0, g1, s));
+    // 3. S = Q^ K^T per query head
+    GemmArgs g1{};
+    g1.a_codes = qc; g1.a_shared = qs; g1.a_pitch = Hq * d / 2; g1.a_sh_pitch = Hq * d / 32;
+    g1.a_bstride = d / 2; g1.a_sh_bstride = d / 32;
+    g1.b_codes = kc; g1.b_scales = ks; g1.b_pitch = Hkv * d / 2; g1.b_sc_pitch = Hkv * d / 32;
+    g1.b_bstride = d / 2; g1.b_sc_bstride = d / 32; g1.b_group = (int)G;
+    g1.c = S; g1.ldc = Tp; g1.c_bstride = T * Tp; g1.row_div = nullptr;
+    g1.M = (int)T; g1.N = (int)T; g1.K = (int)d; g1.batch = (int)Hq; g1.causal = causal ? 1 : 0;
+    HIPCHK(launch_gemm_mfma(1, 1, 0, g1, s));
 
-  // 4. softmax and P^
-  const int64_t nrows = Hq * T;
-  hipLaunchKernelGGL(k_softmax_pquant, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, S, (int)T, (int)Tp, nrows,
-                     causal, scale, pc, ps, l, dbg ? dbg->p : nullptr);
-  HIPCHK(hipGetLastError());
-  if (dbg && dbg->s) HIPCHK(hipMemcpyAsync(dbg->s, S, (size_t)Hq * T * Tp * 4, hipMemcpyDeviceToDevice, s));
+    // 4. softmax and P^
+    const int64_t nrows = Hq * T;
+    hipLaunchKernelGGL(k_softmax_pquant, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, S, (int)T, (int)Tp,
+                       nrows, causal, scale, pc, ps, l, dbg ? dbg->p : nullptr);
+    HIPCHK(hipGetLastError());
+    if (dbg && dbg->s) HIPCHK(hipMemcpyAsync(dbg->s, S, (size_t)Hq * T * Tp * 4, hipMemcpyDeviceToDevice, s));
+
+    // 5. O = (P^ V^) / l
+    GemmArgs g2{};
+    g2.a_codes = pc; g2.a_shared = ps; g2.a_pitch = Tp / 2; g2.a_sh_pitch = Tp / 32;
+    g2.a_bstride = T * Tp / 2; g2.a_sh_bstride = T * (Tp / 32);
+    g2.b_codes = vc; g2.b_scales = vs; g2.b_pitch = Tp / 2; g2.b_sc_pitch = vsp;
+    g2.b_bstride = d * Tp / 2; g2.b_sc_bstride = d * vsp; g2.b_group = (int)G;
+    g2.c = o; g2.ldc = Hq * d; g2.c_bstride = d; g2.row_div = l; g2.row_div_bstride = T;
+    g2.M = (int)T; g2.N = (int)d; g2.K = (int)Tp; g2.batch = (int)Hq; g2.causal = causal ? 2 : 0;
+    HIPCHK(launch_gemm_mfma(1, 1, 1, g2, s));
   }
-
-  // 5. O = (P^ V^) / l
-  GemmArgs g2{};
-  g2.a_codes = pc; g2.a_shared = ps; g2.a_pitch = Tp / 2; g2.a_sh_pitch = Tp / 32;
-  g2.a_bstride = T * Tp / 2; g2.a_sh_bstride = T * (Tp / 32);
-  g2.b_codes = vc; g2.b_scales = vs; g2.b_pitch = Tp / 2; g2.b_sc_pitch = Tp / 32;
-  g2.b_bstride = d * Tp / 2; g2.b_sc_bstride = d * (Tp / 32); g2.b_group = (int)G;
-  g2.c = o; g2.ldc = Hq * d; g2.c_bstride = d; g2.row_div = l; g2.row_div_bstride = T;
-  g2.M = (int)T; g2.N = (int)d; g2.K = (int)Tp; g2.batch = (int)Hq; g2.causal = causal ? 2 : 0;
-  HIPCHK(launch_gemm_mfma(1, 1, 1, g2, s));
 
   if (dbg) {
     if (dbg->p_codes) HIPCHK(hipMemcpyAsync(dbg->p_codes, pc, (size_t)Hq * T * Tp / 2, hipMemcpyDeviceToDevice, s));
