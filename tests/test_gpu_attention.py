@@ -129,6 +129,22 @@ def test_prefill_workload4_full_size_sampled():
     _prefill_stages(g, 4096, 28, 4, 128, True, rows, [0, 6, 7, 13, 20, 27])
 
 
+@pytest.mark.parametrize("T,Hq,Hkv,causal", [(4096, 28, 4, True), (200, 4, 1, True), (100, 2, 2, False),
+                                              (330, 6, 3, True)])
+def test_prefill_production_path_equals_debug_path(T, Hq, Hkv, causal):
+    """The call without debug dumps runs its own kernel instantiation; its O and mean must be the
+    debug path's bit for bit (the debug path's O is checked stage by stage above)."""
+    q = _lib()
+    g = synth.attention_qkv(T=T, Hq=Hq, Hkv=Hkv, d=128, seed_cfg=4)
+    args = (dev_bf16(g["q"]), dev_bf16(g["k"]), dev_bf16(g["v"]))
+    o_fast, mu_fast, _ = q.mix_attn_prefill(*args, causal=causal, debug=False)
+    o_dbg, mu_dbg, _ = q.mix_attn_prefill(*args, causal=causal, debug=True)
+    torch.cuda.synchronize()
+    assert torch.equal(mu_fast, mu_dbg)
+    assert torch.equal(o_fast.view(torch.int16), o_dbg.view(torch.int16)), "production O differs from the debug path"
+    assert torch.isfinite(o_fast.float()).all()
+
+
 def _decode_case(B, Hq, Hkv, L_each, seed=5):
     q = _lib()
     d = 128
