@@ -103,6 +103,7 @@ struct F8Stage {
   static constexpr int AS_OFF = A_BYTES + B_BYTES;
   static constexpr int BS_OFF = AS_OFF + 1024;
   static constexpr int BYTES = BS_OFF + 1024;
+  static constexpr int NS = 2;   // ring stages (a third, measured, was slower)
 };
 
 struct F8Args {
@@ -124,6 +125,12 @@ __device__ __forceinline__ int f8_xcd_tile(int bid, int nt) {
 
 constexpr int F8_THREADS = 512;   // 8 waves: 4 along M x 2 along N, 64 x 128 outputs each
 
+// LDS slot of 16-byte chunk c of a stage row: 128-byte rows (E4M3) take c ^ aswz(row), 64-byte rows
+// (FP4) c ^ bswz(row). With either 8 or 16 lanes served per LDS cycle, the lanes of one read
+// (consecutive rows, the same logical chunk) then fall in distinct banks.
+__device__ __forceinline__ int aswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int bswz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
 // Copies of one K step of tile (tm, tn) into stage buffer `st`; each wave copies whole
 // 1 KB runs (64 lanes x 16 bytes) of the stage image.
 template <int B_FP4>
@@ -132,23 +139,23 @@ __device__ __forceinline__ void f8_issue(const F8Args& g, uint8_t* st, int tm, i
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m0 = tm * FT, n0 = tn * FT, k0 = ks * FK;
   // A: 2048 16-byte chunks; chunk q lands at LDS byte 16 q; q -> (row q/8, slot q%8) holding
-  // logical chunk slot ^ (row & 7) of that row (rows past M repeat row M-1; never stored).
+  // logical chunk slot ^ aswz(row) of that row (rows past M repeat row M-1; never stored).
 #pragma unroll
   for (int p = 0; p < 4; p++) {
     const int q = p * F8_THREADS + wave * 64 + lane;
     const int row = q >> 3, slot = q & 7;
-    const int c = slot ^ (row & 7);
+    const int c = slot ^ aswz(row);
     const int grow = min(m0 + row, g.M - 1);
     dma16(g.a8 + (uint32_t)(grow * g.K + k0 + 16 * c),
           __builtin_amdgcn_readfirstlane(lds_addr(st + (p * F8_THREADS + wave * 64) * 16)));
   }
   if (B_FP4) {
-    // B: 1024 chunks; (row q/4, slot q%4) holds logical chunk slot ^ ((row >> 1) & 3)
+    // B: 1024 chunks; (row q/4, slot q%4) holds logical chunk slot ^ bswz(row)
 #pragma unroll
     for (int p = 0; p < 2; p++) {
       const int q = p * F8_THREADS + wave * 64 + lane;
       const int row = q >> 2, slot = q & 3;
-      const int c = slot ^ ((row >> 1) & 3);
+      const int c = slot ^ bswz(row);
       const int grow = min(n0 + row, g.N - 1);
       dma16(g.b + (uint32_t)(grow * (g.K >> 1) + (k0 >> 1) + 16 * c),
             __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::A_BYTES + (p * F8_THREADS + wave * 64) * 16)));
@@ -158,7 +165,7 @@ __device__ __forceinline__ void f8_issue(const F8Args& g, uint8_t* st, int tm, i
     for (int p = 0; p < 4; p++) {
       const int q = p * F8_THREADS + wave * 64 + lane;
       const int row = q >> 3, slot = q & 7;
-      const int c = slot ^ (row & 7);
+      const int c = slot ^ aswz(row);
       const int grow = min(n0 + row, g.N - 1);
       dma16(g.b + (uint32_t)(grow * g.K + k0 + 16 * c),
             __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::A_BYTES + (p * F8_THREADS + wave * 64) * 16)));
@@ -197,7 +204,7 @@ template <int B_FP4, int C_BF16>
 __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int SB = F8Stage<B_FP4>::BYTES;
-  constexpr int NS = 2;
+  constexpr int NS = F8Stage<B_FP4>::NS;
   const int tiles_m = (g.M + FT - 1) / FT, tiles_n = (g.N + FT - 1) / FT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -236,8 +243,8 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
       for (int i = 0; i < 2; i++) {
         const int row = 64 * wm + 32 * i + r;
         const int c0 = 4 * h + gq, c1 = 4 * h + 2 + gq;
-        const uint4 lo = *(const uint4*)(sa + row * 128 + ((c0 ^ (row & 7)) * 16));
-        const uint4 hi = *(const uint4*)(sa + row * 128 + ((c1 ^ (row & 7)) * 16));
+        const uint4 lo = *(const uint4*)(sa + row * 128 + ((c0 ^ aswz(row)) * 16));
+        const uint4 hi = *(const uint4*)(sa + row * 128 + ((c1 ^ aswz(row)) * 16));
         xf[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
@@ -247,12 +254,12 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
         if (B_FP4) {
           // FP4 operands read only the low 4 registers of the 8-register tuple
           const int c = 2 * h + gq;
-          const v4i w = *(const v4i*)(sbm + row * 64 + ((c ^ ((row >> 1) & 3)) * 16));
+          const v4i w = *(const v4i*)(sbm + row * 64 + ((c ^ bswz(row)) * 16));
           wf = __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
         } else {
           const int c0 = 4 * h + gq, c1 = 4 * h + 2 + gq;
-          const v4i lo = *(const v4i*)(sbm + row * 128 + ((c0 ^ (row & 7)) * 16));
-          const v4i hi = *(const v4i*)(sbm + row * 128 + ((c1 ^ (row & 7)) * 16));
+          const v4i lo = *(const v4i*)(sbm + row * 128 + ((c0 ^ aswz(row)) * 16));
+          const v4i hi = *(const v4i*)(sbm + row * 128 + ((c1 ^ aswz(row)) * 16));
           wf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
         // the scale operands' op_sel picks byte j of the weight word and byte i of the
@@ -493,7 +500,7 @@ size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K) {
 
 template <int B_FP4, int C_BF16>
 constexpr size_t f8_lds_bytes() {
-  const size_t ring = (size_t)2 * F8Stage<B_FP4>::BYTES;
+  const size_t ring = (size_t)F8Stage<B_FP4>::NS * F8Stage<B_FP4>::BYTES;
   const size_t epi = (size_t)(F8_THREADS / 64) * 32 * (C_BF16 ? 272 : 544);
   return ring > epi ? ring : epi;
 }
