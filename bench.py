@@ -206,6 +206,41 @@ def bench_linear(torch, q, args, which):
         eq6_ms.append(a.elapsed_time(b))
     eq6_ms = float(np.median(eq6_ms))
 
+    # the output quantized for a next layer (MiX-4.5b codes + its A image): in the GEMM epilogue
+    # against the unfused chain (bf16 C, then the quantizer reading it back); N % 128 == 0
+    fq = None
+    if a_fmt == "4.5b" and N % 128 == 0:
+        nq = q.mix_gemm_a_image_bytes(M, N)
+        qc = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+        qs = torch.empty((M, N // 32), dtype=torch.int16, device=dev)
+        qi = torch.empty((nq,), dtype=torch.uint8, device=dev)
+
+        def chain(i, fused):
+            x = xs[i % nrot]
+            ac, as_, aimg = bufs[i % 2]
+            q.mix_quantize_gemm(x, a_fmt, codes=ac, shared=as_, image=aimg)
+            if fused:
+                q.mix_mx_gemm_images_quantize(aimg, bimg, keep_c=False, codes=qc, shared=qs, q_image=qi)
+            else:
+                q.mix_mx_gemm_images(aimg, bimg, out=out)
+                q.mix_quantize_gemm(out, "4.5b", codes=qc, shared=qs, image=qi)
+
+        fq = {}
+        for name, fused in (("unfused_ms", False), ("fused_ms", True)):
+            for i in range(args.warmup):
+                chain(i, fused)
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(args.steps):
+                chain(i, fused)
+            b.record()
+            torch.cuda.synchronize()
+            fq[name] = a.elapsed_time(b) / args.steps
+        fq["what"] = ("step that also codes the output as MiX-4.5b with its A image: quantize X, GEMM, then "
+                      "quantize C (unfused, bf16 C through HBM) or the GEMM epilogue codes C (fused, no C)")
+        fq["speedup"] = fq["unfused_ms"] / fq["fused_ms"]
+
     flops = 2.0 * M * N * K
     sh_bytes = 2 if a_fmt == "4.5b" else 1
     tiles_m, tiles_n = -(-M // 256), -(-N // 256)
@@ -239,6 +274,8 @@ def bench_linear(torch, q, args, which):
                              "frac_hbm": wq_bytes / (wq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": wq_bytes},
         "eq6_valu_gemm": {"kernel": "k_gemm_eq6", "ms": eq6_ms, "TFLOP/s": flops / (eq6_ms * 1e-3) / 1e12},
     }
+    if fq is not None:
+        res["fused_output_quantization"] = fq
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_linear(g["x"], g["w_t"], a_fmt, b_fmt, M, N, wl)
     return res

@@ -176,6 +176,21 @@ mix_status_t mix_mx_gemm_images(mx_fmt_t b_fmt, const void* a_img, const void* b
                                 void* stream);
 
 /*
+ * The product of the two images with its output quantized in the same pass -- the pages' output
+ * quantizer at the array output (P1 method overview; the fused quantizer): q_codes [M, N/2] and
+ * q_shared [M, N/32] (u16) are the MiX-4.5b coding along N of the bf16 rounding of C, exactly what
+ * mix_quantize would give for that bf16 matrix; q_img (optional, NULL to skip; needs N a multiple
+ * of 128 and q_img_bytes >= mix_gemm_a_image_bytes(M, N)) receives the A image of those codes for
+ * a next product with K = N. C itself (bf16, pitch ldc) is written only if c is not NULL; for
+ * M <= 16 c is required (the weight stream writes C, then the quantizer reads it) and must be
+ * 16-byte aligned with a 16-byte row pitch. N must be a multiple of 32; other arguments as for
+ * mix_mx_gemm_images.
+ */
+mix_status_t mix_mx_gemm_images_quantize(mx_fmt_t b_fmt, const void* a_img, const void* b_img, const uint8_t* b_codes,
+                                         int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, uint8_t* q_codes,
+                                         void* q_shared, void* q_img, size_t q_img_bytes, void* stream);
+
+/*
  * The same product computed as P1's Eq. (6) on the vector ALUs: integer sub-block sums of the MX
  * mantissas scaled by 2^(7 - dE), times (8 + m_k), one power-of-two scale per block, fp32
  * accumulation across blocks. Same arguments and results (to fp32 rounding) as mix_mx_gemm.

@@ -23,7 +23,7 @@ DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 __all__ = [
     "MixError", "mix_quantize", "mx_quantize", "mx_quantize_cols", "mix_dequantize", "mx_dequantize",
     "mix_mx_gemm", "mix_mx_gemm_eq6", "AImage", "BImage", "mix_gemm_a_image", "mix_quantize_gemm",
-    "mx_gemm_b_image", "mix_mx_gemm_images", "mix_kmean", "mix_attn_prefill", "KVCache", "mix_kv_cache_prefill",
+    "mx_gemm_b_image", "mix_mx_gemm_images", "mix_mx_gemm_images_quantize", "mix_kmean", "mix_attn_prefill", "KVCache", "mix_kv_cache_prefill",
     "mix_attn_decode", "abi_version",
 ]
 
@@ -244,6 +244,34 @@ def mix_mx_gemm_images(a_img, b_img, out_dtype=torch.float32, out=None):
                                      _p(b_img.codes) if b_img.fmt == "fp4" else None, M, N, K, _p(out),
                                      DTYPE[out.dtype], out.stride(0), _stream()), "mix_mx_gemm_images")
     return out
+
+
+def mix_mx_gemm_images_quantize(a_img, b_img, keep_c=False, image=True, out=None, codes=None, shared=None,
+                                q_image=None):
+    """The image product with its output quantized in the same pass: MiX-4.5b codes [M, N/2] and
+    shared fields [M, N/32] of the bf16 rounding of C (as mix_quantize of that bf16 matrix), and
+    with ``image`` that output's AImage for a next product. Returns (C bf16 or None, codes, shared,
+    AImage or None); C is kept with ``keep_c`` (always written when M <= 16)."""
+    if a_img.K != b_img.K:
+        raise MixError("A and B images disagree on K")
+    M, N, K = a_img.M, b_img.N, a_img.K
+    dev = a_img.buf.device
+    if (keep_c or M <= 16) and out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if codes is None:
+        codes = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    if shared is None:
+        shared = torch.empty((M, N // 32), dtype=torch.int16, device=dev)
+    if isinstance(q_image, AImage):
+        q_image = q_image.buf
+    img = _image_buf(mix_gemm_a_image_bytes(M, N), dev, q_image, "mix_mx_gemm_images_quantize") if image else None
+    _need_cuda(out, codes, shared)
+    check(_lib_().mix_mx_gemm_images_quantize(MX_FMT[b_img.fmt], _p(a_img.buf), _p(b_img.buf),
+                                              _p(b_img.codes) if b_img.fmt == "fp4" else None, M, N, K, _p(out),
+                                              out.stride(0) if out is not None else N, _p(codes), _p(shared),
+                                              _p(img), img.numel() if img is not None else 0, _stream()),
+          "mix_mx_gemm_images_quantize")
+    return out, codes, shared, (AImage(img, M, N) if img is not None else None)
 
 
 def mix_mx_gemm_eq6(a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype=torch.float32, out=None):

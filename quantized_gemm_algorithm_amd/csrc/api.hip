@@ -293,6 +293,41 @@ mix_status_t mix_mx_gemm_images(mx_fmt_t b_fmt, const void* a_img, const void* b
                     fn);
 }
 
+mix_status_t mix_mx_gemm_images_quantize(mx_fmt_t b_fmt, const void* a_img, const void* b_img, const uint8_t* b_codes,
+                                         int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, uint8_t* q_codes,
+                                         void* q_shared, void* q_img, size_t q_img_bytes, void* stream) {
+  g_err.clear();
+  const char* fn = "mix_mx_gemm_images_quantize";
+  if (b_fmt != MX_INT4 && b_fmt != MX_FP4) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (M < 0 || N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
+  if (M == 0 || N == 0) return MIX_OK;
+  if (M > INT32_MAX || N > INT32_MAX || !image_k_ok(K))
+    return fail(MIX_E_SHAPE, "%s: K=%lld is not a positive multiple of 128 (or an extent is above 2^31-1)", fn, (long long)K);
+  if (N % 32) return fail(MIX_E_SHAPE, "%s: N=%lld is not a multiple of 32 (MiX blocks run along N)", fn, (long long)N);
+  if (q_img && N % 128)
+    return fail(MIX_E_SHAPE, "%s: the output's A image needs N (its K) a multiple of 128, got %lld", fn, (long long)N);
+  if (c && ldc < N) return fail(MIX_E_SHAPE, "%s: ldc=%lld < N=%lld", fn, (long long)ldc, (long long)N);
+  if (M <= 16 && !c) return fail(MIX_E_NULL, "%s: M <= 16 needs c (the weight stream writes C first)", fn);
+  if (M > 16 && (!mix::gemm_f8_offsets_ok(M, N, K) || (q_img && !mix::gemm_f8_offsets_ok(M, 1, N))))
+    return fail(MIX_E_UNSUPPORTED, "%s: an operand or output image of %lld x %lld x %lld reaches 2^31 bytes", fn,
+                (long long)M, (long long)N, (long long)K);
+  if (!a_img || !b_img || !q_codes || !q_shared) return fail(MIX_E_NULL, "%s: an image or an output is NULL", fn);
+  if (b_fmt == MX_FP4 && !b_codes) return fail(MIX_E_NULL, "%s: MXFP4 codes are NULL", fn);
+  if (((uintptr_t)a_img & 255u) || ((uintptr_t)b_img & 255u) || ((uintptr_t)q_img & 255u))
+    return fail(MIX_E_ALIGN, "%s: images must be 256-byte aligned", fn);
+  if (b_fmt == MX_FP4 && !aligned16(b_codes)) return fail(MIX_E_ALIGN, "%s: codes not 16-byte aligned", fn);
+  if (((uintptr_t)q_codes & 3u) || ((uintptr_t)q_shared & 1u) || ((uintptr_t)c & 1u))
+    return fail(MIX_E_ALIGN, "%s: q_codes must be 4-byte aligned, q_shared and c 2-byte aligned", fn);
+  if (M <= 16 && (!aligned16(c) || (ldc * 2) % 16))
+    return fail(MIX_E_ALIGN, "%s: for M <= 16, c and its row pitch must be 16-byte aligned", fn);
+  if (q_img && q_img_bytes < mix::f8_a_image_layout(M, N).total)
+    return fail(MIX_E_WORKSPACE, "%s: output image buffer %zu < %zu bytes", fn, q_img_bytes,
+                mix::f8_a_image_layout(M, N).total);
+  return hip_status(mix::launch_gemm_images_q(b_fmt == MX_FP4, a_img, b_img, b_codes, M, N, K, c, ldc, q_codes,
+                                              q_shared, q_img, (hipStream_t)stream),
+                    fn);
+}
+
 mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, int64_t ldk, float* mu, void* stream) {
   g_err.clear();
   if (mix_status_t st = check_dtype(dtype)) return st;

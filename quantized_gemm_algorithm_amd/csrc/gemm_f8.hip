@@ -111,10 +111,15 @@ struct F8Args {
   const uint8_t* as_p;    // [K/128][tiles_m][1024] E8M0, permuted
   const uint8_t* b;       // [N, K/2] FP4 codes or [N, K] E4M3
   const uint8_t* bs_p;    // [K/128][bs_tn][1024] E8M0, permuted
-  void* c;
+  void* c;                // C [M, ldc] (may be NULL when the output is quantized)
   int64_t ldc;
   int M, N, K;
   int bs_tn;              // 256-row tiles of the B image (its scale layout)
+  // output quantization (k_gemm_f8<..., OQ = 1>): the bf16 rounding of C as MiX-4.5b along N
+  uint8_t* qc;            // codes [M, N/2]
+  uint16_t* qsh;          // shared fields [M, N/32]
+  uint8_t* qa8;           // the A image of C for a next product (K = N): E4M3 [M, N], or NULL
+  uint8_t* qas_p;         //   and its permuted scales [N/128][ceil(M/256)][1024]
 };
 
 __device__ __forceinline__ int f8_xcd_tile(int bid, int nt) {
@@ -200,7 +205,7 @@ __device__ __forceinline__ void f8_tile(int bid, int tiles_m, int tiles_n, int& 
 // MFMAs run). The MFMA computes C^T tiles: its A operand is the weight fragment (rows n), its B
 // operand the activation fragment (rows m), so result register k of lane l holds
 // C[m = l & 31][n = 8 (k >> 2) + 4 (l >> 5) + (k & 3)].
-template <int B_FP4, int C_BF16>
+template <int B_FP4, int C_BF16, int OQ = 0>
 __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int SB = F8Stage<B_FP4>::BYTES;
@@ -307,6 +312,27 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
       const int row = it * RPI + lane / CPR, ch = lane % CPR;
       const uint4 v = *(const uint4*)(reg + row * PITCH + ch * 16);
       const int gm = mw + 32 * i + row, gn = nw + ch * EPL;
+      if (OQ) {
+        // this lane's 8 bf16 outputs are a MiX sub-block, the 4 lanes of a quad one 32-column
+        // block (N is a multiple of 32, so quads are in or past N together)
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        int emax;
+        uint32_t m, e0, e1;
+        const uint32_t word = mix_quant_lane_bf16_img<1, true>(w4, emax, m, e0, e1);
+        const int q = ch & 3;
+        const uint32_t f = quad_or_dpp((q == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * q)));
+        if (gm < g.M && gn < g.N) {
+          *(uint32_t*)(g.qc + (int64_t)gm * (g.N >> 1) + (gn >> 1)) = word;
+          if (q == 0) g.qsh[(int64_t)gm * (g.N >> 5) + (gn >> 5)] = (uint16_t)f;
+          if (g.qa8) {
+            *(uint2*)(g.qa8 + (int64_t)gm * g.N + gn) = make_uint2(e0, e1);
+            if (q == 0)
+              g.qas_p[((int64_t)(gn >> 7) * ((g.M + FT - 1) / FT) + (gm >> 8)) * 1024 +
+                      f8_scale_pos(gm & (FT - 1), (gn >> 5) & 3)] = (uint8_t)(emax + 126);
+          }
+        }
+        if (!g.c) continue;
+      }
       if (gm >= g.M) continue;
       uint8_t* out = (uint8_t*)g.c + ((int64_t)gm * g.ldc + gn) * ES;
       if (vec_ok && gn + EPL <= g.N) {
@@ -505,19 +531,19 @@ constexpr size_t f8_lds_bytes() {
   return ring > epi ? ring : epi;
 }
 
-template <int B_FP4, int C_BF16>
+template <int B_FP4, int C_BF16, int OQ = 0>
 static hipError_t launch_f8(const F8Args& a, hipStream_t s) {
   constexpr size_t lds = f8_lds_bytes<B_FP4, C_BF16>();
   static_assert(lds <= 160 * 1024, "LDS budget");
   static bool attr = false;  // raise the dynamic LDS limit once per instantiation
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_f8<B_FP4, C_BF16>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_f8<B_FP4, C_BF16, OQ>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int tiles = ((a.M + FT - 1) / FT) * ((a.N + FT - 1) / FT);
-  hipLaunchKernelGGL((k_gemm_f8<B_FP4, C_BF16>), dim3(tiles), dim3(F8_THREADS), lds, s, a);
+  hipLaunchKernelGGL((k_gemm_f8<B_FP4, C_BF16, OQ>), dim3(tiles), dim3(F8_THREADS), lds, s, a);
   return hipGetLastError();
 }
 
@@ -612,6 +638,38 @@ hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const vo
   if (M <= 16) return launch_gemv_f8(b_fp4, c_bf16, a, s);
   if (b_fp4) return c_bf16 ? launch_f8<1, 1>(a, s) : launch_f8<1, 0>(a, s);
   return c_bf16 ? launch_f8<0, 1>(a, s) : launch_f8<0, 0>(a, s);
+}
+
+// The product from the two images with its output quantized: MiX-4.5b codes and shared fields of
+// the bf16 rounding of C along N, and optionally that output's A image for a next product; C
+// itself (bf16) only if c is given. M > 16: in the tiled product's epilogue; M <= 16: the weight
+// stream writes C (required then) and the quantizer codes it.
+hipError_t launch_gemm_images_q(int b_fp4, const void* a_img, const void* b_img, const uint8_t* b_codes, int64_t M,
+                                int64_t N, int64_t K, void* c, int64_t ldc, uint8_t* q_codes, void* q_shared,
+                                void* q_img, hipStream_t s) {
+  if (M <= 16) {
+    hipError_t e = launch_gemm_images(b_fp4, 1, a_img, b_img, b_codes, M, N, K, c, ldc, s);
+    if (e != hipSuccess) return e;
+    if (q_img) return launch_mix_quantize_img(1, c, 1, M, N, ldc, q_codes, q_shared, q_img, s);
+    return launch_mix_quantize(1, c, 1, M, N, ldc, q_codes, q_shared, s);
+  }
+  const F8AImage LA = f8_a_image_layout(M, K);
+  const F8BImage LB = f8_b_image_layout(b_fp4, N, K);
+  F8Args a{};
+  a.a8 = (const uint8_t*)a_img + LA.a8;
+  a.as_p = (const uint8_t*)a_img + LA.as_p;
+  a.b = b_fp4 ? b_codes : (const uint8_t*)b_img + LB.b8;
+  a.bs_p = (const uint8_t*)b_img + LB.bs_p;
+  a.c = c; a.ldc = ldc; a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  a.bs_tn = (int)((N + FT - 1) / FT);
+  a.qc = q_codes;
+  a.qsh = (uint16_t*)q_shared;
+  if (q_img) {
+    const F8AImage LQ = f8_a_image_layout(M, N);
+    a.qa8 = (uint8_t*)q_img + LQ.a8;
+    a.qas_p = (uint8_t*)q_img + LQ.as_p;
+  }
+  return b_fp4 ? launch_f8<1, 1, 1>(a, s) : launch_f8<0, 1, 1>(a, s);
 }
 
 hipError_t launch_gemm_f8(int a_fmt, int b_fp4, int c_bf16, const uint8_t* a_codes, const void* a_shared,

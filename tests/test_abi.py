@@ -149,3 +149,24 @@ def test_image_validation(lib):
     # 32-bit offsets inside the tiled kernel: a 2^31-byte A image is refused (M > 16)
     assert lib.mix_mx_gemm_images(1, FAKE, FAKE, FAKE, 1 << 20, 256, 2048, FAKE, 0, 256, None) == MIX_E_UNSUPPORTED
     assert lib.mix_mx_gemm_workspace_bytes(1, 1, 1 << 20, 256, 2048) == 0
+
+
+def test_image_product_with_quantized_output_validation(lib):
+    f = lib.mix_mx_gemm_images_quantize
+    A16 = P(0x10010)
+    BIG = 1 << 30
+    # (b_fmt, a_img, b_img, b_codes, M, N, K, c, ldc, q_codes, q_shared, q_img, q_img_bytes, stream)
+    assert f(2, FAKE, FAKE, FAKE, 64, 256, 128, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_ENUM
+    assert f(1, FAKE, FAKE, FAKE, 64, 250, 128, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_SHAPE   # N % 32
+    assert f(1, FAKE, FAKE, FAKE, 64, 256, 100, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_SHAPE   # K % 128
+    assert f(1, FAKE, FAKE, FAKE, 64, 160, 128, None, 0, FAKE, FAKE, FAKE, BIG, None) == MIX_E_SHAPE  # image: N % 128
+    assert f(1, FAKE, FAKE, FAKE, 8, 256, 128, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_NULL     # M <= 16 needs c
+    assert f(1, FAKE, FAKE, FAKE, 64, 256, 128, None, 0, None, FAKE, None, 0, None) == MIX_E_NULL
+    assert f(1, FAKE, FAKE, None, 64, 256, 128, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_NULL    # FP4 codes
+    assert f(1, A16, FAKE, FAKE, 64, 256, 128, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_ALIGN
+    assert f(1, FAKE, FAKE, FAKE, 64, 256, 128, None, 0, FAKE, FAKE, A16, BIG, None) == MIX_E_ALIGN
+    assert f(1, FAKE, FAKE, FAKE, 64, 256, 128, None, 0, P(0x10002), FAKE, None, 0, None) == MIX_E_ALIGN
+    assert f(1, FAKE, FAKE, FAKE, 64, 256, 128, FAKE, 100, FAKE, FAKE, None, 0, None) == MIX_E_SHAPE  # ldc < N
+    assert f(1, FAKE, FAKE, FAKE, 64, 256, 128, None, 0, FAKE, FAKE, FAKE, 1000, None) == MIX_E_WORKSPACE
+    assert f(1, None, None, None, 0, 256, 128, None, 0, None, None, None, 0, None) == MIX_OK         # empty
+

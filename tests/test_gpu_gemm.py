@@ -104,6 +104,52 @@ def test_gemm_images(a_fmt, b_fmt, M, N, K):
         assert torch.equal(ws, got)
 
 
+@pytest.mark.parametrize("b_fmt,M,N,K", [("fp4", 300, 512, 256), ("int4", 64, 256, 128), ("fp4", 1000, 384, 384),
+                                         ("fp4", 257, 640, 512), ("fp4", 8, 512, 256), ("int4", 16, 384, 128),
+                                         ("fp4", 4096, 18944, 3584)])
+def test_gemm_images_quantized_output(b_fmt, M, N, K):
+    """The product with its output quantized in the epilogue equals the unfused flow bit for bit:
+    C in bf16, then mix_quantize_gemm of that C (codes, shared fields and the next product's A
+    image); and the codes are the oracle's MiX-4.5b coding of the GPU's bf16 C."""
+    q = _lib()
+    if M * N * K > 1e9:
+        # full size: the workload's own inputs, coded by the GPU quantizers (bit-exact with the
+        # oracle in the quantizer tests)
+        g = synth.prefill_linear()
+        A, S, _ = q.mix_quantize_gemm(dev_bf16(g["x"]), "4.5b")
+        B, Bs = q.mx_quantize(dev_bf16(g["w_t"]), b_fmt)
+    else:
+        rng = np.random.default_rng(3 * M + 7 * N + K)
+        x = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-6, 6, (M, K)))).astype(np.float32)
+        w = (0.05 * rng.standard_normal((N, K))).astype(np.float32)
+        ac, as_, bc, bs = _code(x, w, "4.5b", b_fmt)
+        A, S, B, Bs = _to_dev(ac, as_, bc, bs, "4.5b")
+    ai = q.mix_gemm_a_image(A, S, "4.5b")
+    bi = q.mx_gemm_b_image(B, Bs, b_fmt)
+    c_ref = q.mix_mx_gemm_images(ai, bi, out_dtype=torch.bfloat16)
+    nq = q.mix_gemm_a_image_bytes(M, N)
+    rc, rs, rimg = q.mix_quantize_gemm(c_ref, "4.5b", image=torch.zeros(nq, dtype=torch.uint8, device="cuda"))
+    c1, qc1, qs1, qi1 = q.mix_mx_gemm_images_quantize(ai, bi, keep_c=True,
+                                                      q_image=torch.zeros(nq, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int16), c_ref.view(torch.int16)), "C differs from the image product"
+    assert torch.equal(qc1, rc) and torch.equal(qs1, rs), "fused output codes differ from the quantizer's"
+    assert torch.equal(qi1.buf, rimg.buf), "fused output image differs from the quantizer's"
+    if M > 16:   # without C (only the codes, shared fields and image leave the epilogue)
+        c2, qc2, qs2, qi2 = q.mix_mx_gemm_images_quantize(
+            ai, bi, keep_c=False, q_image=torch.zeros(nq, dtype=torch.uint8, device="cuda"))
+        torch.cuda.synchronize()
+        assert c2 is None
+        assert torch.equal(qc2, rc) and torch.equal(qs2, rs) and torch.equal(qi2.buf, rimg.buf)
+    # against the oracle, on a sample of rows at full size
+    rows = np.arange(M) if M <= 1024 else np.unique(np.linspace(0, M - 1, 64).astype(np.int64))
+    cb = host(c_ref)[rows]
+    oc, osh = o_mix_q(cb, "4.5b", "bf16")
+    assert_codes_equal(host(qc1)[rows], oc, "fused output codes vs oracle")
+    assert_codes_equal(host(qs1)[rows], osh, "fused output shared vs oracle")
+
+
+
 @pytest.mark.parametrize("a_fmt,b_fmt", PAIRS)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (5, 300, 3584), (16, 18, 4096), (16, 5000, 4224), (3, 700, 896),
                                    (16, 40000, 256), (7, 4099, 1152)])
