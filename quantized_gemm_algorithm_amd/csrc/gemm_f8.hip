@@ -15,10 +15,13 @@
 // operand.
 //
 // The GEMM streams both operands global->LDS with global_load_lds_dwordx4 (no registers, no
-// VALU). Each workgroup computes one 256 x 256 tile with 8 waves (two per SIMD, so one wave's
-// LDS reads and barrier wait overlap the other's MFMAs), each wave 64 x 128 outputs (2 x 4 MFMAs
-// of 32 x 32 per 64-wide K half, 128 fp32 accumulators per lane). A two-stage LDS ring carries
-// one barrier per 128-wide K step. Tiles are ordered in bands of 8 tile rows and split into
+// VALU). Each workgroup computes one 256 x 256 tile with 8 waves, each wave 64 x 128 outputs
+// (2 x 4 MFMAs of 32 x 32 per 64-wide K half, 128 fp32 accumulators per lane). The waves form two
+// groups with one wave of each on every SIMD, and the groups alternate between reading a K step's
+// operands from LDS into registers and running the 16 MFMAs of a step from registers, so a SIMD's
+// matrix pipe always has one wave feeding it (a barrier between phases). An LDS ring of three
+// stages (two for E4M3 weights) lets a step's copies land while two phases run. Tiles are
+// ordered in bands of 8 tile rows and split into
 // XCD-contiguous chunks, so the tiles an XCD runs at once share A and B panels in its L2. Block
 // scales are laid out per (K step, tile) in the order the lanes read them: one 8-byte LDS read
 // gives a lane all its scales for a K step, and the MFMA's scale op_sel picks the byte. The
@@ -103,7 +106,9 @@ struct F8Stage {
   static constexpr int AS_OFF = A_BYTES + B_BYTES;
   static constexpr int BS_OFF = AS_OFF + 1024;
   static constexpr int BYTES = BS_OFF + 1024;
-  static constexpr int NS = 2;   // ring stages (a third, measured, was slower)
+  static constexpr int NS = B_FP4 ? 3 : 2;   // ring stages within 160 KB of LDS
+  // copy instructions per issuing wave and K step: A (8), B (4 FP4 or 8 E4M3), two scale dwords
+  static constexpr int PER = 8 + (B_FP4 ? 4 : 8) + 2;
 };
 
 struct F8Args {
@@ -136,54 +141,66 @@ constexpr int F8_THREADS = 512;   // 8 waves: 4 along M x 2 along N, 64 x 128 ou
 __device__ __forceinline__ int aswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int bswz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
-// Copies of one K step of tile (tm, tn) into stage buffer `st`; each wave copies whole
-// 1 KB runs (64 lanes x 16 bytes) of the stage image.
+// Copies of one K step of tile (tm, tn) into the stage at LDS byte address `st`, issued by the
+// four waves of the copying group (w = 0..3, wave-uniform); each copies whole 1 KB runs (64 lanes x
+// 16 bytes) of the stage image. A and E4M3 B: chunk q = 256 p + 64 w + lane lands at LDS byte 16 q
+// and holds (row q / 8, logical chunk (q % 8) ^ aswz(row)) of the operand tile; FP4 B: (row q / 4,
+// chunk (q % 4) ^ bswz(row)). The swizzle depends on row bits the copy index p does not touch, so a
+// lane keeps one chunk column across p. Rows past M (N) repeat the last row; they are never
+// stored. The per-copy offsets are recomputed at each call (the empty asm hides the lane index
+// from loop-invariant hoisting), which costs a few VALU instructions instead of 8 to 16 registers
+// held across the K loop.
 template <int B_FP4>
-__device__ __forceinline__ void f8_issue(const F8Args& g, uint8_t* st, int tm, int tn, int tiles_m, int tiles_n,
-                                         int ks) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void f8_issue(const F8Args& g, uint32_t st, int tm, int tn, int tiles_m, int ks, int w,
+                                         int lane) {
   const int m0 = tm * FT, n0 = tn * FT, k0 = ks * FK;
-  // A: 2048 16-byte chunks; chunk q lands at LDS byte 16 q; q -> (row q/8, slot q%8) holding
-  // logical chunk slot ^ aswz(row) of that row (rows past M repeat row M-1; never stored).
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  {
+    const int ta = w * 8 + (ln >> 3);            // tile row of copy p = 0; copy p reads row 32 p + ta
+    const int ca = (ln & 7) ^ aswz(ta);
+    const int lim = g.M - 1 - m0;
+    const uint8_t* base = g.a8 + (size_t)m0 * g.K + k0;
 #pragma unroll
-  for (int p = 0; p < 4; p++) {
-    const int q = p * F8_THREADS + wave * 64 + lane;
-    const int row = q >> 3, slot = q & 7;
-    const int c = slot ^ aswz(row);
-    const int grow = min(m0 + row, g.M - 1);
-    dma16(g.a8 + (uint32_t)(grow * g.K + k0 + 16 * c),
-          __builtin_amdgcn_readfirstlane(lds_addr(st + (p * F8_THREADS + wave * 64) * 16)));
+    for (int p = 0; p < 8; p++)
+      dma16s(base, (uint32_t)(min(32 * p + ta, lim) * g.K + 16 * ca), st + (p * 256 + w * 64) * 16);
   }
   if (B_FP4) {
-    // B: 1024 chunks; (row q/4, slot q%4) holds logical chunk slot ^ bswz(row)
+    const int tb = w * 16 + (ln >> 2);           // copy p reads row 64 p + tb (64-byte rows)
+    const int cb = (ln & 3) ^ bswz(tb);
+    const int lim = g.N - 1 - n0;
+    const uint8_t* base = g.b + (size_t)n0 * (g.K >> 1) + (k0 >> 1);
 #pragma unroll
-    for (int p = 0; p < 2; p++) {
-      const int q = p * F8_THREADS + wave * 64 + lane;
-      const int row = q >> 2, slot = q & 3;
-      const int c = slot ^ bswz(row);
-      const int grow = min(n0 + row, g.N - 1);
-      dma16(g.b + (uint32_t)(grow * (g.K >> 1) + (k0 >> 1) + 16 * c),
-            __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::A_BYTES + (p * F8_THREADS + wave * 64) * 16)));
-    }
+    for (int p = 0; p < 4; p++)
+      dma16s(base, (uint32_t)(min(64 * p + tb, lim) * (g.K >> 1) + 16 * cb),
+             st + F8Stage<B_FP4>::A_BYTES + (p * 256 + w * 64) * 16);
   } else {
+    const int tb = w * 8 + (ln >> 3);
+    const int cb = (ln & 7) ^ aswz(tb);
+    const int lim = g.N - 1 - n0;
+    const uint8_t* base = g.b + (size_t)n0 * g.K + k0;
 #pragma unroll
-    for (int p = 0; p < 4; p++) {
-      const int q = p * F8_THREADS + wave * 64 + lane;
-      const int row = q >> 3, slot = q & 7;
-      const int c = slot ^ aswz(row);
-      const int grow = min(n0 + row, g.N - 1);
-      dma16(g.b + (uint32_t)(grow * g.K + k0 + 16 * c),
-            __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::A_BYTES + (p * F8_THREADS + wave * 64) * 16)));
-    }
+    for (int p = 0; p < 8; p++)
+      dma16s(base, (uint32_t)(min(32 * p + tb, lim) * g.K + 16 * cb),
+             st + F8Stage<B_FP4>::A_BYTES + (p * 256 + w * 64) * 16);
   }
-  // scales: the (K step, tile) 1 KB blocks are contiguous; waves 0-3 copy A's, waves 4-7 B's
-  if (wave < 4)
-    dma4(g.as_p + (uint32_t)((ks * tiles_m + tm) * 1024 + wave * 256 + lane * 4),
-         __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::AS_OFF + wave * 256)));
-  else
-    dma4(g.bs_p + (uint32_t)((ks * g.bs_tn + tn) * 1024 + (wave - 4) * 256 + lane * 4),
-         __builtin_amdgcn_readfirstlane(lds_addr(st + F8Stage<B_FP4>::BS_OFF + (wave - 4) * 256)));
+  // scales: the (K step, tile) 1 KB blocks are contiguous; a wave copies 256 bytes of each
+  dma4(g.as_p + (uint32_t)((ks * tiles_m + tm) * 1024 + w * 256 + ln * 4), st + F8Stage<B_FP4>::AS_OFF + w * 256);
+  dma4(g.bs_p + (uint32_t)((ks * g.bs_tn + tn) * 1024 + w * 256 + ln * 4), st + F8Stage<B_FP4>::BS_OFF + w * 256);
 }
+
+// Workgroup barrier that the compiler neither moves memory accesses across (the empty asm with a
+// memory clobber) nor schedules instructions across; it waits for nothing by itself.
+__device__ __forceinline__ void f8_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt lgkmcnt(0) alone: this wave's LDS reads have returned
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -200,21 +217,30 @@ __device__ __forceinline__ void f8_tile(int bid, int tiles_m, int tiles_n, int& 
   tm = band * GM + (rem - tn * gm);
 }
 
-// One 256 x 256 output tile per workgroup; a two-stage LDS ring with one barrier per 128-wide K
-// step (the next step's copies are issued right after the barrier and land while this step's
-// MFMAs run). The MFMA computes C^T tiles: its A operand is the weight fragment (rows n), its B
-// operand the activation fragment (rows m), so result register k of lane l holds
-// C[m = l & 31][n = 8 (k >> 2) + 4 (l >> 5) + (k & 3)].
+// One 256 x 256 output tile per workgroup. The MFMA computes C^T tiles: its A operand is the
+// weight fragment (rows n), its B operand the activation fragment (rows m), so result register k
+// of lane l holds C[m = l & 31][n = 8 (k >> 2) + 4 (l >> 5) + (k & 3)].
+//
+// Main loop: ping-pong between two groups of four waves, one wave of each group per SIMD. Every
+// phase ends with a workgroup barrier; in a phase one group reads the operands of a K step from
+// LDS into registers while the other runs the 16 MFMAs of its previous step from registers, so
+// each SIMD's matrix pipe is fed by one wave while the other waits on LDS. Group 0 reads step j in
+// phase 2j and multiplies in 2j + 1; group 1 runs one phase later. Group 0 also issues the
+// global->LDS copies: step j + NS - 1 in phase 2j, into the ring slot that step j - 1 left (both
+// groups read it by phase 2j - 1), and it waits for step j + 1 at the end of phase 2j + 1, so a
+// copy has 2 (NS - 1) phases to land.
 template <int B_FP4, int C_BF16, int OQ = 0>
 __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int SB = F8Stage<B_FP4>::BYTES;
   constexpr int NS = F8Stage<B_FP4>::NS;
+  constexpr int PER = F8Stage<B_FP4>::PER;
   const int tiles_m = (g.M + FT - 1) / FT, tiles_n = (g.N + FT - 1) / FT;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, gq = lane >> 5;
   const int nk = g.K / FK;
+  const uint32_t lds0 = lds_addr(smem);
   // this lane's 8 scale bytes [h][sub-tile] in the permuted 1 KB block (see f8_scale_pos)
   const int sc_a = (((wm >> 1) * 2 + gq) * 32 + r) * 8;
   const int sc_b = ((wn * 2 + gq) * 32 + r) * 8;
@@ -222,7 +248,6 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
 
   int tm, tn;
   f8_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  f8_issue<B_FP4>(g, smem, tm, tn, tiles_m, tiles_n, 0);
 
   v16f acc[2][4];
 #pragma unroll
@@ -230,54 +255,92 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = v16f{};
 
-  for (int kt = 0; kt < nk; kt++) {
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();   // step kt is in LDS; every wave is done with step kt-1's slot
-    if (kt + 1 < nk) f8_issue<B_FP4>(g, smem + ((kt + 1) % NS) * SB, tm, tn, tiles_m, tiles_n, kt + 1);
-    const uint8_t* st = smem + (kt % NS) * SB;
+  // operands of one K step, held in registers between a wave's read phase and its MFMA phase
+  v8i xf[2][2];
+  v8i wf[2][4];
+  int xsw[2], wsw[2];
+
+  auto read_step = [&](int slot) {
+    const uint8_t* st = smem + slot * SB;
     const uint8_t* sa = st;
     const uint8_t* sbm = st + F8Stage<B_FP4>::A_BYTES;
     const uint2 xs8 = *(const uint2*)(st + F8Stage<B_FP4>::AS_OFF + sc_a);
     const uint2 ws8 = *(const uint2*)(st + F8Stage<B_FP4>::BS_OFF + sc_b);
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-      const int xsw = (int)((h ? xs8.y : xs8.x) >> sub_a);
-      const int wsw = (int)(h ? ws8.y : ws8.x);
-      v8i xf[2];
+      xsw[h] = (int)((h ? xs8.y : xs8.x) >> sub_a);
+      wsw[h] = (int)(h ? ws8.y : ws8.x);
 #pragma unroll
       for (int i = 0; i < 2; i++) {
         const int row = 64 * wm + 32 * i + r;
         const int c0 = 4 * h + gq, c1 = 4 * h + 2 + gq;
         const uint4 lo = *(const uint4*)(sa + row * 128 + ((c0 ^ aswz(row)) * 16));
         const uint4 hi = *(const uint4*)(sa + row * 128 + ((c1 ^ aswz(row)) * 16));
-        xf[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        xf[h][i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const int row = 128 * wn + 32 * j + r;
-        v8i wf;
         if (B_FP4) {
           // FP4 operands read only the low 4 registers of the 8-register tuple
           const int c = 2 * h + gq;
           const v4i w = *(const v4i*)(sbm + row * 64 + ((c ^ bswz(row)) * 16));
-          wf = __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
+          wf[h][j] = __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
         } else {
           const int c0 = 4 * h + gq, c1 = 4 * h + 2 + gq;
           const v4i lo = *(const v4i*)(sbm + row * 128 + ((c0 ^ aswz(row)) * 16));
           const v4i hi = *(const v4i*)(sbm + row * 128 + ((c1 ^ aswz(row)) * 16));
-          wf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          wf[h][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        // the scale operands' op_sel picks byte j of the weight word and byte i of the
-        // activation word
-#define F8_MFMA(I, J)                                                                                      \
-  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, xf[I], acc[I][J], B_FP4 ? 4 : 0, 0, J, wsw, \
-                                                              I, xsw)
-        if (j == 0) { F8_MFMA(0, 0); F8_MFMA(1, 0); }
-        if (j == 1) { F8_MFMA(0, 1); F8_MFMA(1, 1); }
-        if (j == 2) { F8_MFMA(0, 2); F8_MFMA(1, 2); }
-        if (j == 3) { F8_MFMA(0, 3); F8_MFMA(1, 3); }
-#undef F8_MFMA
       }
+    }
+  };
+  // the scale operands' op_sel picks byte J of the weight word and byte I of the activation word
+  auto mfma_step = [&]() {
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#define F8_MFMA(I, J)                                                                                      \
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[h][J], xf[h][I], acc[I][J], B_FP4 ? 4 : 0, 0, J, \
+                                                              wsw[h], I, xsw[h])
+      F8_MFMA(0, 0); F8_MFMA(1, 0); F8_MFMA(0, 1); F8_MFMA(1, 1);
+      F8_MFMA(0, 2); F8_MFMA(1, 2); F8_MFMA(0, 3); F8_MFMA(1, 3);
+#undef F8_MFMA
+    }
+  };
+
+  if (wave < 4) {
+    // group 0: copies, then reads step j in phase 2j, multiplies in phase 2j + 1
+#pragma unroll
+    for (int s = 0; s < NS - 1; s++)
+      if (s < nk) f8_issue<B_FP4>(g, lds0 + s * SB, tm, tn, tiles_m, s, wave, lane);
+    if (NS == 3 && nk > 1) wait_vmcnt<PER>(); else wait_vmcnt<0>();   // step 0 has landed
+    f8_sync();
+    int rs = 0;                 // ring slot of step j
+    int is = NS - 1;            // ring slot of step j + NS - 1
+    for (int j = 0; j < nk; j++) {
+      if (j + NS - 1 < nk) f8_issue<B_FP4>(g, lds0 + is * SB, tm, tn, tiles_m, j + NS - 1, wave, lane);
+      read_step(rs);
+      wait_lgkm0();
+      f8_sync();
+      mfma_step();
+      if (NS == 3 && j + 2 < nk) wait_vmcnt<PER>(); else wait_vmcnt<0>();   // step j + 1 has landed
+      f8_sync();
+      rs = rs + 1 == NS ? 0 : rs + 1;
+      is = is + 1 == NS ? 0 : is + 1;
+    }
+    f8_sync();   // group 1's last MFMA phase
+  } else {
+    // group 1: one phase behind
+    f8_sync();
+    f8_sync();
+    int rs = 0;
+    for (int j = 0; j < nk; j++) {
+      read_step(rs);
+      wait_lgkm0();
+      f8_sync();
+      mfma_step();
+      f8_sync();
+      rs = rs + 1 == NS ? 0 : rs + 1;
     }
   }
 
