@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="run the step untimed for this long before the warm-up steps (clock ramp of an idle GPU)")
     ap.add_argument("--workload", default="prefill_linear",
                     choices=["prefill_linear", "vision_linear", "attention_prefill", "decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -85,6 +87,22 @@ def measured_traffic(workload):
         except OSError:
             return None
     return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
+
+
+def settle(torch, fn, ms):
+    """Run fn(i) untimed for at least `ms` of wall time (synchronizing every few calls, so that the GPU
+    is busy throughout). An idle MI355X needs tens of ms of sustained load to reach its steady clocks:
+    the prefill GEMM measured 256-313 us per launch in its first ~10 ms and ~223 us from ~30 ms on,
+    the quantizer ~13.5 us, then 12.3 us. Timing starts from that steady state."""
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        fn(i)
+        i += 1
+        if i % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
 
 
 def rotating(n_bytes_each, min_total=320 << 20):
@@ -156,6 +174,7 @@ def bench_linear(torch, q, args, which):
         e2 = marks.mark() if marks else None
         return e0, e1, e2
 
+    settle(torch, step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -256,7 +275,7 @@ def bench_linear(torch, q, args, which):
         else "A-MiX4.25b x W-MXINT4 GEMM TFLOP/s + quantizer GB/s (% of MI355X peak)",
         "value": flops / (ms_step * 1e-3) / 1e12,
         "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "e4m3xe2m1->f32" if b_fmt == "fp4" else "e4m3xe4m3->f32",
         "data": "synthetic",
@@ -337,6 +356,7 @@ def bench_decode(torch, q, args):
         e3 = marks.mark() if marks else None
         return e0, e1, e2, e3
 
+    settle(torch, step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -363,6 +383,7 @@ def bench_decode(torch, q, args):
         with torch.cuda.graph(gr):
             step(si)
         graphs.append(gr)
+    settle(torch, lambda i: graphs[i % nset].replay(), args.settle_ms)
     for i in range(args.warmup):
         graphs[i % nset].replay()
     torch.cuda.synchronize()
@@ -386,7 +407,7 @@ def bench_decode(torch, q, args):
         "metric": "decode GB/s (% of MI355X HBM peak)",
         "value": step_bytes / (ms_step * 1e-3) / 1e9,
         "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "e4m3xe2m1->f32", "data": "synthetic",
         "config": {"workload": "decode_step_b16_l8192", "B": B, "K": K, "N": N, "L": L, "Hq": Hq, "Hkv": Hkv,
@@ -448,6 +469,7 @@ def bench_attention(torch, q, args):
     def step():
         q.mix_attn_prefill(qd, kd, vd, causal=True, workspace=ws)
 
+    settle(torch, lambda i: step(), args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -466,7 +488,7 @@ def bench_attention(torch, q, args):
     res = {
         "metric": "prefill attention TFLOP/s (causal-exact flops)",
         "value": tf, "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "e4m3xe2m1->f32", "data": "synthetic",
         "config": {"workload": "prefill_attention_t4096_h28_kv4_d128", "T": T, "Hq": Hq, "Hkv": Hkv, "d": d,
@@ -500,6 +522,7 @@ def vendor_gemm(torch, args):
     gen = torch.Generator(device=dev).manual_seed(0)
 
     def timeit(fn):
+        settle(torch, lambda i: fn(), args.settle_ms)
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()

@@ -127,12 +127,6 @@ struct F8Args {
   uint8_t* qas_p;         //   and its permuted scales [N/128][ceil(M/256)][1024]
 };
 
-__device__ __forceinline__ int f8_xcd_tile(int bid, int nt) {
-  const int x = bid & 7, idx = bid >> 3;
-  const int base = nt >> 3, rem = nt & 7;
-  return x * base + min(x, rem) + idx;
-}
-
 constexpr int F8_THREADS = 512;   // 8 waves: 4 along M x 2 along N, 64 x 128 outputs each
 
 // LDS slot of 16-byte chunk c of a stage row: 128-byte rows (E4M3) take c ^ aswz(row), 64-byte rows
@@ -204,11 +198,12 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// Tile order: XCD-contiguous chunks of a banded order (bands of GM tile rows, column by column
-// inside a band), so the ~32 tiles an XCD runs at once share a few A and B panels in its L2.
-__device__ __forceinline__ void f8_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+// Tile order: a banded order (bands of GM tile rows, column by column inside a band) cut into 8
+// contiguous chunks, one per XCD (workgroup b runs on XCD b % 8). The workgroups of an XCD take
+// their chunk's tiles in turn, so the ~32 tiles an XCD runs at once share a few A and B panels in
+// its L2.
+__device__ __forceinline__ void f8_tile(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int GM = 8;
-  const int t = f8_xcd_tile(bid, tiles_m * tiles_n);
   const int band_sz = GM * tiles_n;
   const int band = t / band_sz;
   const int rem = t - band * band_sz;
@@ -217,9 +212,10 @@ __device__ __forceinline__ void f8_tile(int bid, int tiles_m, int tiles_n, int& 
   tm = band * GM + (rem - tn * gm);
 }
 
-// One 256 x 256 output tile per workgroup. The MFMA computes C^T tiles: its A operand is the
-// weight fragment (rows n), its B operand the activation fragment (rows m), so result register k
-// of lane l holds C[m = l & 31][n = 8 (k >> 2) + 4 (l >> 5) + (k & 3)].
+// Persistent: one workgroup per CU takes 256 x 256 output tiles of its XCD's chunk in turn. The
+// MFMA computes C^T tiles: its A operand is the weight fragment (rows n), its B operand the
+// activation fragment (rows m), so result register k of lane l holds
+// C[m = l & 31][n = 8 (k >> 2) + 4 (l >> 5) + (k & 3)].
 //
 // Main loop: ping-pong between two groups of four waves, one wave of each group per SIMD. Every
 // phase ends with a workgroup barrier; in a phase one group reads the operands of a K step from
@@ -228,7 +224,8 @@ __device__ __forceinline__ void f8_tile(int bid, int tiles_m, int tiles_n, int& 
 // phase 2j and multiplies in 2j + 1; group 1 runs one phase later. Group 0 also issues the
 // global->LDS copies: step j + NS - 1 in phase 2j, into the ring slot that step j - 1 left (both
 // groups read it by phase 2j - 1), and it waits for step j + 1 at the end of phase 2j + 1, so a
-// copy has 2 (NS - 1) phases to land.
+// copy has 2 (NS - 1) phases to land. Steps 0 .. NS - 2 of the next tile are issued before the
+// epilogue, which stages C through the last ring slot, so their latency hides behind it.
 template <int B_FP4, int C_BF16, int OQ = 0>
 __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -246,15 +243,22 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   const int sc_b = ((wn * 2 + gq) * 32 + r) * 8;
   const int sub_a = 16 * (wm & 1);   // bit offset of this wave's two A sub-tiles in a 4-byte word
 
+  // this workgroup's tiles: c0 + ix, c0 + ix + gx, ... below c0 + csz
+  const int nt = tiles_m * tiles_n;
+  const int xcd = blockIdx.x & 7, ix = blockIdx.x >> 3;
+  const int gx = ((int)gridDim.x - xcd + 7) >> 3;
+  const int c0 = xcd * (nt >> 3) + min(xcd, nt & 7), csz = (nt >> 3) + (xcd < (nt & 7) ? 1 : 0);
+  int ti = ix;
+  if (ti >= csz) return;
   int tm, tn;
-  f8_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  f8_tile(c0 + ti, tiles_m, tiles_n, tm, tn);
+  if (wave < 4) {
+#pragma unroll
+    for (int s = 0; s < NS - 1; s++)
+      if (s < nk) f8_issue<B_FP4>(g, lds0 + s * SB, tm, tn, tiles_m, s, wave, lane);
+  }
 
   v16f acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = v16f{};
-
   // operands of one K step, held in registers between a wave's read phase and its MFMA phase
   v8i xf[2][2];
   v8i wf[2][4];
@@ -308,108 +312,133 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
     }
   };
 
-  if (wave < 4) {
-    // group 0: copies, then reads step j in phase 2j, multiplies in phase 2j + 1
-#pragma unroll
-    for (int s = 0; s < NS - 1; s++)
-      if (s < nk) f8_issue<B_FP4>(g, lds0 + s * SB, tm, tn, tiles_m, s, wave, lane);
-    if (NS == 3 && nk > 1) wait_vmcnt<PER>(); else wait_vmcnt<0>();   // step 0 has landed
-    f8_sync();
-    int rs = 0;                 // ring slot of step j
-    int is = NS - 1;            // ring slot of step j + NS - 1
-    for (int j = 0; j < nk; j++) {
-      if (j + NS - 1 < nk) f8_issue<B_FP4>(g, lds0 + is * SB, tm, tn, tiles_m, j + NS - 1, wave, lane);
-      read_step(rs);
-      wait_lgkm0();
-      f8_sync();
-      mfma_step();
-      if (NS == 3 && j + 2 < nk) wait_vmcnt<PER>(); else wait_vmcnt<0>();   // step j + 1 has landed
-      f8_sync();
-      rs = rs + 1 == NS ? 0 : rs + 1;
-      is = is + 1 == NS ? 0 : is + 1;
-    }
-    f8_sync();   // group 1's last MFMA phase
-  } else {
-    // group 1: one phase behind
-    f8_sync();
-    f8_sync();
-    int rs = 0;
-    for (int j = 0; j < nk; j++) {
-      read_step(rs);
-      wait_lgkm0();
-      f8_sync();
-      mfma_step();
-      f8_sync();
-      rs = rs + 1 == NS ? 0 : rs + 1;
-    }
-  }
-
-  // Epilogue, staged through LDS so that global stores write whole rows: for each 32-row half
-  // of its sub-tile a wave writes its results into a private LDS region, then reads rows back,
-  // 16 bytes per lane, and stores them. Every wave must be done with the stage buffers first.
+  // epilogue geometry: a pass stages a wave's 32 x CW outputs (128 bytes of each row) in its own
+  // region of the last ring slot, then stores whole 128-byte row segments
   constexpr int ES = C_BF16 ? 2 : 4;                 // output element size
-  constexpr int PITCH = 128 * ES + 8 * ES;           // padded row pitch of the region
+  constexpr int CW = 128 / ES;                       // columns per pass (64 or 32)
+  constexpr int JP = CW / 32;                        // MFMA column blocks per pass (2 or 1)
+  constexpr int PITCH = 128 + 8;                     // padded row pitch of the region
   constexpr int EPL = 16 / ES;                       // outputs per 16-byte chunk
-  constexpr int CPR = 128 / EPL;                     // chunks per row (16 or 32)
-  constexpr int RPI = 64 / CPR;                      // rows per read-back instruction (4 or 2)
-  __builtin_amdgcn_s_barrier();
-  uint8_t* reg = smem + wave * (32 * PITCH);
-  const int mw = tm * FT + 64 * wm, nw = tn * FT + 128 * wn;
+  uint8_t* reg = smem + (NS - 1) * SB + wave * (32 * PITCH);
   const bool vec_ok = (g.ldc % EPL) == 0 && (((uintptr_t)g.c) & 15) == 0;
+
+  while (true) {
 #pragma unroll
-  for (int i = 0; i < 2; i++) {
+    for (int i = 0; i < 2; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        uint8_t* dst = reg + r * PITCH + (32 * j + 8 * q + 4 * gq) * ES;
-        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        if (C_BF16)
-          *(uint2*)dst = make_uint2((uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16),
-                                    (uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16));
-        else
-          *(float4*)dst = make_float4(v0, v1, v2, v3);
+      for (int j = 0; j < 4; j++) acc[i][j] = v16f{};
+
+    if (wave < 4) {
+      // group 0: reads step j in phase 2j, multiplies in phase 2j + 1
+      if (NS == 3 && nk > 1) wait_vmcnt<PER>(); else wait_vmcnt<0>();   // step 0 has landed
+      f8_sync();
+      int rs = 0;                 // ring slot of step j
+      int is = NS - 1;            // ring slot of step j + NS - 1
+      for (int j = 0; j < nk; j++) {
+        if (j + NS - 1 < nk) f8_issue<B_FP4>(g, lds0 + is * SB, tm, tn, tiles_m, j + NS - 1, wave, lane);
+        read_step(rs);
+        wait_lgkm0();
+        f8_sync();
+        mfma_step();
+        if (NS == 3 && j + 2 < nk) wait_vmcnt<PER>(); else wait_vmcnt<0>();   // step j + 1 has landed
+        f8_sync();
+        rs = rs + 1 == NS ? 0 : rs + 1;
+        is = is + 1 == NS ? 0 : is + 1;
       }
+      f8_sync();   // group 1's last MFMA phase
+    } else {
+      // group 1: one phase behind
+      f8_sync();
+      f8_sync();
+      int rs = 0;
+      for (int j = 0; j < nk; j++) {
+        read_step(rs);
+        wait_lgkm0();
+        f8_sync();
+        mfma_step();
+        f8_sync();
+        rs = rs + 1 == NS ? 0 : rs + 1;
+      }
+    }
+
+    // every wave is past its last LDS read of this tile: the ring is free
+    const int cur_tm = tm, cur_tn = tn;
+    ti += gx;
+    const bool more = ti < csz;
+    if (more) {
+      f8_tile(c0 + ti, tiles_m, tiles_n, tm, tn);
+      if (wave < 4) {
 #pragma unroll
-    for (int it = 0; it < 32 / RPI; it++) {
-      const int row = it * RPI + lane / CPR, ch = lane % CPR;
-      const uint4 v = *(const uint4*)(reg + row * PITCH + ch * 16);
-      const int gm = mw + 32 * i + row, gn = nw + ch * EPL;
-      if (OQ) {
-        // this lane's 8 bf16 outputs are a MiX sub-block, the 4 lanes of a quad one 32-column
-        // block (N is a multiple of 32, so quads are in or past N together)
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        int emax;
-        uint32_t m, e0, e1;
-        const uint32_t word = mix_quant_lane_bf16_img<1, true>(w4, emax, m, e0, e1);
-        const int q = ch & 3;
-        const uint32_t f = quad_or_dpp((q == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * q)));
-        if (gm < g.M && gn < g.N) {
-          *(uint32_t*)(g.qc + (int64_t)gm * (g.N >> 1) + (gn >> 1)) = word;
-          if (q == 0) g.qsh[(int64_t)gm * (g.N >> 5) + (gn >> 5)] = (uint16_t)f;
-          if (g.qa8) {
-            *(uint2*)(g.qa8 + (int64_t)gm * g.N + gn) = make_uint2(e0, e1);
-            if (q == 0)
-              g.qas_p[((int64_t)(gn >> 7) * ((g.M + FT - 1) / FT) + (gm >> 8)) * 1024 +
-                      f8_scale_pos(gm & (FT - 1), (gn >> 5) & 3)] = (uint8_t)(emax + 126);
+        for (int s = 0; s < NS - 1; s++)
+          if (s < nk) f8_issue<B_FP4>(g, lds0 + s * SB, tm, tn, tiles_m, s, wave, lane);
+      }
+    }
+
+    // Epilogue, staged through LDS so that global stores write whole 128-byte row segments.
+    const int mw = cur_tm * FT + 64 * wm, nw = cur_tn * FT + 128 * wn;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+#pragma unroll
+      for (int jp = 0; jp < 4 / JP; jp++) {
+#pragma unroll
+        for (int jj = 0; jj < JP; jj++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int j = jp * JP + jj;
+            uint8_t* dst = reg + r * PITCH + (32 * jj + 8 * q + 4 * gq) * ES;
+            const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
+                        v3 = acc[i][j][4 * q + 3];
+            if (C_BF16)
+              *(uint2*)dst = make_uint2((uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16),
+                                        (uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16));
+            else
+              *(float4*)dst = make_float4(v0, v1, v2, v3);
+          }
+#pragma unroll
+        for (int it = 0; it < 4; it++) {
+          const int row = it * 8 + (lane >> 3), ch = lane & 7;
+          const uint4 v = *(const uint4*)(reg + row * PITCH + ch * 16);
+          const int gm = mw + 32 * i + row, gn = nw + jp * CW + ch * EPL;
+          if (OQ) {
+            // this lane's 8 bf16 outputs are a MiX sub-block, the 4 lanes of a quad one 32-column
+            // block (N is a multiple of 32, so quads are in or past N together)
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+            int emax;
+            uint32_t m, e0, e1;
+            const uint32_t word = mix_quant_lane_bf16_img<1, true>(w4, emax, m, e0, e1);
+            const int qd = ch & 3;
+            const uint32_t f = quad_or_dpp((qd == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * qd)));
+            if (gm < g.M && gn < g.N) {
+              *(uint32_t*)(g.qc + (int64_t)gm * (g.N >> 1) + (gn >> 1)) = word;
+              if (qd == 0) g.qsh[(int64_t)gm * (g.N >> 5) + (gn >> 5)] = (uint16_t)f;
+              if (g.qa8) {
+                *(uint2*)(g.qa8 + (int64_t)gm * g.N + gn) = make_uint2(e0, e1);
+                if (qd == 0)
+                  g.qas_p[((int64_t)(gn >> 7) * tiles_m + (gm >> 8)) * 1024 +
+                          f8_scale_pos(gm & (FT - 1), (gn >> 5) & 3)] = (uint8_t)(emax + 126);
+              }
+            }
+            if (!g.c) continue;
+          }
+          if (gm >= g.M) continue;
+          uint8_t* out = (uint8_t*)g.c + ((int64_t)gm * g.ldc + gn) * ES;
+          if (vec_ok && gn + EPL <= g.N) {
+            *(uint4*)out = v;
+          } else {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < EPL; e++) {
+              if (gn + e >= g.N) break;
+              if (C_BF16) ((uint16_t*)out)[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+              else ((uint32_t*)out)[e] = w4[e];
+            }
           }
         }
-        if (!g.c) continue;
-      }
-      if (gm >= g.M) continue;
-      uint8_t* out = (uint8_t*)g.c + ((int64_t)gm * g.ldc + gn) * ES;
-      if (vec_ok && gn + EPL <= g.N) {
-        *(uint4*)out = v;
-      } else {
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < EPL; e++) {
-          if (gn + e >= g.N) break;
-          if (C_BF16) ((uint16_t*)out)[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-          else ((uint32_t*)out)[e] = w4[e];
-        }
       }
     }
+    // the next tile's step NS - 1 goes into the staging slot only after its first barrier, which
+    // every wave reaches with its read-backs returned (their data went to the stores above)
+    if (!more) break;
   }
 }
 
@@ -589,9 +618,23 @@ size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K) {
 
 template <int B_FP4, int C_BF16>
 constexpr size_t f8_lds_bytes() {
+  // the ring, whose last slot (and what lies past it) also holds the epilogue's 8 x 32 x 136 bytes
   const size_t ring = (size_t)F8Stage<B_FP4>::NS * F8Stage<B_FP4>::BYTES;
-  const size_t epi = (size_t)(F8_THREADS / 64) * 32 * (C_BF16 ? 272 : 544);
+  const size_t epi = (size_t)(F8Stage<B_FP4>::NS - 1) * F8Stage<B_FP4>::BYTES + (F8_THREADS / 64) * 32 * 136;
   return ring > epi ? ring : epi;
+}
+
+// compute units of the current device (one persistent GEMM workgroup each)
+static int f8_cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 template <int B_FP4, int C_BF16, int OQ = 0>
@@ -606,7 +649,8 @@ static hipError_t launch_f8(const F8Args& a, hipStream_t s) {
     attr = true;
   }
   const int tiles = ((a.M + FT - 1) / FT) * ((a.N + FT - 1) / FT);
-  hipLaunchKernelGGL((k_gemm_f8<B_FP4, C_BF16, OQ>), dim3(tiles), dim3(F8_THREADS), lds, s, a);
+  const int cus = f8_cu_count();
+  hipLaunchKernelGGL((k_gemm_f8<B_FP4, C_BF16, OQ>), dim3(tiles < cus ? tiles : cus), dim3(F8_THREADS), lds, s, a);
   return hipGetLastError();
 }
 
