@@ -143,10 +143,14 @@ __device__ __forceinline__ int bswz(int row) { return ((row >> 1) ^ (row >> 2)) 
 // lane keeps one chunk column across p. Rows past M (N) repeat the last row; they are never
 // stored. The per-copy offsets are recomputed at each call (the empty asm hides the lane index
 // from loop-invariant hoisting), which costs a few VALU instructions instead of 8 to 16 registers
-// held across the K loop.
-template <int B_FP4>
+// held across the K loop. PART 0 issues the whole step; PART 1 the first half of the A and B copies
+// and the A scales, PART 2 the rest (two groups of waves can then share a step's copies).
+template <int B_FP4, int PART>
 __device__ __forceinline__ void f8_issue(const F8Args& g, uint32_t st, int tm, int tn, int tiles_m, int ks, int w,
                                          int lane) {
+  constexpr int NA = 8, NB = B_FP4 ? 4 : 8;
+  constexpr int A0 = PART == 2 ? NA / 2 : 0, A1 = PART == 1 ? NA / 2 : NA;
+  constexpr int B0 = PART == 2 ? NB / 2 : 0, B1 = PART == 1 ? NB / 2 : NB;
   const int m0 = tm * FT, n0 = tn * FT, k0 = ks * FK;
   int ln = lane;
   asm volatile("" : "+v"(ln));
@@ -156,7 +160,7 @@ __device__ __forceinline__ void f8_issue(const F8Args& g, uint32_t st, int tm, i
     const int lim = g.M - 1 - m0;
     const uint8_t* base = g.a8 + (size_t)m0 * g.K + k0;
 #pragma unroll
-    for (int p = 0; p < 8; p++)
+    for (int p = A0; p < A1; p++)
       dma16s(base, (uint32_t)(min(32 * p + ta, lim) * g.K + 16 * ca), st + (p * 256 + w * 64) * 16);
   }
   if (B_FP4) {
@@ -165,7 +169,7 @@ __device__ __forceinline__ void f8_issue(const F8Args& g, uint32_t st, int tm, i
     const int lim = g.N - 1 - n0;
     const uint8_t* base = g.b + (size_t)n0 * (g.K >> 1) + (k0 >> 1);
 #pragma unroll
-    for (int p = 0; p < 4; p++)
+    for (int p = B0; p < B1; p++)
       dma16s(base, (uint32_t)(min(64 * p + tb, lim) * (g.K >> 1) + 16 * cb),
              st + F8Stage<B_FP4>::A_BYTES + (p * 256 + w * 64) * 16);
   } else {
@@ -174,13 +178,15 @@ __device__ __forceinline__ void f8_issue(const F8Args& g, uint32_t st, int tm, i
     const int lim = g.N - 1 - n0;
     const uint8_t* base = g.b + (size_t)n0 * g.K + k0;
 #pragma unroll
-    for (int p = 0; p < 8; p++)
+    for (int p = B0; p < B1; p++)
       dma16s(base, (uint32_t)(min(32 * p + tb, lim) * g.K + 16 * cb),
              st + F8Stage<B_FP4>::A_BYTES + (p * 256 + w * 64) * 16);
   }
   // scales: the (K step, tile) 1 KB blocks are contiguous; a wave copies 256 bytes of each
-  dma4(g.as_p + (uint32_t)((ks * tiles_m + tm) * 1024 + w * 256 + ln * 4), st + F8Stage<B_FP4>::AS_OFF + w * 256);
-  dma4(g.bs_p + (uint32_t)((ks * g.bs_tn + tn) * 1024 + w * 256 + ln * 4), st + F8Stage<B_FP4>::BS_OFF + w * 256);
+  if (PART != 2)
+    dma4(g.as_p + (uint32_t)((ks * tiles_m + tm) * 1024 + w * 256 + ln * 4), st + F8Stage<B_FP4>::AS_OFF + w * 256);
+  if (PART != 1)
+    dma4(g.bs_p + (uint32_t)((ks * g.bs_tn + tn) * 1024 + w * 256 + ln * 4), st + F8Stage<B_FP4>::BS_OFF + w * 256);
 }
 
 // Workgroup barrier that the compiler neither moves memory accesses across (the empty asm with a
@@ -221,19 +227,26 @@ __device__ __forceinline__ void f8_tile(int t, int tiles_m, int tiles_n, int& tm
 // phase ends with a workgroup barrier; in a phase one group reads the operands of a K step from
 // LDS into registers while the other runs the 16 MFMAs of its previous step from registers, so
 // each SIMD's matrix pipe is fed by one wave while the other waits on LDS. Group 0 reads step j in
-// phase 2j and multiplies in 2j + 1; group 1 runs one phase later. Group 0 also issues the
-// global->LDS copies: step j + NS - 1 in phase 2j, into the ring slot that step j - 1 left (both
-// groups read it by phase 2j - 1), and it waits for step j + 1 at the end of phase 2j + 1, so a
-// copy has 2 (NS - 1) phases to land. Steps 0 .. NS - 2 of the next tile are issued before the
-// epilogue, which stages C through the last ring slot, so their latency hides behind it.
+// phase 2j and multiplies in 2j + 1; group 1 runs one phase later. The global->LDS copies of step
+// j + NS - 1 go into the ring slot that step j - 1 left (both groups read it by phase 2j - 1): with
+// three slots group 0 issues half of them in phase 2j and group 1 the other half in phase 2j + 1
+// (a CU's texture path moves about 64 bytes a cycle, so one group issuing all 50 KB of a step
+// would outlast the other group's MFMA phase); each group waits for its own copies of step j + 1
+// before the barrier that ends phase 2j + 1. With two slots (E4M3 weights) group 0 issues them
+// all. Steps 0 .. NS - 2 of the next tile are issued before the epilogue, which stages C through
+// the last ring slot, so their latency hides behind it.
 template <int B_FP4, int C_BF16, int OQ = 0>
 __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int SB = F8Stage<B_FP4>::BYTES;
   constexpr int NS = F8Stage<B_FP4>::NS;
-  constexpr int PER = F8Stage<B_FP4>::PER;
+  // with three ring slots both groups issue half of each step's copies (group 1 in its read phase);
+  // with two, group 0 issues them all (a copy issued in group 1's read phase would have one phase)
+  constexpr bool SPLIT = NS == 3;
+  constexpr int PH = SPLIT ? F8Stage<B_FP4>::PER / 2 : F8Stage<B_FP4>::PER;   // copies per wave and step
   const int tiles_m = (g.M + FT - 1) / FT, tiles_n = (g.N + FT - 1) / FT;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w4 = wave & 3;
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, gq = lane >> 5;
   const int nk = g.K / FK;
@@ -252,11 +265,19 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   if (ti >= csz) return;
   int tm, tn;
   f8_tile(c0 + ti, tiles_m, tiles_n, tm, tn);
-  if (wave < 4) {
+  // steps 0 .. NS - 2 of a tile
+  auto issue_first = [&]() {
+    if (wave < 4) {
 #pragma unroll
-    for (int s = 0; s < NS - 1; s++)
-      if (s < nk) f8_issue<B_FP4>(g, lds0 + s * SB, tm, tn, tiles_m, s, wave, lane);
-  }
+      for (int s = 0; s < NS - 1; s++)
+        if (s < nk) f8_issue<B_FP4, SPLIT ? 1 : 0>(g, lds0 + s * SB, tm, tn, tiles_m, s, w4, lane);
+    } else if (SPLIT) {
+#pragma unroll
+      for (int s = 0; s < NS - 1; s++)
+        if (s < nk) f8_issue<B_FP4, 2>(g, lds0 + s * SB, tm, tn, tiles_m, s, w4, lane);
+    }
+  };
+  issue_first();
 
   v16f acc[2][4];
   // operands of one K step, held in registers between a wave's read phase and its MFMA phase
@@ -310,6 +331,9 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
       F8_MFMA(0, 2); F8_MFMA(1, 2); F8_MFMA(0, 3); F8_MFMA(1, 3);
 #undef F8_MFMA
     }
+    // all 16 are issued before anything that follows (a copy wait placed between them would hold
+    // the rest of the phase's MFMAs back)
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // epilogue geometry: a pass stages a wave's 32 x CW outputs (128 bytes of each row) in its own
@@ -330,29 +354,60 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
 
     if (wave < 4) {
       // group 0: reads step j in phase 2j, multiplies in phase 2j + 1
-      if (NS == 3 && nk > 1) wait_vmcnt<PER>(); else wait_vmcnt<0>();   // step 0 has landed
+      if (NS == 3 && nk > 1) wait_vmcnt<PH>(); else wait_vmcnt<0>();   // its copies of step 0 have landed
       f8_sync();
       int rs = 0;                 // ring slot of step j
       int is = NS - 1;            // ring slot of step j + NS - 1
-      for (int j = 0; j < nk; j++) {
-        if (j + NS - 1 < nk) f8_issue<B_FP4>(g, lds0 + is * SB, tm, tn, tiles_m, j + NS - 1, wave, lane);
+      int j = 0;
+      // Steps that still issue a copy, then the last NS - 1 steps: each loop body is straight-line
+      // code, so the compiler cannot sink the MFMAs below the copy wait and the barrier that end
+      // the MFMA phase (they would then wait for the next step's copies).
+      for (; j + NS - 1 < nk; j++) {
+        f8_issue<B_FP4, SPLIT ? 1 : 0>(g, lds0 + is * SB, tm, tn, tiles_m, j + NS - 1, w4, lane);
         read_step(rs);
         wait_lgkm0();
         f8_sync();
         mfma_step();
-        if (NS == 3 && j + 2 < nk) wait_vmcnt<PER>(); else wait_vmcnt<0>();   // step j + 1 has landed
+        wait_vmcnt<(NS - 2) * PH>();   // its copies of step j + 1 have landed (step j + NS - 1's may not)
         f8_sync();
         rs = rs + 1 == NS ? 0 : rs + 1;
         is = is + 1 == NS ? 0 : is + 1;
       }
+      for (; j < nk; j++) {
+        read_step(rs);
+        wait_lgkm0();
+        f8_sync();
+        mfma_step();
+        wait_vmcnt<0>();
+        f8_sync();
+        rs = rs + 1 == NS ? 0 : rs + 1;
+      }
       f8_sync();   // group 1's last MFMA phase
     } else {
-      // group 1: one phase behind
+      // group 1: one phase behind; with SPLIT it issues the other half of step j + 2's copies in
+      // its read phase of step j and waits for its half of step j + 1 before that phase ends
+      if (SPLIT) {
+        if (nk > 1) wait_vmcnt<PH>(); else wait_vmcnt<0>();
+      }
       f8_sync();
       f8_sync();
-      int rs = 0;
-      for (int j = 0; j < nk; j++) {
+      int rs = 0, is = NS - 1, j = 0;
+      if (SPLIT) {
+        for (; j + NS - 1 < nk; j++) {
+          f8_issue<B_FP4, 2>(g, lds0 + is * SB, tm, tn, tiles_m, j + NS - 1, w4, lane);
+          read_step(rs);
+          wait_vmcnt<PH>();
+          wait_lgkm0();
+          f8_sync();
+          mfma_step();
+          f8_sync();
+          rs = rs + 1 == NS ? 0 : rs + 1;
+          is = is + 1 == NS ? 0 : is + 1;
+        }
+      }
+      for (; j < nk; j++) {
         read_step(rs);
+        if (SPLIT) wait_vmcnt<0>();
         wait_lgkm0();
         f8_sync();
         mfma_step();
@@ -367,11 +422,7 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
     const bool more = ti < csz;
     if (more) {
       f8_tile(c0 + ti, tiles_m, tiles_n, tm, tn);
-      if (wave < 4) {
-#pragma unroll
-        for (int s = 0; s < NS - 1; s++)
-          if (s < nk) f8_issue<B_FP4>(g, lds0 + s * SB, tm, tn, tiles_m, s, wave, lane);
-      }
+      issue_first();
     }
 
     // Epilogue, staged through LDS so that global stores write whole 128-byte row segments.
