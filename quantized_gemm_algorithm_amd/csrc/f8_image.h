@@ -3,7 +3,8 @@
 //
 // A image of an [M, K] MiX operand:
 //   a8    [M, K]                      E4M3 bytes: element (1.m)_2 2^(Emax-dE) as (1.m)_2 2^(1-dE)
-//   as_p  [K/128][tiles_m][1024]      E8M0 block scales 2^(Emax-1), permuted (f8_scale_pos)
+//   as_p  [K/128][tiles_m][256][4]    E8M0 block scales 2^(Emax-1): per (K step, tile), a row's
+//                                     four block scales in one dword (f8_a_scale_pos)
 // B image of an [N, K] MX operand:
 //   bs_p  [K/128][tiles_n][1024]      E8M0 block scales, permuted
 //   b8    [N, K] (MXINT4 only)        E4M3 bytes of q/4 (MXFP4 codes are used as stored)
@@ -17,9 +18,13 @@ namespace mix {
 constexpr int FT = 256;   // GEMM tile rows (M) and columns (N)
 constexpr int FK = 128;   // K per pipeline step
 
-// Byte position of the scale of (tile row rin, 32-wide block b4 of the K step) inside the 1 KB
-// a (K step, tile) pair owns: [half-tile w][lane group gq][r][K half h][sub-tile i], so that the
-// 8 bytes a GEMM lane needs for one K step are contiguous.
+// Byte position of the A scale of (tile row rin, 32-wide block b4 of the K step) inside the 1 KB
+// a (K step, tile) pair owns: row-major, so a row-wise producer writes one dword per K step.
+__host__ __device__ inline int f8_a_scale_pos(int rin, int b4) { return rin * 4 + b4; }
+
+// Byte position of the B scale of (tile row rin, block b4) inside its 1 KB: [half-tile w][lane
+// group gq][r][K half h][sub-tile i], so that the 8 bytes a GEMM lane needs for one K step (four
+// 32-row sub-tiles, two K halves) are contiguous.
 __host__ __device__ inline int f8_scale_pos(int rin, int b4) {
   const int w = rin >> 7, i = (rin >> 5) & 3, r = rin & 31;
   const int h = b4 >> 1, gq = b4 & 1;

@@ -47,7 +47,7 @@ namespace mix {
 // ------------------------------------------------------------------ decode passes
 
 // One lane per 8-element sub-block: 4 code bytes -> 8 E4M3 bytes. Quad lane 0 writes the block's
-// E8M0 scale 2^(Emax-1) into the permuted scale layout [K/128][tiles_m][1024].
+// E8M0 scale 2^(Emax-1) into the scale layout [K/128][tiles_m][256][4].
 template <int A_FMT>
 __global__ void __launch_bounds__(256) k_expand_a(const uint8_t* __restrict__ codes, const void* __restrict__ shared,
                                                    int64_t M, int64_t K, int tiles_m, uint8_t* __restrict__ a8,
@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(256) k_expand_a(const uint8_t* __restrict__ co
     *(uint2*)(a8 + row * K + sb * 8) = make_uint2(e0, e1);
     if ((sb & 3) == 0) {
       const int64_t st = blk >> 2, tile = row / FT;
-      as_p[(st * tiles_m + tile) * 1024 + f8_scale_pos((int)(row % FT), (int)(blk & 3))] = (uint8_t)((sh & 15u) + 119u);
+      as_p[(st * tiles_m + tile) * 1024 + f8_a_scale_pos((int)(row % FT), (int)(blk & 3))] = (uint8_t)((sh & 15u) + 119u);
     }
   }
 }
@@ -113,7 +113,7 @@ struct F8Stage {
 
 struct F8Args {
   const uint8_t* a8;      // [M, K] E4M3
-  const uint8_t* as_p;    // [K/128][tiles_m][1024] E8M0, permuted
+  const uint8_t* as_p;    // [K/128][tiles_m][256][4] E8M0 (f8_a_scale_pos)
   const uint8_t* b;       // [N, K/2] FP4 codes or [N, K] E4M3
   const uint8_t* bs_p;    // [K/128][bs_tn][1024] E8M0, permuted
   void* c;                // C [M, ldc] (may be NULL when the output is quantized)
@@ -124,7 +124,7 @@ struct F8Args {
   uint8_t* qc;            // codes [M, N/2]
   uint16_t* qsh;          // shared fields [M, N/32]
   uint8_t* qa8;           // the A image of C for a next product (K = N): E4M3 [M, N], or NULL
-  uint8_t* qas_p;         //   and its permuted scales [N/128][ceil(M/256)][1024]
+  uint8_t* qas_p;         //   and its scales [N/128][ceil(M/256)][256][4]
 };
 
 constexpr int F8_THREADS = 512;   // 8 waves: 4 along M x 2 along N, 64 x 128 outputs each
@@ -251,10 +251,11 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   const int r = lane & 31, gq = lane >> 5;
   const int nk = g.K / FK;
   const uint32_t lds0 = lds_addr(smem);
-  // this lane's 8 scale bytes [h][sub-tile] in the permuted 1 KB block (see f8_scale_pos)
-  const int sc_a = (((wm >> 1) * 2 + gq) * 32 + r) * 8;
+  // A scales: the dwords of this lane's two rows 64 wm + 32 i + r (byte b = block b of the K step;
+  // shifted right by 8 gq, byte 2h is the lane's block 2h + gq); B: this lane's 8 bytes [h][sub-tile]
+  // in the permuted 1 KB block (see f8_scale_pos)
+  const int sc_a = (64 * wm + r) * 4;
   const int sc_b = ((wn * 2 + gq) * 32 + r) * 8;
-  const int sub_a = 16 * (wm & 1);   // bit offset of this wave's two A sub-tiles in a 4-byte word
 
   // this workgroup's tiles: c0 + ix, c0 + ix + gx, ... below c0 + csz
   const int nt = tiles_m * tiles_n;
@@ -283,17 +284,19 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   // operands of one K step, held in registers between a wave's read phase and its MFMA phase
   v8i xf[2][2];
   v8i wf[2][4];
-  int xsw[2], wsw[2];
+  int xsw[2], wsw[2];   // A scale word per sub-tile i, B scale word per K half h
 
   auto read_step = [&](int slot) {
     const uint8_t* st = smem + slot * SB;
     const uint8_t* sa = st;
     const uint8_t* sbm = st + F8Stage<B_FP4>::A_BYTES;
-    const uint2 xs8 = *(const uint2*)(st + F8Stage<B_FP4>::AS_OFF + sc_a);
+    const uint32_t xs0 = *(const uint32_t*)(st + F8Stage<B_FP4>::AS_OFF + sc_a);
+    const uint32_t xs1 = *(const uint32_t*)(st + F8Stage<B_FP4>::AS_OFF + sc_a + 32 * 4);
     const uint2 ws8 = *(const uint2*)(st + F8Stage<B_FP4>::BS_OFF + sc_b);
+    xsw[0] = (int)(xs0 >> (8 * gq));
+    xsw[1] = (int)(xs1 >> (8 * gq));
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-      xsw[h] = (int)((h ? xs8.y : xs8.x) >> sub_a);
       wsw[h] = (int)(h ? ws8.y : ws8.x);
 #pragma unroll
       for (int i = 0; i < 2; i++) {
@@ -320,17 +323,16 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
       }
     }
   };
-  // the scale operands' op_sel picks byte J of the weight word and byte I of the activation word
+  // the scale operands' op_sel picks byte J of the weight word and byte 2H of the activation word
   auto mfma_step = [&]() {
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-#define F8_MFMA(I, J)                                                                                      \
-  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[h][J], xf[h][I], acc[I][J], B_FP4 ? 4 : 0, 0, J, \
-                                                              wsw[h], I, xsw[h])
-      F8_MFMA(0, 0); F8_MFMA(1, 0); F8_MFMA(0, 1); F8_MFMA(1, 1);
-      F8_MFMA(0, 2); F8_MFMA(1, 2); F8_MFMA(0, 3); F8_MFMA(1, 3);
+#define F8_MFMA(H, I, J)                                                                                   \
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[H][J], xf[H][I], acc[I][J], B_FP4 ? 4 : 0, 0, J, \
+                                                              wsw[H], 2 * H, xsw[I])
+    F8_MFMA(0, 0, 0); F8_MFMA(0, 1, 0); F8_MFMA(0, 0, 1); F8_MFMA(0, 1, 1);
+    F8_MFMA(0, 0, 2); F8_MFMA(0, 1, 2); F8_MFMA(0, 0, 3); F8_MFMA(0, 1, 3);
+    F8_MFMA(1, 0, 0); F8_MFMA(1, 1, 0); F8_MFMA(1, 0, 1); F8_MFMA(1, 1, 1);
+    F8_MFMA(1, 0, 2); F8_MFMA(1, 1, 2); F8_MFMA(1, 0, 3); F8_MFMA(1, 1, 3);
 #undef F8_MFMA
-    }
     // all 16 are issued before anything that follows (a copy wait placed between them would hold
     // the rest of the phase's MFMAs back)
     __builtin_amdgcn_sched_barrier(0);
@@ -466,7 +468,7 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
                 *(uint2*)(g.qa8 + (int64_t)gm * g.N + gn) = make_uint2(e0, e1);
                 if (qd == 0)
                   g.qas_p[((int64_t)(gn >> 7) * tiles_m + (gm >> 8)) * 1024 +
-                          f8_scale_pos(gm & (FT - 1), (gn >> 5) & 3)] = (uint8_t)(emax + 126);
+                          f8_a_scale_pos(gm & (FT - 1), (gn >> 5) & 3)] = (uint8_t)(emax + 126);
               }
             }
             if (!g.c) continue;
@@ -551,7 +553,7 @@ __global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
       const uint4 lo = *(const uint4*)ap;
       const uint4 hi = *(const uint4*)(ap + 64);
       af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      asc[i] = g.as_p[(int64_t)ks * 1024 + f8_scale_pos(rowA, gq)];
+      asc[i] = g.as_p[(int64_t)ks * 1024 + f8_a_scale_pos(rowA, gq)];
       uint32_t b[G];
 #pragma unroll
       for (int j = 0; j < G; j++) {

@@ -70,9 +70,13 @@ __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ 
   const int scc = col_ok ? sc : (sc & 3);
   const int q = scc & 3;
   const int blk = scc >> 2;
-  // the lane's part of the permuted scale position: [K step][tile][half][gq][r][h][i]
-  const int h = (blk & 3) >> 1, gq = blk & 1;
-  for (int64_t r0 = (int64_t)blockIdx.y * MQ_R; r0 < rows; r0 += (int64_t)gridDim.y * MQ_R) {
+  // Row pairs in XCD-contiguous bands (workgroup y runs on XCD y % 8 when the row fits one chunk):
+  // the small per-row outputs (a row's shared fields and its scale dwords share cache lines with
+  // the neighbouring rows) are then written whole by one XCD's L2 instead of in pieces by all eight.
+  const int gy = gridDim.y, xb = blockIdx.y & 7;
+  const int pr = xb * (gy >> 3) + min(xb, gy & 7) + (int)(blockIdx.y >> 3);
+  for (int64_t r0 = (int64_t)pr * MQ_R; r0 < rows; r0 += (int64_t)gy * MQ_R) {
+    uint32_t sdw[MQ_R];   // IMG: the four E8M0 scales of this lane's K step (valid on lane 16k)
     uint32_t xb[MQ_R][8];  // bf16: the 16 raw bytes in xb[u][0..3]; fp32: the 8 bit patterns
 #pragma unroll
     for (int u = 0; u < MQ_R; u++) {
@@ -98,6 +102,14 @@ __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ 
       }
       uint32_t f = 0;
       if (FMT == 1) f = quad_or_dpp((q == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * q)));
+      if (IMG) {
+        // a 16-lane DPP row is one K step (four blocks, Emax uniform over each quad): lane 16k gathers
+        // the blocks' scales from lanes 16k + 4, + 8, + 12 (rotations right by 12, 8, 4)
+        const int v = emax + 126;
+        sdw[u] = (uint32_t)v | ((uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x12C, 0xF, 0xF, true) << 8) |
+                 ((uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, true) << 16) |
+                 ((uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, true) << 24);
+      }
       if (!col_ok || row >= rows) continue;
       if (!IMG || codes) {
         *(uint32_t*)(codes + row * (cols >> 1) + scc * 4) = word;
@@ -107,15 +119,14 @@ __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ 
           if (q == 0) ((uint8_t*)shared)[row * (cols >> 5) + blk] = (uint8_t)((uint32_t)(emax + 7) | (m << 4));
         }
       }
-      if (IMG) {
-        *(uint2*)(a8 + row * cols + scc * 8) = make_uint2(e0, e1);
-        if (q == 0) {
-          const int rin = (int)(row & (FT - 1));
-          const int64_t tile_base = ((int64_t)(blk >> 2) * tiles_m + (row >> 8)) * 1024;   // FT = 256
-          as_p[tile_base + (((rin >> 7) * 2 + gq) * 32 + (rin & 31)) * 8 + h * 4 + ((rin >> 5) & 3)] =
-              (uint8_t)(emax + 126);
-        }
-      }
+      if (IMG) *(uint2*)(a8 + row * cols + scc * 8) = make_uint2(e0, e1);
+    }
+    if (IMG && col_ok && (scc & 15) == 0) {
+      // the rows' scale dwords of this K step (f8_a_scale_pos: row-major, so the MQ_R = 2 rows of a
+      // workgroup, even-aligned and in one 256-row tile, are adjacent)
+      uint8_t* sp = as_p + ((int64_t)(scc >> 4) * tiles_m + (r0 >> 8)) * 1024 + (r0 & (FT - 1)) * 4;
+      if (r0 + 1 < rows) *(uint2*)sp = make_uint2(sdw[0], sdw[1]);
+      else *(uint32_t*)sp = sdw[0];
     }
   }
 }
