@@ -788,7 +788,8 @@ __device__ __forceinline__ int vswz(int ch) { return (ch ^ (ch >> 3)) & 7; }
 inline size_t decode_pv_lds_bytes(int G) { return 128 * 128 + (size_t)G * DCH + (size_t)G * (DCH / 32) + 16 * 4; }
 
 // grid 8 nchunk ceil(B Hkv / 8) (dec_wg), block 256, LDS decode_pv_lds_bytes(G). P^ codes
-// [B, Hq, Lp/2], shared [B, Hq, Lp/32]; chunk partials lpart [B, Hq, nchunk], opart [B, Hq, nchunk, 128].
+// [B, Hq, Lp/2] and shared [B, Hq, Lp/32] are written only when pc / ps are given (debug dumps);
+// chunk partials lpart [B, Hq, nchunk], opart [B, Hq, nchunk, 128].
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) k_decode_pv(const float* __restrict__ S, const float* __restrict__ pmax,
                                                     const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
                                                     const int32_t* __restrict__ pos, int64_t max_pos, int Hq, int Hkv,
@@ -873,9 +874,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) k
       uint32_t shf;
       const uint32_t word = p_code8(make_float4(pv[0], pv[1], pv[2], pv[3]), make_float4(pv[4], pv[5], pv[6], pv[7]),
                                     sbk & 3, shf);
-      *(uint32_t*)(pc + qrow * (Lp >> 1) + (jb >> 1)) = word;
+      if (pc) *(uint32_t*)(pc + qrow * (Lp >> 1) + (jb >> 1)) = word;
       if ((sbk & 3) == 0) {
-        ps[qrow * (Lp >> 5) + (jb >> 5)] = (uint16_t)shf;
+        if (ps) ps[qrow * (Lp >> 5) + (jb >> 5)] = (uint16_t)shf;
         sPs[row * (DCH / 32) + (sbk >> 2)] = (uint8_t)((shf & 15u) + 119u);
       }
       uint32_t e0, e1;
@@ -1155,7 +1156,8 @@ hipError_t attn_decode_run(const void* q, const void* k_new, const void* v_new, 
   hipLaunchKernelGGL(k_decode_pv, grid, dim3(256), decode_pv_lds_bytes((int)(Hq / Hkv)), s, (const float*)S,
                      (const float*)pmax,
                      (const uint8_t*)c->v_codes, (const uint8_t*)c->v_scales, pos, max_pos, (int)Hq, (int)Hkv, Lmax, Lp,
-                     (int)B, nchunk, scale, pc, ps, lpart, opart, dbg ? dbg->p : nullptr);
+                     (int)B, nchunk, scale, dbg && dbg->p_codes ? pc : nullptr, dbg && dbg->p_shared ? ps : nullptr,
+                     lpart, opart, dbg ? dbg->p : nullptr);
   HIPCHK(hipGetLastError());
   hipLaunchKernelGGL(k_decode_combine, dim3((unsigned)(B * Hq)), dim3((unsigned)d), 0, s, (const float*)lpart,
                      (const float*)opart, pos, max_pos, (int)Hq, nchunk, (int)d, (uint16_t*)o, dbg ? dbg->l : nullptr);

@@ -6,8 +6,9 @@
 //   as_p  [K/128][tiles_m][256][4]    E8M0 block scales 2^(Emax-1): per (K step, tile), a row's
 //                                     four block scales in one dword (f8_a_scale_pos)
 // B image of an [N, K] MX operand:
-//   bs_p  [K/128][tiles_n][1024]      E8M0 block scales, permuted
+//   bs_p  [K/128][tiles_n][1024]      E8M0 block scales, permuted (f8_scale_pos), for the tiled product
 //   b8    [N, K] (MXINT4 only)        E4M3 bytes of q/4 (MXFP4 codes are used as stored)
+//   bs_v  [ceil(N/16)][K/128][16][4]  the same scales per 16-row group, for the small-M product
 // tiles_m = ceil(M / 256), tiles_n = ceil(N / 256); every part starts on a 256-byte boundary.
 #pragma once
 #include <cstddef>
@@ -46,14 +47,15 @@ inline F8AImage f8_a_image_layout(int64_t M, int64_t K) {
 }
 
 struct F8BImage {
-  size_t bs_p, b8, total;
+  size_t bs_p, b8, bs_v, total;
 };
 inline F8BImage f8_b_image_layout(int b_fp4, int64_t N, int64_t K) {
   const int64_t tn = (N + FT - 1) / FT;
   F8BImage L{};
   L.bs_p = 0;
   L.b8 = f8_al256((size_t)(K / FK) * tn * 1024);
-  L.total = L.b8 + (b_fp4 ? 0 : f8_al256((size_t)N * K));
+  L.bs_v = L.b8 + (b_fp4 ? 0 : f8_al256((size_t)N * K));
+  L.total = L.bs_v + f8_al256((size_t)((N + 15) / 16) * (K / FK) * 64);
   return L;
 }
 

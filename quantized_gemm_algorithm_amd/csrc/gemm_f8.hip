@@ -74,13 +74,15 @@ __global__ void __launch_bounds__(256) k_expand_a(const uint8_t* __restrict__ co
 
 // MX scales [N, K/32] -> the permuted layout [K/128][tiles_n][1024].
 __global__ void __launch_bounds__(256) k_permute_b_scales(const uint8_t* __restrict__ bs, int64_t N, int64_t K,
-                                                           int tiles_n, uint8_t* __restrict__ bs_p) {
+                                                           int tiles_n, uint8_t* __restrict__ bs_p,
+                                                           uint8_t* __restrict__ bs_v) {
   const int64_t nb = K >> 5;
   const int64_t total = N * nb;
   for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total; g += (int64_t)gridDim.x * blockDim.x) {
     const int64_t row = g / nb, blk = g - row * nb;
     const int64_t st = blk >> 2, tile = row / FT;
     bs_p[(st * tiles_n + tile) * 1024 + f8_scale_pos((int)(row % FT), (int)(blk & 3))] = bs[g];
+    bs_v[((row >> 4) * (K >> 7) + st) * 64 + (row & 15) * 4 + (blk & 3)] = bs[g];
   }
 }
 
@@ -116,6 +118,7 @@ struct F8Args {
   const uint8_t* as_p;    // [K/128][tiles_m][256][4] E8M0 (f8_a_scale_pos)
   const uint8_t* b;       // [N, K/2] FP4 codes or [N, K] E4M3
   const uint8_t* bs_p;    // [K/128][bs_tn][1024] E8M0, permuted
+  const uint8_t* bs_v;    // [ceil(N/16)][K/128][16][4] E8M0 (small-M product)
   void* c;                // C [M, ldc] (may be NULL when the output is quantized)
   int64_t ldc;
   int M, N, K;
@@ -500,16 +503,19 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // M <= 16: the product is a stream over the weights. A workgroup owns 16 G weight rows
-// (G <= 8). Its slice of B, one K chunk at a time, is copied into LDS in one burst
-// (global_load_lds, rows padded by 16 bytes so that the 16 rows an MFMA reads sit in distinct
-// banks), while each wave loads its A fragments from the image. The 4 waves split the chunk's
-// 128-wide K steps; partial sums are added through LDS at the end. MFMA:
+// (G <= 8). The 4 waves split each K chunk's 128-wide steps; a wave copies its own steps of the
+// slice into its own LDS region (global_load_lds, one 1 KB run per 16 rows of FP4 or 8 rows of
+// E4M3, 16-byte chunks XOR-swizzled by row as in the tiled product so that an MFMA's 16 rows sit in
+// distinct banks) and multiplies step i as soon as that step's copies have landed (vmcnt), with
+// the later steps still in flight; its A fragments come from the image. Partial sums are added
+// through LDS at the end. MFMA:
 // v_mfma_scale_f32_16x16x128_f8f6f4 with the weight rows as its A operand (lane l = r + 16 g holds
 // row r: FP4 K elements [32 g, 32 g + 32) in 16 bytes; E4M3 [16 g, 16 g + 16) and
 // [64 + 16 g, 64 + 16 g + 16)), the 16 activation rows as its B operand (E4M3, same split), and
 // the scale of lane l = the E8M0 scale of its row for K block g. Result register i of lane l is
 // C^T[4 (l >> 4) + i][l & 15]: four consecutive n for one m.
 constexpr int GV_MAXSPW = 8;   // K steps per wave per chunk (chunk <= 32 steps = 4096)
+constexpr int GV_AHEAD = 4;    // steps of copies a wave keeps in flight
 
 struct GvArgs {
   F8Args g;
@@ -517,13 +523,26 @@ struct GvArgs {
   int tiles_n;  // 256-row tiles of the B image's scale layout
 };
 
+// s_waitcnt vmcnt(n) for a small run-time n: at most n vector-memory operations still in flight
+__device__ __forceinline__ void wait_vmcnt_steps(int steps_left, int per_step) {
+  switch (min(steps_left * per_step, 63)) {
+#define GV_W(N) case N: wait_vmcnt<N>(); break;
+    GV_W(0) GV_W(1) GV_W(2) GV_W(3) GV_W(4) GV_W(5) GV_W(6) GV_W(7) GV_W(8) GV_W(9) GV_W(10) GV_W(11) GV_W(12)
+    GV_W(13) GV_W(14) GV_W(15) GV_W(16) GV_W(18) GV_W(20) GV_W(21) GV_W(24) GV_W(25) GV_W(28) GV_W(30) GV_W(32)
+    GV_W(35) GV_W(36) GV_W(40) GV_W(42) GV_W(45) GV_W(48) GV_W(49) GV_W(50) GV_W(54) GV_W(56) GV_W(60)
+#undef GV_W
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
 template <int B_FP4, int C_BF16, int G>
 __global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
   extern __shared__ __align__(16) uint8_t smem[];
   const F8Args& g = ga.g;
   constexpr int R = 16 * G;
   constexpr int CPS = B_FP4 ? 4 : 8;                // 16-byte chunks of a B row per 128-wide K step
-  constexpr int GW = (G + 3) / 4;                   // scale words per step (4 row groups each)
+  constexpr int SBY = CPS * 16;                     // bytes of a B row per step
+  constexpr int NP = R * SBY / 1024;                // 1 KB copy runs per step (G or 2 G)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, gq = lane >> 4;
   const int n0 = blockIdx.x * R;
@@ -534,18 +553,65 @@ __global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
 #pragma unroll
   for (int j = 0; j < G; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  const int spw_max = (ga.kc / FK + 3) >> 2;
+  // this wave's LDS: its weight steps, then its B scales [G][spw][64] and A scales [spw][64],
+  // each rounded up to whole 1 KB copy runs
+  const int scb_runs = (G * spw_max * 64 + 1023) >> 10, sca_runs = (spw_max * 64 + 1023) >> 10;
+  uint8_t* wbase = smem + (size_t)wave * ((size_t)spw_max * R * SBY + (size_t)(scb_runs + sca_runs) * 1024);
   for (int kc0 = 0; kc0 < g.K; kc0 += ga.kc) {
     const int nks = min(ga.kc, g.K - kc0) / FK;      // K steps in this chunk
-    const int c16 = nks * CPS;                       // chunks per row in LDS (+1 pad)
     const int spw = (nks + 3) >> 2;
     const int s0 = wave * spw;
-    // Operand loads that do not wait on the copies: A fragments and scales (A image: E4M3
-    // [M, K], scales [K/128][1][1024]) and the weight rows' scale bytes, four row groups per
-    // register (the MFMA's scale op_sel picks the byte). Indices are clamped so every load is
-    // issued unconditionally; steps past this wave's share are loaded but not used.
+    const int myn = max(0, min(spw, nks - s0));      // this wave's steps
+    const int ks0 = min(kc0 / FK + s0, nkt - 1);      // its first step (clamped when it has none)
+    uint8_t* wreg = wbase;
+    uint8_t* scb = wbase + (size_t)spw_max * R * SBY;
+    uint8_t* sca = scb + (size_t)scb_runs * 1024;
+    // 1. its scales, copied into its own region (no other wave reads them): B scale chunk t (16
+    //    bytes) = row group t / (4 spw), step (t % (4 spw)) / 4, quarter t % 4 (bs_v holds a row
+    //    group's steps contiguously); A scale chunk t = step t / 4, quarter t % 4 of rows 0..15
+    //    (the A image's scale block of a step starts with them). Chunks past this wave's steps
+    //    repeat a valid one.
+    {
+      const int ngrp = (g.N + 15) >> 4;
+      for (int run = 0; run < (G * spw * 4 + 63) / 64; run++) {
+        const int t = run * 64 + lane;
+        const int j = min(t / (4 * spw), G - 1);
+        const int st = min((t % (4 * spw)) >> 2, max(myn - 1, 0));
+        const int grp = min(blockIdx.x * G + j, ngrp - 1);
+        dma16(g.bs_v + ((int64_t)grp * nkt + ks0 + st) * 64 + (t & 3) * 16,
+              __builtin_amdgcn_readfirstlane(lds_addr(scb + run * 1024)));
+      }
+      for (int run = 0; run < (spw * 4 + 63) / 64; run++) {
+        const int t = run * 64 + lane;
+        const int st = min(t >> 2, max(myn - 1, 0));
+        dma16(g.as_p + (int64_t)(ks0 + st) * 1024 + (t & 3) * 16,
+              __builtin_amdgcn_readfirstlane(lds_addr(sca + run * 1024)));
+      }
+    }
+    // 2. B: this wave's steps, step i at wreg + i R SBY; copy run q of a step holds rows
+    // [16 q, +16) (FP4, lane -> row q16 + lane / 4, slot lane % 4) or [8 q, +8) (E4M3, row
+    // q8 + lane / 8, slot lane % 8); slot s of a row holds its logical chunk s ^ swz(row).
+    // The copies are issued GV_AHEAD steps ahead of the MFMAs: issuing them all up front would
+    // stall the wave on memory back-pressure before its first MFMA.
+    auto issue_step = [&](int i) {
+      const int ks = kc0 / FK + s0 + i;
+#pragma unroll
+      for (int qr = 0; qr < NP; qr++) {
+        const int row = B_FP4 ? 16 * qr + (lane >> 2) : 8 * qr + (lane >> 3);
+        const int slot = lane & (CPS - 1);
+        const int c = slot ^ (B_FP4 ? bswz(row) : aswz(row));
+        const int grow = min(n0 + row, g.N - 1);
+        dma16(g.b + (int64_t)grow * browg + (int64_t)ks * SBY + 16 * c,
+              __builtin_amdgcn_readfirstlane(lds_addr(wreg + (size_t)i * R * SBY + qr * 1024)));
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < GV_AHEAD; i++)
+      if (i < myn) issue_step(i);
+    // 3. A fragments (A image: E4M3 [M, K]), loaded from memory; indices are clamped so every load
+    //    is issued unconditionally (steps past this wave's share are loaded but not used)
     v8i af[GV_MAXSPW];
-    int asc[GV_MAXSPW];
-    uint32_t wsc[GV_MAXSPW][GW];
 #pragma unroll
     for (int i = 0; i < GV_MAXSPW; i++) {
       const int ks = min(kc0 / FK + s0 + i, nkt - 1);
@@ -553,63 +619,37 @@ __global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
       const uint4 lo = *(const uint4*)ap;
       const uint4 hi = *(const uint4*)(ap + 64);
       af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      asc[i] = g.as_p[(int64_t)ks * 1024 + f8_a_scale_pos(rowA, gq)];
-      uint32_t b[G];
-#pragma unroll
-      for (int j = 0; j < G; j++) {
-        const int n = min(n0 + 16 * j + r, g.N - 1);
-        b[j] = g.bs_p[((int64_t)ks * ga.tiles_n + n / FT) * 1024 + f8_scale_pos(n % FT, gq)];
-      }
-#pragma unroll
-      for (int w = 0; w < GW; w++) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int j = 4 * w; j < G && j < 4 * w + 4; j++) v |= b[j] << (8 * (j & 3));
-        wsc[i][w] = v;
-      }
     }
-    // B slice: R rows x c16 chunks -> LDS rows of c16 + 1 chunks; each copy instruction fills
-    // 64 consecutive LDS chunks; a pad chunk gets a copy of its row's last chunk (never read)
-    const int total = R * (c16 + 1);
-    for (int base = wave * 64; base < total; base += 256) {
-      const int idx = min(base + lane, total - 1);
-      const int row = idx / (c16 + 1);
-      const int slot = min(idx - row * (c16 + 1), c16 - 1);
-      const int grow = min(n0 + row, g.N - 1);
-      dma16(g.b + (int64_t)grow * browg + (int64_t)kc0 * (B_FP4 ? 1 : 2) / 2 + 16 * slot,
-            __builtin_amdgcn_readfirstlane(lds_addr(smem + base * 16)));
-    }
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int i = 0; i < GV_MAXSPW; i++) {
-      if (i < spw && s0 + i < nks) {
-        const int s = s0 + i;
+      if (i < myn) {
+        // steps i .. min(myn, i + GV_AHEAD) - 1 are in flight, in order: wait for step i (the
+        // scale copies are older still; the A loads issued after the first steps are waited for
+        // too, as the MFMAs need them)
+        wait_vmcnt_steps(min(myn, i + GV_AHEAD) - i - 1, NP);
+        const uint8_t* sp = wreg + (size_t)i * R * SBY;
         v8i wf[G];
+        int wsb[G];
 #pragma unroll
         for (int j = 0; j < G; j++) {
-          const uint8_t* wp = smem + ((16 * j + r) * (c16 + 1) + s * CPS) * 16;
+          const int row = 16 * j + r;
+          const uint8_t* wp = sp + row * SBY;
           if (B_FP4) {
-            const v4i w = *(const v4i*)(wp + 16 * gq);
+            const v4i w = *(const v4i*)(wp + 16 * (gq ^ bswz(row)));
             wf[j] = __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
           } else {
-            const v4i lo = *(const v4i*)(wp + 16 * gq);
-            const v4i hi = *(const v4i*)(wp + 64 + 16 * gq);
+            const v4i lo = *(const v4i*)(wp + 16 * (gq ^ aswz(row)));
+            const v4i hi = *(const v4i*)(wp + 16 * ((4 + gq) ^ aswz(row)));
             wf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           }
+          wsb[j] = scb[(j * spw + i) * 64 + r * 4 + gq];
         }
+        const int asc = sca[i * 64 + rowA * 4 + gq];
 #pragma unroll
-        for (int j = 0; j < G; j++) {
-          const int ws = (int)wsc[i][j >> 2];
-#define GV_MFMA(SEL)                                                                                          \
-  acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], af[i], acc[j], B_FP4 ? 4 : 0, 0, SEL, ws, 0, \
-                                                            asc[i])
-          if ((j & 3) == 0) GV_MFMA(0);
-          if ((j & 3) == 1) GV_MFMA(1);
-          if ((j & 3) == 2) GV_MFMA(2);
-          if ((j & 3) == 3) GV_MFMA(3);
-#undef GV_MFMA
-        }
+        for (int j = 0; j < G; j++)
+          acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], af[i], acc[j], B_FP4 ? 4 : 0, 0, 0, wsb[j],
+                                                                    0, asc);
+        if (i + GV_AHEAD < myn) issue_step(i + GV_AHEAD);
       }
     }
     __builtin_amdgcn_s_barrier();   // the slice is consumed before the next chunk overwrites it
@@ -733,18 +773,19 @@ hipError_t launch_gemm_b_image(int b_fp4, const uint8_t* b_codes, const uint8_t*
   uint8_t* base = (uint8_t*)img;
   const int tiles_n = (int)((N + FT - 1) / FT);
   hipLaunchKernelGGL(k_permute_b_scales, dim3(grid1d(N * (K >> 5))), dim3(256), 0, s, b_scales, N, K, tiles_n,
-                     base + L.bs_p);
+                     base + L.bs_p, base + L.bs_v);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || b_fp4) return e;
   hipLaunchKernelGGL(k_expand_b_int4, dim3(grid1d(N * (K >> 3))), dim3(256), 0, s, b_codes, N, K, base + L.b8);
   return hipGetLastError();
 }
 
-// LDS bytes of k_gemv_f8 for G row groups and a K chunk kc: the padded slice, rounded up to whole
-// 1 KB copy runs, and at least the 4 x G KB of partial sums.
+// LDS bytes of k_gemv_f8 for G row groups and a K chunk kc: the four waves' regions (ceil(steps / 4)
+// weight steps and their scales each), and at least the 4 x G KB of partial sums.
 static size_t gv_lds_bytes(int b_fp4, int G, int kc) {
-  const size_t chunks = (size_t)16 * G * ((size_t)(kc / FK) * (b_fp4 ? 4 : 8) + 1);
-  const size_t slice = (chunks + 63) / 64 * 64 * 16;
+  const size_t spw = (size_t)(kc / FK + 3) / 4;   // steps per wave
+  const size_t scr = (G * spw * 64 + 1023) / 1024 + (spw * 64 + 1023) / 1024;   // scale runs per wave
+  const size_t slice = 4 * (spw * 16 * G * (b_fp4 ? 64 : 128) + scr * 1024);
   const size_t red = (size_t)4 * G * 1024;
   return slice > red ? slice : red;
 }
@@ -793,6 +834,7 @@ hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const vo
   a.as_p = (const uint8_t*)a_img + LA.as_p;
   a.b = b_fp4 ? b_codes : (const uint8_t*)b_img + LB.b8;
   a.bs_p = (const uint8_t*)b_img + LB.bs_p;
+  a.bs_v = (const uint8_t*)b_img + LB.bs_v;
   a.c = c; a.ldc = ldc; a.M = (int)M; a.N = (int)N; a.K = (int)K;
   a.bs_tn = (int)((N + FT - 1) / FT);
   if (M <= 16) return launch_gemv_f8(b_fp4, c_bf16, a, s);
@@ -820,6 +862,7 @@ hipError_t launch_gemm_images_q(int b_fp4, const void* a_img, const void* b_img,
   a.as_p = (const uint8_t*)a_img + LA.as_p;
   a.b = b_fp4 ? b_codes : (const uint8_t*)b_img + LB.b8;
   a.bs_p = (const uint8_t*)b_img + LB.bs_p;
+  a.bs_v = (const uint8_t*)b_img + LB.bs_v;
   a.c = c; a.ldc = ldc; a.M = (int)M; a.N = (int)N; a.K = (int)K;
   a.bs_tn = (int)((N + FT - 1) / FT);
   a.qc = q_codes;
