@@ -90,11 +90,13 @@ def test_gemm_validation(lib):
         assert fn(1, FAKE, FAKE, 1, FAKE, FAKE, 2**31, 4, 32, FAKE, 0, 4, None) == MIX_E_SHAPE
     # fast-path workspace size: zero when the shape does not take it
     # E4M3 A + per-(K step, 256-row tile) 1 KB scale blocks for A and B (+ E4M3 B for MXINT4)
-    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 4096, 18944, 3584) == 4096 * 3584 + 28 * 16 * 1024 + 28 * 74 * 1024
-    assert lib.mix_mx_gemm_workspace_bytes(1, 0, 256, 256, 128) == 256 * 128 + 1024 + 1024 + 256 * 128
+    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 4096, 18944, 3584) == (4096 * 3584 + 28 * 16 * 1024 + 28 * 74 * 1024
+                                                                       + 1184 * 28 * 64)
+    assert lib.mix_mx_gemm_workspace_bytes(1, 0, 256, 256, 128) == 256 * 128 + 1024 + 1024 + 256 * 128 + 16 * 64
     assert lib.mix_mx_gemm_workspace_bytes(1, 1, 256, 256, 96) == 0
     # M <= 16 streams the weights through the same images
-    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 16, 18944, 3584) == 16 * 3584 + 28 * 1024 + 28 * 74 * 1024
+    assert lib.mix_mx_gemm_workspace_bytes(1, 1, 16, 18944, 3584) == (16 * 3584 + 28 * 1024 + 28 * 74 * 1024
+                                                                     + 1184 * 28 * 64)
     assert lib.mix_mx_gemm_workspace_bytes(1, 1, 32, 18944, 3584) == 0
     # a misaligned workspace is rejected when the fast path is taken
     assert lib.mix_mx_gemm(1, FAKE, FAKE, 1, FAKE, FAKE, 256, 256, 128, FAKE, 0, 256, MISALIGNED, 1 << 20,
@@ -117,9 +119,10 @@ def test_image_sizes(lib):
     assert lib.mix_gemm_a_image_bytes(1, 128) == 256 + 1024
     assert lib.mix_gemm_a_image_bytes(4, 96) == 0
     assert lib.mix_gemm_a_image_bytes(0, 128) == 0
-    # B image: permuted scales (+ E4M3 bytes of q/4 for MXINT4)
-    assert lib.mx_gemm_b_image_bytes(1, 18944, 3584) == 28 * 74 * 1024
-    assert lib.mx_gemm_b_image_bytes(0, 300, 256) == 2 * 2 * 1024 + 300 * 256
+    # B image: permuted scales (+ E4M3 bytes of q/4 for MXINT4) + the scales per 16-row group
+    # [ceil(N/16)][K/128][64] for the small-M product (each part 256-byte rounded)
+    assert lib.mx_gemm_b_image_bytes(1, 18944, 3584) == 28 * 74 * 1024 + 1184 * 28 * 64
+    assert lib.mx_gemm_b_image_bytes(0, 300, 256) == 2 * 2 * 1024 + 300 * 256 + 2560
     assert lib.mx_gemm_b_image_bytes(2, 300, 256) == 0
     assert lib.mx_gemm_b_image_bytes(1, 300, 0) == 0
 
