@@ -13,27 +13,38 @@ What it follows:
 * P1, method overview, last bullet: K-smoothing subtracts the per-channel mean of
   K before coding (the optional ``mu`` operand).
 
+* P1, 主要实验设置 (experimental setup), the format bullet: the 4.5-bit tier holds
+  "g16" variants of the MX weights, one shared exponent per 16 elements (4 bits per
+  element plus 8 per 16 = 4.5 bits); MiX-INT4g16 pairs MiX-4.5b activations with
+  MXINT4g16 weights (``block=16`` here; the element rules do not change).
+
 Readings: D8 (X = ceil(log2 amax) - 2 for FP4), D9 (INT4 as OCP-style 1.2
 fixed point, symmetric clamp), D10 (RNE, saturating, FP4 keeps the sign of
-zero), D11 (zero block, exponent clamps), D15 (smoothing in fp32).
+zero), D11 (zero block, exponent clamps), D15 (smoothing in fp32); a g16 block is
+coded exactly as a 32-element block whose other 16 elements are zero.
 
 Pins (tests/test_oracle_mx.py): brute-force nearest grid value with
 ties-to-even on tiny blocks; the closed-form decode by enumeration; the ~41.5%
-floor statistic for MXFP4 and 0% under ceil; scale bytes against frexp.
+floor statistic for MXFP4 and 0% under ceil; scale bytes against frexp; g16:
+brute force on 16-element blocks, equality with the 32-element coding of each
+16-element group padded with zeros, and the 4.5-bit accounting.
 """
 import numpy as np
 
 from .numerics import as_f32, ceil_log2, floor_log2
 
 BLOCK = 32
+BLOCKS = (16, 32)
 FORMATS = ("int4", "fp4")
 E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
-def _check(fmt, x):
+def _check(fmt, x, block):
     if fmt not in FORMATS:
         raise ValueError(f"unknown MX format {fmt!r}")
-    if x.ndim != 2 or x.shape[1] % BLOCK != 0:
+    if block not in BLOCKS:
+        raise ValueError("MX blocks hold 16 or 32 elements")
+    if x.ndim != 2 or x.shape[1] % 32 != 0:
         raise ValueError("MX blocks run along the last axis, whose length must be a multiple of 32")
 
 
@@ -56,20 +67,21 @@ def _rne_grid_index(y):
     return np.where(tie & (first % 2 == 1), nxt, first)
 
 
-def mx_quantize(x, fmt, dtype="f32", mu=None):
-    """Quantize rows of ``x`` to MX blocks of 32 along the last axis.
+def mx_quantize(x, fmt, dtype="f32", mu=None, block=BLOCK):
+    """Quantize rows of ``x`` to MX blocks of ``block`` (32, or 16 for the g16 variants) along
+    the last axis.
 
     x: [rows, cols] float32 values or bf16 bit patterns; mu: optional float32 [cols]
     subtracted first in fp32 (K-smoothing).
-    Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/32] as E8M0 = X + 127).
+    Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/block] as E8M0 = X + 127).
     """
     x = as_f32(x, dtype)
-    _check(fmt, x)
+    _check(fmt, x, block)
     if mu is not None:
         x = smooth(x, mu)
     rows, cols = x.shape
-    nb = cols // BLOCK
-    xb = x.astype(np.float64).reshape(rows, nb, BLOCK)
+    nb = cols // block
+    xb = x.astype(np.float64).reshape(rows, nb, block)
     amax = np.abs(xb).max(axis=2)
     zero = amax == 0.0
     safe = np.where(zero, 1.0, amax)
@@ -89,8 +101,8 @@ def mx_quantize(x, fmt, dtype="f32", mu=None):
     return codes, scales
 
 
-def mx_dequantize(codes, scales, fmt):
-    """Closed-form decode to float64 [rows, cols].
+def mx_dequantize(codes, scales, fmt, block=BLOCK):
+    """Closed-form decode to float64 [rows, cols] (``block`` elements per scale).
 
     FP4: (-1)^s * E2M1(idx) * 2^(scale-127). INT4: two's-complement q * 2^(scale-127-2).
     """
@@ -101,7 +113,9 @@ def mx_dequantize(codes, scales, fmt):
     nib[:, 1::2] = codes >> 4
     cols = nib.shape[1]
     X = np.asarray(scales).astype(np.int64) - 127
-    Xe = np.repeat(X, BLOCK, axis=1)
+    if block not in BLOCKS or X.shape[1] * block != cols:
+        raise ValueError("scales do not match the codes for this block size")
+    Xe = np.repeat(X, block, axis=1)
     if fmt == "fp4":
         v = np.where(nib & 8, -1.0, 1.0) * E2M1_GRID[nib & 7]
         return np.ldexp(v, Xe).reshape(rows, cols)

@@ -124,3 +124,63 @@ def test_rejects_bad_input():
         mx_quantize(np.ones((1, 40), np.float32), "fp4")
     with pytest.raises(ValueError):
         mx_quantize(np.full((1, 32), np.nan, np.float32), "int4")
+
+
+# ---- g16 variants (one shared exponent per 16 elements)
+
+def test_g16_bruteforce_int4_and_fp4():
+    rng = np.random.default_rng(16)
+    x = _rand(rng, 200)
+    for fmt in ("int4", "fp4"):
+        codes, scales = mx_quantize(x, fmt, block=16)
+        assert codes.shape == (200, 16) and scales.shape == (200, 2)
+        for b in range(x.shape[0]):
+            nib = _nibbles(codes[b])
+            for h in range(2):
+                part = x[b, 16 * h:16 * h + 16].astype(np.float64)
+                amax = float(np.max(np.abs(part)))
+                X = int(scales[b, h]) - 127
+                if fmt == "int4":
+                    assert 1 <= amax / 2.0**X < 2
+                else:
+                    assert 2 < amax / 2.0**X <= 4
+                for i in range(16):
+                    c = nib[16 * h + i]
+                    if fmt == "int4":
+                        y = float(part[i]) * 2.0 ** (2 - X)
+                        q = c - 16 if c >= 8 else c
+                        assert q == sorted(range(-7, 8), key=lambda t: (abs(t - y), t & 1))[0]
+                    else:
+                        y = float(part[i]) / 2.0**X
+                        sgn = 1 if math.copysign(1.0, float(part[i])) < 0 else 0
+                        same = [k for k in range(16) if k >> 3 == sgn]
+                        dist = {k: abs(_e2m1_from_fields(k) - y) for k in same}
+                        near = [k for k in same if dist[k] == min(dist.values())]
+                        assert c == (near[0] if len(near) == 1 else [k for k in near if k % 2 == 0][0])
+
+
+def test_g16_equals_32_block_coding_of_zero_padded_groups():
+    # zeros never change a block maximum and code to 0, so each 16-element group coded alone
+    # equals the first half of a 32-element block whose second half is zero
+    rng = np.random.default_rng(17)
+    x = _rand(rng, 64)
+    for fmt in ("int4", "fp4"):
+        c16, s16 = mx_quantize(x, fmt, block=16)
+        pad = np.zeros((64, 64), np.float32)
+        pad[:, 0:16], pad[:, 32:48] = x[:, 0:16], x[:, 16:32]
+        c32, s32 = mx_quantize(pad, fmt)
+        assert np.array_equal(s16, s32)
+        assert np.array_equal(c16[:, 0:8], c32[:, 0:8]) and np.array_equal(c16[:, 8:16], c32[:, 16:24])
+        assert not c32[:, 8:16].any() and not c32[:, 24:32].any()
+        d16 = mx_dequantize(c16, s16, fmt, block=16)
+        d32 = mx_dequantize(c32, s32, fmt)
+        assert np.array_equal(d16, np.concatenate([d32[:, 0:16], d32[:, 32:48]], axis=1))
+
+
+def test_g16_bit_accounting():
+    # 4-bit elements plus one 8-bit shared exponent per 16 elements: 4.5 bits per element
+    x = np.ones((4, 256), np.float32)
+    codes, scales = mx_quantize(x, "int4", block=16)
+    assert (codes.nbytes + scales.nbytes) * 8 / x.size == 4.5
+    codes, scales = mx_quantize(x, "int4")
+    assert (codes.nbytes + scales.nbytes) * 8 / x.size == 4.25
