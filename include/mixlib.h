@@ -56,7 +56,9 @@ typedef enum {
 } mix_status_t;
 
 typedef enum { MIX_4P25 = 0, MIX_4P5 = 1 } mix_fmt_t; /* MiX-4.25b, MiX-4.5b */
-typedef enum { MX_INT4 = 0, MX_FP4 = 1 } mx_fmt_t;    /* MXINT4 (floor exponent), MXFP4 (ceil exponent) */
+/* MXINT4 (floor exponent), MXFP4 (ceil exponent), one E8M0 per 32 elements; the g16 variants share
+ * one E8M0 per 16 elements (the 4.5-bit weight tier; scales are then [rows, cols/16]) */
+typedef enum { MX_INT4 = 0, MX_FP4 = 1, MX_INT4_G16 = 2, MX_FP4_G16 = 3 } mx_fmt_t;
 typedef enum { MIX_F32 = 0, MIX_BF16 = 1 } mix_dtype_t;
 
 /* ABI version compiled into the library (MIX_ABI_VERSION). */
@@ -88,9 +90,11 @@ mix_status_t mix_quantize(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, int64
  *   E2M1 grid, sign of zero kept. MX_INT4: X = clamp(floor(log2 max|x|), -125, 127);
  *   q = clamp(RNE(x 2^(2-X)), -7, 7).
  * If mu != NULL the operand is fp32(x - mu[col]) (K-smoothing, P1 method overview last bullet).
+ * MX_INT4_G16 / MX_FP4_G16 (P1 experimental setup, the format bullet: the 4.5-bit g16 weights)
+ * apply the same rules to blocks of 16 elements.
  *   x       [rows, cols] fp32 or bf16, row pitch ldx
  *   mu      NULL or [cols] fp32
- *   codes   [rows, cols/2] uint8; scales [rows, cols/32] uint8 (E8M0)
+ *   codes   [rows, cols/2] uint8; scales [rows, cols/32] uint8 (E8M0), [rows, cols/16] for g16
  */
 mix_status_t mx_quantize(mx_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
                          const float* mu, uint8_t* codes, uint8_t* scales, void* stream);
@@ -119,6 +123,7 @@ mix_status_t mx_dequantize(mx_fmt_t fmt, const uint8_t* codes, const uint8_t* sc
  *   B: b_codes [N, K/2], b_scales [N, K/32]   (B holds W^T: one row per output column)
  *   c  [M, N] fp32 or bf16 (c_dtype), row pitch ldc elements (ldc >= N)
  *   ws, ws_bytes: optional workspace (see mix_mx_gemm_workspace_bytes); NULL is allowed
+ * g16 weights: MIX_E_UNSUPPORTED (mx_gemm_b_image_g16 + mix_mx_gemm_images, or mix_mx_gemm_eq6).
  */
 mix_status_t mix_mx_gemm(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, mx_fmt_t b_fmt,
                          const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
@@ -160,14 +165,31 @@ mix_status_t mix_gemm_a_image(mix_fmt_t a_fmt, const uint8_t* a_codes, const voi
 mix_status_t mix_quantize_gemm(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols,
                                int64_t ldx, uint8_t* codes, void* shared, void* img, size_t img_bytes, void* stream);
 
-/* B image from MX codes ([N, K/2] codes, [N, K/32] E8M0 scales). */
+/* B image from MX codes ([N, K/2] codes, [N, K/32] E8M0 scales); g16 formats: MIX_E_UNSUPPORTED
+ * (use mx_gemm_b_image_g16). */
 mix_status_t mx_gemm_b_image(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8_t* b_scales, int64_t N, int64_t K,
                              void* img, size_t img_bytes, void* stream);
 
 /*
+ * B image of g16 weights (MX_INT4_G16 / MX_FP4_G16; P1 experimental setup, the 4.5-bit g16
+ * variants; MiX-INT4g16 = MiX-4.5b activations x MXINT4g16 weights). The matrix core takes one
+ * scale per 32 K elements, so each 32-block's two 16-element exponents are folded into E4M3
+ * element bytes over one shared scale (MXINT4g16: the smaller exponent; MXFP4g16: the larger),
+ * exact when the two exponents differ by at most 8. The number of 32-blocks that could not be
+ * folded exactly is written to *unfoldable (device memory, set by this call on the stream); the
+ * products from this image equal the exact ones when it is 0 (mix_mx_gemm_eq6 is exact for every
+ * input). The image has mx_gemm_b_image_bytes(b_fmt, N, K) bytes (the MX_INT4 layout).
+ *   b_codes [N, K/2] uint8 (16-byte aligned); b_scales16 [N, K/16] E8M0; K a multiple of 128
+ *   unfoldable  uint32 in device memory, 4-byte aligned
+ */
+mix_status_t mx_gemm_b_image_g16(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8_t* b_scales16, int64_t N,
+                                 int64_t K, void* img, size_t img_bytes, uint32_t* unfoldable, void* stream);
+
+/*
  * C = A . B^T from the two images (same results as mix_mx_gemm on the codes). For MX_FP4 the
  * E2M1 nibbles are read from b_codes ([N, K/2], 16-byte aligned) -- the B image holds only the
- * scales; for MX_INT4 b_codes is ignored and may be NULL. c and ldc as for mix_mx_gemm. For
+ * scales; for MX_INT4 and the g16 formats (E4M3 images) b_codes is ignored and may be NULL. c and
+ * ldc as for mix_mx_gemm. For
  * M > 16 each operand image must stay below 2^31 bytes (MIX_E_UNSUPPORTED otherwise; mix_mx_gemm
  * then decodes inside the GEMM instead).
  */
@@ -193,7 +215,9 @@ mix_status_t mix_mx_gemm_images_quantize(mx_fmt_t b_fmt, const void* a_img, cons
 /*
  * The same product computed as P1's Eq. (6) on the vector ALUs: integer sub-block sums of the MX
  * mantissas scaled by 2^(7 - dE), times (8 + m_k), one power-of-two scale per block, fp32
- * accumulation across blocks. Same arguments and results (to fp32 rounding) as mix_mx_gemm.
+ * accumulation across blocks. Same arguments and results (to fp32 rounding) as mix_mx_gemm. For the
+ * g16 formats (b_scales [N, K/16]) each block's sum is split by weight half, one power-of-two
+ * scale per half: exact for every input.
  */
 mix_status_t mix_mx_gemm_eq6(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, mx_fmt_t b_fmt,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,

@@ -5,7 +5,9 @@ device, passes raw device pointers and torch's current stream to the C entry poi
 name, and raises ``MixError`` on a non-zero status. All arithmetic runs in the HIP kernels. There
 is no CPU fallback: without a built ``libmix.so`` every call raises.
 
-Format names: MiX ``"4.25b"`` / ``"4.5b"``; MX ``"int4"`` / ``"fp4"``. bf16 inputs are
+Format names: MiX ``"4.25b"`` / ``"4.5b"``; MX ``"int4"`` / ``"fp4"`` (one E8M0 scale per 32 elements)
+and ``"int4g16"`` / ``"fp4g16"`` (one per 16: the 4.5-bit weights; their B image counts blocks whose
+two halves cannot share one scale exactly in ``BImage.unfoldable``). bf16 inputs are
 ``torch.bfloat16`` tensors; MiX-4.5b shared fields come back as ``torch.int16`` holding the uint16
 bit patterns.
 """
@@ -17,7 +19,8 @@ from . import _lib
 from ._lib import MixError, check
 
 MIX_FMT = {"4.25b": 0, "4.5b": 1}
-MX_FMT = {"int4": 0, "fp4": 1}
+MX_FMT = {"int4": 0, "fp4": 1, "int4g16": 2, "fp4g16": 3}
+MX_BLOCK = {"int4": 32, "fp4": 32, "int4g16": 16, "fp4g16": 16}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 
 __all__ = [
@@ -84,7 +87,7 @@ def mx_quantize(x, fmt="fp4", mu=None):
     if mu is not None and (mu.dtype != torch.float32 or mu.numel() != cols or not mu.is_contiguous()):
         raise MixError("mu must be a contiguous float32 tensor with one value per column")
     codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, cols // MX_BLOCK[fmt]), dtype=torch.uint8, device=x.device)
     check(_lib_().mx_quantize(MX_FMT[fmt], _p(x), DTYPE[x.dtype], rows, cols, ld, _p(mu), _p(codes), _p(scales),
                               _stream()), "mx_quantize")
     return codes, scales
@@ -163,10 +166,13 @@ class AImage:
 
 
 class BImage:
-    """Decode-once GEMM operand of an [N, K] MX matrix; MXFP4 images keep a reference to the codes."""
+    """Decode-once GEMM operand of an [N, K] MX matrix; MXFP4 images keep a reference to the codes.
+    g16 images carry ``unfoldable``: a device uint32 counting the 32-blocks that could not be folded
+    into one scale exactly (0: products from the image are exact)."""
 
-    def __init__(self, buf, fmt, N, K, codes):
+    def __init__(self, buf, fmt, N, K, codes, unfoldable=None):
         self.buf, self.fmt, self.N, self.K, self.codes = buf, fmt, N, K, codes
+        self.unfoldable = unfoldable
 
 
 def mix_gemm_a_image_bytes(M, K):
@@ -223,10 +229,16 @@ def mix_quantize_gemm(x, fmt="4.5b", codes=None, shared=None, image=None, write_
 
 
 def mx_gemm_b_image(codes, scales, fmt="fp4", out=None):
-    """B image of MX codes [N, K/2] + E8M0 scales [N, K/32] (built once per weight)."""
+    """B image of MX codes [N, K/2] + E8M0 scales [N, K/32] ([N, K/16] for the g16 formats; built
+    once per weight)."""
     _need_cuda(codes, scales)
     N, K = codes.shape[0], codes.shape[1] * 2
     buf = _image_buf(mx_gemm_b_image_bytes(fmt, N, K), codes.device, out, "mx_gemm_b_image")
+    if MX_BLOCK[fmt] == 16:
+        unf = torch.empty((1,), dtype=torch.int32, device=codes.device)
+        check(_lib_().mx_gemm_b_image_g16(MX_FMT[fmt], _p(codes), _p(scales), N, K, _p(buf), buf.numel(), _p(unf),
+                                          _stream()), "mx_gemm_b_image_g16")
+        return BImage(buf, fmt, N, K, codes, unf)
     check(_lib_().mx_gemm_b_image(MX_FMT[fmt], _p(codes), _p(scales), N, K, _p(buf), buf.numel(), _stream()),
           "mx_gemm_b_image")
     return BImage(buf, fmt, N, K, codes)

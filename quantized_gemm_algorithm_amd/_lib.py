@@ -38,6 +38,7 @@ SIGNATURES = {
     "mix_quantize_gemm": (c_int, [c_int, c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr, c_ptr, c_ptr, ctypes.c_size_t,
                                   c_ptr]),
     "mx_gemm_b_image": (c_int, [c_int, c_ptr, c_ptr, c_i64, c_i64, c_ptr, ctypes.c_size_t, c_ptr]),
+    "mx_gemm_b_image_g16": (c_int, [c_int, c_ptr, c_ptr, c_i64, c_i64, c_ptr, ctypes.c_size_t, c_ptr, c_ptr]),
     "mix_mx_gemm_images": (c_int, [c_int, c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_int, c_i64, c_ptr]),
     "mix_mx_gemm_images_quantize": (c_int, [c_int, c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_i64, c_ptr,
                                             c_ptr, c_ptr, ctypes.c_size_t, c_ptr]),

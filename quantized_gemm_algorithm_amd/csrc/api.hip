@@ -85,18 +85,22 @@ mix_status_t mix_quantize(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, int64
                     "mix_quantize launch");
 }
 
+static bool mx_known(mx_fmt_t f) { return f == MX_INT4 || f == MX_FP4 || f == MX_INT4_G16 || f == MX_FP4_G16; }
+static bool mx_fp4(mx_fmt_t f) { return f == MX_FP4 || f == MX_FP4_G16; }
+static bool mx_g16(mx_fmt_t f) { return f == MX_INT4_G16 || f == MX_FP4_G16; }
+
 mix_status_t mx_quantize(mx_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
                          const float* mu, uint8_t* codes, uint8_t* scales, void* stream) {
   g_err.clear();
-  if (fmt != MX_INT4 && fmt != MX_FP4) return fail(MIX_E_ENUM, "mx_quantize: unknown MX format %d", (int)fmt);
+  if (!mx_known(fmt)) return fail(MIX_E_ENUM, "mx_quantize: unknown MX format %d", (int)fmt);
   if (mix_status_t st = check_dtype(dtype)) return st;
   bool empty;
   if (mix_status_t st = check_matrix_in("mx_quantize", x, dtype, rows, cols, ldx, &empty)) return st;
   if (empty) return MIX_OK;
   if (!codes || !scales) return fail(MIX_E_NULL, "mx_quantize: codes or scales is NULL");
   if (!aligned16(codes) || (mu && !aligned16(mu))) return fail(MIX_E_ALIGN, "mx_quantize: codes or mu not 16-byte aligned");
-  return hip_status(mix::launch_mx_quantize(fmt == MX_FP4, x, (int)dtype, rows, cols, ldx, mu, codes, scales,
-                                            (hipStream_t)stream),
+  return hip_status(mix::launch_mx_quantize(mx_fp4(fmt), x, (int)dtype, rows, cols, ldx, mu, codes, scales,
+                                            (hipStream_t)stream, mx_g16(fmt)),
                     "mx_quantize launch");
 }
 
@@ -132,11 +136,12 @@ mix_status_t mix_dequantize(mix_fmt_t fmt, const uint8_t* codes, const void* sha
 mix_status_t mx_dequantize(mx_fmt_t fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                            float* out, void* stream) {
   g_err.clear();
-  if (fmt != MX_INT4 && fmt != MX_FP4) return fail(MIX_E_ENUM, "mx_dequantize: unknown MX format %d", (int)fmt);
+  if (!mx_known(fmt)) return fail(MIX_E_ENUM, "mx_dequantize: unknown MX format %d", (int)fmt);
   if (rows < 0 || cols < 0 || cols % 32) return fail(MIX_E_SHAPE, "mx_dequantize: bad shape");
   if (rows == 0 || cols == 0) return MIX_OK;
   if (!codes || !scales || !out) return fail(MIX_E_NULL, "mx_dequantize: NULL pointer");
-  return hip_status(mix::launch_mx_dequantize(fmt == MX_FP4, codes, scales, rows, cols, out, (hipStream_t)stream),
+  return hip_status(mix::launch_mx_dequantize(mx_fp4(fmt), codes, scales, rows, cols, out, (hipStream_t)stream,
+                                              mx_g16(fmt)),
                     "mx_dequantize launch");
 }
 
@@ -146,7 +151,10 @@ static mix_status_t gemm_common(const char* fn, bool eq6, mix_fmt_t a_fmt, const
                                 void* stream) {
   g_err.clear();
   if (a_fmt != MIX_4P25 && a_fmt != MIX_4P5) return fail(MIX_E_ENUM, "%s: unknown MiX format %d", fn, (int)a_fmt);
-  if (b_fmt != MX_INT4 && b_fmt != MX_FP4) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (!mx_known(b_fmt)) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (mx_g16(b_fmt) && !eq6)
+    return fail(MIX_E_UNSUPPORTED, "%s: g16 weights go through mx_gemm_b_image_g16 + mix_mx_gemm_images, or "
+                "mix_mx_gemm_eq6", fn);
   if (mix_status_t st = check_dtype(c_dtype)) return st;
   if (M < 0 || N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
   if (K % 32) return fail(MIX_E_SHAPE, "%s: K=%lld is not a multiple of 32", fn, (long long)K);
@@ -169,17 +177,18 @@ static mix_status_t gemm_common(const char* fn, bool eq6, mix_fmt_t a_fmt, const
   }
   mix::GemmArgs g{};
   g.a_codes = a_codes; g.a_shared = a_shared; g.a_pitch = K / 2; g.a_sh_pitch = K / 32;
-  g.b_codes = b_codes; g.b_scales = b_scales; g.b_pitch = K / 2; g.b_sc_pitch = K / 32; g.b_group = 1;
+  g.b_codes = b_codes; g.b_scales = b_scales; g.b_pitch = K / 2; g.b_sc_pitch = mx_g16(b_fmt) ? K / 16 : K / 32;
+  g.b_group = 1; g.b_g16 = mx_g16(b_fmt);
   g.c = c; g.ldc = ldc; g.row_div = nullptr;
   g.M = (int)M; g.N = (int)N; g.K = (int)K; g.batch = 1; g.causal = 0;
-  hipError_t e = eq6 ? mix::launch_gemm_eq6(a_fmt == MIX_4P5, b_fmt == MX_FP4, c_dtype == MIX_BF16, g, (hipStream_t)stream)
+  hipError_t e = eq6 ? mix::launch_gemm_eq6(a_fmt == MIX_4P5, mx_fp4(b_fmt), c_dtype == MIX_BF16, g, (hipStream_t)stream)
                      : mix::launch_gemm_mfma(a_fmt == MIX_4P5, b_fmt == MX_FP4, c_dtype == MIX_BF16, g, (hipStream_t)stream);
   return hip_status(e, eq6 ? "mix_mx_gemm_eq6 launch" : "mix_mx_gemm launch");
 }
 
 size_t mix_mx_gemm_workspace_bytes(mix_fmt_t a_fmt, mx_fmt_t b_fmt, int64_t M, int64_t N, int64_t K) {
   (void)a_fmt;
-  if (M <= 0 || N <= 0 || K <= 0 || (b_fmt != MX_INT4 && b_fmt != MX_FP4)) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || (b_fmt != MX_INT4 && b_fmt != MX_FP4)) return 0;   // g16: no workspace path
   if (!mix::gemm_f8_eligible(M, N, K)) return 0;
   return mix::gemm_f8_ws_bytes(b_fmt == MX_FP4, M, N, K);
 }
@@ -208,8 +217,8 @@ size_t mix_gemm_a_image_bytes(int64_t M, int64_t K) {
 }
 
 size_t mx_gemm_b_image_bytes(mx_fmt_t b_fmt, int64_t N, int64_t K) {
-  if ((b_fmt != MX_INT4 && b_fmt != MX_FP4) || N <= 0 || N > INT32_MAX || !image_k_ok(K)) return 0;
-  return mix::f8_b_image_layout(b_fmt == MX_FP4, N, K).total;
+  if (!mx_known(b_fmt) || N <= 0 || N > INT32_MAX || !image_k_ok(K)) return 0;
+  return mix::f8_b_image_layout(b_fmt == MX_FP4, N, K).total;   // g16 images are E4M3 (the MXINT4 layout)
 }
 
 static mix_status_t check_image(const char* fn, const void* img, size_t img_bytes, size_t need) {
@@ -258,7 +267,8 @@ mix_status_t mx_gemm_b_image(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8
                              void* img, size_t img_bytes, void* stream) {
   g_err.clear();
   const char* fn = "mx_gemm_b_image";
-  if (b_fmt != MX_INT4 && b_fmt != MX_FP4) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (!mx_known(b_fmt)) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (mx_g16(b_fmt)) return fail(MIX_E_UNSUPPORTED, "%s: g16 weights: use mx_gemm_b_image_g16", fn);
   if (N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
   if (N == 0) return MIX_OK;
   if (N > INT32_MAX || !image_k_ok(K)) return fail(MIX_E_SHAPE, "%s: K=%lld is not a positive multiple of 128", fn, (long long)K);
@@ -268,12 +278,29 @@ mix_status_t mx_gemm_b_image(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8
   return hip_status(mix::launch_gemm_b_image(b_fmt == MX_FP4, b_codes, b_scales, N, K, img, (hipStream_t)stream), fn);
 }
 
+mix_status_t mx_gemm_b_image_g16(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8_t* b_scales16, int64_t N,
+                                 int64_t K, void* img, size_t img_bytes, uint32_t* unfoldable, void* stream) {
+  g_err.clear();
+  const char* fn = "mx_gemm_b_image_g16";
+  if (!mx_g16(b_fmt)) return fail(MIX_E_ENUM, "%s: format %d is not a g16 format", fn, (int)b_fmt);
+  if (N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
+  if (N == 0) return MIX_OK;
+  if (N > INT32_MAX || !image_k_ok(K)) return fail(MIX_E_SHAPE, "%s: K=%lld is not a positive multiple of 128", fn, (long long)K);
+  if (!b_codes || !b_scales16 || !unfoldable) return fail(MIX_E_NULL, "%s: codes, scales or the counter is NULL", fn);
+  if (!aligned16(b_codes) || ((uintptr_t)unfoldable & 3u))
+    return fail(MIX_E_ALIGN, "%s: codes not 16-byte aligned or the counter not 4-byte aligned", fn);
+  if (mix_status_t st = check_image(fn, img, img_bytes, mix::f8_b_image_layout(0, N, K).total)) return st;
+  return hip_status(mix::launch_gemm_b_image_g16(b_fmt == MX_FP4_G16, b_codes, b_scales16, N, K, img, unfoldable,
+                                                 (hipStream_t)stream),
+                    fn);
+}
+
 mix_status_t mix_mx_gemm_images(mx_fmt_t b_fmt, const void* a_img, const void* b_img, const uint8_t* b_codes,
                                 int64_t M, int64_t N, int64_t K, void* c, mix_dtype_t c_dtype, int64_t ldc,
                                 void* stream) {
   g_err.clear();
   const char* fn = "mix_mx_gemm_images";
-  if (b_fmt != MX_INT4 && b_fmt != MX_FP4) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (!mx_known(b_fmt)) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
   if (mix_status_t st = check_dtype(c_dtype)) return st;
   if (M < 0 || N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
   if (M == 0 || N == 0) return MIX_OK;
@@ -298,7 +325,7 @@ mix_status_t mix_mx_gemm_images_quantize(mx_fmt_t b_fmt, const void* a_img, cons
                                          void* q_shared, void* q_img, size_t q_img_bytes, void* stream) {
   g_err.clear();
   const char* fn = "mix_mx_gemm_images_quantize";
-  if (b_fmt != MX_INT4 && b_fmt != MX_FP4) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (!mx_known(b_fmt)) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
   if (M < 0 || N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
   if (M == 0 || N == 0) return MIX_OK;
   if (M > INT32_MAX || N > INT32_MAX || !image_k_ok(K))

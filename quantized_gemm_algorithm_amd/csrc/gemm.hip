@@ -440,7 +440,8 @@ __global__ void __launch_bounds__(256) k_gemm_eq6(GemmArgs g) {
   __shared__ int16_t sb[32][EN];
   __shared__ int sam[EM][4];  // 8 + m_k
   __shared__ int sae[EM];     // Emax
-  __shared__ int sbe[EN];     // X
+  __shared__ int sbe[EN];     // X (g16: of the block's first half)
+  __shared__ int sbe1[EN];    // g16: X of the second half
   const int tiles_n = (g.N + EN - 1) / EN;
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
   const int m0 = tm * EM, n0 = tn * EN;
@@ -471,10 +472,15 @@ __global__ void __launch_bounds__(256) k_gemm_eq6(GemmArgs g) {
         sh = A_FMT == 1 ? ((const uint16_t*)g.a_shared)[(int64_t)batch * g.a_sh_bstride + (int64_t)gm * g.a_sh_pitch + gb]
                         : ((const uint8_t*)g.a_shared)[(int64_t)batch * g.a_sh_bstride + (int64_t)gm * g.a_sh_pitch + gb];
       }
-      int X = 0;
+      int X = 0, X1 = 0;
       if (gn < g.N && gb < nkb) {
         bw = *(const uint32_t*)(bb + (int64_t)gn * g.b_pitch + gb * 16 + wd * 4);
-        X = (int)bsc[(int64_t)gn * g.b_sc_pitch + gb] - 127;
+        if (g.b_g16) {
+          X = (int)bsc[(int64_t)gn * g.b_sc_pitch + 2 * gb] - 127;
+          X1 = (int)bsc[(int64_t)gn * g.b_sc_pitch + 2 * gb + 1] - 127;
+        } else {
+          X = X1 = (int)bsc[(int64_t)gn * g.b_sc_pitch + gb] - 127;
+        }
       }
 #pragma unroll
       for (int e = 0; e < 8; e++) {
@@ -496,12 +502,15 @@ __global__ void __launch_bounds__(256) k_gemm_eq6(GemmArgs g) {
       if (wd == 0) {
         sae[row] = (int)(sh & 15u) - 7;
         sbe[row] = X;
+        sbe1[row] = X1;
 #pragma unroll
         for (int k = 0; k < 4; k++) sam[row][k] = 8 + (int)(A_FMT == 1 ? (sh >> (4 + 3 * k)) & 7u : (sh >> 4) & 7u);
       }
     }
     __syncthreads();
-    int blk[4][4] = {};
+    // the block sum of Eq. (6), split by weight half: sub-blocks 0-1 and 2-3 (one weight exponent
+    // each for g16 weights; the same one otherwise)
+    int blk[4][4] = {}, blk1[4][4] = {};
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       int T[4][4] = {};
@@ -521,14 +530,23 @@ __global__ void __launch_bounds__(256) k_gemm_eq6(GemmArgs g) {
       for (int i = 0; i < 4; i++) {
         int mk = sam[4 * ty + i][k];
 #pragma unroll
-        for (int j = 0; j < 4; j++) blk[i][j] += mk * T[i][j];
+        for (int j = 0; j < 4; j++) {
+          if (k < 2) blk[i][j] += mk * T[i][j];
+          else blk1[i][j] += mk * T[i][j];
+        }
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        acc[i][j] += ldexpf((float)blk[i][j], sae[4 * ty + i] + sbe[4 * tx + j] - 10 - cw);
+      for (int j = 0; j < 4; j++) {
+        if (g.b_g16) {
+          acc[i][j] += ldexpf((float)blk[i][j], sae[4 * ty + i] + sbe[4 * tx + j] - 10 - cw);
+          acc[i][j] += ldexpf((float)blk1[i][j], sae[4 * ty + i] + sbe1[4 * tx + j] - 10 - cw);
+        } else {
+          acc[i][j] += ldexpf((float)(blk[i][j] + blk1[i][j]), sae[4 * ty + i] + sbe[4 * tx + j] - 10 - cw);
+        }
+      }
   }
   const float* rdiv = g.row_div ? g.row_div + (int64_t)batch * g.row_div_bstride : nullptr;
 #pragma unroll

@@ -11,13 +11,13 @@ namespace mix {
 hipError_t launch_mix_quantize(int fmt, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                                uint8_t* codes, void* shared, hipStream_t s);
 hipError_t launch_mx_quantize(int fp4, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
-                              const float* mu, uint8_t* codes, uint8_t* scales, hipStream_t s);
+                              const float* mu, uint8_t* codes, uint8_t* scales, hipStream_t s, int g16 = 0);
 hipError_t launch_mx_quantize_cols(const void* x, int dtype, int64_t rows, int64_t prows, int64_t cols, int64_t ldx,
                                    uint8_t* codes, uint8_t* scales, int64_t cpitch, int64_t spitch, hipStream_t s);
 hipError_t launch_mix_dequantize(int fmt, const uint8_t* codes, const void* shared, int64_t rows, int64_t cols,
                                  float* out, hipStream_t s);
 hipError_t launch_mx_dequantize(int fp4, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
-                                float* out, hipStream_t s);
+                                float* out, hipStream_t s, int g16 = 0);
 hipError_t launch_kmean(const void* x, int dtype, int64_t T, int64_t C, int64_t ldx, float* mu, hipStream_t s);
 
 // Operands of the block-scaled product C = deq(A) . deq(B)^T, optionally batched.
@@ -39,6 +39,7 @@ struct GemmArgs {
   int64_t row_div_bstride;
   int M, N, K, batch;
   int causal;               // 0 none; 1 skip tiles strictly above the diagonal; 2 stop K at the tile's last row
+  int b_g16;                // B scales per 16 elements (rows of K/16; Eq. (6) path only)
 };
 
 hipError_t launch_gemm_mfma(int a_fmt, int b_fp4, int c_bf16, const GemmArgs& g, hipStream_t s);
@@ -55,6 +56,11 @@ hipError_t launch_gemm_a_image(int a_fmt, const uint8_t* a_codes, const void* a_
                                void* img, hipStream_t s);
 hipError_t launch_gemm_b_image(int b_fp4, const uint8_t* b_codes, const uint8_t* b_scales, int64_t N, int64_t K,
                                void* img, hipStream_t s);
+// the B image of g16 weights (one E8M0 per 16 elements): an E4M3 image (the MXINT4 layout) whose
+// per-32 scale is folded from the two halves' exponents; 32-element blocks that cannot be folded
+// exactly are counted into *unfoldable (device, zeroed first)
+hipError_t launch_gemm_b_image_g16(int fp4, const uint8_t* b_codes, const uint8_t* b_scales16, int64_t N, int64_t K,
+                                   void* img, uint32_t* unfoldable, hipStream_t s);
 hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const void* b_img, const uint8_t* b_codes,
                               int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, hipStream_t s);
 hipError_t launch_mix_quantize_img(int fmt, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,

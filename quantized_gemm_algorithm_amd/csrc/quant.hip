@@ -133,7 +133,8 @@ __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ 
 
 // ------------------------------------------------------------------ MX quantizer (K2), blocks along rows
 
-template <int DT, int FP4, int MU>
+// G16: one shared exponent per 16 elements (a lane pair) instead of 32 (a quad); scales [rows, cols/16]
+template <int DT, int FP4, int MU, int G16 = 0>
 __global__ void __launch_bounds__(256) k_mx_quantize(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
                                                       const float* __restrict__ mu, uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales) {
@@ -160,7 +161,13 @@ __global__ void __launch_bounds__(256) k_mx_quantize(const void* __restrict__ x,
       uint32_t a = xb[i] & 0x7FFFFFFFu;
       lmax = a > lmax ? a : lmax;
     }
-    uint32_t bmax = quad_max_u32(lmax);
+    uint32_t bmax;
+    if (G16) {
+      const uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)lmax, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+      bmax = lmax > t ? lmax : t;
+    } else {
+      bmax = quad_max_u32(lmax);
+    }
     uint32_t word = 0;
     int X = mx_exponent(bmax, FP4);
     if (bmax != 0) {
@@ -175,7 +182,11 @@ __global__ void __launch_bounds__(256) k_mx_quantize(const void* __restrict__ x,
       }
     }
     *(uint32_t*)(codes + row * (cols >> 1) + sc * 4) = word;
-    if ((sc & 3) == 0) scales[row * (cols >> 5) + (sc >> 2)] = bmax ? (uint8_t)(X + 127) : (uint8_t)0;
+    if (G16) {
+      if ((sc & 1) == 0) scales[row * (cols >> 4) + (sc >> 1)] = bmax ? (uint8_t)(X + 127) : (uint8_t)0;
+    } else if ((sc & 3) == 0) {
+      scales[row * (cols >> 5) + (sc >> 2)] = bmax ? (uint8_t)(X + 127) : (uint8_t)0;
+    }
   }
 }
 
@@ -241,14 +252,14 @@ __global__ void k_mix_dequantize(int fmt, const uint8_t* __restrict__ codes, con
   }
 }
 
-__global__ void k_mx_dequantize(int fp4, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+__global__ void k_mx_dequantize(int fp4, int g16, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                 int64_t rows, int64_t cols, float* __restrict__ out) {
   const float e2m1[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
   int64_t n = rows * cols;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     int64_t r = i / cols, c = i - r * cols;
     uint32_t nib = (codes[r * (cols >> 1) + (c >> 1)] >> ((c & 1) * 4)) & 0xF;
-    int X = (int)scales[r * (cols >> 5) + (c >> 5)] - 127;
+    int X = (int)(g16 ? scales[r * (cols >> 4) + (c >> 4)] : scales[r * (cols >> 5) + (c >> 5)]) - 127;
     float v;
     if (fp4) {
       v = ldexpf(e2m1[nib & 7], X);
@@ -382,16 +393,18 @@ hipError_t launch_mix_quantize_img(int fmt, const void* x, int dtype, int64_t ro
 }
 
 hipError_t launch_mx_quantize(int fp4, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
-                              const float* mu, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+                              const float* mu, uint8_t* codes, uint8_t* scales, hipStream_t s, int g16) {
   int64_t total = rows * (cols >> 3);
   dim3 g(grid_for(total)), b(256);
-#define MXQ(DT, F, M) hipLaunchKernelGGL((k_mx_quantize<DT, F, M>), g, b, 0, s, x, rows, cols, ldx, mu, codes, scales)
+#define MXQ(DT, F, M) \
+  if (g16) hipLaunchKernelGGL((k_mx_quantize<DT, F, M, 1>), g, b, 0, s, x, rows, cols, ldx, mu, codes, scales); \
+  else hipLaunchKernelGGL((k_mx_quantize<DT, F, M, 0>), g, b, 0, s, x, rows, cols, ldx, mu, codes, scales)
   if (dtype == 1) {
-    if (fp4) { if (mu) MXQ(1, 1, 1); else MXQ(1, 1, 0); }
-    else { if (mu) MXQ(1, 0, 1); else MXQ(1, 0, 0); }
+    if (fp4) { if (mu) { MXQ(1, 1, 1); } else { MXQ(1, 1, 0); } }
+    else { if (mu) { MXQ(1, 0, 1); } else { MXQ(1, 0, 0); } }
   } else {
-    if (fp4) { if (mu) MXQ(0, 1, 1); else MXQ(0, 1, 0); }
-    else { if (mu) MXQ(0, 0, 1); else MXQ(0, 0, 0); }
+    if (fp4) { if (mu) { MXQ(0, 1, 1); } else { MXQ(0, 1, 0); } }
+    else { if (mu) { MXQ(0, 0, 1); } else { MXQ(0, 0, 0); } }
   }
 #undef MXQ
   return hipGetLastError();
@@ -414,8 +427,9 @@ hipError_t launch_mix_dequantize(int fmt, const uint8_t* codes, const void* shar
 }
 
 hipError_t launch_mx_dequantize(int fp4, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
-                                float* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_mx_dequantize, dim3(grid_for(rows * cols)), dim3(256), 0, s, fp4, codes, scales, rows, cols, out);
+                                float* out, hipStream_t s, int g16) {
+  hipLaunchKernelGGL(k_mx_dequantize, dim3(grid_for(rows * cols)), dim3(256), 0, s, fp4, g16, codes, scales, rows, cols,
+                     out);
   return hipGetLastError();
 }
 

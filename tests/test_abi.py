@@ -66,7 +66,7 @@ def test_quantize_validation(lib):
     # empty calls succeed without touching memory
     assert lib.mix_quantize(1, None, 0, 0, 32, 32, None, None, None) == MIX_OK
     assert lib.mix_quantize(1, None, 0, 5, 0, 0, None, None, None) == MIX_OK
-    assert lib.mx_quantize(2, FAKE, 0, 1, 32, 32, None, FAKE, FAKE, None) == MIX_E_ENUM
+    assert lib.mx_quantize(4, FAKE, 0, 1, 32, 32, None, FAKE, FAKE, None) == MIX_E_ENUM
     assert lib.mx_quantize(1, FAKE, 0, 1, 32, 32, MISALIGNED, FAKE, FAKE, None) == MIX_E_ALIGN
     assert lib.mx_quantize(1, None, 0, 0, 64, 64, None, None, None, None) == MIX_OK
     assert lib.mx_quantize_cols(FAKE, 1, 10, 4, 2, FAKE, FAKE, None) == MIX_E_SHAPE
@@ -123,7 +123,7 @@ def test_image_sizes(lib):
     # [ceil(N/16)][K/128][64] for the small-M product (each part 256-byte rounded)
     assert lib.mx_gemm_b_image_bytes(1, 18944, 3584) == 28 * 74 * 1024 + 1184 * 28 * 64
     assert lib.mx_gemm_b_image_bytes(0, 300, 256) == 2 * 2 * 1024 + 300 * 256 + 2560
-    assert lib.mx_gemm_b_image_bytes(2, 300, 256) == 0
+    assert lib.mx_gemm_b_image_bytes(4, 300, 256) == 0
     assert lib.mx_gemm_b_image_bytes(1, 300, 0) == 0
 
 
@@ -159,7 +159,7 @@ def test_image_product_with_quantized_output_validation(lib):
     A16 = P(0x10010)
     BIG = 1 << 30
     # (b_fmt, a_img, b_img, b_codes, M, N, K, c, ldc, q_codes, q_shared, q_img, q_img_bytes, stream)
-    assert f(2, FAKE, FAKE, FAKE, 64, 256, 128, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_ENUM
+    assert f(4, FAKE, FAKE, FAKE, 64, 256, 128, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_ENUM
     assert f(1, FAKE, FAKE, FAKE, 64, 250, 128, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_SHAPE   # N % 32
     assert f(1, FAKE, FAKE, FAKE, 64, 256, 100, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_SHAPE   # K % 128
     assert f(1, FAKE, FAKE, FAKE, 64, 160, 128, None, 0, FAKE, FAKE, FAKE, BIG, None) == MIX_E_SHAPE  # image: N % 128
@@ -173,3 +173,22 @@ def test_image_product_with_quantized_output_validation(lib):
     assert f(1, FAKE, FAKE, FAKE, 64, 256, 128, None, 0, FAKE, FAKE, FAKE, 1000, None) == MIX_E_WORKSPACE
     assert f(1, None, None, None, 0, 256, 128, None, 0, None, None, None, 0, None) == MIX_OK         # empty
 
+
+
+def test_g16_validation(lib):
+    # g16 weights: quantizer formats 2 and 3; the image entry point with its counter; the codes-path
+    # product refers callers to the image or Eq. (6) paths
+    assert lib.mx_gemm_b_image_bytes(2, 18944, 3584) == lib.mx_gemm_b_image_bytes(0, 18944, 3584)
+    assert lib.mx_gemm_b_image_bytes(3, 300, 256) == lib.mx_gemm_b_image_bytes(0, 300, 256)
+    assert lib.mx_gemm_b_image_bytes(4, 300, 256) == 0
+    big = 1 << 30
+    assert lib.mx_gemm_b_image(2, FAKE, FAKE, 256, 256, FAKE, big, None) == MIX_E_UNSUPPORTED
+    assert lib.mx_gemm_b_image_g16(1, FAKE, FAKE, 256, 256, FAKE, big, FAKE, None) == MIX_E_ENUM
+    assert lib.mx_gemm_b_image_g16(2, FAKE, FAKE, 256, 96, FAKE, big, FAKE, None) == MIX_E_SHAPE
+    assert lib.mx_gemm_b_image_g16(2, FAKE, FAKE, 256, 256, FAKE, big, None, None) == MIX_E_NULL
+    assert lib.mx_gemm_b_image_g16(3, FAKE, FAKE, 256, 256, FAKE, big, P(0x10002), None) == MIX_E_ALIGN
+    assert lib.mx_gemm_b_image_g16(3, FAKE, FAKE, 256, 256, FAKE, 16, FAKE, None) == MIX_E_WORKSPACE
+    assert lib.mx_gemm_b_image_g16(2, None, None, 0, 256, None, 0, None, None) == MIX_OK
+    assert lib.mix_mx_gemm(1, FAKE, FAKE, 2, FAKE, FAKE, 4, 4, 32, FAKE, 0, 4, None, 0, None) == MIX_E_UNSUPPORTED
+    assert lib.mix_mx_gemm_workspace_bytes(1, 2, 4096, 18944, 3584) == 0
+    assert lib.mx_quantize(4, FAKE, 0, 4, 32, 32, None, FAKE, FAKE, None) == MIX_E_ENUM
