@@ -260,6 +260,32 @@ def bench_linear(torch, q, args, which):
                       "quantize C (unfused, bf16 C through HBM) or the GEMM epilogue codes C (fused, no C)")
         fq["speedup"] = fq["unfused_ms"] / fq["fused_ms"]
 
+    # MiX-INT4g16 (MiX-4.5b activations x MXINT4g16 weights, one exponent per 16 weight elements):
+    # the same A image against the folded E4M3 B image of the g16 weights
+    g16 = None
+    if a_fmt == "4.5b":
+        def evt_ms(fn, reps):
+            ts = []
+            for _ in range(reps):
+                a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+                a.record(); fn(); b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            return float(np.median(ts))
+        gc, gs = q.mx_quantize(w, "int4g16")
+        gwq_ms = evt_ms(lambda: q.mx_quantize(w, "int4g16"), 5)
+        gimg = q.mx_gemm_b_image(gc, gs, "int4g16")
+        gimg_ms = evt_ms(lambda: q.mx_gemm_b_image(gc, gs, "int4g16", out=gimg.buf), 5)
+        aimg0 = bufs[0][2]
+        settle(torch, lambda i, marks=None: q.mix_mx_gemm_images(aimg0, gimg, out=out), 100)
+        gg_ms = evt_ms(lambda: q.mix_mx_gemm_images(aimg0, gimg, out=out), 10)
+        g16 = {"pairing": "MiX-INT4g16 (MiX-4.5b x MXINT4g16)", "kernel": "k_gemm_f8 (E4M3 B image)",
+               "gemm_ms": gg_ms, "TFLOP/s": 2.0 * M * N * K / (gg_ms * 1e-3) / 1e12,
+               "frac_mfma": 2.0 * M * N * K / (gg_ms * 1e-3) / 1e12 / FP8_MFMA_PEAK_TFLOPS,
+               "weight_quantizer_ms": gwq_ms, "image_build_ms": gimg_ms,
+               "unfoldable_blocks": int(gimg.unfoldable.item())}
+        del gc, gs, gimg  # free before the CPU baseline
+
     flops = 2.0 * M * N * K
     sh_bytes = 2 if a_fmt == "4.5b" else 1
     tiles_m, tiles_n = -(-M // 256), -(-N // 256)
@@ -295,6 +321,8 @@ def bench_linear(torch, q, args, which):
     }
     if fq is not None:
         res["fused_output_quantization"] = fq
+    if g16 is not None:
+        res["g16_weights"] = g16
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_linear(g["x"], g["w_t"], a_fmt, b_fmt, M, N, wl)
     return res
