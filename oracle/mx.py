@@ -67,16 +67,20 @@ def _rne_grid_index(y):
     return np.where(tie & (first % 2 == 1), nxt, first)
 
 
-def mx_quantize(x, fmt, dtype="f32", mu=None, block=BLOCK):
+def mx_quantize(x, fmt, dtype="f32", mu=None, block=BLOCK, fp4_rule="ceil"):
     """Quantize rows of ``x`` to MX blocks of ``block`` (32, or 16 for the g16 variants) along
     the last axis.
 
     x: [rows, cols] float32 values or bf16 bit patterns; mu: optional float32 [cols]
-    subtracted first in fp32 (K-smoothing).
+    subtracted first in fp32 (K-smoothing). fp4_rule: the MXFP4 shared exponent, "ceil"
+    (X = ceil(log2 amax) - 2, the paper's MXFP4) or "floor" (the OCP rule X = floor(log2 amax) - 2,
+    which leaves block maxima in (6, 8) * 2^X to saturate; used only as a comparator).
     Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/block] as E8M0 = X + 127).
     """
     x = as_f32(x, dtype)
     _check(fmt, x, block)
+    if fp4_rule not in ("ceil", "floor"):
+        raise ValueError(f"unknown MXFP4 exponent rule {fp4_rule!r}")
     if mu is not None:
         x = smooth(x, mu)
     rows, cols = x.shape
@@ -86,7 +90,7 @@ def mx_quantize(x, fmt, dtype="f32", mu=None, block=BLOCK):
     zero = amax == 0.0
     safe = np.where(zero, 1.0, amax)
     if fmt == "fp4":
-        X = np.maximum(ceil_log2(safe) - 2, -127)
+        X = np.maximum((ceil_log2(safe) if fp4_rule == "ceil" else floor_log2(safe)) - 2, -127)
         y = np.ldexp(xb, -X[:, :, None])
         idx = _rne_grid_index(y)
         nib = (np.signbit(xb).astype(np.int64) << 3) | idx

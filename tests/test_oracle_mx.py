@@ -184,3 +184,29 @@ def test_g16_bit_accounting():
     assert (codes.nbytes + scales.nbytes) * 8 / x.size == 4.5
     codes, scales = mx_quantize(x, "int4")
     assert (codes.nbytes + scales.nbytes) * 8 / x.size == 4.25
+
+
+def test_fp4_floor_rule_bruteforce_and_saturation():
+    # the OCP floor rule (a comparator only): X = floor(log2 amax) - 2, the block max lands in
+    # [4, 8) after scaling and saturates to 6 above 6; elements are the nearest E2M1 value, ties
+    # to the even code
+    rng = np.random.default_rng(15)
+    x = _rand(rng, 300)
+    codes, scales = mx_quantize(x, "fp4", fp4_rule="floor")
+    sat = 0
+    for b in range(x.shape[0]):
+        amax = float(np.max(np.abs(x[b].astype(np.float64))))
+        X = int(scales[b, 0]) - 127
+        assert 4 <= amax / 2.0**X < 8
+        sat += amax / 2.0**X > 6
+        for i, c in enumerate(_nibbles(codes[b])):
+            y = float(x[b, i]) / 2.0**X
+            sgn = 1 if math.copysign(1.0, float(x[b, i])) < 0 else 0
+            same = [k for k in range(16) if k >> 3 == sgn]
+            dist = {k: abs(_e2m1_from_fields(k) - y) for k in same}
+            near = [k for k in same if dist[k] == min(dist.values())]
+            expect = near[0] if len(near) == 1 else [k for k in near if k % 2 == 0][0]
+            assert c == expect, (y, c, near)
+    assert 0.3 < sat / x.shape[0] < 0.55   # about log2(8/6) of the maxima saturate
+    with pytest.raises(ValueError):
+        mx_quantize(x, "fp4", fp4_rule="round")
