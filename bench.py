@@ -525,7 +525,38 @@ def bench_attention(torch, q, args):
                      "frac": tf / FP8_MFMA_PEAK_TFLOPS, "traffic": None,
                      "kernel": "mix_attn_prefill (all kernels of the call)", "kernel_ms": ms_step},
     }
+    res["underflow_map"] = underflow_section(torch, q, kd.view(T, Hkv * d))
     return res
+
+
+def underflow_section(torch, q, k2d):
+    """The underflow ("dead zone") map of the keys [T, Hkv d], blocks of 32 along the head dimension,
+    raw and K-smoothed: per format the fraction of nonzero elements coded to zero, and the time of
+    one mix_underflow_map call (three launches: clear, amax, map; the operand is read twice)."""
+    mu = q.mix_kmean(k2d)
+    out = {"what": "fraction of nonzero key elements each format codes to zero (32-element blocks)",
+           "operand": list(k2d.shape)}
+    for name, m in (("raw", None), ("smoothed", mu)):
+        counts, _ = q.mix_underflow_map(k2d, mu=m)
+        tot = counts.sum(dim=1).cpu().numpy()
+        out[name] = {kind: float(tot[i]) / max(float(tot[-1]), 1.0) for i, kind in enumerate(q.UF_KINDS[:-1])}
+    ws = torch.empty((q.mix_underflow_map_workspace_bytes(*k2d.shape),), dtype=torch.uint8, device=k2d.device)
+    reps = 20
+    for _ in range(3):
+        q.mix_underflow_map(k2d, workspace=ws)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        q.mix_underflow_map(k2d, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = 2 * k2d.numel() * k2d.element_size()
+    out["call_ms"] = ms
+    out["timing"] = f"{reps} back-to-back calls between two HIP events"
+    out["read_GB/s"] = nbytes / (ms * 1e-3) / 1e9
+    return out
 
 
 def calibrate_copy(torch):

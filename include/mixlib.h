@@ -232,6 +232,43 @@ mix_status_t mix_mx_gemm_eq6(mix_fmt_t a_fmt, const uint8_t* a_codes, const void
  */
 mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, int64_t ldk, float* mu, void* stream);
 
+/*
+ * Underflow ("dead zone") map -- P1, figure walk, the underflow-map figure (keys coded with
+ * 32-element blocks in MXINT4, MXFP4, NVFP4 with its block forced to 32, and MiX; nonzero elements
+ * that decode to zero are mathematical underflow) and the key results' MXFP4 bullet (the OCP floor
+ * exponent rule against the ceil rule). A diagnostic: nothing on the product path calls it.
+ *   x      [rows, cols] fp32 or bf16, row pitch ldx (cols a multiple of 32; x and the row pitch in
+ *          bytes 16-byte aligned); blocks of 32 run along cols
+ *   mu     optional fp32 [cols] (16-byte aligned): the map is of fp32(x - mu), the smoothed operand
+ *   counts device uint32 [MIX_UF_KINDS][cols], overwritten: counts[k][c] = the elements of column c
+ *          that are nonzero on input and that format k codes to zero; counts[MIX_UF_NONZERO][c] =
+ *          the nonzero elements of column c
+ *   amax   device float [1], overwritten with the largest magnitude of the (smoothed) operand
+ *   ws     device workspace of ws_bytes >= mix_underflow_map_workspace_bytes(rows, cols) bytes
+ *          (16-byte aligned; caller-owned; its contents on entry do not matter); may be NULL when
+ *          that size is 0
+ * The formats: MXINT4 and MXFP4 (ceil) as mx_quantize codes them; MXFP4 under the OCP rule
+ * X = floor(log2 amax_b) - 2; NVFP4 with a tensor scale g = amax / 2688, block scales the E4M3
+ * value nearest to amax_b / (6 g) (ties to the even code) and E2M1 elements (an element is zero iff
+ * |x| <= s g / 4); MiX-4.25b and MiX-4.5b as mix_quantize codes them. Every decision is exact.
+ * Three launches on the stream (per-workgroup maxima, the map into per-workgroup sums, their
+ * sum), no atomics, so the counts do not depend on scheduling; rows <= 2^31 - 1.
+ */
+typedef enum {
+  MIX_UF_MXINT4 = 0,
+  MIX_UF_MXFP4_FLOOR = 1,
+  MIX_UF_MXFP4_CEIL = 2,
+  MIX_UF_NVFP4_B32 = 3,
+  MIX_UF_MIX_4_25B = 4,
+  MIX_UF_MIX_4_5B = 5,
+  MIX_UF_NONZERO = 6,
+  MIX_UF_KINDS = 7
+} mix_uf_kind_t;
+size_t mix_underflow_map_workspace_bytes(int64_t rows, int64_t cols);
+mix_status_t mix_underflow_map(const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
+                               const float* mu, uint32_t* counts, float* amax, void* ws, size_t ws_bytes,
+                               void* stream);
+
 /* Optional dumps of the attention stages (any pointer may be NULL). Prefill: s and p [Hq, T, Tp]
  * fp32, p_codes [Hq, T, Tp/2], p_shared [Hq, T, Tp/32], l [Hq, T], with Tp = T rounded up to 32.
  * Decode: s and p [B, Hq, Lp], p_codes [B, Hq, Lp/2], p_shared [B, Hq, Lp/32], l [B, Hq], with

@@ -26,7 +26,7 @@ DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 __all__ = [
     "MixError", "mix_quantize", "mx_quantize", "mx_quantize_cols", "mix_dequantize", "mx_dequantize",
     "mix_mx_gemm", "mix_mx_gemm_eq6", "AImage", "BImage", "mix_gemm_a_image", "mix_quantize_gemm",
-    "mx_gemm_b_image", "mix_mx_gemm_images", "mix_mx_gemm_images_quantize", "mix_kmean", "mix_attn_prefill", "KVCache", "mix_kv_cache_prefill",
+    "mx_gemm_b_image", "mix_mx_gemm_images", "mix_mx_gemm_images_quantize", "mix_kmean", "mix_underflow_map", "mix_underflow_map_workspace_bytes", "UF_KINDS", "mix_attn_prefill", "KVCache", "mix_kv_cache_prefill",
     "mix_attn_decode", "abi_version",
 ]
 
@@ -305,6 +305,30 @@ def mix_kmean(k):
     mu = torch.empty((C,), dtype=torch.float32, device=k.device)
     check(_lib_().mix_kmean(_p(k), DTYPE[k.dtype], T, C, ld, _p(mu), _stream()), "mix_kmean")
     return mu
+
+
+def mix_underflow_map_workspace_bytes(rows, cols):
+    return _lib_().mix_underflow_map_workspace_bytes(rows, cols)
+
+
+UF_KINDS = ("mxint4", "mxfp4_floor", "mxfp4_ceil", "nvfp4_b32", "mix_4.25b", "mix_4.5b", "nonzero")
+
+
+def mix_underflow_map(x, mu=None, workspace=None):
+    """Underflow map of x [rows, cols] (optionally smoothed, fp32(x - mu)): returns (counts, amax),
+    counts an int64 tensor [7, cols] -- per column, the nonzero elements each format of UF_KINDS[:6]
+    codes to zero, then the nonzero elements -- and amax the operand's largest magnitude."""
+    _need_cuda(x, mu, workspace)
+    rows, cols, ld = _matrix(x, "x")
+    counts = torch.empty((len(UF_KINDS), cols), dtype=torch.int32, device=x.device)
+    amax = torch.empty((1,), dtype=torch.float32, device=x.device)
+    need = _lib_().mix_underflow_map_workspace_bytes(rows, cols)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    check(_lib_().mix_underflow_map(_p(x), DTYPE[x.dtype], rows, cols, ld, _p(mu), _p(counts), _p(amax),
+                                    _p(workspace), workspace.numel() * workspace.element_size(), _stream()),
+          "mix_underflow_map")
+    return counts.to(torch.int64) & 0xFFFFFFFF, amax
 
 
 # ---------------------------------------------------------------- attention

@@ -43,6 +43,8 @@ SIGNATURES = {
     "mix_mx_gemm_images_quantize": (c_int, [c_int, c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_i64, c_ptr,
                                             c_ptr, c_ptr, ctypes.c_size_t, c_ptr]),
     "mix_kmean": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr, c_ptr]),
+    "mix_underflow_map_workspace_bytes": (ctypes.c_size_t, [c_i64, c_i64]),
+    "mix_underflow_map": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr, c_ptr, c_ptr, c_ptr, ctypes.c_size_t, c_ptr]),
     "mix_attn_prefill_workspace_bytes": (ctypes.c_size_t, [c_i64, c_i64, c_i64, c_i64]),
     "mix_attn_prefill": (c_int, [c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_i64, c_int, c_ptr, c_ptr, c_ptr,
                                  ctypes.c_size_t, c_ptr, c_ptr]),

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmix.so")
-SOURCES = ["quant.hip", "gemm.hip", "gemm_f8.hip", "g16.hip", "attn.hip", "api.hip"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_f8.hip", "g16.hip", "underflow.hip", "attn.hip", "api.hip"]
 ARCH = "gfx950"
 
 

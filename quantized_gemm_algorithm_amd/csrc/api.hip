@@ -369,6 +369,34 @@ mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, i
   return hip_status(mix::launch_kmean(k, (int)dtype, T, C, ldk, mu, (hipStream_t)stream), "mix_kmean launch");
 }
 
+size_t mix_underflow_map_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || cols % 32 || rows > INT32_MAX) return 0;
+  return mix::uf_plan(rows, cols).bytes;
+}
+
+mix_status_t mix_underflow_map(const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
+                               const float* mu, uint32_t* counts, float* amax, void* ws, size_t ws_bytes,
+                               void* stream) {
+  g_err.clear();
+  if (mix_status_t st = check_dtype(dtype)) return st;
+  bool empty;
+  if (mix_status_t st = check_matrix_in("mix_underflow_map", x, dtype, rows, cols, ldx, &empty)) return st;
+  if (rows > INT32_MAX) return fail(MIX_E_SHAPE, "mix_underflow_map: rows above 2^31-1");
+  if (cols == 0) return MIX_OK;
+  if (!counts || !amax) return fail(MIX_E_NULL, "mix_underflow_map: counts or amax is NULL");
+  if (((uintptr_t)counts & 3u) || ((uintptr_t)amax & 3u) || (mu && !aligned16(mu)))
+    return fail(MIX_E_ALIGN, "mix_underflow_map: counts/amax not 4-byte aligned or mu not 16-byte aligned");
+  if (empty) rows = 0;   // zero rows: the counts and amax are still cleared
+  const size_t need = rows ? mix::uf_plan(rows, cols).bytes : 0;
+  if (need) {
+    if (!ws) return fail(MIX_E_NULL, "mix_underflow_map: workspace is NULL (%zu bytes needed)", need);
+    if (ws_bytes < need) return fail(MIX_E_WORKSPACE, "mix_underflow_map: workspace of %zu bytes, %zu needed", ws_bytes, need);
+    if (!aligned16(ws)) return fail(MIX_E_ALIGN, "mix_underflow_map: workspace not 16-byte aligned");
+  }
+  return hip_status(mix::launch_underflow_map(x, (int)dtype, rows, cols, ldx, mu, counts, amax, ws, (hipStream_t)stream),
+                    "mix_underflow_map launch");
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- attention

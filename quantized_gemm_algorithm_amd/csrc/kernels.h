@@ -19,6 +19,14 @@ hipError_t launch_mix_dequantize(int fmt, const uint8_t* codes, const void* shar
 hipError_t launch_mx_dequantize(int fp4, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                                 float* out, hipStream_t s, int g16 = 0);
 hipError_t launch_kmean(const void* x, int dtype, int64_t T, int64_t C, int64_t ldx, float* mu, hipStream_t s);
+// underflow.hip: counts [7][cols] (MXINT4, MXFP4 floor, MXFP4 ceil, NVFP4 B=32, MiX-4.25b, MiX-4.5b, nonzero)
+struct UfPlan {
+  int64_t cb, rpw, gy, ablocks;   // 32-column blocks, rows per workgroup, workgroup rows, amax workgroups
+  size_t part_off, bytes;         // offset of the count partials in the workspace, workspace size
+};
+UfPlan uf_plan(int64_t rows, int64_t cols);
+hipError_t launch_underflow_map(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, const float* mu,
+                                uint32_t* counts, float* amax, void* ws, hipStream_t s);
 
 // Operands of the block-scaled product C = deq(A) . deq(B)^T, optionally batched.
 struct GemmArgs {

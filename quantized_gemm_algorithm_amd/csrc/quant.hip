@@ -20,28 +20,6 @@
 
 namespace mix {
 
-// ------------------------------------------------------------------ loading 8 elements
-
-template <int DT>
-__device__ __forceinline__ void load8(const void* base, int64_t row, int64_t ld, int64_t col, uint32_t (&x)[8]) {
-  if (DT == 1) {  // bf16
-    const uint16_t* p = (const uint16_t*)base + row * ld + col;
-    uint4 v = *(const uint4*)p;
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      x[2 * i] = (w[i] & 0xFFFFu) << 16;
-      x[2 * i + 1] = w[i] & 0xFFFF0000u;
-    }
-  } else {  // fp32
-    const float* p = (const float*)base + row * ld + col;
-    uint4 v0 = *(const uint4*)p;
-    uint4 v1 = *(const uint4*)(p + 4);
-    x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
-    x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
-  }
-}
-
 // ------------------------------------------------------------------ MiX quantizer (K1)
 
 // With IMG the lane also writes the GEMM A image of its sub-block (f8_image.h): 8 E4M3 bytes, and

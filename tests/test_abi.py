@@ -192,3 +192,31 @@ def test_g16_validation(lib):
     assert lib.mix_mx_gemm(1, FAKE, FAKE, 2, FAKE, FAKE, 4, 4, 32, FAKE, 0, 4, None, 0, None) == MIX_E_UNSUPPORTED
     assert lib.mix_mx_gemm_workspace_bytes(1, 2, 4096, 18944, 3584) == 0
     assert lib.mx_quantize(4, FAKE, 0, 4, 32, 32, None, FAKE, FAKE, None) == MIX_E_ENUM
+
+
+def test_underflow_map_validation(lib):
+    f = lib.mix_underflow_map
+    W = 1 << 30
+    # (x, dtype, rows, cols, ldx, mu, counts, amax, ws, ws_bytes, stream)
+    assert f(FAKE, 5, 4, 32, 32, None, FAKE, FAKE, FAKE, W, None) == MIX_E_ENUM
+    assert f(FAKE, 0, 4, 40, 40, None, FAKE, FAKE, FAKE, W, None) == MIX_E_SHAPE
+    assert f(FAKE, 0, 4, 32, 16, None, FAKE, FAKE, FAKE, W, None) == MIX_E_SHAPE
+    assert f(FAKE, 0, -1, 32, 32, None, FAKE, FAKE, FAKE, W, None) == MIX_E_SHAPE
+    assert f(None, 0, 4, 32, 32, None, FAKE, FAKE, FAKE, W, None) == MIX_E_NULL
+    assert f(FAKE, 0, 4, 32, 32, None, None, FAKE, FAKE, W, None) == MIX_E_NULL
+    assert f(FAKE, 0, 4, 32, 32, None, FAKE, None, FAKE, W, None) == MIX_E_NULL
+    assert f(FAKE, 0, 4, 32, 32, None, FAKE, FAKE, None, W, None) == MIX_E_NULL
+    assert f(MISALIGNED, 0, 4, 32, 32, None, FAKE, FAKE, FAKE, W, None) == MIX_E_ALIGN
+    assert f(FAKE, 1, 4, 32, 36, None, FAKE, FAKE, FAKE, W, None) == MIX_E_ALIGN
+    assert f(FAKE, 0, 4, 32, 32, P(0x10004), FAKE, FAKE, FAKE, W, None) == MIX_E_ALIGN
+    assert f(FAKE, 0, 4, 32, 32, None, P(0x10002), FAKE, FAKE, W, None) == MIX_E_ALIGN
+    assert f(FAKE, 0, 4, 32, 32, None, FAKE, FAKE, P(0x10008), W, None) == MIX_E_ALIGN
+    assert f(FAKE, 0, 1 << 31, 32, 32, None, FAKE, FAKE, FAKE, W, None) == MIX_E_SHAPE
+    need = lib.mix_underflow_map_workspace_bytes(4096, 512)
+    # 512 amax partials + per workgroup row 7 sums per column (32 workgroup rows of 128 rows here)
+    assert need == 2048 + 32 * 7 * 512 * 4
+    assert f(FAKE, 0, 4096, 512, 512, None, FAKE, FAKE, FAKE, need - 1, None) == MIX_E_WORKSPACE
+    assert lib.mix_underflow_map_workspace_bytes(0, 512) == 0
+    assert lib.mix_underflow_map_workspace_bytes(4, 40) == 0
+    assert lib.mix_underflow_map_workspace_bytes(1, 32) == 2048 + 1024   # 7 x 32 x 4 rounded to 256
+    assert f(None, 0, 4, 0, 0, None, None, None, None, 0, None) == MIX_OK
