@@ -92,13 +92,17 @@ __global__ void __launch_bounds__(256) k_expand_b_g16(const uint8_t* __restrict_
   }
 }
 
+__global__ void k_clear_u32(uint32_t* p) {
+  if (threadIdx.x == 0) *p = 0u;
+}
+
 hipError_t launch_gemm_b_image_g16(int fp4, const uint8_t* b_codes, const uint8_t* b_scales16, int64_t N, int64_t K,
                                    void* img, uint32_t* unfoldable, hipStream_t s) {
   const F8BImage L = f8_b_image_layout(0, N, K);
   uint8_t* base = (uint8_t*)img;
   const int tiles_n = (int)((N + FT - 1) / FT);
-  hipError_t e = hipMemsetAsync(unfoldable, 0, sizeof(uint32_t), s);
-  if (e != hipSuccess) return e;
+  // the counter is cleared by a kernel, not a memset node, so the call can also be captured in a graph
+  hipLaunchKernelGGL(k_clear_u32, dim3(1), dim3(64), 0, s, unfoldable);
   int64_t blocks = (N * (K >> 5) + 255) / 256;
   if (blocks > 65535 * 4) blocks = 65535 * 4;
   if (fp4)
