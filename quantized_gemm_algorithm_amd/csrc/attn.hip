@@ -1,5 +1,8 @@
 // K-smoothed attention over MiX/MX-coded operands, prefill and decode, for gfx950.
 //
+// "P1" below is the pchao.org digest of the paper, titled
+// "MiX：面向端到端低比特视觉语言模型加速的微反缩放"; citations name its sections and figures.
+//
 // What it computes (P1, 方法概览 / method overview, last bullet; 核心创新 / innovations, third
 // bullet; 关键结果 / key results, first bullet): keys are smoothed by subtracting their per-channel
 // mean over the prefill tokens (softmax is unchanged by a constant shift per query row), the mean is

@@ -1,5 +1,8 @@
 // The GEMM B image of g16 weights: MXINT4g16 / MXFP4g16, one shared exponent per 16 elements.
 //
+// "P1" below is the pchao.org digest of the paper, titled
+// "MiX：面向端到端低比特视觉语言模型加速的微反缩放"; citations name its sections and figures.
+//
 // P1 (主要实验设置 / experimental setup, the format bullet) lists the 4.5-bit "g16" weight
 // variants; MiX-INT4g16 pairs MiX-4.5b activations with MXINT4g16 weights. The block-scaled MFMA
 // takes one E8M0 scale per 32 K elements, so the two 16-element halves of a 32-block share one

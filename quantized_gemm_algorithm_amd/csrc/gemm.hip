@@ -1,5 +1,8 @@
 // A-MiX x W-MX matrix product for gfx950.
 //
+// "P1" below is the pchao.org digest of the paper, titled
+// "MiX：面向端到端低比特视觉语言模型加速的微反缩放"; citations name its sections and figures.
+//
 // The method (P1, 方法概览 / method overview, the dual-format bullet and Eq. (6)): activations are
 // MiX-coded and weights MX-coded; in each 32-element block dot product the shared MiX mantissa
 // and the exponents factor out, leaving per-element shifts of the MX mantissa.

@@ -1,5 +1,8 @@
 // Fast A-MiX x W-MX product: a decode pass, then an MXFP8 x MX{FP4,FP8} block-scaled MFMA GEMM.
 //
+// "P1" below is the pchao.org digest of the paper, titled
+// "MiX：面向端到端低比特视觉语言模型加速的微反缩放"; citations name its sections and figures.
+//
 // P1 (method overview, the dual-format bullet and Eq. (6)) factors the shared MiX mantissa out of
 // each block sum. On MI355X the exact multiplier is the matrix core. Each MiX element
 // (1.m)_2 2^(Emax-dE) is exactly the E4M3 byte (1.m)_2 2^(1-dE) times the block power of two

@@ -1,5 +1,8 @@
 // Underflow ("dead zone") map of the 4-bit block formats on one operand.
 //
+// "P1" below is the pchao.org digest of the paper, titled
+// "MiX：面向端到端低比特视觉语言模型加速的微反缩放"; citations name its sections and figures.
+//
 // P1 (逐图理解论文 / figure walk, the underflow-map figure) compares how many key elements each
 // 4-bit format codes to zero with 32-element blocks: MXINT4, MXFP4, NVFP4 (its block forced to
 // 32) and MiX; the MXFP4 bullet of the key results adds the floor-versus-ceil exponent rule. Per
