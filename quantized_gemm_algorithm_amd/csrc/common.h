@@ -20,6 +20,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 -> packed bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32; the kernels keep fp32
+// denormals, so subnormal inputs round like any other), a in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16_rne(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// 16-byte global store marked non-temporal: an output written once and not read back by this
+// kernel, so it should not displace the operand lines the L2 keeps for other tiles.
+__device__ __forceinline__ void store16_nt(void* p, uint4 v) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (u32x4_t*)p);
+}
+
 // Exact fp32 bit pattern of k * 2^e for 1 <= k < 2^24 (normal or subnormal result; e >= -149 - bits).
 __device__ __forceinline__ uint32_t exact_f32_bits(uint32_t k, int e) {
   int nb = 31 - __builtin_clz(k);  // index of the leading one

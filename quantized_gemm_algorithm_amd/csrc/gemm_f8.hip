@@ -448,8 +448,7 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
             const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
                         v3 = acc[i][j][4 * q + 3];
             if (C_BF16)
-              *(uint2*)dst = make_uint2((uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16),
-                                        (uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16));
+              *(uint2*)dst = make_uint2(pk_bf16_rne(v0, v1), pk_bf16_rne(v2, v3));
             else
               *(float4*)dst = make_float4(v0, v1, v2, v3);
           }
@@ -482,7 +481,7 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
           if (gm >= g.M) continue;
           uint8_t* out = (uint8_t*)g.c + ((int64_t)gm * g.ldc + gn) * ES;
           if (vec_ok && gn + EPL <= g.N) {
-            *(uint4*)out = v;
+            store16_nt(out, v);
           } else {
             const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
