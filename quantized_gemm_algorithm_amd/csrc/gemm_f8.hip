@@ -435,6 +435,9 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
 
     // Epilogue, staged through LDS so that global stores write whole 128-byte row segments.
     const int mw = cur_tm * FT + 64 * wm, nw = cur_tn * FT + 128 * wn;
+    // a tile inside C with aligned rows: each pass reads its four rows back and stores them with no
+    // per-store bounds checks, so the four LDS reads are in flight together
+    const bool fast = !OQ && vec_ok && (cur_tm + 1) * FT <= g.M && (cur_tn + 1) * FT <= g.N;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
 #pragma unroll
@@ -452,6 +455,17 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
             else
               *(float4*)dst = make_float4(v0, v1, v2, v3);
           }
+        if (fast) {
+          const int ch = lane & 7;
+          uint4 v[4];
+#pragma unroll
+          for (int it = 0; it < 4; it++) v[it] = *(const uint4*)(reg + (it * 8 + (lane >> 3)) * PITCH + ch * 16);
+          uint8_t* out = (uint8_t*)g.c + ((int64_t)(mw + 32 * i + (lane >> 3)) * g.ldc + nw + jp * CW + ch * EPL) * ES;
+          const int64_t step8 = (int64_t)8 * g.ldc * ES;   // 8 rows
+#pragma unroll
+          for (int it = 0; it < 4; it++) store16_nt(out + it * step8, v[it]);
+          continue;
+        }
 #pragma unroll
         for (int it = 0; it < 4; it++) {
           const int row = it * 8 + (lane >> 3), ch = lane & 7;
