@@ -442,7 +442,8 @@ def bench_decode(torch, q, args):
                    "d": d, "frac_hbm": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                    "bytes_per_step": step_bytes, "rotating_sets": nset},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "k_gemv_f8", "kernel_ms": gv_ms,
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"), "kernel": "k_gemv_f8",
+                     "kernel_ms": gv_ms,
                      "algorithmic_bytes": gv_bytes},
         "parts": {"execution": "HIP graph per step (parts timed on eager launches)",
                   "eager_ms_per_step": ms_eager, "quantize_x_ms": q_ms, "gemv_ms": gv_ms,
@@ -522,7 +523,7 @@ def bench_attention(torch, q, args):
         "config": {"workload": "prefill_attention_t4096_h28_kv4_d128", "T": T, "Hq": Hq, "Hkv": Hkv, "d": d,
                    "causal": True, "workspace_bytes": wsb},
         "roofline": {"bound": "mfma", "achieved": tf, "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / FP8_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "frac": tf / FP8_MFMA_PEAK_TFLOPS, "traffic": measured_traffic("attention_prefill"),
                      "kernel": "mix_attn_prefill (all kernels of the call)", "kernel_ms": ms_step},
     }
     res["underflow_map"] = underflow_section(torch, q, kd.view(T, Hkv * d))
