@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MIX_ABI_VERSION 1
+#define MIX_ABI_VERSION 2
 
 typedef enum {
   MIX_OK = 0,
@@ -145,7 +145,7 @@ size_t mix_mx_gemm_workspace_bytes(mix_fmt_t a_fmt, mx_fmt_t b_fmt, int64_t M, i
  * dual-format bullet and Eq. (6)): a MiX element (1.m)_2 2^(Emax - dE) is stored as the E4M3
  * byte of (1.m)_2 2^(1 - dE) under the E8M0 block scale 2^(Emax - 1); an MXINT4 element
  * q 2^(X - 2) as the E4M3 byte of q/4 under its unchanged scale 2^X; MXFP4 codes are the E2M1
- * operand as stored.
+ * operand, copied step-major (each 128-wide K step's 64-byte row slices contiguous over the rows).
  * Images are opaque byte buffers of the sizes below (0 = no image for that shape: K must be a
  * positive multiple of 128), 256-byte aligned, owned by the caller. An image depends only on the
  * operand's codes and shape (not on the other operand).
@@ -165,8 +165,8 @@ mix_status_t mix_gemm_a_image(mix_fmt_t a_fmt, const uint8_t* a_codes, const voi
 mix_status_t mix_quantize_gemm(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols,
                                int64_t ldx, uint8_t* codes, void* shared, void* img, size_t img_bytes, void* stream);
 
-/* B image from MX codes ([N, K/2] codes, [N, K/32] E8M0 scales); g16 formats: MIX_E_UNSUPPORTED
- * (use mx_gemm_b_image_g16). */
+/* B image from MX codes ([N, K/2] codes, 16-byte aligned; [N, K/32] E8M0 scales); g16 formats:
+ * MIX_E_UNSUPPORTED (use mx_gemm_b_image_g16). */
 mix_status_t mx_gemm_b_image(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8_t* b_scales, int64_t N, int64_t K,
                              void* img, size_t img_bytes, void* stream);
 
@@ -186,10 +186,9 @@ mix_status_t mx_gemm_b_image_g16(mx_fmt_t b_fmt, const uint8_t* b_codes, const u
                                  int64_t K, void* img, size_t img_bytes, uint32_t* unfoldable, void* stream);
 
 /*
- * C = A . B^T from the two images (same results as mix_mx_gemm on the codes). For MX_FP4 the
- * E2M1 nibbles are read from b_codes ([N, K/2], 16-byte aligned) -- the B image holds only the
- * scales; for MX_INT4 and the g16 formats (E4M3 images) b_codes is ignored and may be NULL. c and
- * ldc as for mix_mx_gemm. For
+ * C = A . B^T from the two images (same results as mix_mx_gemm on the codes). The images hold
+ * every operand byte: b_codes is not read and may be NULL (kept for the signature). c and ldc as
+ * for mix_mx_gemm. For
  * M > 16 each operand image must stay below 2^31 bytes (MIX_E_UNSUPPORTED otherwise; mix_mx_gemm
  * then decodes inside the GEMM instead).
  */

@@ -253,7 +253,7 @@ def mix_mx_gemm_images(a_img, b_img, out_dtype=torch.float32, out=None):
         out = torch.empty((M, N), dtype=out_dtype, device=a_img.buf.device)
     _need_cuda(out)
     check(_lib_().mix_mx_gemm_images(MX_FMT[b_img.fmt], _p(a_img.buf), _p(b_img.buf),
-                                     _p(b_img.codes) if b_img.fmt == "fp4" else None, M, N, K, _p(out),
+                                     None, M, N, K, _p(out),
                                      DTYPE[out.dtype], out.stride(0), _stream()), "mix_mx_gemm_images")
     return out
 
@@ -279,7 +279,7 @@ def mix_mx_gemm_images_quantize(a_img, b_img, keep_c=False, image=True, out=None
     img = _image_buf(mix_gemm_a_image_bytes(M, N), dev, q_image, "mix_mx_gemm_images_quantize") if image else None
     _need_cuda(out, codes, shared)
     check(_lib_().mix_mx_gemm_images_quantize(MX_FMT[b_img.fmt], _p(a_img.buf), _p(b_img.buf),
-                                              _p(b_img.codes) if b_img.fmt == "fp4" else None, M, N, K, _p(out),
+                                              None, M, N, K, _p(out),
                                               out.stride(0) if out is not None else N, _p(codes), _p(shared),
                                               _p(img), img.numel() if img is not None else 0, _stream()),
           "mix_mx_gemm_images_quantize")

@@ -272,8 +272,8 @@ mix_status_t mx_gemm_b_image(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8
   if (N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
   if (N == 0) return MIX_OK;
   if (N > INT32_MAX || !image_k_ok(K)) return fail(MIX_E_SHAPE, "%s: K=%lld is not a positive multiple of 128", fn, (long long)K);
-  if (!b_scales || (b_fmt == MX_INT4 && !b_codes)) return fail(MIX_E_NULL, "%s: codes or scales is NULL", fn);
-  if (b_fmt == MX_INT4 && !aligned16(b_codes)) return fail(MIX_E_ALIGN, "%s: codes not 16-byte aligned", fn);
+  if (!b_scales || !b_codes) return fail(MIX_E_NULL, "%s: codes or scales is NULL", fn);
+  if (!aligned16(b_codes)) return fail(MIX_E_ALIGN, "%s: codes not 16-byte aligned", fn);
   if (mix_status_t st = check_image(fn, img, img_bytes, mix::f8_b_image_layout(b_fmt == MX_FP4, N, K).total)) return st;
   return hip_status(mix::launch_gemm_b_image(b_fmt == MX_FP4, b_codes, b_scales, N, K, img, (hipStream_t)stream), fn);
 }
@@ -311,12 +311,11 @@ mix_status_t mix_mx_gemm_images(mx_fmt_t b_fmt, const void* a_img, const void* b
     return fail(MIX_E_UNSUPPORTED, "%s: an operand image of %lld x %lld x %lld reaches 2^31 bytes", fn, (long long)M,
                 (long long)N, (long long)K);
   if (!c || !a_img || !b_img) return fail(MIX_E_NULL, "%s: c or an image is NULL", fn);
-  if (b_fmt == MX_FP4 && !b_codes) return fail(MIX_E_NULL, "%s: MXFP4 codes are NULL", fn);
+  (void)b_codes;   // the B image holds every operand byte
   if (((uintptr_t)a_img & 255u) || ((uintptr_t)b_img & 255u)) return fail(MIX_E_ALIGN, "%s: images must be 256-byte aligned", fn);
-  if (b_fmt == MX_FP4 && !aligned16(b_codes)) return fail(MIX_E_ALIGN, "%s: codes not 16-byte aligned", fn);
   if ((uintptr_t)c % dtype_size(c_dtype)) return fail(MIX_E_ALIGN, "%s: c misaligned", fn);
-  return hip_status(mix::launch_gemm_images(b_fmt == MX_FP4, c_dtype == MIX_BF16, a_img, b_img, b_codes, M, N, K, c,
-                                            ldc, (hipStream_t)stream),
+  return hip_status(mix::launch_gemm_images(b_fmt == MX_FP4, c_dtype == MIX_BF16, a_img, b_img, M, N, K, c, ldc,
+                                            (hipStream_t)stream),
                     fn);
 }
 
@@ -339,10 +338,9 @@ mix_status_t mix_mx_gemm_images_quantize(mx_fmt_t b_fmt, const void* a_img, cons
     return fail(MIX_E_UNSUPPORTED, "%s: an operand or output image of %lld x %lld x %lld reaches 2^31 bytes", fn,
                 (long long)M, (long long)N, (long long)K);
   if (!a_img || !b_img || !q_codes || !q_shared) return fail(MIX_E_NULL, "%s: an image or an output is NULL", fn);
-  if (b_fmt == MX_FP4 && !b_codes) return fail(MIX_E_NULL, "%s: MXFP4 codes are NULL", fn);
+  (void)b_codes;   // the B image holds every operand byte
   if (((uintptr_t)a_img & 255u) || ((uintptr_t)b_img & 255u) || ((uintptr_t)q_img & 255u))
     return fail(MIX_E_ALIGN, "%s: images must be 256-byte aligned", fn);
-  if (b_fmt == MX_FP4 && !aligned16(b_codes)) return fail(MIX_E_ALIGN, "%s: codes not 16-byte aligned", fn);
   if (((uintptr_t)q_codes & 3u) || ((uintptr_t)q_shared & 1u) || ((uintptr_t)c & 1u))
     return fail(MIX_E_ALIGN, "%s: q_codes must be 4-byte aligned, q_shared and c 2-byte aligned", fn);
   if (M <= 16 && (!aligned16(c) || (ldc * 2) % 16))
@@ -350,8 +348,8 @@ mix_status_t mix_mx_gemm_images_quantize(mx_fmt_t b_fmt, const void* a_img, cons
   if (q_img && q_img_bytes < mix::f8_a_image_layout(M, N).total)
     return fail(MIX_E_WORKSPACE, "%s: output image buffer %zu < %zu bytes", fn, q_img_bytes,
                 mix::f8_a_image_layout(M, N).total);
-  return hip_status(mix::launch_gemm_images_q(b_fmt == MX_FP4, a_img, b_img, b_codes, M, N, K, c, ldc, q_codes,
-                                              q_shared, q_img, (hipStream_t)stream),
+  return hip_status(mix::launch_gemm_images_q(b_fmt == MX_FP4, a_img, b_img, M, N, K, c, ldc, q_codes, q_shared,
+                                              q_img, (hipStream_t)stream),
                     fn);
 }
 

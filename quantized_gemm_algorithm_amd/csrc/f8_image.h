@@ -7,7 +7,9 @@
 //                                     four block scales in one dword (f8_a_scale_pos)
 // B image of an [N, K] MX operand:
 //   bs_p  [K/128][tiles_n][1024]      E8M0 block scales, permuted (f8_scale_pos), for the tiled product
-//   b8    [N, K] (MXINT4 only)        E4M3 bytes of q/4 (MXFP4 codes are used as stored)
+//   b8    MXFP4: [K/128][N][64]       the codes step-major: a K step's 64-byte slices of all rows are
+//                                     contiguous, so a tile's slice of a step is whole cache lines
+//         MXINT4 (and g16): [N, K]    E4M3 bytes of the element values (q/4, or the folded g16 values)
 //   bs_v  [ceil(N/16)][K/128][16][4]  the same scales per 16-row group, for the small-M product
 // tiles_m = ceil(M / 256), tiles_n = ceil(N / 256); every part starts on a 256-byte boundary.
 #pragma once
@@ -54,7 +56,7 @@ inline F8BImage f8_b_image_layout(int b_fp4, int64_t N, int64_t K) {
   F8BImage L{};
   L.bs_p = 0;
   L.b8 = f8_al256((size_t)(K / FK) * tn * 1024);
-  L.bs_v = L.b8 + (b_fp4 ? 0 : f8_al256((size_t)N * K));
+  L.bs_v = L.b8 + f8_al256(b_fp4 ? (size_t)N * K / 2 : (size_t)N * K);
   L.total = L.bs_v + f8_al256((size_t)((N + 15) / 16) * (K / FK) * 64);
   return L;
 }

@@ -173,10 +173,10 @@ __device__ __forceinline__ void f8_issue(const F8Args& g, uint32_t st, int tm, i
     const int tb = w * 16 + (ln >> 2);           // copy p reads row 64 p + tb (64-byte rows)
     const int cb = (ln & 3) ^ bswz(tb);
     const int lim = g.N - 1 - n0;
-    const uint8_t* base = g.b + (size_t)n0 * (g.K >> 1) + (k0 >> 1);
+    const uint8_t* base = g.b + ((size_t)ks * g.N + n0) * 64;   // step-major image: rows 64 bytes apart
 #pragma unroll
     for (int p = B0; p < B1; p++)
-      dma16s(base, (uint32_t)(min(64 * p + tb, lim) * (g.K >> 1) + 16 * cb),
+      dma16s(base, (uint32_t)(min(64 * p + tb, lim) * 64 + 16 * cb),
              st + F8Stage<B_FP4>::A_BYTES + (p * 256 + w * 64) * 16);
   } else {
     const int tb = w * 8 + (ln >> 3);
@@ -563,7 +563,7 @@ __global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
   const int r = lane & 15, gq = lane >> 4;
   const int n0 = blockIdx.x * R;
   const int rowA = min(r, g.M - 1);
-  const int64_t browg = B_FP4 ? (g.K >> 1) : g.K;   // bytes per B row in global memory
+  const int64_t browg = g.K;                        // bytes per E4M3 B row (FP4 codes are step-major)
   const int nkt = g.K / FK;
   v4f acc[G];
 #pragma unroll
@@ -618,7 +618,8 @@ __global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
         const int slot = lane & (CPS - 1);
         const int c = slot ^ (B_FP4 ? bswz(row) : aswz(row));
         const int grow = min(n0 + row, g.N - 1);
-        dma16(g.b + (int64_t)grow * browg + (int64_t)ks * SBY + 16 * c,
+        const int64_t boff = B_FP4 ? ((int64_t)ks * g.N + grow) * SBY : (int64_t)grow * browg + (int64_t)ks * SBY;
+        dma16(g.b + boff + 16 * c,
               __builtin_amdgcn_readfirstlane(lds_addr(wreg + (size_t)i * R * SBY + qr * 1024)));
       }
     };
@@ -783,6 +784,18 @@ hipError_t launch_gemm_a_image(int a_fmt, const uint8_t* a_codes, const void* a_
   return hipGetLastError();
 }
 
+// MXFP4 codes [N, K/2] -> the image's step-major copy [K/128][N][64]; one thread per 16 bytes
+__global__ void __launch_bounds__(256) k_b4_step_major(const uint8_t* __restrict__ codes, int64_t N, int64_t K,
+                                                        uint8_t* __restrict__ dst) {
+  const int64_t cpr = K >> 5;   // 16-byte chunks per row
+  const int64_t total = N * cpr;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = t / cpr, c = t - row * cpr;
+    const uint4 v = *(const uint4*)(codes + row * (K >> 1) + c * 16);
+    *(uint4*)(dst + ((c >> 2) * N + row) * 64 + (c & 3) * 16) = v;
+  }
+}
+
 hipError_t launch_gemm_b_image(int b_fp4, const uint8_t* b_codes, const uint8_t* b_scales, int64_t N, int64_t K,
                                void* img, hipStream_t s) {
   const F8BImage L = f8_b_image_layout(b_fp4, N, K);
@@ -791,8 +804,11 @@ hipError_t launch_gemm_b_image(int b_fp4, const uint8_t* b_codes, const uint8_t*
   hipLaunchKernelGGL(k_permute_b_scales, dim3(grid1d(N * (K >> 5))), dim3(256), 0, s, b_scales, N, K, tiles_n,
                      base + L.bs_p, base + L.bs_v);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || b_fp4) return e;
-  hipLaunchKernelGGL(k_expand_b_int4, dim3(grid1d(N * (K >> 3))), dim3(256), 0, s, b_codes, N, K, base + L.b8);
+  if (e != hipSuccess) return e;
+  if (b_fp4)
+    hipLaunchKernelGGL(k_b4_step_major, dim3(grid1d(N * (K >> 5))), dim3(256), 0, s, b_codes, N, K, base + L.b8);
+  else
+    hipLaunchKernelGGL(k_expand_b_int4, dim3(grid1d(N * (K >> 3))), dim3(256), 0, s, b_codes, N, K, base + L.b8);
   return hipGetLastError();
 }
 
@@ -841,14 +857,14 @@ static hipError_t launch_gemv_f8(int b_fp4, int c_bf16, const F8Args& f, hipStre
   return c_bf16 ? launch_gv_g<0, 1>(f, s) : launch_gv_g<0, 0>(f, s);
 }
 
-hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const void* b_img, const uint8_t* b_codes,
-                              int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, hipStream_t s) {
+hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const void* b_img, int64_t M, int64_t N,
+                              int64_t K, void* c, int64_t ldc, hipStream_t s) {
   const F8AImage LA = f8_a_image_layout(M, K);
   const F8BImage LB = f8_b_image_layout(b_fp4, N, K);
   F8Args a{};
   a.a8 = (const uint8_t*)a_img + LA.a8;
   a.as_p = (const uint8_t*)a_img + LA.as_p;
-  a.b = b_fp4 ? b_codes : (const uint8_t*)b_img + LB.b8;
+  a.b = (const uint8_t*)b_img + LB.b8;
   a.bs_p = (const uint8_t*)b_img + LB.bs_p;
   a.bs_v = (const uint8_t*)b_img + LB.bs_v;
   a.c = c; a.ldc = ldc; a.M = (int)M; a.N = (int)N; a.K = (int)K;
@@ -862,11 +878,10 @@ hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const vo
 // the bf16 rounding of C along N, and optionally that output's A image for a next product; C
 // itself (bf16) only if c is given. M > 16: in the tiled product's epilogue; M <= 16: the weight
 // stream writes C (required then) and the quantizer codes it.
-hipError_t launch_gemm_images_q(int b_fp4, const void* a_img, const void* b_img, const uint8_t* b_codes, int64_t M,
-                                int64_t N, int64_t K, void* c, int64_t ldc, uint8_t* q_codes, void* q_shared,
-                                void* q_img, hipStream_t s) {
+hipError_t launch_gemm_images_q(int b_fp4, const void* a_img, const void* b_img, int64_t M, int64_t N, int64_t K,
+                                void* c, int64_t ldc, uint8_t* q_codes, void* q_shared, void* q_img, hipStream_t s) {
   if (M <= 16) {
-    hipError_t e = launch_gemm_images(b_fp4, 1, a_img, b_img, b_codes, M, N, K, c, ldc, s);
+    hipError_t e = launch_gemm_images(b_fp4, 1, a_img, b_img, M, N, K, c, ldc, s);
     if (e != hipSuccess) return e;
     if (q_img) return launch_mix_quantize_img(1, c, 1, M, N, ldc, q_codes, q_shared, q_img, s);
     return launch_mix_quantize(1, c, 1, M, N, ldc, q_codes, q_shared, s);
@@ -876,7 +891,7 @@ hipError_t launch_gemm_images_q(int b_fp4, const void* a_img, const void* b_img,
   F8Args a{};
   a.a8 = (const uint8_t*)a_img + LA.a8;
   a.as_p = (const uint8_t*)a_img + LA.as_p;
-  a.b = b_fp4 ? b_codes : (const uint8_t*)b_img + LB.b8;
+  a.b = (const uint8_t*)b_img + LB.b8;
   a.bs_p = (const uint8_t*)b_img + LB.bs_p;
   a.bs_v = (const uint8_t*)b_img + LB.bs_v;
   a.c = c; a.ldc = ldc; a.M = (int)M; a.N = (int)N; a.K = (int)K;
@@ -899,7 +914,7 @@ hipError_t launch_gemm_f8(int a_fmt, int b_fp4, int c_bf16, const uint8_t* a_cod
   hipError_t e = launch_gemm_a_image(a_fmt, a_codes, a_shared, M, K, a_img, s);
   if (e != hipSuccess) return e;
   if ((e = launch_gemm_b_image(b_fp4, b_codes, b_scales, N, K, b_img, s)) != hipSuccess) return e;
-  return launch_gemm_images(b_fp4, c_bf16, a_img, b_img, b_codes, M, N, K, c, ldc, s);
+  return launch_gemm_images(b_fp4, c_bf16, a_img, b_img, M, N, K, c, ldc, s);
 }
 
 }  // namespace mix

@@ -69,13 +69,12 @@ hipError_t launch_gemm_b_image(int b_fp4, const uint8_t* b_codes, const uint8_t*
 // exactly are counted into *unfoldable (device, zeroed first)
 hipError_t launch_gemm_b_image_g16(int fp4, const uint8_t* b_codes, const uint8_t* b_scales16, int64_t N, int64_t K,
                                    void* img, uint32_t* unfoldable, hipStream_t s);
-hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const void* b_img, const uint8_t* b_codes,
-                              int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, hipStream_t s);
+hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const void* b_img, int64_t M, int64_t N,
+                              int64_t K, void* c, int64_t ldc, hipStream_t s);
 hipError_t launch_mix_quantize_img(int fmt, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                                    uint8_t* codes, void* shared, void* img, hipStream_t s);
-hipError_t launch_gemm_images_q(int b_fp4, const void* a_img, const void* b_img, const uint8_t* b_codes, int64_t M,
-                                int64_t N, int64_t K, void* c, int64_t ldc, uint8_t* q_codes, void* q_shared,
-                                void* q_img, hipStream_t s);
+hipError_t launch_gemm_images_q(int b_fp4, const void* a_img, const void* b_img, int64_t M, int64_t N, int64_t K,
+                                void* c, int64_t ldc, uint8_t* q_codes, void* q_shared, void* q_img, hipStream_t s);
 
 // attention (arguments validated by the C-ABI layer)
 size_t attn_prefill_ws_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t d);

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mix_abi_version() == 1
+    assert lib.mix_abi_version() == 2
     for s in range(8):
         assert lib.mix_status_str(s)
     assert lib.mix_status_str(99) == b"unknown status"
@@ -89,14 +89,15 @@ def test_gemm_validation(lib):
         assert fn(1, None, None, 1, None, None, 4, 0, 32, None, 0, 0, None) == MIX_OK
         assert fn(1, FAKE, FAKE, 1, FAKE, FAKE, 2**31, 4, 32, FAKE, 0, 4, None) == MIX_E_SHAPE
     # fast-path workspace size: zero when the shape does not take it
-    # E4M3 A + per-(K step, 256-row tile) 1 KB scale blocks for A and B (+ E4M3 B for MXINT4)
+    # E4M3 A + per-(K step, 256-row tile) 1 KB scale blocks for A and B + the B operand (MXFP4 codes
+    # step-major, E4M3 B for MXINT4) + the B scales per 16-row group
     assert lib.mix_mx_gemm_workspace_bytes(1, 1, 4096, 18944, 3584) == (4096 * 3584 + 28 * 16 * 1024 + 28 * 74 * 1024
-                                                                       + 1184 * 28 * 64)
+                                                                       + 18944 * 1792 + 1184 * 28 * 64)
     assert lib.mix_mx_gemm_workspace_bytes(1, 0, 256, 256, 128) == 256 * 128 + 1024 + 1024 + 256 * 128 + 16 * 64
     assert lib.mix_mx_gemm_workspace_bytes(1, 1, 256, 256, 96) == 0
     # M <= 16 streams the weights through the same images
     assert lib.mix_mx_gemm_workspace_bytes(1, 1, 16, 18944, 3584) == (16 * 3584 + 28 * 1024 + 28 * 74 * 1024
-                                                                     + 1184 * 28 * 64)
+                                                                     + 18944 * 1792 + 1184 * 28 * 64)
     assert lib.mix_mx_gemm_workspace_bytes(1, 1, 32, 18944, 3584) == 0
     # a misaligned workspace is rejected when the fast path is taken
     assert lib.mix_mx_gemm(1, FAKE, FAKE, 1, FAKE, FAKE, 256, 256, 128, FAKE, 0, 256, MISALIGNED, 1 << 20,
@@ -119,9 +120,11 @@ def test_image_sizes(lib):
     assert lib.mix_gemm_a_image_bytes(1, 128) == 256 + 1024
     assert lib.mix_gemm_a_image_bytes(4, 96) == 0
     assert lib.mix_gemm_a_image_bytes(0, 128) == 0
-    # B image: permuted scales (+ E4M3 bytes of q/4 for MXINT4) + the scales per 16-row group
-    # [ceil(N/16)][K/128][64] for the small-M product (each part 256-byte rounded)
-    assert lib.mx_gemm_b_image_bytes(1, 18944, 3584) == 28 * 74 * 1024 + 1184 * 28 * 64
+    # B image: permuted scales + the operand (MXFP4: the codes step-major, N K / 2 bytes; MXINT4: E4M3
+    # bytes of q/4, N K) + the scales per 16-row group [ceil(N/16)][K/128][64] for the small-M product
+    # (each part 256-byte rounded)
+    assert lib.mx_gemm_b_image_bytes(1, 18944, 3584) == 28 * 74 * 1024 + 18944 * 1792 + 1184 * 28 * 64
+    assert lib.mx_gemm_b_image_bytes(1, 300, 256) == 2 * 2 * 1024 + 300 * 128 + 2560
     assert lib.mx_gemm_b_image_bytes(0, 300, 256) == 2 * 2 * 1024 + 300 * 256 + 2560
     assert lib.mx_gemm_b_image_bytes(4, 300, 256) == 0
     assert lib.mx_gemm_b_image_bytes(1, 300, 0) == 0
@@ -141,10 +144,12 @@ def test_image_validation(lib):
     assert lib.mix_quantize_gemm(1, FAKE, 1, 4, 128, 128, None, None, FAKE, 10, None) == MIX_E_WORKSPACE
     assert lib.mix_quantize_gemm(1, None, 1, 0, 128, 128, None, None, None, 0, None) == MIX_OK
     assert lib.mx_gemm_b_image(1, FAKE, None, 4, 128, FAKE, 1 << 20, None) == MIX_E_NULL
+    assert lib.mx_gemm_b_image(1, None, FAKE, 4, 128, FAKE, 1 << 20, None) == MIX_E_NULL
+    assert lib.mx_gemm_b_image(1, P(0x10008), FAKE, 4, 128, FAKE, 1 << 20, None) == MIX_E_ALIGN
     assert lib.mx_gemm_b_image(0, None, FAKE, 4, 128, FAKE, 1 << 20, None) == MIX_E_NULL
     assert lib.mx_gemm_b_image(0, FAKE, FAKE, 4, 128, A16, 1 << 20, None) == MIX_E_ALIGN
-    # GEMM from images: MXFP4 needs the codes; K a multiple of 128; images 256-byte aligned
-    assert lib.mix_mx_gemm_images(1, FAKE, FAKE, None, 4, 4, 128, FAKE, 0, 4, None) == MIX_E_NULL
+    # GEMM from images: K a multiple of 128; images 256-byte aligned (the codes are not needed)
+    assert lib.mix_mx_gemm_images(1, None, FAKE, None, 4, 4, 128, FAKE, 0, 4, None) == MIX_E_NULL
     assert lib.mix_mx_gemm_images(0, FAKE, FAKE, None, 4, 4, 100, FAKE, 0, 4, None) == MIX_E_SHAPE
     assert lib.mix_mx_gemm_images(0, A16, FAKE, None, 4, 4, 128, FAKE, 0, 4, None) == MIX_E_ALIGN
     assert lib.mix_mx_gemm_images(0, FAKE, FAKE, None, 4, 4, 128, FAKE, 0, 3, None) == MIX_E_SHAPE
@@ -165,7 +170,7 @@ def test_image_product_with_quantized_output_validation(lib):
     assert f(1, FAKE, FAKE, FAKE, 64, 160, 128, None, 0, FAKE, FAKE, FAKE, BIG, None) == MIX_E_SHAPE  # image: N % 128
     assert f(1, FAKE, FAKE, FAKE, 8, 256, 128, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_NULL     # M <= 16 needs c
     assert f(1, FAKE, FAKE, FAKE, 64, 256, 128, None, 0, None, FAKE, None, 0, None) == MIX_E_NULL
-    assert f(1, FAKE, FAKE, None, 64, 256, 128, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_NULL    # FP4 codes
+    assert f(1, FAKE, None, None, 64, 256, 128, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_NULL    # B image
     assert f(1, A16, FAKE, FAKE, 64, 256, 128, None, 0, FAKE, FAKE, None, 0, None) == MIX_E_ALIGN
     assert f(1, FAKE, FAKE, FAKE, 64, 256, 128, None, 0, FAKE, FAKE, A16, BIG, None) == MIX_E_ALIGN
     assert f(1, FAKE, FAKE, FAKE, 64, 256, 128, None, 0, P(0x10002), FAKE, None, 0, None) == MIX_E_ALIGN
