@@ -166,9 +166,9 @@ class AImage:
 
 
 class BImage:
-    """Decode-once GEMM operand of an [N, K] MX matrix; MXFP4 images keep a reference to the codes.
-    g16 images carry ``unfoldable``: a device uint32 counting the 32-blocks that could not be folded
-    into one scale exactly (0: products from the image are exact)."""
+    """Decode-once GEMM operand of an [N, K] MX matrix (it holds every operand byte; ``codes`` is the
+    tensor it was built from). g16 images carry ``unfoldable``: a device uint32 counting the 32-blocks
+    that could not be folded into one scale exactly (0: products from the image are exact)."""
 
     def __init__(self, buf, fmt, N, K, codes, unfoldable=None):
         self.buf, self.fmt, self.N, self.K, self.codes = buf, fmt, N, K, codes
