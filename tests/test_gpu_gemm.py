@@ -269,3 +269,35 @@ def test_gemm_eq6_workload3_sampled():
     out = q.mix_mx_gemm_eq6(ac, as_, "4.25b", bc, bs, "int4", out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     _sampled_check(host(out), host(ac), host(as_), "4.25b", host(bc), host(bs), "int4", 2048, 4, "workload 3 eq6")
+
+
+@pytest.mark.parametrize("M,N,K,b_fmt", [(65536, 512, 4096, "fp4"), (512, 1024, 65536, "int4"), (8, 2048, 65536, "fp4")])
+def test_gemm_images_large_extents_sampled(M, N, K, b_fmt):
+    # extents far from the workloads' (a 268 MB activation image; 512 K steps per tile; the weight
+    # stream over K = 65536), seeded on the device: the sampled rows' codes are checked against the
+    # oracle's coding of the same values, then sampled outputs against the oracle's dot products
+    q = _lib()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(M + N + K)
+    x = (torch.randn((M, K), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+    w = (torch.randn((N, K), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+    ac, as_, ai = q.mix_quantize_gemm(x, "4.5b")
+    bc, bs = q.mx_quantize(w, b_fmt)
+    bi = q.mx_gemm_b_image(bc, bs, b_fmt)
+    out = q.mix_mx_gemm_images(ai, bi, out_dtype=torch.float32 if b_fmt == "int4" else torch.bfloat16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(K)
+    rows = np.unique(rng.integers(0, M, 6))
+    xs = x[torch.as_tensor(rows, device="cuda")].view(torch.int16).cpu().numpy().view(np.uint16)
+    wc, ws = o_mix_q(xs, "4.5b", "bf16")
+    assert_codes_equal(host(ac)[rows], wc, "sampled activation codes")
+    assert_codes_equal(host(as_)[rows], ws, "sampled shared fields")
+    cols = np.unique(rng.integers(0, N, 6))
+    ad = o_mix_deq(wc, ws, "4.5b")
+    bd = o_mx_deq(host(bc)[cols], host(bs)[cols], b_fmt)
+    ref, bound = gemm_ref(ad, bd), gemm_abs_bound(ad, bd)
+    got = host(out)[np.ix_(rows, cols)]
+    if b_fmt == "int4":
+        assert_gemm_close(got, ref, bound, f"{M}x{N}x{K} {b_fmt}")
+    else:
+        assert_bf16_matches(got, ref, bound, f"{M}x{N}x{K} {b_fmt}")
