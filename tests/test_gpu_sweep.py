@@ -82,3 +82,23 @@ def test_sweep_attention(seed):
         L = [int(v) for v in rng.integers(1, 1500, B)]
         r = ta._decode_case(B=B, Hq=Hq, Hkv=Hkv, L_each=L, seed=int(rng.integers(0, 1000)))
         ta._check_decode(r, Hq, Hkv)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_underflow_map(seed):
+    import quantized_gemm_algorithm_amd as q
+    from oracle.underflow import underflow_map as o_map
+    rng = np.random.default_rng(3000 + seed)
+    rows = int(rng.integers(1, 900))
+    cols = 32 * int(rng.integers(1, 40))
+    spread = int(rng.integers(0, 40))
+    x = (rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-spread, spread + 1, (rows, cols)))).astype(np.float32)
+    if rng.random() < 0.5:
+        x[rng.random((rows, cols)) < 0.1] = 0.0
+    mu = rng.standard_normal(cols).astype(np.float32) if seed % 2 else None
+    counts, amax = q.mix_underflow_map(dev_f32(x), mu=dev_f32(mu) if mu is not None else None)
+    torch.cuda.synchronize()
+    want = o_map(x, "f32", mu)
+    assert np.array_equal(host(counts), want), f"{rows}x{cols} spread {spread}"
+    xs = (x - mu).astype(np.float32) if mu is not None else x
+    assert float(host(amax)[0]) == float(np.abs(xs).max())
