@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import test_gpu_attention as ta
-from helpers import assert_bf16_matches, assert_codes_equal, assert_gemm_close, dev_f32, host
+from helpers import assert_bf16_matches, assert_codes_equal, assert_gemm_close, dev_bf16, dev_f32, host
 from oracle.gemm import gemm_abs_bound, gemm_ref
 from oracle.mix import mix_dequantize as o_mix_deq, mix_quantize as o_mix_q
 from oracle.mx import mx_dequantize as o_mx_deq, mx_quantize as o_mx_q
@@ -38,11 +38,19 @@ def test_sweep_gemm(seed):
     base = b_fmt[:-3] if b_fmt.endswith("g16") else b_fmt
     blk = 16 if b_fmt.endswith("g16") else 32
     what = f"{M}x{N}x{K} {a_fmt} x {b_fmt}"
-    ac, as_ = q.mix_quantize(dev_f32(x), a_fmt)
-    bc, bs = q.mx_quantize(dev_f32(w), b_fmt)
+    if seed % 2:   # bf16 inputs (the quantizers' other instantiation)
+        xb, wb = synth.f32_to_bf16_bits(x), synth.f32_to_bf16_bits(w)
+        ac, as_ = q.mix_quantize(dev_bf16(xb), a_fmt)
+        bc, bs = q.mx_quantize(dev_bf16(wb), b_fmt)
+        wac, was = o_mix_q(xb, a_fmt, "bf16")
+        wbc, wbs = o_mx_q(wb, base, "bf16", block=blk)
+        what += " bf16 in"
+    else:
+        ac, as_ = q.mix_quantize(dev_f32(x), a_fmt)
+        bc, bs = q.mx_quantize(dev_f32(w), b_fmt)
+        wac, was = o_mix_q(x, a_fmt, "f32")
+        wbc, wbs = o_mx_q(w, base, "f32", block=blk)
     torch.cuda.synchronize()
-    wac, was = o_mix_q(x, a_fmt, "f32")
-    wbc, wbs = o_mx_q(w, base, "f32", block=blk)
     assert_codes_equal(host(ac), wac, what + " A codes")
     assert_codes_equal(host(as_), was, what + " A shared")
     assert_codes_equal(host(bc), wbc, what + " B codes")
