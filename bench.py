@@ -314,6 +314,7 @@ def bench_linear(torch, q, args, which):
                       "GB/s": q_bytes / (q_stream_ms * 1e-3) / 1e9,
                       "frac_hbm": q_bytes / (q_stream_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": q_bytes,
                       "timing": f"{qrep} back-to-back launches between two HIP events",
+                      "traffic": measured_traffic(which + "_quantizer"),
                       "in_step_ms": q_ms, "rotating_buffers": nrot},
         "weight_quantizer": {"kernel": "k_mx_quantize", "ms": wq_ms, "GB/s": wq_bytes / (wq_ms * 1e-3) / 1e9,
                              "frac_hbm": wq_bytes / (wq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": wq_bytes},
