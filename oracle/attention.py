@@ -22,7 +22,12 @@ unquantised p), D17 (partial V block at decode).
 Pins (tests/test_oracle_attention.py): the K-mean against a brute-force Fraction
 mean; smoothing invariance of the softmax on unquantised inputs; the staged
 pipeline against a hand-built single-head example; decode with all keys present
-equals the prefill's last row with the same mean.
+equals the prefill's last row with the same mean. The composition: query head h
+reads KV head h // (Hq / Hkv) (S against hand-indexed products with two different
+key sets); V is blocked along tokens (a one-token spike moves only its own
+block's scale in every channel, and a closed-form output where the token
+blocking zeroes small values); the softmax scale is 1/sqrt(d) (d = 64 gives
+z = S / 8 exactly, checked against exp of the hand-scaled logits).
 """
 import math
 

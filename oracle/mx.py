@@ -13,7 +13,7 @@ What it follows:
 * P1, method overview, last bullet: K-smoothing subtracts the per-channel mean of
   K before coding (the optional ``mu`` operand).
 
-* P1, 主要实验设置 (experimental setup), the format bullet: the 4.5-bit tier holds
+* P1, 实验如何设计 (experiment design), the format bullet: the 4.5-bit tier holds
   "g16" variants of the MX weights, one shared exponent per 16 elements (4 bits per
   element plus 8 per 16 = 4.5 bits); MiX-INT4g16 pairs MiX-4.5b activations with
   MXINT4g16 weights (``block=16`` here; the element rules do not change).

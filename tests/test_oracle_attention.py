@@ -112,3 +112,101 @@ def test_ragged_prefill_pads_keys_with_zero():
     assert r["p"].shape == (2, 40, 64)
     assert np.all(r["p"][:, :, 40:] == 0)
     assert np.all(r["p_codes"][:, :, 20:] == 0x77)
+
+
+# ---------------------------------------------------------------- composition pins
+# The three tests below pin how the attention oracle composes its parts (P1, 方法概览 / method
+# overview, last bullet: the attention products over smoothed K; the operand mapping D14): which KV
+# head a query head reads, the axis V is blocked along, and the softmax scale. Each would fail on
+# the plausible mistake it names.
+
+def _two_kv_heads(T, d, seed):
+    rng = np.random.default_rng(seed)
+    q1 = rng.standard_normal((T, 1, d)).astype(np.float32)
+    q = np.repeat(q1, 4, axis=1)                       # every query head the same
+    k = np.empty((T, 2, d), np.float32)
+    k[:, 0] = rng.standard_normal((T, d))
+    k[:, 1] = -3.0 * rng.standard_normal((T, d)) + 1.0  # a different key set on KV head 1
+    v = rng.standard_normal((T, 2, d)).astype(np.float32)
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+def test_gqa_query_head_reads_kv_head_h_div_group():
+    # Hq = 4 over Hkv = 2: heads 0, 1 read KV head 0 and heads 2, 3 read KV head 1 (h // 2). With
+    # h % Hkv, head 1 would read KV head 1 and S[1] would differ from S[0].
+    T, d = 64, 64
+    q, k, v = _two_kv_heads(T, d, 41)
+    r = attn_prefill_ref(q, k, v, "bf16", causal=True)
+    S = r["S"]
+    assert np.array_equal(S[0], S[1]) and np.array_equal(S[2], S[3])
+    assert not np.array_equal(S[0], S[2])
+    # hand-indexed: S[h] = Qd_h Kd_{h // 2}^T on the lower triangle, Qd / Kd decoded by the
+    # separately pinned decoders from the oracle's own codes
+    from oracle.mix import mix_dequantize
+    for h in range(4):
+        qd = mix_dequantize(r["q_codes"][:, h], r["q_shared"][:, h], "4.5b")
+        kd = mx_dequantize(r["k_codes"][:, h // 2], r["k_scales"][:, h // 2], "fp4")
+        want = np.tril(qd @ kd.T)
+        assert np.array_equal(S[h][:, :T], want)
+    # decode takes the same mapping
+    mu = r["mu"]
+    dec = attn_decode_ref(q[T - 1][None], k[None], v[None], mu[None], np.array([T]))
+    for h in range(4):
+        assert np.array_equal(dec["S"][0][h][:T], S[h][T - 1, :T])
+
+
+def test_v_is_blocked_along_tokens():
+    # A spike at token t changes, in every channel, the E8M0 scale of block t // 32 only: V^ is MXFP4
+    # along tokens (D14). Blocking along the head dimension would change the scales of token t's
+    # row instead.
+    T, H, d, t = 96, 1, 64, 45
+    rng = np.random.default_rng(42)
+    base = (rng.standard_normal((T, H, d)) * 0.1).astype(np.float32)
+    spiked = base.copy()
+    spiked[t] = 100.0
+    c0, s0 = code_v(f32_to_bf16_bits(base), "bf16")
+    c1, s1 = code_v(f32_to_bf16_bits(spiked), "bf16")
+    assert s0.shape == (H, d, T // 32)
+    changed = s0 != s1
+    assert np.all(changed[:, :, t // 32])
+    assert not changed[:, :, [j for j in range(T // 32) if j != t // 32]].any()
+    byte_changed = (c0 != c1).any(axis=(0, 1))
+    assert not byte_changed[: 16 * (t // 32)].any() and not byte_changed[16 * (t // 32 + 1):].any()
+
+
+def test_v_token_blocks_in_output_closed_form():
+    # q = 0 gives equal logits, so O[i] = mean over tokens 0..i of V^. Every channel holds 6 at token
+    # 0 and 0.1 elsewhere. Along tokens the first block's scale is 2^1 (X = ceil(log2 6) - 2), so
+    # 0.1 / 2 = 0.05 codes to zero and O[i] = 6 / (i + 1) for i < 32. (Blocked along the head
+    # dimension the 0.1 tokens would code to 0.09375 and O[i] would be larger.)
+    T, d = 32, 32
+    q = np.zeros((T, 1, d), np.uint16)
+    k = f32_to_bf16_bits(np.random.default_rng(43).standard_normal((T, 1, d)).astype(np.float32))
+    vf = np.full((T, 1, d), 0.1, np.float32)
+    vf[0] = 6.0
+    r = attn_prefill_ref(q, k, f32_to_bf16_bits(vf), "bf16", causal=True)
+    for i in (0, 1, 5, 31):
+        assert np.all(r["o"][0, i] == 6.0 / (i + 1))
+
+
+def test_softmax_scale_is_inverse_sqrt_d():
+    # d = 64: z = S 2^-3 exactly (1/sqrt(64) = 0.125), so p = exp(fp32(z - m)) with z = S / 8. With a
+    # 1/d scale (S / 64) the weights would differ.
+    assert softmax_scale(64) == np.float32(0.125)
+    assert softmax_scale(128) == np.float32(0.08838834764831845)
+    assert softmax_scale(32) == np.float32(0.17677669529663687)
+    s = np.array([[8.0, 0.0, -8.0, 16.0, 4.0, -24.0, 12.0, 2.0] * 4], np.float32)
+    p, l, m = softmax_rows(s, np.array([32]), 64)
+    z = s[0].astype(np.float64) / 8.0
+    assert m[0] == np.float32(2.0)
+    want = np.exp(z - 2.0).astype(np.float32)
+    assert np.array_equal(p[0], want)
+    # the same through the whole prefill: p of every row is exp(fp32(S / 8 - max)) of its own S
+    T, d = 64, 64
+    q, k, v = _two_kv_heads(T, d, 44)
+    r = attn_prefill_ref(q[:, :1], k[:, :1], v[:, :1], "bf16", causal=True)
+    S = r["S"][0].astype(np.float32)
+    for i in (0, 7, 40, 63):
+        zf = (S[i, : i + 1] / np.float32(8.0)).astype(np.float32)
+        diff = (zf - zf.max()).astype(np.float32)
+        assert np.array_equal(r["p"][0, i, : i + 1], np.exp(diff.astype(np.float64)).astype(np.float32))
