@@ -90,7 +90,7 @@ mix_status_t mix_quantize(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, int64
  *   E2M1 grid, sign of zero kept. MX_INT4: X = clamp(floor(log2 max|x|), -125, 127);
  *   q = clamp(RNE(x 2^(2-X)), -7, 7).
  * If mu != NULL the operand is fp32(x - mu[col]) (K-smoothing, P1 method overview last bullet).
- * MX_INT4_G16 / MX_FP4_G16 (P1 experimental setup, the format bullet: the 4.5-bit g16 weights)
+ * MX_INT4_G16 / MX_FP4_G16 (P1 实验如何设计 (experiment design), the format bullet: the 4.5-bit g16 weights)
  * apply the same rules to blocks of 16 elements.
  *   x       [rows, cols] fp32 or bf16, row pitch ldx
  *   mu      NULL or [cols] fp32
@@ -171,7 +171,7 @@ mix_status_t mx_gemm_b_image(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8
                              void* img, size_t img_bytes, void* stream);
 
 /*
- * B image of g16 weights (MX_INT4_G16 / MX_FP4_G16; P1 experimental setup, the 4.5-bit g16
+ * B image of g16 weights (MX_INT4_G16 / MX_FP4_G16; P1 实验如何设计 (experiment design), the 4.5-bit g16
  * variants; MiX-INT4g16 = MiX-4.5b activations x MXINT4g16 weights). The matrix core takes one
  * scale per 32 K elements, so each 32-block's two 16-element exponents are folded into E4M3
  * element bytes over one shared scale (MXINT4g16: the smaller exponent; MXFP4g16: the larger),

@@ -57,6 +57,22 @@ def _matrix(x, name):
     return x.shape[0], x.shape[1], x.stride(0)
 
 
+def _out_matrix(out, M, N, what, dtypes=(torch.float32, torch.bfloat16)):
+    """A caller-supplied output must hold [M, N] with unit column stride (the C-ABI takes only its
+    pointer and row pitch, so a smaller buffer would be written past its end)."""
+    _need_cuda(out)
+    if out.dtype not in dtypes:
+        raise MixError(f"{what}: out must be one of {dtypes}")
+    if out.dim() != 2 or tuple(out.shape) != (M, N) or out.stride(1) != 1 or out.stride(0) < N:
+        raise MixError(f"{what}: out must be a [{M}, {N}] tensor with unit column stride")
+    return out
+
+
+def _dense(t, shape, dtype, what):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise MixError(f"{what} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
 def abi_version():
     return _lib_().mix_abi_version()
 
@@ -144,6 +160,7 @@ def mix_mx_gemm(a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtype=to
     M, N, K = _gemm_shapes(a_codes, b_codes)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    _out_matrix(out, M, N, "mix_mx_gemm")
     ws = None
     if isinstance(workspace, str):
         nb = mix_mx_gemm_workspace_bytes(a_fmt, b_fmt, M, N, K)
@@ -228,9 +245,14 @@ def mix_quantize_gemm(x, fmt="4.5b", codes=None, shared=None, image=None, write_
     return codes, shared, AImage(buf, rows, cols)
 
 
-def mx_gemm_b_image(codes, scales, fmt="fp4", out=None):
+def mx_gemm_b_image(codes, scales, fmt="fp4", out=None, allow_inexact=False):
     """B image of MX codes [N, K/2] + E8M0 scales [N, K/32] ([N, K/16] for the g16 formats; built
-    once per weight)."""
+    once per weight).
+
+    g16 formats: the call waits for the image and reads its count of 32-blocks whose halves could
+    not share one scale exactly; if there are any it raises MixError (their products would not be
+    exact; ``mix_mx_gemm_eq6`` is exact for every input) unless ``allow_inexact`` is set, in which
+    case the image is returned with the count in ``BImage.unfoldable``."""
     _need_cuda(codes, scales)
     N, K = codes.shape[0], codes.shape[1] * 2
     buf = _image_buf(mx_gemm_b_image_bytes(fmt, N, K), codes.device, out, "mx_gemm_b_image")
@@ -238,6 +260,11 @@ def mx_gemm_b_image(codes, scales, fmt="fp4", out=None):
         unf = torch.empty((1,), dtype=torch.int32, device=codes.device)
         check(_lib_().mx_gemm_b_image_g16(MX_FMT[fmt], _p(codes), _p(scales), N, K, _p(buf), buf.numel(), _p(unf),
                                           _stream()), "mx_gemm_b_image_g16")
+        n_unf = int(unf.item())   # synchronises: an image is built once per weight, off the product path
+        if n_unf and not allow_inexact:
+            raise MixError(f"mx_gemm_b_image: {n_unf} {fmt} block(s) have halves whose exponents differ by more "
+                           "than the E4M3 fold holds exactly; their image products would not be exact "
+                           "(use mix_mx_gemm_eq6, or pass allow_inexact=True)")
         return BImage(buf, fmt, N, K, codes, unf)
     check(_lib_().mx_gemm_b_image(MX_FMT[fmt], _p(codes), _p(scales), N, K, _p(buf), buf.numel(), _stream()),
           "mx_gemm_b_image")
@@ -251,7 +278,7 @@ def mix_mx_gemm_images(a_img, b_img, out_dtype=torch.float32, out=None):
     M, N, K = a_img.M, b_img.N, a_img.K
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_img.buf.device)
-    _need_cuda(out)
+    _out_matrix(out, M, N, "mix_mx_gemm_images")
     check(_lib_().mix_mx_gemm_images(MX_FMT[b_img.fmt], _p(a_img.buf), _p(b_img.buf),
                                      None, M, N, K, _p(out),
                                      DTYPE[out.dtype], out.stride(0), _stream()), "mix_mx_gemm_images")
@@ -278,6 +305,10 @@ def mix_mx_gemm_images_quantize(a_img, b_img, keep_c=False, image=True, out=None
         q_image = q_image.buf
     img = _image_buf(mix_gemm_a_image_bytes(M, N), dev, q_image, "mix_mx_gemm_images_quantize") if image else None
     _need_cuda(out, codes, shared)
+    if out is not None:
+        _out_matrix(out, M, N, "mix_mx_gemm_images_quantize", (torch.bfloat16,))
+    _dense(codes, (M, N // 2), torch.uint8, "codes")
+    _dense(shared, (M, N // 32), torch.int16, "shared")
     check(_lib_().mix_mx_gemm_images_quantize(MX_FMT[b_img.fmt], _p(a_img.buf), _p(b_img.buf),
                                               None, M, N, K, _p(out),
                                               out.stride(0) if out is not None else N, _p(codes), _p(shared),
@@ -292,6 +323,7 @@ def mix_mx_gemm_eq6(a_codes, a_shared, a_fmt, b_codes, b_scales, b_fmt, out_dtyp
     M, N, K = _gemm_shapes(a_codes, b_codes)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    _out_matrix(out, M, N, "mix_mx_gemm_eq6")
     check(_lib_().mix_mx_gemm_eq6(MIX_FMT[a_fmt], _p(a_codes), _p(a_shared), MX_FMT[b_fmt], _p(b_codes),
                                   _p(b_scales), M, N, K, _p(out), DTYPE[out.dtype], out.stride(0), _stream()),
           "mix_mx_gemm_eq6")
@@ -358,6 +390,8 @@ def mix_attn_prefill(q, k, v, causal=True, debug=False, workspace=None):
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise MixError("q, k, v must be contiguous bfloat16")
+    if k.dim() != 3 or tuple(k.shape) != (T, Hkv, d) or tuple(v.shape) != (T, Hkv, d):
+        raise MixError("k and v must be [T, Hkv, d] with q's T and d")
     lib = _lib_()
     wsb = lib.mix_attn_prefill_workspace_bytes(T, Hq, Hkv, d)
     if workspace is None or workspace.numel() < wsb:
@@ -416,7 +450,17 @@ def mix_attn_decode(q, k_new, v_new, cache, pos, max_pos, mu, debug=False, works
     """One decode step. q [B, Hq, d], k_new/v_new [B, Hkv, d] bf16; pos int32 [B] (device);
     mu fp32 [B, Hkv, d]. Returns (o bf16 [B, Hq, d], dbg dict or None)."""
     _need_cuda(q, k_new, v_new, pos, mu)
+    if q.dim() != 3:
+        raise MixError("q must be [B, Hq, d]")
     B, Hq, d = q.shape
+    if B != cache.B or d != cache.d:
+        raise MixError(f"q is [{B}, {Hq}, {d}] but the cache holds B = {cache.B}, d = {cache.d}")
+    _dense(q, (B, Hq, d), torch.bfloat16, "q")
+    _dense(k_new, (B, cache.Hkv, d), torch.bfloat16, "k_new")
+    _dense(v_new, (B, cache.Hkv, d), torch.bfloat16, "v_new")
+    _dense(pos, (B,), torch.int32, "pos")
+    if mu.dtype != torch.float32 or mu.numel() != B * cache.Hkv * d or not mu.is_contiguous():
+        raise MixError(f"mu must be a contiguous float32 tensor of {B} x {cache.Hkv} x {d} values")
     lib = _lib_()
     wsb = lib.mix_attn_decode_workspace_bytes(B, Hq, cache.Hkv, d, max_pos)
     if workspace is None or workspace.numel() < wsb:

@@ -3,19 +3,22 @@
 // "P1" below is the pchao.org digest of the paper, titled
 // "MiX：面向端到端低比特视觉语言模型加速的微反缩放"; citations name its sections and figures.
 //
-// P1 (主要实验设置 / experimental setup, the format bullet) lists the 4.5-bit "g16" weight
+// P1 (实验如何设计 / experiment design, the format bullet) lists the 4.5-bit "g16" weight
 // variants; MiX-INT4g16 pairs MiX-4.5b activations with MXINT4g16 weights. The block-scaled MFMA
 // takes one E8M0 scale per 32 K elements, so the two 16-element halves of a 32-block share one
 // scale 2^b here and each half's own exponent X_h moves into its elements: an element v 2^X_h is
-// stored as the E4M3 byte of v 2^(X_h - b). MXINT4g16 uses b = the smaller exponent (values
-// (q/4) 2^d, d = X_h - b in [0, 8], at most 1.75 * 2^8 = 448, the largest E4M3); MXFP4g16 uses
-// b = the larger one (E2M1 values times 2^-d, the smallest, 0.5 * 2^-8, still a multiple of the
-// E4M3 subnormal step 2^-9). Either is exact when the halves' exponents differ by at most 8; a
-// block beyond that (a half more than 256 times smaller than the other, never seen in Gaussian
-// weights) cannot be folded exactly: its unrepresentable elements are stored as zero and the
-// block is counted, so the caller knows whether this image gives the exact product (the Eq. (6)
-// path is exact for every input). The image layout is the MXINT4 one (f8_image.h): permuted
-// per-32 scales, E4M3 bytes, scales per 16-row group.
+// stored as the E4M3 byte of v 2^(X_h - b). An MXINT4 element q 2^(X_h - 2) (|q| <= 7, three
+// significant bits) is the E4M3 value |q| 2^(d - 2) with d = X_h - b, representable for d - 2 in
+// [-9, 6] (down to the subnormal step 2^-9, up to 7 * 2^6 = 448, the largest E4M3); an MXFP4
+// element (E2M1 magnitude k/2, k in {0, 1, 2, 3, 4, 6, 8, 12}) is k 2^(d - 1), representable for
+// d - 1 in [-9, 5] (12 * 2^5 = 384). So a block folds exactly when its halves' exponents differ by
+// at most 15 (MXINT4g16) or 14 (MXFP4g16): b is the smaller exponent (MXINT4g16) or the larger
+// (MXFP4g16) when they differ by at most 8, otherwise the value that keeps both halves in range.
+// A block beyond that (one half more than 2^14 times smaller than the other, never seen in
+// Gaussian weights) cannot be folded exactly: its unrepresentable elements are stored as zero and
+// the block is counted, so the caller knows whether this image gives the exact product (the
+// Eq. (6) path is exact for every input). The image layout is the MXINT4 one (f8_image.h): the
+// permuted per-32 scales, E4M3 bytes, scales per 16-row group.
 #include "common.h"
 #include "f8_image.h"
 #include "kernels.h"
@@ -64,8 +67,12 @@ __global__ void __launch_bounds__(256) k_expand_b_g16(const uint8_t* __restrict_
     const int s0 = sc16[row * (K >> 4) + 2 * blk], s1 = sc16[row * (K >> 4) + 2 * blk + 1];
     // base E8M0 byte; a zero half (scale byte 0, codes 0) places no constraint
     int base;
-    if (FP4) base = s0 > s1 ? s0 : s1;
-    else base = s0 == 0 ? s1 : (s1 == 0 ? s0 : (s0 < s1 ? s0 : s1));
+    if (s0 == 0 || s1 == 0) {
+      base = s0 + s1;
+    } else {
+      const int lo = min(s0, s1), hi = max(s0, s1);
+      base = FP4 ? min(hi, lo + 8) : max(lo, hi - 8);
+    }
     const uint4 w = *(const uint4*)(codes + row * (K >> 1) + blk * 16);
     const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
     uint32_t out[8];

@@ -669,7 +669,11 @@ __global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
         if (i + GV_AHEAD < myn) issue_step(i + GV_AHEAD);
       }
     }
-    __builtin_amdgcn_s_barrier();   // the slice is consumed before the next chunk overwrites it
+    // every copy this wave issued has landed (a wave with no steps in this chunk still copied its
+    // scales, and an LDS copy in flight is invisible to the barrier) and the slice is consumed
+    // before the next chunk or the partial sums below overwrite it
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
   }
 
   // add the 4 waves' partial sums: wave w stores its G x 64 x 4 floats, then wave w sums result

@@ -40,22 +40,67 @@ def test_missing_library_fails_loudly(tmp_path):
 
 
 def test_traffic_record_follows_the_sources(tmp_path, monkeypatch):
+    import hashlib
+
     import bench
     rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
     assert set(rec) >= {"prefill_linear", "vision_linear", "decode", "attention_prefill"}
     for w, r in rec.items():
         assert r["traffic_bytes"] == r["fetch_bytes"] + r["write_bytes"] > 0
-    # a copy of the tree whose kernel source differs by one byte: the record no longer applies
+    # a copy of the tree with a record taken on its sources applies; once a kernel source differs by
+    # one byte it no longer does
     fake = tmp_path / "repo"
     (fake / "profiles").mkdir(parents=True)
-    (fake / "profiles" / "traffic.json").write_text(json.dumps(rec))
-    for f in rec["prefill_linear"]["source_files"]:
+    r = dict(rec["prefill_linear"])
+    h = hashlib.sha256()
+    for f in r["source_files"]:
         dst = fake / f
         dst.parent.mkdir(parents=True, exist_ok=True)
         dst.write_bytes(open(os.path.join(ROOT, f), "rb").read())
+        h.update(dst.read_bytes())
+    r["source_sha256"] = h.hexdigest()
+    (fake / "profiles" / "traffic.json").write_text(json.dumps({"prefill_linear": r}))
     monkeypatch.setattr(bench.os.path, "abspath", lambda p: str(fake / "bench.py"))
-    assert bench.measured_traffic("prefill_linear") == rec["prefill_linear"]["traffic_bytes"]
-    src = fake / rec["prefill_linear"]["source_files"][0]
+    assert bench.measured_traffic("prefill_linear") == r["traffic_bytes"]
+    src = fake / r["source_files"][0]
     src.write_bytes(src.read_bytes() + b" ")
     assert bench.measured_traffic("prefill_linear") is None
     assert bench.measured_traffic("no_such_workload") is None
+
+
+def test_caller_outputs_and_decode_shapes_are_checked(monkeypatch):
+    # the C-ABI takes only a pointer and a row pitch for C, so the binding refuses an output that
+    # does not hold [M, N] with unit column stride, before any library call (CPU tensors stand in
+    # for device ones here: the device check is switched off)
+    monkeypatch.setattr(q, "_need_cuda", lambda *a: None)
+    monkeypatch.setattr(q, "_lib_", lambda: (_ for _ in ()).throw(AssertionError("library reached")))
+    a = q.AImage(torch.zeros(16, dtype=torch.uint8), 64, 256)
+    b = q.BImage(torch.zeros(16, dtype=torch.uint8), "fp4", 300, 256, None)
+    for bad in (torch.zeros((64, 299)), torch.zeros((63, 300)), torch.zeros((300, 64)).t(),
+                torch.zeros((64, 300), dtype=torch.float16), torch.zeros(64 * 300)):
+        with pytest.raises(q.MixError):
+            q.mix_mx_gemm_images(a, b, out=bad)
+    ac, bc = torch.zeros((64, 128), dtype=torch.uint8), torch.zeros((300, 128), dtype=torch.uint8)
+    with pytest.raises(q.MixError):
+        q.mix_mx_gemm(ac, None, "4.5b", bc, None, "fp4", out=torch.zeros((64, 200)))
+    with pytest.raises(q.MixError):
+        q.mix_mx_gemm_eq6(ac, None, "4.5b", bc, None, "fp4", out=torch.zeros((64, 300))[:, ::2])
+    with pytest.raises(q.MixError):
+        q.mix_mx_gemm_images_quantize(a, q.BImage(None, "fp4", 256, 256, None), image=False,
+                                      out=torch.zeros((64, 256)))
+
+    class FakeCache:
+        B, Lmax, Hkv, d = 2, 64, 1, 32
+
+    bf = torch.bfloat16
+    qv, kn = torch.zeros((2, 2, 32), dtype=bf), torch.zeros((2, 1, 32), dtype=bf)
+    pos, mu = torch.zeros(2, dtype=torch.int32), torch.zeros((2, 1, 32))
+    ok = dict(q=qv, k_new=kn, v_new=kn, cache=FakeCache(), pos=pos, max_pos=10, mu=mu)
+    for key, val in (("q", torch.zeros((3, 2, 32), dtype=bf)), ("q", torch.zeros((2, 2, 64), dtype=bf)),
+                     ("q", torch.zeros((2, 32, 2), dtype=bf).transpose(1, 2)), ("k_new", torch.zeros((2, 2, 32), dtype=bf)),
+                     ("pos", torch.zeros(2, dtype=torch.int64)), ("mu", torch.zeros((2, 16)))):
+        with pytest.raises(q.MixError):
+            q.mix_attn_decode(**{**ok, key: val})
+    with pytest.raises(q.MixError):
+        q.mix_attn_prefill(torch.zeros((8, 2, 32), dtype=bf), torch.zeros((8, 1, 64), dtype=bf),
+                           torch.zeros((8, 1, 64), dtype=bf))

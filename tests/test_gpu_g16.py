@@ -1,5 +1,5 @@
 """g16 weights (MXINT4g16 / MXFP4g16: one shared exponent per 16 elements, the 4.5-bit tier of the
-pages' experimental setup): the GPU quantizer against the oracle bit for bit, and the products
+pages' experiment design (实验如何设计)): the GPU quantizer against the oracle bit for bit, and the products
 (MFMA from the folded image, and Eq. (6)) against the oracle's exact dyadic dot products within
 the fp32-accumulation tolerance, including MiX-INT4g16 at the prefill-linear size."""
 import numpy as np
@@ -107,18 +107,47 @@ def test_g16_eq6_product(fmt, a_fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", G16)
-def test_g16_unfoldable_blocks_are_counted(fmt):
-    # a 32-block whose halves' exponents differ by more than 8 cannot share one scale exactly:
-    # the image counts it; Eq. (6) stays exact on the same weights
+def test_g16_wide_exponent_gaps_fold_exactly(fmt):
+    # halves up to 14 binades apart share one scale exactly (the E4M3 element takes the difference),
+    # so the image product is exact on every column
     q = _q()
     M, N, K = 32, 256, 256
     x, w = _operands(M, N, K, 9, spread=1)
     w[3, 32:48] *= 2.0 ** -12        # row 3, block 1: first half 2^-12 smaller
     w[200, 144:160] *= 2.0 ** 11     # row 200, block 4: second half 2^11 larger
+    w[17, 64:80] *= 2.0 ** -5
+    w[90, 0:16] *= 2.0 ** 12
+    ac, as_ = o_mix_q(x, "4.5b", "f32")
+    bc, bs = o_mx_q(w, _base(fmt), "f32", block=16)
+    s16 = bs.astype(np.int64).reshape(N, K // 32, 2)
+    nz = (s16[..., 0] > 0) & (s16[..., 1] > 0)
+    assert (np.abs(s16[..., 0] - s16[..., 1]) * nz).max() >= 12
+    bi = q.mx_gemm_b_image(dev_u8(bc), dev_u8(bs), fmt)
+    torch.cuda.synchronize()
+    assert int(bi.unfoldable.item()) == 0
+    ad, bd = o_mix_deq(ac, as_, "4.5b"), o_mx_deq(bc, bs, _base(fmt), block=16)
+    ref, bound = gemm_ref(ad, bd), gemm_abs_bound(ad, bd)
+    img = q.mix_mx_gemm_images(q.mix_gemm_a_image(dev_u8(ac), dev_u16(as_), "4.5b"), bi, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_gemm_close(host(img), ref, bound, f"image {fmt} with wide exponent gaps")
+
+
+@pytest.mark.parametrize("fmt", G16)
+def test_g16_unfoldable_blocks_are_refused(fmt):
+    # a 32-block whose halves' exponents differ by more than the fold holds (here 2^20) cannot share
+    # one scale exactly: building its image raises unless inexact images are allowed, and then the
+    # image counts it; Eq. (6) stays exact on the same weights
+    q = _q()
+    M, N, K = 32, 256, 256
+    x, w = _operands(M, N, K, 9, spread=1)
+    w[3, 32:48] *= 2.0 ** -20        # row 3, block 1: first half 2^-20 smaller
+    w[200, 144:160] *= 2.0 ** 19     # row 200, block 4: second half 2^19 larger
     w[17, 64:80] *= 2.0 ** -5        # a difference of a few binades still folds exactly
     ac, as_ = o_mix_q(x, "4.5b", "f32")
     bc, bs = o_mx_q(w, _base(fmt), "f32", block=16)
-    bi = q.mx_gemm_b_image(dev_u8(bc), dev_u8(bs), fmt)
+    with pytest.raises(q.MixError, match="not be exact"):
+        q.mx_gemm_b_image(dev_u8(bc), dev_u8(bs), fmt)
+    bi = q.mx_gemm_b_image(dev_u8(bc), dev_u8(bs), fmt, allow_inexact=True)
     torch.cuda.synchronize()
     assert int(bi.unfoldable.item()) == 2
     ad, bd = o_mix_deq(ac, as_, "4.5b"), o_mx_deq(bc, bs, _base(fmt), block=16)

@@ -152,7 +152,7 @@ def test_gemm_images_quantized_output(b_fmt, M, N, K):
 
 @pytest.mark.parametrize("a_fmt,b_fmt", PAIRS)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (5, 300, 3584), (16, 18, 4096), (16, 5000, 4224), (3, 700, 896),
-                                   (16, 40000, 256), (7, 4099, 1152)])
+                                   (16, 40000, 256), (16, 8192, 128), (7, 4099, 1152)])
 def test_gemv_shapes(a_fmt, b_fmt, M, N, K):
     # M <= 16: the weight-streaming kernel (row groups per workgroup, K chunks, 4-way K split);
     # ragged N, K above one LDS chunk, and more row groups than fit one workgroup
