@@ -330,9 +330,10 @@ def bench_linear(torch, q, args, which):
 
 
 def bench_decode(torch, q, args):
-    """Decode step (batch 16): x [16, 3584] -> MiX-4.5b (+ A image) -> product with the MXFP4
-    weights [18944, 3584]; attention of q [16, 28, 128] over 8192 MX-coded cached tokens per row
-    (the new token at position 8191 smoothed with the frozen prefill mean and appended)."""
+    """Decode step (batch 16): x [16, 3584] -> MiX-4.5b -> product with the MXFP4 weights
+    [18944, 3584] -> y bf16, and attention of q [16, 28, 128] over 8192 MX-coded cached tokens per
+    row (the new token at position 8191 smoothed with the frozen prefill mean and appended), all in
+    one mix_decode_step call (two launches), replayed as a HIP graph."""
     from quantized_gemm_algorithm_amd import synth
     g = synth.decode_step()
     B, L, Hkv, d = g["k_hist"].shape
@@ -348,7 +349,7 @@ def bench_decode(torch, q, args):
     w = bf16(g["w_t"])
     bc, bs = q.mx_quantize(w, "fp4")
     del w
-    # one set = weights (codes + image) and a KV cache; sets rotate to defeat the 256 MB MALL
+    # one set = weights (image) and a KV cache; sets rotate to defeat the 256 MB MALL
     w_bytes = N * K // 2 + N * (K // 32)
     kv_bytes = 2 * B * Hkv * L * (d // 2 + d // 32)
     nset = rotating(w_bytes + kv_bytes, min_total=600 << 20)
@@ -369,43 +370,19 @@ def bench_decode(torch, q, args):
         sets.append((q.mx_gemm_b_image(bci, bsi, "fp4"), cache))
     torch.cuda.synchronize()
     y = torch.empty((B, N), dtype=torch.bfloat16, device=dev)
-    _, _, aimg = q.mix_quantize_gemm(x, "4.5b")
-    ac, as_ = q.mix_quantize(x, "4.5b")
-    wsb = q._lib_().mix_attn_decode_workspace_bytes(B, Hq, Hkv, d, L - 1)
-    ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+    o = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((q._lib_().mix_decode_step_workspace_bytes(B, K, Hq, Hkv, d, L - 1),), dtype=torch.uint8,
+                     device=dev)
 
-    def step(i, marks=None):
+    def step(i):
         bimg, cache = sets[i % nset]
-        e0 = marks.mark() if marks else None
-        q.mix_quantize_gemm(x, "4.5b", codes=ac, shared=as_, image=aimg)
-        e1 = marks.mark() if marks else None
-        q.mix_mx_gemm_images(aimg, bimg, out=y)
-        e2 = marks.mark() if marks else None
-        q.mix_attn_decode(qd, k_new, v_new, cache, pos, L - 1, mu, workspace=ws)
-        e3 = marks.mark() if marks else None
-        return e0, e1, e2, e3
+        q.mix_decode_step(x, bimg, qd, k_new, v_new, cache, pos, L - 1, mu, y=y, o=o, workspace=ws)
 
-    settle(torch, step, args.settle_ms)
-    for i in range(args.warmup):
-        step(i)
+    # the step as a serving loop runs it: one HIP graph per weight/cache set (the step's two launches
+    # replayed without host launch gaps); outputs are checked against the eager step
+    step(0)
     torch.cuda.synchronize()
-    # per-part times: eager launches with HIP events between the parts
-    timer = KernelTimer(torch)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    evs = []
-    t0.record()
-    for i in range(args.steps):
-        evs.append(step(i, timer))
-    t1.record()
-    torch.cuda.synchronize()
-    ms_eager = t0.elapsed_time(t1) / args.steps
-    q_ms = float(np.mean([a.elapsed_time(b) for a, b, _, _ in evs]))
-    gv_ms = float(np.mean([b.elapsed_time(c) for _, b, c, _ in evs]))
-    at_ms = float(np.mean([c.elapsed_time(e) for _, _, c, e in evs]))
-    # the step as a serving loop runs it: one HIP graph per weight/cache set (the five launches of
-    # a step replayed without host launch gaps); outputs are checked against the eager step
-    y_ref = y.clone()
+    y_ref, o_ref = y.clone(), o.clone()
     graphs = []
     for si in range(nset):
         gr = torch.cuda.CUDAGraph()
@@ -416,57 +393,83 @@ def bench_decode(torch, q, args):
     for i in range(args.warmup):
         graphs[i % nset].replay()
     torch.cuda.synchronize()
-    if not torch.equal(y, y_ref):
+    if not (torch.equal(y, y_ref) and torch.equal(o, o_ref)):
         raise RuntimeError("graph replay of the decode step differs from the eager step")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(args.steps):
         graphs[i % nset].replay()
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
-
-    # the GEMV on its own, as the roofline's kernel time: back-to-back launches over the rotating
-    # weight images captured in one graph and timed between two HIP events (an event pair around a
-    # single eager launch also holds the launch itself)
-    nrep = 4 * nset
-    gv_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gv_graph):
-        for i in range(nrep):
-            q.mix_mx_gemm_images(aimg, sets[i % nset][0], out=y)
-    gv_graph.replay()
-    torch.cuda.synchronize()
     t0.record()
-    gv_graph.replay()
+    for i in range(args.steps):
+        step(i)
     t1.record()
     torch.cuda.synchronize()
-    gv_ms_in_step = gv_ms
-    gv_ms = t0.elapsed_time(t1) / nrep
+    ms_eager = t0.elapsed_time(t1) / args.steps
+
+    # the same work as separate calls (quantize x with its A image, the weight-stream product,
+    # attention alone), each timed as back-to-back launches in one graph over the rotating sets
+    ac, as_, aimg = q.mix_quantize_gemm(x, "4.5b")
+    wsa = torch.empty((q._lib_().mix_attn_decode_workspace_bytes(B, Hq, Hkv, d, L - 1),), dtype=torch.uint8,
+                      device=dev)
+    gv_nset = max(nset, rotating(w_bytes, 320 << 20))
+    gv_imgs = [sets[i % nset][0] if i < nset else None for i in range(gv_nset)]
+    for i in range(nset, gv_nset):
+        gv_imgs[i] = q.mx_gemm_b_image(bc.clone(), bs.clone(), "fp4")
+
+    def graph_ms(fn, reps):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(reps):
+                fn(i)
+        gr.replay()
+        torch.cuda.synchronize()
+        t0.record()
+        gr.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    parts_q = graph_ms(lambda i: q.mix_quantize_gemm(x, "4.5b", codes=ac, shared=as_, image=aimg), 16)
+    parts_gv = graph_ms(lambda i: q.mix_mx_gemm_images(aimg, gv_imgs[i % gv_nset], out=y), 2 * gv_nset)
+    parts_at = graph_ms(lambda i: q.mix_attn_decode(qd, k_new, v_new, sets[i % nset][1], pos, L - 1, mu,
+                                                    workspace=wsa), 2 * nset)
+    del gv_imgs
 
     a_img_bytes = B * K + (K // 128) * 1024
     gv_bytes = N * K // 2 + (K // 128) * (-(-N // 256)) * 1024 + a_img_bytes + B * N * 2
-    q_bytes = B * K * 2 + B * K // 2 + B * (K // 32) * 2 + a_img_bytes
-    # attention: the cached K and V codes + scales of 8192 tokens, q, the new token in and out, o
+    # the step's algorithmic bytes: x in; the weights (codes + scales) and the cached K and V codes +
+    # scales of 8192 tokens read once; q, the new token in and out, mu; y and o out
+    step_bytes = (B * K * 2 + w_bytes + kv_bytes + B * Hq * d * 2 + 2 * B * Hkv * d * 2 + B * Hkv * d * 4
+                  + B * N * 2 + B * Hq * d * 2)
     at_bytes = kv_bytes + B * Hq * d * 2 * 2 + 2 * B * Hkv * d * 2 + B * Hkv * d * 4
-    step_bytes = q_bytes + gv_bytes + at_bytes
-    gbs = gv_bytes / (gv_ms * 1e-3) / 1e9
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
     res = {
         "metric": "decode GB/s (% of MI355X HBM peak)",
-        "value": step_bytes / (ms_step * 1e-3) / 1e9,
+        "value": gbs,
         "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "e4m3xe2m1->f32", "data": "synthetic",
         "config": {"workload": "decode_step_b16_l8192", "B": B, "K": K, "N": N, "L": L, "Hq": Hq, "Hkv": Hkv,
-                   "d": d, "frac_hbm": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                   "bytes_per_step": step_bytes, "rotating_sets": nset},
+                   "d": d, "bytes_per_step": step_bytes, "rotating_sets": nset},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"), "kernel": "k_gemv_f8",
-                     "kernel_ms": gv_ms, "timing": f"{nrep} back-to-back launches (one graph) between two HIP events",
-                     "algorithmic_bytes": gv_bytes},
-        "parts": {"execution": "HIP graph per step (parts timed on eager launches)",
-                  "eager_ms_per_step": ms_eager, "quantize_x_ms": q_ms, "gemv_ms": gv_ms_in_step,
-                  "attention_ms": at_ms, "attention_GB/s": at_bytes / (at_ms * 1e-3) / 1e9,
-                  "attention_bytes": at_bytes},
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"),
+                     "traffic_source": "profiles/traffic.json (FETCH_SIZE + WRITE_SIZE runs), null once the sources change",
+                     "kernel": "mix_decode_step (k_decode_scores + k_decode_pv)",
+                     "kernel_ms": ms_step, "timing": f"{args.steps} graph replays between two HIP events",
+                     "algorithmic_bytes": step_bytes},
+        "parts": {"eager_ms_per_step": ms_eager,
+                  "separate_calls": {"what": "the same work as separate calls, each timed as back-to-back launches "
+                                             "in one graph",
+                                     "quantize_x_ms": parts_q, "gemv_ms": parts_gv,
+                                     "gemv_GB/s": gv_bytes / (parts_gv * 1e-3) / 1e9,
+                                     "attention_ms": parts_at,
+                                     "attention_GB/s": at_bytes / (parts_at * 1e-3) / 1e9,
+                                     "sum_ms": parts_q + parts_gv + parts_at}},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(g, w_bytes, kv_bytes // B)

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MIX_ABI_VERSION 2
+#define MIX_ABI_VERSION 3
 
 typedef enum {
   MIX_OK = 0,
@@ -331,7 +331,7 @@ mix_status_t mix_kv_cache_prefill(const mix_kv_cache_t* cache, int64_t b, const 
 /*
  * One decode step for B sequences: append k_new/v_new [B, Hkv, d] bf16 at position pos[b]
  * (device int32 [B]), then attend q [B, Hq, d] bf16 over keys [0, pos[b]] with no causal mask,
- * using the frozen mean mu [B, Hkv, d] fp32; o [B, Hq, d] bf16. Same operand formats and softmax
+ * using the frozen mean mu [B, Hkv, d] fp32; o [B, Hq, d] bf16 (8-byte aligned). Same operand formats and softmax
  * as prefill. `max_pos` (host) bounds every pos[b] (0 <= pos[b] <= max_pos < Lmax); rows whose pos
  * is outside [0, max_pos] write zeros to o and leave the cache untouched.
  *   ws: at least mix_attn_decode_workspace_bytes(B, Hq, Hkv, d, max_pos) bytes, 256-B aligned
@@ -340,6 +340,32 @@ size_t mix_attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64
 mix_status_t mix_attn_decode(const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* cache,
                              const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
                              size_t ws_bytes, const mix_attn_debug_t* dbg, void* stream);
+
+/*
+ * One whole decode step -- P1, 方法概览 (method overview), the dual-format bullet (the linear's
+ * MiX-coded activations times its MX-coded weights) and the last bullet with 阅读时需要注意
+ * (caveats), first bullet (K-smoothing with the prefill mean frozen, so decode streams the cached
+ * keys once and never re-codes them):
+ *   y = bf16( deq(MiX-4.5b(x)) . deq(W)^T )   for the linear x [B, K] -> y [B, N], and
+ *   the attention step of mix_attn_decode (append k_new / v_new at pos[b], attend q over keys
+ *   [0, pos[b]], o [B, Hq, d]).
+ * The results equal mix_quantize_gemm(x) + mix_mx_gemm_images (bf16 out) followed by mix_attn_decode
+ * with the same arguments; the two parts are independent and run in the same two launches (the
+ * first codes x and computes the scores, the second streams the weights and the values).
+ *   x      [B, K] bf16, dense (B = cache->B <= 16; K a positive multiple of 128), 16-byte aligned
+ *   b_fmt, b_img  the weights' B image (mx_gemm_b_image / mx_gemm_b_image_g16 for an [N, K] operand;
+ *          g16 images must have no unfoldable block for the product to be exact), 256-byte aligned
+ *   y      [B, N] bf16, dense
+ *   q, k_new, v_new, cache, pos, max_pos, Hq, mu, o  as for mix_attn_decode (d = 128)
+ *   ws     at least mix_decode_step_workspace_bytes(B, K, Hq, Hkv, d, max_pos) bytes, 256-byte
+ *          aligned; scratch (its contents on entry do not matter)
+ * Errors as for mix_attn_decode and mix_mx_gemm_images; MIX_E_UNSUPPORTED for B > 16.
+ */
+size_t mix_decode_step_workspace_bytes(int64_t B, int64_t K, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos);
+mix_status_t mix_decode_step(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt, const void* b_img, void* y,
+                             const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* cache,
+                             const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
+                             size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ __all__ = [
     "MixError", "mix_quantize", "mx_quantize", "mx_quantize_cols", "mix_dequantize", "mx_dequantize",
     "mix_mx_gemm", "mix_mx_gemm_eq6", "AImage", "BImage", "mix_gemm_a_image", "mix_quantize_gemm",
     "mx_gemm_b_image", "mix_mx_gemm_images", "mix_mx_gemm_images_quantize", "mix_kmean", "mix_underflow_map", "mix_underflow_map_workspace_bytes", "UF_KINDS", "mix_attn_prefill", "KVCache", "mix_kv_cache_prefill",
-    "mix_attn_decode", "abi_version",
+    "mix_attn_decode", "mix_decode_step", "abi_version",
 ]
 
 
@@ -479,3 +479,39 @@ def mix_attn_decode(q, k_new, v_new, cache, pos, max_pos, mu, debug=False, works
     check(lib.mix_attn_decode(_p(q), _p(k_new), _p(v_new), cache.ref, _p(pos), max_pos, Hq, _p(mu), _p(o),
                               _p(workspace), workspace.numel(), ref, _stream()), "mix_attn_decode")
     return o, dbg
+
+
+def mix_decode_step(x, b_img, q, k_new, v_new, cache, pos, max_pos, mu, y=None, o=None, workspace=None):
+    """One whole decode step: y = bf16(MiX-4.5b(x) . W^T) for x [B, K] bf16 and the weights' BImage
+    (N x K), and the attention step of mix_attn_decode (q [B, Hq, d], k_new/v_new [B, Hkv, d] bf16,
+    pos int32 [B], mu fp32 [B, Hkv, d]). Returns (y bf16 [B, N], o bf16 [B, Hq, d])."""
+    _need_cuda(x, q, k_new, v_new, pos, mu, y, o, workspace)
+    if q.dim() != 3:
+        raise MixError("q must be [B, Hq, d]")
+    B, Hq, d = q.shape
+    if B != cache.B or d != cache.d:
+        raise MixError(f"q is [{B}, {Hq}, {d}] but the cache holds B = {cache.B}, d = {cache.d}")
+    if x.dim() != 2 or x.shape[0] != B or x.shape[1] != b_img.K:
+        raise MixError(f"x must be [{B}, {b_img.K}] (the batch and the weights' K)")
+    N, K = b_img.N, b_img.K
+    _dense(x, (B, K), torch.bfloat16, "x")
+    _dense(q, (B, Hq, d), torch.bfloat16, "q")
+    _dense(k_new, (B, cache.Hkv, d), torch.bfloat16, "k_new")
+    _dense(v_new, (B, cache.Hkv, d), torch.bfloat16, "v_new")
+    _dense(pos, (B,), torch.int32, "pos")
+    if mu.dtype != torch.float32 or mu.numel() != B * cache.Hkv * d or not mu.is_contiguous():
+        raise MixError(f"mu must be a contiguous float32 tensor of {B} x {cache.Hkv} x {d} values")
+    if y is None:
+        y = torch.empty((B, N), dtype=torch.bfloat16, device=x.device)
+    _dense(y, (B, N), torch.bfloat16, "y")
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=x.device)
+    _dense(o, (B, Hq, d), torch.bfloat16, "o")
+    lib = _lib_()
+    wsb = lib.mix_decode_step_workspace_bytes(B, K, Hq, cache.Hkv, d, max_pos)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=x.device)
+    check(lib.mix_decode_step(_p(x), K, N, MX_FMT[b_img.fmt], _p(b_img.buf), _p(y), _p(q), _p(k_new), _p(v_new),
+                              cache.ref, _p(pos), max_pos, Hq, _p(mu), _p(o), _p(workspace), workspace.numel(),
+                              _stream()), "mix_decode_step")
+    return y, o

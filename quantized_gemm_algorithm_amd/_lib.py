@@ -52,6 +52,9 @@ SIGNATURES = {
     "mix_attn_decode_workspace_bytes": (ctypes.c_size_t, [c_i64, c_i64, c_i64, c_i64, c_i64]),
     "mix_attn_decode": (c_int, [c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_ptr, ctypes.c_size_t,
                                 c_ptr, c_ptr]),
+    "mix_decode_step_workspace_bytes": (ctypes.c_size_t, [c_i64, c_i64, c_i64, c_i64, c_i64, c_i64]),
+    "mix_decode_step": (c_int, [c_ptr, c_i64, c_i64, c_int, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_i64,
+                                c_i64, c_ptr, c_ptr, c_ptr, ctypes.c_size_t, c_ptr]),
 }
 
 

@@ -448,9 +448,8 @@ mix_status_t mix_kv_cache_prefill(const mix_kv_cache_t* cache, int64_t b, const 
 }
 
 size_t mix_attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos) {
-  (void)Hkv;
-  if (B <= 0 || Hq <= 0 || d <= 0 || max_pos < 0) return 0;
-  return mix::attn_decode_ws_bytes(B, Hq, d, max_pos);
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_pos < 0) return 0;
+  return mix::attn_decode_ws_bytes(B, Hq, Hkv, d, max_pos);
 }
 
 mix_status_t mix_attn_decode(const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* cache,
@@ -463,13 +462,46 @@ mix_status_t mix_attn_decode(const void* q, const void* k_new, const void* v_new
   if (Hq / cache->Hkv > 16) return fail(MIX_E_UNSUPPORTED, "mix_attn_decode: more than 16 query heads per KV head");
   if (max_pos < 0 || max_pos >= cache->Lmax) return fail(MIX_E_SHAPE, "mix_attn_decode: max_pos=%lld outside [0, Lmax)", (long long)max_pos);
   if (!q || !k_new || !v_new || !pos || !mu || !o || !ws) return fail(MIX_E_NULL, "mix_attn_decode: NULL pointer");
-  if (((uintptr_t)ws & 255u) || !aligned16(q) || ((uintptr_t)o & 1u) || ((uintptr_t)pos & 3u) || ((uintptr_t)mu & 3u))
-    return fail(MIX_E_ALIGN, "mix_attn_decode: misaligned argument (ws must be 256-byte aligned, q 16-byte)");
+  if (((uintptr_t)ws & 255u) || !aligned16(q) || ((uintptr_t)o & 7u) || ((uintptr_t)pos & 3u) || ((uintptr_t)mu & 3u))
+    return fail(MIX_E_ALIGN, "mix_attn_decode: misaligned argument (ws must be 256-byte aligned, q 16-byte, o 8-byte)");
   if (dbg && !aligned16(dbg->p)) return fail(MIX_E_ALIGN, "mix_attn_decode: debug p must be 16-byte aligned");
-  size_t need = mix::attn_decode_ws_bytes(cache->B, Hq, cache->d, max_pos);
+  size_t need = mix::attn_decode_ws_bytes(cache->B, Hq, cache->Hkv, cache->d, max_pos);
   if (ws_bytes < need) return fail(MIX_E_WORKSPACE, "mix_attn_decode: workspace %zu < %zu bytes", ws_bytes, need);
   return hip_status(mix::attn_decode_run(q, k_new, v_new, cache, pos, max_pos, Hq, mu, o, ws, dbg, (hipStream_t)stream),
                     "mix_attn_decode");
+}
+
+size_t mix_decode_step_workspace_bytes(int64_t B, int64_t K, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos) {
+  if (B <= 0 || K <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_pos < 0) return 0;
+  return mix::decode_step_ws_bytes(B, K, Hq, Hkv, d, max_pos);
+}
+
+mix_status_t mix_decode_step(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt, const void* b_img, void* y,
+                             const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* cache,
+                             const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
+                             size_t ws_bytes, void* stream) {
+  g_err.clear();
+  const char* fn = "mix_decode_step";
+  if (mix_status_t st = check_cache(fn, cache)) return st;
+  if (!mx_known(b_fmt)) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (Hq <= 0 || Hq % cache->Hkv) return fail(MIX_E_SHAPE, "%s: Hq must be a positive multiple of Hkv", fn);
+  if (cache->d != 128) return fail(MIX_E_UNSUPPORTED, "%s: head dim %lld (only 128 is implemented)", fn, (long long)cache->d);
+  if (Hq / cache->Hkv > 16) return fail(MIX_E_UNSUPPORTED, "%s: more than 16 query heads per KV head", fn);
+  if (cache->B > 16) return fail(MIX_E_UNSUPPORTED, "%s: batch %lld above 16 (the weight stream's rows)", fn, (long long)cache->B);
+  if (max_pos < 0 || max_pos >= cache->Lmax) return fail(MIX_E_SHAPE, "%s: max_pos=%lld outside [0, Lmax)", fn, (long long)max_pos);
+  if (N <= 0 || N > INT32_MAX || !image_k_ok(K) || K > INT32_MAX)
+    return fail(MIX_E_SHAPE, "%s: K=%lld must be a positive multiple of 128 and N=%lld positive", fn, (long long)K, (long long)N);
+  if (!mix::gemm_f8_offsets_ok(1, N, K) || cache->B * K >= ((int64_t)1 << 31))
+    return fail(MIX_E_UNSUPPORTED, "%s: an operand image of %lld x %lld reaches 2^31 bytes", fn, (long long)N, (long long)K);
+  if (!x || !b_img || !y || !q || !k_new || !v_new || !pos || !mu || !o || !ws) return fail(MIX_E_NULL, "%s: NULL pointer", fn);
+  if (((uintptr_t)ws & 255u) || ((uintptr_t)b_img & 255u) || !aligned16(x) || !aligned16(q) || ((uintptr_t)y & 1u) ||
+      ((uintptr_t)o & 7u) || ((uintptr_t)pos & 3u) || ((uintptr_t)mu & 3u))
+    return fail(MIX_E_ALIGN, "%s: misaligned argument (ws and b_img 256-byte, x and q 16-byte, o 8-byte)", fn);
+  const size_t need = mix::decode_step_ws_bytes(cache->B, K, Hq, cache->Hkv, cache->d, max_pos);
+  if (ws_bytes < need) return fail(MIX_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  return hip_status(mix::decode_step_run(x, K, N, b_fmt == MX_FP4, b_img, y, q, k_new, v_new, cache, pos, max_pos, Hq,
+                                         mu, o, ws, (hipStream_t)stream),
+                    fn);
 }
 
 }  // extern "C"

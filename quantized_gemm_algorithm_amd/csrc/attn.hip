@@ -19,11 +19,13 @@
 //
 // Decode keeps the exact global row max with two passes over the keys: pass 1 (scores) computes S
 // for 256-key chunks on the MFMA and per-chunk maxima; pass 2 (pv) takes the global max, forms p
-// and P^ for its chunk and multiplies by V^ on the MFMA; a final kernel sums the chunk partials.
+// and P^ for its chunk and multiplies by V^ on the MFMA; a third launch sums the chunk partials.
 #include <type_traits>
 
 #include "../../include/mixlib.h"
 #include "common.h"
+#include "f8_image.h"
+#include "gemv_dev.h"
 #include "kernels.h"
 #include "quant_dev.h"
 
@@ -579,23 +581,34 @@ __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* _
 // ------------------------------------------------------------------ decode: scores (pass 1)
 //
 // Decode attends the G = Hq/Hkv query rows of each (sequence b, KV head h) over keys [0, pos[b]]
-// in chunks of DCH keys: pass 1 (one workgroup per chunk, one more that appends the new key and
-// value) codes the query rows and writes S and the chunk maxima; pass 2 turns S into p and P^ with the row
-// maximum over all chunks and multiplies P^ by V^ (the chunk partials); a third pass sums the
-// partials into O.
+// in chunks of DCH keys, in three launches. The first (scores) has one workgroup per chunk, which
+// codes the query rows and writes S and the chunk maxima, and one more per (b, h), which appends
+// the new key and value. The second (pv) turns S into p and P^ with the row maximum over all
+// chunks, multiplies P^ by V^ on the MFMA and writes the chunk's partial sums; the third adds the
+// partials of all chunks in chunk order into O. The exact global maximum is what P^ needs, and it
+// is known only once every chunk's scores exist, hence the launch boundaries and the S round trip.
+// (A last-arriving workgroup could combine inside the pv launch, but making the partials visible
+// across CUs takes an agent-scope release and acquire per workgroup, which write back and
+// invalidate the L2: far dearer on this part than a third launch.)
+//
+// The full decode step (mix_decode_step) puts its independent work into the same launches as
+// further workgroups: the first also codes the linear's activation rows into their A image, a later
+// one also streams the weights (gemv_block), so the weight stream and the KV-cache stream run side
+// by side instead of one after the other.
 
 constexpr int DCH = 256;  // keys per chunk
 
-// Decode workgroup -> (chunk, KV head h, sequence b) over a 1-D grid of 8 per ceil(B Hkv / 8)
-// workgroups, per workgroups for each (b, h). Workgroups are spread over the 8 XCDs round-robin, so the chunks of one (b, h) get
-// ids equal modulo 8: they run on one XCD and share its L2 for the per-channel value scales (one
-// 128-byte line serves 16 chunks), the chunk maxima and the S rows pass 2 reads back.
+// Decode workgroup -> (chunk, KV head h, sequence b) from a role-local index vb over 8 per
+// ceil(B Hkv / 8) groups of `per` workgroups. Workgroups are spread over the 8 XCDs round-robin
+// (each role starts at a multiple of 8, so vb and the hardware index agree modulo 8), so the chunks
+// of one (b, h) get ids equal modulo 8: they run on one XCD and share its L2 for the per-channel
+// value scales (one 128-byte line serves 16 chunks), the chunk maxima, S and the chunk partials.
 struct DecWg {
   int chunk, h, b;
   bool valid;
 };
-__device__ __forceinline__ DecWg dec_wg(int per, int Hkv, int B) {
-  const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+__device__ __forceinline__ DecWg dec_wg(int vb, int per, int Hkv, int B) {
+  const int x = vb & 7, i = vb >> 3;
   const int bh = x + 8 * (i / per);
   DecWg w;
   w.chunk = i % per;
@@ -619,47 +632,68 @@ __device__ __forceinline__ void new_key_code(uint32_t kraw, float muc, uint32_t&
   scale = amax ? (uint32_t)(X + 127) : 0u;
 }
 
-// grid 8 (nchunk + 1) ceil(B Hkv / 8) (dec_wg over nchunk + 1 workgroups per (b, h)), block 256.
-// Requires d == 128 and G <= 16. Workgroup `nchunk` of (b, h) appends the new token to the cache:
-// the new key's codes into slot pos; the new value into the staging rows and the value block that
-// holds pos re-coded along tokens from the staged tokens present (zero for the rest). The others,
-// one per chunk of 256 keys (4 waves x 64 keys):
+// Arguments of both decode passes (d = 128, G <= 16).
+struct DecOps {
+  const uint16_t* q;        // [B, Hq, d] bf16
+  const uint16_t* k_new;    // [B, Hkv, d]
+  const uint16_t* v_new;    // [B, Hkv, d]
+  const float* mu;          // [B, Hkv, d]
+  const int32_t* pos;       // [B]
+  int64_t max_pos, Lmax, Lp;
+  int Hq, Hkv, B, nchunk;
+  uint8_t* kc;              // cache K codes [B, Hkv, Lmax, d/2]
+  uint8_t* ks;              //   scales [B, Hkv, Lmax, d/32]
+  uint8_t* vc;              // cache V codes [B, Hkv, d, Lmax/2]
+  uint8_t* vs;              //   scales [B, Hkv, d, Lmax/32]
+  uint16_t* stage;          // [B, 32, Hkv, d] bf16
+  float* S;                 // [B, Hq, Lp]
+  float* pmax;              // [B, Hq, nchunk]
+  float* lpart;             // [B, Hq, nchunk]
+  float* opart;             // [B, Hq, nchunk, d]
+  float scale;              // fp32(1 / sqrt(d))
+  uint16_t* o;              // [B, Hq, d] bf16
+  // debug dumps (NULL when not wanted)
+  uint8_t* pc;              // [B, Hq, Lp/2]
+  uint16_t* ps;             // [B, Hq, Lp/32]
+  float* dbg_p;             // [B, Hq, Lp]
+  float* dbg_l;             // [B, Hq]
+};
+
+// Scores pass, workgroup vb of 8 (nchunk + 1) ceil(B Hkv / 8) (dec_wg over nchunk + 1 per (b, h)),
+// 256 threads. Workgroup `nchunk` of (b, h) appends the new token to the cache: the new key's codes into slot pos; the new value into the staging rows
+// and the value block that holds pos re-coded along tokens from the staged tokens present (zero
+// for the rest). The others, one per chunk of 256 keys (4 waves x 64 keys):
 // 1. code the G query rows of this KV head: MiX-4.5b along the head dimension, decoded to the
 //    MFMA's E4M3 operand (per-block E8M0 scale 2^(Emax-1)) in LDS;
 // 2. the chunk that holds pos codes the new key too and uses it in place of the slot's contents;
 // 3. write S [B, Hq, Lp] fp32 for keys <= pos and the chunk maxima pmax [B, Hq, nchunk]. Cache rows
 //    past pos are never used: their loads are clamped to row pos and their products discarded.
-__global__ void __launch_bounds__(256) k_decode_qk(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
-                                                    const uint16_t* __restrict__ v_new, const float* __restrict__ mu,
-                                                    const int32_t* __restrict__ pos, int64_t max_pos, int Hq, int Hkv,
-                                                    int64_t Lmax, uint8_t* __restrict__ kc, uint8_t* __restrict__ ks,
-                                                    uint8_t* __restrict__ vc, uint8_t* __restrict__ vs,
-                                                    uint16_t* __restrict__ stage, int64_t Lp, int B,
-                                                    int nchunk, float* __restrict__ S, float* __restrict__ pmax) {
+__device__ __forceinline__ void dec_scores(const DecOps& a, int vb) {
   constexpr int d = 128;
-  const DecWg wg = dec_wg(nchunk + 1, Hkv, B);
+  const DecWg wg = dec_wg(vb, a.nchunk + 1, a.Hkv, a.B);
   if (!wg.valid) return;
-  const int h = wg.h, b = wg.b;
-  const int p = pos[b];
-  if (p < 0 || p > max_pos) return;
+  const int h = wg.h, b = wg.b, Hkv = a.Hkv, Hq = a.Hq;
+  const int64_t Lmax = a.Lmax;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t bh = (int64_t)b * Hkv + h;
+  const int p = a.pos[b];
+  if (p < 0 || p > a.max_pos) return;
 
-  if (wg.chunk == nchunk) {
+  if (wg.chunk == a.nchunk) {
     // append: loads first (key channel, mean, value channel, the 16 staged rows of this thread)
     const int c = tid >> 1, half = tid & 1, slot = p & 31;
-    const uint32_t kraw = k_new[bh * d + (tid & (d - 1))];
-    const float muc = mu[bh * d + (tid & (d - 1))];
-    const uint16_t vnew = v_new[bh * d + c];
+    const uint32_t kraw = a.k_new[bh * d + (tid & (d - 1))];
+    const float muc = a.mu[bh * d + (tid & (d - 1))];
+    const uint16_t vnew = a.v_new[bh * d + c];
     uint32_t u[16];
 #pragma unroll
-    for (int i = 0; i < 16; i++) u[i] = stage[(((int64_t)b * 32 + 16 * half + i) * Hkv + h) * d + c];
+    for (int i = 0; i < 16; i++) u[i] = a.stage[(((int64_t)b * 32 + 16 * half + i) * Hkv + h) * d + c];
     if (tid < d) {
       uint32_t byte, sc;
       new_key_code(kraw, muc, byte, sc);
       const int64_t krow = bh * Lmax + p;
-      if ((tid & 1) == 0) kc[krow * (d >> 1) + (tid >> 1)] = (uint8_t)byte;
-      if ((tid & 31) == 0) ks[krow * (d >> 5) + (tid >> 5)] = (uint8_t)sc;
+      if ((tid & 1) == 0) a.kc[krow * (d >> 1) + (tid >> 1)] = (uint8_t)byte;
+      if ((tid & 31) == 0) a.ks[krow * (d >> 5) + (tid >> 5)] = (uint8_t)sc;
     }
     // value: thread -> (channel c, tokens [16 half, +16) of the block)
     uint32_t vmax = 0;
@@ -670,7 +704,7 @@ __global__ void __launch_bounds__(256) k_decode_qk(const uint16_t* __restrict__ 
       vmax = max(vmax, u[i] & 0x7FFFFFFFu);
     }
     vmax = max(vmax, (uint32_t)__shfl_xor((int)vmax, 1, 64));
-    if (half == (slot >> 4)) stage[(((int64_t)b * 32 + slot) * Hkv + h) * d + c] = vnew;
+    if (half == (slot >> 4)) a.stage[(((int64_t)b * 32 + slot) * Hkv + h) * d + c] = vnew;
     const int XV = mx_exponent(vmax, 1);
     uint32_t w0 = 0, w1 = 0;
     if (vmax) {
@@ -682,8 +716,8 @@ __global__ void __launch_bounds__(256) k_decode_qk(const uint16_t* __restrict__ 
       }
     }
     const int64_t vrow = bh * d + c;
-    *(uint2*)(vc + vrow * (Lmax >> 1) + (p >> 5) * 16 + 8 * half) = make_uint2(w0, w1);
-    if (half == 0) vs[vrow * (Lmax >> 5) + (p >> 5)] = vmax ? (uint8_t)(XV + 127) : (uint8_t)0;
+    *(uint2*)(a.vc + vrow * (Lmax >> 1) + (p >> 5) * 16 + 8 * half) = make_uint2(w0, w1);
+    if (half == 0) a.vs[vrow * (Lmax >> 5) + (p >> 5)] = vmax ? (uint8_t)(XV + 127) : (uint8_t)0;
     return;
   }
 
@@ -704,13 +738,13 @@ __global__ void __launch_bounds__(256) k_decode_qk(const uint16_t* __restrict__ 
 #pragma unroll
   for (int t = 0; t < 4; t++) {
     const int j = min(chunk * DCH + wave * 64 + t * 16 + r, p);
-    kv[t] = *(const uint4*)(kc + (bh * Lmax + j) * 64 + g * 16);
-    ksc[t] = ks[(bh * Lmax + j) * 4 + g];
+    kv[t] = *(const uint4*)(a.kc + (bh * Lmax + j) * 64 + g * 16);
+    ksc[t] = a.ks[(bh * Lmax + j) * 4 + g];
   }
   const int qr = tid >> 4, qsb = tid & 15;   // query row, 8-element sub-block (quads are blocks)
-  const uint4 qv = *(const uint4*)(q + ((int64_t)b * Hq + (int64_t)h * G + min(qr, G - 1)) * d + qsb * 8);
-  const uint32_t kraw = k_new[bh * d + (tid & (d - 1))];
-  const float muc = mu[bh * d + (tid & (d - 1))];
+  const uint4 qv = *(const uint4*)(a.q + ((int64_t)b * Hq + (int64_t)h * G + min(qr, G - 1)) * d + qsb * 8);
+  const uint32_t kraw = a.k_new[bh * d + (tid & (d - 1))];
+  const float muc = a.mu[bh * d + (tid & (d - 1))];
   // 1. query operand
   if (qr < G) {
     const uint32_t w4[4] = {qv.x, qv.y, qv.z, qv.w};
@@ -757,7 +791,7 @@ __global__ void __launch_bounds__(256) k_decode_qk(const uint16_t* __restrict__ 
     for (int i = 0; i < 4; i++) {
       const int row = 4 * g + i;
       if (row < G && live) {
-        S[((int64_t)b * Hq + (int64_t)h * G + row) * Lp + j] = acc[i];
+        a.S[((int64_t)b * Hq + (int64_t)h * G + row) * a.Lp + j] = acc[i];
         rmax[i] = fmaxf(rmax[i], acc[i]);
       }
     }
@@ -775,8 +809,52 @@ __global__ void __launch_bounds__(256) k_decode_qk(const uint16_t* __restrict__ 
   __syncthreads();
   if (tid < G) {
     const float v = fmaxf(fmaxf(smax[0][tid], smax[1][tid]), fmaxf(smax[2][tid], smax[3][tid]));
-    pmax[((int64_t)b * Hq + (int64_t)h * G + tid) * nchunk + chunk] = v;
+    a.pmax[((int64_t)b * Hq + (int64_t)h * G + tid) * a.nchunk + chunk] = v;
   }
+}
+
+// The linear's activation rows coded into their A image inside the scores launch (the full decode
+// step): M <= 16 rows of K bf16 values, row pitch ldx; a lane codes one 8-element sub-block (a quad
+// is a 32-element block, a 16-lane DPP row one 128-wide K step) exactly as mix_quantize_gemm does,
+// writing the 8 E4M3 bytes and, on the first lane of each DPP row, the row's four block scales of
+// that K step.
+struct XqOps {
+  const uint16_t* x;
+  int64_t ldx;
+  int M, K;
+  uint8_t* a8;    // [M, K] E4M3
+  uint8_t* as_p;  // [K/128][1][256][4] (tiles_m = 1 for M <= 256)
+};
+
+__device__ __forceinline__ void dec_xquant(const XqOps& o, int vb) {
+  const int spr = o.K >> 3;
+  const int idx = vb * 256 + threadIdx.x;
+  const bool ok = idx < o.M * spr;            // M spr is a multiple of 16: whole DPP rows in or out
+  const int id = ok ? idx : (idx & 15);
+  const int row = id / spr, sc = id - row * spr;
+  const uint4 v = *(const uint4*)(o.x + (int64_t)row * o.ldx + (int64_t)sc * 8);
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  int emax;
+  uint32_t m, e0, e1;
+  mix_quant_lane_bf16_img<1, true>(w4, emax, m, e0, e1);
+  const int ev = emax + 126;
+  const uint32_t sdw = (uint32_t)ev | ((uint32_t)__builtin_amdgcn_update_dpp(0, ev, 0x12C, 0xF, 0xF, true) << 8) |
+                       ((uint32_t)__builtin_amdgcn_update_dpp(0, ev, 0x128, 0xF, 0xF, true) << 16) |
+                       ((uint32_t)__builtin_amdgcn_update_dpp(0, ev, 0x124, 0xF, 0xF, true) << 24);
+  if (!ok) return;
+  *(uint2*)(o.a8 + (int64_t)row * o.K + sc * 8) = make_uint2(e0, e1);
+  if ((sc & 15) == 0) *(uint32_t*)(o.as_p + (int64_t)(sc >> 4) * 1024 + row * 4) = sdw;
+}
+
+// grid nxq + 8 (nchunk + 1) ceil(B Hkv / 8), block 256: workgroups [0, nxq) code the linear's
+// activations (nxq a multiple of 8, 0 for attention alone), the rest run dec_scores.
+__global__ void __launch_bounds__(256) k_decode_scores(DecOps a, XqOps xq, int nxq) {
+  const int vb = (int)blockIdx.x;
+  if (vb < nxq) {
+    dec_xquant(xq, vb);
+    return;
+  }
+  dec_scores(a, vb - nxq);
 }
 
 // ------------------------------------------------------------------ decode: p, P^, P^ V^, O (pass 2)
@@ -786,31 +864,34 @@ __global__ void __launch_bounds__(256) k_decode_qk(const uint16_t* __restrict__ 
 // read serves at once hit distinct banks.
 __device__ __forceinline__ int vswz(int ch) { return (ch ^ (ch >> 3)) & 7; }
 
-// LDS bytes of k_decode_pv: the value tile, then P^ as E4M3 [G][DCH] and its scales [G][DCH/32],
+// LDS bytes of the pv pass: the value tile, then P^ as E4M3 [G][DCH] and its scales [G][DCH/32],
 // then the row maxima
-inline size_t decode_pv_lds_bytes(int G) { return 128 * 128 + (size_t)G * DCH + (size_t)G * (DCH / 32) + 16 * 4; }
+inline size_t decode_pv_lds_bytes(int G) { return 128 * 128 + (size_t)G * DCH + (size_t)G * (DCH / 32) + 4 + 16 * 4; }
 
-// grid 8 nchunk ceil(B Hkv / 8) (dec_wg), block 256, LDS decode_pv_lds_bytes(G). P^ codes
-// [B, Hq, Lp/2] and shared [B, Hq, Lp/32] are written only when pc / ps are given (debug dumps);
-// chunk partials lpart [B, Hq, nchunk], opart [B, Hq, nchunk, 128].
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) k_decode_pv(const float* __restrict__ S, const float* __restrict__ pmax,
-                                                    const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
-                                                    const int32_t* __restrict__ pos, int64_t max_pos, int Hq, int Hkv,
-                                                    int64_t Lmax, int64_t Lp, int B, int nchunk, float scale,
-                                                    uint8_t* __restrict__ pc, uint16_t* __restrict__ ps,
-                                                    float* __restrict__ lpart, float* __restrict__ opart,
-                                                    float* __restrict__ dbg_p) {
+// The pv pass for workgroup vb of 8 nchunk ceil(B Hkv / 8) (dec_wg), 256 threads, LDS dsm of
+// decode_pv_lds_bytes(G) bytes. Writes the chunk partials lpart [B, Hq, nchunk] and opart [B, Hq,
+// nchunk, 128]. P^ codes [B, Hq, Lp/2] and shared fields [B, Hq, Lp/32] are written only when pc /
+// ps are given (debug dumps).
+__device__ __forceinline__ void dec_pv(const DecOps& a, int vb, uint8_t* dsm) {
   constexpr int d = 128;
-  extern __shared__ __align__(16) uint8_t dsm[];
-  const DecWg wg = dec_wg(nchunk, Hkv, B);
+  const DecWg wg = dec_wg(vb, a.nchunk, a.Hkv, a.B);
   if (!wg.valid) return;
-  const int chunk = wg.chunk, h = wg.h, b = wg.b;
+  const int chunk = wg.chunk, h = wg.h, b = wg.b, Hq = a.Hq, Hkv = a.Hkv;
+  const int64_t Lmax = a.Lmax, Lp = a.Lp;
+  const int nchunk = a.nchunk;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int p = pos[b];
-  if (p < 0 || p > max_pos || chunk * DCH > p) return;
-  const int r = lane & 15, g = lane >> 4;
+  const int p = a.pos[b];
   const int64_t bh = (int64_t)b * Hkv + h;
+  const int64_t qrow0 = (int64_t)b * Hq + (int64_t)h * G;
+  if (p < 0 || p > a.max_pos) {
+    // rows outside [0, max_pos]: O is zero (written once, by chunk 0)
+    if (chunk == 0)
+      for (int t = tid; t < G * d; t += 256) a.o[qrow0 * d + t] = 0;
+    return;
+  }
+  if (chunk * DCH > p) return;
+  const int r = lane & 15, g = lane >> 4;
   uint8_t* sV = dsm;                                   // [128][128] value codes
   uint8_t* sP = dsm + 128 * 128;                       // [G][DCH] P^ as E4M3
   uint8_t* sPs = sP + G * DCH;                         // [G][DCH/32] its scales
@@ -824,7 +905,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) k
   for (int it = 0; it < 4; it++) {
     const int row0 = 32 * wave + 8 * it, ch = row0 + (lane >> 3), slot = lane & 7;
     const int kb = min(chunk * (DCH / 32) + (slot ^ vswz(ch)), pb);
-    dma16(vc + (bh * d + ch) * (Lmax >> 1) + kb * 16, __builtin_amdgcn_readfirstlane(lds_addr(sV + row0 * 128)));
+    dma16(a.vc + (bh * d + ch) * (Lmax >> 1) + kb * 16, __builtin_amdgcn_readfirstlane(lds_addr(sV + row0 * 128)));
   }
   // value scales of the wave's channel tiles 2w, 2w+1 (16 channels each), K steps k2, blocks g
   int vsc[DCH / 128][2];
@@ -832,13 +913,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) k
   for (int k2 = 0; k2 < DCH / 128; k2++) {
     const int kb = min(chunk * DCH + k2 * 128 + 32 * g, p) >> 5;
 #pragma unroll
-    for (int t = 0; t < 2; t++) vsc[k2][t] = vs[(bh * d + (2 * wave + t) * 16 + r) * (Lmax >> 5) + kb];
+    for (int t = 0; t < 2; t++) vsc[k2][t] = a.vs[(bh * d + (2 * wave + t) * 16 + r) * (Lmax >> 5) + kb];
   }
   // S of the thread's (row, 8 keys): thread -> (row = tid / 32 + 8 pass, sub-block = tid % 32);
   // the first pass's values are loaded here, a second pass (G > 8) loads its own
   const int sbk = tid & 31, jb = chunk * DCH + sbk * 8;
   auto load_s = [&](int row, float (&v)[8]) {
-    const float* sp = S + ((int64_t)b * Hq + (int64_t)h * G + row) * Lp + jb;
+    const float* sp = a.S + (qrow0 + row) * Lp + jb;
     const float4 s0 = *(const float4*)sp;
     const float4 s1 = *(const float4*)(sp + 4);
     v[0] = s0.x; v[1] = s0.y; v[2] = s0.z; v[3] = s0.w;
@@ -850,12 +931,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) k
   // do not change a maximum)
   const int last = p / DCH;
   const int mrow = min(tid >> 4, G - 1), part = tid & 15;
-  const float* pm = pmax + ((int64_t)b * Hq + (int64_t)h * G + mrow) * nchunk;
+  const float* pm = a.pmax + (qrow0 + mrow) * nchunk;
   float pmv = fmaxf(pm[min(part, last)], pm[min(part + 16, last)]);
   for (int c = part + 32; c <= last; c += 16) pmv = fmaxf(pmv, pm[c]);
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) pmv = fmaxf(pmv, __shfl_xor(pmv, off, 64));
-  if ((tid & 15) == 0 && (tid >> 4) < G) sm[tid >> 4] = __fmul_rn(pmv, scale);
+  if ((tid & 15) == 0 && (tid >> 4) < G) sm[tid >> 4] = __fmul_rn(pmv, a.scale);
   __syncthreads();
 
   // p and P^
@@ -864,36 +945,36 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) k
     const int row = 8 * pass + (tid >> 5);
     if (row < G) {  // 32 threads per row: whole quads
       if (pass == 1) load_s(row, sv);
-      const int64_t qrow = (int64_t)b * Hq + (int64_t)h * G + row;
+      const int64_t qrow = qrow0 + row;
       const float m = sm[row];
       float pv[8];
       float lsum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        const float v = exp_nonpos(__fsub_rn(__fmul_rn(sv[e], scale), m));
+        const float v = exp_nonpos(__fsub_rn(__fmul_rn(sv[e], a.scale), m));
         pv[e] = jb + e <= p ? v : 0.f;
         lsum += pv[e];
       }
       uint32_t shf;
       const uint32_t word = p_code8(make_float4(pv[0], pv[1], pv[2], pv[3]), make_float4(pv[4], pv[5], pv[6], pv[7]),
                                     sbk & 3, shf);
-      if (pc) *(uint32_t*)(pc + qrow * (Lp >> 1) + (jb >> 1)) = word;
+      if (a.pc) *(uint32_t*)(a.pc + qrow * (Lp >> 1) + (jb >> 1)) = word;
       if ((sbk & 3) == 0) {
-        if (ps) ps[qrow * (Lp >> 5) + (jb >> 5)] = (uint16_t)shf;
+        if (a.ps) a.ps[qrow * (Lp >> 5) + (jb >> 5)] = (uint16_t)shf;
         sPs[row * (DCH / 32) + (sbk >> 2)] = (uint8_t)((shf & 15u) + 119u);
       }
       uint32_t e0, e1;
       mix8_to_e4m3(word, (shf >> (4 + 3 * (sbk & 3))) & 7u, e0, e1);
       *(uint2*)(sP + row * DCH + sbk * 8) = make_uint2(e0, e1);
-      if (dbg_p) {
-        float* dp = dbg_p + qrow * Lp + jb;
+      if (a.dbg_p) {
+        float* dp = a.dbg_p + qrow * Lp + jb;
         *(float4*)dp = make_float4(pv[0], pv[1], pv[2], pv[3]);
         *(float4*)(dp + 4) = make_float4(pv[4], pv[5], pv[6], pv[7]);
       }
       // l partial: sum over the 32 threads of this row (half a wave)
 #pragma unroll
       for (int off = 16; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off, 32);
-      if (sbk == 0) lpart[qrow * nchunk + chunk] = lsum;
+      if (sbk == 0) a.lpart[qrow * nchunk + chunk] = lsum;
     }
   }
   wait_vmcnt<0>();   // this wave's value copies have landed
@@ -929,44 +1010,78 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) k
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int row = 4 * g + i;
-      if (row < G) opart[(((int64_t)b * Hq + (int64_t)h * G + row) * nchunk + chunk) * d + ch] = acc[t][i];
+      if (row < G) a.opart[((qrow0 + row) * nchunk + chunk) * d + ch] = acc[t][i];
     }
   }
+
 }
 
-// grid (B * Hq), block d: O = sum_chunks O_part / sum_chunks l_part, rounded to bf16 (rows whose
-// pos is outside [0, max_pos]: zeros). Four independent partial sums keep the chunk loads in
-// flight together.
-__global__ void k_decode_combine(const float* __restrict__ lpart, const float* __restrict__ opart,
-                                 const int32_t* __restrict__ pos, int64_t max_pos, int Hq, int nchunk, int d,
-                                 uint16_t* __restrict__ o, float* __restrict__ dbg_l) {
-  const int64_t qrow = blockIdx.x;
-  const int b = (int)(qrow / Hq), c = threadIdx.x;
-  const int p = pos[b];
-  if (p < 0 || p > max_pos) {
-    o[qrow * d + c] = 0;
-    return;
-  }
+// The combine pass, workgroup vb of ceil(B Hq / 2), 256 threads: thread t owns channel t % 128 of
+// query row 2 vb + t / 128 and adds the chunk partials in chunk order (eight loads in flight):
+// O = sum_chunks O_part / sum_chunks l_part, rounded to bf16 (rows whose pos is outside
+// [0, max_pos]: zeros, written by the pv pass).
+__device__ __forceinline__ void dec_combine(const DecOps& a, int vb) {
+  constexpr int d = 128;
+  const int64_t qrow = (int64_t)vb * 2 + (threadIdx.x >> 7);
+  if (qrow >= (int64_t)a.B * a.Hq) return;
+  const int b = (int)(qrow / a.Hq), c = threadIdx.x & (d - 1);
+  const int p = a.pos[b];
+  if (p < 0 || p > a.max_pos) return;
   const int n = p / DCH + 1;
-  const float* lp = lpart + qrow * nchunk;
-  const float* op = opart + qrow * nchunk * d + c;
-  float l4[4] = {0.f, 0.f, 0.f, 0.f}, a4[4] = {0.f, 0.f, 0.f, 0.f};
+  const float* lp = a.lpart + qrow * a.nchunk;
+  const float* op = a.opart + qrow * a.nchunk * d + c;
+  float l = 0.f, acc = 0.f;
   int k = 0;
-  for (; k + 4 <= n; k += 4) {
+  for (; k + 8 <= n; k += 8) {
+    float lv[8], ov[8];
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      l4[u] += lp[k + u];
-      a4[u] += op[(int64_t)(k + u) * d];
+    for (int u = 0; u < 8; u++) {
+      lv[u] = lp[k + u];
+      ov[u] = op[(int64_t)(k + u) * d];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      l += lv[u];
+      acc += ov[u];
     }
   }
   for (; k < n; k++) {
-    l4[0] += lp[k];
-    a4[0] += op[(int64_t)k * d];
+    l += lp[k];
+    acc += op[(int64_t)k * d];
   }
-  const float l = (l4[0] + l4[1]) + (l4[2] + l4[3]);
-  const float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-  o[qrow * d + c] = f32_to_bf16_rne(__fdiv_rn(acc, l));
-  if (dbg_l && c == 0) dbg_l[qrow] = l;
+  a.o[qrow * d + c] = f32_to_bf16_rne(__fdiv_rn(acc, l));
+  if (a.dbg_l && c == 0) a.dbg_l[qrow] = l;
+}
+
+// Weight-stream workgroups inside a decode launch: 16 DEC_GV_RG output columns each, DEC_GV_D K steps
+// of operands in flight per wave (registers are shared with the pass they run beside).
+constexpr int DEC_GV_RG = 2, DEC_GV_D = 2;
+
+// grid 8 nchunk ceil(B Hkv / 8) + ngv, block 256, dynamic LDS max(decode_pv_lds_bytes(G),
+// gv_lds_bytes): workgroups [0, npv) run the pv pass, the rest (ngv of them; GV = 0: none) stream the
+// linear's weights (GV = 1: MXFP4 image, 2: E4M3 image) into bf16 C.
+template <int GV>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) k_decode_pv(DecOps a, int npv, GvOps gv) {
+  extern __shared__ __align__(16) uint8_t dsm[];
+  const int vb = (int)blockIdx.x;
+  if (GV && vb >= npv) {
+    gemv_block<GV == 1, 1, DEC_GV_RG, DEC_GV_D>(gv, vb - npv, (float*)dsm);
+    return;
+  }
+  dec_pv(a, vb, dsm);
+}
+
+// grid ncb + ngv, block 256, dynamic LDS gv_lds_bytes when GV: workgroups [0, ncb) add the chunk
+// partials into O (ncb = ceil(B Hq / 2)), the rest stream the linear's weights as in k_decode_pv.
+template <int GV>
+__global__ void __launch_bounds__(256) k_decode_combine(DecOps a, int ncb, GvOps gv) {
+  extern __shared__ __align__(16) uint8_t dsm[];
+  const int vb = (int)blockIdx.x;
+  if (GV && vb >= ncb) {
+    gemv_block<GV == 1, 1, DEC_GV_RG, DEC_GV_D>(gv, vb - ncb, (float*)dsm);
+    return;
+  }
+  dec_combine(a, vb);
 }
 
 // ------------------------------------------------------------------ host orchestration
@@ -1109,10 +1224,13 @@ hipError_t kv_cache_prefill_run(const mix_kv_cache_t* c, int64_t b, const void* 
 }
 
 struct DecodeWs {
-  size_t s, pmax, pc, ps, lpart, opart, total;
+  size_t s, pmax, pc, ps, lpart, opart, a_img, total;
 };
 
-static DecodeWs decode_layout(int64_t B, int64_t Hq, int64_t d, int64_t max_pos, int64_t* Lp_out, int* nchunk_out) {
+// Workspace of a decode step: S, chunk maxima, debug copies of P^, the chunk partials and, for the
+// full step (K > 0), the A image of the linear's B x K activations.
+static DecodeWs decode_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos, int64_t K,
+                              int64_t* Lp_out, int* nchunk_out) {
   const int nchunk = (int)((max_pos + 1 + DCH - 1) / DCH);
   const int64_t Lp = (int64_t)nchunk * DCH;
   DecodeWs w{};
@@ -1124,54 +1242,113 @@ static DecodeWs decode_layout(int64_t B, int64_t Hq, int64_t d, int64_t max_pos,
   w.ps = take((size_t)B * Hq * (Lp / 32) * 2);
   w.lpart = take((size_t)B * Hq * nchunk * 4);
   w.opart = take((size_t)B * Hq * nchunk * d * 4);
+  w.a_img = take(K > 0 ? f8_a_image_layout(B, K).total : 0);
   w.total = off;
   if (Lp_out) *Lp_out = Lp;
   if (nchunk_out) *nchunk_out = nchunk;
   return w;
 }
 
-size_t attn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t d, int64_t max_pos) {
-  return decode_layout(B, Hq, d, max_pos, nullptr, nullptr).total;
+size_t attn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos) {
+  return decode_layout(B, Hq, Hkv, d, max_pos, 0, nullptr, nullptr).total;
+}
+
+size_t decode_step_ws_bytes(int64_t B, int64_t K, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos) {
+  return decode_layout(B, Hq, Hkv, d, max_pos, K, nullptr, nullptr).total;
+}
+
+// The two decode launches. lin == NULL: attention alone. Otherwise the full step: the scores launch
+// also codes x [B, K] (bf16, row pitch K) into the A image in the workspace, and the pv launch also
+// streams the weights' B image into y [B, N] (bf16, row pitch N).
+struct DecodeLinear {
+  const void* x;
+  int64_t K, N;
+  int b_fp4;
+  const void* b_img;
+  void* y;
+};
+
+static hipError_t decode_run(const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* c,
+                             const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
+                             const mix_attn_debug_t* dbg, const DecodeLinear* lin, hipStream_t s) {
+  const int64_t B = c->B, Hkv = c->Hkv, d = c->d, Lmax = c->Lmax;
+  int64_t Lp;
+  int nchunk;
+  const DecodeWs w = decode_layout(B, Hq, Hkv, d, max_pos, lin ? lin->K : 0, &Lp, &nchunk);
+  uint8_t* base = (uint8_t*)ws;
+  DecOps a{};
+  a.q = (const uint16_t*)q; a.k_new = (const uint16_t*)k_new; a.v_new = (const uint16_t*)v_new; a.mu = mu;
+  a.pos = pos; a.max_pos = max_pos; a.Lmax = Lmax; a.Lp = Lp;
+  a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.B = (int)B; a.nchunk = nchunk;
+  a.kc = c->k_codes; a.ks = c->k_scales; a.vc = c->v_codes; a.vs = c->v_scales; a.stage = (uint16_t*)c->v_stage;
+  a.S = (float*)(base + w.s);
+  a.pmax = (float*)(base + w.pmax);
+  a.lpart = (float*)(base + w.lpart);
+  a.opart = (float*)(base + w.opart);
+  a.scale = (float)(1.0 / sqrt((double)d));
+  a.o = (uint16_t*)o;
+  a.pc = dbg && dbg->p_codes ? base + w.pc : nullptr;
+  a.ps = dbg && dbg->p_shared ? (uint16_t*)(base + w.ps) : nullptr;
+  a.dbg_p = dbg ? dbg->p : nullptr;
+  a.dbg_l = dbg ? dbg->l : nullptr;
+
+  XqOps xq{};
+  GvOps gv{};
+  int nxq = 0, ngv = 0;
+  if (lin) {
+    const F8AImage LA = f8_a_image_layout(B, lin->K);
+    const F8BImage LB = f8_b_image_layout(lin->b_fp4, lin->N, lin->K);
+    uint8_t* aimg = base + w.a_img;
+    xq.x = (const uint16_t*)lin->x; xq.ldx = lin->K; xq.M = (int)B; xq.K = (int)lin->K;
+    xq.a8 = aimg + LA.a8; xq.as_p = aimg + LA.as_p;
+    nxq = (int)((B * (lin->K / 8) + 255) / 256 + 7) / 8 * 8;
+    gv.a8 = aimg + LA.a8; gv.as_p = aimg + LA.as_p;
+    gv.b8 = (const uint8_t*)lin->b_img + LB.b8; gv.bs_v = (const uint8_t*)lin->b_img + LB.bs_v;
+    gv.c = lin->y; gv.ldc = lin->N; gv.M = (int)B; gv.N = (int)lin->N; gv.K = (int)lin->K; gv.tiles_m = 1;
+    ngv = (int)(((lin->N + 15) / 16 + DEC_GV_RG - 1) / DEC_GV_RG);
+  }
+
+  const int bh8 = (int)((B * Hkv + 7) / 8);
+  const int nsc = 8 * (nchunk + 1) * bh8, npv = 8 * nchunk * bh8, ncb = (int)((B * Hq + 1) / 2);
+  hipLaunchKernelGGL(k_decode_scores, dim3((unsigned)(nxq + nsc)), dim3(256), 0, s, a, xq, nxq);
+  HIPCHK(hipGetLastError());
+  const size_t lds_pv = decode_pv_lds_bytes((int)(Hq / Hkv));
+  const size_t lds_gv = gv_lds_bytes<DEC_GV_RG>();
+  // the weight stream runs beside the pv pass (measured: 50 us per workload-5 step, against 55 us
+  // beside the combine, which it then no longer overlaps with the value stream)
+  const int gvk = !lin ? 0 : (lin->b_fp4 ? 1 : 2);
+  const int g2 = gvk, g3 = 0;
+  const size_t l2 = g2 && lds_gv > lds_pv ? lds_gv : lds_pv;
+  const unsigned n2 = (unsigned)(npv + (g2 ? ngv : 0)), n3 = (unsigned)(ncb + (g3 ? ngv : 0));
+  if (g2 == 1) hipLaunchKernelGGL(k_decode_pv<1>, dim3(n2), dim3(256), l2, s, a, npv, gv);
+  else if (g2 == 2) hipLaunchKernelGGL(k_decode_pv<2>, dim3(n2), dim3(256), l2, s, a, npv, gv);
+  else hipLaunchKernelGGL(k_decode_pv<0>, dim3(n2), dim3(256), l2, s, a, npv, gv);
+  HIPCHK(hipGetLastError());
+  if (g3 == 1) hipLaunchKernelGGL(k_decode_combine<1>, dim3(n3), dim3(256), lds_gv, s, a, ncb, gv);
+  else if (g3 == 2) hipLaunchKernelGGL(k_decode_combine<2>, dim3(n3), dim3(256), lds_gv, s, a, ncb, gv);
+  else hipLaunchKernelGGL(k_decode_combine<0>, dim3(n3), dim3(256), 0, s, a, ncb, gv);
+  HIPCHK(hipGetLastError());
+  if (dbg) {
+    if (dbg->s) HIPCHK(hipMemcpyAsync(dbg->s, a.S, (size_t)B * Hq * Lp * 4, hipMemcpyDeviceToDevice, s));
+    if (dbg->p_codes)
+      HIPCHK(hipMemcpyAsync(dbg->p_codes, a.pc, (size_t)B * Hq * Lp / 2, hipMemcpyDeviceToDevice, s));
+    if (dbg->p_shared)
+      HIPCHK(hipMemcpyAsync(dbg->p_shared, a.ps, (size_t)B * Hq * (Lp / 32) * 2, hipMemcpyDeviceToDevice, s));
+  }
+  return hipSuccess;
 }
 
 hipError_t attn_decode_run(const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* c,
                            const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
                            const mix_attn_debug_t* dbg, hipStream_t s) {
-  const int64_t B = c->B, Hkv = c->Hkv, d = c->d, Lmax = c->Lmax;
-  int64_t Lp;
-  int nchunk;
-  DecodeWs w = decode_layout(B, Hq, d, max_pos, &Lp, &nchunk);
-  uint8_t* base = (uint8_t*)ws;
-  float* S = (float*)(base + w.s);
-  float* pmax = (float*)(base + w.pmax);
-  uint8_t* pc = base + w.pc;
-  uint16_t* ps = (uint16_t*)(base + w.ps);
-  float* lpart = (float*)(base + w.lpart);
-  float* opart = (float*)(base + w.opart);
+  return decode_run(q, k_new, v_new, c, pos, max_pos, Hq, mu, o, ws, dbg, nullptr, s);
+}
 
-  const unsigned bh8 = (unsigned)((B * Hkv + 7) / 8);
-  const dim3 grid_qk(8u * (unsigned)(nchunk + 1) * bh8), grid((unsigned)(8 * nchunk) * bh8);
-  hipLaunchKernelGGL(k_decode_qk, grid_qk, dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)k_new,
-                     (const uint16_t*)v_new, mu, pos, max_pos, (int)Hq, (int)Hkv, Lmax, c->k_codes, c->k_scales,
-                     c->v_codes, c->v_scales, (uint16_t*)c->v_stage, Lp, (int)B, nchunk, S, pmax);
-  HIPCHK(hipGetLastError());
-  const float scale = (float)(1.0 / sqrt((double)d));
-  hipLaunchKernelGGL(k_decode_pv, grid, dim3(256), decode_pv_lds_bytes((int)(Hq / Hkv)), s, (const float*)S,
-                     (const float*)pmax,
-                     (const uint8_t*)c->v_codes, (const uint8_t*)c->v_scales, pos, max_pos, (int)Hq, (int)Hkv, Lmax, Lp,
-                     (int)B, nchunk, scale, dbg && dbg->p_codes ? pc : nullptr, dbg && dbg->p_shared ? ps : nullptr,
-                     lpart, opart, dbg ? dbg->p : nullptr);
-  HIPCHK(hipGetLastError());
-  hipLaunchKernelGGL(k_decode_combine, dim3((unsigned)(B * Hq)), dim3((unsigned)d), 0, s, (const float*)lpart,
-                     (const float*)opart, pos, max_pos, (int)Hq, nchunk, (int)d, (uint16_t*)o, dbg ? dbg->l : nullptr);
-  HIPCHK(hipGetLastError());
-  if (dbg) {
-    if (dbg->s) HIPCHK(hipMemcpyAsync(dbg->s, S, (size_t)B * Hq * Lp * 4, hipMemcpyDeviceToDevice, s));
-    if (dbg->p_codes) HIPCHK(hipMemcpyAsync(dbg->p_codes, pc, (size_t)B * Hq * Lp / 2, hipMemcpyDeviceToDevice, s));
-    if (dbg->p_shared)
-      HIPCHK(hipMemcpyAsync(dbg->p_shared, ps, (size_t)B * Hq * (Lp / 32) * 2, hipMemcpyDeviceToDevice, s));
-  }
-  return hipSuccess;
+hipError_t decode_step_run(const void* x, int64_t K, int64_t N, int b_fp4, const void* b_img, void* y, const void* q,
+                           const void* k_new, const void* v_new, const mix_kv_cache_t* c, const int32_t* pos,
+                           int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws, hipStream_t s) {
+  const DecodeLinear lin{x, K, N, b_fp4, b_img, y};
+  return decode_run(q, k_new, v_new, c, pos, max_pos, Hq, mu, o, ws, nullptr, &lin, s);
 }
 
 }  // namespace mix

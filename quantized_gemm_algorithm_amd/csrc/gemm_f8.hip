@@ -38,6 +38,7 @@
 // C[8 (k >> 2) + 4 (l >> 5) + (k & 3)][l & 31].
 #include "common.h"
 #include "f8_image.h"
+#include "gemv_dev.h"
 #include "kernels.h"
 #include "quant_dev.h"
 
@@ -856,9 +857,26 @@ static hipError_t launch_gv_g(const F8Args& f, hipStream_t s) {
   return launch_gv<B_FP4, C_BF16, 8>(f, s);
 }
 
+// M <= 16 as a plain launch of the weight stream (gemv_dev.h): each workgroup owns 16 GV_RG output
+// columns, its four waves split K and keep GV_D steps of operands in flight in registers.
+constexpr int GV_RG = 2, GV_D = 4;
+
+template <int B_FP4, int C_BF16>
+__global__ void __launch_bounds__(256) k_gemv_rs(GvOps g) {
+  __shared__ __align__(16) float red[gv_lds_bytes<GV_RG>() / 4];
+  gemv_block<B_FP4, C_BF16, GV_RG, GV_D>(g, (int)blockIdx.x, red);
+}
+
 static hipError_t launch_gemv_f8(int b_fp4, int c_bf16, const F8Args& f, hipStream_t s) {
-  if (b_fp4) return c_bf16 ? launch_gv_g<1, 1>(f, s) : launch_gv_g<1, 0>(f, s);
-  return c_bf16 ? launch_gv_g<0, 1>(f, s) : launch_gv_g<0, 0>(f, s);
+  GvOps g{};
+  g.a8 = f.a8; g.as_p = f.as_p; g.b8 = f.b; g.bs_v = f.bs_v;
+  g.c = f.c; g.ldc = f.ldc; g.M = f.M; g.N = f.N; g.K = f.K; g.tiles_m = (f.M + FT - 1) / FT;
+  const dim3 grid((unsigned)(((f.N + 15) / 16 + GV_RG - 1) / GV_RG));
+#define GVL(F, C) hipLaunchKernelGGL((k_gemv_rs<F, C>), grid, dim3(256), 0, s, g)
+  if (b_fp4) { if (c_bf16) GVL(1, 1); else GVL(1, 0); }
+  else { if (c_bf16) GVL(0, 1); else GVL(0, 0); }
+#undef GVL
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const void* b_img, int64_t M, int64_t N,

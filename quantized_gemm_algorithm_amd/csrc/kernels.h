@@ -83,7 +83,13 @@ hipError_t attn_prefill_run(const void* q, const void* k, const void* v, int64_t
                             hipStream_t s);
 hipError_t kv_cache_prefill_run(const mix_kv_cache_t* c, int64_t b, const void* k, const void* v, int64_t T,
                                 const float* mu, hipStream_t s);
-size_t attn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t d, int64_t max_pos);
+size_t attn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos);
+// the full decode step: the linear x [B, K] -> y [B, N] (bf16, weights as a B image) and the attention
+// step, in the same two launches
+size_t decode_step_ws_bytes(int64_t B, int64_t K, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos);
+hipError_t decode_step_run(const void* x, int64_t K, int64_t N, int b_fp4, const void* b_img, void* y, const void* q,
+                           const void* k_new, const void* v_new, const mix_kv_cache_t* c, const int32_t* pos,
+                           int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws, hipStream_t s);
 hipError_t attn_decode_run(const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* c,
                            const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
                            const mix_attn_debug_t* dbg, hipStream_t s);

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mix_abi_version() == 2
+    assert lib.mix_abi_version() == 3
     for s in range(8):
         assert lib.mix_status_str(s)
     assert lib.mix_status_str(99) == b"unknown status"
@@ -225,3 +225,79 @@ def test_underflow_map_validation(lib):
     assert lib.mix_underflow_map_workspace_bytes(4, 40) == 0
     assert lib.mix_underflow_map_workspace_bytes(1, 32) == 2048 + 1024   # 7 x 32 x 4 rounded to 256
     assert f(None, 0, 4, 0, 0, None, None, None, None, 0, None) == MIX_OK
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("k_codes", P), ("k_scales", P), ("v_codes", P), ("v_scales", P), ("v_stage", P),
+                ("B", ctypes.c_int64), ("Lmax", ctypes.c_int64), ("Hkv", ctypes.c_int64), ("d", ctypes.c_int64)]
+
+
+def _cache(B=16, Lmax=8192, Hkv=4, d=128):
+    return _Cache(FAKE, FAKE, FAKE, FAKE, FAKE, B, Lmax, Hkv, d)
+
+
+def test_decode_validation(lib):
+    W = 1 << 30
+    c = _cache()
+    ref = ctypes.byref(c)
+    f = lib.mix_attn_decode
+    # (q, k_new, v_new, cache, pos, max_pos, Hq, mu, o, ws, ws_bytes, dbg, stream)
+    assert f(FAKE, FAKE, FAKE, ref, FAKE, 8191, 30, FAKE, FAKE, FAKE, W, None, None) == MIX_E_SHAPE
+    assert f(FAKE, FAKE, FAKE, ref, FAKE, 8192, 28, FAKE, FAKE, FAKE, W, None, None) == MIX_E_SHAPE
+    assert f(FAKE, FAKE, FAKE, ref, FAKE, 8191, 68, FAKE, FAKE, FAKE, W, None, None) == MIX_E_UNSUPPORTED
+    assert f(None, FAKE, FAKE, ref, FAKE, 8191, 28, FAKE, FAKE, FAKE, W, None, None) == MIX_E_NULL
+    assert f(FAKE, FAKE, FAKE, ref, FAKE, 8191, 28, FAKE, FAKE, P(0x10010), W, None, None) == MIX_E_ALIGN
+    need = lib.mix_attn_decode_workspace_bytes(16, 28, 4, 128, 8191)
+    assert need > 16 * 28 * 8192 * 4   # at least S
+    assert f(FAKE, FAKE, FAKE, ref, FAKE, 8191, 28, FAKE, FAKE, FAKE, need - 1, None, None) == MIX_E_WORKSPACE
+    assert lib.mix_attn_decode_workspace_bytes(16, 28, 0, 128, 8191) == 0
+    c64 = _cache(d=64)
+    assert f(FAKE, FAKE, FAKE, ctypes.byref(c64), FAKE, 8191, 28, FAKE, FAKE, FAKE, W, None, None) == MIX_E_UNSUPPORTED
+
+
+def test_decode_step_validation(lib):
+    W = 1 << 30
+    c = _cache()
+    ref = ctypes.byref(c)
+    f = lib.mix_decode_step
+    # (x, K, N, b_fmt, b_img, y, q, k_new, v_new, cache, pos, max_pos, Hq, mu, o, ws, ws_bytes, stream)
+    args = [FAKE, 3584, 18944, 1, FAKE, FAKE, FAKE, FAKE, FAKE, ref, FAKE, 8191, 28, FAKE, FAKE, FAKE, W, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, name in enumerate(("x", "K", "N", "b_fmt", "b_img", "y", "q", "k_new", "v_new", "cache", "pos",
+                                  "max_pos", "Hq", "mu", "o", "ws", "ws_bytes")):
+            if name in kw:
+                a[i] = kw[name]
+        return f(*a)
+
+    need = lib.mix_decode_step_workspace_bytes(16, 3584, 28, 4, 128, 8191)
+    assert need == lib.mix_attn_decode_workspace_bytes(16, 28, 4, 128, 8191) + \
+        lib.mix_gemm_a_image_bytes(16, 3584)   # plus the activations' A image
+    assert lib.mix_decode_step_workspace_bytes(16, 0, 28, 4, 128, 8191) == 0
+    assert call(b_fmt=7) == MIX_E_ENUM
+    assert call(K=3600) == MIX_E_SHAPE
+    assert call(N=0) == MIX_E_SHAPE
+    assert call(Hq=30) == MIX_E_SHAPE
+    assert call(max_pos=8192) == MIX_E_SHAPE
+    assert call(x=None) == MIX_E_NULL
+    assert call(b_img=None) == MIX_E_NULL
+    assert call(y=None) == MIX_E_NULL
+    assert call(b_img=P(0x10010)) == MIX_E_ALIGN
+    assert call(x=MISALIGNED) == MIX_E_ALIGN
+    assert call(ws=P(0x10010)) == MIX_E_ALIGN
+    assert call(ws_bytes=need - 1) == MIX_E_WORKSPACE
+    big = _cache(B=17)
+    assert call(cache=ctypes.byref(big)) == MIX_E_UNSUPPORTED
+    c64 = _cache(d=64)
+    assert call(cache=ctypes.byref(c64)) == MIX_E_UNSUPPORTED
+
+
+def test_decode_output_alignment(lib):
+    c = _cache()
+    ref = ctypes.byref(c)
+    W = 1 << 30
+    assert lib.mix_attn_decode(FAKE, FAKE, FAKE, ref, FAKE, 8191, 28, FAKE, P(0x10004), FAKE, W, None, None) == \
+        MIX_E_ALIGN
+    assert lib.mix_decode_step(FAKE, 3584, 18944, 1, FAKE, FAKE, FAKE, FAKE, FAKE, ref, FAKE, 8191, 28, FAKE,
+                               P(0x10004), FAKE, W, None) == MIX_E_ALIGN

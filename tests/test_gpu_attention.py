@@ -176,7 +176,7 @@ def _decode_case(B, Hq, Hkv, L_each, seed=5):
                 cache=cache, Lmax=Lmax, d=d)
 
 
-def _check_decode(r, Hq, Hkv, batch_rows=None):
+def _check_decode(r, Hq, Hkv, batch_rows=None, e2e_rows=None):
     d = r["d"]
     G = Hq // Hkv
     pos, mu = r["pos"], r["mu"]
@@ -223,6 +223,8 @@ def _check_decode(r, Hq, Hkv, batch_rows=None):
             absb = np.abs(vd) @ np.abs(pd)
             assert_bf16_matches(r["o"][b, h], num / lg, absb / lg + 2.0**-23 * np.abs(num / lg), f"O b{b} h{h}")
         # end to end (unpinned): the independent oracle
+        if e2e_rows is not None and b not in e2e_rows:
+            continue
         full = attn_decode_ref(r["qd"][b][None], r["kh"][b][None, :L], r["vh"][b][None, :L], mu[b][None],
                                np.array([L]))
         o_ind = (np.stack(full["o_bf16"][0]).astype(np.uint32) << 16).view(np.float32)
@@ -257,8 +259,9 @@ def test_decode_rejects_unsupported_and_skips_bad_rows():
     assert torch.all(o[1].float() == 1.0)
 
 
-def test_decode_workload5_full_size_sampled():
-    # batch 16, 28 query / 4 KV heads, d = 128, 8191 prefill tokens per row, the new token at 8191
+def test_decode_workload5_full_size():
+    # batch 16, 28 query / 4 KV heads, d = 128, 8191 prefill tokens per row, the new token at 8191:
+    # every stage of every batch row and head (the end-to-end comparison on two rows)
     q = _lib()
     g = synth.decode_step(with_weights=False)
     B, L = 16, 8192
@@ -277,7 +280,7 @@ def test_decode_workload5_full_size_sampled():
     torch.cuda.synchronize()
     r = dict(qd=g["q"], kh=g["k_hist"], vh=g["v_hist"], pos=np.full(B, L - 1, np.int32), mu=host(mu_all), o=host(o),
              dbg={k: host(v) for k, v in dbg.items()}, cache=cache, Lmax=L, d=d)
-    _check_decode(r, Hq, Hkv, batch_rows=[0, 15])
+    _check_decode(r, Hq, Hkv, e2e_rows=[0, 15])
 
 
 def test_decode_linear_workload5_sampled():
