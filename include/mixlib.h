@@ -367,6 +367,21 @@ mix_status_t mix_decode_step(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt
                              const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
                              size_t ws_bytes, void* stream);
 
+/*
+ * mix_decode_step for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments and results without ws and
+ * ws_bytes. The workspace is a file-scope device array of mix_decode_step_static_max_bytes() bytes
+ * (32 MiB) that the library holds on each device it runs on until the process ends; a shape whose
+ * mix_decode_step_workspace_bytes exceeds it returns MIX_E_WORKSPACE. The call allocates nothing and
+ * needs no cleared memory. Every call on a device shares that device's array, so calls that overlap
+ * on one device (different streams, or host threads) race; serialise them.
+ */
+size_t mix_decode_step_static_max_bytes(void);
+mix_status_t mix_decode_step_static(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt, const void* b_img, void* y,
+                                    const void* q, const void* k_new, const void* v_new,
+                                    const mix_kv_cache_t* cache, const int32_t* pos, int64_t max_pos, int64_t Hq,
+                                    const float* mu, void* o, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -476,12 +476,10 @@ size_t mix_decode_step_workspace_bytes(int64_t B, int64_t K, int64_t Hq, int64_t
   return mix::decode_step_ws_bytes(B, K, Hq, Hkv, d, max_pos);
 }
 
-mix_status_t mix_decode_step(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt, const void* b_img, void* y,
-                             const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* cache,
-                             const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
-                             size_t ws_bytes, void* stream) {
-  g_err.clear();
-  const char* fn = "mix_decode_step";
+static mix_status_t check_decode_step(const char* fn, const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt,
+                                      const void* b_img, void* y, const void* q, const void* k_new,
+                                      const void* v_new, const mix_kv_cache_t* cache, const int32_t* pos,
+                                      int64_t max_pos, int64_t Hq, const float* mu, void* o) {
   if (mix_status_t st = check_cache(fn, cache)) return st;
   if (!mx_known(b_fmt)) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
   if (Hq <= 0 || Hq % cache->Hkv) return fail(MIX_E_SHAPE, "%s: Hq must be a positive multiple of Hkv", fn);
@@ -493,14 +491,48 @@ mix_status_t mix_decode_step(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt
     return fail(MIX_E_SHAPE, "%s: K=%lld must be a positive multiple of 128 and N=%lld positive", fn, (long long)K, (long long)N);
   if (!mix::gemm_f8_offsets_ok(1, N, K) || cache->B * K >= ((int64_t)1 << 31))
     return fail(MIX_E_UNSUPPORTED, "%s: an operand image of %lld x %lld reaches 2^31 bytes", fn, (long long)N, (long long)K);
-  if (!x || !b_img || !y || !q || !k_new || !v_new || !pos || !mu || !o || !ws) return fail(MIX_E_NULL, "%s: NULL pointer", fn);
-  if (((uintptr_t)ws & 255u) || ((uintptr_t)b_img & 255u) || !aligned16(x) || !aligned16(q) || ((uintptr_t)y & 1u) ||
-      ((uintptr_t)o & 7u) || ((uintptr_t)pos & 3u) || ((uintptr_t)mu & 3u))
-    return fail(MIX_E_ALIGN, "%s: misaligned argument (ws and b_img 256-byte, x and q 16-byte, o 8-byte)", fn);
+  if (!x || !b_img || !y || !q || !k_new || !v_new || !pos || !mu || !o) return fail(MIX_E_NULL, "%s: NULL pointer", fn);
+  if (((uintptr_t)b_img & 255u) || !aligned16(x) || !aligned16(q) || ((uintptr_t)y & 1u) || ((uintptr_t)o & 7u) ||
+      ((uintptr_t)pos & 3u) || ((uintptr_t)mu & 3u))
+    return fail(MIX_E_ALIGN, "%s: misaligned argument (b_img 256-byte, x and q 16-byte, o 8-byte)", fn);
+  return MIX_OK;
+}
+
+mix_status_t mix_decode_step(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt, const void* b_img, void* y,
+                             const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* cache,
+                             const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
+                             size_t ws_bytes, void* stream) {
+  g_err.clear();
+  const char* fn = "mix_decode_step";
+  if (mix_status_t st = check_decode_step(fn, x, K, N, b_fmt, b_img, y, q, k_new, v_new, cache, pos, max_pos, Hq, mu,
+                                          o))
+    return st;
+  if (!ws) return fail(MIX_E_NULL, "%s: ws is NULL", fn);
+  if ((uintptr_t)ws & 255u) return fail(MIX_E_ALIGN, "%s: ws must be 256-byte aligned", fn);
   const size_t need = mix::decode_step_ws_bytes(cache->B, K, Hq, cache->Hkv, cache->d, max_pos);
   if (ws_bytes < need) return fail(MIX_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   return hip_status(mix::decode_step_run(x, K, N, b_fmt == MX_FP4, b_img, y, q, k_new, v_new, cache, pos, max_pos, Hq,
                                          mu, o, ws, (hipStream_t)stream),
+                    fn);
+}
+
+size_t mix_decode_step_static_max_bytes(void) { return mix::DECODE_SCRATCH_BYTES; }
+
+mix_status_t mix_decode_step_static(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt, const void* b_img, void* y,
+                                    const void* q, const void* k_new, const void* v_new,
+                                    const mix_kv_cache_t* cache, const int32_t* pos, int64_t max_pos, int64_t Hq,
+                                    const float* mu, void* o, void* stream) {
+  g_err.clear();
+  const char* fn = "mix_decode_step_static";
+  if (mix_status_t st = check_decode_step(fn, x, K, N, b_fmt, b_img, y, q, k_new, v_new, cache, pos, max_pos, Hq, mu,
+                                          o))
+    return st;
+  const size_t need = mix::decode_step_ws_bytes(cache->B, K, Hq, cache->Hkv, cache->d, max_pos);
+  if (need > mix::DECODE_SCRATCH_BYTES)
+    return fail(MIX_E_WORKSPACE, "%s: this shape needs %zu bytes of scratch, above the library's %zu", fn, need,
+                mix::DECODE_SCRATCH_BYTES);
+  return hip_status(mix::decode_step_static_run(x, K, N, b_fmt == MX_FP4, b_img, y, q, k_new, v_new, cache, pos,
+                                                max_pos, Hq, mu, o, (hipStream_t)stream),
                     fn);
 }
 

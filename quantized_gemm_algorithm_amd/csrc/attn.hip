@@ -20,6 +20,7 @@
 // Decode keeps the exact global row max with two passes over the keys: pass 1 (scores) computes S
 // for 256-key chunks on the MFMA and per-chunk maxima; pass 2 (pv) takes the global max, forms p
 // and P^ for its chunk and multiplies by V^ on the MFMA; a third launch sums the chunk partials.
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/mixlib.h"
@@ -1349,6 +1350,41 @@ hipError_t decode_step_run(const void* x, int64_t K, int64_t N, int b_fp4, const
                            int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws, hipStream_t s) {
   const DecodeLinear lin{x, K, N, b_fp4, b_img, y};
   return decode_run(q, k_new, v_new, c, pos, max_pos, Hq, mu, o, ws, nullptr, &lin, s);
+}
+
+// ------------------------------------------------------------------ decode step without allocation
+
+// The decode step's workspace as a file-scope device array, for callers that cannot allocate (code
+// under graph capture, serving loops that forbid allocation). Each device that runs the library
+// holds its own copy until the process ends; calls on one device share it and race if they overlap.
+// Nothing in it needs to start at zero: every byte a launch reads was written earlier in the step.
+static __device__ __align__(256) uint8_t scratch[DECODE_SCRATCH_BYTES];
+
+// The device address of `scratch` on the current device, looked up once per device (the host-side
+// name is only a stand-in, never a device address).
+static hipError_t decode_scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {nullptr};
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
+
+hipError_t decode_step_static_run(const void* x, int64_t K, int64_t N, int b_fp4, const void* b_img, void* y,
+                                  const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* c,
+                                  const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o,
+                                  hipStream_t s) {
+  void* ws = nullptr;
+  HIPCHK(decode_scratch_ptr(&ws));
+  return decode_step_run(x, K, N, b_fp4, b_img, y, q, k_new, v_new, c, pos, max_pos, Hq, mu, o, ws, s);
 }
 
 }  // namespace mix
