@@ -13,8 +13,10 @@ against the dense block-scaled FP8 MFMA peak; per-kernel times come from HIP eve
 the stream the kernels run on. ``cpu_baseline`` times the CPU oracle on a bounded sample of the
 same workload.
 
-Other workloads (``--workload``) print the same line shape for the vision-encoder linear, the
-prefill attention and the decode step.
+By default the same line also carries the other workloads as sections (``vision_linear``,
+``attention_prefill``, ``decode``), each with its kernel time, algorithmic work, roofline fraction
+and its own ``cpu_baseline``, and ``streaming_ceiling``: what this GPU reads and copies in practice,
+measured in the same run. ``--workload`` prints one workload's line alone.
 """
 import argparse
 import json
@@ -27,6 +29,8 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense, block-scaled FP8 (E4M3 A operand sets the rate)
+TRAFFIC_SOURCE = ("stored figure: profiles/traffic.json, from rocprofv3 FETCH_SIZE and WRITE_SIZE runs scaled by a "
+                  "plain copy's counts; null once the kernel's sources differ from those it was taken on")
 
 
 def parse():
@@ -36,8 +40,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="run the step untimed for this long before the warm-up steps (clock ramp of an idle GPU)")
-    ap.add_argument("--workload", default="prefill_linear",
-                    choices=["prefill_linear", "vision_linear", "attention_prefill", "decode"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "prefill_linear", "vision_linear", "attention_prefill", "decode"],
+                    help="all (default): the prefill-linear line with the other workloads as sections")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -194,17 +199,25 @@ def bench_linear(torch, q, args, which):
     ms_step = total_ms / args.steps
 
     # the quantizer's throughput: back-to-back launches on rotating inputs between two events (the
-    # in-step events above also hold the dispatch gap around each event)
+    # in-step events above also hold the dispatch gap around each event); the codes-only kernel (the
+    # quantizer as the pages define it) and the step's variant that also writes the A image
     qrep = 20
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(qrep):
-        ac, as_, aimg = bufs[i % 2]
-        q.mix_quantize_gemm(xs[i % nrot], a_fmt, codes=ac, shared=as_, image=aimg)
-    b.record()
-    torch.cuda.synchronize()
-    q_stream_ms = a.elapsed_time(b) / qrep
+
+    def q_stream(fn):
+        for i in range(qrep):
+            fn(i)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(qrep):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / qrep
+
+    q_stream_ms = q_stream(lambda i: q.mix_quantize_gemm(xs[i % nrot], a_fmt, codes=bufs[i % 2][0],
+                                                         shared=bufs[i % 2][1], image=bufs[i % 2][2]))
+    q_codes_ms = q_stream(lambda i: q.mix_quantize(xs[i % nrot], a_fmt, codes=bufs[i % 2][0], shared=bufs[i % 2][1]))
 
     # weight quantizer, timed on its own (offline in deployment)
     wq_ms = []
@@ -290,8 +303,9 @@ def bench_linear(torch, q, args, which):
     sh_bytes = 2 if a_fmt == "4.5b" else 1
     tiles_m, tiles_n = -(-M // 256), -(-N // 256)
     a_img_bytes = M * K + (K // 128) * tiles_m * 1024
-    # quantizer: bf16 in; codes + shared fields + the A image out
-    q_bytes = M * K * 2 + M * K // 2 + M * (K // 32) * sh_bytes + a_img_bytes
+    # quantizer: bf16 in; codes + shared fields out (the algorithmic bytes), + the A image (the step's variant)
+    q_codes_bytes = M * K * 2 + M * K // 2 + M * (K // 32) * sh_bytes
+    q_bytes = q_codes_bytes + a_img_bytes
     wq_bytes = N * K * 2 + N * K // 2 + N * (K // 32)
     b_bytes = (N * K // 2 if b_fmt == "fp4" else N * K) + (K // 128) * tiles_n * 1024
     gemm_bytes = a_img_bytes + b_bytes + M * N * 2  # each operand once + C
@@ -308,14 +322,23 @@ def bench_linear(torch, q, args, which):
         "config": {"workload": wl, "M": M, "K": K, "N": N, "a_format": "MiX-" + a_fmt,
                    "b_format": "MX" + b_fmt.upper(), "out": "bf16"},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gemm_tflops / FP8_MFMA_PEAK_TFLOPS, "traffic": measured_traffic(which), "kernel": "k_gemm_f8",
+                     "frac": gemm_tflops / FP8_MFMA_PEAK_TFLOPS, "traffic": measured_traffic(which),
+                     "traffic_source": TRAFFIC_SOURCE, "kernel": "k_gemm_f8",
                      "kernel_ms": g_ms, "algorithmic_flops": flops, "operand_bytes": gemm_bytes},
-        "quantizer": {"kernel": "k_mix_quantize (codes + A image)", "ms": q_stream_ms,
-                      "GB/s": q_bytes / (q_stream_ms * 1e-3) / 1e9,
-                      "frac_hbm": q_bytes / (q_stream_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": q_bytes,
+        "quantizer": {"kernel": "k_mix_quantize (codes and shared fields)", "ms": q_codes_ms,
+                      "GB/s": q_codes_bytes / (q_codes_ms * 1e-3) / 1e9,
+                      "frac_hbm": q_codes_bytes / (q_codes_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "algorithmic_bytes": q_codes_bytes,
                       "timing": f"{qrep} back-to-back launches between two HIP events",
-                      "traffic": measured_traffic(which + "_quantizer"),
-                      "in_step_ms": q_ms, "rotating_buffers": nrot},
+                      "rotating_buffers": nrot,
+                      "with_a_image": {"kernel": "k_mix_quantize (codes + the GEMM's A image, the step's variant)",
+                                       "ms": q_stream_ms, "bytes": q_bytes,
+                                       "GB/s": q_bytes / (q_stream_ms * 1e-3) / 1e9,
+                                       "frac_hbm": q_bytes / (q_stream_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                       "frac_hbm_on_algorithmic_bytes":
+                                           q_codes_bytes / (q_stream_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                       "traffic": measured_traffic(which + "_quantizer"),
+                                       "in_step_ms": q_ms}},
         "weight_quantizer": {"kernel": "k_mx_quantize", "ms": wq_ms, "GB/s": wq_bytes / (wq_ms * 1e-3) / 1e9,
                              "frac_hbm": wq_bytes / (wq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": wq_bytes},
         "eq6_valu_gemm": {"kernel": "k_gemm_eq6", "ms": eq6_ms, "TFLOP/s": flops / (eq6_ms * 1e-3) / 1e12},
@@ -458,7 +481,7 @@ def bench_decode(torch, q, args):
                    "d": d, "bytes_per_step": step_bytes, "rotating_sets": nset},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"),
-                     "traffic_source": "profiles/traffic.json (FETCH_SIZE + WRITE_SIZE runs), null once the sources change",
+                     "traffic_source": TRAFFIC_SOURCE,
                      "kernel": "mix_decode_step (k_decode_scores + k_decode_pv)",
                      "kernel_ms": ms_step, "timing": f"{args.steps} graph replays between two HIP events",
                      "algorithmic_bytes": step_bytes},
@@ -545,10 +568,33 @@ def bench_attention(torch, q, args):
                    "causal": True, "workspace_bytes": wsb},
         "roofline": {"bound": "mfma", "achieved": tf, "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / FP8_MFMA_PEAK_TFLOPS, "traffic": measured_traffic("attention_prefill"),
+                     "traffic_source": TRAFFIC_SOURCE,
                      "kernel": "mix_attn_prefill (all kernels of the call)", "kernel_ms": ms_step},
     }
     res["underflow_map"] = underflow_section(torch, q, kd.view(T, Hkv * d))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_attention(g, d)
     return res
+
+
+def cpu_baseline_attention(g, d, nrows=64):
+    """The oracle's prefill (K-mean, coding, S, softmax, P coding, O) for every head over the last
+    nrows query rows (which see the most keys); credited with their causal-exact flops."""
+    import oracle.attention as oa
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    T, Hq, _ = g["q"].shape
+    rows = np.arange(T - nrows, T)
+    t0 = time.perf_counter()
+    oa.attn_prefill_ref(g["q"], g["k"], g["v"], "bf16", causal=True, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 2 * 2.0 * d * Hq * float(np.sum(rows + 1))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"prefill attention: query rows {T - nrows}..{T - 1} of all {Hq} heads against all keys (the "
+                      f"oracle codes the full K and V itself), {dt:.1f} s; credited with those rows' causal flops"}
 
 
 def underflow_section(torch, q, k2d):
@@ -579,6 +625,43 @@ def underflow_section(torch, q, k2d):
     out["timing"] = f"{reps} back-to-back calls between two HIP events"
     out["read_GB/s"] = nbytes / (ms * 1e-3) / 1e9
     return out
+
+
+def streaming_ceiling(torch):
+    """What this GPU streams in practice, measured in the same run: a plain read (a sum over 1 GiB
+    of int64) and a device-to-device copy (1 GiB each way), each the best of 5."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    s64 = src.view(torch.int64)
+    torch.cuda.synchronize()
+
+    def best(fn):
+        ts = []
+        for _ in range(6):
+            a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+            a.record(); fn(); b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return min(ts[1:])
+
+    read_ms = best(lambda: s64.sum())
+    copy_ms = best(lambda: dst.copy_(src))
+    out = {"read_GB/s": n / (read_ms * 1e-3) / 1e9, "copy_GB/s": 2 * n / (copy_ms * 1e-3) / 1e9,
+           "what": "torch int64 sum over 1 GiB (read) and a 1 GiB device copy (read + write), best of 5"}
+    out["read_frac_hbm"] = out["read_GB/s"] / HBM_PEAK_GBS
+    out["copy_frac_hbm"] = out["copy_GB/s"] / HBM_PEAK_GBS
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def section(res):
+    """A workload's result as a section of the default line (the contract keys dropped)."""
+    keep = {k: v for k, v in res.items() if k not in ("n_gpus", "steps", "warmup", "settle_ms", "higher_is_better",
+                                                      "scaling", "vs_baseline", "data")}
+    return keep
 
 
 def calibrate_copy(torch):
@@ -661,8 +744,29 @@ def main():
         res = bench_linear(torch, q, args, args.workload)
     elif args.workload == "decode":
         res = bench_decode(torch, q, args)
-    else:
+    elif args.workload == "attention_prefill":
         res = bench_attention(torch, q, args)
+    else:
+        # the headline workload's line, then the other workloads as sections of it, then what this GPU
+        # streams in practice (the ceiling the HBM-bound kernels are compared with besides 8 TB/s)
+        res = bench_linear(torch, q, args, "prefill_linear")
+        log("prefill_linear done")
+        torch.cuda.empty_cache()
+        res["vision_linear"] = section(bench_linear(torch, q, args, "vision_linear"))
+        log("vision_linear done")
+        torch.cuda.empty_cache()
+        res["attention_prefill"] = section(bench_attention(torch, q, args))
+        log("attention_prefill done")
+        torch.cuda.empty_cache()
+        res["decode"] = section(bench_decode(torch, q, args))
+        log("decode done")
+        torch.cuda.empty_cache()
+        ceil = streaming_ceiling(torch)
+        qz = res["quantizer"]
+        ceil["quantizer_frac_of_copy"] = qz["GB/s"] / ceil["copy_GB/s"]
+        ceil["quantizer_with_image_frac_of_copy"] = qz["with_a_image"]["GB/s"] / ceil["copy_GB/s"]
+        ceil["decode_frac_of_read"] = res["decode"]["value"] / ceil["read_GB/s"]
+        res["streaming_ceiling"] = ceil
     print(json.dumps(res))
 
 

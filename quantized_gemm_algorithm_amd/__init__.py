@@ -96,14 +96,19 @@ def mix_quantize(x, fmt="4.5b", codes=None, shared=None):
     return codes, shared
 
 
-def mx_quantize(x, fmt="fp4", mu=None):
-    """MX-quantize rows of x [rows, cols] (optionally fp32(x - mu)). Returns (codes, scales uint8)."""
-    _need_cuda(x, mu)
+def mx_quantize(x, fmt="fp4", mu=None, codes=None, scales=None):
+    """MX-quantize rows of x [rows, cols] (optionally fp32(x - mu)). Returns (codes, scales uint8);
+    ``codes``/``scales`` may be passed to write into existing dense tensors of those shapes."""
+    _need_cuda(x, mu, codes, scales)
     rows, cols, ld = _matrix(x, "x")
     if mu is not None and (mu.dtype != torch.float32 or mu.numel() != cols or not mu.is_contiguous()):
         raise MixError("mu must be a contiguous float32 tensor with one value per column")
-    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((rows, cols // MX_BLOCK[fmt]), dtype=torch.uint8, device=x.device)
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // MX_BLOCK[fmt]), dtype=torch.uint8, device=x.device)
+    _dense(codes, (rows, cols // 2), torch.uint8, "codes")
+    _dense(scales, (rows, cols // MX_BLOCK[fmt]), torch.uint8, "scales")
     check(_lib_().mx_quantize(MX_FMT[fmt], _p(x), DTYPE[x.dtype], rows, cols, ld, _p(mu), _p(codes), _p(scales),
                               _stream()), "mx_quantize")
     return codes, scales
@@ -378,7 +383,7 @@ def _debug_struct(d):
     return st, ctypes.byref(st)
 
 
-def mix_attn_prefill(q, k, v, causal=True, debug=False, workspace=None):
+def mix_attn_prefill(q, k, v, causal=True, debug=False, workspace=None, o=None):
     """K-smoothed MiX/MX attention prefill. q [T, Hq, d], k/v [T, Hkv, d] bf16.
 
     Returns (o bf16 [T, Hq, d], mu fp32 [Hkv, d], dbg dict or None). With ``debug`` the dict holds
@@ -396,7 +401,10 @@ def mix_attn_prefill(q, k, v, causal=True, debug=False, workspace=None):
     wsb = lib.mix_attn_prefill_workspace_bytes(T, Hq, Hkv, d)
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=q.device)
-    o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if o is None:
+        o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=q.device)
+    _need_cuda(o)
+    _dense(o, (T, Hq, d), torch.bfloat16, "o")
     mu = torch.empty((Hkv, d), dtype=torch.float32, device=q.device)
     dbg = None
     if debug:

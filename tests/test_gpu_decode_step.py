@@ -1,5 +1,5 @@
 """GPU parity of the whole decode step (mix_decode_step): the linear x -> MiX-4.5b x W-MX -> bf16 and
-the attention step, run together in two launches.
+the attention step, run together in three launches.
 
 The step must equal its parts bit for bit: y equals mix_mx_gemm_images of the quantizer's A image
 (the same per-wave K ranges and sum order), and o equals mix_attn_decode on an identical cache (the
@@ -107,8 +107,12 @@ def test_decode_step_workload5_full_size():
     pos_d = torch.as_tensor(pos, device="cuda")
     y, o = q.mix_decode_step(x, bimg, qd, knew, vnew, c1, pos_d, L - 1, mu)
     o_ref, _ = q.mix_attn_decode(qd, knew, vnew, c2, pos_d, L - 1, mu)
+    # the linear alone through the codes path (quantizer, images, weight stream) gives the same y
+    ac, as_ = q.mix_quantize(x, "4.5b")
+    y_codes = q.mix_mx_gemm(ac, as_, "4.5b", bc, bs, "fp4", out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    assert torch.equal(y.view(torch.int16), y_codes.view(torch.int16))
     _same_cache(c1, c2)
     ac, as_ = o_mix_q(g["x"], "4.5b", "bf16")
     obc, obs = o_mx_q(g["w_t"], "fp4", "bf16")
@@ -118,8 +122,8 @@ def test_decode_step_workload5_full_size():
 
 
 def test_decode_step_repeated_calls_and_bad_rows():
-    # the chunk counters are cleared inside every call: two steps in a row (the second appends the
-    # next token) equal two separate mix_attn_decode calls; a row outside [0, max_pos] gives zeros
+    # no state is carried between calls: two steps in a row (the second appends the next token) equal
+    # two separate mix_attn_decode calls; a row outside [0, max_pos] gives zeros
     q = _q()
     B, Hq, Hkv, d, N, K = 3, 8, 2, 128, 256, 256
     rng = np.random.default_rng(77)

@@ -235,30 +235,39 @@ def _sampled_check(out_bits, ac, as_, a_fmt, bc, bs, b_fmt, nsamp, seed, what):
     assert_bf16_matches(got, ref, bound, what)
 
 
-def test_gemm_workload2_full_size_sampled():
-    # Qwen2-VL-7B-shaped prefill linear: 4096 x 18944 x 3584, MiX-4.5b x MXFP4, bf16 out
+def _full_size_chain(g, a_fmt, b_fmt, what):
+    """The bench's chain at full size -- the quantizer writing codes and the A image in one pass, the
+    weights' MX codes and B image, the product from the images (bf16 C) -- against the oracle: every
+    activation and weight code, and every element of C against the fp64 product of the oracle's codes."""
     q = _lib()
-    g = synth.prefill_linear()
     xd, wd = dev_bf16(g["x"]), dev_bf16(g["w_t"])
-    ac, as_ = q.mix_quantize(xd, "4.5b")
-    bc, bs = q.mx_quantize(wd, "fp4")
-    out = q.mix_mx_gemm(ac, as_, "4.5b", bc, bs, "fp4", out_dtype=torch.bfloat16)
+    ac, as_, aimg = q.mix_quantize_gemm(xd, a_fmt)
+    bc, bs = q.mx_quantize(wd, b_fmt)
+    bimg = q.mx_gemm_b_image(bc, bs, b_fmt)
+    out = q.mix_mx_gemm_images(aimg, bimg, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    # the GPU's codes equal the oracle's (checked in test_gpu_quant); take them as the operands
-    _sampled_check(host(out), host(ac), host(as_), "4.5b", host(bc), host(bs), "fp4", 4096, 2, "workload 2")
+    del xd, wd
+    oac, oas = o_mix_q(g["x"], a_fmt, "bf16")
+    assert_codes_equal(host(ac), oac, f"{what} activation codes")
+    assert_codes_equal(host(as_), oas, f"{what} activation shared fields")
+    obc, obs = o_mx_q(g["w_t"], b_fmt, "bf16")
+    assert_codes_equal(host(bc), obc, f"{what} weight codes")
+    assert_codes_equal(host(bs), obs, f"{what} weight scales")
+    ad, bd = o_mix_deq(oac, oas, a_fmt), o_mx_deq(obc, obs, b_fmt)
+    del oac, oas, obc, obs
+    ref, bound = gemm_ref(ad, bd), gemm_abs_bound(ad, bd)
+    del ad, bd
+    assert_bf16_matches(host(out), ref, bound, f"{what} C, every element")
 
 
-def test_gemm_workload3_full_size_sampled():
-    q = _lib()
-    g = synth.vision_linear()
-    ac, as_ = q.mix_quantize(dev_bf16(g["x"]), "4.25b")
-    bc, bs = q.mx_quantize(dev_bf16(g["w_t"]), "int4")
-    out = q.mix_mx_gemm(ac, as_, "4.25b", bc, bs, "int4", out_dtype=torch.bfloat16)
-    torch.cuda.synchronize()
-    _sampled_check(host(out), host(ac), host(as_), "4.25b", host(bc), host(bs), "int4", 4096, 3, "workload 3")
-    # spot-check the codes against the oracle on a slice
-    want = o_mix_q(g["x"][:512], "4.25b", "bf16")
-    assert_codes_equal(host(ac)[:512], want[0], "x codes slice")
+def test_gemm_workload2_full_size():
+    # Qwen2-VL-7B-shaped prefill linear: 4096 x 18944 x 3584, MiX-4.5b x MXFP4, bf16 out
+    _full_size_chain(synth.prefill_linear(), "4.5b", "fp4", "workload 2")
+
+
+def test_gemm_workload3_full_size():
+    # vision-encoder linear: 16384 x 5120 x 1280, MiX-4.25b x MXINT4, bf16 out
+    _full_size_chain(synth.vision_linear(), "4.25b", "int4", "workload 3")
 
 
 def test_gemm_eq6_workload3_sampled():

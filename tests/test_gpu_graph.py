@@ -68,8 +68,8 @@ def test_decode_step_graph_replays_match_eager():
 
 
 def test_fused_decode_step_graph_replays_match_eager():
-    # the same step through mix_decode_step (two launches whose chunk counters are cleared inside the
-    # step, no memset node): every replay equals the eager call and the separate calls above
+    # the same step through mix_decode_step (three launches, no memset node): every replay equals the
+    # eager call, and its y equals the separate image product
     import quantized_gemm_algorithm_amd as q
     B, K, N, L, Hq, Hkv, d = 4, 512, 1024, 640, 8, 2, 128
     g = synth.decode_step(B=B, K=K, N=N, L=L, Hq=Hq, Hkv=Hkv, d=d, seed_cfg=11)

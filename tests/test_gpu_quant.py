@@ -178,17 +178,6 @@ def test_workload2_prefill_activations_full():
     assert_codes_equal(host(s), want[1], "shared")
 
 
-def test_workload2_weights_sampled_rows():
-    q = _lib()
-    g = synth.prefill_linear()
-    w = g["w_t"]
-    c, s = q.mx_quantize(dev_bf16(w), "fp4")
-    rows = np.random.default_rng(2).choice(w.shape[0], 512, replace=False)
-    want = o_mx_q(w[rows], "fp4", "bf16")
-    assert_codes_equal(host(c)[rows], want[0], "codes")
-    assert_codes_equal(host(s)[rows], want[1], "scales")
-
-
 def test_workload3_vision_full():
     q = _lib()
     g = synth.vision_linear()
