@@ -519,203 +519,12 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// M <= 16: the product is a stream over the weights. A workgroup owns 16 G weight rows
-// (G <= 8). The 4 waves split each K chunk's 128-wide steps; a wave copies its own steps of the
-// slice into its own LDS region (global_load_lds, one 1 KB run per 16 rows of FP4 or 8 rows of
-// E4M3, 16-byte chunks XOR-swizzled by row as in the tiled product so that an MFMA's 16 rows sit in
-// distinct banks) and multiplies step i as soon as that step's copies have landed (vmcnt), with
-// the later steps still in flight; its A fragments come from the image. Partial sums are added
-// through LDS at the end. MFMA:
-// v_mfma_scale_f32_16x16x128_f8f6f4 with the weight rows as its A operand (lane l = r + 16 g holds
-// row r: FP4 K elements [32 g, 32 g + 32) in 16 bytes; E4M3 [16 g, 16 g + 16) and
-// [64 + 16 g, 64 + 16 g + 16)), the 16 activation rows as its B operand (E4M3, same split), and
-// the scale of lane l = the E8M0 scale of its row for K block g. Result register i of lane l is
-// C^T[4 (l >> 4) + i][l & 15]: four consecutive n for one m.
-constexpr int GV_MAXSPW = 8;   // K steps per wave per chunk (chunk <= 32 steps = 4096)
-constexpr int GV_AHEAD = 4;    // steps of copies a wave keeps in flight
-
-struct GvArgs {
-  F8Args g;
-  int kc;       // K chunk (multiple of 128, <= 4096)
-  int tiles_n;  // 256-row tiles of the B image's scale layout
-};
-
-// s_waitcnt vmcnt(n) for a small run-time n: at most n vector-memory operations still in flight
-__device__ __forceinline__ void wait_vmcnt_steps(int steps_left, int per_step) {
-  switch (min(steps_left * per_step, 63)) {
-#define GV_W(N) case N: wait_vmcnt<N>(); break;
-    GV_W(0) GV_W(1) GV_W(2) GV_W(3) GV_W(4) GV_W(5) GV_W(6) GV_W(7) GV_W(8) GV_W(9) GV_W(10) GV_W(11) GV_W(12)
-    GV_W(13) GV_W(14) GV_W(15) GV_W(16) GV_W(18) GV_W(20) GV_W(21) GV_W(24) GV_W(25) GV_W(28) GV_W(30) GV_W(32)
-    GV_W(35) GV_W(36) GV_W(40) GV_W(42) GV_W(45) GV_W(48) GV_W(49) GV_W(50) GV_W(54) GV_W(56) GV_W(60)
-#undef GV_W
-    default: wait_vmcnt<0>(); break;
-  }
-}
-
-template <int B_FP4, int C_BF16, int G>
-__global__ void __launch_bounds__(256) k_gemv_f8(GvArgs ga) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const F8Args& g = ga.g;
-  constexpr int R = 16 * G;
-  constexpr int CPS = B_FP4 ? 4 : 8;                // 16-byte chunks of a B row per 128-wide K step
-  constexpr int SBY = CPS * 16;                     // bytes of a B row per step
-  constexpr int NP = R * SBY / 1024;                // 1 KB copy runs per step (G or 2 G)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15, gq = lane >> 4;
-  const int n0 = blockIdx.x * R;
-  const int rowA = min(r, g.M - 1);
-  const int64_t browg = g.K;                        // bytes per E4M3 B row (FP4 codes are step-major)
-  const int nkt = g.K / FK;
-  v4f acc[G];
-#pragma unroll
-  for (int j = 0; j < G; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  const int spw_max = (ga.kc / FK + 3) >> 2;
-  // this wave's LDS: its weight steps, then its B scales [G][spw][64] and A scales [spw][64],
-  // each rounded up to whole 1 KB copy runs
-  const int scb_runs = (G * spw_max * 64 + 1023) >> 10, sca_runs = (spw_max * 64 + 1023) >> 10;
-  uint8_t* wbase = smem + (size_t)wave * ((size_t)spw_max * R * SBY + (size_t)(scb_runs + sca_runs) * 1024);
-  for (int kc0 = 0; kc0 < g.K; kc0 += ga.kc) {
-    const int nks = min(ga.kc, g.K - kc0) / FK;      // K steps in this chunk
-    const int spw = (nks + 3) >> 2;
-    const int s0 = wave * spw;
-    const int myn = max(0, min(spw, nks - s0));      // this wave's steps
-    const int ks0 = min(kc0 / FK + s0, nkt - 1);      // its first step (clamped when it has none)
-    uint8_t* wreg = wbase;
-    uint8_t* scb = wbase + (size_t)spw_max * R * SBY;
-    uint8_t* sca = scb + (size_t)scb_runs * 1024;
-    // 1. its scales, copied into its own region (no other wave reads them): B scale chunk t (16
-    //    bytes) = row group t / (4 spw), step (t % (4 spw)) / 4, quarter t % 4 (bs_v holds a row
-    //    group's steps contiguously); A scale chunk t = step t / 4, quarter t % 4 of rows 0..15
-    //    (the A image's scale block of a step starts with them). Chunks past this wave's steps
-    //    repeat a valid one.
-    {
-      const int ngrp = (g.N + 15) >> 4;
-      for (int run = 0; run < (G * spw * 4 + 63) / 64; run++) {
-        const int t = run * 64 + lane;
-        const int j = min(t / (4 * spw), G - 1);
-        const int st = min((t % (4 * spw)) >> 2, max(myn - 1, 0));
-        const int grp = min(blockIdx.x * G + j, ngrp - 1);
-        dma16(g.bs_v + ((int64_t)grp * nkt + ks0 + st) * 64 + (t & 3) * 16,
-              __builtin_amdgcn_readfirstlane(lds_addr(scb + run * 1024)));
-      }
-      for (int run = 0; run < (spw * 4 + 63) / 64; run++) {
-        const int t = run * 64 + lane;
-        const int st = min(t >> 2, max(myn - 1, 0));
-        dma16(g.as_p + (int64_t)(ks0 + st) * 1024 + (t & 3) * 16,
-              __builtin_amdgcn_readfirstlane(lds_addr(sca + run * 1024)));
-      }
-    }
-    // 2. B: this wave's steps, step i at wreg + i R SBY; copy run q of a step holds rows
-    // [16 q, +16) (FP4, lane -> row q16 + lane / 4, slot lane % 4) or [8 q, +8) (E4M3, row
-    // q8 + lane / 8, slot lane % 8); slot s of a row holds its logical chunk s ^ swz(row).
-    // The copies are issued GV_AHEAD steps ahead of the MFMAs: issuing them all up front would
-    // stall the wave on memory back-pressure before its first MFMA.
-    auto issue_step = [&](int i) {
-      const int ks = kc0 / FK + s0 + i;
-#pragma unroll
-      for (int qr = 0; qr < NP; qr++) {
-        const int row = B_FP4 ? 16 * qr + (lane >> 2) : 8 * qr + (lane >> 3);
-        const int slot = lane & (CPS - 1);
-        const int c = slot ^ (B_FP4 ? bswz(row) : aswz(row));
-        const int grow = min(n0 + row, g.N - 1);
-        const int64_t boff = B_FP4 ? ((int64_t)ks * g.N + grow) * SBY : (int64_t)grow * browg + (int64_t)ks * SBY;
-        dma16(g.b + boff + 16 * c,
-              __builtin_amdgcn_readfirstlane(lds_addr(wreg + (size_t)i * R * SBY + qr * 1024)));
-      }
-    };
-#pragma unroll
-    for (int i = 0; i < GV_AHEAD; i++)
-      if (i < myn) issue_step(i);
-    // 3. A fragments (A image: E4M3 [M, K]), loaded from memory; indices are clamped so every load
-    //    is issued unconditionally (steps past this wave's share are loaded but not used)
-    v8i af[GV_MAXSPW];
-#pragma unroll
-    for (int i = 0; i < GV_MAXSPW; i++) {
-      const int ks = min(kc0 / FK + s0 + i, nkt - 1);
-      const uint8_t* ap = g.a8 + (int64_t)rowA * g.K + (int64_t)ks * FK + 16 * gq;
-      const uint4 lo = *(const uint4*)ap;
-      const uint4 hi = *(const uint4*)(ap + 64);
-      af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-#pragma unroll
-    for (int i = 0; i < GV_MAXSPW; i++) {
-      if (i < myn) {
-        // steps i .. min(myn, i + GV_AHEAD) - 1 are in flight, in order: wait for step i (the
-        // scale copies are older still; the A loads issued after the first steps are waited for
-        // too, as the MFMAs need them)
-        wait_vmcnt_steps(min(myn, i + GV_AHEAD) - i - 1, NP);
-        const uint8_t* sp = wreg + (size_t)i * R * SBY;
-        v8i wf[G];
-        int wsb[G];
-#pragma unroll
-        for (int j = 0; j < G; j++) {
-          const int row = 16 * j + r;
-          const uint8_t* wp = sp + row * SBY;
-          if (B_FP4) {
-            const v4i w = *(const v4i*)(wp + 16 * (gq ^ bswz(row)));
-            wf[j] = __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
-          } else {
-            const v4i lo = *(const v4i*)(wp + 16 * (gq ^ aswz(row)));
-            const v4i hi = *(const v4i*)(wp + 16 * ((4 + gq) ^ aswz(row)));
-            wf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
-          wsb[j] = scb[(j * spw + i) * 64 + r * 4 + gq];
-        }
-        const int asc = sca[i * 64 + rowA * 4 + gq];
-#pragma unroll
-        for (int j = 0; j < G; j++)
-          acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], af[i], acc[j], B_FP4 ? 4 : 0, 0, 0, wsb[j],
-                                                                    0, asc);
-        if (i + GV_AHEAD < myn) issue_step(i + GV_AHEAD);
-      }
-    }
-    // every copy this wave issued has landed (a wave with no steps in this chunk still copied its
-    // scales, and an LDS copy in flight is invisible to the barrier) and the slice is consumed
-    // before the next chunk or the partial sums below overwrite it
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-  }
-
-  // add the 4 waves' partial sums: wave w stores its G x 64 x 4 floats, then wave w sums result
-  // groups w, w + 4, ...
-  float* red = (float*)smem;
-#pragma unroll
-  for (int j = 0; j < G; j++) *(v4f*)(red + ((wave * G + j) * 64 + lane) * 4) = acc[j];
-  __builtin_amdgcn_s_barrier();
-  for (int j = wave; j < G; j += 4) {
-    v4f sum = *(const v4f*)(red + (j * 64 + lane) * 4);
-#pragma unroll
-    for (int w = 1; w < 4; w++) {
-      const v4f v = *(const v4f*)(red + ((w * G + j) * 64 + lane) * 4);
-      sum = v4f{sum[0] + v[0], sum[1] + v[1], sum[2] + v[2], sum[3] + v[3]};
-    }
-    const int m = r, n = n0 + 16 * j + 4 * gq;
-    if (m >= g.M || n >= g.N) continue;
-    const float vv[4] = {sum[0], sum[1], sum[2], sum[3]};
-    const bool vec = n + 4 <= g.N && (g.ldc % 4) == 0 && (((uintptr_t)g.c) & 15) == 0;
-    if (C_BF16) {
-      uint16_t* dst = (uint16_t*)g.c + (int64_t)m * g.ldc + n;
-      if (vec) {
-        *(uint2*)dst = make_uint2((uint32_t)f32_to_bf16_rne(vv[0]) | ((uint32_t)f32_to_bf16_rne(vv[1]) << 16),
-                                  (uint32_t)f32_to_bf16_rne(vv[2]) | ((uint32_t)f32_to_bf16_rne(vv[3]) << 16));
-      } else {
-        for (int e = 0; e < 4 && n + e < g.N; e++) dst[e] = f32_to_bf16_rne(vv[e]);
-      }
-    } else {
-      float* dst = (float*)g.c + (int64_t)m * g.ldc + n;
-      if (vec) *(float4*)dst = make_float4(vv[0], vv[1], vv[2], vv[3]);
-      else for (int e = 0; e < 4 && n + e < g.N; e++) dst[e] = vv[e];
-    }
-  }
-}
-
 // ------------------------------------------------------------------ host side
 
 bool gemm_f8_offsets_ok(int64_t M, int64_t N, int64_t K);
 
 // Shapes mix_mx_gemm sends through the images: the tiled GEMM for M >= 64 and N >= 256, the
-// weight stream (k_gemv_f8) for M <= 16; others decode inside k_gemm_mfma.
+// weight stream (k_gemv_rs, gemv_dev.h) for M <= 16; others decode inside k_gemm_mfma.
 bool gemm_f8_eligible(int64_t M, int64_t N, int64_t K) {
   return K > 0 && K % FK == 0 && ((M >= 64 && N >= FT) || (M >= 1 && M <= 16)) && gemm_f8_offsets_ok(M, N, K);
 }
@@ -817,66 +626,38 @@ hipError_t launch_gemm_b_image(int b_fp4, const uint8_t* b_codes, const uint8_t*
   return hipGetLastError();
 }
 
-// LDS bytes of k_gemv_f8 for G row groups and a K chunk kc: the four waves' regions (ceil(steps / 4)
-// weight steps and their scales each), and at least the 4 x G KB of partial sums.
-static size_t gv_lds_bytes(int b_fp4, int G, int kc) {
-  const size_t spw = (size_t)(kc / FK + 3) / 4;   // steps per wave
-  const size_t scr = (G * spw * 64 + 1023) / 1024 + (spw * 64 + 1023) / 1024;   // scale runs per wave
-  const size_t slice = 4 * (spw * 16 * G * (b_fp4 ? 64 : 128) + scr * 1024);
-  const size_t red = (size_t)4 * G * 1024;
-  return slice > red ? slice : red;
-}
+// M <= 16 as a plain launch of the weight stream (gemv_dev.h): each workgroup owns RG groups of 16
+// output columns, with RG chosen so that about one workgroup lands on each CU (fewer, longer
+// workgroups streamed faster than many short ones: 10.8 against 13.1 us for 18944 x 3584 MXFP4);
+// its four waves split K and keep two steps of operands in flight in registers.
+constexpr int GV_D = 2;
 
-template <int B_FP4, int C_BF16, int G>
-static hipError_t launch_gv(const F8Args& f, hipStream_t s) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemv_f8<B_FP4, C_BF16, G>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  // the largest K chunk whose slice fits in LDS
-  int kc = f.K < 32 * FK ? f.K : 32 * FK;
-  while (kc > FK && gv_lds_bytes(B_FP4, G, kc) > 160 * 1024) kc -= FK;
-  GvArgs a{};
-  a.g = f; a.kc = kc; a.tiles_n = f.bs_tn;
-  const int blocks = (f.N + 16 * G - 1) / (16 * G);
-  hipLaunchKernelGGL((k_gemv_f8<B_FP4, C_BF16, G>), dim3(blocks), dim3(256), gv_lds_bytes(B_FP4, G, kc), s, a);
-  return hipGetLastError();
-}
-
-template <int B_FP4, int C_BF16>
-static hipError_t launch_gv_g(const F8Args& f, hipStream_t s) {
-  // enough 16-row groups per workgroup that about one workgroup lands on each of the 256 CUs
-  const int need = (int)((f.N + 16 * 256 - 1) / (16 * 256));
-  if (need <= 1) return launch_gv<B_FP4, C_BF16, 1>(f, s);
-  if (need <= 2) return launch_gv<B_FP4, C_BF16, 2>(f, s);
-  if (need <= 4) return launch_gv<B_FP4, C_BF16, 4>(f, s);
-  if (need <= 5) return launch_gv<B_FP4, C_BF16, 5>(f, s);
-  return launch_gv<B_FP4, C_BF16, 8>(f, s);
-}
-
-// M <= 16 as a plain launch of the weight stream (gemv_dev.h): each workgroup owns 16 GV_RG output
-// columns, its four waves split K and keep GV_D steps of operands in flight in registers.
-constexpr int GV_RG = 2, GV_D = 4;
-
-template <int B_FP4, int C_BF16>
+template <int B_FP4, int C_BF16, int RG>
 __global__ void __launch_bounds__(256) k_gemv_rs(GvOps g) {
-  __shared__ __align__(16) float red[gv_lds_bytes<GV_RG>() / 4];
-  gemv_block<B_FP4, C_BF16, GV_RG, GV_D>(g, (int)blockIdx.x, red);
+  __shared__ __align__(16) float red[gv_lds_bytes<RG>() / 4];
+  gemv_block<B_FP4, C_BF16, RG, GV_D>(g, (int)blockIdx.x, red);
+}
+
+template <int B_FP4, int C_BF16>
+static hipError_t launch_gv_rs(const GvOps& g, hipStream_t s) {
+  const int ngrp = (g.N + 15) / 16;
+  const int need = (ngrp + f8_cu_count() - 1) / f8_cu_count();
+#define GVL(RG) hipLaunchKernelGGL((k_gemv_rs<B_FP4, C_BF16, RG>), dim3((unsigned)((ngrp + RG - 1) / RG)), dim3(256), 0, s, g)
+  if (need <= 1) GVL(1);
+  else if (need <= 2) GVL(2);
+  else if (need <= 4) GVL(4);
+  else if (need <= 5) GVL(5);
+  else GVL(8);
+#undef GVL
+  return hipGetLastError();
 }
 
 static hipError_t launch_gemv_f8(int b_fp4, int c_bf16, const F8Args& f, hipStream_t s) {
   GvOps g{};
   g.a8 = f.a8; g.as_p = f.as_p; g.b8 = f.b; g.bs_v = f.bs_v;
   g.c = f.c; g.ldc = f.ldc; g.M = f.M; g.N = f.N; g.K = f.K; g.tiles_m = (f.M + FT - 1) / FT;
-  const dim3 grid((unsigned)(((f.N + 15) / 16 + GV_RG - 1) / GV_RG));
-#define GVL(F, C) hipLaunchKernelGGL((k_gemv_rs<F, C>), grid, dim3(256), 0, s, g)
-  if (b_fp4) { if (c_bf16) GVL(1, 1); else GVL(1, 0); }
-  else { if (c_bf16) GVL(0, 1); else GVL(0, 0); }
-#undef GVL
-  return hipGetLastError();
+  if (b_fp4) return c_bf16 ? launch_gv_rs<1, 1>(g, s) : launch_gv_rs<1, 0>(g, s);
+  return c_bf16 ? launch_gv_rs<0, 1>(g, s) : launch_gv_rs<0, 0>(g, s);
 }
 
 hipError_t launch_gemm_images(int b_fp4, int c_bf16, const void* a_img, const void* b_img, int64_t M, int64_t N,

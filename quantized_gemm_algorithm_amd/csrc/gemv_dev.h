@@ -147,8 +147,7 @@ __device__ __forceinline__ void gemv_block(const GvOps& g, int wg, float* red) {
 #pragma unroll
   for (int j = 0; j < RG; j++) *(gv_v4f*)(red + ((wave * RG + j) * 64 + lane) * 4) = acc[j];
   __syncthreads();
-  const int t = threadIdx.x;
-  if (t < RG * 64) {
+  for (int t = threadIdx.x; t < RG * 64; t += 256) {   // RG > 4: some threads sum two groups
     const int j = t >> 6, l = t & 63;
     gv_v4f sum = *(const gv_v4f*)(red + (j * 64 + l) * 4);
 #pragma unroll

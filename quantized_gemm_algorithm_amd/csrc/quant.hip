@@ -25,13 +25,11 @@ namespace mix {
 // With IMG the lane also writes the GEMM A image of its sub-block (f8_image.h): 8 E4M3 bytes, and
 // on quad lane 0 the block's E8M0 scale 2^(Emax-1). codes/shared may then be NULL (not written).
 //
-// Work layout: grid (column chunks, row pairs); a workgroup codes MQ_R rows of one chunk of
-// blockDim.x sub-blocks (the launcher sizes blocks to the row when it has at most 1024
+// Work layout: grid (column chunks, row groups); a workgroup codes R rows of one chunk of
+// blockDim.x sub-blocks per pass (the launcher sizes blocks to the row when it has at most 1024
 // sub-blocks), so every row-dependent offset is a wave-uniform scalar and a lane only adds its
-// sub-block's offset. The MQ_R rows' loads are issued together.
-constexpr int MQ_R = 2;
-
-template <int DT, int FMT, int IMG>  // FMT 0 = MiX-4.25b, 1 = MiX-4.5b
+// sub-block's offset. The R rows' loads are issued together, R 16-byte loads in flight per lane.
+template <int DT, int FMT, int IMG, int R = 2>  // FMT 0 = MiX-4.25b, 1 = MiX-4.5b
 __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
                                                         uint8_t* __restrict__ codes, void* __restrict__ shared,
                                                         uint8_t* __restrict__ a8, uint8_t* __restrict__ as_p,
@@ -48,16 +46,16 @@ __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ 
   const int scc = col_ok ? sc : (sc & 3);
   const int q = scc & 3;
   const int blk = scc >> 2;
-  // Row pairs in XCD-contiguous bands (workgroup y runs on XCD y % 8 when the row fits one chunk):
+  // Row groups in XCD-contiguous bands (workgroup y runs on XCD y % 8 when the row fits one chunk):
   // the small per-row outputs (a row's shared fields and its scale dwords share cache lines with
   // the neighbouring rows) are then written whole by one XCD's L2 instead of in pieces by all eight.
   const int gy = gridDim.y, xb = blockIdx.y & 7;
   const int pr = xb * (gy >> 3) + min(xb, gy & 7) + (int)(blockIdx.y >> 3);
-  for (int64_t r0 = (int64_t)pr * MQ_R; r0 < rows; r0 += (int64_t)gy * MQ_R) {
-    uint32_t sdw[MQ_R];   // IMG: the four E8M0 scales of this lane's K step (valid on lane 16k)
-    uint32_t xb[MQ_R][8];  // bf16: the 16 raw bytes in xb[u][0..3]; fp32: the 8 bit patterns
+  for (int64_t r0 = (int64_t)pr * R; r0 < rows; r0 += (int64_t)gy * R) {
+    uint32_t sdw[R];   // IMG: the four E8M0 scales of this lane's K step (valid on lane 16k)
+    uint32_t xb[R][8];  // bf16: the 16 raw bytes in xb[u][0..3]; fp32: the 8 bit patterns
 #pragma unroll
-    for (int u = 0; u < MQ_R; u++) {
+    for (int u = 0; u < R; u++) {
       const int64_t row = r0 + u < rows ? r0 + u : rows - 1;
       if (DT == 1) {
         const uint4 v = *(const uint4*)((const uint16_t*)x + row * ldx + (int64_t)scc * 8);
@@ -67,7 +65,7 @@ __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ 
       }
     }
 #pragma unroll
-    for (int u = 0; u < MQ_R; u++) {
+    for (int u = 0; u < R; u++) {
       const int64_t row = r0 + u;
       int emax;
       uint32_t m, e0, e1;   // e0, e1: the sub-block's 8 E4M3 image bytes (IMG)
@@ -100,12 +98,92 @@ __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ 
       if (IMG) *(uint2*)(a8 + row * cols + scc * 8) = make_uint2(e0, e1);
     }
     if (IMG && col_ok && (scc & 15) == 0) {
-      // the rows' scale dwords of this K step (f8_a_scale_pos: row-major, so the MQ_R = 2 rows of a
-      // workgroup, even-aligned and in one 256-row tile, are adjacent)
+      // the rows' scale dwords of this K step (f8_a_scale_pos: row-major, so the R rows of a
+      // workgroup, R-aligned and in one 256-row tile, are adjacent)
       uint8_t* sp = as_p + ((int64_t)(scc >> 4) * tiles_m + (r0 >> 8)) * 1024 + (r0 & (FT - 1)) * 4;
-      if (r0 + 1 < rows) *(uint2*)sp = make_uint2(sdw[0], sdw[1]);
-      else *(uint32_t*)sp = sdw[0];
+      if (r0 + R <= rows) {
+#pragma unroll
+        for (int u = 0; u < R; u += 2) *(uint2*)(sp + 4 * u) = make_uint2(sdw[u], sdw[u + 1]);
+      } else {
+        for (int u = 0; u < R && r0 + u < rows; u++) *(uint32_t*)(sp + 4 * u) = sdw[u];
+      }
     }
+  }
+}
+
+// The bf16 quantizer with the work dealt to a fixed grid: a wave owns a segment of 64 sub-blocks
+// (512 elements, four 128-wide K steps) of one row; the (row, segment) tasks in row-major order are
+// dealt round-robin to the grid's waves, and each wave walks its tasks with the next task's 16-byte
+// loads in flight while it codes the current one. Short-lived workgroups (one or two rows each)
+// left the GPU waiting on workgroup launches: about one resident wave per SIMD on average.
+// The coding, the outputs and their layout are those of k_mix_quantize.
+template <int FMT, int IMG>
+__global__ void __launch_bounds__(256) k_mix_quantize_seg(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                           int64_t ldx, uint8_t* __restrict__ codes,
+                                                           void* __restrict__ shared, uint8_t* __restrict__ a8,
+                                                           uint8_t* __restrict__ as_p, int tiles_m) {
+  __shared__ uint4 pk_tbl[128];   // block constants of the pair coder per (Emax, m)
+  mix_pk_table_fill(pk_tbl);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int spr = (int)(cols >> 3);                 // sub-blocks per row (a multiple of 4)
+  const int nseg = (spr + 63) >> 6;                 // segments per row
+  const int64_t nw = (int64_t)gridDim.x * 4;        // waves in the grid
+  const int dq = (int)(nw / nseg), dr = (int)(nw % nseg);
+  const int64_t t0 = (int64_t)blockIdx.x * 4 + wave;
+  int64_t row = t0 / nseg;
+  int seg = (int)(t0 % nseg);
+  const int q = lane & 3;
+  auto sub = [&](int sg) {                           // this lane's sub-block in segment sg, and whether it is real
+    const int sc = sg * 64 + lane;
+    return sc < spr ? sc : -1 - (sc & 3);           // past the row: a valid sub-block of the same quad position
+  };
+  auto load = [&](int64_t r, int sg) {
+    const int sc = sub(sg);
+    return *(const uint4*)(x + r * ldx + (int64_t)(sc >= 0 ? sc : -1 - sc) * 8);
+  };
+  uint4 cur = row < rows ? load(row, seg) : make_uint4(0, 0, 0, 0);
+  while (row < rows) {
+    int64_t nrow = row + dq;
+    int nsg = seg + dr;
+    if (nsg >= nseg) { nsg -= nseg; nrow++; }
+    const uint4 nxt = nrow < rows ? load(nrow, nsg) : make_uint4(0, 0, 0, 0);   // next task's loads in flight
+    const int sc0 = sub(seg);
+    const bool ok = sc0 >= 0;
+    const int scc = ok ? sc0 : -1 - sc0;
+    const uint32_t w4[4] = {cur.x, cur.y, cur.z, cur.w};
+    int emax;
+    uint32_t m, e0, e1;
+    const uint32_t word = mix_quant_lane_bf16_tbl<FMT, IMG != 0>(w4, pk_tbl, emax, m, e0, e1);
+    uint32_t f = 0;
+    if (FMT == 1) f = quad_or_dpp((q == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * q)));
+    uint32_t sdw = 0;
+    if (IMG) {
+      const int v = emax + 126;
+      sdw = (uint32_t)v | ((uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x12C, 0xF, 0xF, true) << 8) |
+            ((uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, true) << 16) |
+            ((uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, true) << 24);
+    }
+    if (ok) {
+      const int blk = scc >> 2;
+      if (!IMG || codes) {
+        *(uint32_t*)(codes + row * (cols >> 1) + scc * 4) = word;
+        if (FMT == 1) {
+          if (q == 0) ((uint16_t*)shared)[row * (cols >> 5) + blk] = (uint16_t)f;
+        } else {
+          if (q == 0) ((uint8_t*)shared)[row * (cols >> 5) + blk] = (uint8_t)((uint32_t)(emax + 7) | (m << 4));
+        }
+      }
+      if (IMG) {
+        *(uint2*)(a8 + row * cols + scc * 8) = make_uint2(e0, e1);
+        if ((scc & 15) == 0)
+          *(uint32_t*)(as_p + ((int64_t)(scc >> 4) * tiles_m + (row >> 8)) * 1024 + (row & (FT - 1)) * 4) = sdw;
+      }
+    }
+    row = nrow;
+    seg = nsg;
+    cur = nxt;
   }
 }
 
@@ -332,41 +410,88 @@ static inline int grid_for(int64_t threads_needed) {
   return (int)(b < 1 ? 1 : b);
 }
 
-static void mq_grid(int64_t rows, int64_t cols, dim3& g, dim3& b) {
+// rows per workgroup pass of k_mix_quantize (fp32 input)
+constexpr int MQ_ROWS = 2;
+
+// compute units of the current device
+static int mq_cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+static void mq_grid(int64_t rows, int64_t cols, int R, dim3& g, dim3& b) {
   const int64_t spr = cols >> 3;
   const int64_t bx = spr <= 1024 ? (spr + 63) / 64 * 64 : 1024;
   b = dim3((unsigned)bx);
   const int64_t gx = (spr + bx - 1) / bx;
-  int64_t gy = (rows + MQ_R - 1) / MQ_R;
+  int64_t gy = (rows + R - 1) / R;
   if (gy > 65535) gy = 65535;
   g = dim3((unsigned)gx, (unsigned)(gy < 1 ? 1 : gy));
 }
 
+// bf16 input: the segment-dealt kernel on a grid of up to 8 workgroups (32 waves) per CU
+static dim3 mq_seg_grid(int64_t rows, int64_t cols) {
+  const int64_t tasks = rows * (((cols >> 3) + 63) >> 6);
+  int64_t g = (tasks + 3) / 4;
+  const int64_t cap = 8 * (int64_t)mq_cu_count();
+  if (g > cap) g = cap;
+  return dim3((unsigned)(g < 1 ? 1 : g));
+}
+
 hipError_t launch_mix_quantize(int fmt, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                                uint8_t* codes, void* shared, hipStream_t s) {
+  if (dtype == 1) {
+    const dim3 g = mq_seg_grid(rows, cols);
+    if (fmt == 1)
+      hipLaunchKernelGGL((k_mix_quantize_seg<1, 0>), g, dim3(256), 0, s, (const uint16_t*)x, rows, cols, ldx, codes,
+                         shared, nullptr, nullptr, 0);
+    else
+      hipLaunchKernelGGL((k_mix_quantize_seg<0, 0>), g, dim3(256), 0, s, (const uint16_t*)x, rows, cols, ldx, codes,
+                         shared, nullptr, nullptr, 0);
+    return hipGetLastError();
+  }
   dim3 g, b;
-  mq_grid(rows, cols, g, b);
-#define MQ(DT, F) hipLaunchKernelGGL((k_mix_quantize<DT, F, 0>), g, b, 0, s, x, rows, cols, ldx, codes, shared, \
-                                     nullptr, nullptr, 0)
-  if (dtype == 1) { if (fmt == 1) MQ(1, 1); else MQ(1, 0); }
-  else { if (fmt == 1) MQ(0, 1); else MQ(0, 0); }
-#undef MQ
+  mq_grid(rows, cols, MQ_ROWS, g, b);
+  if (fmt == 1)
+    hipLaunchKernelGGL((k_mix_quantize<0, 1, 0, MQ_ROWS>), g, b, 0, s, x, rows, cols, ldx, codes, shared, nullptr,
+                       nullptr, 0);
+  else
+    hipLaunchKernelGGL((k_mix_quantize<0, 0, 0, MQ_ROWS>), g, b, 0, s, x, rows, cols, ldx, codes, shared, nullptr,
+                       nullptr, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_mix_quantize_img(int fmt, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                                    uint8_t* codes, void* shared, void* img, hipStream_t s) {
-  dim3 g, b;
-  mq_grid(rows, cols, g, b);
   const F8AImage L = f8_a_image_layout(rows, cols);
   uint8_t* a8 = (uint8_t*)img + L.a8;
   uint8_t* as_p = (uint8_t*)img + L.as_p;
   const int tiles_m = (int)((rows + FT - 1) / FT);
-#define MQ(DT, F) hipLaunchKernelGGL((k_mix_quantize<DT, F, 1>), g, b, 0, s, x, rows, cols, ldx, codes, shared, a8, \
-                                     as_p, tiles_m)
-  if (dtype == 1) { if (fmt == 1) MQ(1, 1); else MQ(1, 0); }
-  else { if (fmt == 1) MQ(0, 1); else MQ(0, 0); }
-#undef MQ
+  if (dtype == 1) {
+    const dim3 g = mq_seg_grid(rows, cols);
+    if (fmt == 1)
+      hipLaunchKernelGGL((k_mix_quantize_seg<1, 1>), g, dim3(256), 0, s, (const uint16_t*)x, rows, cols, ldx, codes,
+                         shared, a8, as_p, tiles_m);
+    else
+      hipLaunchKernelGGL((k_mix_quantize_seg<0, 1>), g, dim3(256), 0, s, (const uint16_t*)x, rows, cols, ldx, codes,
+                         shared, a8, as_p, tiles_m);
+    return hipGetLastError();
+  }
+  dim3 g, b;
+  mq_grid(rows, cols, MQ_ROWS, g, b);
+  if (fmt == 1)
+    hipLaunchKernelGGL((k_mix_quantize<0, 1, 1, MQ_ROWS>), g, b, 0, s, x, rows, cols, ldx, codes, shared, a8, as_p,
+                       tiles_m);
+  else
+    hipLaunchKernelGGL((k_mix_quantize<0, 0, 1, MQ_ROWS>), g, b, 0, s, x, rows, cols, ldx, codes, shared, a8, as_p,
+                       tiles_m);
   return hipGetLastError();
 }
 

@@ -67,7 +67,7 @@ def test_static_decode_step_rejects_shapes_beyond_its_array():
     import quantized_gemm_algorithm_amd as q
     lib = q._lib_()
     P = ctypes.c_void_p
-    B, K, N, L, Hq, Hkv = 16, 3584, 18944, 32768, 28, 4
+    B, K, N, L, Hq, Hkv = 16, 3584, 18944, 65536, 28, 4
     assert lib.mix_decode_step_workspace_bytes(B, K, Hq, Hkv, 128, L - 1) > 32 << 20
     cache = q.KVCache(B, 64, Hkv, 128)   # small real buffers; the shape check fails before any launch
     cache._st.Lmax = L
