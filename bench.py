@@ -94,6 +94,31 @@ def measured_traffic(workload):
     return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
 
 
+# VALU issue peak: 256 CUs x 4 SIMDs, a wave64 instruction every 4 cycles per SIMD (16 lanes a
+# cycle; the published 157.3 TFLOP/s fp32 vector figure counts packed two-element FMAs), 2.4 GHz
+VALU_PEAK_GINSTS = 256 * 4 * 2.4e9 / 4 / 1e9
+
+
+def measured_valu(workload):
+    """VALU wave-instructions per call of the workload, from the SQ_INSTS_VALU counter run recorded in
+    profiles/valu.json; None if none was recorded or the sources changed since."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        rec = json.load(open(os.path.join(root, "profiles", "valu.json"))).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in rec["source_files"]:
+        try:
+            h.update(open(os.path.join(root, f), "rb").read())
+        except OSError:
+            return None
+    return rec if h.hexdigest() == rec["source_sha256"] else None
+
+
 def settle(torch, fn, ms):
     """Run fn(i) untimed for at least `ms` of wall time (synchronizing every few calls, so that the GPU
     is busy throughout). An idle MI355X needs tens of ms of sustained load to reach its steady clocks:
@@ -330,6 +355,7 @@ def bench_linear(torch, q, args, which):
                       "frac_hbm": q_codes_bytes / (q_codes_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                       "algorithmic_bytes": q_codes_bytes,
                       "timing": f"{qrep} back-to-back launches between two HIP events",
+                      "traffic": measured_traffic(which + "_quantizer_codes"), "traffic_source": TRAFFIC_SOURCE,
                       "rotating_buffers": nrot,
                       "with_a_image": {"kernel": "k_mix_quantize (codes + the GEMM's A image, the step's variant)",
                                        "ms": q_stream_ms, "bytes": q_bytes,
@@ -356,7 +382,7 @@ def bench_decode(torch, q, args):
     """Decode step (batch 16): x [16, 3584] -> MiX-4.5b -> product with the MXFP4 weights
     [18944, 3584] -> y bf16, and attention of q [16, 28, 128] over 8192 MX-coded cached tokens per
     row (the new token at position 8191 smoothed with the frozen prefill mean and appended), all in
-    one mix_decode_step call (two launches), replayed as a HIP graph."""
+    one mix_decode_step call (three launches)."""
     from quantized_gemm_algorithm_amd import synth
     g = synth.decode_step()
     B, L, Hkv, d = g["k_hist"].shape
@@ -401,8 +427,8 @@ def bench_decode(torch, q, args):
         bimg, cache = sets[i % nset]
         q.mix_decode_step(x, bimg, qd, k_new, v_new, cache, pos, L - 1, mu, y=y, o=o, workspace=ws)
 
-    # the step as a serving loop runs it: one HIP graph per weight/cache set (the step's two launches
-    # replayed without host launch gaps); outputs are checked against the eager step
+    # the step captured once per weight/cache set as a HIP graph and replayed (outputs checked
+    # against the eager step)
     step(0)
     torch.cuda.synchronize()
     y_ref, o_ref = y.clone(), o.clone()
@@ -425,13 +451,19 @@ def bench_decode(torch, q, args):
         graphs[i % nset].replay()
     t1.record()
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
+    ms_graph = t0.elapsed_time(t1) / args.steps
+    # the timed steps: back-to-back calls on the stream (three launches each), as for the other
+    # workloads; the graph replay above is reported beside them
+    settle(torch, step, args.settle_ms)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
     t0.record()
     for i in range(args.steps):
         step(i)
     t1.record()
     torch.cuda.synchronize()
-    ms_eager = t0.elapsed_time(t1) / args.steps
+    ms_step = t0.elapsed_time(t1) / args.steps
 
     # the same work as separate calls (quantize x with its A image, the weight-stream product,
     # attention alone), each timed as back-to-back launches in one graph over the rotating sets
@@ -482,10 +514,10 @@ def bench_decode(torch, q, args):
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"),
                      "traffic_source": TRAFFIC_SOURCE,
-                     "kernel": "mix_decode_step (k_decode_scores + k_decode_pv)",
-                     "kernel_ms": ms_step, "timing": f"{args.steps} graph replays between two HIP events",
+                     "kernel": "mix_decode_step (k_decode_scores + k_decode_pv + k_decode_combine)",
+                     "kernel_ms": ms_step, "timing": f"{args.steps} back-to-back steps between two HIP events",
                      "algorithmic_bytes": step_bytes},
-        "parts": {"eager_ms_per_step": ms_eager,
+        "parts": {"graph_replay_ms_per_step": ms_graph,
                   "separate_calls": {"what": "the same work as separate calls, each timed as back-to-back launches "
                                              "in one graph",
                                      "quantize_x_ms": parts_q, "gemv_ms": parts_gv,
@@ -571,6 +603,18 @@ def bench_attention(torch, q, args):
                      "traffic_source": TRAFFIC_SOURCE,
                      "kernel": "mix_attn_prefill (all kernels of the call)", "kernel_ms": ms_step},
     }
+    vr = measured_valu("attention_prefill")
+    if vr is not None:
+        gis = vr["valu_insts_per_call"] / (ms_step * 1e-3) / 1e9
+        res["roofline_valu"] = {
+            "bound": "alu", "achieved": gis, "peak": VALU_PEAK_GINSTS, "unit": "G wave-instructions/s",
+            "frac": gis / VALU_PEAK_GINSTS, "kernel": "mix_attn_prefill (all kernels of the call)",
+            "valu_insts_per_call": vr["valu_insts_per_call"],
+            "source": "stored figure: profiles/valu.json (rocprofv3 SQ_INSTS_VALU, device total per kernel); null "
+                      "once the sources differ from those it was taken on",
+            "dominant_kernel": {"kernel": "k_attn_pcode", "valu_insts": vr["valu_insts_per_kernel"]["k_attn_pcode<false>"],
+                                "valu_time_floor_ms": vr["valu_insts_per_kernel"]["k_attn_pcode<false>"] /
+                                                      (VALU_PEAK_GINSTS * 1e9) * 1e3}}
     res["underflow_map"] = underflow_section(torch, q, kd.view(T, Hkv * d))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_attention(g, d)

@@ -100,10 +100,16 @@ mix_status_t mx_quantize(mx_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t
                          const float* mu, uint8_t* codes, uint8_t* scales, void* stream);
 
 /*
- * MXFP4 with blocks running down the columns (the V operand along tokens): block j of column c
- * covers rows [32 j, 32 j + 32); rows at or beyond `rows` count as zero.
- *   x       [rows, cols] fp32 or bf16, row pitch ldx
- *   codes   [cols, prows/2], scales [cols, prows/32] where prows = rows rounded up to 32
+ * MXFP4 (the ceil rule of mx_quantize) with blocks running down the columns -- P1, 核心创新
+ * (innovations), third bullet: the attention products, the KV cache included, are coded too. In
+ * P^ V the contraction runs along tokens, so V is the MX operand of that product with its blocks
+ * along tokens (one block per 32 tokens of a channel). Block j of column c covers rows
+ * [32 j, 32 j + 32); rows at or beyond `rows` count as zero.
+ *   x       [rows, cols] fp32 or bf16, row pitch ldx elements (ldx >= cols), element-aligned
+ *   codes   [cols, prows/2] uint8, 16-byte aligned; scales [cols, prows/32] E8M0, where
+ *           prows = rows rounded up to 32 (the output is written transposed: one row per column)
+ * Errors: MIX_E_SHAPE for negative extents, ldx < cols or prows / 32 > 65535; MIX_E_NULL,
+ * MIX_E_ALIGN as above. Empty input: MIX_OK, nothing written.
  */
 mix_status_t mx_quantize_cols(const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, void* stream);
@@ -153,20 +159,41 @@ size_t mix_mx_gemm_workspace_bytes(mix_fmt_t a_fmt, mx_fmt_t b_fmt, int64_t M, i
 size_t mix_gemm_a_image_bytes(int64_t M, int64_t K);
 size_t mx_gemm_b_image_bytes(mx_fmt_t b_fmt, int64_t N, int64_t K);
 
-/* A image from MiX codes ([M, K/2] codes, [M, K/32] shared fields as for mix_mx_gemm). */
+/*
+ * A image from MiX codes -- P1, 方法概览 (method overview), the dual-format bullet: the MiX
+ * activation's shared mantissa factors out of the block dot product, which leaves a per-element
+ * power of two (the E4M3 byte) under a per-block power of two (the E8M0 scale).
+ *   a_codes [M, K/2] uint8 (16-byte aligned), a_shared [M, K/32] uint8 / uint16 by a_fmt
+ *   img     mix_gemm_a_image_bytes(M, K) bytes at least (MIX_E_WORKSPACE below), 256-byte aligned
+ * Errors: MIX_E_SHAPE unless K is a positive multiple of 128 (M <= 2^31 - 1); MIX_E_NULL,
+ * MIX_E_ALIGN, MIX_E_ENUM. M == 0: MIX_OK, nothing written.
+ */
 mix_status_t mix_gemm_a_image(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, int64_t M, int64_t K,
                               void* img, size_t img_bytes, void* stream);
 
 /*
  * mix_quantize that also writes the A image of the quantized rows in the same pass (rows = M,
- * cols = K). codes and shared may both be NULL: then only the image is written. The image equals
- * mix_gemm_a_image of the codes mix_quantize produces.
+ * cols = K) -- P1, 方法概览 (method overview): the Algorithm 1 bullet (the quantizer) and the
+ * dual-format bullet (the operand the product consumes). codes and shared may both be NULL: then
+ * only the image is written. The image equals mix_gemm_a_image of the codes mix_quantize produces.
+ *   x, dtype, rows, cols, ldx, codes, shared  as for mix_quantize (cols a positive multiple of 128)
+ *   img     mix_gemm_a_image_bytes(rows, cols) bytes at least, 256-byte aligned
+ * Errors: as for mix_quantize and mix_gemm_a_image; MIX_E_NULL if exactly one of codes / shared
+ * is NULL.
  */
 mix_status_t mix_quantize_gemm(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols,
                                int64_t ldx, uint8_t* codes, void* shared, void* img, size_t img_bytes, void* stream);
 
-/* B image from MX codes ([N, K/2] codes, 16-byte aligned; [N, K/32] E8M0 scales); g16 formats:
- * MIX_E_UNSUPPORTED (use mx_gemm_b_image_g16). */
+/*
+ * B image from MX codes -- P1, 方法概览 (method overview), the dual-format bullet (W-MX weights),
+ * and 逐图理解论文 (figure walk), Fig. 4 (the MXINT4 / MXFP4 fields): MXINT4 elements become E4M3
+ * bytes of q/4 under their unchanged scale, MXFP4 codes are copied step-major.
+ *   b_codes [N, K/2] uint8, 16-byte aligned; b_scales [N, K/32] E8M0
+ *   img     mx_gemm_b_image_bytes(b_fmt, N, K) bytes at least, 256-byte aligned
+ * Errors: MIX_E_UNSUPPORTED for the g16 formats (use mx_gemm_b_image_g16); MIX_E_SHAPE unless K
+ * is a positive multiple of 128; MIX_E_NULL, MIX_E_ALIGN, MIX_E_WORKSPACE (image too small).
+ * N == 0: MIX_OK, nothing written.
+ */
 mix_status_t mx_gemm_b_image(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8_t* b_scales, int64_t N, int64_t K,
                              void* img, size_t img_bytes, void* stream);
 
@@ -186,11 +213,16 @@ mix_status_t mx_gemm_b_image_g16(mx_fmt_t b_fmt, const uint8_t* b_codes, const u
                                  int64_t K, void* img, size_t img_bytes, uint32_t* unfoldable, void* stream);
 
 /*
- * C = A . B^T from the two images (same results as mix_mx_gemm on the codes). The images hold
- * every operand byte: b_codes is not read and may be NULL (kept for the signature). c and ldc as
- * for mix_mx_gemm. For
- * M > 16 each operand image must stay below 2^31 bytes (MIX_E_UNSUPPORTED otherwise; mix_mx_gemm
- * then decodes inside the GEMM instead).
+ * C = A . B^T from the two images -- P1, 方法概览 (method overview), the dual-format bullet and
+ * Eq. (6): the same exact products and fp32 sums as mix_mx_gemm on the codes (bit-identical
+ * results). The images hold every operand byte: b_codes is not read and may be NULL (kept for the
+ * signature). M <= 16 runs the weight stream (each weight byte read once), larger M the tiled
+ * product.
+ *   a_img, b_img  images of an [M, K] and an [N, K] operand, 256-byte aligned
+ *   c      [M, N] fp32 or bf16 (c_dtype), row pitch ldc >= N elements, element-aligned
+ * Errors: MIX_E_SHAPE unless K is a positive multiple of 128 (M, N <= 2^31 - 1) or if ldc < N;
+ * MIX_E_UNSUPPORTED for M > 16 when an operand image reaches 2^31 bytes (mix_mx_gemm then decodes
+ * inside the GEMM instead); MIX_E_NULL, MIX_E_ALIGN, MIX_E_ENUM. M or N == 0: MIX_OK.
  */
 mix_status_t mix_mx_gemm_images(mx_fmt_t b_fmt, const void* a_img, const void* b_img, const uint8_t* b_codes,
                                 int64_t M, int64_t N, int64_t K, void* c, mix_dtype_t c_dtype, int64_t ldc,
@@ -329,12 +361,21 @@ mix_status_t mix_kv_cache_prefill(const mix_kv_cache_t* cache, int64_t b, const 
                                   const float* mu, void* stream);
 
 /*
- * One decode step for B sequences: append k_new/v_new [B, Hkv, d] bf16 at position pos[b]
- * (device int32 [B]), then attend q [B, Hq, d] bf16 over keys [0, pos[b]] with no causal mask,
- * using the frozen mean mu [B, Hkv, d] fp32; o [B, Hq, d] bf16 (8-byte aligned). Same operand formats and softmax
- * as prefill. `max_pos` (host) bounds every pos[b] (0 <= pos[b] <= max_pos < Lmax); rows whose pos
- * is outside [0, max_pos] write zeros to o and leave the cache untouched.
- *   ws: at least mix_attn_decode_workspace_bytes(B, Hq, Hkv, d, max_pos) bytes, 256-B aligned
+ * One decode step of the attention -- P1, 方法概览 (method overview), last bullet, and 阅读时需要注意
+ * (caveats), first bullet: keys are smoothed with the prefill K-mean frozen for decode, so the
+ * cached MXFP4 keys are read once per step and never re-coded; the operand formats and softmax
+ * are those of mix_attn_prefill. For B sequences: append k_new/v_new [B, Hkv, d] bf16 at
+ * position pos[b] (device int32 [B]), then attend q [B, Hq, d] bf16 over keys [0, pos[b]] with no causal mask,
+ * using the frozen mean mu [B, Hkv, d] fp32; o [B, Hq, d] bf16 (8-byte aligned). `max_pos`
+ * (host) bounds every pos[b] (0 <= pos[b] <= max_pos < Lmax); rows whose pos is outside
+ * [0, max_pos] write zeros to o and leave the cache untouched.
+ *   q      [B, Hq, d] bf16 dense, 16-byte aligned; k_new, v_new [B, Hkv, d] bf16 dense
+ *   pos    device int32 [B], 4-byte aligned; mu device fp32 [B, Hkv, d], 4-byte aligned
+ *   ws: at least mix_attn_decode_workspace_bytes(B, Hq, Hkv, d, max_pos) bytes, 256-B aligned;
+ *       scratch (its contents on entry do not matter)
+ * Errors: MIX_E_NULL (a pointer or cache buffer), MIX_E_SHAPE (cache extents, Hq not a positive
+ * multiple of Hkv, max_pos outside [0, Lmax)), MIX_E_UNSUPPORTED (d != 128 or more than 16 query
+ * heads per KV head), MIX_E_ALIGN, MIX_E_WORKSPACE; nothing is enqueued on an error.
  */
 size_t mix_attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos);
 mix_status_t mix_attn_decode(const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* cache,
@@ -350,8 +391,9 @@ mix_status_t mix_attn_decode(const void* q, const void* k_new, const void* v_new
  *   the attention step of mix_attn_decode (append k_new / v_new at pos[b], attend q over keys
  *   [0, pos[b]], o [B, Hq, d]).
  * The results equal mix_quantize_gemm(x) + mix_mx_gemm_images (bf16 out) followed by mix_attn_decode
- * with the same arguments; the two parts are independent and run in the same two launches (the
- * first codes x and computes the scores, the second streams the weights and the values).
+ * with the same arguments; the two parts are independent and share three launches (the first
+ * codes x beside the scores, the second streams the weights beside the values, the third adds the
+ * per-chunk partial sums of O).
  *   x      [B, K] bf16, dense (B = cache->B <= 16; K a positive multiple of 128), 16-byte aligned
  *   b_fmt, b_img  the weights' B image (mx_gemm_b_image / mx_gemm_b_image_g16 for an [N, K] operand;
  *          g16 images must have no unfoldable block for the product to be exact), 256-byte aligned

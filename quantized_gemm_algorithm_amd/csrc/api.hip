@@ -2,6 +2,7 @@
 // stream. Nothing here allocates, frees or synchronises.
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <string>
 
@@ -29,12 +30,29 @@ mix_status_t hip_status(hipError_t e, const char* what) {
 }
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Enum arguments come from C callers and foreign-function bindings, which can pass any int, and in
+// C++ a value outside an unscoped enum's range may not be read as that enum type. Validation
+// therefore reads such an argument's bits as an int, through its address, before anything uses it
+// as the enum.
+template <class E>
+inline int enum_bits(const E* e) {
+  static_assert(sizeof(E) == sizeof(int), "the C enums are int-sized");
+  int v;
+  memcpy(&v, e, sizeof v);
+  return v;
+}
+inline bool mix_known(int f) { return f == MIX_4P25 || f == MIX_4P5; }
 inline int dtype_size(int dt) { return dt == MIX_BF16 ? 2 : 4; }
 
 mix_status_t check_dtype(int dt) {
   if (dt != MIX_F32 && dt != MIX_BF16) return fail(MIX_E_ENUM, "unknown dtype %d", dt);
   return MIX_OK;
 }
+
+// Largest input matrix (elements, pitch included): 2^46, with every extent below 2^31, so that no
+// size or grid computation below can overflow.
+constexpr int64_t kMaxElems = (int64_t)1 << 46;
 
 // Common checks for a [rows, cols] input with blocks along cols. Sets *empty for zero extents.
 mix_status_t check_matrix_in(const char* fn, const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx,
@@ -44,6 +62,8 @@ mix_status_t check_matrix_in(const char* fn, const void* x, int dt, int64_t rows
   if (cols % 32) return fail(MIX_E_SHAPE, "%s: cols=%lld is not a multiple of 32", fn, (long long)cols);
   if (rows == 0 || cols == 0) { *empty = true; return MIX_OK; }
   if (ldx < cols) return fail(MIX_E_SHAPE, "%s: ldx=%lld < cols=%lld", fn, (long long)ldx, (long long)cols);
+  if (rows > INT32_MAX || ldx > INT32_MAX || rows * ldx > kMaxElems)
+    return fail(MIX_E_SHAPE, "%s: %lld rows of pitch %lld exceed the library's extents", fn, (long long)rows, (long long)ldx);
   if (!x) return fail(MIX_E_NULL, "%s: x is NULL", fn);
   if (!aligned16(x) || (ldx * dtype_size(dt)) % 16) return fail(MIX_E_ALIGN, "%s: x or its row pitch is not 16-byte aligned", fn);
   return MIX_OK;
@@ -56,7 +76,7 @@ extern "C" {
 int mix_abi_version(void) { return MIX_ABI_VERSION; }
 
 const char* mix_status_str(mix_status_t s) {
-  switch (s) {
+  switch (enum_bits(&s)) {
     case MIX_OK: return "ok";
     case MIX_E_NULL: return "null pointer";
     case MIX_E_SHAPE: return "bad shape";
@@ -74,8 +94,8 @@ const char* mix_last_error(void) { return g_err.c_str(); }
 mix_status_t mix_quantize(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
                           uint8_t* codes, void* shared, void* stream) {
   g_err.clear();
-  if (fmt != MIX_4P25 && fmt != MIX_4P5) return fail(MIX_E_ENUM, "mix_quantize: unknown MiX format %d", (int)fmt);
-  if (mix_status_t st = check_dtype(dtype)) return st;
+  if (!mix_known(enum_bits(&fmt))) return fail(MIX_E_ENUM, "mix_quantize: unknown MiX format %d", enum_bits(&fmt));
+  if (mix_status_t st = check_dtype(enum_bits(&dtype))) return st;
   bool empty;
   if (mix_status_t st = check_matrix_in("mix_quantize", x, dtype, rows, cols, ldx, &empty)) return st;
   if (empty) return MIX_OK;
@@ -85,15 +105,15 @@ mix_status_t mix_quantize(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, int64
                     "mix_quantize launch");
 }
 
-static bool mx_known(mx_fmt_t f) { return f == MX_INT4 || f == MX_FP4 || f == MX_INT4_G16 || f == MX_FP4_G16; }
+static bool mx_known(int f) { return f == MX_INT4 || f == MX_FP4 || f == MX_INT4_G16 || f == MX_FP4_G16; }
 static bool mx_fp4(mx_fmt_t f) { return f == MX_FP4 || f == MX_FP4_G16; }
 static bool mx_g16(mx_fmt_t f) { return f == MX_INT4_G16 || f == MX_FP4_G16; }
 
 mix_status_t mx_quantize(mx_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
                          const float* mu, uint8_t* codes, uint8_t* scales, void* stream) {
   g_err.clear();
-  if (!mx_known(fmt)) return fail(MIX_E_ENUM, "mx_quantize: unknown MX format %d", (int)fmt);
-  if (mix_status_t st = check_dtype(dtype)) return st;
+  if (!mx_known(enum_bits(&fmt))) return fail(MIX_E_ENUM, "mx_quantize: unknown MX format %d", enum_bits(&fmt));
+  if (mix_status_t st = check_dtype(enum_bits(&dtype))) return st;
   bool empty;
   if (mix_status_t st = check_matrix_in("mx_quantize", x, dtype, rows, cols, ldx, &empty)) return st;
   if (empty) return MIX_OK;
@@ -107,10 +127,12 @@ mix_status_t mx_quantize(mx_fmt_t fmt, const void* x, mix_dtype_t dtype, int64_t
 mix_status_t mx_quantize_cols(const void* x, mix_dtype_t dtype, int64_t rows, int64_t cols, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, void* stream) {
   g_err.clear();
-  if (mix_status_t st = check_dtype(dtype)) return st;
+  if (mix_status_t st = check_dtype(enum_bits(&dtype))) return st;
   if (rows < 0 || cols < 0) return fail(MIX_E_SHAPE, "mx_quantize_cols: negative extent");
   if (rows == 0 || cols == 0) return MIX_OK;
   if (ldx < cols) return fail(MIX_E_SHAPE, "mx_quantize_cols: ldx < cols");
+  if (rows > INT32_MAX || ldx > INT32_MAX || rows * ldx > kMaxElems)
+    return fail(MIX_E_SHAPE, "mx_quantize_cols: extents too large");
   if (!x || !codes || !scales) return fail(MIX_E_NULL, "mx_quantize_cols: NULL pointer");
   if (!aligned16(codes)) return fail(MIX_E_ALIGN, "mx_quantize_cols: codes not 16-byte aligned");
   if ((uintptr_t)x % dtype_size(dtype)) return fail(MIX_E_ALIGN, "mx_quantize_cols: x misaligned");
@@ -124,7 +146,7 @@ mix_status_t mx_quantize_cols(const void* x, mix_dtype_t dtype, int64_t rows, in
 mix_status_t mix_dequantize(mix_fmt_t fmt, const uint8_t* codes, const void* shared, int64_t rows, int64_t cols,
                             float* out, void* stream) {
   g_err.clear();
-  if (fmt != MIX_4P25 && fmt != MIX_4P5) return fail(MIX_E_ENUM, "mix_dequantize: unknown MiX format %d", (int)fmt);
+  if (!mix_known(enum_bits(&fmt))) return fail(MIX_E_ENUM, "mix_dequantize: unknown MiX format %d", enum_bits(&fmt));
   if (rows < 0 || cols < 0 || cols % 32) return fail(MIX_E_SHAPE, "mix_dequantize: bad shape");
   if (rows == 0 || cols == 0) return MIX_OK;
   if (!codes || !shared || !out) return fail(MIX_E_NULL, "mix_dequantize: NULL pointer");
@@ -136,7 +158,7 @@ mix_status_t mix_dequantize(mix_fmt_t fmt, const uint8_t* codes, const void* sha
 mix_status_t mx_dequantize(mx_fmt_t fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                            float* out, void* stream) {
   g_err.clear();
-  if (!mx_known(fmt)) return fail(MIX_E_ENUM, "mx_dequantize: unknown MX format %d", (int)fmt);
+  if (!mx_known(enum_bits(&fmt))) return fail(MIX_E_ENUM, "mx_dequantize: unknown MX format %d", enum_bits(&fmt));
   if (rows < 0 || cols < 0 || cols % 32) return fail(MIX_E_SHAPE, "mx_dequantize: bad shape");
   if (rows == 0 || cols == 0) return MIX_OK;
   if (!codes || !scales || !out) return fail(MIX_E_NULL, "mx_dequantize: NULL pointer");
@@ -145,17 +167,21 @@ mix_status_t mx_dequantize(mx_fmt_t fmt, const uint8_t* codes, const uint8_t* sc
                     "mx_dequantize launch");
 }
 
-static mix_status_t gemm_common(const char* fn, bool eq6, mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared,
-                                mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
-                                int64_t K, void* c, mix_dtype_t c_dtype, int64_t ldc, void* ws, size_t ws_bytes,
-                                void* stream) {
+// the enums arrive by address: a by-value copy would already read them as the enum type
+static mix_status_t gemm_common(const char* fn, bool eq6, const mix_fmt_t* a_fmt_p, const uint8_t* a_codes,
+                                const void* a_shared, const mx_fmt_t* b_fmt_p, const uint8_t* b_codes,
+                                const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
+                                const mix_dtype_t* c_dtype_p, int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
-  if (a_fmt != MIX_4P25 && a_fmt != MIX_4P5) return fail(MIX_E_ENUM, "%s: unknown MiX format %d", fn, (int)a_fmt);
-  if (!mx_known(b_fmt)) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (!mix_known(enum_bits(a_fmt_p))) return fail(MIX_E_ENUM, "%s: unknown MiX format %d", fn, enum_bits(a_fmt_p));
+  if (!mx_known(enum_bits(b_fmt_p))) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, enum_bits(b_fmt_p));
+  if (mix_status_t st = check_dtype(enum_bits(c_dtype_p))) return st;
+  const mix_fmt_t a_fmt = *a_fmt_p;
+  const mx_fmt_t b_fmt = *b_fmt_p;
+  const mix_dtype_t c_dtype = *c_dtype_p;
   if (mx_g16(b_fmt) && !eq6)
     return fail(MIX_E_UNSUPPORTED, "%s: g16 weights go through mx_gemm_b_image_g16 + mix_mx_gemm_images, or "
                 "mix_mx_gemm_eq6", fn);
-  if (mix_status_t st = check_dtype(c_dtype)) return st;
   if (M < 0 || N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
   if (K % 32) return fail(MIX_E_SHAPE, "%s: K=%lld is not a multiple of 32", fn, (long long)K);
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(MIX_E_SHAPE, "%s: extent above 2^31-1", fn);
@@ -188,7 +214,9 @@ static mix_status_t gemm_common(const char* fn, bool eq6, mix_fmt_t a_fmt, const
 
 size_t mix_mx_gemm_workspace_bytes(mix_fmt_t a_fmt, mx_fmt_t b_fmt, int64_t M, int64_t N, int64_t K) {
   (void)a_fmt;
-  if (M <= 0 || N <= 0 || K <= 0 || (b_fmt != MX_INT4 && b_fmt != MX_FP4)) return 0;   // g16: no workspace path
+  const int bf = enum_bits(&b_fmt);
+  if (M <= 0 || N <= 0 || K <= 0 || (bf != MX_INT4 && bf != MX_FP4)) return 0;   // g16: no workspace path
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return 0;
   if (!mix::gemm_f8_eligible(M, N, K)) return 0;
   return mix::gemm_f8_ws_bytes(b_fmt == MX_FP4, M, N, K);
 }
@@ -196,15 +224,15 @@ size_t mix_mx_gemm_workspace_bytes(mix_fmt_t a_fmt, mx_fmt_t b_fmt, int64_t M, i
 mix_status_t mix_mx_gemm(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, mx_fmt_t b_fmt,
                          const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
                          mix_dtype_t c_dtype, int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
-  return gemm_common("mix_mx_gemm", false, a_fmt, a_codes, a_shared, b_fmt, b_codes, b_scales, M, N, K, c, c_dtype, ldc,
-                     ws, ws_bytes, stream);
+  return gemm_common("mix_mx_gemm", false, &a_fmt, a_codes, a_shared, &b_fmt, b_codes, b_scales, M, N, K, c, &c_dtype,
+                     ldc, ws, ws_bytes, stream);
 }
 
 mix_status_t mix_mx_gemm_eq6(mix_fmt_t a_fmt, const uint8_t* a_codes, const void* a_shared, mx_fmt_t b_fmt,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
                              void* c, mix_dtype_t c_dtype, int64_t ldc, void* stream) {
-  return gemm_common("mix_mx_gemm_eq6", true, a_fmt, a_codes, a_shared, b_fmt, b_codes, b_scales, M, N, K, c, c_dtype,
-                     ldc, nullptr, 0, stream);
+  return gemm_common("mix_mx_gemm_eq6", true, &a_fmt, a_codes, a_shared, &b_fmt, b_codes, b_scales, M, N, K, c,
+                     &c_dtype, ldc, nullptr, 0, stream);
 }
 
 // ---------------------------------------------------------------- GEMM operand images
@@ -217,7 +245,7 @@ size_t mix_gemm_a_image_bytes(int64_t M, int64_t K) {
 }
 
 size_t mx_gemm_b_image_bytes(mx_fmt_t b_fmt, int64_t N, int64_t K) {
-  if (!mx_known(b_fmt) || N <= 0 || N > INT32_MAX || !image_k_ok(K)) return 0;
+  if (!mx_known(enum_bits(&b_fmt)) || N <= 0 || N > INT32_MAX || !image_k_ok(K)) return 0;
   return mix::f8_b_image_layout(b_fmt == MX_FP4, N, K).total;   // g16 images are E4M3 (the MXINT4 layout)
 }
 
@@ -232,7 +260,7 @@ mix_status_t mix_gemm_a_image(mix_fmt_t a_fmt, const uint8_t* a_codes, const voi
                               void* img, size_t img_bytes, void* stream) {
   g_err.clear();
   const char* fn = "mix_gemm_a_image";
-  if (a_fmt != MIX_4P25 && a_fmt != MIX_4P5) return fail(MIX_E_ENUM, "%s: unknown MiX format %d", fn, (int)a_fmt);
+  if (!mix_known(enum_bits(&a_fmt))) return fail(MIX_E_ENUM, "%s: unknown MiX format %d", fn, enum_bits(&a_fmt));
   if (M < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
   if (M == 0) return MIX_OK;
   if (M > INT32_MAX || !image_k_ok(K)) return fail(MIX_E_SHAPE, "%s: K=%lld is not a positive multiple of 128", fn, (long long)K);
@@ -247,8 +275,8 @@ mix_status_t mix_quantize_gemm(mix_fmt_t fmt, const void* x, mix_dtype_t dtype, 
                                int64_t ldx, uint8_t* codes, void* shared, void* img, size_t img_bytes, void* stream) {
   g_err.clear();
   const char* fn = "mix_quantize_gemm";
-  if (fmt != MIX_4P25 && fmt != MIX_4P5) return fail(MIX_E_ENUM, "%s: unknown MiX format %d", fn, (int)fmt);
-  if (mix_status_t st = check_dtype(dtype)) return st;
+  if (!mix_known(enum_bits(&fmt))) return fail(MIX_E_ENUM, "%s: unknown MiX format %d", fn, enum_bits(&fmt));
+  if (mix_status_t st = check_dtype(enum_bits(&dtype))) return st;
   bool empty;
   if (mix_status_t st = check_matrix_in(fn, x, dtype, rows, cols, ldx, &empty)) return st;
   if (rows == 0) return MIX_OK;
@@ -267,7 +295,7 @@ mix_status_t mx_gemm_b_image(mx_fmt_t b_fmt, const uint8_t* b_codes, const uint8
                              void* img, size_t img_bytes, void* stream) {
   g_err.clear();
   const char* fn = "mx_gemm_b_image";
-  if (!mx_known(b_fmt)) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (!mx_known(enum_bits(&b_fmt))) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, enum_bits(&b_fmt));
   if (mx_g16(b_fmt)) return fail(MIX_E_UNSUPPORTED, "%s: g16 weights: use mx_gemm_b_image_g16", fn);
   if (N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
   if (N == 0) return MIX_OK;
@@ -282,7 +310,8 @@ mix_status_t mx_gemm_b_image_g16(mx_fmt_t b_fmt, const uint8_t* b_codes, const u
                                  int64_t K, void* img, size_t img_bytes, uint32_t* unfoldable, void* stream) {
   g_err.clear();
   const char* fn = "mx_gemm_b_image_g16";
-  if (!mx_g16(b_fmt)) return fail(MIX_E_ENUM, "%s: format %d is not a g16 format", fn, (int)b_fmt);
+  if (enum_bits(&b_fmt) != MX_INT4_G16 && enum_bits(&b_fmt) != MX_FP4_G16)
+    return fail(MIX_E_ENUM, "%s: format %d is not a g16 format", fn, enum_bits(&b_fmt));
   if (N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
   if (N == 0) return MIX_OK;
   if (N > INT32_MAX || !image_k_ok(K)) return fail(MIX_E_SHAPE, "%s: K=%lld is not a positive multiple of 128", fn, (long long)K);
@@ -300,8 +329,8 @@ mix_status_t mix_mx_gemm_images(mx_fmt_t b_fmt, const void* a_img, const void* b
                                 void* stream) {
   g_err.clear();
   const char* fn = "mix_mx_gemm_images";
-  if (!mx_known(b_fmt)) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
-  if (mix_status_t st = check_dtype(c_dtype)) return st;
+  if (!mx_known(enum_bits(&b_fmt))) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, enum_bits(&b_fmt));
+  if (mix_status_t st = check_dtype(enum_bits(&c_dtype))) return st;
   if (M < 0 || N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
   if (M == 0 || N == 0) return MIX_OK;
   if (M > INT32_MAX || N > INT32_MAX || !image_k_ok(K))
@@ -324,7 +353,7 @@ mix_status_t mix_mx_gemm_images_quantize(mx_fmt_t b_fmt, const void* a_img, cons
                                          void* q_shared, void* q_img, size_t q_img_bytes, void* stream) {
   g_err.clear();
   const char* fn = "mix_mx_gemm_images_quantize";
-  if (!mx_known(b_fmt)) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (!mx_known(enum_bits(&b_fmt))) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, enum_bits(&b_fmt));
   if (M < 0 || N < 0 || K < 0) return fail(MIX_E_SHAPE, "%s: negative extent", fn);
   if (M == 0 || N == 0) return MIX_OK;
   if (M > INT32_MAX || N > INT32_MAX || !image_k_ok(K))
@@ -355,7 +384,7 @@ mix_status_t mix_mx_gemm_images_quantize(mx_fmt_t b_fmt, const void* a_img, cons
 
 mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, int64_t ldk, float* mu, void* stream) {
   g_err.clear();
-  if (mix_status_t st = check_dtype(dtype)) return st;
+  if (mix_status_t st = check_dtype(enum_bits(&dtype))) return st;
   if (T < 0 || C < 0) return fail(MIX_E_SHAPE, "mix_kmean: negative extent");
   if (C == 0) return MIX_OK;
   if (T == 0) return fail(MIX_E_SHAPE, "mix_kmean: the mean of zero tokens is undefined");
@@ -368,7 +397,7 @@ mix_status_t mix_kmean(const void* k, mix_dtype_t dtype, int64_t T, int64_t C, i
 }
 
 size_t mix_underflow_map_workspace_bytes(int64_t rows, int64_t cols) {
-  if (rows <= 0 || cols <= 0 || cols % 32 || rows > INT32_MAX) return 0;
+  if (rows <= 0 || cols <= 0 || cols % 32 || rows > INT32_MAX || cols > INT32_MAX || rows * cols > kMaxElems) return 0;
   return mix::uf_plan(rows, cols).bytes;
 }
 
@@ -376,7 +405,7 @@ mix_status_t mix_underflow_map(const void* x, mix_dtype_t dtype, int64_t rows, i
                                const float* mu, uint32_t* counts, float* amax, void* ws, size_t ws_bytes,
                                void* stream) {
   g_err.clear();
-  if (mix_status_t st = check_dtype(dtype)) return st;
+  if (mix_status_t st = check_dtype(enum_bits(&dtype))) return st;
   bool empty;
   if (mix_status_t st = check_matrix_in("mix_underflow_map", x, dtype, rows, cols, ldx, &empty)) return st;
   if (rows > INT32_MAX) return fail(MIX_E_SHAPE, "mix_underflow_map: rows above 2^31-1");
@@ -400,8 +429,19 @@ mix_status_t mix_underflow_map(const void* x, mix_dtype_t dtype, int64_t rows, i
 // ---------------------------------------------------------------- attention
 extern "C" {
 
+// Extents the attention entry points accept (each checked before any product of them is formed).
+static bool prefill_extents_ok(int64_t T, int64_t Hq, int64_t Hkv, int64_t d) {
+  return T <= (1 << 24) && Hq <= (1 << 20) && Hkv <= Hq && d <= (1 << 20) && Hq * d <= (1 << 20);
+}
+
+static bool decode_extents_ok(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t L) {
+  if (B > (1 << 20) || Hq > (1 << 20) || Hkv > (1 << 20) || d > 1024 || L > INT32_MAX) return false;
+  const int64_t bh = B * (Hq > Hkv ? Hq : Hkv);   // below 2^40
+  return bh <= (1 << 24) && bh * L <= kMaxElems && bh * L * d <= kMaxElems;
+}
+
 size_t mix_attn_prefill_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t d) {
-  if (T <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return 0;
+  if (T <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || !prefill_extents_ok(T, Hq, Hkv, d)) return 0;
   return mix::attn_prefill_ws_bytes(T, Hq, Hkv, d);
 }
 
@@ -413,7 +453,7 @@ mix_status_t mix_attn_prefill(const void* q, const void* k, const void* v, int64
   if (T == 0 || Hq == 0 || d == 0) return MIX_OK;
   if (Hkv == 0 || Hq % Hkv) return fail(MIX_E_SHAPE, "mix_attn_prefill: Hq=%lld is not a multiple of Hkv=%lld", (long long)Hq, (long long)Hkv);
   if (d % 32) return fail(MIX_E_SHAPE, "mix_attn_prefill: head dim %lld is not a multiple of 32", (long long)d);
-  if (T > (1 << 24) || Hq * d > (1 << 20)) return fail(MIX_E_SHAPE, "mix_attn_prefill: extent too large");
+  if (!prefill_extents_ok(T, Hq, Hkv, d)) return fail(MIX_E_SHAPE, "mix_attn_prefill: extent too large");
   if (!q || !k || !v || !mu || !o || !ws) return fail(MIX_E_NULL, "mix_attn_prefill: NULL pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(mu) || ((uintptr_t)ws & 255u) || ((uintptr_t)o & 1u))
     return fail(MIX_E_ALIGN, "mix_attn_prefill: q/k/v/mu must be 16-byte aligned and ws 256-byte aligned");
@@ -431,6 +471,8 @@ static mix_status_t check_cache(const char* fn, const mix_kv_cache_t* c) {
     return fail(MIX_E_NULL, "%s: a cache buffer is NULL", fn);
   if (c->B <= 0 || c->Hkv <= 0 || c->Lmax <= 0 || c->Lmax % 32 || c->d <= 0 || c->d % 32)
     return fail(MIX_E_SHAPE, "%s: bad cache extents (Lmax and d must be positive multiples of 32)", fn);
+  if (!decode_extents_ok(c->B, c->Hkv, c->Hkv, c->d, c->Lmax))
+    return fail(MIX_E_SHAPE, "%s: cache extents too large", fn);
   if (!aligned16(c->k_codes) || !aligned16(c->v_codes) || !aligned16(c->v_stage))
     return fail(MIX_E_ALIGN, "%s: cache code buffers must be 16-byte aligned", fn);
   return MIX_OK;
@@ -448,7 +490,7 @@ mix_status_t mix_kv_cache_prefill(const mix_kv_cache_t* cache, int64_t b, const 
 }
 
 size_t mix_attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_pos < 0) return 0;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_pos < 0 || max_pos >= INT32_MAX || !decode_extents_ok(B, Hq, Hkv, d, max_pos + 1)) return 0;
   return mix::attn_decode_ws_bytes(B, Hq, Hkv, d, max_pos);
 }
 
@@ -460,6 +502,8 @@ mix_status_t mix_attn_decode(const void* q, const void* k_new, const void* v_new
   if (Hq <= 0 || Hq % cache->Hkv) return fail(MIX_E_SHAPE, "mix_attn_decode: Hq must be a positive multiple of Hkv");
   if (cache->d != 128) return fail(MIX_E_UNSUPPORTED, "mix_attn_decode: head dim %lld (only 128 is implemented)", (long long)cache->d);
   if (Hq / cache->Hkv > 16) return fail(MIX_E_UNSUPPORTED, "mix_attn_decode: more than 16 query heads per KV head");
+  if (!decode_extents_ok(cache->B, Hq, cache->Hkv, cache->d, cache->Lmax))
+    return fail(MIX_E_SHAPE, "mix_attn_decode: extents too large");
   if (max_pos < 0 || max_pos >= cache->Lmax) return fail(MIX_E_SHAPE, "mix_attn_decode: max_pos=%lld outside [0, Lmax)", (long long)max_pos);
   if (!q || !k_new || !v_new || !pos || !mu || !o || !ws) return fail(MIX_E_NULL, "mix_attn_decode: NULL pointer");
   if (((uintptr_t)ws & 255u) || !aligned16(q) || ((uintptr_t)o & 7u) || ((uintptr_t)pos & 3u) || ((uintptr_t)mu & 3u))
@@ -472,19 +516,23 @@ mix_status_t mix_attn_decode(const void* q, const void* k_new, const void* v_new
 }
 
 size_t mix_decode_step_workspace_bytes(int64_t B, int64_t K, int64_t Hq, int64_t Hkv, int64_t d, int64_t max_pos) {
-  if (B <= 0 || K <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_pos < 0) return 0;
+  if (B <= 0 || K <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_pos < 0 || max_pos >= INT32_MAX || K > INT32_MAX ||
+      !decode_extents_ok(B, Hq, Hkv, d, max_pos + 1) || B * K > kMaxElems)
+    return 0;
   return mix::decode_step_ws_bytes(B, K, Hq, Hkv, d, max_pos);
 }
 
-static mix_status_t check_decode_step(const char* fn, const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt,
+static mix_status_t check_decode_step(const char* fn, const void* x, int64_t K, int64_t N, const mx_fmt_t* b_fmt,
                                       const void* b_img, void* y, const void* q, const void* k_new,
                                       const void* v_new, const mix_kv_cache_t* cache, const int32_t* pos,
                                       int64_t max_pos, int64_t Hq, const float* mu, void* o) {
   if (mix_status_t st = check_cache(fn, cache)) return st;
-  if (!mx_known(b_fmt)) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, (int)b_fmt);
+  if (!mx_known(enum_bits(b_fmt))) return fail(MIX_E_ENUM, "%s: unknown MX format %d", fn, enum_bits(b_fmt));
   if (Hq <= 0 || Hq % cache->Hkv) return fail(MIX_E_SHAPE, "%s: Hq must be a positive multiple of Hkv", fn);
   if (cache->d != 128) return fail(MIX_E_UNSUPPORTED, "%s: head dim %lld (only 128 is implemented)", fn, (long long)cache->d);
   if (Hq / cache->Hkv > 16) return fail(MIX_E_UNSUPPORTED, "%s: more than 16 query heads per KV head", fn);
+  if (!decode_extents_ok(cache->B, Hq, cache->Hkv, cache->d, cache->Lmax))
+    return fail(MIX_E_SHAPE, "%s: extents too large", fn);
   if (cache->B > 16) return fail(MIX_E_UNSUPPORTED, "%s: batch %lld above 16 (the weight stream's rows)", fn, (long long)cache->B);
   if (max_pos < 0 || max_pos >= cache->Lmax) return fail(MIX_E_SHAPE, "%s: max_pos=%lld outside [0, Lmax)", fn, (long long)max_pos);
   if (N <= 0 || N > INT32_MAX || !image_k_ok(K) || K > INT32_MAX)
@@ -504,7 +552,7 @@ mix_status_t mix_decode_step(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt
                              size_t ws_bytes, void* stream) {
   g_err.clear();
   const char* fn = "mix_decode_step";
-  if (mix_status_t st = check_decode_step(fn, x, K, N, b_fmt, b_img, y, q, k_new, v_new, cache, pos, max_pos, Hq, mu,
+  if (mix_status_t st = check_decode_step(fn, x, K, N, &b_fmt, b_img, y, q, k_new, v_new, cache, pos, max_pos, Hq, mu,
                                           o))
     return st;
   if (!ws) return fail(MIX_E_NULL, "%s: ws is NULL", fn);
@@ -524,7 +572,7 @@ mix_status_t mix_decode_step_static(const void* x, int64_t K, int64_t N, mx_fmt_
                                     const float* mu, void* o, void* stream) {
   g_err.clear();
   const char* fn = "mix_decode_step_static";
-  if (mix_status_t st = check_decode_step(fn, x, K, N, b_fmt, b_img, y, q, k_new, v_new, cache, pos, max_pos, Hq, mu,
+  if (mix_status_t st = check_decode_step(fn, x, K, N, &b_fmt, b_img, y, q, k_new, v_new, cache, pos, max_pos, Hq, mu,
                                           o))
     return st;
   const size_t need = mix::decode_step_ws_bytes(cache->B, K, Hq, cache->Hkv, cache->d, max_pos);
