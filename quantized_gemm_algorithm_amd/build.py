@@ -39,8 +39,14 @@ def common_flags():
     ]
 
 
+# per-source device code generation: the attention kernels feed their S tiles from the MFMA
+# straight to vector instructions, so their MFMA results go to ordinary VGPRs (no copies out of
+# the accumulation registers; 16 fewer moves per key tile of the prefill kernels)
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src, obj):
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -286,20 +286,23 @@ __global__ void __launch_bounds__(256) k_attn_rowmax(PrefillOps P, float* __rest
   if (g == 0 && q < P.T) smax[(int64_t)h * P.T + q] = mx;
 }
 
-// exp(x) for finite x <= 0: 2^(x log2 e), with x log2 e carried as t + pl (log2 e split into a
-// fp32 head and tail, the product's rounding error recovered exactly with an fma), the integer
-// part of t applied by ldexp and the remaining fraction in [-1/2, 1/2] by the hardware exp2.
-// Within about 2 ulp of the correctly rounded exponential; below exp(-160) the result is 0, as is
-// the fp32 rounding of the exact value.
+// exp(x) for finite x <= 0 as 2^t (1 + c): t = fp32(x L_HI) with L_HI the fp32 rounding of
+// log2 e, and c = d ln 2 for the remainder d = x log2 e - t, formed from the product's rounding
+// error (recovered exactly with an fma) and x times log2 e's tail. |d| < 2^-16 wherever 2^t is not
+// zero, so 2^d = 1 + d ln 2 up to d^2 (far below an ulp), and the hardware exp2 of t is within about
+// an ulp: p is within about 2 ulp of the correctly rounded exponential for p >= 2^-126. Below that
+// (x < -87.3) the hardware exp2 may return 0; such a p is under every P^ code threshold (at most
+// 2^-15 below the block maximum, which is >= 2^-7) and under half an ulp of l >= 1, so no output
+// depends on it.
 __device__ __forceinline__ float exp_nonpos(float x) {
   constexpr float L_HI = 1.44269502162933349609375f;   // fp32 rounding of log2 e
-  constexpr float L_LO = 1.925963033500011e-08f;       // log2 e - L_HI, rounded
-  x = fmaxf(x, -160.f);
+  constexpr float LN2 = 0.693147182464599609375f;      // fp32 rounding of ln 2
+  constexpr float K2 = 1.3349757743696955e-08f;        // (log2 e - L_HI) ln 2, rounded
   const float t = __fmul_rn(x, L_HI);
-  const float pl = __fmaf_rn(x, L_LO, __fmaf_rn(x, L_HI, -t));
-  const float e = __builtin_rintf(t);
-  const float f = __fadd_rn(__fsub_rn(t, e), pl);
-  return __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(f), (int)e);
+  const float et = __fmaf_rn(x, L_HI, -t);             // x L_HI - t, exactly
+  const float c = __fmaf_rn(et, LN2, __fmul_rn(x, K2));
+  const float y = __builtin_amdgcn_exp2f(t);
+  return __fmaf_rn(y, c, y);
 }
 
 // MiX-4.5b codes of 8 consecutive softmax weights p = a ++ b (non-negative, this lane's sub-block
@@ -367,8 +370,10 @@ __device__ __forceinline__ uint32_t p_code8_img(const float4& a, const float4& b
     const u16x2 gt = (PB2 - __builtin_bit_cast(u16x2, w)) >> (u16x2)15;   // a' > pb
     const u16x2 e7 = (cu + (u16x2)1) >> (u16x2)3;                          // d* == 7
     if (CODES) word |= __builtin_bit_cast(uint32_t, cu | ((gt & e7) << (u16x2)3)) << (4 * i);
-    const u16x2 zm = (e7 & ~gt) - (u16x2)1;                                // all ones unless zero
-    im[i] = __builtin_bit_cast(uint32_t, (M64 - (cu << (u16x2)3)) & zm);   // elements i (low), i + 4 (high)
+    // z = 1 where the element codes to zero: its byte is shifted out of the low byte that the
+    // perms below keep (elements i in the low half, i + 4 in the high half)
+    const u16x2 z = e7 & ~gt;
+    im[i] = __builtin_bit_cast(uint32_t, (M64 - (cu << (u16x2)3)) << (z << (u16x2)3));
   }
   out0 = __builtin_amdgcn_perm(im[1], im[0], 0x0C0C0400u) | __builtin_amdgcn_perm(im[3], im[2], 0x04000C0Cu);
   out1 = __builtin_amdgcn_perm(im[1], im[0], 0x0C0C0602u) | __builtin_amdgcn_perm(im[3], im[2], 0x06020C0Cu);
@@ -1093,7 +1098,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline int64_t prefill_vsp(int64_t Tp) { return (Tp / 32 + 3) / 4 * 4; }
 
 struct PrefillWs {
-  size_t qc, qs, kc, ks, vc, vs, s, pc, ps, l, total;
+  size_t qc, qs, kc, ks, vc, vs, s, pc, ps, l, km, total;
 };
 
 static PrefillWs prefill_layout(int64_t T, int64_t Hq, int64_t Hkv, int64_t d) {
@@ -1112,6 +1117,7 @@ static PrefillWs prefill_layout(int64_t T, int64_t Hq, int64_t Hkv, int64_t d) {
   w.pc = take((size_t)Hq * T * Tp / 2);
   w.ps = take((size_t)Hq * T * (Tp / 32) * 2);
   w.l = take((size_t)Hq * T * 4);
+  w.km = take(kmean_ws_bytes(T, Hkv * d));
   w.total = off;
   return w;
 }
@@ -1145,7 +1151,7 @@ hipError_t attn_prefill_run(const void* q, const void* k, const void* v, int64_t
   float* l = (float*)(base + w.l);
 
   // 1. K-mean; 2. coded operands
-  HIPCHK(launch_kmean(k, 1, T, Hkv * d, Hkv * d, mu, s));
+  HIPCHK(launch_kmean_ws(k, 1, T, Hkv * d, Hkv * d, mu, base + w.km, s));
   HIPCHK(launch_mx_quantize(1, k, 1, T, Hkv * d, Hkv * d, mu, kc, ks, s));
   HIPCHK(launch_mix_quantize(1, q, 1, T, Hq * d, Hq * d, qc, qs, s));
   const int64_t vsp = prefill_vsp(Tp);

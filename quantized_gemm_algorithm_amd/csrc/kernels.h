@@ -19,6 +19,10 @@ hipError_t launch_mix_dequantize(int fmt, const uint8_t* codes, const void* shar
 hipError_t launch_mx_dequantize(int fp4, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                                 float* out, hipStream_t s, int g16 = 0);
 hipError_t launch_kmean(const void* x, int dtype, int64_t T, int64_t C, int64_t ldx, float* mu, hipStream_t s);
+// the K-mean in two launches through a workspace of kmean_ws_bytes(T, C) bytes (8-byte aligned)
+size_t kmean_ws_bytes(int64_t T, int64_t C);
+hipError_t launch_kmean_ws(const void* x, int dtype, int64_t T, int64_t C, int64_t ldx, float* mu, void* ws,
+                           hipStream_t s);
 // underflow.hip: counts [7][cols] (MXINT4, MXFP4 floor, MXFP4 ceil, NVFP4 B=32, MiX-4.25b, MiX-4.5b, nonzero)
 struct UfPlan {
   int64_t cb, rpw, gy, ablocks;   // 32-column blocks, rows per workgroup, workgroup rows, amax workgroups

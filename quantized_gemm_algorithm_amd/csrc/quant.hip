@@ -252,37 +252,75 @@ __global__ void __launch_bounds__(256) k_mx_quantize(const void* __restrict__ x,
 // transposed layout used for V along tokens). Rows beyond `rows` up to the padded count `prows`
 // are zero.
 template <int DT>
+struct MqcTile {
+  static constexpr int COLS = 64;                       // columns per workgroup
+  static constexpr int ROWS = 128;                      // rows per workgroup: four 32-row blocks
+  static constexpr int LPR = COLS * (DT == 1 ? 2 : 4) / 16;   // 16-byte loads per row
+  static constexpr int RPP = 256 / LPR;                 // rows per load pass of the workgroup
+};
+
+// A workgroup of 256 threads owns 64 columns x 128 rows: its loads read whole row segments (VEC:
+// 16 bytes a lane, consecutive lanes along the row; otherwise one element a lane, for inputs whose
+// rows are not 16-byte aligned), the tile is transposed through LDS, and thread t then codes the
+// 32-row block t >> 6 of column t & 63. Rows at or beyond `rows` read as zero.
+template <int DT, int VEC>
 __global__ void __launch_bounds__(256) k_mx_quantize_cols(const void* __restrict__ x, int64_t rows, int64_t prows,
                                                            int64_t cols, int64_t ldx, uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales, int64_t cpitch,
                                                            int64_t spitch) {
-  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t rb = blockIdx.y;  // 32-row block
-  if (c >= cols) return;
+  using TL = MqcTile<DT>;
+  constexpr int ESZ = DT == 1 ? 2 : 4;
+  __shared__ __align__(16) uint8_t tile[TL::ROWS * TL::COLS * ESZ];
+  const int64_t c0 = (int64_t)blockIdx.x * TL::COLS;
+  const int64_t r0 = (int64_t)blockIdx.y * TL::ROWS;
+  if (VEC) {
+    const int seg = threadIdx.x % TL::LPR, rr = threadIdx.x / TL::LPR;
+    const int64_t cl = c0 + seg * (16 / ESZ);           // first column of this lane's 16 bytes
+    uint4 v[TL::ROWS / TL::RPP];
+#pragma unroll
+    for (int p = 0; p < TL::ROWS / TL::RPP; p++) {
+      const int64_t r = r0 + rr + p * TL::RPP;
+      v[p] = make_uint4(0u, 0u, 0u, 0u);
+      if (r < rows && cl < cols) v[p] = *(const uint4*)((const uint8_t*)x + (r * ldx + cl) * ESZ);
+    }
+#pragma unroll
+    for (int p = 0; p < TL::ROWS / TL::RPP; p++)
+      *(uint4*)(tile + ((rr + p * TL::RPP) * TL::COLS + seg * (16 / ESZ)) * ESZ) = v[p];
+  } else {
+    for (int e = threadIdx.x; e < TL::ROWS * TL::COLS; e += 256) {
+      const int64_t r = r0 + e / TL::COLS, c = c0 + e % TL::COLS;
+      if (DT == 1) {
+        const uint16_t u = r < rows && c < cols ? ((const uint16_t*)x)[r * ldx + c] : (uint16_t)0;
+        ((uint16_t*)tile)[e] = u;
+      } else {
+        const uint32_t u = r < rows && c < cols ? ((const uint32_t*)x)[r * ldx + c] : 0u;
+        ((uint32_t*)tile)[e] = u;
+      }
+    }
+  }
+  __syncthreads();
+  const int c = threadIdx.x & 63, blk = threadIdx.x >> 6;
+  const int64_t cg = c0 + c, rb = r0 / 32 + blk;
+  if (cg >= cols || rb * 32 >= prows) return;
   uint32_t xb[32];
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < 32; i++) {
-    int64_t r = rb * 32 + i;
-    uint32_t v = 0;
-    if (r < rows) {
-      if (DT == 1) v = (uint32_t)((const uint16_t*)x)[r * ldx + c] << 16;
-      else v = ((const uint32_t*)x)[r * ldx + c];
-    }
-    xb[i] = v;
-    uint32_t a = v & 0x7FFFFFFFu;
+    const int e = (blk * 32 + i) * TL::COLS + c;
+    const uint32_t u = DT == 1 ? (uint32_t)((const uint16_t*)tile)[e] << 16 : ((const uint32_t*)tile)[e];
+    xb[i] = u;
+    const uint32_t a = u & 0x7FFFFFFFu;
     amax = a > amax ? a : amax;
   }
   uint32_t w[4] = {0, 0, 0, 0};
-  int X = mx_exponent(amax, 1);
+  const int X = mx_exponent(amax, 1);
   if (amax != 0) {
-    Fp4Thr r = fp4_thresholds(X);
+    const Fp4Thr r = fp4_thresholds(X);
 #pragma unroll
     for (int i = 0; i < 32; i++) w[i >> 3] |= fp4_code(xb[i], r) << (4 * (i & 7));
   }
-  uint4 o = {w[0], w[1], w[2], w[3]};
-  *(uint4*)(codes + c * cpitch + rb * 16) = o;
-  scales[c * spitch + rb] = amax ? (uint8_t)(X + 127) : (uint8_t)0;
+  *(uint4*)(codes + cg * cpitch + rb * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  scales[cg * spitch + rb] = amax ? (uint8_t)(X + 127) : (uint8_t)0;
 }
 
 // ------------------------------------------------------------------ decoders (debug / tests)
@@ -402,6 +440,87 @@ __global__ void __launch_bounds__(KM_THREADS) k_kmean(const void* __restrict__ x
   }
 }
 
+// The K-mean in two launches, for callers with a workspace: the first spreads the rows over the
+// whole GPU (workgroup (x, y): rows [KMP_ROWS y, KMP_ROWS (y + 1)) of 64 CW columns, each wave
+// reading whole row segments, 16 bytes a lane) and writes one exact pair per (row slice, column);
+// the second adds each column's pairs. Same result as k_kmean whenever the exact sum fits the pair.
+constexpr int KMP_ROWS = 16;
+
+template <int DT>
+__global__ void __launch_bounds__(256) k_kmean_part(const void* __restrict__ x, int64_t T, int64_t C, int64_t ldx,
+                                                    double2* __restrict__ part) {
+  constexpr int CW = DT == 1 ? 8 : 4;   // columns per lane (one 16-byte load)
+  __shared__ double2 red[4][64 * CW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t cbase = (int64_t)blockIdx.x * 64 * CW;
+  const int64_t c0 = cbase + (int64_t)lane * CW;
+  const int64_t r0 = (int64_t)blockIdx.y * KMP_ROWS;
+  DD acc[CW];
+#pragma unroll
+  for (int j = 0; j < CW; j++) acc[j] = DD{0.0, 0.0};
+  if (c0 < C) {
+    uint4 v[KMP_ROWS / 4];
+    // every load is issued before the first use: rows past T repeat row T - 1 and add zero
+#pragma unroll
+    for (int i = 0; i < KMP_ROWS / 4; i++) {
+      const int64_t t = min(r0 + wave + 4 * i, T - 1);
+      v[i] = DT == 1 ? *(const uint4*)((const uint16_t*)x + t * ldx + c0) : *(const uint4*)((const float*)x + t * ldx + c0);
+    }
+#pragma unroll
+    for (int i = 0; i < KMP_ROWS / 4; i++) {
+      const bool ok = r0 + wave + 4 * i < T;
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int j = 0; j < CW; j++) {
+        const float f = DT == 1 ? __uint_as_float(j & 1 ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16)) : __uint_as_float(w[j]);
+        acc[j] = dd_add(acc[j], ok ? (double)f : 0.0);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < CW; j++) red[wave][lane * CW + j] = make_double2(acc[j].hi, acc[j].lo);
+  __syncthreads();
+  for (int cc = threadIdx.x; cc < 64 * CW; cc += 256) {
+    DD sum{red[0][cc].x, red[0][cc].y};
+#pragma unroll
+    for (int w2 = 1; w2 < 4; w2++) sum = dd_add(sum, DD{red[w2][cc].x, red[w2][cc].y});
+    if (cbase + cc < C) part[(int64_t)blockIdx.y * C + cbase + cc] = make_double2(sum.hi, sum.lo);
+  }
+}
+
+// Workgroup of 256 threads per 32 columns: 8 threads per column each add every 8th row slice's pair,
+// then the 8 sums are added in LDS.
+__global__ void __launch_bounds__(256) k_kmean_fin(const double2* __restrict__ part, int64_t nslices, int64_t T,
+                                                   int64_t C, float* __restrict__ mu) {
+  __shared__ double2 red[8][32];
+  const int cc = threadIdx.x & 31, j = threadIdx.x >> 5;
+  const int64_t c = (int64_t)blockIdx.x * 32 + cc;
+  DD sum{0.0, 0.0};
+  if (c < C) {
+    int64_t p = j;
+    for (; p + 24 < nslices; p += 32) {   // four loads in flight
+      const double2 a = part[p * C + c], b = part[(p + 8) * C + c], e = part[(p + 16) * C + c],
+                    f = part[(p + 24) * C + c];
+      sum = dd_add(sum, DD{a.x, a.y});
+      sum = dd_add(sum, DD{b.x, b.y});
+      sum = dd_add(sum, DD{e.x, e.y});
+      sum = dd_add(sum, DD{f.x, f.y});
+    }
+    for (; p < nslices; p += 8) {
+      const double2 a = part[p * C + c];
+      sum = dd_add(sum, DD{a.x, a.y});
+    }
+  }
+  red[j][cc] = make_double2(sum.hi, sum.lo);
+  __syncthreads();
+  if (j == 0 && c < C) {
+    DD s2{red[0][cc].x, red[0][cc].y};
+#pragma unroll
+    for (int w2 = 1; w2 < 8; w2++) s2 = dd_add(s2, DD{red[w2][cc].x, red[w2][cc].y});
+    mu[c] = (float)((s2.hi + s2.lo) / (double)T);
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 
 static inline int grid_for(int64_t threads_needed) {
@@ -515,11 +634,17 @@ hipError_t launch_mx_quantize(int fp4, const void* x, int dtype, int64_t rows, i
 
 hipError_t launch_mx_quantize_cols(const void* x, int dtype, int64_t rows, int64_t prows, int64_t cols, int64_t ldx,
                                    uint8_t* codes, uint8_t* scales, int64_t cpitch, int64_t spitch, hipStream_t s) {
-  dim3 g((unsigned)((cols + 255) / 256), (unsigned)(prows / 32)), b(256);
-  if (dtype == 1)
-    hipLaunchKernelGGL((k_mx_quantize_cols<1>), g, b, 0, s, x, rows, prows, cols, ldx, codes, scales, cpitch, spitch);
-  else
-    hipLaunchKernelGGL((k_mx_quantize_cols<0>), g, b, 0, s, x, rows, prows, cols, ldx, codes, scales, cpitch, spitch);
+  dim3 g((unsigned)((cols + 63) / 64), (unsigned)((prows + 127) / 128)), b(256);
+  const int esz = dtype == 1 ? 2 : 4;
+  const bool vec = ((uintptr_t)x & 15) == 0 && (ldx * esz) % 16 == 0 && (cols * esz) % 16 == 0;
+#define MQC(DT, V) \
+  hipLaunchKernelGGL((k_mx_quantize_cols<DT, V>), g, b, 0, s, x, rows, prows, cols, ldx, codes, scales, cpitch, spitch)
+  if (dtype == 1) {
+    if (vec) MQC(1, 1); else MQC(1, 0);
+  } else {
+    if (vec) MQC(0, 1); else MQC(0, 0);
+  }
+#undef MQC
   return hipGetLastError();
 }
 
@@ -533,6 +658,21 @@ hipError_t launch_mx_dequantize(int fp4, const uint8_t* codes, const uint8_t* sc
                                 float* out, hipStream_t s, int g16) {
   hipLaunchKernelGGL(k_mx_dequantize, dim3(grid_for(rows * cols)), dim3(256), 0, s, fp4, g16, codes, scales, rows, cols,
                      out);
+  return hipGetLastError();
+}
+
+size_t kmean_ws_bytes(int64_t T, int64_t C) { return (size_t)((T + KMP_ROWS - 1) / KMP_ROWS) * C * 16; }
+
+hipError_t launch_kmean_ws(const void* x, int dtype, int64_t T, int64_t C, int64_t ldx, float* mu, void* ws,
+                           hipStream_t s) {
+  const int64_t nsl = (T + KMP_ROWS - 1) / KMP_ROWS;
+  const int64_t cw = dtype == 1 ? 8 : 4;
+  dim3 g((unsigned)((C + 64 * cw - 1) / (64 * cw)), (unsigned)nsl);
+  if (dtype == 1) hipLaunchKernelGGL((k_kmean_part<1>), g, dim3(256), 0, s, x, T, C, ldx, (double2*)ws);
+  else hipLaunchKernelGGL((k_kmean_part<0>), g, dim3(256), 0, s, x, T, C, ldx, (double2*)ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_kmean_fin, dim3((unsigned)((C + 31) / 32)), dim3(256), 0, s, (const double2*)ws, nsl, T, C, mu);
   return hipGetLastError();
 }
 

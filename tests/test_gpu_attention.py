@@ -4,7 +4,8 @@ Staged parity: every stage is checked against the oracle applied to the GPU's ow
 stage, so each comparison is exact or bounded:
   1. the K-mean is bit-exact;
   2. S is within the fp32 accumulation bound of the exact Q^ K^T;
-  3. the oracle's softmax of the GPU's S is within 4 ulp of the GPU's p (libm vs device exp);
+  3. the oracle's softmax of the GPU's S is within 4 ulp of the GPU's p (libm vs device exp; a
+     weight below 2^-126 may be flushed to 0, which no output depends on);
   4. the oracle's MiX-4.5b coding of the GPU's p reproduces the GPU's P^ bit for bit;
   5. O is the bf16 rounding of (P^ V^)/l within the accumulation bound, given the GPU's P^ and l.
 End to end against a fully independent oracle run the P codes may flip at midpoints (exp differs by
@@ -34,6 +35,19 @@ def _ulp_dist(a, b):
     a = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
     b = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
     return np.abs(a - b)
+
+
+TINY = np.float32(2.0 ** -126)
+
+
+def _p_close(p_gpu, p_ref):
+    """The GPU's p within 4 ulp of the oracle's correctly rounded softmax weight; a weight below
+    2^-126 may also come out as 0 (the device exponential may flush such results: they lie below
+    every P^ code threshold and below half an ulp of l >= 1, so no output depends on them)."""
+    p_gpu, p_ref = np.asarray(p_gpu, np.float32), np.asarray(p_ref, np.float32)
+    ok = _ulp_dist(p_gpu, p_ref) <= 4
+    ok |= (p_ref < TINY) & (p_gpu == 0)
+    return bool(np.all(ok))
 
 
 def _prefill_stages(g, T, Hq, Hkv, d, causal, rows, heads, e2e_heads=None):
@@ -81,7 +95,7 @@ def _prefill_stages(g, T, Hq, Hkv, d, causal, rows, heads, e2e_heads=None):
         p_ref, l_ref, _ = softmax_rows(s_gpu, n_valid, d)
         for t in range(len(rows)):
             nv = n_valid[t]
-            assert np.all(_ulp_dist(P[a, t, :nv], p_ref[t, :nv]) <= 4), (h, rows[t])
+            assert _p_close(P[a, t, :nv], p_ref[t, :nv]), (h, rows[t])
             nw = min(Tp, ((rows[t] + 1 + 255) // 256) * 256) if causal else Tp
             assert np.all(P[a, t, nv:nw] == 0)
             # l: fp32 sum of the GPU's p in another order
@@ -214,7 +228,7 @@ def _check_decode(r, Hq, Hkv, batch_rows=None, e2e_rows=None):
             p_ref, _, _ = softmax_rows(s_gpu, np.array([L]), d)
             P = r["dbg"]["p"][b, h]
             nw = ((L - 1) // 256 + 1) * 256  # the chunks this row's P^ is written for
-            assert np.all(_ulp_dist(P[:L], p_ref[0, :L]) <= 4), (b, h)
+            assert _p_close(P[:L], p_ref[0, :L]), (b, h)
             assert np.all(P[L:nw] == 0)
             pc_ref, ps_ref = o_mix_q(P[None, :nw].astype(np.float32), "4.5b", "f32")
             assert_codes_equal(r["dbg"]["p_codes"][b, h][None, : nw // 2], pc_ref, f"P codes b{b} h{h}")
@@ -234,6 +248,21 @@ def _check_decode(r, Hq, Hkv, batch_rows=None, e2e_rows=None):
         o_ind = (np.stack(full["o_bf16"][0]).astype(np.uint32) << 16).view(np.float32)
         o_gpu = (r["o"][b].astype(np.uint32) << 16).view(np.float32)
         assert np.abs(o_gpu - o_ind).max() <= 0.05 * (np.abs(o_ind).max() + 1e-30)
+
+
+@pytest.mark.parametrize("T,Hkv,d", [(1, 1, 128), (15, 2, 128), (17, 2, 64), (4097, 4, 128), (300, 3, 96)])
+def test_prefill_kmean_any_row_split(T, Hkv, d):
+    # the prefill K-mean sums row slices on many workgroups, then the slices: bit for bit the
+    # oracle's fp32 of the exact mean, for a T of one row, one partial slice, ragged tails, and head
+    # counts whose channel count is not a multiple of the 512-column wave width
+    q = _lib()
+    g = synth.attention_qkv(T=T, Hq=Hkv, Hkv=Hkv, d=d, seed_cfg=T)
+    kf = synth.bf16_bits_to_f32(g["k"]) * np.exp2(np.random.default_rng(T).integers(-8, 8, (T, Hkv, d)))
+    k = synth.f32_to_bf16_bits(kf.astype(np.float32))
+    _, mu, _ = q.mix_attn_prefill(dev_bf16(g["q"]), dev_bf16(k), dev_bf16(g["v"]), causal=True)
+    torch.cuda.synchronize()
+    assert_codes_equal(host(mu).reshape(-1).view(np.uint32), kmean_ref(k, "bf16").reshape(-1).view(np.uint32),
+                       f"mu T={T}")
 
 
 def test_decode_small_partial_blocks():

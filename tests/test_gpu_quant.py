@@ -129,7 +129,7 @@ def test_mx_quantize_exhaustive_bf16():
 def test_mx_quantize_cols_matches_transposed_rows():
     q = _lib()
     rng = np.random.default_rng(8)
-    for T in (32, 100, 256):
+    for T in (32, 100, 256, 300):
         v = _bf16((rng.standard_normal((T, 96)) * 3).astype(np.float32))
         codes, scales = q.mx_quantize_cols(dev_bf16(v))
         Tp = (T + 31) // 32 * 32
@@ -138,6 +138,36 @@ def test_mx_quantize_cols_matches_transposed_rows():
         want = o_mx_q(np.ascontiguousarray(vp.T), "fp4", "bf16")
         assert_codes_equal(host(codes), want[0], "codes")
         assert_codes_equal(host(scales), want[1], "scales")
+
+
+@pytest.mark.parametrize("T,cols,off,dtype", [(100, 36, 0, "bf16"), (130, 64, 3, "bf16"), (257, 200, 0, "bf16"),
+                                              (70, 48, 0, "f32"), (33, 20, 1, "f32"), (512, 128, 0, "f32")])
+def test_mx_quantize_cols_pitches_and_alignment(T, cols, off, dtype):
+    # column counts that are not a multiple of the 16-byte load, a view starting off a 16-byte
+    # boundary, a row pitch wider than the columns, fp32 input, rows past a 128-row tile
+    import torch
+    q = _lib()
+    rng = np.random.default_rng(T + cols)
+    vf = (rng.standard_normal((T, cols)) * np.exp2(rng.integers(-5, 5, (T, cols)))).astype(np.float32)
+    ld = cols + off + 8
+    if dtype == "bf16":
+        bits = _bf16(vf)
+        wide = np.zeros((T, ld), np.uint16)
+        wide[:, off:off + cols] = bits
+        x = dev_bf16(wide)[:, off:off + cols]
+        src, dt = bits, "bf16"
+    else:
+        wide = np.zeros((T, ld), np.float32)
+        wide[:, off:off + cols] = vf
+        x = torch.from_numpy(wide).cuda()[:, off:off + cols]
+        src, dt = vf, "f32"
+    codes, scales = q.mx_quantize_cols(x)
+    Tp = (T + 31) // 32 * 32
+    vp = np.zeros((Tp, cols), src.dtype)
+    vp[:T] = src
+    want = o_mx_q(np.ascontiguousarray(vp.T), "fp4", dt)
+    assert_codes_equal(host(codes), want[0], "codes")
+    assert_codes_equal(host(scales), want[1], "scales")
 
 
 def test_dequantizers_match_oracle():
