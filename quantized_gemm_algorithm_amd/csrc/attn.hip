@@ -215,16 +215,30 @@ __device__ __forceinline__ void q_operand(const PrefillOps& P, int q, int h, int
 constexpr int KST = PK * 64 + PK * 4;
 __device__ __forceinline__ int kswz(int kl) { return ((kl >> 1) ^ (kl >> 3)) & 3; }
 
+// a wave-uniform address as the scalar operand of a copy (the compiler may otherwise keep a value it
+// computed inside a loop in vector registers)
+__device__ __forceinline__ const uint8_t* sgpr_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // wave w copies keys 16 w .. 16 w + 15 of the tile at k0 (keys past T repeat key T-1 and are
-// masked later); wave 0 also copies the scales
+// masked later); wave 0 also copies the scales. Each copy reads from a wave-uniform base (the
+// tile's first key of KV head hk) plus a 32-bit lane offset, so a tile costs a few vector
+// instructions of addressing.
 __device__ __forceinline__ void k_stage(const PrefillOps& P, int hk, int k0, uint8_t* st) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kl = 16 * wave + (lane >> 2);
-  const int64_t krow = (int64_t)min(k0 + kl, P.T - 1) * P.Hkv + hk;
-  dma16(P.kc + krow * 64 + 16 * ((lane & 3) ^ kswz(kl)), __builtin_amdgcn_readfirstlane(lds_addr(st + wave * 1024)));
+  const int lim = P.T - 1 - k0;                       // the last key, relative to the tile
+  const int rs = P.Hkv * 64;                          // bytes between consecutive keys of one head
+  const uint8_t* kb = sgpr_ptr(P.kc + ((int64_t)k0 * P.Hkv + hk) * 64);
+  dma16s(kb, (uint32_t)(min(kl, lim) * rs + 16 * ((lane & 3) ^ kswz(kl))),
+         __builtin_amdgcn_readfirstlane(lds_addr(st + wave * 1024)));
   if (wave == 0) {
-    const int64_t srow = (int64_t)min(k0 + lane, P.T - 1) * P.Hkv + hk;
-    dma4(P.ks + srow * 4, __builtin_amdgcn_readfirstlane(lds_addr(st + PK * 64)));
+    const uint8_t* sb = sgpr_ptr(P.ks + ((int64_t)k0 * P.Hkv + hk) * 4);
+    dma4s(sb, (uint32_t)(min(lane, lim) * (P.Hkv * 4)), __builtin_amdgcn_readfirstlane(lds_addr(st + PK * 64)));
   }
 }
 
@@ -352,7 +366,10 @@ __device__ __forceinline__ uint32_t p_code8_img(const float4& a, const float4& b
   const uint32_t lmax = max(max(max(x[0], x[1]), max(x[2], x[3])), max(max(x[4], x[5]), max(x[6], x[7])));
   const uint32_t bmax = quad_max_dpp(lmax);
   const int emax = min(max((int)(bmax >> 23) - 127, -7), 8);
-  const uint32_t m = mant3_of(lmax);
+  // The image needs m only where some element codes nonzero, i.e. is above M 2^(Emax-8) >= 2^-15;
+  // a subnormal sub-block maximum (below 2^-126) has none, so its m may be the raw field bits.
+  // The code words and shared fields take the exact mantissa.
+  const uint32_t m = CODES ? mant3_of(lmax) : (lmax >> 20) & 7u;
   const uint32_t t3 = 24u + 3u * m;
   const uint32_t mu = t3 < 32u ? (((uint32_t)(emax + 126) << 7) | ((t3 << 3) & 0x7Fu))
                                : (((uint32_t)(emax + 127) << 7) | ((t3 << 2) & 0x7Fu));
@@ -360,6 +377,9 @@ __device__ __forceinline__ uint32_t p_code8_img(const float4& a, const float4& b
   const i16x2 MU1 = __builtin_bit_cast(i16x2, (mu + 128u) * 0x00010001u);
   const u16x2 PB2 = __builtin_bit_cast(u16x2, pb * 0x00010001u);
   const u16x2 M64 = __builtin_bit_cast(u16x2, (64u + m) * 0x00010001u);
+  // a' <= pb exactly when a' + (0xFFFF - pb) does not carry into bit 16, i.e. has bit 15 set
+  // (a' and pb are below 2^15: p is non-negative)
+  const u16x2 NPB = __builtin_bit_cast(u16x2, (0xFFFFu - pb) * 0x00010001u);
   uint32_t word = 0, im[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -367,12 +387,16 @@ __device__ __forceinline__ uint32_t p_code8_img(const float4& a, const float4& b
     i16x2 c = (MU1 - __builtin_bit_cast(i16x2, w)) >> (i16x2)7;
     c = __builtin_elementwise_min(__builtin_elementwise_max(c, (i16x2)0), (i16x2)7);
     const u16x2 cu = __builtin_bit_cast(u16x2, c);
-    const u16x2 gt = (PB2 - __builtin_bit_cast(u16x2, w)) >> (u16x2)15;   // a' > pb
-    const u16x2 e7 = (cu + (u16x2)1) >> (u16x2)3;                          // d* == 7
-    if (CODES) word |= __builtin_bit_cast(uint32_t, cu | ((gt & e7) << (u16x2)3)) << (4 * i);
-    // z = 1 where the element codes to zero: its byte is shifted out of the low byte that the
-    // perms below keep (elements i in the low half, i + 4 in the high half)
-    const u16x2 z = e7 & ~gt;
+    if (CODES) {
+      const u16x2 gt = (PB2 - __builtin_bit_cast(u16x2, w)) >> (u16x2)15;   // a' > pb
+      const u16x2 e7 = (cu + (u16x2)1) >> (u16x2)3;                          // d* == 7
+      word |= __builtin_bit_cast(uint32_t, cu | ((gt & e7) << (u16x2)3)) << (4 * i);
+    }
+    // z = 1 where the element codes to zero, which is where a' <= pb (pb lies below the midpoint
+    // between the dE = 6 and dE = 7 values, so such an element already has d* = 7). Its byte
+    // 64 + m - 8 d* is shifted out of the low byte that the perms below keep (elements i in the
+    // low half, i + 4 in the high half).
+    const u16x2 z = (__builtin_bit_cast(u16x2, w) + NPB) >> (u16x2)15;
     im[i] = __builtin_bit_cast(uint32_t, (M64 - (cu << (u16x2)3)) << (z << (u16x2)3));
   }
   out0 = __builtin_amdgcn_perm(im[1], im[0], 0x0C0C0400u) | __builtin_amdgcn_perm(im[3], im[2], 0x04000C0Cu);
@@ -412,16 +436,16 @@ __device__ __forceinline__ int vslot(int ch) { return ((ch >> 2) ^ (ch >> 3)) & 
 // wave w copies the V^ codes of channels 32 w .. 32 w + 31; waves 0 and 1 the scale dwords.
 // A chunk past Tp (the tile's upper half in the last tile) repeats chunk 0; its keys have p = 0.
 __device__ __forceinline__ void v_stage(const PrefillOps& P, int hk, int k0, uint8_t* st) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ch = 32 * wave + (lane >> 1);
   int c = (lane & 1) ^ vslot(ch);
   if (k0 + 32 * c >= P.Tp) c = 0;
-  dma16(P.vc + ((int64_t)hk * 128 + ch) * (P.Tp >> 1) + (k0 >> 1) + 16 * c,
-        __builtin_amdgcn_readfirstlane(lds_addr(st + wave * 1024)));
+  const uint8_t* vb = sgpr_ptr(P.vc + (int64_t)hk * 128 * (P.Tp >> 1) + (k0 >> 1));
+  dma16s(vb, (uint32_t)(ch * (P.Tp >> 1) + 16 * c), __builtin_amdgcn_readfirstlane(lds_addr(st + wave * 1024)));
   if (wave < 2) {
     const int ch2 = 64 * wave + lane;
-    dma4(P.vs + ((int64_t)hk * 128 + ch2) * P.vsp + ((k0 >> 5) & ~3),
-         __builtin_amdgcn_readfirstlane(lds_addr(st + 128 * 32 + wave * 256)));
+    const uint8_t* sb = sgpr_ptr(P.vs + (int64_t)hk * 128 * P.vsp + ((k0 >> 5) & ~3));
+    dma4s(sb, (uint32_t)(ch2 * P.vsp), __builtin_amdgcn_readfirstlane(lds_addr(st + 128 * 32 + wave * 256)));
   }
 }
 
