@@ -1174,12 +1174,17 @@ hipError_t attn_prefill_run(const void* q, const void* k, const void* v, int64_t
   uint16_t* ps = (uint16_t*)(base + w.ps);
   float* l = (float*)(base + w.l);
 
-  // 1. K-mean; 2. coded operands
-  HIPCHK(launch_kmean_ws(k, 1, T, Hkv * d, Hkv * d, mu, base + w.km, s));
-  HIPCHK(launch_mx_quantize(1, k, 1, T, Hkv * d, Hkv * d, mu, kc, ks, s));
-  HIPCHK(launch_mix_quantize(1, q, 1, T, Hq * d, Hq * d, qc, qs, s));
+  // 1. Q^, V^ and the K-mean's row-slice pairs in one launch; the K-mean; K^ (smoothed by it)
   const int64_t vsp = prefill_vsp(Tp);
-  HIPCHK(launch_mx_quantize_cols(v, 1, T, Tp, Hkv * d, Hkv * d, vc, vs, Tp / 2, vsp, s));
+  PrefillOperandArgs oa{};
+  oa.q = (const uint16_t*)q; oa.cq = Hq * d; oa.ldq = Hq * d; oa.qc = qc; oa.qs = qs;
+  oa.v = (const uint16_t*)v; oa.cv = Hkv * d; oa.ldv = Hkv * d; oa.vc = vc; oa.vs = vs; oa.cpitch = Tp / 2;
+  oa.spitch = vsp;
+  oa.k = (const uint16_t*)k; oa.ck = Hkv * d; oa.ldk = Hkv * d; oa.part = (double2*)(base + w.km);
+  oa.T = T; oa.Tp = Tp;
+  HIPCHK(launch_prefill_operands(oa, s));
+  HIPCHK(launch_kmean_fin(base + w.km, T, Hkv * d, mu, s));
+  HIPCHK(launch_mx_quantize(1, k, 1, T, Hkv * d, Hkv * d, mu, kc, ks, s));
 
   const float scale = (float)(1.0 / sqrt((double)d));
   if (d == 128) {

@@ -23,6 +23,20 @@ hipError_t launch_kmean(const void* x, int dtype, int64_t T, int64_t C, int64_t 
 size_t kmean_ws_bytes(int64_t T, int64_t C);
 hipError_t launch_kmean_ws(const void* x, int dtype, int64_t T, int64_t C, int64_t ldx, float* mu, void* ws,
                            hipStream_t s);
+// its second launch alone (the pairs of the first are in part)
+hipError_t launch_kmean_fin(const void* part, int64_t T, int64_t C, float* mu, hipStream_t s);
+
+// The prefill attention's independent operand passes in one launch (bf16 inputs, rows 16-byte
+// aligned): V along tokens as MXFP4, the K-mean's row-slice pairs (finished by launch_kmean_fin)
+// and Q as MiX-4.5b. The launcher fills the role counts (nvx .. nq).
+struct PrefillOperandArgs {
+  const uint16_t* q; int64_t cq, ldq; uint8_t* qc; uint16_t* qs;             // Q [T, cq]
+  const uint16_t* v; int64_t cv, ldv; uint8_t* vc; uint8_t* vs; int64_t cpitch, spitch;   // V [T, cv]
+  const uint16_t* k; int64_t ck, ldk; double2* part;                          // K [T, ck]
+  int64_t T, Tp;
+  int64_t nvx, nv, nkx, nk, nq;
+};
+hipError_t launch_prefill_operands(const PrefillOperandArgs& a, hipStream_t s);
 // underflow.hip: counts [7][cols] (MXINT4, MXFP4 floor, MXFP4 ceil, NVFP4 B=32, MiX-4.25b, MiX-4.5b, nonzero)
 struct UfPlan {
   int64_t cb, rpw, gy, ablocks;   // 32-column blocks, rows per workgroup, workgroup rows, amax workgroups

@@ -117,21 +117,22 @@ __global__ void __launch_bounds__(1024) k_mix_quantize(const void* __restrict__ 
 // loads in flight while it codes the current one. Short-lived workgroups (one or two rows each)
 // left the GPU waiting on workgroup launches: about one resident wave per SIMD on average.
 // The coding, the outputs and their layout are those of k_mix_quantize.
+// The body as a device function of workgroup wg of nwg (so that a kernel with other roles can run
+// it on a part of its grid); pk_tbl is 128 uint4 of LDS.
 template <int FMT, int IMG>
-__global__ void __launch_bounds__(256) k_mix_quantize_seg(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
-                                                           int64_t ldx, uint8_t* __restrict__ codes,
-                                                           void* __restrict__ shared, uint8_t* __restrict__ a8,
-                                                           uint8_t* __restrict__ as_p, int tiles_m) {
-  __shared__ uint4 pk_tbl[128];   // block constants of the pair coder per (Emax, m)
-  mix_pk_table_fill(pk_tbl);
+__device__ __forceinline__ void mq_seg_body(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                                            uint8_t* __restrict__ codes, void* __restrict__ shared,
+                                            uint8_t* __restrict__ a8, uint8_t* __restrict__ as_p, int tiles_m,
+                                            int64_t nwg, int64_t wg, uint4* pk_tbl) {
+  mix_pk_table_fill(pk_tbl);   // block constants of the pair coder per (Emax, m)
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int spr = (int)(cols >> 3);                 // sub-blocks per row (a multiple of 4)
   const int nseg = (spr + 63) >> 6;                 // segments per row
-  const int64_t nw = (int64_t)gridDim.x * 4;        // waves in the grid
+  const int64_t nw = nwg * 4;                       // waves dealt tasks
   const int dq = (int)(nw / nseg), dr = (int)(nw % nseg);
-  const int64_t t0 = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t t0 = wg * 4 + wave;
   int64_t row = t0 / nseg;
   int seg = (int)(t0 % nseg);
   const int q = lane & 3;
@@ -185,6 +186,15 @@ __global__ void __launch_bounds__(256) k_mix_quantize_seg(const uint16_t* __rest
     seg = nsg;
     cur = nxt;
   }
+}
+
+template <int FMT, int IMG>
+__global__ void __launch_bounds__(256) k_mix_quantize_seg(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                           int64_t ldx, uint8_t* __restrict__ codes,
+                                                           void* __restrict__ shared, uint8_t* __restrict__ a8,
+                                                           uint8_t* __restrict__ as_p, int tiles_m) {
+  __shared__ uint4 pk_tbl[128];
+  mq_seg_body<FMT, IMG>(x, rows, cols, ldx, codes, shared, a8, as_p, tiles_m, gridDim.x, blockIdx.x, pk_tbl);
 }
 
 // ------------------------------------------------------------------ MX quantizer (K2), blocks along rows
@@ -263,16 +273,14 @@ struct MqcTile {
 // 16 bytes a lane, consecutive lanes along the row; otherwise one element a lane, for inputs whose
 // rows are not 16-byte aligned), the tile is transposed through LDS, and thread t then codes the
 // 32-row block t >> 6 of column t & 63. Rows at or beyond `rows` read as zero.
-template <int DT, int VEC>
-__global__ void __launch_bounds__(256) k_mx_quantize_cols(const void* __restrict__ x, int64_t rows, int64_t prows,
-                                                           int64_t cols, int64_t ldx, uint8_t* __restrict__ codes,
-                                                           uint8_t* __restrict__ scales, int64_t cpitch,
-                                                           int64_t spitch) {
+template <int DT, int VEC>   // workgroup (bx, by); tile: TL::ROWS * TL::COLS elements of LDS, 16-byte aligned
+__device__ __forceinline__ void mqc_body(const void* __restrict__ x, int64_t rows, int64_t prows, int64_t cols,
+                                         int64_t ldx, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                         int64_t cpitch, int64_t spitch, int64_t bx, int64_t by, uint8_t* tile) {
   using TL = MqcTile<DT>;
   constexpr int ESZ = DT == 1 ? 2 : 4;
-  __shared__ __align__(16) uint8_t tile[TL::ROWS * TL::COLS * ESZ];
-  const int64_t c0 = (int64_t)blockIdx.x * TL::COLS;
-  const int64_t r0 = (int64_t)blockIdx.y * TL::ROWS;
+  const int64_t c0 = bx * TL::COLS;
+  const int64_t r0 = by * TL::ROWS;
   if (VEC) {
     const int seg = threadIdx.x % TL::LPR, rr = threadIdx.x / TL::LPR;
     const int64_t cl = c0 + seg * (16 / ESZ);           // first column of this lane's 16 bytes
@@ -321,6 +329,16 @@ __global__ void __launch_bounds__(256) k_mx_quantize_cols(const void* __restrict
   }
   *(uint4*)(codes + cg * cpitch + rb * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   scales[cg * spitch + rb] = amax ? (uint8_t)(X + 127) : (uint8_t)0;
+}
+
+template <int DT, int VEC>
+__global__ void __launch_bounds__(256) k_mx_quantize_cols(const void* __restrict__ x, int64_t rows, int64_t prows,
+                                                           int64_t cols, int64_t ldx, uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales, int64_t cpitch,
+                                                           int64_t spitch) {
+  using TL = MqcTile<DT>;
+  __shared__ __align__(16) uint8_t tile[TL::ROWS * TL::COLS * (DT == 1 ? 2 : 4)];
+  mqc_body<DT, VEC>(x, rows, prows, cols, ldx, codes, scales, cpitch, spitch, blockIdx.x, blockIdx.y, tile);
 }
 
 // ------------------------------------------------------------------ decoders (debug / tests)
@@ -446,15 +464,15 @@ __global__ void __launch_bounds__(KM_THREADS) k_kmean(const void* __restrict__ x
 // the second adds each column's pairs. Same result as k_kmean whenever the exact sum fits the pair.
 constexpr int KMP_ROWS = 16;
 
+// workgroup (bx, by); red: 2 x 64 CW double2 of LDS (the four waves' pairs are added in two rounds)
 template <int DT>
-__global__ void __launch_bounds__(256) k_kmean_part(const void* __restrict__ x, int64_t T, int64_t C, int64_t ldx,
-                                                    double2* __restrict__ part) {
+__device__ __forceinline__ void kmp_body(const void* __restrict__ x, int64_t T, int64_t C, int64_t ldx,
+                                         double2* __restrict__ part, int64_t bx, int64_t by, double2* red) {
   constexpr int CW = DT == 1 ? 8 : 4;   // columns per lane (one 16-byte load)
-  __shared__ double2 red[4][64 * CW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t cbase = (int64_t)blockIdx.x * 64 * CW;
+  const int64_t cbase = bx * 64 * CW;
   const int64_t c0 = cbase + (int64_t)lane * CW;
-  const int64_t r0 = (int64_t)blockIdx.y * KMP_ROWS;
+  const int64_t r0 = by * KMP_ROWS;
   DD acc[CW];
 #pragma unroll
   for (int j = 0; j < CW; j++) acc[j] = DD{0.0, 0.0};
@@ -477,48 +495,93 @@ __global__ void __launch_bounds__(256) k_kmean_part(const void* __restrict__ x, 
       }
     }
   }
+  // waves 2, 3 hand their pairs to waves 0, 1; wave 1 then hands its sums to wave 0, which writes
+  double2* mine = red + (wave & 1) * 64 * CW + lane * CW;
+  if (wave >= 2) {
 #pragma unroll
-  for (int j = 0; j < CW; j++) red[wave][lane * CW + j] = make_double2(acc[j].hi, acc[j].lo);
+    for (int j = 0; j < CW; j++) mine[j] = make_double2(acc[j].hi, acc[j].lo);
+  }
   __syncthreads();
-  for (int cc = threadIdx.x; cc < 64 * CW; cc += 256) {
-    DD sum{red[0][cc].x, red[0][cc].y};
+  if (wave < 2) {
 #pragma unroll
-    for (int w2 = 1; w2 < 4; w2++) sum = dd_add(sum, DD{red[w2][cc].x, red[w2][cc].y});
-    if (cbase + cc < C) part[(int64_t)blockIdx.y * C + cbase + cc] = make_double2(sum.hi, sum.lo);
+    for (int j = 0; j < CW; j++) acc[j] = dd_add(acc[j], DD{mine[j].x, mine[j].y});
+  }
+  __syncthreads();
+  if (wave == 1) {
+#pragma unroll
+    for (int j = 0; j < CW; j++) red[lane * CW + j] = make_double2(acc[j].hi, acc[j].lo);
+  }
+  __syncthreads();
+  if (wave == 0 && c0 < C) {
+#pragma unroll
+    for (int j = 0; j < CW; j++) {
+      const DD sum = dd_add(acc[j], DD{red[lane * CW + j].x, red[lane * CW + j].y});
+      part[by * C + c0 + j] = make_double2(sum.hi, sum.lo);
+    }
   }
 }
 
-// Workgroup of 256 threads per 32 columns: 8 threads per column each add every 8th row slice's pair,
-// then the 8 sums are added in LDS.
+template <int DT>
+__global__ void __launch_bounds__(256) k_kmean_part(const void* __restrict__ x, int64_t T, int64_t C, int64_t ldx,
+                                                    double2* __restrict__ part) {
+  __shared__ double2 red[2 * 64 * (DT == 1 ? 8 : 4)];
+  kmp_body<DT>(x, T, C, ldx, part, blockIdx.x, blockIdx.y, red);
+}
+
+// The prefill attention's three independent operand passes in one launch: V^ coding along tokens
+// (workgroups [0, nv)), the K-mean's row-slice pairs ([nv, nv + nk)) and Q^ coding (the rest, dealt
+// the segment tasks of a grid of nq). The short roles come first so that they are dispatched
+// before the Q coder's workgroups take every slot. Inputs bf16, rows 16-byte aligned.
+__global__ void __launch_bounds__(256) k_prefill_operands(PrefillOperandArgs a) {
+  __shared__ __align__(16) uint8_t lds[MqcTile<1>::ROWS * MqcTile<1>::COLS * 2];   // 16 KB, every role's LDS
+  int64_t b = blockIdx.x;
+  if (b < a.nv) {
+    mqc_body<1, 1>(a.v, a.T, a.Tp, a.cv, a.ldv, a.vc, a.vs, a.cpitch, a.spitch, b % a.nvx, b / a.nvx, lds);
+    return;
+  }
+  b -= a.nv;
+  if (b < a.nk) {
+    kmp_body<1>(a.k, a.T, a.ck, a.ldk, a.part, b % a.nkx, b / a.nkx, (double2*)lds);
+    return;
+  }
+  b -= a.nk;
+  mq_seg_body<1, 0>(a.q, a.T, a.cq, a.ldq, a.qc, a.qs, nullptr, nullptr, 0, a.nq, b, (uint4*)lds);
+}
+
+// Workgroup of 256 threads per 8 columns: 32 threads per column each add every 32nd row slice's
+// pair (their loads issued together), then a tree in LDS adds the 32 sums.
 __global__ void __launch_bounds__(256) k_kmean_fin(const double2* __restrict__ part, int64_t nslices, int64_t T,
                                                    int64_t C, float* __restrict__ mu) {
-  __shared__ double2 red[8][32];
-  const int cc = threadIdx.x & 31, j = threadIdx.x >> 5;
-  const int64_t c = (int64_t)blockIdx.x * 32 + cc;
+  __shared__ double2 red[32][8];
+  const int cc = threadIdx.x & 7, j = threadIdx.x >> 3;
+  const int64_t c = (int64_t)blockIdx.x * 8 + cc;
   DD sum{0.0, 0.0};
   if (c < C) {
     int64_t p = j;
-    for (; p + 24 < nslices; p += 32) {   // four loads in flight
-      const double2 a = part[p * C + c], b = part[(p + 8) * C + c], e = part[(p + 16) * C + c],
-                    f = part[(p + 24) * C + c];
-      sum = dd_add(sum, DD{a.x, a.y});
-      sum = dd_add(sum, DD{b.x, b.y});
-      sum = dd_add(sum, DD{e.x, e.y});
-      sum = dd_add(sum, DD{f.x, f.y});
+    for (; p + 7 * 32 < nslices; p += 8 * 32) {   // eight loads in flight
+      double2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) v[u] = part[(p + 32 * u) * C + c];
+#pragma unroll
+      for (int u = 0; u < 8; u++) sum = dd_add(sum, DD{v[u].x, v[u].y});
     }
-    for (; p < nslices; p += 8) {
+    for (; p < nslices; p += 32) {
       const double2 a = part[p * C + c];
       sum = dd_add(sum, DD{a.x, a.y});
     }
   }
   red[j][cc] = make_double2(sum.hi, sum.lo);
-  __syncthreads();
-  if (j == 0 && c < C) {
-    DD s2{red[0][cc].x, red[0][cc].y};
 #pragma unroll
-    for (int w2 = 1; w2 < 8; w2++) s2 = dd_add(s2, DD{red[w2][cc].x, red[w2][cc].y});
-    mu[c] = (float)((s2.hi + s2.lo) / (double)T);
+  for (int h = 16; h >= 1; h >>= 1) {
+    __syncthreads();
+    if (j < h) {
+      const DD o{red[j + h][cc].x, red[j + h][cc].y};
+      const DD m{red[j][cc].x, red[j][cc].y};
+      const DD r = dd_add(m, o);
+      red[j][cc] = make_double2(r.hi, r.lo);
+    }
   }
+  if (j == 0 && c < C) mu[c] = (float)((red[0][cc].x + red[0][cc].y) / (double)T);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -661,6 +724,17 @@ hipError_t launch_mx_dequantize(int fp4, const uint8_t* codes, const uint8_t* sc
   return hipGetLastError();
 }
 
+hipError_t launch_prefill_operands(const PrefillOperandArgs& a0, hipStream_t s) {
+  PrefillOperandArgs a = a0;
+  a.nvx = (a.cv + MqcTile<1>::COLS - 1) / MqcTile<1>::COLS;
+  a.nv = a.nvx * ((a.Tp + MqcTile<1>::ROWS - 1) / MqcTile<1>::ROWS);
+  a.nkx = (a.ck + 512 - 1) / 512;
+  a.nk = a.nkx * ((a.T + KMP_ROWS - 1) / KMP_ROWS);
+  a.nq = mq_seg_grid(a.T, a.cq).x;
+  hipLaunchKernelGGL(k_prefill_operands, dim3((unsigned)(a.nv + a.nk + a.nq)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 size_t kmean_ws_bytes(int64_t T, int64_t C) { return (size_t)((T + KMP_ROWS - 1) / KMP_ROWS) * C * 16; }
 
 hipError_t launch_kmean_ws(const void* x, int dtype, int64_t T, int64_t C, int64_t ldx, float* mu, void* ws,
@@ -672,7 +746,13 @@ hipError_t launch_kmean_ws(const void* x, int dtype, int64_t T, int64_t C, int64
   else hipLaunchKernelGGL((k_kmean_part<0>), g, dim3(256), 0, s, x, T, C, ldx, (double2*)ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_kmean_fin, dim3((unsigned)((C + 31) / 32)), dim3(256), 0, s, (const double2*)ws, nsl, T, C, mu);
+  return launch_kmean_fin(ws, T, C, mu, s);
+}
+
+hipError_t launch_kmean_fin(const void* part, int64_t T, int64_t C, float* mu, hipStream_t s) {
+  const int64_t nsl = (T + KMP_ROWS - 1) / KMP_ROWS;
+  hipLaunchKernelGGL(k_kmean_fin, dim3((unsigned)((C + 7) / 8)), dim3(256), 0, s, (const double2*)part, nsl, T, C,
+                     mu);
   return hipGetLastError();
 }
 
