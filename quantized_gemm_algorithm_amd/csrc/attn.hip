@@ -224,21 +224,45 @@ __device__ __forceinline__ const uint8_t* sgpr_ptr(const uint8_t* p) {
   return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+// The V^ tile of 64 keys in LDS (defined below) puts the 16-byte chunk c of channel ch at slot
+// c ^ vslot(ch).
+__device__ __forceinline__ int vslot(int ch) { return ((ch >> 2) ^ (ch >> 3)) & 1; }
+
+// Lane offsets of the tile copies (relative to the tile's scalar base) for a tile with all 64 keys
+// below T: computed once per workgroup, so an inner tile's copies cost no vector addressing.
+struct KvOff {
+  uint32_t k, ks;   // K^ codes (wave w: keys 16 w .. 16 w + 15) and scales (wave 0: key = lane)
+  uint32_t v, vs;   // V^ codes (wave w: channels 32 w .. 32 w + 31) and scales (waves 0, 1)
+};
+__device__ __forceinline__ KvOff kv_offsets(const PrefillOps& P) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kl = 16 * wave + (lane >> 2), ch = 32 * wave + (lane >> 1);
+  KvOff o;
+  o.k = (uint32_t)(kl * P.Hkv * 64 + 16 * ((lane & 3) ^ kswz(kl)));
+  o.ks = (uint32_t)(lane * P.Hkv * 4);
+  o.v = (uint32_t)(ch * (P.Tp >> 1) + 16 * ((lane & 1) ^ vslot(ch)));
+  o.vs = (uint32_t)((64 * wave + lane) * P.vsp);
+  return o;
+}
+
 // wave w copies keys 16 w .. 16 w + 15 of the tile at k0 (keys past T repeat key T-1 and are
 // masked later); wave 0 also copies the scales. Each copy reads from a wave-uniform base (the
-// tile's first key of KV head hk) plus a 32-bit lane offset, so a tile costs a few vector
-// instructions of addressing.
-__device__ __forceinline__ void k_stage(const PrefillOps& P, int hk, int k0, uint8_t* st) {
+// tile's first key of KV head hk) plus a 32-bit lane offset; only the last tile recomputes the
+// offsets with its keys clamped.
+__device__ __forceinline__ void k_stage(const PrefillOps& P, int hk, int k0, uint8_t* st, const KvOff& o) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kl = 16 * wave + (lane >> 2);
-  const int lim = P.T - 1 - k0;                       // the last key, relative to the tile
-  const int rs = P.Hkv * 64;                          // bytes between consecutive keys of one head
+  uint32_t koff = o.k, ksoff = o.ks;
+  if (k0 + PK > P.T) {
+    const int kl = 16 * wave + (lane >> 2);
+    const int lim = P.T - 1 - k0;   // the last key, relative to the tile
+    koff = (uint32_t)(min(kl, lim) * P.Hkv * 64 + 16 * ((lane & 3) ^ kswz(kl)));
+    ksoff = (uint32_t)(min(lane, lim) * P.Hkv * 4);
+  }
   const uint8_t* kb = sgpr_ptr(P.kc + ((int64_t)k0 * P.Hkv + hk) * 64);
-  dma16s(kb, (uint32_t)(min(kl, lim) * rs + 16 * ((lane & 3) ^ kswz(kl))),
-         __builtin_amdgcn_readfirstlane(lds_addr(st + wave * 1024)));
+  dma16s(kb, koff, __builtin_amdgcn_readfirstlane(lds_addr(st + wave * 1024)));
   if (wave == 0) {
     const uint8_t* sb = sgpr_ptr(P.ks + ((int64_t)k0 * P.Hkv + hk) * 4);
-    dma4s(sb, (uint32_t)(min(lane, lim) * (P.Hkv * 4)), __builtin_amdgcn_readfirstlane(lds_addr(st + PK * 64)));
+    dma4s(sb, ksoff, __builtin_amdgcn_readfirstlane(lds_addr(st + PK * 64)));
   }
 }
 
@@ -276,14 +300,17 @@ __global__ void __launch_bounds__(256) k_attn_rowmax(PrefillOps P, float* __rest
   const int kend = P.causal ? min(qt * PQ + PQ, P.T) : P.T;    // keys any row of the tile sees
   const int nt = (kend + PK - 1) / PK;
   float mx = -INFINITY;
-  if (nt > 0) k_stage(P, hk, 0, kst[0]);
-  for (int it = 0; it < nt; it++) {
+  const KvOff ko = kv_offsets(P);
+  if (nt > 0) k_stage(P, hk, 0, kst[0], ko);
+  // one key tile from ring stage SG (a constant, so its LDS addresses are immediates)
+  auto tile = [&](int it, auto stage) {
+    constexpr int SG = decltype(stage)::value;
     const int k0 = it * PK;
     wait_vmcnt<0>();
-    __syncthreads();   // stage it is complete; every wave is done with the other stage
-    if (it + 1 < nt) k_stage(P, hk, k0 + PK, kst[(it + 1) & 1]);
+    __syncthreads();   // stage SG is complete; every wave is done with the other stage
+    if (it + 1 < nt) k_stage(P, hk, k0 + PK, kst[SG ^ 1], ko);
     v4f acc[4];
-    s_tile(kst[it & 1], r, g, qf, qsc, acc);
+    s_tile(kst[SG], r, g, qf, qsc, acc);
     if (k0 + PK <= nfull) {
 #pragma unroll
       for (int j = 0; j < 4; j++) mx = fmaxf(fmaxf(mx, fmaxf(acc[j][0], acc[j][1])), fmaxf(acc[j][2], acc[j][3]));
@@ -294,27 +321,30 @@ __global__ void __launch_bounds__(256) k_attn_rowmax(PrefillOps P, float* __rest
         for (int e = 0; e < 4; e++)
           if (k0 + 16 * j + 4 * g + e < nvalid) mx = fmaxf(mx, acc[j][e]);
     }
+  };
+  for (int it = 0; it < nt; it += 2) {
+    tile(it, std::integral_constant<int, 0>{});
+    if (it + 1 < nt) tile(it + 1, std::integral_constant<int, 1>{});
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   if (g == 0 && q < P.T) smax[(int64_t)h * P.T + q] = mx;
 }
 
-// exp(x) for finite x <= 0 as 2^t (1 + c): t = fp32(x L_HI) with L_HI the fp32 rounding of
-// log2 e, and c = d ln 2 for the remainder d = x log2 e - t, formed from the product's rounding
-// error (recovered exactly with an fma) and x times log2 e's tail. |d| < 2^-16 wherever 2^t is not
-// zero, so 2^d = 1 + d ln 2 up to d^2 (far below an ulp), and the hardware exp2 of t is within about
-// an ulp: p is within about 2 ulp of the correctly rounded exponential for p >= 2^-126. Below that
-// (x < -87.3) the hardware exp2 may return 0; such a p is under every P^ code threshold (at most
-// 2^-15 below the block maximum, which is >= 2^-7) and under half an ulp of l >= 1, so no output
-// depends on it.
+// exp(x) for finite x <= 0 as 2^t (1 + c): t = fp32(x L2E) with L2E the fp32 rounding of log2 e,
+// and c = x - t ln 2 (exact reals: e^x = 2^t e^(x - t ln 2)), formed by two fmas with ln 2 split
+// into LN2_HI + LN2_LO (Cody-Waite): x - t LN2_HI is rounded once and is tiny, so c carries an
+// absolute error near 2^-40. |c| < 2^-18 wherever 2^t is not zero, so e^c = 1 + c up to c^2 / 2
+// (far below an ulp), and the hardware exp2 of t is within about an ulp: p is within about 2 ulp of
+// the correctly rounded exponential for p >= 2^-126. Below that (x < -87.3) the hardware exp2 may
+// return 0; such a p is under every P^ code threshold (at most 2^-15 below the block maximum, which
+// is >= 2^-7) and under half an ulp of l >= 1, so no output depends on it. x = 0 gives 1 exactly.
 __device__ __forceinline__ float exp_nonpos(float x) {
-  constexpr float L_HI = 1.44269502162933349609375f;   // fp32 rounding of log2 e
-  constexpr float LN2 = 0.693147182464599609375f;      // fp32 rounding of ln 2
-  constexpr float K2 = 1.3349757743696955e-08f;        // (log2 e - L_HI) ln 2, rounded
-  const float t = __fmul_rn(x, L_HI);
-  const float et = __fmaf_rn(x, L_HI, -t);             // x L_HI - t, exactly
-  const float c = __fmaf_rn(et, LN2, __fmul_rn(x, K2));
+  constexpr float L2E = 1.44269502162933349609375f;         // fp32 rounding of log2 e
+  constexpr float LN2_HI = 0.693147182464599609375f;        // fp32 rounding of ln 2
+  constexpr float LN2_LO = -1.9046542121259335544891655e-9f;  // fp32 rounding of ln 2 - LN2_HI
+  const float t = __fmul_rn(x, L2E);
+  const float c = __fmaf_rn(-t, LN2_LO, __fmaf_rn(-t, LN2_HI, x));
   const float y = __builtin_amdgcn_exp2f(t);
   return __fmaf_rn(y, c, y);
 }
@@ -358,6 +388,10 @@ __device__ __forceinline__ uint32_t p_code8(const float4& a, const float4& b, in
 
 // p_code8 that also returns the 8 E4M3 bytes of the coded values in element order (the MFMA
 // operand of P^ V^): 64 + m - 8 d for a nonzero code d, 0 for zero.
+// The thresholds are those of p_code8 with the biased exponent eb = Emax + 127 folded in:
+// mu0 + 128 = 128 eb + 64 + D(m), where D(m) is the low part of the 16-bit pattern of the first
+// midpoint 1.5 M 2^(Emax-1) (D = 24 m below m = 3, where the midpoint stays in binade Emax - 1, and
+// 12 m + 32 from m = 3 on, where it reaches binade Emax), looked up from an 8-byte table by v_perm.
 template <bool CODES>   // CODES: also form the code word and the full shared field (else only Emax)
 __device__ __forceinline__ uint32_t p_code8_img(const float4& a, const float4& b, int quad_pos, uint32_t& shared,
                                                 uint32_t& out0, uint32_t& out1) {
@@ -365,21 +399,17 @@ __device__ __forceinline__ uint32_t p_code8_img(const float4& a, const float4& b
                          f32_bits(b.x), f32_bits(b.y), f32_bits(b.z), f32_bits(b.w)};
   const uint32_t lmax = max(max(max(x[0], x[1]), max(x[2], x[3])), max(max(x[4], x[5]), max(x[6], x[7])));
   const uint32_t bmax = quad_max_dpp(lmax);
-  const int emax = min(max((int)(bmax >> 23) - 127, -7), 8);
+  const uint32_t eb = min(max(bmax >> 23, 120u), 135u);   // Emax + 127, Emax in [-7, 8]
   // The image needs m only where some element codes nonzero, i.e. is above M 2^(Emax-8) >= 2^-15;
   // a subnormal sub-block maximum (below 2^-126) has none, so its m may be the raw field bits.
   // The code words and shared fields take the exact mantissa.
   const uint32_t m = CODES ? mant3_of(lmax) : (lmax >> 20) & 7u;
-  const uint32_t t3 = 24u + 3u * m;
-  const uint32_t mu = t3 < 32u ? (((uint32_t)(emax + 126) << 7) | ((t3 << 3) & 0x7Fu))
-                               : (((uint32_t)(emax + 127) << 7) | ((t3 << 2) & 0x7Fu));
-  const uint32_t pb = ((uint32_t)(emax + 119) << 7) | (m << 4);
-  const i16x2 MU1 = __builtin_bit_cast(i16x2, (mu + 128u) * 0x00010001u);
-  const u16x2 PB2 = __builtin_bit_cast(u16x2, pb * 0x00010001u);
+  const uint32_t dm = __builtin_amdgcn_perm(0x74685C50u, 0x44301800u, m | 0x0C0C0C00u);   // D(m)
+  const i16x2 MU1 = __builtin_bit_cast(i16x2, ((eb << 7) + dm + 64u) * 0x00010001u);
   const u16x2 M64 = __builtin_bit_cast(u16x2, (64u + m) * 0x00010001u);
-  // a' <= pb exactly when a' + (0xFFFF - pb) does not carry into bit 16, i.e. has bit 15 set
-  // (a' and pb are below 2^15: p is non-negative)
-  const u16x2 NPB = __builtin_bit_cast(u16x2, (0xFFFFu - pb) * 0x00010001u);
+  // a' > pb = M 2^(Emax-8) = 128 (eb - 8) + 16 m exactly when a' + (0x7FFF - pb) has bit 15 set
+  // (a' and pb are below 2^15: p is non-negative and at most 1)
+  const u16x2 NPB = __builtin_bit_cast(u16x2, (33791u - (((eb << 3) + m) << 4)) * 0x00010001u);
   uint32_t word = 0, im[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -387,22 +417,20 @@ __device__ __forceinline__ uint32_t p_code8_img(const float4& a, const float4& b
     i16x2 c = (MU1 - __builtin_bit_cast(i16x2, w)) >> (i16x2)7;
     c = __builtin_elementwise_min(__builtin_elementwise_max(c, (i16x2)0), (i16x2)7);
     const u16x2 cu = __builtin_bit_cast(u16x2, c);
+    // nz = 1 where the element codes nonzero (a' > pb; pb lies below the midpoint between the
+    // dE = 6 and dE = 7 values, so every element at or below it has d* = 7 and codes to zero)
+    const u16x2 nz = (__builtin_bit_cast(u16x2, w) + NPB) >> (u16x2)15;
     if (CODES) {
-      const u16x2 gt = (PB2 - __builtin_bit_cast(u16x2, w)) >> (u16x2)15;   // a' > pb
       const u16x2 e7 = (cu + (u16x2)1) >> (u16x2)3;                          // d* == 7
-      word |= __builtin_bit_cast(uint32_t, cu | ((gt & e7) << (u16x2)3)) << (4 * i);
+      word |= __builtin_bit_cast(uint32_t, cu | ((nz & e7) << (u16x2)3)) << (4 * i);
     }
-    // z = 1 where the element codes to zero, which is where a' <= pb (pb lies below the midpoint
-    // between the dE = 6 and dE = 7 values, so such an element already has d* = 7). Its byte
-    // 64 + m - 8 d* is shifted out of the low byte that the perms below keep (elements i in the
-    // low half, i + 4 in the high half).
-    const u16x2 z = (__builtin_bit_cast(u16x2, w) + NPB) >> (u16x2)15;
-    im[i] = __builtin_bit_cast(uint32_t, (M64 - (cu << (u16x2)3)) << (z << (u16x2)3));
+    // the byte 64 + m - 8 d* (16-bit arithmetic: + d* 0xFFF8), times nz; elements i in the low half,
+    // i + 4 in the high half
+    im[i] = __builtin_bit_cast(uint32_t, (M64 + cu * (u16x2)0xFFF8u) * nz);
   }
   out0 = __builtin_amdgcn_perm(im[1], im[0], 0x0C0C0400u) | __builtin_amdgcn_perm(im[3], im[2], 0x04000C0Cu);
   out1 = __builtin_amdgcn_perm(im[1], im[0], 0x0C0C0602u) | __builtin_amdgcn_perm(im[3], im[2], 0x06020C0Cu);
-  shared = CODES ? quad_or_dpp((quad_pos == 0 ? (uint32_t)(emax + 7) : 0u) | (m << (4 + 3 * quad_pos)))
-                 : (uint32_t)(emax + 7);
+  shared = CODES ? quad_or_dpp((quad_pos == 0 ? eb - 120u : 0u) | (m << (4 + 3 * quad_pos))) : eb - 120u;
   return word;
 }
 
@@ -431,21 +459,19 @@ __device__ __forceinline__ float p_tile(const v4f (&acc)[4], float scale, float 
 // scale dword per channel (the four 32-token blocks from floor(k0 / 128)).
 constexpr int VST = 128 * 32 + 128 * 4;
 constexpr int FST = KST + VST;   // one ring stage: the K^ tile, then the V^ tile
-__device__ __forceinline__ int vslot(int ch) { return ((ch >> 2) ^ (ch >> 3)) & 1; }
 
 // wave w copies the V^ codes of channels 32 w .. 32 w + 31; waves 0 and 1 the scale dwords.
-// A chunk past Tp (the tile's upper half in the last tile) repeats chunk 0; its keys have p = 0.
-__device__ __forceinline__ void v_stage(const PrefillOps& P, int hk, int k0, uint8_t* st) {
+// When the tile's upper half lies past Tp (Tp is a multiple of 32, so only in the last tile) every
+// chunk repeats chunk 0; those keys have p = 0.
+__device__ __forceinline__ void v_stage(const PrefillOps& P, int hk, int k0, uint8_t* st, const KvOff& o) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ch = 32 * wave + (lane >> 1);
-  int c = (lane & 1) ^ vslot(ch);
-  if (k0 + 32 * c >= P.Tp) c = 0;
+  uint32_t voff = o.v;
+  if (k0 + PK > P.Tp) voff = (uint32_t)((32 * wave + (lane >> 1)) * (P.Tp >> 1));
   const uint8_t* vb = sgpr_ptr(P.vc + (int64_t)hk * 128 * (P.Tp >> 1) + (k0 >> 1));
-  dma16s(vb, (uint32_t)(ch * (P.Tp >> 1) + 16 * c), __builtin_amdgcn_readfirstlane(lds_addr(st + wave * 1024)));
+  dma16s(vb, voff, __builtin_amdgcn_readfirstlane(lds_addr(st + wave * 1024)));
   if (wave < 2) {
-    const int ch2 = 64 * wave + lane;
     const uint8_t* sb = sgpr_ptr(P.vs + (int64_t)hk * 128 * P.vsp + ((k0 >> 5) & ~3));
-    dma4s(sb, (uint32_t)(ch2 * P.vsp), __builtin_amdgcn_readfirstlane(lds_addr(st + 128 * 32 + wave * 256)));
+    dma4s(sb, o.vs, __builtin_amdgcn_readfirstlane(lds_addr(st + 128 * 32 + wave * 256)));
   }
 }
 
@@ -511,20 +537,23 @@ __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* _
     }
   };
   const int ntc = (kend + PK - 1) / PK, nt = (kwrite + PK - 1) / PK;
+  const KvOff ko = kv_offsets(P);
   if (ntc > 0) {
-    k_stage(P, hk, 0, fst[0]);
-    v_stage(P, hk, 0, fst[0] + KST);
+    k_stage(P, hk, 0, fst[0], ko);
+    v_stage(P, hk, 0, fst[0] + KST, ko);
   }
-  for (int it = 0; it < ntc; it++) {
+  // one key tile from ring stage SG (a constant, so its LDS addresses are immediates)
+  auto tile = [&](int it, auto stage) {
+    constexpr int SG = decltype(stage)::value;
     const int k0 = it * PK;
     wait_vmcnt<0>();
     __syncthreads();
     if (DBG && pc && kprev >= 0) store_codes(kprev);
     if (it + 1 < ntc) {
-      k_stage(P, hk, k0 + PK, fst[(it + 1) & 1]);
-      v_stage(P, hk, k0 + PK, fst[(it + 1) & 1] + KST);
+      k_stage(P, hk, k0 + PK, fst[SG ^ 1], ko);
+      v_stage(P, hk, k0 + PK, fst[SG ^ 1] + KST, ko);
     }
-    const uint8_t* st = fst[it & 1];
+    const uint8_t* st = fst[SG];
     v4f acc[4];
     s_tile(st, r, g, qf, qsc, acc);
     if (k0 + PK <= nfull)
@@ -569,21 +598,29 @@ __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* _
     // O^T += V^ P^ over the tile's keys
     const uint4 pb = *(const uint4*)(pbw + r * 64 + 16 * (g ^ pswz(r)));
     const v8i pf = v8i{(int)pb.x, (int)pb.y, (int)pb.z, (int)pb.w, 0, 0, 0, 0};
-    const int psc = g < 2 ? (int)pbw[16 * 64 + r * 2 + g] : 127;
-    // lanes g = 2, 3 carry K elements [64, 128), where P^ is zero: any finite V^ data will do (FP4
-    // has no inf or NaN), with scale 1
+    // Lane g gives the scale of K block g. Blocks 2 and 3 (K elements [64, 128)) are zero in P^, so
+    // lanes g = 2, 3 may take any finite scale: they read the same bytes as lanes g - 2.
+    const int psc = pbw[16 * 64 + r * 2 + (g & 1)];
+    // V^ lanes g = 2, 3 carry K elements [64, 128) with the data of lanes g - 2 (finite FP4, times the
+    // zeros of P^). When the tile's upper 32 keys lie past Tp (the last tile only), their block has
+    // no scale in the cache (the byte may be anything), so K block 1 then takes scale 1: its P^ is 0.
     const uint8_t* sv = st + KST;
     const int vblk = ((k0 >> 5) & 3) + (g & 1);              // byte of this lane's block in the dword
-    const bool vlive = g < 2 && k0 + 32 * g < P.Tp;
+    const bool vtail = k0 + PK > P.Tp && (g & 1);
 #pragma unroll
     for (int t = 0; t < 8; t++) {
       const int ch = 16 * t + r;
       const uint4 vf = *(const uint4*)(sv + ch * 32 + 16 * ((g & 1) ^ vslot(ch)));
-      const int vsc = vlive ? (int)sv[128 * 32 + ch * 4 + vblk] : 127;
+      const int vraw = sv[128 * 32 + ch * 4 + vblk];
+      const int vsc = vtail ? 127 : vraw;
       const v8i vfa = v8i{(int)vf.x, (int)vf.y, (int)vf.z, (int)vf.w, 0, 0, 0, 0};
       acc_o[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vfa, pf, acc_o[t], 4, 0, 0, vsc, 0, psc);
       __builtin_amdgcn_sched_barrier(0);   // one V^ fragment live at a time
     }
+  };
+  for (int it = 0; it < ntc; it += 2) {
+    tile(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntc) tile(it + 1, std::integral_constant<int, 1>{});
   }
   if (DBG && pc) {
     if (kprev >= 0) store_codes(kprev);
