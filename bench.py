@@ -701,6 +701,34 @@ def streaming_ceiling(torch):
     return out
 
 
+def same_size_stream(torch, nbytes, kind, reps=20):
+    """A device copy (nbytes moved: nbytes / 2 read, nbytes / 2 written) or an int64 sum (nbytes
+    read) of the size one call of a streaming kernel moves, timed like that kernel: `reps`
+    back-to-back launches between two HIP events over buffers rotating through >= 320 MB, so each
+    launch reads from HBM. This is the rate a launch of that size reaches, start-up included."""
+    n = (nbytes // 2 if kind == "copy" else nbytes) // 256 * 256
+    nrot = max(2, -(-320_000_000 // n))
+    srcs = [torch.ones(n // 8, dtype=torch.int64, device="cuda") for _ in range(nrot)]
+    dsts = [torch.empty_like(srcs[0]) for _ in range(2)]
+    fn = (lambda i: dsts[i % 2].copy_(srcs[i % nrot])) if kind == "copy" else (lambda i: srcs[i % nrot].sum())
+    for i in range(2 * nrot):
+        fn(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    moved = 2 * n if kind == "copy" else n
+    del srcs, dsts
+    torch.cuda.empty_cache()
+    return {"bytes": moved, "ms": ms, "GB/s": moved / (ms * 1e-3) / 1e9,
+            "what": f"torch {'device copy' if kind == 'copy' else 'int64 sum'} of the same bytes, "
+                    f"{reps} back-to-back launches over rotating buffers"}
+
+
 def section(res):
     """A workload's result as a section of the default line (the contract keys dropped)."""
     keep = {k: v for k, v in res.items() if k not in ("n_gpus", "steps", "warmup", "settle_ms", "higher_is_better",
@@ -810,6 +838,14 @@ def main():
         ceil["quantizer_frac_of_copy"] = qz["GB/s"] / ceil["copy_GB/s"]
         ceil["quantizer_with_image_frac_of_copy"] = qz["with_a_image"]["GB/s"] / ceil["copy_GB/s"]
         ceil["decode_frac_of_read"] = res["decode"]["value"] / ceil["read_GB/s"]
+        # the same measurement at the size one call moves: a launch of 38 MB or 108 MB does not reach
+        # the 1 GiB rate (start-up and drain are a larger share of it)
+        cq = same_size_stream(torch, qz["algorithmic_bytes"], "copy")
+        cq["quantizer_frac"] = qz["GB/s"] / cq["GB/s"]
+        ceil["copy_quantizer_bytes"] = cq
+        rd = same_size_stream(torch, res["decode"]["roofline"]["algorithmic_bytes"], "read")
+        rd["decode_frac"] = res["decode"]["value"] / rd["GB/s"]
+        ceil["read_decode_bytes"] = rd
         res["streaming_ceiling"] = ceil
     print(json.dumps(res))
 
