@@ -346,11 +346,15 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   };
 
   // epilogue geometry: a pass stages a wave's 32 x CW outputs (128 bytes of each row) in its own
-  // region of the last ring slot, then stores whole 128-byte row segments
+  // region of the last ring slot, then stores whole 128-byte row segments. Rows are 128 bytes with
+  // the 16-byte chunk c of row r at slot c ^ (r & 7): every access stays 16-byte aligned (a padded
+  // 136-byte pitch makes the row read-backs unaligned, which costs this part about three times the
+  // LDS cycles of the whole staging) and the MFMA-layout writes of one chunk column spread over
+  // eight slots.
   constexpr int ES = C_BF16 ? 2 : 4;                 // output element size
   constexpr int CW = 128 / ES;                       // columns per pass (64 or 32)
   constexpr int JP = CW / 32;                        // MFMA column blocks per pass (2 or 1)
-  constexpr int PITCH = 128 + 8;                     // padded row pitch of the region
+  constexpr int PITCH = 128;                         // row pitch of the region
   constexpr int EPL = 16 / ES;                       // outputs per 16-byte chunk
   uint8_t* reg = smem + (NS - 1) * SB + wave * (32 * PITCH);
   const bool vec_ok = (g.ldc % EPL) == 0 && (((uintptr_t)g.c) & 15) == 0;
@@ -448,7 +452,8 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
 #pragma unroll
           for (int q = 0; q < 4; q++) {
             const int j = jp * JP + jj;
-            uint8_t* dst = reg + r * PITCH + (32 * jj + 8 * q + 4 * gq) * ES;
+            const int cb = (32 * jj + 8 * q + 4 * gq) * ES;   // byte of the row segment
+            uint8_t* dst = reg + r * PITCH + ((((cb >> 4) ^ r) & 7) << 4) + (cb & 15);
             const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
                         v3 = acc[i][j][4 * q + 3];
             if (C_BF16)
@@ -460,7 +465,10 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
           const int ch = lane & 7;
           uint4 v[4];
 #pragma unroll
-          for (int it = 0; it < 4; it++) v[it] = *(const uint4*)(reg + (it * 8 + (lane >> 3)) * PITCH + ch * 16);
+          for (int it = 0; it < 4; it++) {
+            const int row = it * 8 + (lane >> 3);
+            v[it] = *(const uint4*)(reg + row * PITCH + ((ch ^ row) & 7) * 16);
+          }
           uint8_t* out = (uint8_t*)g.c + ((int64_t)(mw + 32 * i + (lane >> 3)) * g.ldc + nw + jp * CW + ch * EPL) * ES;
           const int64_t step8 = (int64_t)8 * g.ldc * ES;   // 8 rows
 #pragma unroll
@@ -470,7 +478,7 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
 #pragma unroll
         for (int it = 0; it < 4; it++) {
           const int row = it * 8 + (lane >> 3), ch = lane & 7;
-          const uint4 v = *(const uint4*)(reg + row * PITCH + ch * 16);
+          const uint4 v = *(const uint4*)(reg + row * PITCH + ((ch ^ row) & 7) * 16);
           const int gm = mw + 32 * i + row, gn = nw + jp * CW + ch * EPL;
           if (OQ) {
             // this lane's 8 bf16 outputs are a MiX sub-block, the 4 lanes of a quad one 32-column
@@ -542,9 +550,9 @@ size_t gemm_f8_ws_bytes(int b_fp4, int64_t M, int64_t N, int64_t K) {
 
 template <int B_FP4, int C_BF16>
 constexpr size_t f8_lds_bytes() {
-  // the ring, whose last slot (and what lies past it) also holds the epilogue's 8 x 32 x 136 bytes
+  // the ring, whose last slot (and what lies past it) also holds the epilogue's 8 x 32 x 128 bytes
   const size_t ring = (size_t)F8Stage<B_FP4>::NS * F8Stage<B_FP4>::BYTES;
-  const size_t epi = (size_t)(F8Stage<B_FP4>::NS - 1) * F8Stage<B_FP4>::BYTES + (F8_THREADS / 64) * 32 * 136;
+  const size_t epi = (size_t)(F8Stage<B_FP4>::NS - 1) * F8Stage<B_FP4>::BYTES + (F8_THREADS / 64) * 32 * 128;
   return ring > epi ? ring : epi;
 }
 
