@@ -287,8 +287,11 @@ __device__ __forceinline__ int q_tile(const PrefillOps& P) {
 }
 
 // grid (Hq, ceil(T / 64)), block 256. smax [Hq, T]: max of S over the unmasked keys of each row.
+// Every workgroup is resident at once, so the pass lasts as long as its longest workgroups (the last
+// query tiles, which see every key), whose time is a chain of per-iteration latencies: each
+// iteration therefore takes two key tiles (a 4-slot ring, one barrier per pair of tiles).
 __global__ void __launch_bounds__(256) k_attn_rowmax(PrefillOps P, float* __restrict__ smax) {
-  __shared__ __align__(16) uint8_t kst[2][KST];
+  __shared__ __align__(16) uint8_t kst[4][KST];
   const int h = blockIdx.x, hk = h / (P.Hq / P.Hkv), qt = q_tile(P);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -304,15 +307,12 @@ __global__ void __launch_bounds__(256) k_attn_rowmax(PrefillOps P, float* __rest
   float mx = -INFINITY;
   const KvOff ko = kv_offsets(P);
   if (nt > 0) k_stage(P, hk, 0, kst[0], ko);
-  // one key tile from ring stage SG (a constant, so its LDS addresses are immediates)
-  auto tile = [&](int it, auto stage) {
-    constexpr int SG = decltype(stage)::value;
+  if (nt > 1) k_stage(P, hk, PK, kst[1], ko);
+  // the row maxima over key tile it, staged at st
+  auto tile = [&](int it, const uint8_t* st) {
     const int k0 = it * PK;
-    wait_vmcnt<0>();
-    __syncthreads();   // stage SG is complete; every wave is done with the other stage
-    if (it + 1 < nt) k_stage(P, hk, k0 + PK, kst[SG ^ 1], ko);
     v4f acc[4];
-    s_tile(kst[SG], r, g, qf, qsc, acc);
+    s_tile(st, r, g, qf, qsc, acc);
     if (k0 + PK <= nfull) {
 #pragma unroll
       for (int j = 0; j < 4; j++) mx = fmaxf(fmaxf(mx, fmaxf(acc[j][0], acc[j][1])), fmaxf(acc[j][2], acc[j][3]));
@@ -324,9 +324,20 @@ __global__ void __launch_bounds__(256) k_attn_rowmax(PrefillOps P, float* __rest
           if (k0 + 16 * j + 4 * g + e < nvalid) mx = fmaxf(mx, acc[j][e]);
     }
   };
-  for (int it = 0; it < nt; it += 2) {
-    tile(it, std::integral_constant<int, 0>{});
-    if (it + 1 < nt) tile(it + 1, std::integral_constant<int, 1>{});
+  // key tiles it and it + 1 from ring slots 2 H and 2 H + 1 (H a constant, so the LDS addresses are
+  // immediates)
+  auto pair = [&](int it, auto half) {
+    constexpr int H = decltype(half)::value;
+    wait_vmcnt<0>();
+    __syncthreads();   // both tiles are complete; every wave is done with the other two slots
+    if (it + 2 < nt) k_stage(P, hk, (it + 2) * PK, kst[2 * (H ^ 1)], ko);
+    if (it + 3 < nt) k_stage(P, hk, (it + 3) * PK, kst[2 * (H ^ 1) + 1], ko);
+    tile(it, kst[2 * H]);
+    if (it + 1 < nt) tile(it + 1, kst[2 * H + 1]);
+  };
+  for (int it = 0; it < nt; it += 4) {
+    pair(it, std::integral_constant<int, 0>{});
+    if (it + 2 < nt) pair(it + 2, std::integral_constant<int, 1>{});
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
