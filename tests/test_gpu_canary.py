@@ -103,6 +103,22 @@ def test_gemm_outputs_stay_inside(M, N, K, b_fmt):
             chk("quantized product C")
             chk_qc("quantized product codes")
             chk_qs("quantized product shared")
+            # with the next product's A image (N % 128 == 0), and with the code buffer 4 bytes off a
+            # 16-byte boundary (the epilogue's narrower stores)
+            nq = q.mix_gemm_a_image_bytes(M, N) if N % 128 == 0 else 0
+            for off in (0, 4):
+                qc2, chk_qc2 = _guarded(M * N // 2 + off, torch.uint8, 0xA5)
+                qs2, chk_qs2 = _guarded(M * N // 32, torch.int16, 0x5A)
+                qi2, chk_qi2 = _guarded(nq, torch.uint8, 0x3C) if nq else (None, None)
+                _, qc_o, qs_o, _ = q.mix_mx_gemm_images_quantize(
+                    ai, bi, keep_c=False, image=nq > 0, codes=qc2[off:].view(M, N // 2),
+                    shared=qs2.view(M, N // 32), q_image=qi2)
+                chk_qc2(f"quantized product codes (offset {off})")
+                chk_qs2(f"quantized product shared (offset {off})")
+                if nq:
+                    chk_qi2("quantized product image")
+                assert torch.equal(qc_o, qc.view(M, N // 2)) and torch.equal(qs_o, qs.view(M, N // 32)), \
+                    f"quantized outputs depend on the code buffer's alignment (offset {off})"
 
 
 @pytest.mark.parametrize("T,Hq,Hkv", [(200, 4, 1), (77, 6, 3)])
