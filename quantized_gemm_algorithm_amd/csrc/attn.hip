@@ -287,9 +287,10 @@ __device__ __forceinline__ int q_tile(const PrefillOps& P) {
 }
 
 // grid (Hq, ceil(T / 64)), block 256. smax [Hq, T]: max of S over the unmasked keys of each row.
-// Every workgroup is resident at once, so the pass lasts as long as its longest workgroups (the last
-// query tiles, which see every key), whose time is a chain of per-iteration latencies: each
-// iteration therefore takes two key tiles (a 4-slot ring, one barrier per pair of tiles).
+// When every workgroup fits on the GPU at once (4096 tokens x 28 heads: 1792 workgroups, eight per CU),
+// the pass lasts as long as its longest workgroups (the last query tiles, which see every key), whose
+// time is a chain of per-iteration latencies: each iteration therefore takes two key tiles (a 4-slot
+// ring, one barrier per pair of tiles).
 __global__ void __launch_bounds__(256) k_attn_rowmax(PrefillOps P, float* __restrict__ smax) {
   __shared__ __align__(16) uint8_t kst[4][KST];
   const int h = blockIdx.x, hk = h / (P.Hq / P.Hkv), qt = q_tile(P);
