@@ -39,12 +39,11 @@ def common_flags():
     ]
 
 
-# per-source device code generation for the attention kernels: their S tiles go from the MFMA
-# straight to vector instructions, so MFMA results are placed in ordinary VGPRs (no copies out of
-# the accumulation registers), and as no value there is ever a NaN (finite inputs; masked keys are
-# replaced, never used), fmax needs no NaN quieting of its operands (IEEE mode off): 16 fewer
-# instructions per key tile for each of the two
-EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# per-source device code generation for the attention kernels: as no value there is ever a NaN
+# (finite inputs; masked keys are replaced, never used), fmax needs no NaN quieting of its
+# operands. (Which MFMA forms they use, and so whether their results land in ordinary VGPRs, is set
+# by the register limits the kernels declare.)
+EXTRA = {"attn.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src, obj):

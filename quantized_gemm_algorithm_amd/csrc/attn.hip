@@ -286,12 +286,18 @@ __device__ __forceinline__ int q_tile(const PrefillOps& P) {
   return P.causal ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
 }
 
+// Kernels whose MFMA results feed vector code are limited to 256 registers a wave (two waves per
+// SIMD): the compiler then selects the MFMA forms that read and write ordinary VGPRs. With the
+// whole 512-register file allowed it selects the accumulation-register forms and copies every
+// product and every running sum between the two files on each key tile.
+#define MIX_MFMA_VGPR __attribute__((amdgpu_waves_per_eu(2)))
+
 // grid (Hq, ceil(T / 64)), block 256. smax [Hq, T]: max of S over the unmasked keys of each row.
 // When every workgroup fits on the GPU at once (4096 tokens x 28 heads: 1792 workgroups, eight per CU),
 // the pass lasts as long as its longest workgroups (the last query tiles, which see every key), whose
 // time is a chain of per-iteration latencies: each iteration therefore takes two key tiles (a 4-slot
 // ring, one barrier per pair of tiles).
-__global__ void __launch_bounds__(256) k_attn_rowmax(PrefillOps P, float* __restrict__ smax) {
+__global__ void __launch_bounds__(256) MIX_MFMA_VGPR k_attn_rowmax(PrefillOps P, float* __restrict__ smax) {
   __shared__ __align__(16) uint8_t kst[4][KST];
   const int h = blockIdx.x, hk = h / (P.Hq / P.Hkv), qt = q_tile(P);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -401,12 +407,14 @@ __device__ __forceinline__ uint32_t p_code8(const float4& a, const float4& b, in
 }
 
 // p_code8 that also returns the 8 E4M3 bytes of the coded values in element order (the MFMA
-// operand of P^ V^): 64 + m - 8 d for a nonzero code d, 0 for zero.
+// operand of P^ V^): 64 + m - 8 d for a nonzero code d, 0 for zero; the debug path's coder.
 // The thresholds are those of p_code8 with the biased exponent eb = Emax + 127 folded in:
 // mu0 + 128 = 128 eb + 64 + D(m), where D(m) is the low part of the 16-bit pattern of the first
 // midpoint 1.5 M 2^(Emax-1) (D = 24 m below m = 3, where the midpoint stays in binade Emax - 1, and
 // 12 m + 32 from m = 3 on, where it reaches binade Emax), looked up from an 8-byte table by v_perm.
-template <bool CODES>   // CODES: also form the code word and the full shared field (else only Emax)
+__device__ __forceinline__ uint32_t pd_of(uint32_t m) {
+  return __builtin_amdgcn_perm(0x74685C50u, 0x44301800u, m | 0x0C0C0C00u);
+}
 __device__ __forceinline__ uint32_t p_code8_img(const float4& a, const float4& b, int quad_pos, uint32_t& shared,
                                                 uint32_t& out0, uint32_t& out1) {
   const uint32_t x[8] = {f32_bits(a.x), f32_bits(a.y), f32_bits(a.z), f32_bits(a.w),
@@ -414,12 +422,8 @@ __device__ __forceinline__ uint32_t p_code8_img(const float4& a, const float4& b
   const uint32_t lmax = max(max(max(x[0], x[1]), max(x[2], x[3])), max(max(x[4], x[5]), max(x[6], x[7])));
   const uint32_t bmax = quad_max_dpp(lmax);
   const uint32_t eb = min(max(bmax >> 23, 120u), 135u);   // Emax + 127, Emax in [-7, 8]
-  // The image needs m only where some element codes nonzero, i.e. is above M 2^(Emax-8) >= 2^-15;
-  // a subnormal sub-block maximum (below 2^-126) has none, so its m may be the raw field bits.
-  // The code words and shared fields take the exact mantissa.
-  const uint32_t m = CODES ? mant3_of(lmax) : (lmax >> 20) & 7u;
-  const uint32_t dm = __builtin_amdgcn_perm(0x74685C50u, 0x44301800u, m | 0x0C0C0C00u);   // D(m)
-  const i16x2 MU1 = __builtin_bit_cast(i16x2, ((eb << 7) + dm + 64u) * 0x00010001u);
+  const uint32_t m = mant3_of(lmax);
+  const i16x2 MU1 = __builtin_bit_cast(i16x2, ((eb << 7) + pd_of(m) + 64u) * 0x00010001u);
   const u16x2 M64 = __builtin_bit_cast(u16x2, (64u + m) * 0x00010001u);
   // a' > pb = M 2^(Emax-8) = 128 (eb - 8) + 16 m exactly when a' + (0x7FFF - pb) has bit 15 set
   // (a' and pb are below 2^15: p is non-negative and at most 1)
@@ -434,18 +438,52 @@ __device__ __forceinline__ uint32_t p_code8_img(const float4& a, const float4& b
     // nz = 1 where the element codes nonzero (a' > pb; pb lies below the midpoint between the
     // dE = 6 and dE = 7 values, so every element at or below it has d* = 7 and codes to zero)
     const u16x2 nz = (__builtin_bit_cast(u16x2, w) + NPB) >> (u16x2)15;
-    if (CODES) {
-      const u16x2 e7 = (cu + (u16x2)1) >> (u16x2)3;                          // d* == 7
-      word |= __builtin_bit_cast(uint32_t, cu | ((nz & e7) << (u16x2)3)) << (4 * i);
-    }
+    const u16x2 e7 = (cu + (u16x2)1) >> (u16x2)3;                          // d* == 7
+    word |= __builtin_bit_cast(uint32_t, cu | ((nz & e7) << (u16x2)3)) << (4 * i);
     // the byte 64 + m - 8 d* (16-bit arithmetic: + d* 0xFFF8), times nz; elements i in the low half,
     // i + 4 in the high half
     im[i] = __builtin_bit_cast(uint32_t, (M64 + cu * (u16x2)0xFFF8u) * nz);
   }
   out0 = __builtin_amdgcn_perm(im[1], im[0], 0x0C0C0400u) | __builtin_amdgcn_perm(im[3], im[2], 0x04000C0Cu);
   out1 = __builtin_amdgcn_perm(im[1], im[0], 0x0C0C0602u) | __builtin_amdgcn_perm(im[3], im[2], 0x06020C0Cu);
-  shared = CODES ? quad_or_dpp((quad_pos == 0 ? eb - 120u : 0u) | (m << (4 + 3 * quad_pos))) : eb - 120u;
+  shared = quad_or_dpp((quad_pos == 0 ? eb - 120u : 0u) | (m << (4 + 3 * quad_pos)));
   return word;
+}
+
+// The E4M3 bytes of p_code8_img without the code words (the production path): the same decisions,
+// rearranged into fewer instructions. With a' the rounded-up 16-bit pattern of p and MU1 = mu0 + 128
+// (the pattern of 1.5 M 2^Emax), p_code8_img takes d* = clamp((MU1 - a') >> 7, 0, 7). Here
+// MU1 - a' >= 0 always: p <= lmax < (M + 1/8) 2^E(lmax) <= 1.5 M 2^Emax, since M is lmax's mantissa
+// cut to 3 bits and Emax >= E(lmax) (p <= 1 never meets the upper clamp of Emax), so d* needs no
+// lower clamp. The byte 64 + m - 8 d* is 8 (8 - d*) + m, and 8 - d* = max(e, 1) with
+// e = (a' + 1151 - MU1) >> 7 (8 - floor(n / 128) = floor((1151 - n) / 128) for an integer n). a' + K for
+// a block constant K is the high half of the one 32-bit sum x + (K << 16) + 0xFFFF. The element codes
+// nonzero where a' > pb, i.e. where (pb + 1151 - MU1) - (a' + 1151 - MU1) < 0; pb + 1151 - MU1 =
+// 63 + 16 m - D(m) does not depend on Emax. A subnormal sub-block maximum (below 2^-126) has no
+// element above pb >= 2^-15, so its m may be the raw field bits. Elements pair up as (2i, 2i + 1).
+// Returns eb = Emax + 127.
+__device__ __forceinline__ uint32_t p_img8(const float4& a, const float4& b, uint32_t& out0, uint32_t& out1) {
+  const uint32_t x[8] = {f32_bits(a.x), f32_bits(a.y), f32_bits(a.z), f32_bits(a.w),
+                         f32_bits(b.x), f32_bits(b.y), f32_bits(b.z), f32_bits(b.w)};
+  const uint32_t lmax = max(max(max(x[0], x[1]), max(x[2], x[3])), max(max(x[4], x[5]), max(x[6], x[7])));
+  const uint32_t bmax = quad_max_dpp(lmax);
+  const uint32_t eb = min(max(bmax >> 23, 120u), 135u);
+  const uint32_t m = (lmax >> 20) & 7u;
+  const uint32_t dm = pd_of(m);
+  const uint32_t c2 = ((1087u - dm - (eb << 7)) << 16) | 0xFFFFu;   // ((1151 - MU1) << 16) + 0xFFFF
+  const i16x2 PK = __builtin_bit_cast(i16x2, (63u + 16u * m - dm) * 0x00010001u);
+  const uint32_t m2 = m * 0x00010001u;
+  uint32_t im[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const i16x2 v = __builtin_bit_cast(i16x2, __builtin_amdgcn_perm(x[2 * i + 1] + c2, x[2 * i] + c2, 0x07060302u));
+    const i16x2 e = __builtin_elementwise_max(v >> (i16x2)7, (i16x2)1);
+    const uint32_t nzm = __builtin_bit_cast(uint32_t, (PK - v) >> (i16x2)15);
+    im[i] = ((__builtin_bit_cast(uint32_t, e) << 3) | m2) & nzm;   // e <= 8: no carry across halves
+  }
+  out0 = __builtin_amdgcn_perm(im[1], im[0], 0x06040200u);
+  out1 = __builtin_amdgcn_perm(im[3], im[2], 0x06040200u);
+  return eb;
 }
 
 // p = exp(fp32(S scale) - fp32(m scale)) of the lane's 16 scores into the wave's LDS p row, masked
@@ -503,8 +541,10 @@ __device__ __forceinline__ void v_stage(const PrefillOps& P, int hk, int k0, uin
 // PV: v_mfma_scale_f32_16x16x128_f8f6f4 with V^ (FP4, 16 channels) as A and P^ (E4M3, 16 queries)
 // as B, the tile's 64 keys as K elements [0, 64) and zeros above; result register e of lane
 // r + 16 g is O^T[channel 4 g + e][query r].
+// Four workgroups per CU (39.5 KB of LDS each): at most 128 registers a wave, which also selects the
+// VGPR forms of the MFMAs (the debug instantiation spills at that limit).
 template <bool DBG>   // DBG: the debug dumps (S, p, P^ codes and shared fields) are written
-__global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* __restrict__ smax, float scale,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) k_attn_pcode(PrefillOps P, const float* __restrict__ smax, float scale,
                                                      uint16_t* __restrict__ o, uint8_t* __restrict__ pc,
                                                      uint16_t* __restrict__ ps, float* __restrict__ l,
                                                      float* __restrict__ dbg_s, float* __restrict__ dbg_p) {
@@ -593,14 +633,17 @@ __global__ void __launch_bounds__(256) k_attn_pcode(PrefillOps P, const float* _
       const int rr = rr0 + 8 * pass;
       const float4 a = *(const float4*)&sp[wave][rr][kk];
       const float4 b = *(const float4*)&sp[wave][rr][kk + 4];
-      uint32_t e0, e1, sh;
-      const uint32_t word = p_code8_img<decltype(codes)::value>(a, b, lane & 3, sh, e0, e1);
+      uint32_t e0, e1, eb;
       if (decltype(codes)::value) {
-        cw[pass] = word;
+        uint32_t sh;
+        cw[pass] = p_code8_img(a, b, lane & 3, sh, e0, e1);
         cs[pass] = sh;
+        eb = (sh & 15u) + 120u;
+      } else {
+        eb = p_img8(a, b, e0, e1);
       }
       *(uint2*)(pbw + 256 * (kk >> 4) + 16 * rr + (kk & 8)) = make_uint2(e0, e1);
-      if ((lane & 3) == 0) pbw[16 * 64 + rr * 2 + (kk >> 5)] = (uint8_t)((sh & 15u) + 119u);
+      if ((lane & 3) == 0) pbw[16 * 64 + rr * 2 + (kk >> 5)] = (uint8_t)(eb - 1u);   // E8M0 2^(Emax-1)
     };
     if (DBG && pc) {
       code_pass(std::true_type{}, 0);
@@ -930,7 +973,7 @@ __device__ __forceinline__ void dec_xquant(const XqOps& o, int vb) {
 
 // grid nxq + 8 (nchunk + 1) ceil(B Hkv / 8), block 256: workgroups [0, nxq) code the linear's
 // activations (nxq a multiple of 8, 0 for attention alone), the rest run dec_scores.
-__global__ void __launch_bounds__(256) k_decode_scores(DecOps a, XqOps xq, int nxq) {
+__global__ void __launch_bounds__(256) MIX_MFMA_VGPR k_decode_scores(DecOps a, XqOps xq, int nxq) {
   const int vb = (int)blockIdx.x;
   if (vb < nxq) {
     dec_xquant(xq, vb);
