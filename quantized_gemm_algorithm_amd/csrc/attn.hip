@@ -186,7 +186,8 @@ struct PrefillOps {
   const uint8_t* kc;     // K^ codes [T, Hkv, d/2]
   const uint8_t* ks;     // K^ scales [T, Hkv, d/32]
   const uint8_t* vc;     // V^ codes [Hkv, d, Tp/2] (blocks along tokens)
-  const uint8_t* vs;     // V^ scales [Hkv, d, vsp] (vsp = Tp/32 rounded up to a multiple of 4)
+  const uint8_t* vs;     // V^ scales [Hkv, d, vsp] (vsp = Tp/32 rounded up to a multiple of 4; block Tp/32,
+                         // when it is padding, holds 127)
   int T, Tp, Hq, Hkv, causal, vsp;
 };
 
@@ -660,17 +661,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) k
     // lanes g = 2, 3 may take any finite scale: they read the same bytes as lanes g - 2.
     const int psc = pbw[16 * 64 + r * 2 + (g & 1)];
     // V^ lanes g = 2, 3 carry K elements [64, 128) with the data of lanes g - 2 (finite FP4, times the
-    // zeros of P^). When the tile's upper 32 keys lie past Tp (the last tile only), their block has
-    // no scale in the cache (the byte may be anything), so K block 1 then takes scale 1: its P^ is 0.
+    // zeros of P^). When the tile's upper 32 keys lie past Tp (the last tile only), K block 1 reads the
+    // scale byte after the last block, which the V coder sets to 127 (scale 1): its P^ is 0.
     const uint8_t* sv = st + KST;
     const int vblk = ((k0 >> 5) & 3) + (g & 1);              // byte of this lane's block in the dword
-    const bool vtail = k0 + PK > P.Tp && (g & 1);
 #pragma unroll
     for (int t = 0; t < 8; t++) {
       const int ch = 16 * t + r;
       const uint4 vf = *(const uint4*)(sv + ch * 32 + 16 * (g & 1));
-      const int vraw = sv[128 * 32 + ch * 4 + vblk];
-      const int vsc = vtail ? 127 : vraw;
+      const int vsc = sv[128 * 32 + ch * 4 + vblk];
       const v8i vfa = v8i{(int)vf.x, (int)vf.y, (int)vf.z, (int)vf.w, 0, 0, 0, 0};
       acc_o[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vfa, pf, acc_o[t], 4, 0, 0, vsc, 0, psc);
       __builtin_amdgcn_sched_barrier(0);   // one V^ fragment live at a time

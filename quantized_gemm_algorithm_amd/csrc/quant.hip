@@ -272,8 +272,11 @@ struct MqcTile {
 // A workgroup of 256 threads owns 64 columns x 128 rows: its loads read whole row segments (VEC:
 // 16 bytes a lane, consecutive lanes along the row; otherwise one element a lane, for inputs whose
 // rows are not 16-byte aligned), the tile is transposed through LDS, and thread t then codes the
-// 32-row block t >> 6 of column t & 63. Rows at or beyond `rows` read as zero.
-template <int DT, int VEC>   // workgroup (bx, by); tile: TL::ROWS * TL::COLS elements of LDS, 16-byte aligned
+// 32-row block t >> 6 of column t & 63. Rows at or beyond `rows` read as zero. With PAD, the scale
+// byte of block prows / 32 (the first block past the padded rows), when it lies inside the scale
+// row's pitch, is set to 127 (scale 1): a product that reads a whole 64-row tile of V^ past the end
+// then multiplies its zero weights by a finite scale.
+template <int DT, int VEC, int PAD = 0>   // workgroup (bx, by); tile: TL::ROWS * TL::COLS elements of LDS, 16-byte aligned
 __device__ __forceinline__ void mqc_body(const void* __restrict__ x, int64_t rows, int64_t prows, int64_t cols,
                                          int64_t ldx, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                          int64_t cpitch, int64_t spitch, int64_t bx, int64_t by, uint8_t* tile) {
@@ -309,7 +312,11 @@ __device__ __forceinline__ void mqc_body(const void* __restrict__ x, int64_t row
   __syncthreads();
   const int c = threadIdx.x & 63, blk = threadIdx.x >> 6;
   const int64_t cg = c0 + c, rb = r0 / 32 + blk;
-  if (cg >= cols || rb * 32 >= prows) return;
+  if (cg >= cols) return;
+  if (rb * 32 >= prows) {
+    if (PAD && rb * 32 == prows && rb < spitch) scales[cg * spitch + rb] = 127;
+    return;
+  }
   uint32_t xb[32];
   uint32_t amax = 0;
 #pragma unroll
@@ -536,7 +543,7 @@ __global__ void __launch_bounds__(256) k_prefill_operands(PrefillOperandArgs a) 
   __shared__ __align__(16) uint8_t lds[MqcTile<1>::ROWS * MqcTile<1>::COLS * 2];   // 16 KB, every role's LDS
   int64_t b = blockIdx.x;
   if (b < a.nv) {
-    mqc_body<1, 1>(a.v, a.T, a.Tp, a.cv, a.ldv, a.vc, a.vs, a.cpitch, a.spitch, b % a.nvx, b / a.nvx, lds);
+    mqc_body<1, 1, 1>(a.v, a.T, a.Tp, a.cv, a.ldv, a.vc, a.vs, a.cpitch, a.spitch, b % a.nvx, b / a.nvx, lds);
     return;
   }
   b -= a.nv;
