@@ -466,14 +466,15 @@ __device__ __forceinline__ uint32_t p_code8_img(const float4& a, const float4& b
 __device__ __forceinline__ uint32_t p_img8(const float4& a, const float4& b, uint32_t& out0, uint32_t& out1) {
   const uint32_t x[8] = {f32_bits(a.x), f32_bits(a.y), f32_bits(a.z), f32_bits(a.w),
                          f32_bits(b.x), f32_bits(b.y), f32_bits(b.z), f32_bits(b.w)};
-  const uint32_t lmax = max(max(max(x[0], x[1]), max(x[2], x[3])), max(max(x[4], x[5]), max(x[6], x[7])));
+  const uint32_t lmax = max(max(max(max(max(x[0], x[1]), x[2]), max(max(x[3], x[4]), x[5])), x[6]), x[7]);
   const uint32_t bmax = quad_max_dpp(lmax);
   const uint32_t eb = min(max(bmax >> 23, 120u), 135u);
   const uint32_t m = (lmax >> 20) & 7u;
   const uint32_t dm = pd_of(m);
-  const uint32_t c2 = ((1087u - dm - (eb << 7)) << 16) | 0xFFFFu;   // ((1151 - MU1) << 16) + 0xFFFF
-  const i16x2 PK = __builtin_bit_cast(i16x2, (63u + 16u * m - dm) * 0x00010001u);
   const uint32_t m2 = m * 0x00010001u;
+  const uint32_t c2 = 0x043FFFFFu - ((dm << 16) + (eb << 23));   // ((1151 - MU1) << 16) + 0xFFFF
+  // 63 + 16 m - D(m) for m = 0..7 in both halves, from a byte table
+  const i16x2 PK = __builtin_bit_cast(i16x2, __builtin_amdgcn_perm(0x3B37332Fu, 0x2B2F373Fu, m2 | 0x0C000C00u));
   uint32_t im[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -1156,19 +1157,24 @@ __device__ __forceinline__ void dec_combine(const DecOps& a, int vb) {
   const float* op = a.opart + qrow * a.nchunk * d + c;
   float l = 0.f, acc = 0.f;
   int k = 0;
-  for (; k + 8 <= n; k += 8) {
-    float lv[8], ov[8];
+  // all loads of a group in flight together (a full 8192-token history is one group of 32 chunks:
+  // one memory round trip), then the sums in chunk order
+  auto group = [&](auto width) {
+    constexpr int W = decltype(width)::value;
+    float lv[W], ov[W];
 #pragma unroll
-    for (int u = 0; u < 8; u++) {
+    for (int u = 0; u < W; u++) {
       lv[u] = lp[k + u];
       ov[u] = op[(int64_t)(k + u) * d];
     }
 #pragma unroll
-    for (int u = 0; u < 8; u++) {
+    for (int u = 0; u < W; u++) {
       l += lv[u];
       acc += ov[u];
     }
-  }
+  };
+  for (; k + 32 <= n; k += 32) group(std::integral_constant<int, 32>{});
+  for (; k + 8 <= n; k += 8) group(std::integral_constant<int, 8>{});
   for (; k < n; k++) {
     l += lp[k];
     acc += op[(int64_t)k * d];
