@@ -273,11 +273,16 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   if (ti >= csz) return;
   // Every workgroup runs tiles of the same length, so without a stagger all CUs would reach their
   // epilogues together and store every round's C in one burst, while they also issue the next
-  // tiles' first copies together. The workgroups of odd index within an XCD start about 6000 cycles
-  // (s_sleep 96 x 64) later, so the two halves' store bursts and first copies fall apart in time
-  // (measured with the outputs unchanged: 16384 x 5120 x 1280 104 -> 99 us, 4096 x 18944 x 3584
-  // 200 -> 196 us); only where each workgroup has at least two tiles.
-  if ((ix & 1) && csz >= 2 * gx) __builtin_amdgcn_s_sleep(96);
+  // tiles' first copies together. Part of the workgroups start about 6000 cycles (s_sleep 96 x 64)
+  // later, so the store bursts and first copies of the two sets fall apart in time: those that run
+  // one tile fewer than the rest (they finish early anyway), or the odd ones of an XCD when all run
+  // the same count; only where each workgroup has at least two tiles. Measured with the outputs
+  // unchanged: 16384 x 5120 x 1280 100-104 -> 97-99 us, 4096 x 18944 x 3584 187-200 -> 186-196 us.
+  {
+    const int rem = csz % gx;   // workgroups ix < rem run one tile more than the rest
+    const bool late = rem ? ix >= rem : (ix & 1);
+    if (late && csz >= 2 * gx) __builtin_amdgcn_s_sleep(96);
+  }
   int tm, tn;
   f8_tile(c0 + ti, tiles_m, tiles_n, tm, tn);
   // steps 0 .. NS - 2 of a tile
