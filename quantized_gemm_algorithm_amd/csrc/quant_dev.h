@@ -107,16 +107,19 @@ template <bool IMG>
 __device__ __forceinline__ uint32_t mix_pair(uint32_t x, const MixPk& k, uint32_t& img) {
   const u16x2 a = __builtin_bit_cast(u16x2, x & 0x7FFF7FFFu);
   const u16x2 s = __builtin_bit_cast(u16x2, x) >> (u16x2)15;
-  i16x2 c = (__builtin_bit_cast(i16x2, k.mu1) - __builtin_bit_cast(i16x2, a)) >> (i16x2)7;
-  c = __builtin_elementwise_max(c, (i16x2)0);
-  const u16x2 v = __builtin_elementwise_min(__builtin_bit_cast(u16x2, c), (u16x2)7 - s);
-  const u16x2 s7 = s << (u16x2)7;
+  // max((mu1 - a) >> 7, 0) as an unsigned saturating subtract and a logical shift (mu1 - a never
+  // leaves the signed 16-bit range: mu1 < 2^15 and a < 2^15)
+  const u16x2 c = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, k.mu1), a) >> (u16x2)7;
+  const u16x2 v = __builtin_elementwise_min(c, s ^ (u16x2)7);   // 7 - s
+  // shifts and adds that cannot carry between the halves as 32-bit operations (s is 0 or 1 a half,
+  // v at most 7, pb and 64 + m below 2^15 - 128), so that they fuse into shift-and-add instructions
+  const uint32_t s32 = __builtin_bit_cast(uint32_t, s), v32 = __builtin_bit_cast(uint32_t, v);
+  const uint32_t s7pb = (s32 << 7) + k.pb;
   const uint32_t nzm = __builtin_bit_cast(
-      uint32_t, (__builtin_bit_cast(i16x2, s7 + __builtin_bit_cast(u16x2, k.pb)) - __builtin_bit_cast(i16x2, a)) >>
-                    (i16x2)15);
-  const uint32_t w = __builtin_bit_cast(uint32_t, (s << (u16x2)3) | v);
+      uint32_t, (__builtin_bit_cast(i16x2, s7pb) - __builtin_bit_cast(i16x2, a)) >> (i16x2)15);
+  const uint32_t w = (s32 << 3) | v32;
   const uint32_t wz = (w & nzm) | (0x00070007u & ~nzm);
-  if (IMG) img = __builtin_bit_cast(uint32_t, s7 + __builtin_bit_cast(u16x2, k.m64) - (v << (u16x2)3)) & nzm;
+  if (IMG) img = (((s32 << 7) + k.m64) - (v32 << 3)) & nzm;   // at least 64 + m - 56 > 0 a half: no borrow
   return wz | (__builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, wz) - __builtin_bit_cast(u16x2, nzm)) &
                0x00080008u);
 }
@@ -126,17 +129,18 @@ __device__ __forceinline__ uint32_t mix_pair(uint32_t x, const MixPk& k, uint32_
 template <bool IMG>
 __device__ __forceinline__ uint32_t mix_code8_pk(const uint32_t (&w)[4], const MixPk& k, uint32_t& out0,
                                                  uint32_t& out1) {
-  uint32_t t[4], im[4];
+  uint32_t c2[4], im[4];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const uint32_t c2 = mix_pair<IMG>(w[i], k, im[i]);
-    t[i] = c2 | (c2 >> 12);   // byte 0: element 2i's nibble, then element 2i + 1's
-  }
+  for (int i = 0; i < 4; i++) c2[i] = mix_pair<IMG>(w[i], k, im[i]);   // nibbles at bits 0 and 16
   if (IMG) {
     out0 = __builtin_amdgcn_perm(im[1], im[0], 0x06040200u);
     out1 = __builtin_amdgcn_perm(im[3], im[2], 0x06040200u);
   }
-  return __builtin_amdgcn_perm(t[1], t[0], 0x0C0C0400u) | __builtin_amdgcn_perm(t[3], t[2], 0x04000C0Cu);
+  // two pairs in one word (elements 4j, 4j + 2 at bits 0 and 8, 4j + 1, 4j + 3 at bits 16 and 24),
+  // then the odd elements' nibbles shifted down beside the even ones: the low half holds elements
+  // 4j .. 4j + 3 in order
+  const uint32_t p01 = c2[0] | (c2[1] << 8), p23 = c2[2] | (c2[3] << 8);
+  return __builtin_amdgcn_perm(p23 | (p23 >> 12), p01 | (p01 >> 12), 0x05040100u);
 }
 
 __device__ __forceinline__ uint32_t mix_code8_packed(const uint32_t (&w)[4], int emax, uint32_t m) {
