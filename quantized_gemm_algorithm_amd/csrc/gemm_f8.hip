@@ -134,6 +134,9 @@ struct F8Args {
   uint8_t* qas_p;         //   and its scales [N/128][ceil(M/256)][256][4]
 };
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int F8_C_CPOL = 17;            // buffer store cache policy: sc0 | sc1 (system scope)
+constexpr int F8_RSRC_W3 = 0x00020000;   // buffer resource word 3 for raw 32-bit-offset access
 constexpr int F8_THREADS = 512;   // 8 waves: 4 along M x 2 along N, 64 x 128 outputs each
 
 // LDS slot of 16-byte chunk c of a stage row: 128-byte rows (E4M3) take c ^ aswz(row), 64-byte rows
@@ -370,6 +373,10 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
   constexpr int EPL = 16 / ES;                       // outputs per 16-byte chunk
   uint8_t* reg = smem + (NS - 1) * SB + wave * (32 * PITCH);
   const bool vec_ok = (g.ldc % EPL) == 0 && (((uintptr_t)g.c) & 15) == 0;
+  // Whole-tile stores of C go out as buffer stores (a wave-uniform base and a 32-bit offset a lane)
+  // with system scope (sc0 sc1): they write through the XCD's L2 instead of leaving dirty lines
+  // there for a later write-back. Measured on the 16384 x 5120 x 1280 product (168 MB of C; outputs
+  // unchanged): 101.6 -> 97.3 us; within noise on 4096 x 18944 x 3584.
 
   while (true) {
 #pragma unroll
@@ -454,7 +461,7 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
     const int mw = cur_tm * FT + 64 * wm, nw = cur_tn * FT + 128 * wn;
     // a tile inside C with aligned rows: each pass reads its four rows back and stores them with no
     // per-store bounds checks, so the four LDS reads are in flight together
-    const bool fast = !OQ && vec_ok && (cur_tm + 1) * FT <= g.M && (cur_tn + 1) * FT <= g.N;
+    const bool fast = !OQ && vec_ok && g.ldc <= (1 << 21) && (cur_tm + 1) * FT <= g.M && (cur_tn + 1) * FT <= g.N;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
 #pragma unroll
@@ -481,10 +488,17 @@ __global__ void __launch_bounds__(F8_THREADS, 1) k_gemm_f8(F8Args g) {
             const int row = it * 8 + (lane >> 3);
             v[it] = *(const uint4*)(reg + row * PITCH + ((ch ^ row) & 7) * 16);
           }
-          uint8_t* out = (uint8_t*)g.c + ((int64_t)(mw + 32 * i + (lane >> 3)) * g.ldc + nw + jp * CW + ch * EPL) * ES;
-          const int64_t step8 = (int64_t)8 * g.ldc * ES;   // 8 rows
+          // the pass's 32 rows from a wave-uniform base: the lane offsets stay below 2^31 (fast
+          // requires ldc <= 2^21)
+          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+              (uint8_t*)g.c + (int64_t)(mw + 32 * i) * g.ldc * ES, 0, 0x7FFFFFFF, F8_RSRC_W3);
+          const int off = ((lane >> 3) * (int)g.ldc + nw + jp * CW + ch * EPL) * ES;
+          const int step8 = 8 * (int)g.ldc * ES;   // 8 rows
 #pragma unroll
-          for (int it = 0; it < 4; it++) store16_nt(out + it * step8, v[it]);
+          for (int it = 0; it < 4; it++) {
+            const u32x4_t d = {v[it].x, v[it].y, v[it].z, v[it].w};
+            __builtin_amdgcn_raw_buffer_store_b128(d, rs, off + it * step8, 0, F8_C_CPOL);
+          }
           continue;
         }
 #pragma unroll
