@@ -207,6 +207,32 @@ def test_gemm_workload1_against_exact_integer_product():
         assert_gemm_close(got, exact, bound, fn)
 
 
+@pytest.mark.parametrize("pitch,dtype", [((1 << 21), torch.bfloat16), ((1 << 21) + 16, torch.bfloat16),
+                                         ((1 << 21), torch.float32)])
+def test_gemm_images_wide_row_pitch(pitch, dtype):
+    # whole 256 x 256 tiles written into an output with a very wide row pitch: up to 2^21 elements the
+    # tiles leave through the buffer-store path (32-bit offsets from each pass's first row), beyond it
+    # through the bounds-checked path; both must give the contiguous result and leave the rest of
+    # each row untouched
+    q = _lib()
+    M, N, K = 256, 512, 256
+    rng = np.random.default_rng(pitch % 997)
+    x = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-6, 6, (M, K)))).astype(np.float32)
+    w = (0.05 * rng.standard_normal((N, K))).astype(np.float32)
+    ac, as_, bc, bs = _code(x, w, "4.5b", "fp4")
+    A, S, B, Bs = _to_dev(ac, as_, bc, bs, "4.5b")
+    ai = q.mix_gemm_a_image(A, S, "4.5b")
+    bi = q.mx_gemm_b_image(B, Bs, "fp4")
+    ref = q.mix_mx_gemm_images(ai, bi, out_dtype=dtype)
+    big = torch.full((M, pitch), -3.0, dtype=dtype, device="cuda")
+    out = big[:, :N]
+    q.mix_mx_gemm_images(ai, bi, out_dtype=dtype, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), f"pitch {pitch}: tiles differ from the contiguous product"
+    assert bool((big[:, N:N + 4096] == -3.0).all()) and bool((big[:, -4096:] == -3.0).all()), "row tail touched"
+    del big
+
+
 def test_gemm_zero_and_empty():
     q = _lib()
     # K = 0 gives zeros; M = 0 is an empty call
