@@ -208,20 +208,27 @@ def bench_linear(torch, q, args, which):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    timer = KernelTimer(torch)
-    evs = []
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    # the timed steps: the two launches back to back, nothing recorded between them (an event marker
+    # between launches costs about 3 us of the step each: 216.1 us with none, 225.3 us with three)
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
     torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    # the same steps again with events around each launch: the kernels' own durations
+    timer = KernelTimer(torch)
+    evs = []
     t_start.record()
     for i in range(args.steps):
         evs.append(step(i, timer))
     t_end.record()
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    ms_step_marked = t_start.elapsed_time(t_end) / args.steps
     q_ms = np.mean([KernelTimer.ms(a, b) for a, b, _ in evs])
     g_ms = np.mean([KernelTimer.ms(b, c) for _, b, c in evs])
-    ms_step = total_ms / args.steps
 
     # the quantizer's throughput: back-to-back launches on rotating inputs between two events (the
     # in-step events above also hold the dispatch gap around each event); the codes-only kernel (the
@@ -349,7 +356,10 @@ def bench_linear(torch, q, args, which):
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": gemm_tflops / FP8_MFMA_PEAK_TFLOPS, "traffic": measured_traffic(which),
                      "traffic_source": TRAFFIC_SOURCE, "kernel": "k_gemm_f8",
-                     "kernel_ms": g_ms, "algorithmic_flops": flops, "operand_bytes": gemm_bytes},
+                     "kernel_ms": g_ms, "algorithmic_flops": flops, "operand_bytes": gemm_bytes,
+                     "timing": f"{args.steps} steps with HIP events around each launch, run right after the "
+                               f"{args.steps} timed steps (which carry no events between launches; "
+                               f"{ms_step_marked:.4f} ms per step with them)"},
         "quantizer": {"kernel": "k_mix_quantize (codes and shared fields)", "ms": q_codes_ms,
                       "GB/s": q_codes_bytes / (q_codes_ms * 1e-3) / 1e9,
                       "frac_hbm": q_codes_bytes / (q_codes_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
