@@ -475,6 +475,26 @@ def bench_decode(torch, q, args):
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
 
+    # the same step in one cooperative launch (grid-wide barriers where the launch boundaries stand),
+    # checked against the eager step and timed the same way
+    def step_single(i):
+        bimg, cache = sets[i % nset]
+        q.mix_decode_step(x, bimg, qd, k_new, v_new, cache, pos, L - 1, mu, y=y, o=o, workspace=ws, single=True)
+
+    step_single(0)
+    torch.cuda.synchronize()
+    if not (torch.equal(y, y_ref) and torch.equal(o, o_ref)):
+        raise RuntimeError("the single-launch decode step differs from the three-launch step")
+    for i in range(args.warmup):
+        step_single(i)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step_single(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_single = t0.elapsed_time(t1) / args.steps
+
     # the same work as separate calls (quantize x with its A image, the weight-stream product,
     # attention alone), each timed as back-to-back launches in one graph over the rotating sets
     ac, as_, aimg = q.mix_quantize_gemm(x, "4.5b")
@@ -528,6 +548,7 @@ def bench_decode(torch, q, args):
                      "kernel_ms": ms_step, "timing": f"{args.steps} back-to-back steps between two HIP events",
                      "algorithmic_bytes": step_bytes},
         "parts": {"graph_replay_ms_per_step": ms_graph,
+                  "single_launch_ms_per_step": ms_single,
                   "separate_calls": {"what": "the same work as separate calls, each timed as back-to-back launches "
                                              "in one graph",
                                      "quantize_x_ms": parts_q, "gemv_ms": parts_gv,

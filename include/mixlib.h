@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MIX_ABI_VERSION 3
+#define MIX_ABI_VERSION 4
 
 typedef enum {
   MIX_OK = 0,
@@ -408,6 +408,20 @@ mix_status_t mix_decode_step(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt
                              const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* cache,
                              const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
                              size_t ws_bytes, void* stream);
+
+/*
+ * mix_decode_step in one launch -- the same passages: the exact row maximum that the P^ codes need
+ * (the maximum over every cached key, P1 method overview, last bullet) is kept by a grid-wide barrier
+ * between the scores and the values, and another before the partial sums of O are added, instead of
+ * launch boundaries. Same arguments and workspace as mix_decode_step, and bit-identical results
+ * (the same per-chunk work in the same order). The grid is launched cooperatively, sized to the
+ * workgroups the device holds at once (the launch admits it only if all of them are resident);
+ * MIX_E_HIP if the device cannot launch cooperatively. Not for HIP graph capture.
+ */
+mix_status_t mix_decode_step_single(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt, const void* b_img, void* y,
+                                    const void* q, const void* k_new, const void* v_new,
+                                    const mix_kv_cache_t* cache, const int32_t* pos, int64_t max_pos, int64_t Hq,
+                                    const float* mu, void* o, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mix_decode_step for callers that cannot allocate device memory (code under HIP graph capture, tight

@@ -489,10 +489,12 @@ def mix_attn_decode(q, k_new, v_new, cache, pos, max_pos, mu, debug=False, works
     return o, dbg
 
 
-def mix_decode_step(x, b_img, q, k_new, v_new, cache, pos, max_pos, mu, y=None, o=None, workspace=None):
+def mix_decode_step(x, b_img, q, k_new, v_new, cache, pos, max_pos, mu, y=None, o=None, workspace=None,
+                    single=False):
     """One whole decode step: y = bf16(MiX-4.5b(x) . W^T) for x [B, K] bf16 and the weights' BImage
     (N x K), and the attention step of mix_attn_decode (q [B, Hq, d], k_new/v_new [B, Hkv, d] bf16,
-    pos int32 [B], mu fp32 [B, Hkv, d]). Returns (y bf16 [B, N], o bf16 [B, Hq, d])."""
+    pos int32 [B], mu fp32 [B, Hkv, d]). Returns (y bf16 [B, N], o bf16 [B, Hq, d]). ``single``:
+    the same step in one cooperative launch (mix_decode_step_single)."""
     _need_cuda(x, q, k_new, v_new, pos, mu, y, o, workspace)
     if q.dim() != 3:
         raise MixError("q must be [B, Hq, d]")
@@ -519,7 +521,8 @@ def mix_decode_step(x, b_img, q, k_new, v_new, cache, pos, max_pos, mu, y=None, 
     wsb = lib.mix_decode_step_workspace_bytes(B, K, Hq, cache.Hkv, d, max_pos)
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=x.device)
-    check(lib.mix_decode_step(_p(x), K, N, MX_FMT[b_img.fmt], _p(b_img.buf), _p(y), _p(q), _p(k_new), _p(v_new),
-                              cache.ref, _p(pos), max_pos, Hq, _p(mu), _p(o), _p(workspace), workspace.numel(),
-                              _stream()), "mix_decode_step")
+    entry = lib.mix_decode_step_single if single else lib.mix_decode_step
+    check(entry(_p(x), K, N, MX_FMT[b_img.fmt], _p(b_img.buf), _p(y), _p(q), _p(k_new), _p(v_new), cache.ref,
+                _p(pos), max_pos, Hq, _p(mu), _p(o), _p(workspace), workspace.numel(), _stream()),
+          "mix_decode_step_single" if single else "mix_decode_step")
     return y, o

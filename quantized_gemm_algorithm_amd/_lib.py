@@ -55,6 +55,8 @@ SIGNATURES = {
     "mix_decode_step_workspace_bytes": (ctypes.c_size_t, [c_i64, c_i64, c_i64, c_i64, c_i64, c_i64]),
     "mix_decode_step": (c_int, [c_ptr, c_i64, c_i64, c_int, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_i64,
                                 c_i64, c_ptr, c_ptr, c_ptr, ctypes.c_size_t, c_ptr]),
+    "mix_decode_step_single": (c_int, [c_ptr, c_i64, c_i64, c_int, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
+                                       c_i64, c_i64, c_ptr, c_ptr, c_ptr, ctypes.c_size_t, c_ptr]),
     "mix_decode_step_static_max_bytes": (ctypes.c_size_t, []),
     "mix_decode_step_static": (c_int, [c_ptr, c_i64, c_i64, c_int, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
                                        c_i64, c_i64, c_ptr, c_ptr, c_ptr]),

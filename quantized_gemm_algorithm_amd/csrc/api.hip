@@ -564,6 +564,24 @@ mix_status_t mix_decode_step(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt
                     fn);
 }
 
+mix_status_t mix_decode_step_single(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt, const void* b_img, void* y,
+                                    const void* q, const void* k_new, const void* v_new,
+                                    const mix_kv_cache_t* cache, const int32_t* pos, int64_t max_pos, int64_t Hq,
+                                    const float* mu, void* o, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  const char* fn = "mix_decode_step_single";
+  if (mix_status_t st = check_decode_step(fn, x, K, N, &b_fmt, b_img, y, q, k_new, v_new, cache, pos, max_pos, Hq, mu,
+                                          o))
+    return st;
+  if (!ws) return fail(MIX_E_NULL, "%s: ws is NULL", fn);
+  if ((uintptr_t)ws & 255u) return fail(MIX_E_ALIGN, "%s: ws must be 256-byte aligned", fn);
+  const size_t need = mix::decode_step_ws_bytes(cache->B, K, Hq, cache->Hkv, cache->d, max_pos);
+  if (ws_bytes < need) return fail(MIX_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  return hip_status(mix::decode_step_single_run(x, K, N, b_fmt == MX_FP4, b_img, y, q, k_new, v_new, cache, pos,
+                                                max_pos, Hq, mu, o, ws, (hipStream_t)stream),
+                    fn);
+}
+
 size_t mix_decode_step_static_max_bytes(void) { return mix::DECODE_SCRATCH_BYTES; }
 
 mix_status_t mix_decode_step_static(const void* x, int64_t K, int64_t N, mx_fmt_t b_fmt, const void* b_img, void* y,

@@ -20,6 +20,7 @@
 // Decode keeps the exact global row max with two passes over the keys: pass 1 (scores) computes S
 // for 256-key chunks on the MFMA and per-chunk maxima; pass 2 (pv) takes the global max, forms p
 // and P^ for its chunk and multiplies by V^ on the MFMA; a third launch sums the chunk partials.
+#include <hip/hip_cooperative_groups.h>
 #include <mutex>
 #include <type_traits>
 
@@ -1214,6 +1215,32 @@ __global__ void __launch_bounds__(256) k_decode_combine(DecOps a, int ncb, GvOps
   dec_combine(a, vb);
 }
 
+// The whole decode step in one cooperative launch: the same roles as the three launches above, taken
+// in turn by the grid's workgroups (role-local indices keep their residue modulo 8, so every role keeps
+// its XCD placement), with a grid-wide barrier where a launch boundary stood: the scores need the exact
+// maximum over every chunk before any P^ is coded, and the combine needs every chunk's partials. The
+// cooperative launch admits the grid only if every workgroup is resident, so each barrier is reached
+// by all of them. grid: a multiple of 8 workgroups of 256 threads, dynamic LDS as for k_decode_pv.
+template <int GV>
+__global__ void __launch_bounds__(256) MIX_MFMA_VGPR k_decode_single(DecOps a, XqOps xq, GvOps gv, int nxq, int nsc,
+                                                                     int npv, int ngv, int ncb) {
+  extern __shared__ __align__(16) uint8_t dsm[];
+  const int nwg = (int)gridDim.x;
+  for (int v = (int)blockIdx.x; v < nxq + nsc; v += nwg) {
+    if (v < nxq) dec_xquant(xq, v);
+    else dec_scores(a, v - nxq);
+    __syncthreads();   // the next role's LDS writes wait for this one's reads
+  }
+  cooperative_groups::this_grid().sync();
+  for (int v = (int)blockIdx.x; v < npv + ngv; v += nwg) {
+    if (v < npv) dec_pv(a, v, dsm);
+    else if (GV) gemv_block<GV == 1, 1, DEC_GV_RG, DEC_GV_D>(gv, v - npv, (float*)dsm);
+    __syncthreads();
+  }
+  cooperative_groups::this_grid().sync();
+  for (int v = (int)blockIdx.x; v < ncb; v += nwg) dec_combine(a, v);
+}
+
 // ------------------------------------------------------------------ host orchestration
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1404,9 +1431,23 @@ struct DecodeLinear {
   void* y;
 };
 
+// The resident grid of k_decode_single<GV> with `lds` bytes of dynamic LDS (a multiple of 8 workgroups),
+// or 0 when the device cannot launch cooperatively.
+template <int GV>
+static hipError_t decode_single_grid(size_t lds, int* out) {
+  int dev = 0, coop = 0, ncu = 0, per = 0;
+  HIPCHK(hipGetDevice(&dev));
+  HIPCHK(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+  HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+  HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_decode_single<GV>, 256, lds));
+  *out = coop ? per * ncu / 8 * 8 : 0;
+  return hipSuccess;
+}
+
 static hipError_t decode_run(const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* c,
                              const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
-                             const mix_attn_debug_t* dbg, const DecodeLinear* lin, hipStream_t s) {
+                             const mix_attn_debug_t* dbg, const DecodeLinear* lin, hipStream_t s,
+                             bool single = false) {
   const int64_t B = c->B, Hkv = c->Hkv, d = c->d, Lmax = c->Lmax;
   int64_t Lp;
   int nchunk;
@@ -1446,10 +1487,27 @@ static hipError_t decode_run(const void* q, const void* k_new, const void* v_new
 
   const int bh8 = (int)((B * Hkv + 7) / 8);
   const int nsc = 8 * (nchunk + 1) * bh8, npv = 8 * nchunk * bh8, ncb = (int)((B * Hq + 1) / 2);
-  hipLaunchKernelGGL(k_decode_scores, dim3((unsigned)(nxq + nsc)), dim3(256), 0, s, a, xq, nxq);
-  HIPCHK(hipGetLastError());
   const size_t lds_pv = decode_pv_lds_bytes((int)(Hq / Hkv));
   const size_t lds_gv = gv_lds_bytes<DEC_GV_RG>();
+  if (single) {
+    const int gvk = !lin ? 0 : (lin->b_fp4 ? 1 : 2);
+    const size_t lds = gvk && lds_gv > lds_pv ? lds_gv : lds_pv;
+    int grid = 0;
+    if (gvk == 1) HIPCHK(decode_single_grid<1>(lds, &grid));
+    else if (gvk == 2) HIPCHK(decode_single_grid<2>(lds, &grid));
+    else HIPCHK(decode_single_grid<0>(lds, &grid));
+    if (grid < 8) return hipErrorNotSupported;
+    const int most = std::max(nxq + nsc, std::max(npv + (gvk ? ngv : 0), ncb));
+    grid = std::min(grid, (most + 7) / 8 * 8);
+    int n_xq = nxq, n_sc = nsc, n_pv = npv, n_gv = gvk ? ngv : 0, n_cb = ncb;
+    void* args[] = {&a, &xq, &gv, &n_xq, &n_sc, &n_pv, &n_gv, &n_cb};
+    const void* fn = gvk == 1 ? (const void*)k_decode_single<1>
+                              : gvk == 2 ? (const void*)k_decode_single<2> : (const void*)k_decode_single<0>;
+    HIPCHK(hipLaunchCooperativeKernel(fn, dim3((unsigned)grid), dim3(256), args, (unsigned)lds, s));
+    return hipSuccess;
+  }
+  hipLaunchKernelGGL(k_decode_scores, dim3((unsigned)(nxq + nsc)), dim3(256), 0, s, a, xq, nxq);
+  HIPCHK(hipGetLastError());
   // the weight stream runs beside the pv pass (measured: 50 us per workload-5 step, against 55 us
   // beside the combine, which it then no longer overlaps with the value stream)
   const int gvk = !lin ? 0 : (lin->b_fp4 ? 1 : 2);
@@ -1485,6 +1543,14 @@ hipError_t decode_step_run(const void* x, int64_t K, int64_t N, int b_fp4, const
                            int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws, hipStream_t s) {
   const DecodeLinear lin{x, K, N, b_fp4, b_img, y};
   return decode_run(q, k_new, v_new, c, pos, max_pos, Hq, mu, o, ws, nullptr, &lin, s);
+}
+
+hipError_t decode_step_single_run(const void* x, int64_t K, int64_t N, int b_fp4, const void* b_img, void* y,
+                                  const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* c,
+                                  const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
+                                  hipStream_t s) {
+  const DecodeLinear lin{x, K, N, b_fp4, b_img, y};
+  return decode_run(q, k_new, v_new, c, pos, max_pos, Hq, mu, o, ws, nullptr, &lin, s, true);
 }
 
 // ------------------------------------------------------------------ decode step without allocation

@@ -108,6 +108,11 @@ size_t decode_step_ws_bytes(int64_t B, int64_t K, int64_t Hq, int64_t Hkv, int64
 hipError_t decode_step_run(const void* x, int64_t K, int64_t N, int b_fp4, const void* b_img, void* y, const void* q,
                            const void* k_new, const void* v_new, const mix_kv_cache_t* c, const int32_t* pos,
                            int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws, hipStream_t s);
+// the same step in one cooperative launch (grid-wide barriers where the launch boundaries stood)
+hipError_t decode_step_single_run(const void* x, int64_t K, int64_t N, int b_fp4, const void* b_img, void* y,
+                                  const void* q, const void* k_new, const void* v_new, const mix_kv_cache_t* c,
+                                  const int32_t* pos, int64_t max_pos, int64_t Hq, const float* mu, void* o, void* ws,
+                                  hipStream_t s);
 // the same with the workspace in a file-scope device array of DECODE_SCRATCH_BYTES (no allocation)
 constexpr size_t DECODE_SCRATCH_BYTES = (size_t)32 << 20;
 hipError_t decode_step_static_run(const void* x, int64_t K, int64_t N, int b_fp4, const void* b_img, void* y,

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mix_abi_version() == 3
+    assert lib.mix_abi_version() == 4
     for s in range(8):
         assert lib.mix_status_str(s)
     assert lib.mix_status_str(99) == b"unknown status"

@@ -5,7 +5,9 @@ The step must equal its parts bit for bit: y equals mix_mx_gemm_images of the qu
 (the same per-wave K ranges and sum order), and o equals mix_attn_decode on an identical cache (the
 same kernels); the cache it leaves is the oracle's coding. The parts are checked against the oracle
 elsewhere (tests/test_gpu_attention.py, tests/test_gpu_gemm.py); here y is also compared with the
-oracle's product on every element, and the full-size attention stages on every batch row.
+oracle's product on every element, and the full-size attention stages on every batch row. The
+single-launch form (mix_decode_step_single) must equal the three-launch step bit for bit, over two
+steps in a row.
 """
 import numpy as np
 import pytest
@@ -153,3 +155,60 @@ def test_decode_step_repeated_calls_and_bad_rows():
         assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), step
         _same_cache(c1, c2)
     assert torch.all(o[2].float() == 0)
+
+
+def _single_vs_three(q, B, Hq, Hkv, L_each, N, K, fmt, rng, kh, vh, Lmax, steps=2):
+    """mix_decode_step_single against mix_decode_step on identical caches, `steps` steps in a row
+    (each appends the next token): y, o and the caches bit for bit."""
+    d = 128
+    pos = np.array(L_each, np.int32)
+    (c1, c2), mu = _caches(q, B, Lmax, Hkv, d, kh, vh, pos)
+    wb = synth.f32_to_bf16_bits((0.02 * rng.standard_normal((N, K))).astype(np.float32))
+    bc, bs = q.mx_quantize(dev_bf16(wb), fmt)
+    bimg = q.mx_gemm_b_image(bc, bs, fmt)
+    for s in range(steps):
+        p = pos + s
+        qd = dev_bf16(synth.f32_to_bf16_bits(rng.standard_normal((B, Hq, d)).astype(np.float32) * 3))
+        knew = dev_bf16(np.stack([kh[b, p[b]] for b in range(B)]))
+        vnew = dev_bf16(np.stack([vh[b, p[b]] for b in range(B)]))
+        x = dev_bf16(synth.f32_to_bf16_bits(rng.standard_normal((B, K)).astype(np.float32)))
+        pos_d = torch.as_tensor(p, device="cuda")
+        max_pos = int(p.max())
+        y3, o3 = q.mix_decode_step(x, bimg, qd, knew, vnew, c1, pos_d, max_pos, mu)
+        y1, o1 = q.mix_decode_step(x, bimg, qd, knew, vnew, c2, pos_d, max_pos, mu, single=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y3.view(torch.int16)), f"step {s}: y differs"
+        assert torch.equal(o1.view(torch.int16), o3.view(torch.int16)), f"step {s}: o differs"
+        _same_cache(c1, c2)
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "int4"])
+@pytest.mark.parametrize("B,Hq,Hkv,L_each,N,K", [
+    (4, 8, 2, [40, 63, 255, 300], 300, 256),
+    (3, 28, 4, [511, 17, 1000], 1000, 3584),
+    (16, 14, 2, [5 + 37 * i for i in range(16)], 64, 128),
+])
+def test_decode_step_single_launch_equals_three_launches(fmt, B, Hq, Hkv, L_each, N, K):
+    q = _q()
+    d = 128
+    print(f"single-launch decode step: {fmt} B={B} Hq={Hq} Hkv={Hkv} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(7 * B + N + K)
+    Lmax = ((max(L_each) + 2 + 31) // 32) * 32 + 32
+    kh = np.zeros((B, Lmax, Hkv, d), np.uint16)
+    vh = np.zeros((B, Lmax, Hkv, d), np.uint16)
+    for b in range(B):
+        g = synth.attention_qkv(T=Lmax, Hq=1, Hkv=Hkv, d=d, rng=rng)
+        kh[b], vh[b] = g["k"], g["v"]
+    _single_vs_three(q, B, Hq, Hkv, L_each, N, K, fmt, rng, kh, vh, Lmax)
+
+
+def test_decode_step_single_launch_workload5():
+    # batch 16, x [16, 3584] -> y [16, 18944] (MXFP4), attention over 8192 cached tokens, 28 / 4 heads
+    q = _q()
+    print("single-launch decode step: workload 5 full size", flush=True)
+    g = synth.decode_step()
+    B, L, Hkv, d = g["k_hist"].shape
+    Hq = g["q"].shape[1]
+    N, K = g["w_t"].shape
+    rng = np.random.default_rng(5)
+    _single_vs_three(q, B, Hq, Hkv, [L - 2] * B, N, K, "fp4", rng, g["k_hist"], g["v_hist"], L)
